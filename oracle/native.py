@@ -1,0 +1,71 @@
+"""Build and load the fp64 oracle library (oracle/attention.c).
+
+TEST INFRASTRUCTURE ONLY: the product path never imports this module.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+SOURCE = os.path.join(_HERE, "attention.c")
+LIBRARY = os.path.join(_HERE, "liboracle_attention.so")
+_lib = None
+
+
+def build(force: bool = True) -> str:
+    """Compile the oracle with gcc (-O2, OpenMP, no fast-math) into oracle/."""
+    if not force and os.path.exists(LIBRARY) and os.path.getmtime(LIBRARY) >= os.path.getmtime(SOURCE):
+        return LIBRARY
+    tmp = LIBRARY + ".tmp"
+    subprocess.run(["gcc", "-O2", "-fopenmp", "-fPIC", "-shared", "-std=c11", "-Wall",
+                    "-o", tmp, SOURCE, "-lm"], check=True)
+    os.replace(tmp, LIBRARY)
+    return LIBRARY
+
+
+def load(path: str):
+    """Load a compiled copy of attention.c and return its entry point."""
+    L = ctypes.CDLL(path)
+    f = L.oracle_link_attention
+    f.restype = ctypes.c_int
+    f.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int,
+                  ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
+                  ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p,
+                  ctypes.c_double, ctypes.c_void_p, ctypes.c_void_p]
+    f._keepalive = L
+    return f
+
+
+def lib():
+    global _lib
+    if _lib is None:
+        build(force=False)
+        _lib = load(LIBRARY)
+    return _lib
+
+
+def attention(k, v, key_pos, q, row_pos, rope_theta, entry=None):
+    """fp64 causal RoPE attention; see attention.c. Returns (out [R][Hq][d], lse [R][Hq])."""
+    k = np.ascontiguousarray(k, dtype=np.float64)
+    v = np.ascontiguousarray(v, dtype=np.float64)
+    q = np.ascontiguousarray(q, dtype=np.float64)
+    key_pos = np.ascontiguousarray(key_pos, dtype=np.int64)
+    row_pos = np.ascontiguousarray(row_pos, dtype=np.int64)
+    n_keys, hkv, d = k.shape
+    n_rows, hq, dq = q.shape
+    if v.shape != k.shape or dq != d or key_pos.shape != (n_keys,) or row_pos.shape != (n_rows,):
+        raise ValueError("shape mismatch")
+    out = np.empty((n_rows, hq, d), dtype=np.float64)
+    lse = np.empty((n_rows, hq), dtype=np.float64)
+    fn = entry if entry is not None else lib()
+    rc = fn(n_keys, hkv, hq, d, k.ctypes.data, v.ctypes.data,
+                                     key_pos.ctypes.data, n_rows, q.ctypes.data,
+                                     row_pos.ctypes.data, float(rope_theta),
+                                     out.ctypes.data, lse.ctypes.data)
+    if rc != 0:
+        raise RuntimeError(f"oracle_link_attention failed with {rc}")
+    return out, lse

@@ -1,0 +1,5 @@
+"""Seeded synthetic link workloads: configs and input generators (no link arithmetic)."""
+from .configs import CONFIGS, CONFIG_ORDER, LinkConfig
+from . import gen
+
+__all__ = ["CONFIGS", "CONFIG_ORDER", "LinkConfig", "gen"]

@@ -1,0 +1,110 @@
+"""Seeded synthetic inputs for the link workloads.
+
+Every array is drawn from numpy's PCG64 keyed by (config seed, kind, identifier),
+so a pooled chunk's position-free K/V is the same in every request that links
+it. Values are drawn in float32, scaled, and (for bf16 workloads) rounded to
+bfloat16 with round-to-nearest-even; the rounded values are returned as
+float32 arrays so that every consumer sees exactly the same numbers.
+
+This module holds no part of the link step: it does not select rows, place
+tokens or compute attention.
+"""
+from __future__ import annotations
+
+import numpy as np
+
+from .configs import LinkConfig
+
+KIND_CHUNK_K = 1
+KIND_CHUNK_V = 2
+KIND_Q = 3
+KIND_K_NEW = 4
+KIND_V_NEW = 5
+KIND_PREFIX_K = 6
+KIND_PREFIX_V = 7
+KIND_DRAW = 8
+KIND_Q_ALL = 9
+
+
+def rng(seed: int, kind: int, ident: int) -> np.random.Generator:
+    return np.random.Generator(np.random.PCG64(np.random.SeedSequence([seed, kind, ident])))
+
+
+def round_bf16(x: np.ndarray) -> np.ndarray:
+    """Round float32 values to the nearest bfloat16 (ties to even), kept as float32."""
+    x = np.ascontiguousarray(x, dtype=np.float32)
+    bits = x.view(np.uint32).astype(np.uint64)
+    lsb = (bits >> 16) & 1
+    rounded = ((bits + 0x7FFF + lsb) >> 16) << 16
+    out = rounded.astype(np.uint32).view(np.float32)
+    # NaN/Inf never occur for finite normal draws; keep them untouched anyway.
+    bad = ~np.isfinite(x)
+    if bad.any():
+        out = out.copy()
+        out[bad] = x[bad]
+    return out
+
+
+def normal(seed: int, kind: int, ident: int, shape, scale: float, dtype: str) -> np.ndarray:
+    a = rng(seed, kind, ident).standard_normal(shape, dtype=np.float32)
+    if scale != 1.0:
+        a *= np.float32(scale)
+    if dtype == "bf16":
+        a = round_bf16(a)
+    return a
+
+
+def chunk_kv(cfg: LinkConfig, chunk_id: int) -> tuple[np.ndarray, np.ndarray]:
+    """Position-free K and V of one pooled chunk, each [chunk_len][Hkv][d]."""
+    shape = (cfg.chunk_len, cfg.num_kv_heads, cfg.head_dim)
+    return (normal(cfg.seed, KIND_CHUNK_K, chunk_id, shape, cfg.kv_scale, cfg.dtype),
+            normal(cfg.seed, KIND_CHUNK_V, chunk_id, shape, cfg.kv_scale, cfg.dtype))
+
+
+def prefix_kv(cfg: LinkConfig, request: int) -> tuple[np.ndarray, np.ndarray]:
+    """Cached K and V of a request's prefix, each [prefix_len][Hkv][d]."""
+    shape = (cfg.prefix_len, cfg.num_kv_heads, cfg.head_dim)
+    return (normal(cfg.seed, KIND_PREFIX_K, request, shape, cfg.kv_scale, cfg.dtype),
+            normal(cfg.seed, KIND_PREFIX_V, request, shape, cfg.kv_scale, cfg.dtype))
+
+
+def new_rows(cfg: LinkConfig, request: int, n_rows: int):
+    """New Q [n][Hq][d] and new K, V [n][Hkv][d] for the n recomputed rows of a request."""
+    qs = (n_rows, cfg.num_q_heads, cfg.head_dim)
+    ks = (n_rows, cfg.num_kv_heads, cfg.head_dim)
+    return (normal(cfg.seed, KIND_Q, request, qs, cfg.q_scale, cfg.dtype),
+            normal(cfg.seed, KIND_K_NEW, request, ks, cfg.kv_scale, cfg.dtype),
+            normal(cfg.seed, KIND_V_NEW, request, ks, cfg.kv_scale, cfg.dtype))
+
+
+def request_chunks(cfg: LinkConfig) -> list[list[int]]:
+    """Chunk ids linked by every request, in prompt order."""
+    out = []
+    for r in range(cfg.n_requests):
+        if cfg.pool_draw == "sequential":
+            ids = list(range(cfg.chunks_per_request))
+        elif cfg.pool_draw == "uniform":
+            g = rng(cfg.seed, KIND_DRAW, r)
+            ids = [int(i) for i in g.choice(cfg.pool_size, size=cfg.chunks_per_request, replace=False)]
+        elif cfg.pool_draw == "zipf":
+            # p(rank) ~ rank^-s over ranks 1..pool_size, drawn one at a time
+            # without replacement; chunk id = rank - 1.
+            g = rng(cfg.seed, KIND_DRAW, r)
+            w = np.arange(1, cfg.pool_size + 1, dtype=np.float64) ** (-cfg.zipf_s)
+            avail = np.ones(cfg.pool_size, dtype=bool)
+            ids = []
+            for _ in range(cfg.chunks_per_request):
+                p = np.where(avail, w, 0.0)
+                p /= p.sum()
+                pick = int(g.choice(cfg.pool_size, p=p))
+                avail[pick] = False
+                ids.append(pick)
+        else:
+            raise ValueError(f"unknown pool draw {cfg.pool_draw!r}")
+        out.append(ids)
+    return out
+
+
+def used_chunks(cfg: LinkConfig) -> list[int]:
+    """Distinct chunk ids referenced by any request, ascending."""
+    return sorted({c for ids in request_chunks(cfg) for c in ids})
