@@ -1,0 +1,235 @@
+/*
+ * piclink — the link step of position-independent KV caching on AMD MI355X
+ * (gfx950), as a C ABI.
+ *
+ * The operation. Position-independent caching splits prompt processing into
+ * a per-chunk compile step and a per-request link step: every immutable chunk
+ * is prefilled on its own (positions from 0) and its KV stored; at request
+ * time the stored chunks are concatenated and only a few rows are recomputed,
+ * the first k tokens of each chunk (LegoLink-k, k <= 32 in the paper) plus
+ * the request's new suffix (EPIC, atlas.scime.ai summary, "Approach"; EPIC
+ * abstract on shd-paper.top). MEPIC's paged layout stores chunk KV page
+ * aligned and without positional encoding, applies RoPE inside attention,
+ * recomputes a whole first page per chunk in its block-level variant, and
+ * shares every other page across requests and batches (MEPIC,
+ * searcharxiv.org abstract).
+ *
+ * This library implements:
+ *   pic_store_*   a paged chunk-KV store over caller-owned device pools:
+ *                 page-aligned, refcounted, shareable pages;
+ *   pic_link_plan the host link planner: absolute positions, selected rows,
+ *                 per-request block tables, private/copy-on-write pages and
+ *                 the attention work list;
+ *   pic_link_attend the device link step: scatter of the recomputed rows'
+ *                 K/V into private pages, then causal attention of the
+ *                 selected rows over the linked cache with RoPE applied at
+ *                 each token's linked absolute position.
+ *
+ * Conventions shared by every call.
+ *   - Layouts are row-major. Device K/V pools are [num_pages][Hkv][page][d];
+ *     per-row tensors are [rows][heads][d]; element type is the store's dtype
+ *     (bfloat16 or float32).
+ *   - RoPE pairs dimension i with i + d/2 ("rotate half") at angle
+ *     pos * theta^(-2i/d), no frequency scaling.
+ *   - Attention: query head h reads KV head h / (Hq/Hkv); softmax scale
+ *     1/sqrt(d); a row at position p sees every linked token at position
+ *     <= p.
+ *   - All device memory belongs to the caller. The library allocates none:
+ *     no hipMalloc, no device-side buffers. It owns host metadata only.
+ *   - Device work is enqueued on the caller's stream and returns
+ *     asynchronously; execution faults surface at the caller's next
+ *     synchronisation. One thread at a time per store.
+ *   - Every call returns a pic_status. On a non-OK status, pic_last_error()
+ *     gives a message (thread-local, valid until the next call on the
+ *     thread). No C++ exception crosses the ABI.
+ */
+#ifndef PICLINK_H
+#define PICLINK_H
+
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef int32_t pic_status;
+#define PIC_OK 0
+#define PIC_ERR_INVALID (-1)    /* bad argument, shape or option */
+#define PIC_ERR_OOM (-2)        /* page pool exhausted */
+#define PIC_ERR_NOT_FOUND (-3)  /* unknown chunk id */
+#define PIC_ERR_EXISTS (-4)     /* chunk id already stored */
+#define PIC_ERR_DEVICE (-5)     /* HIP runtime error or kernel launch failure */
+#define PIC_ERR_WORKSPACE (-6)  /* workspace too small or not the uploaded one */
+#define PIC_ERR_STATE (-7)      /* call out of order (e.g. attend before upload) */
+
+#define PIC_DTYPE_BF16 0
+#define PIC_DTYPE_F32 1
+
+typedef struct pic_store pic_store;
+typedef struct pic_plan pic_plan;
+
+/* Shape of the attention layer and of the page pool.
+ *   head_dim      64 or 128
+ *   page_size     tokens per page: 16, 32 or 64
+ *   num_q_heads   a multiple of num_kv_heads, with Hq/Hkv in {1, 2, 4, 8}
+ *   max_position  every linked position must be < max_position (RoPE table rows) */
+typedef struct {
+    int32_t num_q_heads;
+    int32_t num_kv_heads;
+    int32_t head_dim;
+    int32_t page_size;
+    int32_t num_pages;
+    int32_t dtype;
+    double rope_theta;
+    int32_t max_position;
+} pic_store_config;
+
+/* One prompt to link: [prefix] chunk_ids[0..n_chunks) [suffix of suffix_len new tokens].
+ * The prefix is a stored chunk placed first and never recomputed (unless
+ * recompute_all). chunk_ids point to host memory read during pic_link_plan only. */
+typedef struct {
+    int32_t has_prefix;
+    uint64_t prefix_id;
+    const uint64_t *chunk_ids;
+    int32_t n_chunks;
+    int32_t suffix_len;
+} pic_request;
+
+/* k            recomputed leading rows per chunk (LegoLink-k); 0 = link half of LegoLink-0
+ * block_level  recompute the whole first page of every chunk instead (MEPIC)
+ * pos_offset   absolute position of the first token of every request (>= 0)
+ * recompute_all  select every row of every segment (full-recompute comparator)
+ * split_pages  KV pages per attention work item: 0 = automatic, > 0 = at most
+ *              that many, < 0 = never split a (row tile, KV head) */
+typedef struct {
+    int32_t k;
+    int32_t block_level;
+    int32_t pos_offset;
+    int32_t recompute_all;
+    int32_t split_pages;
+} pic_link_options;
+
+/* Sizes of a plan. rows = selected rows R over all requests (the first dim of
+ * q_new/k_new/v_new/out); pages = logical pages over all requests. */
+typedef struct {
+    int64_t rows;
+    int64_t pages;
+    int64_t private_pages;
+    int64_t cow_pages;
+    int64_t work_items;
+    int64_t split_items;
+    int64_t workspace_bytes;
+    int64_t requests;
+} pic_plan_sizes;
+
+/* Device bytes the caller must provide: each K and V pool
+ * (num_pages * Hkv * page_size * head_dim * element size) and the RoPE table
+ * (max_position * head_dim * 4: per position, d/2 cosines then d/2 sines,
+ * float32). */
+pic_status pic_store_sizes(const pic_store_config *cfg, int64_t *pool_bytes, int64_t *rope_table_bytes);
+
+/* Create a store over caller-owned device pools (MEPIC abstract: paged,
+ * page-aligned chunk KV). k_pool/v_pool/rope_table may all be NULL for a
+ * metadata-only store (host planning and tests; pic_link_attend then fails
+ * with PIC_ERR_STATE). With a rope_table, the cos/sin table is computed on the
+ * host in double precision, rounded once to float32, and copied in (blocking
+ * copy on `stream`). The caller keeps the pools alive until pic_store_destroy. */
+pic_status pic_store_create(const pic_store_config *cfg, void *k_pool, void *v_pool, void *rope_table,
+                            hipStream_t stream, pic_store **out);
+
+/* Destroy a store. Outstanding plans must be freed first (PIC_ERR_STATE otherwise). */
+pic_status pic_store_destroy(pic_store *store);
+
+/* Compile-step product in: store the position-free K and V of one chunk
+ * (EPIC summary, "Approach": each chunk compiled independently from
+ * position 0; MEPIC abstract: KV kept without positional encoding, page
+ * aligned). k, v: device [n_tokens][Hkv][d] of the store dtype, pre-RoPE.
+ * Takes ceil(n_tokens / page_size) pages, lowest free ids first; the last
+ * page's padding slots are zero-filled. NULL k and v reserve the pages
+ * without writing (metadata-only use). Errors: PIC_ERR_EXISTS,
+ * PIC_ERR_OOM, PIC_ERR_INVALID (n_tokens <= 0). Asynchronous on `stream`. */
+pic_status pic_store_chunk(pic_store *store, uint64_t id, const void *k, const void *v, int32_t n_tokens,
+                           hipStream_t stream);
+
+/* Page ids (in order) and token count of a stored chunk. pages may be NULL to
+ * query the count; otherwise cap must be >= the page count. */
+pic_status pic_store_chunk_pages(const pic_store *store, uint64_t id, int32_t *pages, int32_t cap,
+                                 int32_t *n_pages, int32_t *n_tokens);
+
+/* Drop a chunk from the table. Its pages return to the pool once no live
+ * plan references them. */
+pic_status pic_store_release(pic_store *store, uint64_t id);
+
+/* Free pages in the pool, stored chunks, live plans. Any pointer may be NULL. */
+pic_status pic_store_stats(const pic_store *store, int32_t *free_pages, int32_t *chunks, int32_t *plans);
+
+/* Link planner (host only, no device work). For every request it walks the
+ * segments, accumulates absolute starts from pos_offset, selects rows (first
+ * min(k, L) of each chunk, or min(page_size, L) in block mode, plus the whole
+ * suffix; EPIC summary, "Approach"; MEPIC abstract), lays every segment on
+ * fresh pages, keeps pages without selected rows shared with the store, and
+ * takes private pages (lowest free ids) for the rest; a private chunk page
+ * that keeps cached rows is copy-on-write from its stored page. It then
+ * builds the attention work list. The plan references every page it uses, so
+ * releasing a chunk while a plan is alive is safe. Errors: PIC_ERR_NOT_FOUND,
+ * PIC_ERR_OOM (private pages), PIC_ERR_INVALID (positions >= max_position,
+ * negative k or offset). */
+pic_status pic_link_plan(pic_store *store, const pic_request *reqs, int32_t n_reqs,
+                         const pic_link_options *opts, pic_plan **out);
+
+pic_status pic_plan_info(const pic_plan *plan, pic_plan_sizes *sizes);
+
+/* Host copies of the plan tables, for checks. Any pointer may be NULL.
+ *   row_pos   [rows]         absolute position of each selected row (request order, then position)
+ *   row_dst   [rows]         physical slot written: page * page_size + slot
+ *   block_table [pages]      physical page of each logical page (requests concatenated)
+ *   pos_map   [pages*page_size] absolute position per logical slot, -1 = padding
+ *   cu_rows   [requests+1]   row offsets per request
+ *   cu_pages  [requests+1]   logical page offsets per request
+ *   cow_src, cow_dst [cow_pages]  stored page copied into each copy-on-write private page */
+pic_status pic_plan_export(const pic_plan *plan, int32_t *row_pos, int32_t *row_dst, int32_t *block_table,
+                           int32_t *pos_map, int32_t *cu_rows, int32_t *cu_pages, int32_t *cow_src,
+                           int32_t *cow_dst);
+
+/* Copy the plan's device tables into the caller's workspace (device memory
+ * of at least sizes.workspace_bytes, 256-byte aligned). Blocking: returns
+ * after the copy on `stream` has completed, so the plan's host memory is free
+ * to go. Must precede pic_link_attend with the same workspace. */
+pic_status pic_plan_upload(pic_store *store, pic_plan *plan, void *workspace, int64_t workspace_bytes,
+                           hipStream_t stream);
+
+/* The link step on the device (EPIC summary, "Approach"; MEPIC abstract).
+ *   q_new  [rows][Hq][d]   queries of the selected rows, pre-RoPE
+ *   k_new, v_new [rows][Hkv][d]  their recomputed keys (pre-RoPE) and values
+ *   out    [rows][Hq][d]   attention output, store dtype
+ *   lse    [rows][Hq]      optional float32 natural-log softmax denominators
+ * 1. scatter: every private page gets the new rows it holds, the cached rows
+ *    copied from its stored page (copy-on-write) and zeroed padding;
+ * 2. attention: every selected row attends causally over its request's linked
+ *    pages with RoPE applied at each token's absolute position;
+ * 3. merge of split KV ranges (log-sum-exp weighted), when the plan split.
+ * workspace must be the one the plan was uploaded to. Asynchronous. */
+pic_status pic_link_attend(pic_store *store, const pic_plan *plan, const void *q_new, const void *k_new,
+                           const void *v_new, void *out, float *lse, void *workspace, int64_t workspace_bytes,
+                           hipStream_t stream);
+
+/* Free a plan and drop its page references (its private pages return to the
+ * pool). Device work that uses the plan must have completed. */
+pic_status pic_plan_free(pic_store *store, pic_plan *plan);
+
+/* Per-kernel timing of pic_link_attend with HIP events on the call's stream.
+ * While enabled, every call records events around the scatter, attention and
+ * merge launches. pic_profile_read synchronises on the recorded events and
+ * returns the summed milliseconds of each stage (ms[0..2]) and the number of
+ * calls since enabling; enabling again resets the sums. */
+pic_status pic_profile_enable(pic_store *store, int32_t on);
+pic_status pic_profile_read(pic_store *store, double *ms, int32_t *calls);
+
+const char *pic_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PICLINK_H */

@@ -1,0 +1,9 @@
+"""piclink: the link step of position-independent KV caching on MI355X (gfx950).
+
+Python face of libpiclink.so (include/piclink.h). The library must be built
+(``__graft_entry__.build()``); nothing here falls back to another
+implementation.
+"""
+from .binding import (DTYPES, LinkRequest, Plan, PicError, Store, link_attend, lib)
+
+__all__ = ["DTYPES", "LinkRequest", "Plan", "PicError", "Store", "link_attend", "lib"]

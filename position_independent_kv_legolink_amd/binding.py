@@ -1,0 +1,285 @@
+"""ctypes binding of libpiclink.so (include/piclink.h): argument marshalling only.
+
+Every step of the link path runs in the library: page allocation, planning,
+the scatter, attention and merge kernels. This module turns torch tensors into
+device pointers and the current torch stream into a hipStream_t, and raises
+on any non-OK status. PyTorch is used for device memory and streams only.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from dataclasses import dataclass
+
+import numpy as np
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIBRARY = os.path.join(HERE, "libpiclink.so")
+
+PIC_OK = 0
+STATUS_NAMES = {-1: "PIC_ERR_INVALID", -2: "PIC_ERR_OOM", -3: "PIC_ERR_NOT_FOUND", -4: "PIC_ERR_EXISTS",
+                -5: "PIC_ERR_DEVICE", -6: "PIC_ERR_WORKSPACE", -7: "PIC_ERR_STATE"}
+DTYPES = {"bf16": 0, "f32": 1}
+
+EXPORTS = ["pic_store_sizes", "pic_store_create", "pic_store_destroy", "pic_store_chunk",
+           "pic_store_chunk_pages", "pic_store_release", "pic_store_stats", "pic_link_plan",
+           "pic_plan_info", "pic_plan_export", "pic_plan_upload", "pic_link_attend", "pic_plan_free",
+           "pic_profile_enable", "pic_profile_read", "pic_last_error"]
+
+
+class PicError(RuntimeError):
+    def __init__(self, status: int, message: str):
+        super().__init__(f"{STATUS_NAMES.get(status, status)}: {message}")
+        self.status = status
+
+
+class StoreConfig(ctypes.Structure):
+    _fields_ = [("num_q_heads", ctypes.c_int32), ("num_kv_heads", ctypes.c_int32),
+                ("head_dim", ctypes.c_int32), ("page_size", ctypes.c_int32),
+                ("num_pages", ctypes.c_int32), ("dtype", ctypes.c_int32),
+                ("rope_theta", ctypes.c_double), ("max_position", ctypes.c_int32)]
+
+
+class Request(ctypes.Structure):
+    _fields_ = [("has_prefix", ctypes.c_int32), ("prefix_id", ctypes.c_uint64),
+                ("chunk_ids", ctypes.POINTER(ctypes.c_uint64)), ("n_chunks", ctypes.c_int32),
+                ("suffix_len", ctypes.c_int32)]
+
+
+class LinkOptions(ctypes.Structure):
+    _fields_ = [("k", ctypes.c_int32), ("block_level", ctypes.c_int32), ("pos_offset", ctypes.c_int32),
+                ("recompute_all", ctypes.c_int32), ("split_pages", ctypes.c_int32)]
+
+
+class PlanSizes(ctypes.Structure):
+    _fields_ = [("rows", ctypes.c_int64), ("pages", ctypes.c_int64), ("private_pages", ctypes.c_int64),
+                ("cow_pages", ctypes.c_int64), ("work_items", ctypes.c_int64),
+                ("split_items", ctypes.c_int64), ("workspace_bytes", ctypes.c_int64),
+                ("requests", ctypes.c_int64)]
+
+
+_lib = None
+
+
+def lib():
+    """Load libpiclink.so; fails loudly when it has not been built."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIBRARY):
+            raise RuntimeError(f"{LIBRARY} is missing: build it first (python -c "
+                               "'import __graft_entry__ as g; g.build()')")
+        L = ctypes.CDLL(LIBRARY)
+        vp, i32, i64, u64 = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_uint64
+        P = ctypes.POINTER
+        sig = {
+            "pic_store_sizes": [P(StoreConfig), P(i64), P(i64)],
+            "pic_store_create": [P(StoreConfig), vp, vp, vp, vp, P(vp)],
+            "pic_store_destroy": [vp],
+            "pic_store_chunk": [vp, u64, vp, vp, i32, vp],
+            "pic_store_chunk_pages": [vp, u64, vp, i32, P(i32), P(i32)],
+            "pic_store_release": [vp, u64],
+            "pic_store_stats": [vp, P(i32), P(i32), P(i32)],
+            "pic_link_plan": [vp, P(Request), i32, P(LinkOptions), P(vp)],
+            "pic_plan_info": [vp, P(PlanSizes)],
+            "pic_plan_export": [vp, vp, vp, vp, vp, vp, vp, vp, vp],
+            "pic_plan_upload": [vp, vp, vp, i64, vp],
+            "pic_link_attend": [vp, vp, vp, vp, vp, vp, vp, vp, i64, vp],
+            "pic_plan_free": [vp, vp],
+            "pic_profile_enable": [vp, i32],
+            "pic_profile_read": [vp, P(ctypes.c_double), P(i32)],
+        }
+        for name, args in sig.items():
+            f = getattr(L, name)
+            f.argtypes = args
+            f.restype = ctypes.c_int32
+        L.pic_last_error.argtypes = []
+        L.pic_last_error.restype = ctypes.c_char_p
+        _lib = L
+    return _lib
+
+
+def _check(status: int):
+    if status != PIC_OK:
+        raise PicError(status, lib().pic_last_error().decode())
+
+
+def _stream():
+    import torch
+    return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+@dataclass
+class LinkRequest:
+    chunk_ids: list
+    suffix_len: int = 0
+    prefix_id: int | None = None
+
+
+class Store:
+    """Paged chunk-KV store over caller-owned torch device pools.
+
+    With ``device=None`` the store holds metadata only (host planning, tests
+    without a GPU).
+    """
+
+    def __init__(self, *, num_q_heads, num_kv_heads, head_dim, page_size, num_pages, dtype,
+                 rope_theta, max_position, device="cuda"):
+        self.cfg = StoreConfig(num_q_heads, num_kv_heads, head_dim, page_size, num_pages, DTYPES[dtype],
+                               float(rope_theta), max_position)
+        self.dtype = dtype
+        self.device = device
+        self.k_pool = self.v_pool = self.rope_table = None
+        L = lib()
+        if device is not None:
+            import torch
+            pool_bytes, rope_bytes = ctypes.c_int64(), ctypes.c_int64()
+            _check(L.pic_store_sizes(ctypes.byref(self.cfg), ctypes.byref(pool_bytes), ctypes.byref(rope_bytes)))
+            tdt = torch.bfloat16 if dtype == "bf16" else torch.float32
+            shape = (num_pages, num_kv_heads, page_size, head_dim)
+            self.k_pool = torch.empty(shape, dtype=tdt, device=device)
+            self.v_pool = torch.empty(shape, dtype=tdt, device=device)
+            self.rope_table = torch.empty((max_position, head_dim), dtype=torch.float32, device=device)
+            assert self.k_pool.numel() * self.k_pool.element_size() == pool_bytes.value
+            assert self.rope_table.numel() * 4 == rope_bytes.value
+        h = ctypes.c_void_p()
+        _check(L.pic_store_create(ctypes.byref(self.cfg), _ptr(self.k_pool), _ptr(self.v_pool),
+                                  _ptr(self.rope_table), _stream() if device is not None else None,
+                                  ctypes.byref(h)))
+        self.handle = h
+
+    def close(self):
+        if self.handle:
+            _check(lib().pic_store_destroy(self.handle))
+            self.handle = None
+
+    def __del__(self):
+        try:
+            if getattr(self, "handle", None):
+                lib().pic_store_destroy(self.handle)
+        except Exception:
+            pass
+
+    def store_chunk(self, chunk_id: int, k=None, v=None, n_tokens: int | None = None):
+        """k, v: device tensors [n][Hkv][d] of the store dtype (position-free); or n_tokens only."""
+        if k is not None:
+            n_tokens = k.shape[0]
+            exp = (n_tokens, self.cfg.num_kv_heads, self.cfg.head_dim)
+            if tuple(k.shape) != exp or tuple(v.shape) != exp or not k.is_contiguous() or not v.is_contiguous():
+                raise ValueError(f"chunk K/V must be contiguous {exp}")
+            if k.dtype != self.k_pool.dtype or v.dtype != self.k_pool.dtype:
+                raise ValueError("chunk K/V dtype differs from the store's")
+        _check(lib().pic_store_chunk(self.handle, chunk_id, _ptr(k), _ptr(v), int(n_tokens),
+                                     _stream() if k is not None else None))
+
+    def chunk_pages(self, chunk_id: int):
+        n, t = ctypes.c_int32(), ctypes.c_int32()
+        _check(lib().pic_store_chunk_pages(self.handle, chunk_id, None, 0, ctypes.byref(n), ctypes.byref(t)))
+        out = np.zeros(n.value, dtype=np.int32)
+        _check(lib().pic_store_chunk_pages(self.handle, chunk_id, out.ctypes.data_as(ctypes.c_void_p), n.value,
+                                           ctypes.byref(n), ctypes.byref(t)))
+        return out, t.value
+
+    def release(self, chunk_id: int):
+        _check(lib().pic_store_release(self.handle, chunk_id))
+
+    def stats(self):
+        f, c, p = ctypes.c_int32(), ctypes.c_int32(), ctypes.c_int32()
+        _check(lib().pic_store_stats(self.handle, ctypes.byref(f), ctypes.byref(c), ctypes.byref(p)))
+        return dict(free_pages=f.value, chunks=c.value, plans=p.value)
+
+    def link_plan(self, requests, *, k=0, block_level=False, pos_offset=0, recompute_all=False,
+                  split_pages=0):
+        n = len(requests)
+        reqs = (Request * max(n, 1))()
+        keep = []
+        for i, r in enumerate(requests):
+            ids = (ctypes.c_uint64 * max(len(r.chunk_ids), 1))(*[int(c) for c in r.chunk_ids])
+            keep.append(ids)
+            reqs[i] = Request(0 if r.prefix_id is None else 1, 0 if r.prefix_id is None else int(r.prefix_id),
+                              ctypes.cast(ids, ctypes.POINTER(ctypes.c_uint64)), len(r.chunk_ids),
+                              int(r.suffix_len))
+        opts = LinkOptions(int(k), int(bool(block_level)), int(pos_offset), int(bool(recompute_all)),
+                           int(split_pages))
+        h = ctypes.c_void_p()
+        _check(lib().pic_link_plan(self.handle, reqs, n, ctypes.byref(opts), ctypes.byref(h)))
+        return Plan(self, h)
+
+    def profile_enable(self, on=True):
+        _check(lib().pic_profile_enable(self.handle, int(bool(on))))
+
+    def profile_read(self):
+        ms = (ctypes.c_double * 3)()
+        calls = ctypes.c_int32()
+        _check(lib().pic_profile_read(self.handle, ms, ctypes.byref(calls)))
+        return dict(scatter_ms=ms[0], attention_ms=ms[1], merge_ms=ms[2], calls=calls.value)
+
+
+class Plan:
+    def __init__(self, store: Store, handle):
+        self.store = store
+        self.handle = handle
+        s = PlanSizes()
+        _check(lib().pic_plan_info(handle, ctypes.byref(s)))
+        self.sizes = {f: getattr(s, f) for f, _ in PlanSizes._fields_}
+        self.workspace = None
+
+    @property
+    def rows(self):
+        return self.sizes["rows"]
+
+    def export(self):
+        s = self.sizes
+        B = self.store.cfg.page_size
+        a = dict(row_pos=np.zeros(s["rows"], np.int32), row_dst=np.zeros(s["rows"], np.int32),
+                 block_table=np.zeros(s["pages"], np.int32), pos_map=np.zeros(s["pages"] * B, np.int32),
+                 cu_rows=np.zeros(s["requests"] + 1, np.int32), cu_pages=np.zeros(s["requests"] + 1, np.int32),
+                 cow_src=np.zeros(s["cow_pages"], np.int32), cow_dst=np.zeros(s["cow_pages"], np.int32))
+        P = lambda x: x.ctypes.data_as(ctypes.c_void_p)
+        _check(lib().pic_plan_export(self.handle, P(a["row_pos"]), P(a["row_dst"]), P(a["block_table"]),
+                                     P(a["pos_map"]), P(a["cu_rows"]), P(a["cu_pages"]), P(a["cow_src"]),
+                                     P(a["cow_dst"])))
+        return a
+
+    def upload(self, workspace=None):
+        """Copy the plan's device tables into ``workspace`` (a uint8 device tensor; allocated if None)."""
+        import torch
+        if workspace is None:
+            workspace = torch.empty(self.sizes["workspace_bytes"], dtype=torch.uint8, device=self.store.device)
+        _check(lib().pic_plan_upload(self.store.handle, self.handle, _ptr(workspace),
+                                     workspace.numel(), _stream()))
+        self.workspace = workspace
+        return workspace
+
+    def free(self):
+        if self.handle:
+            _check(lib().pic_plan_free(self.store.handle, self.handle))
+            self.handle = None
+
+
+def link_attend(store: Store, plan: Plan, q_new, k_new, v_new, out=None, lse=None):
+    """Run the link step; returns ``out`` [R][Hq][d] (and fills ``lse`` [R][Hq] if given)."""
+    import torch
+    c = store.cfg
+    R = plan.rows
+    tdt = store.k_pool.dtype
+    for name, t, h in (("q_new", q_new, c.num_q_heads), ("k_new", k_new, c.num_kv_heads),
+                       ("v_new", v_new, c.num_kv_heads)):
+        if tuple(t.shape) != (R, h, c.head_dim) or t.dtype != tdt or not t.is_contiguous() or t.device.type != "cuda":
+            raise ValueError(f"{name} must be a contiguous {tdt} device tensor of shape {(R, h, c.head_dim)}")
+    if out is None:
+        out = torch.empty((R, c.num_q_heads, c.head_dim), dtype=tdt, device=q_new.device)
+    if tuple(out.shape) != (R, c.num_q_heads, c.head_dim) or out.dtype != tdt or not out.is_contiguous():
+        raise ValueError("out has the wrong shape or dtype")
+    if lse is not None and (tuple(lse.shape) != (R, c.num_q_heads) or lse.dtype != torch.float32
+                            or not lse.is_contiguous()):
+        raise ValueError("lse must be a contiguous float32 tensor [R][Hq]")
+    if plan.workspace is None:
+        raise RuntimeError("upload the plan before link_attend")
+    ws = plan.workspace
+    _check(lib().pic_link_attend(store.handle, plan.handle, _ptr(q_new), _ptr(k_new), _ptr(v_new), _ptr(out),
+                                 _ptr(lse), _ptr(ws), ws.numel(), _stream()))
+    return out

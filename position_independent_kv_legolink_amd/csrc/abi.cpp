@@ -1,0 +1,393 @@
+// The C ABI (include/piclink.h): paged chunk store, planner entry points and the link call.
+// Every export converts C++ exceptions into a pic_status and a thread-local message.
+#include <hip/hip_runtime.h>
+#include <math.h>
+#include <string.h>
+
+#include <algorithm>
+#include <new>
+
+#include "runtime.h"
+
+namespace piclink {
+
+thread_local std::string g_last_error;
+
+void fail(pic_status status, const std::string &message) { throw Error{status, message}; }
+
+namespace {
+
+template <typename F>
+pic_status guarded(F &&f) {
+    try {
+        f();
+        return PIC_OK;
+    } catch (const Error &e) {
+        g_last_error = e.message;
+        return e.status;
+    } catch (const std::bad_alloc &) {
+        g_last_error = "host allocation failed";
+        return PIC_ERR_OOM;
+    } catch (const std::exception &e) {
+        g_last_error = e.what();
+        return PIC_ERR_INVALID;
+    } catch (...) {
+        g_last_error = "unknown error";
+        return PIC_ERR_INVALID;
+    }
+}
+
+void check_hip(hipError_t e, const char *what) {
+    if (e != hipSuccess) fail(PIC_ERR_DEVICE, std::string(what) + ": " + hipGetErrorString(e));
+}
+
+int64_t elem_bytes(int32_t dtype) { return dtype == PIC_DTYPE_BF16 ? 2 : 4; }
+
+bool pow2(int x) { return x > 0 && (x & (x - 1)) == 0; }
+
+}  // namespace
+
+void store_check_config(const pic_store_config &c) {
+    if (c.num_kv_heads <= 0 || c.num_q_heads <= 0 || c.num_q_heads % c.num_kv_heads != 0)
+        fail(PIC_ERR_INVALID, "num_q_heads must be a positive multiple of num_kv_heads");
+    const int g = c.num_q_heads / c.num_kv_heads;
+    if (!pow2(g) || g > 8) fail(PIC_ERR_INVALID, "num_q_heads / num_kv_heads must be 1, 2, 4 or 8");
+    if (c.head_dim != 64 && c.head_dim != 128) fail(PIC_ERR_INVALID, "head_dim must be 64 or 128");
+    if (c.page_size != 16 && c.page_size != 32 && c.page_size != 64)
+        fail(PIC_ERR_INVALID, "page_size must be 16, 32 or 64");
+    if (c.num_pages <= 0) fail(PIC_ERR_INVALID, "num_pages must be positive");
+    if (c.dtype != PIC_DTYPE_BF16 && c.dtype != PIC_DTYPE_F32) fail(PIC_ERR_INVALID, "dtype must be bf16 or f32");
+    if (!(c.rope_theta > 0.0)) fail(PIC_ERR_INVALID, "rope_theta must be positive");
+    if (c.max_position <= 0) fail(PIC_ERR_INVALID, "max_position must be positive");
+}
+
+int32_t store_alloc_page(pic_store *s) {
+    if (s->free_pages.empty()) fail(PIC_ERR_OOM, "page pool exhausted");
+    const int32_t p = *s->free_pages.begin();
+    s->free_pages.erase(s->free_pages.begin());
+    s->refs[p] = 1;
+    return p;
+}
+
+void store_ref(pic_store *s, int32_t page) { s->refs[page] += 1; }
+
+void store_unref(pic_store *s, int32_t page) {
+    if (--s->refs[page] == 0) s->free_pages.insert(page);
+}
+
+const Chunk &store_find(const pic_store *s, uint64_t id) {
+    auto it = s->chunks.find(id);
+    if (it == s->chunks.end()) fail(PIC_ERR_NOT_FOUND, "chunk " + std::to_string(id) + " is not stored");
+    return it->second;
+}
+
+}  // namespace piclink
+
+using namespace piclink;
+
+extern "C" {
+
+const char *pic_last_error(void) { return g_last_error.c_str(); }
+
+pic_status pic_store_sizes(const pic_store_config *cfg, int64_t *pool_bytes, int64_t *rope_table_bytes) {
+    return guarded([&] {
+        if (!cfg) fail(PIC_ERR_INVALID, "null config");
+        store_check_config(*cfg);
+        if (pool_bytes)
+            *pool_bytes = (int64_t)cfg->num_pages * cfg->num_kv_heads * cfg->page_size * cfg->head_dim *
+                          elem_bytes(cfg->dtype);
+        if (rope_table_bytes) *rope_table_bytes = (int64_t)cfg->max_position * cfg->head_dim * 4;
+    });
+}
+
+pic_status pic_store_create(const pic_store_config *cfg, void *k_pool, void *v_pool, void *rope_table,
+                            hipStream_t stream, pic_store **out) {
+    return guarded([&] {
+        if (!cfg || !out) fail(PIC_ERR_INVALID, "null argument");
+        *out = nullptr;
+        store_check_config(*cfg);
+        const bool any = k_pool || v_pool || rope_table;
+        if (any && !(k_pool && v_pool && rope_table))
+            fail(PIC_ERR_INVALID, "k_pool, v_pool and rope_table must all be given or all be NULL");
+        pic_store *s = new pic_store();
+        s->cfg = *cfg;
+        s->shape = {cfg->num_q_heads, cfg->num_kv_heads, cfg->head_dim, cfg->page_size, cfg->dtype,
+                    (int64_t)cfg->num_kv_heads * cfg->page_size * cfg->head_dim};
+        s->k_pool = k_pool;
+        s->v_pool = v_pool;
+        s->rope = static_cast<float *>(rope_table);
+        s->refs.assign(cfg->num_pages, 0);
+        for (int32_t p = 0; p < cfg->num_pages; ++p) s->free_pages.insert(s->free_pages.end(), p);
+        if (rope_table) {
+            try {
+                int dev = 0;
+                hipDeviceProp_t prop;
+                check_hip(hipGetDevice(&dev), "hipGetDevice");
+                check_hip(hipGetDeviceProperties(&prop, dev), "hipGetDeviceProperties");
+                s->num_cus = prop.multiProcessorCount;
+                // cos/sin of pos * theta^(-2i/d) in double precision, rounded once to float
+                const int d = cfg->head_dim, half = d / 2;
+                std::vector<double> inv(half);
+                for (int i = 0; i < half; ++i) inv[i] = pow(cfg->rope_theta, -2.0 * i / d);
+                std::vector<float> table((size_t)cfg->max_position * d);
+                for (int64_t pos = 0; pos < cfg->max_position; ++pos)
+                    for (int i = 0; i < half; ++i) {
+                        const double a = (double)pos * inv[i];
+                        table[pos * d + i] = (float)cos(a);
+                        table[pos * d + half + i] = (float)sin(a);
+                    }
+                check_hip(hipMemcpyAsync(rope_table, table.data(), table.size() * sizeof(float),
+                                         hipMemcpyHostToDevice, stream),
+                          "RoPE table upload");
+                check_hip(hipStreamSynchronize(stream), "RoPE table upload");
+            } catch (...) {
+                delete s;
+                throw;
+            }
+        }
+        *out = s;
+    });
+}
+
+pic_status pic_store_destroy(pic_store *s) {
+    return guarded([&] {
+        if (!s) return;
+        if (s->live_plans > 0) fail(PIC_ERR_STATE, "free every plan before destroying the store");
+        for (auto &m : s->pending)
+            for (hipEvent_t e : m.ev) (void)hipEventDestroy(e);
+        for (hipEvent_t e : s->spare_events) (void)hipEventDestroy(e);
+        delete s;
+    });
+}
+
+pic_status pic_store_chunk(pic_store *s, uint64_t id, const void *k, const void *v, int32_t n_tokens,
+                           hipStream_t stream) {
+    return guarded([&] {
+        if (!s) fail(PIC_ERR_INVALID, "null store");
+        if (n_tokens <= 0) fail(PIC_ERR_INVALID, "n_tokens must be positive");
+        if ((k == nullptr) != (v == nullptr)) fail(PIC_ERR_INVALID, "k and v must both be given or both be NULL");
+        if (k && !s->k_pool) fail(PIC_ERR_STATE, "metadata-only store cannot hold chunk data");
+        if (s->chunks.count(id)) fail(PIC_ERR_EXISTS, "chunk " + std::to_string(id) + " is already stored");
+        const int B = s->cfg.page_size;
+        const int32_t n_pages = (n_tokens + B - 1) / B;
+        if (n_pages > (int64_t)s->free_pages.size())
+            fail(PIC_ERR_OOM, "chunk needs " + std::to_string(n_pages) + " pages, " +
+                                  std::to_string(s->free_pages.size()) + " free");
+        Chunk c;
+        c.n_tokens = n_tokens;
+        for (int i = 0; i < n_pages; ++i) c.pages.push_back(store_alloc_page(s));
+        if (k) {
+            for (int32_t first = 0; first < n_pages; first += kMaxFillPages) {
+                FillPages fp;
+                fp.count = std::min<int32_t>(kMaxFillPages, n_pages - first);
+                fp.first_token = first * B;
+                fp.n_tokens = n_tokens;
+                for (int i = 0; i < fp.count; ++i) fp.ids[i] = c.pages[first + i];
+                const hipError_t e = launch_store_fill(s->shape, s->k_pool, s->v_pool, k, v, fp, stream);
+                if (e != hipSuccess) {
+                    for (int32_t p : c.pages) store_unref(s, p);
+                    check_hip(e, "store_fill launch");
+                }
+            }
+        }
+        s->chunks.emplace(id, std::move(c));
+    });
+}
+
+pic_status pic_store_chunk_pages(const pic_store *s, uint64_t id, int32_t *pages, int32_t cap, int32_t *n_pages,
+                                 int32_t *n_tokens) {
+    return guarded([&] {
+        if (!s) fail(PIC_ERR_INVALID, "null store");
+        const Chunk &c = store_find(s, id);
+        if (n_pages) *n_pages = (int32_t)c.pages.size();
+        if (n_tokens) *n_tokens = c.n_tokens;
+        if (pages) {
+            if (cap < (int32_t)c.pages.size()) fail(PIC_ERR_INVALID, "page buffer too small");
+            std::copy(c.pages.begin(), c.pages.end(), pages);
+        }
+    });
+}
+
+pic_status pic_store_release(pic_store *s, uint64_t id) {
+    return guarded([&] {
+        if (!s) fail(PIC_ERR_INVALID, "null store");
+        auto it = s->chunks.find(id);
+        if (it == s->chunks.end()) fail(PIC_ERR_NOT_FOUND, "chunk " + std::to_string(id) + " is not stored");
+        for (int32_t p : it->second.pages) store_unref(s, p);
+        s->chunks.erase(it);
+    });
+}
+
+pic_status pic_store_stats(const pic_store *s, int32_t *free_pages, int32_t *chunks, int32_t *plans) {
+    return guarded([&] {
+        if (!s) fail(PIC_ERR_INVALID, "null store");
+        if (free_pages) *free_pages = (int32_t)s->free_pages.size();
+        if (chunks) *chunks = (int32_t)s->chunks.size();
+        if (plans) *plans = s->live_plans;
+    });
+}
+
+pic_status pic_link_plan(pic_store *s, const pic_request *reqs, int32_t n_reqs, const pic_link_options *opts,
+                         pic_plan **out) {
+    return guarded([&] {
+        if (!s || !opts || !out) fail(PIC_ERR_INVALID, "null argument");
+        *out = nullptr;
+        *out = build_plan(s, reqs, n_reqs, *opts);
+    });
+}
+
+pic_status pic_plan_info(const pic_plan *plan, pic_plan_sizes *sz) {
+    return guarded([&] {
+        if (!plan || !sz) fail(PIC_ERR_INVALID, "null argument");
+        sz->rows = (int64_t)plan->row_pos.size();
+        sz->pages = (int64_t)plan->pages.size();
+        sz->private_pages = (int64_t)plan->scatter.size();
+        sz->cow_pages = (int64_t)plan->cow_src.size();
+        sz->work_items = (int64_t)plan->work.size();
+        sz->split_items = plan->n_split_items;
+        sz->workspace_bytes = plan->workspace_bytes;
+        sz->requests = plan->n_requests;
+    });
+}
+
+pic_status pic_plan_export(const pic_plan *plan, int32_t *row_pos, int32_t *row_dst, int32_t *block_table,
+                           int32_t *pos_map, int32_t *cu_rows, int32_t *cu_pages, int32_t *cow_src,
+                           int32_t *cow_dst) {
+    return guarded([&] {
+        if (!plan) fail(PIC_ERR_INVALID, "null plan");
+        const int B = plan->owner->cfg.page_size;
+        if (row_pos) std::copy(plan->row_pos.begin(), plan->row_pos.end(), row_pos);
+        if (row_dst) std::copy(plan->row_dst.begin(), plan->row_dst.end(), row_dst);
+        for (size_t i = 0; i < plan->pages.size(); ++i) {
+            const PageDesc &pd = plan->pages[i];
+            if (block_table) block_table[i] = pd.phys;
+            if (pos_map)
+                for (int sl = 0; sl < B; ++sl) pos_map[i * B + sl] = sl < pd.valid ? pd.pos0 + sl : -1;
+        }
+        if (cu_rows) std::copy(plan->cu_rows.begin(), plan->cu_rows.end(), cu_rows);
+        if (cu_pages) std::copy(plan->cu_pages.begin(), plan->cu_pages.end(), cu_pages);
+        if (cow_src) std::copy(plan->cow_src.begin(), plan->cow_src.end(), cow_src);
+        if (cow_dst) std::copy(plan->cow_dst.begin(), plan->cow_dst.end(), cow_dst);
+    });
+}
+
+pic_status pic_plan_upload(pic_store *s, pic_plan *plan, void *workspace, int64_t workspace_bytes,
+                           hipStream_t stream) {
+    return guarded([&] {
+        if (!s || !plan) fail(PIC_ERR_INVALID, "null argument");
+        if (plan->owner != s) fail(PIC_ERR_INVALID, "plan belongs to another store");
+        if (!s->k_pool) fail(PIC_ERR_STATE, "metadata-only store has no device");
+        if (!workspace || workspace_bytes < plan->workspace_bytes)
+            fail(PIC_ERR_WORKSPACE, "workspace needs " + std::to_string(plan->workspace_bytes) + " bytes");
+        if (reinterpret_cast<uintptr_t>(workspace) % 256 != 0) fail(PIC_ERR_WORKSPACE, "workspace must be 256-byte aligned");
+        std::vector<uint8_t> blob(plan->table_bytes, 0);
+        auto put = [&](int64_t off, const void *src, size_t bytes) {
+            if (bytes) memcpy(blob.data() + off, src, bytes);
+        };
+        put(plan->off_pages, plan->pages.data(), plan->pages.size() * sizeof(PageDesc));
+        put(plan->off_row_pos, plan->row_pos.data(), plan->row_pos.size() * sizeof(int32_t));
+        put(plan->off_scatter, plan->scatter.data(), plan->scatter.size() * sizeof(ScatterDesc));
+        put(plan->off_work, plan->work.data(), plan->work.size() * sizeof(WorkDesc));
+        put(plan->off_merge, plan->merge.data(), plan->merge.size() * sizeof(MergeDesc));
+        if (!blob.empty()) {
+            check_hip(hipMemcpyAsync(workspace, blob.data(), blob.size(), hipMemcpyHostToDevice, stream),
+                      "plan upload");
+            check_hip(hipStreamSynchronize(stream), "plan upload");
+        }
+        plan->uploaded_to = workspace;
+    });
+}
+
+pic_status pic_link_attend(pic_store *s, const pic_plan *plan, const void *q_new, const void *k_new,
+                           const void *v_new, void *out, float *lse, void *workspace, int64_t workspace_bytes,
+                           hipStream_t stream) {
+    return guarded([&] {
+        if (!s || !plan) fail(PIC_ERR_INVALID, "null argument");
+        if (plan->owner != s) fail(PIC_ERR_INVALID, "plan belongs to another store");
+        if (!s->k_pool) fail(PIC_ERR_STATE, "metadata-only store has no device");
+        if (!plan->uploaded_to || plan->uploaded_to != workspace)
+            fail(PIC_ERR_WORKSPACE, "workspace is not the one this plan was uploaded to");
+        if (workspace_bytes < plan->workspace_bytes) fail(PIC_ERR_WORKSPACE, "workspace too small");
+        const bool has_rows = !plan->row_pos.empty();
+        if (has_rows && (!q_new || !k_new || !v_new || !out)) fail(PIC_ERR_INVALID, "null row tensor");
+        uint8_t *ws = static_cast<uint8_t *>(workspace);
+        AttnTables t;
+        t.pages = reinterpret_cast<const PageDesc *>(ws + plan->off_pages);
+        t.row_pos = reinterpret_cast<const int32_t *>(ws + plan->off_row_pos);
+        t.work = reinterpret_cast<const WorkDesc *>(ws + plan->off_work);
+        t.n_work = (int)plan->work.size();
+        t.merge = reinterpret_cast<const MergeDesc *>(ws + plan->off_merge);
+        t.n_merge = (int)plan->merge.size();
+        t.part_o = reinterpret_cast<float *>(ws + plan->off_part_o);
+        t.part_lse = reinterpret_cast<float *>(ws + plan->off_part_lse);
+
+        ProfileMarks marks{};
+        const bool prof = s->profiling;
+        if (prof) {
+            for (int i = 0; i < 4; ++i) {
+                if (!s->spare_events.empty()) {
+                    marks.ev[i] = s->spare_events.back();
+                    s->spare_events.pop_back();
+                } else {
+                    check_hip(hipEventCreate(&marks.ev[i]), "hipEventCreate");
+                }
+            }
+            check_hip(hipEventRecord(marks.ev[0], stream), "hipEventRecord");
+        }
+        check_hip(launch_scatter(s->shape, s->k_pool, s->v_pool, k_new, v_new,
+                                 reinterpret_cast<const ScatterDesc *>(ws + plan->off_scatter),
+                                 (int)plan->scatter.size(), stream),
+                  "scatter launch");
+        if (prof) check_hip(hipEventRecord(marks.ev[1], stream), "hipEventRecord");
+        check_hip(launch_attention(s->shape, q_new, s->k_pool, s->v_pool, s->rope, t, out, lse, stream),
+                  "attention launch");
+        if (prof) check_hip(hipEventRecord(marks.ev[2], stream), "hipEventRecord");
+        check_hip(launch_merge(s->shape, t, out, lse, stream), "merge launch");
+        if (prof) {
+            check_hip(hipEventRecord(marks.ev[3], stream), "hipEventRecord");
+            s->pending.push_back(marks);
+        }
+    });
+}
+
+pic_status pic_plan_free(pic_store *s, pic_plan *plan) {
+    return guarded([&] {
+        if (!s || !plan) fail(PIC_ERR_INVALID, "null argument");
+        if (plan->owner != s) fail(PIC_ERR_INVALID, "plan belongs to another store");
+        release_plan(s, plan);
+    });
+}
+
+pic_status pic_profile_enable(pic_store *s, int32_t on) {
+    return guarded([&] {
+        if (!s) fail(PIC_ERR_INVALID, "null store");
+        for (auto &m : s->pending)
+            for (hipEvent_t e : m.ev) s->spare_events.push_back(e);
+        s->pending.clear();
+        s->profiling = on != 0;
+        s->profiled_calls = 0;
+        s->profiled_ms[0] = s->profiled_ms[1] = s->profiled_ms[2] = 0.0;
+    });
+}
+
+pic_status pic_profile_read(pic_store *s, double *ms, int32_t *calls) {
+    return guarded([&] {
+        if (!s) fail(PIC_ERR_INVALID, "null store");
+        for (auto &m : s->pending) {
+            check_hip(hipEventSynchronize(m.ev[3]), "hipEventSynchronize");
+            for (int i = 0; i < 3; ++i) {
+                float t = 0.0f;
+                check_hip(hipEventElapsedTime(&t, m.ev[i], m.ev[i + 1]), "hipEventElapsedTime");
+                s->profiled_ms[i] += t;
+            }
+            s->profiled_calls += 1;
+            for (hipEvent_t e : m.ev) s->spare_events.push_back(e);
+        }
+        s->pending.clear();
+        if (ms)
+            for (int i = 0; i < 3; ++i) ms[i] = s->profiled_ms[i];
+        if (calls) *calls = s->profiled_calls;
+    });
+}
+
+}  // extern "C"

@@ -1,0 +1,842 @@
+// HIP kernels of the link step for gfx950 (CDNA4).
+//
+//   store_fill     chunk K/V [n][Hkv][d] -> page-aligned pool pages (compile-step product in)
+//   link_scatter   recomputed rows' K/V -> request-private pages, copy-on-write of cached rows
+//   link_attention causal attention of the selected rows over their request's linked pages,
+//                  RoPE applied in registers at each token's absolute position, grouped-query
+//                  rows of one KV head per work group, MFMA for QK^T and PV, online softmax
+//   link_merge     log-sum-exp combination of split KV ranges
+//
+// Method: EPIC (atlas.scime.ai summary, "Approach": chunks compiled from position 0, the first
+// k tokens of every chunk recomputed at link time) and MEPIC (searcharxiv.org abstract:
+// page-aligned position-free chunk KV, RoPE fused in the attention kernel, first block
+// request-specific, other blocks shared).
+#include <hip/hip_runtime.h>
+#include <limits.h>
+#include <math.h>
+#include <stdint.h>
+
+#include "launch.h"
+
+namespace piclink {
+namespace {
+
+typedef float floatx2 __attribute__((ext_vector_type(2)));
+typedef float floatx4 __attribute__((ext_vector_type(4)));
+typedef float floatx16 __attribute__((ext_vector_type(16)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef int32_t i32x4 __attribute__((ext_vector_type(4)));
+
+// Scores are kept in raw q.k units; the running maximum is only moved when a
+// row's maximum grows by more than 2^kRescaleLog2 in softmax units, so the
+// accumulator is rescaled rarely. Exact for any stale maximum: exponentials
+// stay <= 2^kRescaleLog2.
+constexpr float kRescaleLog2 = 8.0f;
+constexpr float kInitMax = -1.0e30f;
+constexpr int kNeverAttended = INT_MAX;
+
+__device__ __forceinline__ float bf_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+
+__device__ __forceinline__ uint32_t pack_bf16(float a, float b) {
+    floatx2 f = {a, b};
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector(f, bf16x2));
+}
+
+__device__ __forceinline__ int swap_bits23(int x) {
+    return (x & ~12) | ((x & 4) << 1) | ((x & 8) >> 1);
+}
+
+struct AttnParams {
+    const void *q;
+    const void *k_pool;
+    const void *v_pool;
+    const float *rope;          // [max_position][d]: d/2 cosines, then d/2 sines
+    const PageDesc *pages;
+    const int32_t *row_pos;
+    const WorkDesc *work;
+    void *out;
+    float *lse;
+    float *part_o;
+    float *part_lse;
+    int hq, hkv, gshift, pshift;
+    int64_t page_elems;
+    float scale_log2;           // log2(e) / sqrt(d)
+    float scale;                // 1 / sqrt(d)
+};
+
+// Rotate 8 bf16 pairs (x_i, x_{i+d/2}) by (cos, sin); returns rounded bf16 words.
+__device__ __forceinline__ void rope8_bf16(const u32x4 &lo, const u32x4 &hi, const floatx4 c[2],
+                                           const floatx4 s[2], u32x4 &olo, u32x4 &ohi) {
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+        const float x0 = bf_lo(lo[w]), x1 = bf_hi(lo[w]);
+        const float y0 = bf_lo(hi[w]), y1 = bf_hi(hi[w]);
+        const float c0 = c[w >> 1][2 * (w & 1)], c1 = c[w >> 1][2 * (w & 1) + 1];
+        const float s0 = s[w >> 1][2 * (w & 1)], s1 = s[w >> 1][2 * (w & 1) + 1];
+        olo[w] = pack_bf16(fmaf(x0, c0, -y0 * s0), fmaf(x1, c1, -y1 * s1));
+        ohi[w] = pack_bf16(fmaf(y0, c0, x0 * s0), fmaf(y1, c1, x1 * s1));
+    }
+}
+
+// Does a key tile need the causal / padding mask for this work group?
+__device__ __forceinline__ bool tile_needs_mask(const PageDesc *pg, const WorkDesc &w, int lp0, int ppt,
+                                                int page_size) {
+    if (lp0 + ppt > w.page_end) return true;
+    for (int q = 0; q < ppt; ++q)
+        if (pg[lp0 + q].valid < page_size) return true;
+    const PageDesc last = pg[lp0 + ppt - 1];
+    return last.pos0 + page_size - 1 > w.rpos_min;
+}
+
+// ---------------------------------------------------------------------------------------------
+// bf16 attention. Work group = NW waves; wave w owns M-rows [32*MB*w, 32*MB*(w+1)) as MB 32-row
+// MFMA blocks; M-row m is (tile row m / G, query head m % G of the work item's KV head).
+//   S^T = K' Q'^T   (v_mfma_f32_32x32x16_bf16, A = rotated K rows from LDS, B = rotated Q in VGPRs)
+//   O^T += V^T P^T  (A = V^T from LDS, B = P straight from the S^T accumulators)
+// Keys of a 16-key group are stored in V^T in the order that makes each lane's P values a
+// contiguous MFMA operand (bits 2 and 3 of the key index swapped).
+template <int D, int NW, int MB>
+__global__ __launch_bounds__(NW * 64, 1) void link_attention_bf16(AttnParams p) {
+    constexpr int NT = NW * 64;
+    constexpr int KT = kKeysPerTile;
+    constexpr int KS = D + 8;          // K' row stride in LDS (bf16)
+    constexpr int VS = KT + 8;         // V^T row stride in LDS (bf16)
+    constexpr int NS = D / 16;         // k-steps of QK^T
+    constexpr int NDB = D / 32;        // 32-wide d blocks of PV
+    constexpr int KPAIRS = KT * (D / 16);          // (key, 8-dim lo/hi) pairs per tile
+    constexpr int VPAIRS = (KT / 2) * (D / 8);     // (key pair, 8 dims) chunks per tile
+    constexpr int NKP = (KPAIRS + NT - 1) / NT;
+    constexpr int NVP = (VPAIRS + NT - 1) / NT;
+    constexpr int TQ = NW * MB * 32;
+
+    __shared__ __attribute__((aligned(16))) uint16_t ks[2][KT * KS];
+    __shared__ __attribute__((aligned(16))) uint16_t vts[2][D * VS];
+    __shared__ __attribute__((aligned(16))) int kpos_s[2][KT];
+
+    const WorkDesc w = p.work[blockIdx.x];
+    if (w.n_rows <= 0) return;
+
+    const int tid = threadIdx.x;
+    const int wave = tid >> 6, lane = tid & 63, ln = lane & 31, lg = lane >> 5;
+    const int G = 1 << p.gshift;
+    const int page_size = 1 << p.pshift;
+    const int ppt = KT >> p.pshift;
+    const PageDesc *pg = p.pages + w.page_base;
+    const uint16_t *kpool = static_cast<const uint16_t *>(p.k_pool);
+    const uint16_t *vpool = static_cast<const uint16_t *>(p.v_pool);
+    const int64_t head_off = (int64_t)w.kv_head * page_size * D;
+
+    // ---- rotated Q fragments, held for the whole key range
+    u32x4 qf[MB][NS];
+    int rpos[MB];
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb) {
+        const int m = (wave * MB + mb) * 32 + ln;
+        const int ti = m >> p.gshift;
+        const bool valid = ti < w.n_rows;
+        const int row = w.row0 + (valid ? ti : 0);
+        const int qh = w.kv_head * G + (m & (G - 1));
+        const int rp = valid ? p.row_pos[row] : -1;
+        rpos[mb] = rp;
+        const uint16_t *qrow = static_cast<const uint16_t *>(p.q) + ((int64_t)row * p.hq + qh) * D;
+        const float *cs = p.rope + (int64_t)(valid ? rp : 0) * D;
+#pragma unroll
+        for (int s = 0; s < NS / 2; ++s) {
+            const int e0 = 16 * s + 8 * lg;
+            u32x4 lo = {0, 0, 0, 0}, hi = {0, 0, 0, 0};
+            if (valid) {
+                lo = *reinterpret_cast<const u32x4 *>(qrow + e0);
+                hi = *reinterpret_cast<const u32x4 *>(qrow + D / 2 + e0);
+            }
+            floatx4 c[2], sn[2];
+            c[0] = *reinterpret_cast<const floatx4 *>(cs + e0);
+            c[1] = *reinterpret_cast<const floatx4 *>(cs + e0 + 4);
+            sn[0] = *reinterpret_cast<const floatx4 *>(cs + D / 2 + e0);
+            sn[1] = *reinterpret_cast<const floatx4 *>(cs + D / 2 + e0 + 4);
+            rope8_bf16(lo, hi, c, sn, qf[mb][s], qf[mb][s + NS / 2]);
+        }
+    }
+
+    // ---- staging registers of the next key tile
+    u32x4 k_lo[NKP], k_hi[NKP];
+    floatx4 k_c[NKP][2], k_s[NKP][2];
+    u32x4 v_a[NVP], v_b[NVP];
+    int kp_next = kNeverAttended;
+
+    auto load_tile = [&](int t) {
+        const int lp0 = w.page_begin + t * ppt;
+#pragma unroll
+        for (int u = 0; u < NKP; ++u) {
+            const int pi = tid + NT * u;
+            if (KPAIRS % NT != 0 && pi >= KPAIRS) break;
+            const int key = pi / (D / 16), c = pi % (D / 16);
+            const int lp = lp0 + (key >> p.pshift), slot = key & (page_size - 1);
+            bool ok = false;
+            int pos = 0;
+            int64_t base = 0;
+            if (lp < w.page_end) {
+                const PageDesc pd = pg[lp];
+                if (slot < pd.valid) {
+                    ok = true;
+                    pos = pd.pos0 + slot;
+                    base = (int64_t)pd.phys * p.page_elems + head_off + (int64_t)slot * D;
+                }
+            }
+            k_lo[u] = ok ? *reinterpret_cast<const u32x4 *>(kpool + base + 8 * c) : u32x4{0, 0, 0, 0};
+            k_hi[u] = ok ? *reinterpret_cast<const u32x4 *>(kpool + base + D / 2 + 8 * c) : u32x4{0, 0, 0, 0};
+            const float *cs = p.rope + (int64_t)pos * D + 8 * c;
+            k_c[u][0] = *reinterpret_cast<const floatx4 *>(cs);
+            k_c[u][1] = *reinterpret_cast<const floatx4 *>(cs + 4);
+            k_s[u][0] = *reinterpret_cast<const floatx4 *>(cs + D / 2);
+            k_s[u][1] = *reinterpret_cast<const floatx4 *>(cs + D / 2 + 4);
+        }
+#pragma unroll
+        for (int u = 0; u < NVP; ++u) {
+            const int pi = tid + NT * u;
+            if (VPAIRS % NT != 0 && pi >= VPAIRS) break;
+            const int key0 = 2 * (pi / (D / 8)), c16 = pi % (D / 8);
+            const int lp = lp0 + (key0 >> p.pshift), slot = key0 & (page_size - 1);
+            u32x4 a = {0, 0, 0, 0}, b = {0, 0, 0, 0};
+            if (lp < w.page_end) {
+                const PageDesc pd = pg[lp];
+                const int64_t base = (int64_t)pd.phys * p.page_elems + head_off + (int64_t)slot * D + 8 * c16;
+                if (slot < pd.valid) a = *reinterpret_cast<const u32x4 *>(vpool + base);
+                if (slot + 1 < pd.valid) b = *reinterpret_cast<const u32x4 *>(vpool + base + D);
+            }
+            v_a[u] = a;
+            v_b[u] = b;
+        }
+        if (tid < KT) {
+            const int lp = lp0 + (tid >> p.pshift), slot = tid & (page_size - 1);
+            int kp = kNeverAttended;
+            if (lp < w.page_end) {
+                const PageDesc pd = pg[lp];
+                if (slot < pd.valid) kp = pd.pos0 + slot;
+            }
+            kp_next = kp;
+        }
+    };
+
+    auto store_tile = [&](int buf) {
+#pragma unroll
+        for (int u = 0; u < NKP; ++u) {
+            const int pi = tid + NT * u;
+            if (KPAIRS % NT != 0 && pi >= KPAIRS) break;
+            const int key = pi / (D / 16), c = pi % (D / 16);
+            u32x4 olo, ohi;
+            rope8_bf16(k_lo[u], k_hi[u], k_c[u], k_s[u], olo, ohi);
+            *reinterpret_cast<u32x4 *>(&ks[buf][key * KS + 8 * c]) = olo;
+            *reinterpret_cast<u32x4 *>(&ks[buf][key * KS + D / 2 + 8 * c]) = ohi;
+        }
+#pragma unroll
+        for (int u = 0; u < NVP; ++u) {
+            const int pi = tid + NT * u;
+            if (VPAIRS % NT != 0 && pi >= VPAIRS) break;
+            const int key0 = 2 * (pi / (D / 8)), c16 = pi % (D / 8);
+            const int col = (key0 & ~15) | swap_bits23(key0 & 15);
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+                const uint32_t wa = v_a[u][i >> 1], wb = v_b[u][i >> 1];
+                const uint32_t word = (i & 1) ? ((wa >> 16) | (wb & 0xffff0000u)) : ((wa & 0xffffu) | (wb << 16));
+                *reinterpret_cast<uint32_t *>(&vts[buf][(8 * c16 + i) * VS + col]) = word;
+            }
+        }
+        if (tid < KT) kpos_s[buf][tid] = kp_next;
+    };
+
+    floatx16 oacc[MB][NDB];
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+        for (int db = 0; db < NDB; ++db)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) oacc[mb][db][r] = 0.0f;
+    float mrow[MB], lrow[MB];
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb) {
+        mrow[mb] = kInitMax;
+        lrow[mb] = 0.0f;
+    }
+
+    const int ntiles = (w.page_end - w.page_begin + ppt - 1) / ppt;
+    load_tile(0);
+    store_tile(0);
+    __syncthreads();
+
+    for (int t = 0; t < ntiles; ++t) {
+        const int buf = t & 1;
+        const bool more = t + 1 < ntiles;
+        if (more) load_tile(t + 1);
+        const bool need_mask = tile_needs_mask(pg, w, w.page_begin + t * ppt, ppt, page_size);
+
+        floatx16 sacc[2][MB];
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+            for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) sacc[kb][mb][r] = 0.0f;
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb) {
+#pragma unroll
+            for (int s = 0; s < NS; ++s) {
+                const bf16x8 a = *reinterpret_cast<const bf16x8 *>(&ks[buf][(kb * 32 + ln) * KS + 16 * s + 8 * lg]);
+#pragma unroll
+                for (int mb = 0; mb < MB; ++mb)
+                    sacc[kb][mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+                        a, __builtin_bit_cast(bf16x8, qf[mb][s]), sacc[kb][mb], 0, 0, 0);
+            }
+        }
+
+        u32x4 pf[MB][2][2];
+#pragma unroll
+        for (int mb = 0; mb < MB; ++mb) {
+            if (need_mask) {
+#pragma unroll
+                for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        const i32x4 kp4 = *reinterpret_cast<const i32x4 *>(&kpos_s[buf][kb * 32 + 8 * i + 4 * lg]);
+#pragma unroll
+                        for (int j = 0; j < 4; ++j)
+                            if (kp4[j] > rpos[mb]) sacc[kb][mb][4 * i + j] = -INFINITY;
+                    }
+            }
+            float mx = sacc[0][mb][0];
+#pragma unroll
+            for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sacc[kb][mb][r]);
+            mx = fmaxf(mx, __shfl_xor(mx, 32));
+            const bool upd = (mx - mrow[mb]) * p.scale_log2 > kRescaleLog2;
+            if (__any(upd)) {
+                const float mnew = upd ? mx : mrow[mb];
+                const float alpha = __builtin_amdgcn_exp2f((mrow[mb] - mnew) * p.scale_log2);
+                lrow[mb] *= alpha;
+#pragma unroll
+                for (int db = 0; db < NDB; ++db)
+#pragma unroll
+                    for (int r = 0; r < 16; ++r) oacc[mb][db][r] *= alpha;
+                mrow[mb] = mnew;
+            }
+            const float msc = mrow[mb] * p.scale_log2;
+            float lsum = 0.0f;
+#pragma unroll
+            for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) {
+                    const float e = __builtin_amdgcn_exp2f(fmaf(sacc[kb][mb][r], p.scale_log2, -msc));
+                    sacc[kb][mb][r] = e;
+                    lsum += e;
+                }
+            lrow[mb] += lsum;
+#pragma unroll
+            for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+                for (int s2 = 0; s2 < 2; ++s2)
+#pragma unroll
+                    for (int u = 0; u < 4; ++u)
+                        pf[mb][kb][s2][u] = pack_bf16(sacc[kb][mb][8 * s2 + 2 * u], sacc[kb][mb][8 * s2 + 2 * u + 1]);
+        }
+
+#pragma unroll
+        for (int db = 0; db < NDB; ++db)
+#pragma unroll
+            for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+                for (int s2 = 0; s2 < 2; ++s2) {
+                    const bf16x8 a = *reinterpret_cast<const bf16x8 *>(
+                        &vts[buf][(db * 32 + ln) * VS + kb * 32 + 16 * s2 + 8 * lg]);
+#pragma unroll
+                    for (int mb = 0; mb < MB; ++mb)
+                        oacc[mb][db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+                            a, __builtin_bit_cast(bf16x8, pf[mb][kb][s2]), oacc[mb][db], 0, 0, 0);
+                }
+
+        if (more) store_tile(buf ^ 1);
+        __syncthreads();
+    }
+
+    // ---- epilogue: normalise, write the output (or this split's partial result)
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb) {
+        const int m = (wave * MB + mb) * 32 + ln;
+        const int ti = m >> p.gshift;
+        const float lt = lrow[mb] + __shfl_xor(lrow[mb], 32);
+        const float inv = lt > 0.0f ? 1.0f / lt : 0.0f;
+        const float lse_v = lt > 0.0f ? mrow[mb] * p.scale + logf(lt) : -INFINITY;
+        if (ti >= w.n_rows) continue;
+        const int row = w.row0 + ti;
+        const int qh = w.kv_head * G + (m & (G - 1));
+        if (w.partial < 0) {
+            uint16_t *orow = static_cast<uint16_t *>(p.out) + ((int64_t)row * p.hq + qh) * D;
+#pragma unroll
+            for (int db = 0; db < NDB; ++db)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const int d0 = db * 32 + 8 * i + 4 * lg;
+                    u32x2 v;
+                    v[0] = pack_bf16(oacc[mb][db][4 * i] * inv, oacc[mb][db][4 * i + 1] * inv);
+                    v[1] = pack_bf16(oacc[mb][db][4 * i + 2] * inv, oacc[mb][db][4 * i + 3] * inv);
+                    *reinterpret_cast<u32x2 *>(orow + d0) = v;
+                }
+            if (p.lse && lg == 0) p.lse[(int64_t)row * p.hq + qh] = lse_v;
+        } else {
+            float *po = p.part_o + ((int64_t)w.partial * TQ + m) * D;
+#pragma unroll
+            for (int db = 0; db < NDB; ++db)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const int d0 = db * 32 + 8 * i + 4 * lg;
+                    floatx4 v = {oacc[mb][db][4 * i] * inv, oacc[mb][db][4 * i + 1] * inv,
+                                 oacc[mb][db][4 * i + 2] * inv, oacc[mb][db][4 * i + 3] * inv};
+                    *reinterpret_cast<floatx4 *>(po + d0) = v;
+                }
+            if (lg == 0) p.part_lse[(int64_t)w.partial * TQ + m] = lse_v;
+        }
+    }
+}
+
+// ---------------------------------------------------------------------------------------------
+// fp32 attention. Work group = 4 waves of one 32-row MFMA block each (128 M-rows).
+//   S^T = K' Q'^T   (v_mfma_f32_32x32x2f32; lane group lg supplies dimension 8(s/4) + 4lg + s%4
+//                    at k-step s, so each lane reads 4 consecutive dimensions per 4 steps)
+//   O^T += V^T P^T  (k-step s of a 32-key block pairs the key held in S^T accumulator s)
+template <int D>
+__global__ __launch_bounds__(kThreads, 1) void link_attention_f32(AttnParams p) {
+    constexpr int KT = kKeysPerTile;
+    constexpr int KS = D + 4;
+    constexpr int VS = D + 4;
+    constexpr int NDB = D / 32;
+    constexpr int NQ = D / 8;                       // float4 groups of Q held per lane
+    constexpr int NKP = KT * (D / 8) / kThreads;    // K (lo, hi) float4 pairs per thread
+    constexpr int NV = KT * (D / 4) / kThreads;     // V float4 chunks per thread
+    constexpr int TQ = 128;
+    static_assert(NKP >= 1 && NV >= 1, "tile too small for the work group");
+
+    __shared__ __attribute__((aligned(16))) float ks[2][KT * KS];
+    __shared__ __attribute__((aligned(16))) float vs[2][KT * VS];
+    __shared__ __attribute__((aligned(16))) int kpos_s[2][KT];
+
+    const WorkDesc w = p.work[blockIdx.x];
+    if (w.n_rows <= 0) return;
+
+    const int tid = threadIdx.x;
+    const int wave = tid >> 6, lane = tid & 63, ln = lane & 31, lg = lane >> 5;
+    const int G = 1 << p.gshift;
+    const int page_size = 1 << p.pshift;
+    const int ppt = KT >> p.pshift;
+    const PageDesc *pg = p.pages + w.page_base;
+    const float *kpool = static_cast<const float *>(p.k_pool);
+    const float *vpool = static_cast<const float *>(p.v_pool);
+    const int64_t head_off = (int64_t)w.kv_head * page_size * D;
+
+    // rotated Q: qf[g] = Q'[m][8g + 4lg .. +3]
+    floatx4 qf[NQ];
+    int rpos;
+    {
+        const int m = wave * 32 + ln;
+        const int ti = m >> p.gshift;
+        const bool valid = ti < w.n_rows;
+        const int row = w.row0 + (valid ? ti : 0);
+        const int qh = w.kv_head * G + (m & (G - 1));
+        const int rp = valid ? p.row_pos[row] : -1;
+        rpos = rp;
+        const float *qrow = static_cast<const float *>(p.q) + ((int64_t)row * p.hq + qh) * D;
+        const float *cs = p.rope + (int64_t)(valid ? rp : 0) * D;
+#pragma unroll
+        for (int g = 0; g < NQ / 2; ++g) {
+            const int e0 = 8 * g + 4 * lg;
+            floatx4 lo = {0, 0, 0, 0}, hi = {0, 0, 0, 0};
+            if (valid) {
+                lo = *reinterpret_cast<const floatx4 *>(qrow + e0);
+                hi = *reinterpret_cast<const floatx4 *>(qrow + D / 2 + e0);
+            }
+            const floatx4 c = *reinterpret_cast<const floatx4 *>(cs + e0);
+            const floatx4 sn = *reinterpret_cast<const floatx4 *>(cs + D / 2 + e0);
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                qf[g][j] = fmaf(lo[j], c[j], -hi[j] * sn[j]);
+                qf[g + NQ / 2][j] = fmaf(hi[j], c[j], lo[j] * sn[j]);
+            }
+        }
+    }
+
+    floatx4 k_lo[NKP], k_hi[NKP], k_c[NKP], k_s[NKP];
+    floatx4 v_r[NV];
+    int kp_next = kNeverAttended;
+
+    auto load_tile = [&](int t) {
+        const int lp0 = w.page_begin + t * ppt;
+#pragma unroll
+        for (int u = 0; u < NKP; ++u) {
+            const int pi = tid + kThreads * u;
+            const int key = pi / (D / 8), c = pi % (D / 8);
+            const int lp = lp0 + (key >> p.pshift), slot = key & (page_size - 1);
+            bool ok = false;
+            int pos = 0;
+            int64_t base = 0;
+            if (lp < w.page_end) {
+                const PageDesc pd = pg[lp];
+                if (slot < pd.valid) {
+                    ok = true;
+                    pos = pd.pos0 + slot;
+                    base = (int64_t)pd.phys * p.page_elems + head_off + (int64_t)slot * D;
+                }
+            }
+            k_lo[u] = ok ? *reinterpret_cast<const floatx4 *>(kpool + base + 4 * c) : floatx4{0, 0, 0, 0};
+            k_hi[u] = ok ? *reinterpret_cast<const floatx4 *>(kpool + base + D / 2 + 4 * c) : floatx4{0, 0, 0, 0};
+            const float *cs = p.rope + (int64_t)pos * D + 4 * c;
+            k_c[u] = *reinterpret_cast<const floatx4 *>(cs);
+            k_s[u] = *reinterpret_cast<const floatx4 *>(cs + D / 2);
+        }
+#pragma unroll
+        for (int u = 0; u < NV; ++u) {
+            const int pi = tid + kThreads * u;
+            const int key = pi / (D / 4), c = pi % (D / 4);
+            const int lp = lp0 + (key >> p.pshift), slot = key & (page_size - 1);
+            floatx4 v = {0, 0, 0, 0};
+            if (lp < w.page_end) {
+                const PageDesc pd = pg[lp];
+                if (slot < pd.valid)
+                    v = *reinterpret_cast<const floatx4 *>(vpool + (int64_t)pd.phys * p.page_elems + head_off +
+                                                           (int64_t)slot * D + 4 * c);
+            }
+            v_r[u] = v;
+        }
+        if (tid < KT) {
+            const int lp = lp0 + (tid >> p.pshift), slot = tid & (page_size - 1);
+            int kp = kNeverAttended;
+            if (lp < w.page_end) {
+                const PageDesc pd = pg[lp];
+                if (slot < pd.valid) kp = pd.pos0 + slot;
+            }
+            kp_next = kp;
+        }
+    };
+
+    auto store_tile = [&](int buf) {
+#pragma unroll
+        for (int u = 0; u < NKP; ++u) {
+            const int pi = tid + kThreads * u;
+            const int key = pi / (D / 8), c = pi % (D / 8);
+            floatx4 olo, ohi;
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                olo[j] = fmaf(k_lo[u][j], k_c[u][j], -k_hi[u][j] * k_s[u][j]);
+                ohi[j] = fmaf(k_hi[u][j], k_c[u][j], k_lo[u][j] * k_s[u][j]);
+            }
+            *reinterpret_cast<floatx4 *>(&ks[buf][key * KS + 4 * c]) = olo;
+            *reinterpret_cast<floatx4 *>(&ks[buf][key * KS + D / 2 + 4 * c]) = ohi;
+        }
+#pragma unroll
+        for (int u = 0; u < NV; ++u) {
+            const int pi = tid + kThreads * u;
+            const int key = pi / (D / 4), c = pi % (D / 4);
+            *reinterpret_cast<floatx4 *>(&vs[buf][key * VS + 4 * c]) = v_r[u];
+        }
+        if (tid < KT) kpos_s[buf][tid] = kp_next;
+    };
+
+    floatx16 oacc[NDB];
+#pragma unroll
+    for (int db = 0; db < NDB; ++db)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) oacc[db][r] = 0.0f;
+    float mrow = kInitMax, lrow = 0.0f;
+
+    const int ntiles = (w.page_end - w.page_begin + ppt - 1) / ppt;
+    load_tile(0);
+    store_tile(0);
+    __syncthreads();
+
+    for (int t = 0; t < ntiles; ++t) {
+        const int buf = t & 1;
+        const bool more = t + 1 < ntiles;
+        if (more) load_tile(t + 1);
+        const bool need_mask = tile_needs_mask(pg, w, w.page_begin + t * ppt, ppt, page_size);
+
+        floatx16 sacc[2];
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb) {
+#pragma unroll
+            for (int r = 0; r < 16; ++r) sacc[kb][r] = 0.0f;
+#pragma unroll
+            for (int g = 0; g < NQ; ++g) {
+                const floatx4 a = *reinterpret_cast<const floatx4 *>(&ks[buf][(kb * 32 + ln) * KS + 8 * g + 4 * lg]);
+#pragma unroll
+                for (int j = 0; j < 4; ++j)
+                    sacc[kb] = __builtin_amdgcn_mfma_f32_32x32x2f32(a[j], qf[g][j], sacc[kb], 0, 0, 0);
+            }
+        }
+        if (need_mask) {
+#pragma unroll
+            for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const i32x4 kp4 = *reinterpret_cast<const i32x4 *>(&kpos_s[buf][kb * 32 + 8 * i + 4 * lg]);
+#pragma unroll
+                    for (int j = 0; j < 4; ++j)
+                        if (kp4[j] > rpos) sacc[kb][4 * i + j] = -INFINITY;
+                }
+        }
+        float mx = sacc[0][0];
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sacc[kb][r]);
+        mx = fmaxf(mx, __shfl_xor(mx, 32));
+        const bool upd = (mx - mrow) * p.scale_log2 > kRescaleLog2;
+        if (__any(upd)) {
+            const float mnew = upd ? mx : mrow;
+            const float alpha = exp2f((mrow - mnew) * p.scale_log2);
+            lrow *= alpha;
+#pragma unroll
+            for (int db = 0; db < NDB; ++db)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) oacc[db][r] *= alpha;
+            mrow = mnew;
+        }
+        const float msc = mrow * p.scale_log2;
+        float lsum = 0.0f;
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                const float e = exp2f(fmaf(sacc[kb][r], p.scale_log2, -msc));
+                sacc[kb][r] = e;
+                lsum += e;
+            }
+        lrow += lsum;
+
+#pragma unroll
+        for (int db = 0; db < NDB; ++db)
+#pragma unroll
+            for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+                for (int s = 0; s < 16; ++s) {
+                    const int key = kb * 32 + 8 * (s >> 2) + 4 * lg + (s & 3);
+                    const float a = vs[buf][key * VS + db * 32 + ln];
+                    oacc[db] = __builtin_amdgcn_mfma_f32_32x32x2f32(a, sacc[kb][s], oacc[db], 0, 0, 0);
+                }
+
+        if (more) store_tile(buf ^ 1);
+        __syncthreads();
+    }
+
+    {
+        const int m = wave * 32 + ln;
+        const int ti = m >> p.gshift;
+        const float lt = lrow + __shfl_xor(lrow, 32);
+        const float inv = lt > 0.0f ? 1.0f / lt : 0.0f;
+        const float lse_v = lt > 0.0f ? mrow * p.scale + logf(lt) : -INFINITY;
+        if (ti < w.n_rows) {
+            const int row = w.row0 + ti;
+            const int qh = w.kv_head * G + (m & (G - 1));
+            float *dst = w.partial < 0 ? static_cast<float *>(p.out) + ((int64_t)row * p.hq + qh) * D
+                                       : p.part_o + ((int64_t)w.partial * TQ + m) * D;
+#pragma unroll
+            for (int db = 0; db < NDB; ++db)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const int d0 = db * 32 + 8 * i + 4 * lg;
+                    floatx4 v = {oacc[db][4 * i] * inv, oacc[db][4 * i + 1] * inv, oacc[db][4 * i + 2] * inv,
+                                 oacc[db][4 * i + 3] * inv};
+                    *reinterpret_cast<floatx4 *>(dst + d0) = v;
+                }
+            if (lg == 0) {
+                if (w.partial < 0) {
+                    if (p.lse) p.lse[(int64_t)row * p.hq + qh] = lse_v;
+                } else {
+                    p.part_lse[(int64_t)w.partial * TQ + m] = lse_v;
+                }
+            }
+        }
+    }
+}
+
+// ---------------------------------------------------------------------------------------------
+// Combine the splits of one (row tile, KV head): o = sum_s e^{lse_s - L} o_s / sum_s e^{lse_s - L}.
+template <typename T, int D>
+__global__ __launch_bounds__(kThreads) void link_merge(const MergeDesc *merge, const float *part_o,
+                                                       const float *part_lse, T *out, float *lse, int hq,
+                                                       int gshift, int tq) {
+    const MergeDesc md = merge[blockIdx.x];
+    const int G = 1 << gshift;
+    const int mrows = md.n_rows << gshift;
+    for (int idx = threadIdx.x; idx < mrows * (D / 4); idx += kThreads) {
+        const int m = idx / (D / 4), d4 = idx % (D / 4);
+        float L = -INFINITY;
+        for (int s = 0; s < md.n_split; ++s) L = fmaxf(L, part_lse[(int64_t)(md.slot0 + s) * tq + m]);
+        floatx4 acc = {0, 0, 0, 0};
+        float wsum = 0.0f;
+        for (int s = 0; s < md.n_split; ++s) {
+            const float ls = part_lse[(int64_t)(md.slot0 + s) * tq + m];
+            const float wgt = ls == -INFINITY ? 0.0f : expf(ls - L);
+            const floatx4 o = *reinterpret_cast<const floatx4 *>(part_o + ((int64_t)(md.slot0 + s) * tq + m) * D + 4 * d4);
+            acc += wgt * o;
+            wsum += wgt;
+        }
+        const float inv = wsum > 0.0f ? 1.0f / wsum : 0.0f;
+        const int row = md.row0 + (m >> gshift);
+        const int qh = md.kv_head * G + (m & (G - 1));
+        T *dst = out + ((int64_t)row * hq + qh) * D + 4 * d4;
+        if constexpr (sizeof(T) == 2) {
+            u32x2 v;
+            v[0] = pack_bf16(acc[0] * inv, acc[1] * inv);
+            v[1] = pack_bf16(acc[2] * inv, acc[3] * inv);
+            *reinterpret_cast<u32x2 *>(dst) = v;
+        } else {
+            *reinterpret_cast<floatx4 *>(dst) = acc * inv;
+        }
+        if (lse && d4 == 0) lse[(int64_t)row * hq + qh] = wsum > 0.0f ? L + logf(wsum) : -INFINITY;
+    }
+}
+
+// ---------------------------------------------------------------------------------------------
+// Page writers. One work group per (page, KV head); each thread moves 16-byte pieces.
+__global__ __launch_bounds__(kThreads) void store_fill(FillPages pages, uint8_t *k_pool, uint8_t *v_pool,
+                                                       const uint8_t *k, const uint8_t *v, int hkv,
+                                                       int page_size, int row_bytes, int64_t page_bytes) {
+    const int i = blockIdx.x, h = blockIdx.y;
+    const int page = pages.ids[i];
+    const int tok0 = pages.first_token + i * page_size;
+    const int pieces_per_row = row_bytes / 16;
+    const int64_t dst0 = (int64_t)page * page_bytes + (int64_t)h * page_size * row_bytes;
+    for (int c = threadIdx.x; c < page_size * pieces_per_row; c += kThreads) {
+        const int slot = c / pieces_per_row, piece = c % pieces_per_row;
+        const int tok = tok0 + slot;
+        u32x4 a = {0, 0, 0, 0}, b = {0, 0, 0, 0};
+        if (tok < pages.n_tokens) {
+            const int64_t src = ((int64_t)tok * hkv + h) * row_bytes + piece * 16;
+            a = *reinterpret_cast<const u32x4 *>(k + src);
+            b = *reinterpret_cast<const u32x4 *>(v + src);
+        }
+        const int64_t dst = dst0 + (int64_t)slot * row_bytes + piece * 16;
+        *reinterpret_cast<u32x4 *>(k_pool + dst) = a;
+        *reinterpret_cast<u32x4 *>(v_pool + dst) = b;
+    }
+}
+
+__global__ __launch_bounds__(kThreads) void link_scatter(const ScatterDesc *table, uint8_t *k_pool, uint8_t *v_pool,
+                                                         const uint8_t *k_new, const uint8_t *v_new, int hkv,
+                                                         int page_size, int row_bytes, int64_t page_bytes) {
+    const ScatterDesc sd = table[blockIdx.x];
+    const int h = blockIdx.y;
+    const int pieces_per_row = row_bytes / 16;
+    const int64_t head_bytes = (int64_t)h * page_size * row_bytes;
+    const int64_t dst0 = (int64_t)sd.dst * page_bytes + head_bytes;
+    for (int c = threadIdx.x; c < page_size * pieces_per_row; c += kThreads) {
+        const int slot = c / pieces_per_row, piece = c % pieces_per_row;
+        u32x4 a = {0, 0, 0, 0}, b = {0, 0, 0, 0};
+        if (slot < sd.n_new) {
+            const int64_t src = ((int64_t)(sd.row0 + slot) * hkv + h) * row_bytes + piece * 16;
+            a = *reinterpret_cast<const u32x4 *>(k_new + src);
+            b = *reinterpret_cast<const u32x4 *>(v_new + src);
+        } else if (slot < sd.n_valid) {
+            const int64_t src = (int64_t)sd.src * page_bytes + head_bytes + (int64_t)slot * row_bytes + piece * 16;
+            a = *reinterpret_cast<const u32x4 *>(k_pool + src);
+            b = *reinterpret_cast<const u32x4 *>(v_pool + src);
+        }
+        const int64_t dst = dst0 + (int64_t)slot * row_bytes + piece * 16;
+        *reinterpret_cast<u32x4 *>(k_pool + dst) = a;
+        *reinterpret_cast<u32x4 *>(v_pool + dst) = b;
+    }
+}
+
+int log2_exact(int x) {
+    int s = 0;
+    while ((1 << s) < x) ++s;
+    return s;
+}
+
+}  // namespace
+
+hipError_t launch_store_fill(const LayerShape &s, void *k_pool, void *v_pool, const void *k, const void *v,
+                             const FillPages &pages, hipStream_t stream) {
+    if (pages.count <= 0) return hipSuccess;
+    const int elem = s.dtype == 0 ? 2 : 4;
+    dim3 grid(pages.count, s.hkv);
+    hipLaunchKernelGGL(store_fill, grid, dim3(kThreads), 0, stream, pages, static_cast<uint8_t *>(k_pool),
+                       static_cast<uint8_t *>(v_pool), static_cast<const uint8_t *>(k),
+                       static_cast<const uint8_t *>(v), s.hkv, s.page_size, s.d * elem, s.page_elems * elem);
+    return hipGetLastError();
+}
+
+hipError_t launch_scatter(const LayerShape &s, void *k_pool, void *v_pool, const void *k_new, const void *v_new,
+                          const ScatterDesc *table, int n, hipStream_t stream) {
+    if (n <= 0) return hipSuccess;
+    const int elem = s.dtype == 0 ? 2 : 4;
+    dim3 grid(n, s.hkv);
+    hipLaunchKernelGGL(link_scatter, grid, dim3(kThreads), 0, stream, table, static_cast<uint8_t *>(k_pool),
+                       static_cast<uint8_t *>(v_pool), static_cast<const uint8_t *>(k_new),
+                       static_cast<const uint8_t *>(v_new), s.hkv, s.page_size, s.d * elem, s.page_elems * elem);
+    return hipGetLastError();
+}
+
+hipError_t launch_attention(const LayerShape &s, const void *q, const void *k_pool, const void *v_pool,
+                            const float *rope, const AttnTables &t, void *out, float *lse, hipStream_t stream) {
+    if (t.n_work <= 0) return hipSuccess;
+    AttnParams p;
+    p.q = q;
+    p.k_pool = k_pool;
+    p.v_pool = v_pool;
+    p.rope = rope;
+    p.pages = t.pages;
+    p.row_pos = t.row_pos;
+    p.work = t.work;
+    p.out = out;
+    p.lse = lse;
+    p.part_o = t.part_o;
+    p.part_lse = t.part_lse;
+    p.hq = s.hq;
+    p.hkv = s.hkv;
+    p.gshift = log2_exact(s.hq / s.hkv);
+    p.pshift = log2_exact(s.page_size);
+    p.page_elems = s.page_elems;
+    p.scale = 1.0f / sqrtf((float)s.d);
+    p.scale_log2 = 1.4426950408889634f / sqrtf((float)s.d);
+    dim3 grid(t.n_work);
+    if (s.dtype == 0) {
+        if (s.d == 128)
+            hipLaunchKernelGGL((link_attention_bf16<128, kBf16Waves, kBf16Blocks>), grid, dim3(kBf16Waves * 64), 0,
+                               stream, p);
+        else
+            hipLaunchKernelGGL((link_attention_bf16<64, kBf16Waves, kBf16Blocks>), grid, dim3(kBf16Waves * 64), 0,
+                               stream, p);
+    } else {
+        if (s.d == 128) hipLaunchKernelGGL(link_attention_f32<128>, grid, dim3(kThreads), 0, stream, p);
+        else hipLaunchKernelGGL(link_attention_f32<64>, grid, dim3(kThreads), 0, stream, p);
+    }
+    return hipGetLastError();
+}
+
+hipError_t launch_merge(const LayerShape &s, const AttnTables &t, void *out, float *lse, hipStream_t stream) {
+    if (t.n_merge <= 0) return hipSuccess;
+    const int gshift = log2_exact(s.hq / s.hkv);
+    const int tq = tile_qrows(s.dtype);
+    dim3 grid(t.n_merge);
+    if (s.dtype == 0) {
+        typedef uint16_t T;
+        if (s.d == 128)
+            hipLaunchKernelGGL((link_merge<T, 128>), grid, dim3(kThreads), 0, stream, t.merge, t.part_o, t.part_lse,
+                               static_cast<T *>(out), lse, s.hq, gshift, tq);
+        else
+            hipLaunchKernelGGL((link_merge<T, 64>), grid, dim3(kThreads), 0, stream, t.merge, t.part_o, t.part_lse,
+                               static_cast<T *>(out), lse, s.hq, gshift, tq);
+    } else {
+        if (s.d == 128)
+            hipLaunchKernelGGL((link_merge<float, 128>), grid, dim3(kThreads), 0, stream, t.merge, t.part_o,
+                               t.part_lse, static_cast<float *>(out), lse, s.hq, gshift, tq);
+        else
+            hipLaunchKernelGGL((link_merge<float, 64>), grid, dim3(kThreads), 0, stream, t.merge, t.part_o,
+                               t.part_lse, static_cast<float *>(out), lse, s.hq, gshift, tq);
+    }
+    return hipGetLastError();
+}
+
+}  // namespace piclink

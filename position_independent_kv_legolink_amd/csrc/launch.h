@@ -1,0 +1,49 @@
+// Host-side launchers of the HIP kernels (kernels.hip). Internal to the library.
+#pragma once
+
+#include <hip/hip_runtime_api.h>
+#include <stdint.h>
+
+#include "layout.h"
+
+namespace piclink {
+
+struct LayerShape {
+    int hq, hkv, d, page_size, dtype;
+    int64_t page_elems;   // elements of one page in one pool: Hkv * page_size * d
+};
+
+constexpr int kMaxFillPages = 480;
+
+struct FillPages {
+    int32_t count;
+    int32_t first_token;   // token index of slot 0 of ids[0] within the chunk
+    int32_t n_tokens;      // tokens of the whole chunk
+    int32_t ids[kMaxFillPages];
+};
+
+// Copy one chunk's [n][Hkv][d] K and V into its pages ([Hkv][page][d] each), zeroing padding.
+hipError_t launch_store_fill(const LayerShape &s, void *k_pool, void *v_pool, const void *k, const void *v,
+                             const FillPages &pages, hipStream_t stream);
+
+// Scatter kernel over `n` private pages described in `table` (device).
+hipError_t launch_scatter(const LayerShape &s, void *k_pool, void *v_pool, const void *k_new, const void *v_new,
+                          const ScatterDesc *table, int n, hipStream_t stream);
+
+struct AttnTables {
+    const PageDesc *pages;
+    const int32_t *row_pos;
+    const WorkDesc *work;
+    int n_work;
+    const MergeDesc *merge;
+    int n_merge;
+    float *part_o;
+    float *part_lse;
+};
+
+hipError_t launch_attention(const LayerShape &s, const void *q, const void *k_pool, const void *v_pool,
+                            const float *rope, const AttnTables &t, void *out, float *lse, hipStream_t stream);
+
+hipError_t launch_merge(const LayerShape &s, const AttnTables &t, void *out, float *lse, hipStream_t stream);
+
+}  // namespace piclink

@@ -1,0 +1,64 @@
+// Device-side plan tables shared by the host planner and the HIP kernels.
+// Every struct is plain int32 data, uploaded once per plan into the caller's
+// workspace and read by the kernels of one link call.
+#pragma once
+
+#include <stdint.h>
+
+namespace piclink {
+
+// One logical page of a request: where it lives and which positions it holds.
+struct PageDesc {
+    int32_t phys;    // physical page id in the pools
+    int32_t pos0;    // absolute position of slot 0
+    int32_t valid;   // slots [0, valid) hold tokens, the rest are padding
+    int32_t pad;
+};
+
+// One private page written by the scatter kernel before attention:
+// slots [0, n_new) take new rows row0.., slots [n_new, n_valid) are copied
+// from page `src` (copy-on-write, src >= 0), slots [n_valid, page) are zeroed.
+struct ScatterDesc {
+    int32_t dst;
+    int32_t src;
+    int32_t n_new;
+    int32_t row0;
+    int32_t n_valid;
+    int32_t pad0, pad1, pad2;
+};
+
+// One attention work item: a tile of consecutive selected rows of one request
+// (all query heads of one KV head) over the logical pages [page_begin,
+// page_end) of that request.
+struct WorkDesc {
+    int32_t page_base;   // index of the request's logical page 0 in the PageDesc table
+    int32_t page_begin;
+    int32_t page_end;
+    int32_t row0;        // first selected row (global index)
+    int32_t n_rows;      // selected rows in the tile; 0 = empty slot, exit
+    int32_t kv_head;
+    int32_t partial;     // -1: final output; else partial-result slot of this split
+    int32_t rpos_min;    // position of the tile's first row
+};
+
+// Combine the partial results of the splits of one (row tile, KV head).
+struct MergeDesc {
+    int32_t row0;
+    int32_t n_rows;
+    int32_t kv_head;
+    int32_t n_split;
+    int32_t slot0;
+    int32_t pad0, pad1, pad2;
+};
+
+constexpr int kKeysPerTile = 64;   // keys staged in LDS per attention iteration
+constexpr int kThreads = 256;      // page writers, merge and the fp32 attention kernel
+
+// bf16 attention work group: kBf16Waves waves of kBf16Blocks 32-row MFMA blocks each.
+constexpr int kBf16Waves = 8;
+constexpr int kBf16Blocks = 1;
+
+// (row, head) pairs handled by one attention work group.
+constexpr int tile_qrows(int dtype) { return dtype == 0 ? kBf16Waves * kBf16Blocks * 32 : 128; }
+
+}  // namespace piclink

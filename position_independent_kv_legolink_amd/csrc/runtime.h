@@ -1,0 +1,83 @@
+// Host-side state behind the C ABI: the paged chunk store and link plans.
+#pragma once
+
+#include <stdint.h>
+
+#include <set>
+#include <string>
+#include <unordered_map>
+#include <vector>
+
+#include "../../include/piclink.h"
+#include "launch.h"
+#include "layout.h"
+
+namespace piclink {
+
+// Status + message carried back to the C ABI.
+struct Error {
+    pic_status status;
+    std::string message;
+};
+
+[[noreturn]] void fail(pic_status status, const std::string &message);
+
+struct Chunk {
+    int32_t n_tokens = 0;
+    std::vector<int32_t> pages;
+};
+
+struct ProfileMarks {
+    hipEvent_t ev[4];   // before scatter, before attention, before merge, after merge
+};
+
+}  // namespace piclink
+
+struct pic_store {
+    pic_store_config cfg{};
+    piclink::LayerShape shape{};
+    void *k_pool = nullptr;
+    void *v_pool = nullptr;
+    float *rope = nullptr;
+    std::vector<int32_t> refs;          // references per physical page (chunk table + live plans)
+    std::set<int32_t> free_pages;       // lowest id first
+    std::unordered_map<uint64_t, piclink::Chunk> chunks;
+    int32_t live_plans = 0;
+    int32_t num_cus = 256;              // compute units used by the work-list split policy
+    bool profiling = false;
+    int32_t profiled_calls = 0;
+    double profiled_ms[3] = {0, 0, 0};
+    std::vector<piclink::ProfileMarks> pending;
+    std::vector<hipEvent_t> spare_events;
+};
+
+struct pic_plan {
+    pic_store *owner = nullptr;
+    int32_t n_requests = 0;
+    std::vector<int32_t> row_pos, row_dst, cu_rows, cu_pages;
+    std::vector<piclink::PageDesc> pages;
+    std::vector<piclink::ScatterDesc> scatter;
+    std::vector<int32_t> cow_src, cow_dst;
+    std::vector<piclink::WorkDesc> work;
+    std::vector<piclink::MergeDesc> merge;
+    std::vector<int32_t> page_refs;     // every physical page this plan holds a reference on
+    int32_t n_slots = 0;
+    int64_t n_split_items = 0;
+    // workspace layout (byte offsets)
+    int64_t off_pages = 0, off_row_pos = 0, off_scatter = 0, off_work = 0, off_merge = 0;
+    int64_t off_part_o = 0, off_part_lse = 0, table_bytes = 0, workspace_bytes = 0;
+    void *uploaded_to = nullptr;
+};
+
+namespace piclink {
+
+void store_check_config(const pic_store_config &cfg);
+int32_t store_alloc_page(pic_store *s);
+void store_ref(pic_store *s, int32_t page);
+void store_unref(pic_store *s, int32_t page);
+const Chunk &store_find(const pic_store *s, uint64_t id);
+
+pic_plan *build_plan(pic_store *s, const pic_request *reqs, int32_t n_reqs, const pic_link_options &opts);
+void release_plan(pic_store *s, pic_plan *plan);
+
+}  // namespace piclink

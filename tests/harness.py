@@ -1,0 +1,154 @@
+"""Shared test helpers: run a link workload through the library and through the oracle.
+
+Tests may use both sides; the product package never imports this module.
+"""
+from __future__ import annotations
+
+import numpy as np
+
+import position_independent_kv_legolink_amd as pic
+from oracle import link as olink
+from oracle import plan as oplan
+from workloads import gen
+
+
+# ------------------------------------------------------------------ plans
+def oracle_segments(cfg, chunk_ids, request, *, pos_offset=0, recompute_all=False, chunk_lens=None,
+                    prefix_len=None, suffix_len=None, k=None, block_level=None):
+    plen = cfg.prefix_len if prefix_len is None else prefix_len
+    return oplan.link_segments(prefix_id=cfg.prefix_id(request) if plen else None, prefix_len=plen,
+                               chunk_ids=list(chunk_ids),
+                               chunk_lens=chunk_lens if chunk_lens is not None else [cfg.chunk_len] * len(chunk_ids),
+                               suffix_len=cfg.suffix_len if suffix_len is None else suffix_len,
+                               k=cfg.k if k is None else k,
+                               block_level=cfg.block_level if block_level is None else block_level,
+                               page_size=cfg.page_size, pos_offset=pos_offset, recompute_all=recompute_all)
+
+
+def compare_plan(store, plan, seg_lists, page_size):
+    """Check the library plan against the oracle planner, bit for bit.
+
+    Physical page ids are the allocator's choice, so shared pages are compared
+    by resolving them to (chunk id, page number) and private pages must be
+    fresh, distinct pages outside every stored chunk.
+    """
+    B = page_size
+    ex = plan.export()
+    chunk_page_cache = {}
+
+    def chunk_pages(cid):
+        if cid not in chunk_page_cache:
+            chunk_page_cache[cid] = store.chunk_pages(cid)[0]
+        return chunk_page_cache[cid]
+
+    assert ex["cu_rows"][0] == 0 and ex["cu_pages"][0] == 0
+    stored = set()
+    for segs in seg_lists:
+        for s in segs:
+            if s.chunk_id is not None:
+                stored.update(int(p) for p in chunk_pages(s.chunk_id))
+    private_seen = set()
+    cow_pairs = set(zip(ex["cow_src"].tolist(), ex["cow_dst"].tolist()))
+    cow_expected = set()
+    for r, segs in enumerate(seg_lists):
+        r0, r1 = ex["cu_rows"][r], ex["cu_rows"][r + 1]
+        p0, p1 = ex["cu_pages"][r], ex["cu_pages"][r + 1]
+        sel = oplan.selected_positions(segs)
+        assert ex["row_pos"][r0:r1].tolist() == sel
+        pages = oplan.logical_pages(segs, B)
+        assert p1 - p0 == len(pages)
+        assert ex["pos_map"][p0 * B:p1 * B].tolist() == oplan.position_map(pages, B)
+        bt = ex["block_table"][p0:p1]
+        for i, pg in enumerate(pages):
+            phys = int(bt[i])
+            if pg.private:
+                assert phys not in stored, "private page aliases a stored page"
+                assert phys not in private_seen, "private page used twice"
+                private_seen.add(phys)
+                if pg.cow:
+                    cid, q = pg.source
+                    cow_expected.add((int(chunk_pages(cid)[q]), phys))
+            else:
+                cid, q = pg.source
+                assert phys == int(chunk_pages(cid)[q])
+        slots = oplan.row_slots(segs, B)
+        assert ex["row_dst"][r0:r1].tolist() == [int(bt[lp]) * B + s for lp, s in slots]
+    assert cow_pairs == cow_expected
+    assert plan.sizes["private_pages"] == len(private_seen)
+    return ex
+
+
+# ---------------------------------------------------------------- workloads
+class Workload:
+    """A config's store contents and requests, generated from its seeds."""
+
+    def __init__(self, cfg, requests=None, n_requests=None):
+        self.cfg = cfg
+        draws = gen.request_chunks(cfg)
+        if n_requests is not None:
+            draws = draws[:n_requests]
+        self.requests = requests if requests is not None else list(range(len(draws)))
+        self.draws = [draws[r] for r in self.requests]
+        self.chunk_ids = sorted({c for ids in self.draws for c in ids})
+
+    def cached(self):
+        out = {}
+        for c in self.chunk_ids:
+            out[c] = gen.chunk_kv(self.cfg, c)
+        if self.cfg.prefix_len:
+            for r in self.requests:
+                out[self.cfg.prefix_id(r)] = gen.prefix_kv(self.cfg, r)
+        return out
+
+    def segments(self, **kw):
+        return [oracle_segments(self.cfg, ids, r, **kw) for r, ids in zip(self.requests, self.draws)]
+
+    def link_requests(self):
+        return [pic.LinkRequest(chunk_ids=ids, suffix_len=self.cfg.suffix_len,
+                                prefix_id=self.cfg.prefix_id(r) if self.cfg.prefix_len else None)
+                for r, ids in zip(self.requests, self.draws)]
+
+    def new_rows(self, seg_lists):
+        rows = []
+        for r, segs in zip(self.requests, seg_lists):
+            rows.append(gen.new_rows(self.cfg, r, len(oplan.selected_positions(segs))))
+        return rows
+
+
+def gpu_store(cfg, cached: dict, *, num_pages, max_position, device="cuda"):
+    import torch
+    store = pic.Store(num_q_heads=cfg.num_q_heads, num_kv_heads=cfg.num_kv_heads, head_dim=cfg.head_dim,
+                      page_size=cfg.page_size, num_pages=num_pages, dtype=cfg.dtype,
+                      rope_theta=cfg.rope_theta, max_position=max_position, device=device)
+    tdt = torch.bfloat16 if cfg.dtype == "bf16" else torch.float32
+    for cid, (k, v) in cached.items():
+        store.store_chunk(cid, torch.from_numpy(k).to(device=device, dtype=tdt).contiguous(),
+                          torch.from_numpy(v).to(device=device, dtype=tdt).contiguous())
+    return store
+
+
+def oracle_outputs(seg_lists, cached, rows, theta, sample=None):
+    """fp64 oracle outputs per request; ``sample`` maps request index -> row indices."""
+    outs = []
+    for i, (segs, (q, k, v)) in enumerate(zip(seg_lists, rows)):
+        sel = None if sample is None else sample.get(i)
+        outs.append(olink.link_attention(segs, cached, q, k, v, theta, rows=sel))
+    return outs
+
+
+def assert_close(got, want, atol, rtol, what=""):
+    got = np.asarray(got, dtype=np.float64)
+    want = np.asarray(want, dtype=np.float64)
+    assert got.shape == want.shape, (got.shape, want.shape)
+    err = np.abs(got - want)
+    bound = atol + rtol * np.abs(want)
+    bad = ~(err <= bound)
+    if bad.any():
+        idx = np.argwhere(bad)[:5]
+        raise AssertionError(f"{what}: {int(bad.sum())} of {bad.size} elements out of tolerance "
+                             f"(max abs err {err.max():.3e}); first at {idx.tolist()}: got "
+                             f"{got[tuple(idx[0])]}, want {want[tuple(idx[0])]}")
+    return float(err.max())
+
+
+TOLERANCE = {"bf16": (2e-2, 1e-2), "f32": (1e-5, 1e-5)}

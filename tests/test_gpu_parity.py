@@ -1,0 +1,264 @@
+"""GPU parity of the link step against the fp64 oracle (needs an MI355X).
+
+Every case runs store_chunk -> link_plan -> plan upload -> link_attend through
+the C ABI and compares the outputs with the oracle element by element:
+bf16 within |gpu - oracle| <= 2e-2 + 1e-2 |oracle|, fp32 within 1e-5 + 1e-5
+|oracle|. Small cases compare every row; the full-size workloads compare
+sampled rows (first, last, longest and seeded random ones), which the oracle
+computes one by one over the complete merged cache.
+"""
+from __future__ import annotations
+
+import dataclasses
+import sys
+
+import numpy as np
+import pytest
+
+import position_independent_kv_legolink_amd as pic
+from oracle import plan as oplan
+from tests.harness import (TOLERANCE, Workload, assert_close, compare_plan, gpu_store, oracle_outputs)
+from workloads import CONFIGS, gen
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+
+
+def _say(msg):
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _need_gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    pic.lib()
+
+
+def run_workload(cfg, *, n_requests=None, sample_rows=None, pos_offset=0, split_pages=0, k=None,
+                 recompute_all=False, seed=0, check_plan=True, repeat=1, lse=True, num_pages=None):
+    """Link a config's requests on the GPU; return (gpu outs, oracle outs, extras)."""
+    wl = Workload(cfg, n_requests=n_requests)
+    kk = cfg.k if k is None else k
+    segs = wl.segments(pos_offset=pos_offset, recompute_all=recompute_all, k=kk)
+    cached = wl.cached()
+    B = cfg.page_size
+    private = sum(p.private for s in segs for p in oplan.logical_pages(s, B))
+    stored = sum(-(-v[0].shape[0] // B) for v in cached.values())
+    n_tokens = max(oplan.total_tokens(s) for s in segs)
+    store = gpu_store(cfg, cached, num_pages=num_pages or (stored + private + 8),
+                      max_position=pos_offset + n_tokens + 1)
+    plan = store.link_plan(wl.link_requests(), k=kk, block_level=cfg.block_level, pos_offset=pos_offset,
+                           recompute_all=recompute_all, split_pages=split_pages)
+    if check_plan:
+        compare_plan(store, plan, segs, B)
+    rows = wl.new_rows(segs)
+    tdt = torch.bfloat16 if cfg.dtype == "bf16" else torch.float32
+    q = torch.from_numpy(np.concatenate([r[0] for r in rows])).to("cuda", tdt).contiguous()
+    kn = torch.from_numpy(np.concatenate([r[1] for r in rows])).to("cuda", tdt).contiguous()
+    vn = torch.from_numpy(np.concatenate([r[2] for r in rows])).to("cuda", tdt).contiguous()
+    plan.upload()
+    outs = []
+    lse_t = torch.empty((plan.rows, cfg.num_q_heads), dtype=torch.float32, device="cuda") if lse else None
+    for _ in range(repeat):
+        out = pic.link_attend(store, plan, q, kn, vn, lse=lse_t)
+        torch.cuda.synchronize()
+        outs.append(out.float().cpu().numpy())
+    got_lse = lse_t.cpu().numpy() if lse else None
+    ex = plan.export()
+    sample = None
+    if sample_rows is not None:
+        sample = {}
+        g = np.random.default_rng(seed)
+        for i, s in enumerate(segs):
+            R = len(oplan.selected_positions(s))
+            pick = {0, R - 1, R // 2} | set(int(x) for x in g.integers(0, R, size=max(0, sample_rows - 3)))
+            sample[i] = np.array(sorted(x for x in pick if 0 <= x < R), dtype=np.int64)
+    want = oracle_outputs(segs, cached, rows, cfg.rope_theta, sample=sample)
+    extras = dict(store=store, plan=plan, export=ex, segs=segs, cached=cached, rows=rows, sample=sample,
+                  lse=got_lse, outs=outs)
+    return outs[0], want, extras
+
+
+def check(cfg, got, want, extras, what):
+    atol, rtol = TOLERANCE[cfg.dtype]
+    ex = extras["export"]
+    worst = 0.0
+    for i, (wo, wl) in enumerate(want):
+        r0 = ex["cu_rows"][i]
+        idx = np.arange(wo.shape[0]) if extras["sample"] is None else extras["sample"][i]
+        g = got[r0 + idx]
+        worst = max(worst, assert_close(g, wo, atol, rtol, f"{what} request {i} out"))
+        if extras["lse"] is not None:
+            assert_close(extras["lse"][r0 + idx], wl, atol, rtol, f"{what} request {i} lse")
+    _say(f"{what}: max abs err {worst:.3e}")
+    return worst
+
+
+# ------------------------------------------------------------------ the five workloads
+def test_tiny_fp32_all_rows():
+    cfg = CONFIGS["tiny"]
+    got, want, ex = run_workload(cfg)
+    check(cfg, got, want, ex, "tiny")
+
+
+def test_llama3_k2_all_rows():
+    cfg = CONFIGS["llama3_k2"]
+    got, want, ex = run_workload(cfg)
+    check(cfg, got, want, ex, "llama3_k2")
+
+
+def test_batched_k16_sampled():
+    cfg = CONFIGS["batched_k16"]
+    got, want, ex = run_workload(cfg, sample_rows=24)
+    check(cfg, got, want, ex, "batched_k16")
+
+
+def test_long50k_k32_sampled():
+    cfg = CONFIGS["long50k_k32"]
+    got, want, ex = run_workload(cfg, sample_rows=40, repeat=2)
+    check(cfg, got, want, ex, "long50k_k32")
+    assert np.array_equal(ex["outs"][0], ex["outs"][1]), "run-to-run results differ"
+
+
+def test_block_zipf_sampled():
+    cfg = CONFIGS["block_zipf"]
+    got, want, ex = run_workload(cfg, sample_rows=6)
+    check(cfg, got, want, ex, "block_zipf")
+
+
+# ------------------------------------------------------------------ edge cases
+def small_cfg(**over):
+    base = dict(name="edge", description="edge case", num_q_heads=8, num_kv_heads=2, head_dim=128, dtype="bf16",
+                rope_theta=5e5, page_size=16, k=3, block_level=False, prefix_len=21, chunk_len=70,
+                chunks_per_request=5, suffix_len=37, n_requests=2, pool_size=6, pool_draw="uniform",
+                q_scale=1.0, kv_scale=0.5, seed=77)
+    base.update(over)
+    return CONFIGS["tiny"].__class__(**base)
+
+
+EDGE = {
+    "ragged_bf16": dict(),
+    "ragged_f32": dict(dtype="f32", kv_scale=1.0),
+    "k0_link_half": dict(k=0),
+    "k_beyond_chunk": dict(k=90),
+    "block_page32": dict(block_level=True, page_size=32),
+    "page64_k40": dict(page_size=64, k=40),
+    "no_prefix_no_suffix": dict(prefix_len=0, suffix_len=0, k=5),
+    "suffix_only": dict(chunks_per_request=0, prefix_len=0, suffix_len=300),
+    "d64_bf16_g1": dict(head_dim=64, num_q_heads=4, num_kv_heads=4),
+    "d64_f32_g8": dict(head_dim=64, num_q_heads=8, num_kv_heads=1, dtype="f32", kv_scale=1.0),
+    "g2_many_requests": dict(num_q_heads=4, num_kv_heads=2, n_requests=5, chunk_len=33),
+    "hkv8_xcd_buckets": dict(num_q_heads=32, num_kv_heads=8, chunk_len=140, k=20),
+}
+
+
+@pytest.mark.parametrize("name", list(EDGE))
+def test_edge_cases_all_rows(name):
+    cfg = small_cfg(**EDGE[name])
+    _say(f"edge case {name}")
+    got, want, ex = run_workload(cfg)
+    check(cfg, got, want, ex, name)
+
+
+@pytest.mark.parametrize("split", [-1, 4, 12])
+def test_split_and_merge(split):
+    cfg = small_cfg(chunk_len=300, chunks_per_request=6, k=20, n_requests=2)
+    _say(f"split_pages {split}")
+    got, want, ex = run_workload(cfg, split_pages=split)
+    if split > 0:
+        assert ex["plan"].sizes["split_items"] > 0
+    check(cfg, got, want, ex, f"split {split}")
+
+
+@pytest.mark.parametrize("offset", [1, 4097, 100000])
+def test_position_offset(offset):
+    cfg = small_cfg(chunk_len=64)
+    _say(f"pos_offset {offset}")
+    got, want, ex = run_workload(cfg, pos_offset=offset)
+    check(cfg, got, want, ex, f"offset {offset}")
+
+
+def test_dense_recompute_all():
+    cfg = small_cfg(chunk_len=100, chunks_per_request=3, n_requests=1)
+    got, want, ex = run_workload(cfg, recompute_all=True)
+    assert ex["plan"].sizes["cow_pages"] == 0
+    check(cfg, got, want, ex, "recompute_all")
+
+
+def test_empty_plan_is_a_noop():
+    cfg = small_cfg(prefix_len=0, suffix_len=0, k=0, n_requests=1)
+    wl = Workload(cfg)
+    store = gpu_store(cfg, wl.cached(), num_pages=200, max_position=4096)
+    plan = store.link_plan(wl.link_requests(), k=0)
+    assert plan.rows == 0
+    plan.upload()
+    z = torch.empty((0, cfg.num_q_heads, cfg.head_dim), dtype=torch.bfloat16, device="cuda")
+    zk = torch.empty((0, cfg.num_kv_heads, cfg.head_dim), dtype=torch.bfloat16, device="cuda")
+    out = pic.link_attend(store, plan, z, zk, zk)
+    torch.cuda.synchronize()
+    assert out.shape[0] == 0
+
+
+def test_scatter_writes_private_pages_exactly():
+    """Private pages hold new rows, copied cached rows and zero padding, byte for byte."""
+    cfg = small_cfg(k=3, chunk_len=45)
+    got, want, ex = run_workload(cfg)
+    store, segs, rows, cached = ex["store"], ex["segs"], ex["rows"], ex["cached"]
+    exp_ = ex["export"]
+    B = cfg.page_size
+    kp = store.k_pool.float().cpu().numpy()
+    vp = store.v_pool.float().cpu().numpy()
+    for i, s in enumerate(segs):
+        pages = oplan.logical_pages(s, B)
+        p0 = exp_["cu_pages"][i]
+        qn, kn, vn = rows[i]
+        row_of_seg = np.cumsum([0] + [g.recompute for g in s])
+        for lp, pg in enumerate(pages):
+            if not pg.private:
+                continue
+            seg = s[pg.segment]
+            phys = exp_["block_table"][p0 + lp]
+            want_k = np.zeros((cfg.num_kv_heads, B, cfg.head_dim), np.float32)
+            want_v = np.zeros_like(want_k)
+            for slot in range(pg.valid):
+                j = pg.index * B + slot
+                if j < seg.recompute:
+                    r = row_of_seg[pg.segment] + j
+                    want_k[:, slot], want_v[:, slot] = kn[r], vn[r]
+                else:
+                    want_k[:, slot] = cached[seg.chunk_id][0][j]
+                    want_v[:, slot] = cached[seg.chunk_id][1][j]
+            assert np.array_equal(kp[phys], want_k) and np.array_equal(vp[phys], want_v)
+
+
+def test_page_placement_does_not_change_results():
+    """Permuting the physical pages of every chunk gives bitwise identical output."""
+    cfg = small_cfg(n_requests=1)
+    a, _, ex_a = run_workload(cfg, check_plan=False)
+    # a store with a different physical layout: occupy some pages first
+    wl = Workload(cfg, n_requests=1)
+    cached = wl.cached()
+    store = pic.Store(num_q_heads=cfg.num_q_heads, num_kv_heads=cfg.num_kv_heads, head_dim=cfg.head_dim,
+                      page_size=cfg.page_size, num_pages=400, dtype=cfg.dtype, rope_theta=cfg.rope_theta,
+                      max_position=4096)
+    dummy = torch.zeros((40, cfg.num_kv_heads, cfg.head_dim), dtype=torch.bfloat16, device="cuda")
+    for j in range(7):
+        store.store_chunk(9000 + j, dummy, dummy)
+    for cid in reversed(list(cached)):
+        k, v = cached[cid]
+        store.store_chunk(cid, torch.from_numpy(k).to("cuda", torch.bfloat16).contiguous(),
+                          torch.from_numpy(v).to("cuda", torch.bfloat16).contiguous())
+    for j in range(0, 7, 2):
+        store.release(9000 + j)
+    plan = store.link_plan(wl.link_requests(), k=cfg.k)
+    assert not np.array_equal(plan.export()["block_table"], ex_a["export"]["block_table"])
+    rows = ex_a["rows"]
+    q = torch.from_numpy(rows[0][0]).to("cuda", torch.bfloat16).contiguous()
+    kn = torch.from_numpy(rows[0][1]).to("cuda", torch.bfloat16).contiguous()
+    vn = torch.from_numpy(rows[0][2]).to("cuda", torch.bfloat16).contiguous()
+    plan.upload()
+    b = pic.link_attend(store, plan, q, kn, vn).float().cpu().numpy()
+    assert np.array_equal(a, b)
