@@ -1,0 +1,372 @@
+"""Link-step benchmark on one MI355X.
+
+A step is one pass of the whole link path over one batch: link_plan (host),
+plan upload, copy-on-write scatter, attention, and split merge. The default
+workload is the 50,304-token request (64-token prefix + 98 x 512-token chunks
++ 64-token suffix, LegoLink-32, Llama-3-8B layer shape, bf16). Its chunk KV and
+new rows are seeded synthetic data, resident in HBM before timing starts.
+
+Output: one JSON line with the step throughput (algorithmic TFLOP/s), the
+attention kernel's roofline position (timed live with HIP events on the
+stream it runs on), the dense full-recompute comparator on the same inputs,
+and the fp64 CPU oracle timed on a bounded sample of rows.
+
+    python bench.py [--steps K] [--warmup W] [--workload NAME] [--no-cpu-baseline] [--no-dense]
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "link-step attention TFLOP/s + HBM GB/s (% MI355X peak); link latency @50k tok"
+PEAK_BF16_TFLOPS = 2500.0     # MI355X dense bf16 MFMA
+PEAK_F32_TFLOPS = 157.3       # MI355X fp32
+PEAK_HBM_GBPS = 8000.0        # MI355X HBM3E
+KERNEL_SOURCE = os.path.join(ROOT, "position_independent_kv_legolink_amd", "csrc", "kernels.hip")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "attention_traffic.json")
+
+
+def log(msg):
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def kernel_hash():
+    return hashlib.sha256(open(KERNEL_SOURCE, "rb").read()).hexdigest()[:16]
+
+
+def algorithmic_counts(cfg, export, sizes, n_tokens_per_request):
+    """FLOP (QK^T + PV over unmasked keys) and HBM bytes of one link call."""
+    d, hq, hkv = cfg.head_dim, cfg.num_q_heads, cfg.num_kv_heads
+    elem = 2 if cfg.dtype == "bf16" else 4
+    flop = 0
+    kv_bytes = 0
+    cu = export["cu_rows"]
+    for r in range(len(cu) - 1):
+        pos = export["row_pos"][cu[r]:cu[r + 1]].astype(np.int64)
+        if pos.size == 0:
+            continue
+        first = int(export["pos_map"][export["cu_pages"][r] * cfg.page_size])
+        keys = pos - first + 1                      # tokens at positions <= p
+        flop += int(4 * d * hq * keys.sum())
+        kv_bytes += int(keys.max()) * hkv * d * elem * 2
+    R = sizes["rows"]
+    q_out = 2 * R * hq * d * elem
+    new_kv = 2 * R * hkv * d * elem
+    page_bytes = hkv * cfg.page_size * d * elem
+    private = 2 * sizes["private_pages"] * page_bytes
+    cow = 2 * sizes["cow_pages"] * page_bytes
+    attn_bytes = kv_bytes + q_out
+    total = attn_bytes + new_kv + private + cow
+    return flop, attn_bytes, total
+
+
+class LinkJob:
+    """Store, requests and device tensors of one workload."""
+
+    def __init__(self, cfg, *, dense_pages=0):
+        import torch
+
+        import position_independent_kv_legolink_amd as pic
+        from workloads import gen
+
+        self.cfg = cfg
+        self.pic = pic
+        self.torch = torch
+        draws = gen.request_chunks(cfg)
+        chunk_ids = sorted({c for ids in draws for c in ids})
+        B = cfg.page_size
+        pages = len(chunk_ids) * -(-cfg.chunk_len // B) + len(draws) * (-(-cfg.prefix_len // B))
+        private = len(draws) * (cfg.chunks_per_request * -(-max(cfg.k, B if cfg.block_level else 0) // B)
+                                + -(-cfg.suffix_len // B))
+        self.n_tokens = cfg.prefix_len + cfg.chunks_per_request * cfg.chunk_len + cfg.suffix_len
+        self.store = pic.Store(num_q_heads=cfg.num_q_heads, num_kv_heads=cfg.num_kv_heads, head_dim=cfg.head_dim,
+                               page_size=B, num_pages=pages + private + dense_pages + 64, dtype=cfg.dtype,
+                               rope_theta=cfg.rope_theta, max_position=self.n_tokens + 1)
+        self.tdt = torch.bfloat16 if cfg.dtype == "bf16" else torch.float32
+        t = time.time()
+        for c in chunk_ids:
+            k, v = gen.chunk_kv(cfg, c)
+            self.store.store_chunk(c, self._dev(k), self._dev(v))
+        self.requests = []
+        for r, ids in enumerate(draws):
+            pid = None
+            if cfg.prefix_len:
+                pid = cfg.prefix_id(r)
+                k, v = gen.prefix_kv(cfg, r)
+                self.store.store_chunk(pid, self._dev(k), self._dev(v))
+            self.requests.append(pic.LinkRequest(ids, cfg.suffix_len, pid))
+        torch.cuda.synchronize()
+        log(f"stored {len(chunk_ids)} chunks in {time.time() - t:.1f}s")
+        self.plan_kw = dict(k=cfg.k, block_level=cfg.block_level)
+        plan = self.store.link_plan(self.requests, **self.plan_kw)
+        self.sizes = dict(plan.sizes)
+        self.export = plan.export()
+        cu = self.export["cu_rows"]
+        qs, ks, vs = [], [], []
+        for r in range(len(self.requests)):
+            q, k, v = gen.new_rows(cfg, r, int(cu[r + 1] - cu[r]))
+            qs.append(q), ks.append(k), vs.append(v)
+        self.q = self._dev(np.concatenate(qs))
+        self.k = self._dev(np.concatenate(ks))
+        self.v = self._dev(np.concatenate(vs))
+        self.workspace = torch.empty(self.sizes["workspace_bytes"], dtype=torch.uint8, device="cuda")
+        self.out = torch.empty((self.sizes["rows"], cfg.num_q_heads, cfg.head_dim), dtype=self.tdt, device="cuda")
+        plan.free()
+
+    def _dev(self, a):
+        return self.torch.from_numpy(np.ascontiguousarray(a)).to("cuda", self.tdt).contiguous()
+
+    def step(self):
+        plan = self.store.link_plan(self.requests, **self.plan_kw)
+        plan.upload(self.workspace)
+        self.pic.link_attend(self.store, plan, self.q, self.k, self.v, out=self.out)
+        plan.free()
+
+
+def time_steps(job, steps, warmup):
+    torch = job.torch
+    for _ in range(warmup):
+        job.step()
+    torch.cuda.synchronize()
+    job.store.profile_enable(True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        job.step()
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    prof = job.store.profile_read()
+    job.store.profile_enable(False)
+    return (t1 - t0) * 1e3 / steps, prof
+
+
+def dense_comparator(job, reps=3):
+    """Full recompute of every token (prefix and suffix included) on the same inputs.
+
+    Every token's K/V is the linked cache's (cached chunk rows, with the link's
+    recomputed rows in place), so the dense output at the link's selected rows
+    must equal the link output; the largest difference is reported.
+    """
+    from workloads import gen
+
+    torch, cfg = job.torch, job.cfg
+    plan = job.store.link_plan(job.requests, k=cfg.k, recompute_all=True)
+    sizes, ex = dict(plan.sizes), plan.export()
+    R = sizes["rows"]
+    B = cfg.page_size
+    k_all = torch.empty((R, cfg.num_kv_heads, cfg.head_dim), dtype=job.tdt, device="cuda")
+    v_all = torch.empty_like(k_all)
+    link_rows = []          # dense row index of every link row, in link order
+    lcu = job.export["cu_rows"]
+    at = 0
+    for r, req in enumerate(job.requests):
+        segs = ([("p", req.prefix_id, cfg.prefix_len, 0)] if req.prefix_id is not None else []) + \
+               [("c", c, cfg.chunk_len, min(B, cfg.chunk_len) if cfg.block_level else min(cfg.k, cfg.chunk_len))
+                for c in req.chunk_ids] + ([("s", None, cfg.suffix_len, cfg.suffix_len)] if cfg.suffix_len else [])
+        lr = int(lcu[r])
+        for kind, cid, length, rec in segs:
+            if kind == "s":
+                kk = job.k[lr:lr + rec]
+                vv = job.v[lr:lr + rec]
+            else:
+                ck, cv = gen.prefix_kv(cfg, r) if kind == "p" else gen.chunk_kv(cfg, cid)
+                kk, vv = job._dev(ck), job._dev(cv)
+                kk[:rec] = job.k[lr:lr + rec]
+                vv[:rec] = job.v[lr:lr + rec]
+            k_all[at:at + length] = kk
+            v_all[at:at + length] = vv
+            link_rows.extend(range(at, at + rec))
+            lr += rec
+            at += length
+    assert at == R
+    g = gen.rng(cfg.seed, gen.KIND_Q_ALL, 0)
+    q = job._dev(g.standard_normal((R, cfg.num_q_heads, cfg.head_dim), dtype=np.float32) * cfg.q_scale)
+    idx = torch.tensor(link_rows, dtype=torch.long, device="cuda")
+    q[idx] = job.q
+    ws = torch.empty(sizes["workspace_bytes"], dtype=torch.uint8, device="cuda")
+    out = torch.empty((R, cfg.num_q_heads, cfg.head_dim), dtype=job.tdt, device="cuda")
+    plan.upload(ws)
+    job.pic.link_attend(job.store, plan, q, k_all, v_all, out=out)
+    torch.cuda.synchronize()
+    job.store.profile_enable(True)
+    t0 = time.perf_counter()
+    for _ in range(reps):
+        job.pic.link_attend(job.store, plan, q, k_all, v_all, out=out)
+    torch.cuda.synchronize()
+    wall = (time.perf_counter() - t0) * 1e3 / reps
+    prof = job.store.profile_read()
+    job.store.profile_enable(False)
+    flop, attn_bytes, _ = algorithmic_counts(cfg, ex, sizes, job.n_tokens)
+    plan.free()
+    job.step()
+    torch.cuda.synchronize()
+    diff = float((out[idx].float() - job.out.float()).abs().max())
+    del q, k_all, v_all, ws, out
+    attn_ms = prof["attention_ms"] / max(prof["calls"], 1)
+    return dict(rows=R, gflop=round(flop / 1e9, 1), ms=round(wall, 4), attention_ms=round(attn_ms, 4),
+                attention_tflops=round(flop / attn_ms / 1e9, 2), max_abs_diff_at_link_rows=diff)
+
+
+def cpu_baseline(cfg, target_s):
+    """The fp64 oracle on a bounded, evenly spread sample of the same workload's rows."""
+    from oracle import link as olink
+    from oracle import plan as oplan
+    from workloads import gen
+
+    draws = gen.request_chunks(cfg)
+    segs = oplan.link_segments(prefix_id=cfg.prefix_id(0) if cfg.prefix_len else None, prefix_len=cfg.prefix_len,
+                               chunk_ids=draws[0], chunk_lens=[cfg.chunk_len] * len(draws[0]),
+                               suffix_len=cfg.suffix_len, k=cfg.k, block_level=cfg.block_level,
+                               page_size=cfg.page_size)
+    cached = {c: gen.chunk_kv(cfg, c) for c in set(draws[0])}
+    if cfg.prefix_len:
+        cached[cfg.prefix_id(0)] = gen.prefix_kv(cfg, 0)
+    pos = np.asarray(oplan.selected_positions(segs), dtype=np.int64)
+    R = len(pos)
+    q, k, v = gen.new_rows(cfg, 0, R)
+    cores = int(os.environ.get("OMP_NUM_THREADS", os.cpu_count() or 1))
+    # calibrate on a few rows, then take as many evenly spread rows as fit the time target
+    probe = np.linspace(0, R - 1, 4).astype(np.int64)
+    t = time.perf_counter()
+    olink.link_attention(segs, cached, q, k, v, cfg.rope_theta, rows=probe)
+    per_row = (time.perf_counter() - t) / len(probe)
+    n = int(max(4, min(R, target_s / max(per_row, 1e-6))))
+    rows = np.unique(np.linspace(0, R - 1, n).astype(np.int64))
+    t = time.perf_counter()
+    olink.link_attention(segs, cached, q, k, v, cfg.rope_theta, rows=rows)
+    dt = time.perf_counter() - t
+    first = segs[0].start
+    flop = int(4 * cfg.head_dim * cfg.num_q_heads * (pos[rows] - first + 1).sum())
+    return dict(value=round(flop / dt / 1e12, 6), unit="TFLOP/s", cores=cores, kind="oracle",
+                sample=f"{len(rows)} of {R} selected rows of request 0, evenly spread over positions, all "
+                       f"{cfg.num_q_heads} heads, fp64 with explicit loops; {dt:.1f} s")
+
+
+def traffic_from_profiles(attn_calls_per_step):
+    """HBM bytes per attention launch from the committed counter summary, if it is current."""
+    if not os.path.exists(TRAFFIC_FILE):
+        return None
+    try:
+        t = json.load(open(TRAFFIC_FILE))
+    except Exception:
+        return None
+    if t.get("kernel_source_sha256_16") != kernel_hash():
+        return None
+    return t.get("hbm_bytes_per_launch")
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="long50k_k32")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--no-dense", action="store_true")
+    ap.add_argument("--copy-probe-mib", type=int, default=0,
+                    help="also run one device copy of this size per step (counter calibration runs)")
+    args = ap.parse_args()
+
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(f"bench.py measures one GPU only: the link step of one request batch runs on one MI355X "
+              f"here (asked for --gpus {args.gpus}, WORLD_SIZE {world}).", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    from workloads import CONFIGS
+
+    import position_independent_kv_legolink_amd as pic
+    pic.lib()
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    torch.cuda.set_device(0)
+    cfg = CONFIGS[args.workload]
+    dense_pages = 0 if args.no_dense else (-(-(cfg.prefix_len + cfg.chunks_per_request * cfg.chunk_len +
+                                                 cfg.suffix_len) // cfg.page_size)) * cfg.n_requests
+    job = LinkJob(cfg, dense_pages=dense_pages)
+    flop, attn_bytes, total_bytes = algorithmic_counts(cfg, job.export, job.sizes, job.n_tokens)
+    log(f"{cfg.name}: rows {job.sizes['rows']}, pages {job.sizes['pages']}, work items {job.sizes['work_items']} "
+        f"({job.sizes['split_items']} split), {flop / 1e9:.1f} GFLOP, {total_bytes / 1e6:.1f} MB")
+
+    copy_src = copy_dst = None
+    if args.copy_probe_mib:
+        copy_src = torch.ones(args.copy_probe_mib << 18, dtype=torch.float32, device="cuda")
+        copy_dst = torch.empty_like(copy_src)
+
+    ms_step, prof = time_steps(job, args.steps, args.warmup)
+    if copy_src is not None:
+        for _ in range(args.steps):
+            copy_dst.copy_(copy_src)
+        torch.cuda.synchronize()
+    calls = max(prof["calls"], 1)
+    attn_ms = prof["attention_ms"] / calls
+    scatter_ms = prof["scatter_ms"] / calls
+    merge_ms = prof["merge_ms"] / calls
+    link_ms = scatter_ms + attn_ms + merge_ms
+    log(f"step {ms_step:.3f} ms; scatter {scatter_ms:.4f} attention {attn_ms:.4f} merge {merge_ms:.4f} ms")
+
+    peak = PEAK_BF16_TFLOPS if cfg.dtype == "bf16" else PEAK_F32_TFLOPS
+    achieved = flop / (attn_ms * 1e-3) / 1e12
+    roofline = dict(bound="mfma", achieved=round(achieved, 2), peak=peak, unit="TFLOP/s",
+                    frac=round(achieved / peak, 4), traffic=traffic_from_profiles(1))
+
+    dense = None
+    if not args.no_dense:
+        dense = dense_comparator(job)
+        dense["link_speedup"] = round(dense["ms"] / link_ms, 2)
+        log(f"dense full recompute: {dense}")
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline(cfg, args.cpu_seconds)
+        log(f"cpu oracle: {cpu}")
+
+    result = {
+        "metric": METRIC,
+        "value": round(flop / (ms_step * 1e-3) / 1e12, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": cfg.dtype,
+        "data": "synthetic",
+        "config": {"workload": cfg.name, "tokens_per_request": job.n_tokens, "requests": cfg.n_requests,
+                   "selected_rows": job.sizes["rows"], "q_heads": cfg.num_q_heads, "kv_heads": cfg.num_kv_heads,
+                   "head_dim": cfg.head_dim, "page_size": cfg.page_size, "k": cfg.k,
+                   "block_level": cfg.block_level, "parallelism": "single GPU"},
+        "link_latency_ms": round(link_ms, 4),
+        "attention_ms": round(attn_ms, 4),
+        "scatter_ms": round(scatter_ms, 4),
+        "merge_ms": round(merge_ms, 4),
+        "algorithmic_gflop": round(flop / 1e9, 3),
+        "algorithmic_mb": round(total_bytes / 1e6, 2),
+        "hbm_gbps": round(total_bytes / (link_ms * 1e-3) / 1e9, 1),
+        "hbm_frac": round(total_bytes / (link_ms * 1e-3) / 1e9 / PEAK_HBM_GBPS, 4),
+        "mfma_frac_step": round(flop / (ms_step * 1e-3) / 1e12 / peak, 4),
+        "roofline": roofline,
+        "dense_comparator": dense,
+        "cpu_baseline": cpu,
+        "kernel_source_sha256_16": kernel_hash(),
+    }
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()
