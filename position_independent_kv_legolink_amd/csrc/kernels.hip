@@ -82,40 +82,38 @@ __device__ __forceinline__ void rope8_bf16(const u32x4 &lo, const u32x4 &hi, con
     }
 }
 
-// Does a key tile need the causal / padding mask for this work group?
-__device__ __forceinline__ bool tile_needs_mask(const PageDesc *pg, const WorkDesc &w, int lp0, int ppt,
-                                                int page_size) {
-    if (lp0 + ppt > w.page_end) return true;
-    for (int q = 0; q < ppt; ++q)
-        if (pg[lp0 + q].valid < page_size) return true;
-    const PageDesc last = pg[lp0 + ppt - 1];
-    return last.pos0 + page_size - 1 > w.rpos_min;
-}
-
 // ---------------------------------------------------------------------------------------------
-// bf16 attention. Work group = NW waves; wave w owns M-rows [32*MB*w, 32*MB*(w+1)) as MB 32-row
-// MFMA blocks; M-row m is (tile row m / G, query head m % G of the work item's KV head).
-//   S^T = K' Q'^T   (v_mfma_f32_32x32x16_bf16, A = rotated K rows from LDS, B = rotated Q in VGPRs)
-//   O^T += V^T P^T  (A = V^T from LDS, B = P straight from the S^T accumulators)
-// Keys of a 16-key group are stored in V^T in the order that makes each lane's P values a
-// contiguous MFMA operand (bits 2 and 3 of the key index swapped).
-template <int D, int NW, int MB>
-__global__ __launch_bounds__(NW * 64, 1) void link_attention_bf16(AttnParams p) {
-    constexpr int NT = NW * 64;
+// bf16 attention. Work group = 8 waves; wave w owns M-rows [32w, 32w + 32) as one 32-row MFMA
+// block; M-row m is (tile row m / G, query head m % G of the work item's KV head).
+//   S^T = K' Q'^T   (v_mfma_f32_32x32x16_bf16; A = rotated K rows from LDS, B = rotated Q in VGPRs)
+//   O^T += V^T P^T  (A = V^T built by transposing LDS reads of V, B = P straight from the S^T
+//                    accumulators)
+// Ping-pong schedule: waves 0-3 (group A, one per SIMD) and waves 4-7 (group B) run the same
+// per-tile sequence one phase apart, so that one wave's MFMA phase meets the other wave's VALU
+// phase on every SIMD:
+//   Y(t): softmax of tile t, RoPE + LDS staging of tile t+2, global loads of tile t+3  (VALU)
+//   X(t): PV of tile t, QK^T of tile t+1                                             (MFMA)
+// with a work-group barrier after each phase; group B passes one extra barrier at the start
+// (and group A one at the end), so B's phase k overlaps A's phase k+1. Tile buffers are deep
+// enough for the one-phase skew: K' and key positions x3, V x4.
+template <int D>
+__global__ __launch_bounds__(512, 1) void link_attention_bf16(AttnParams p) {
+    constexpr int NT = 512;
     constexpr int KT = kKeysPerTile;
-    constexpr int KS = D + 8;          // K' row stride in LDS (bf16)
-    constexpr int VS = KT + 8;         // V^T row stride in LDS (bf16)
+    constexpr int KS = D + 8;          // K' row stride in LDS (bf16): conflict-free A-fragment reads
+    constexpr int VS = D + 16;         // V row stride in LDS (bf16): conflict-free transposing reads
     constexpr int NS = D / 16;         // k-steps of QK^T
     constexpr int NDB = D / 32;        // 32-wide d blocks of PV
-    constexpr int KPAIRS = KT * (D / 16);          // (key, 8-dim lo/hi) pairs per tile
-    constexpr int VPAIRS = (KT / 2) * (D / 8);     // (key pair, 8 dims) chunks per tile
+    constexpr int KPAIRS = KT * (D / 16);          // (key, 8 dims of each half) per tile
+    constexpr int VCHUNKS = KT * (D / 8);          // (key, 8 dims) per tile
     constexpr int NKP = (KPAIRS + NT - 1) / NT;
-    constexpr int NVP = (VPAIRS + NT - 1) / NT;
-    constexpr int TQ = NW * MB * 32;
+    constexpr int NVC = (VCHUNKS + NT - 1) / NT;
+    constexpr int TQ = 256;
+    static_assert(KT == 64, "one key per lane when deciding the tile mask");
 
-    __shared__ __attribute__((aligned(16))) uint16_t ks[2][KT * KS];
-    __shared__ __attribute__((aligned(16))) uint16_t vts[2][D * VS];
-    __shared__ __attribute__((aligned(16))) int kpos_s[2][KT];
+    __shared__ __attribute__((aligned(16))) uint16_t ks[3][KT * KS];
+    __shared__ __attribute__((aligned(16))) uint16_t vs[4][KT * VS];
+    __shared__ __attribute__((aligned(16))) int kpos_s[3][KT];
 
     const WorkDesc w = p.work[blockIdx.x];
     if (w.n_rows <= 0) return;
@@ -129,19 +127,19 @@ __global__ __launch_bounds__(NW * 64, 1) void link_attention_bf16(AttnParams p) 
     const uint16_t *kpool = static_cast<const uint16_t *>(p.k_pool);
     const uint16_t *vpool = static_cast<const uint16_t *>(p.v_pool);
     const int64_t head_off = (int64_t)w.kv_head * page_size * D;
+    const int last_page = w.page_end - 1;
 
     // ---- rotated Q fragments, held for the whole key range
-    u32x4 qf[MB][NS];
-    int rpos[MB];
-#pragma unroll
-    for (int mb = 0; mb < MB; ++mb) {
-        const int m = (wave * MB + mb) * 32 + ln;
+    u32x4 qf[NS];
+    int rpos;
+    {
+        const int m = wave * 32 + ln;
         const int ti = m >> p.gshift;
         const bool valid = ti < w.n_rows;
         const int row = w.row0 + (valid ? ti : 0);
         const int qh = w.kv_head * G + (m & (G - 1));
         const int rp = valid ? p.row_pos[row] : -1;
-        rpos[mb] = rp;
+        rpos = rp;
         const uint16_t *qrow = static_cast<const uint16_t *>(p.q) + ((int64_t)row * p.hq + qh) * D;
         const float *cs = p.rope + (int64_t)(valid ? rp : 0) * D;
 #pragma unroll
@@ -157,71 +155,81 @@ __global__ __launch_bounds__(NW * 64, 1) void link_attention_bf16(AttnParams p) 
             c[1] = *reinterpret_cast<const floatx4 *>(cs + e0 + 4);
             sn[0] = *reinterpret_cast<const floatx4 *>(cs + D / 2 + e0);
             sn[1] = *reinterpret_cast<const floatx4 *>(cs + D / 2 + e0 + 4);
-            rope8_bf16(lo, hi, c, sn, qf[mb][s], qf[mb][s + NS / 2]);
+            rope8_bf16(lo, hi, c, sn, qf[s], qf[s + NS / 2]);
         }
     }
 
-    // ---- staging registers of the next key tile
+    // ---- staging registers of one key tile (global -> registers -> LDS)
     u32x4 k_lo[NKP], k_hi[NKP];
+    int k_pos[NKP];
     floatx4 k_c[NKP][2], k_s[NKP][2];
-    u32x4 v_a[NVP], v_b[NVP];
-    int kp_next = kNeverAttended;
+    u32x4 v_r[NVC];
+    int kp_stage = kNeverAttended;
+    unsigned mask_ring = 7u;           // bit (t % 3): tile t needs the causal/padding mask
 
+    // Keys of one wave's K pieces (and of each of its V pieces) lie in one page (page >= 16
+    // tokens), so their page descriptors are wave-uniform scalar loads. Keys past the work
+    // item's range or in page padding read real, finite pool data (the last page, or the zeroed
+    // padding slots) and are removed by the mask (position kNeverAttended).
     auto load_tile = [&](int t) {
         const int lp0 = w.page_begin + t * ppt;
+        const int wv = __builtin_amdgcn_readfirstlane(wave);
 #pragma unroll
         for (int u = 0; u < NKP; ++u) {
             const int pi = tid + NT * u;
-            if (KPAIRS % NT != 0 && pi >= KPAIRS) break;
             const int key = pi / (D / 16), c = pi % (D / 16);
-            const int lp = lp0 + (key >> p.pshift), slot = key & (page_size - 1);
-            bool ok = false;
-            int pos = 0;
-            int64_t base = 0;
-            if (lp < w.page_end) {
-                const PageDesc pd = pg[lp];
-                if (slot < pd.valid) {
-                    ok = true;
-                    pos = pd.pos0 + slot;
-                    base = (int64_t)pd.phys * p.page_elems + head_off + (int64_t)slot * D;
-                }
+            const int lpu = lp0 + (((NT * u + 64 * wv) / (D / 16)) >> p.pshift);
+            const PageDesc pd = pg[min(lpu, last_page)];
+            const int slot = key & (page_size - 1);
+            const bool ok = (KPAIRS % NT == 0 || pi < KPAIRS) && lpu <= last_page && slot < pd.valid;
+            const int64_t base = (int64_t)pd.phys * p.page_elems + head_off + (int64_t)slot * D;
+            k_lo[u] = *reinterpret_cast<const u32x4 *>(kpool + base + 8 * c);
+            k_hi[u] = *reinterpret_cast<const u32x4 *>(kpool + base + D / 2 + 8 * c);
+            k_pos[u] = ok ? pd.pos0 + slot : pd.pos0;
+        }
+#pragma unroll
+        for (int u = 0; u < NVC; ++u) {
+            const int pi = tid + NT * u;
+            const int key = pi / (D / 8), c16 = pi % (D / 8);
+            const int lpu = lp0 + (((NT * u + 64 * wv) / (D / 8)) >> p.pshift);
+            const PageDesc pd = pg[min(lpu, last_page)];
+            const int slot = key & (page_size - 1);
+            const int64_t base = (int64_t)pd.phys * p.page_elems + head_off + (int64_t)slot * D;
+            v_r[u] = *reinterpret_cast<const u32x4 *>(vpool + base + 8 * c16);
+        }
+        {
+            // every wave holds the position of key `lane` of the tile (64 keys, 64 lanes)
+            const int q = lane >> p.pshift, slot = lane & (page_size - 1);
+            int pos0 = 0, valid = 0;
+#pragma unroll
+            for (int j = 0; j < KT / 16; ++j) {
+                const int lpj = lp0 + j;
+                const PageDesc pd = pg[min(lpj, last_page)];
+                const int vj = lpj <= last_page ? pd.valid : 0;
+                pos0 = q == j ? pd.pos0 : pos0;
+                valid = q == j ? vj : valid;
             }
-            k_lo[u] = ok ? *reinterpret_cast<const u32x4 *>(kpool + base + 8 * c) : u32x4{0, 0, 0, 0};
-            k_hi[u] = ok ? *reinterpret_cast<const u32x4 *>(kpool + base + D / 2 + 8 * c) : u32x4{0, 0, 0, 0};
-            const float *cs = p.rope + (int64_t)pos * D + 8 * c;
+            kp_stage = slot < valid ? pos0 + slot : kNeverAttended;
+        }
+    };
+
+    // cos/sin of the staged keys; issued ahead of the MFMAs that hide their latency
+    auto load_rope = [&]() {
+#pragma unroll
+        for (int u = 0; u < NKP; ++u) {
+            const int pi = tid + NT * u;
+            const int c = pi % (D / 16);
+            const float *cs = p.rope + (int64_t)k_pos[u] * D + 8 * c;
             k_c[u][0] = *reinterpret_cast<const floatx4 *>(cs);
             k_c[u][1] = *reinterpret_cast<const floatx4 *>(cs + 4);
             k_s[u][0] = *reinterpret_cast<const floatx4 *>(cs + D / 2);
             k_s[u][1] = *reinterpret_cast<const floatx4 *>(cs + D / 2 + 4);
         }
-#pragma unroll
-        for (int u = 0; u < NVP; ++u) {
-            const int pi = tid + NT * u;
-            if (VPAIRS % NT != 0 && pi >= VPAIRS) break;
-            const int key0 = 2 * (pi / (D / 8)), c16 = pi % (D / 8);
-            const int lp = lp0 + (key0 >> p.pshift), slot = key0 & (page_size - 1);
-            u32x4 a = {0, 0, 0, 0}, b = {0, 0, 0, 0};
-            if (lp < w.page_end) {
-                const PageDesc pd = pg[lp];
-                const int64_t base = (int64_t)pd.phys * p.page_elems + head_off + (int64_t)slot * D + 8 * c16;
-                if (slot < pd.valid) a = *reinterpret_cast<const u32x4 *>(vpool + base);
-                if (slot + 1 < pd.valid) b = *reinterpret_cast<const u32x4 *>(vpool + base + D);
-            }
-            v_a[u] = a;
-            v_b[u] = b;
-        }
-        if (tid < KT) {
-            const int lp = lp0 + (tid >> p.pshift), slot = tid & (page_size - 1);
-            int kp = kNeverAttended;
-            if (lp < w.page_end) {
-                const PageDesc pd = pg[lp];
-                if (slot < pd.valid) kp = pd.pos0 + slot;
-            }
-            kp_next = kp;
-        }
     };
 
-    auto store_tile = [&](int buf) {
+    auto store_tile = [&](int t) {
+        uint16_t *kb = ks[t % 3];
+        uint16_t *vb = vs[t & 3];
 #pragma unroll
         for (int u = 0; u < NKP; ++u) {
             const int pi = tid + NT * u;
@@ -229,174 +237,203 @@ __global__ __launch_bounds__(NW * 64, 1) void link_attention_bf16(AttnParams p) 
             const int key = pi / (D / 16), c = pi % (D / 16);
             u32x4 olo, ohi;
             rope8_bf16(k_lo[u], k_hi[u], k_c[u], k_s[u], olo, ohi);
-            *reinterpret_cast<u32x4 *>(&ks[buf][key * KS + 8 * c]) = olo;
-            *reinterpret_cast<u32x4 *>(&ks[buf][key * KS + D / 2 + 8 * c]) = ohi;
+            *reinterpret_cast<u32x4 *>(&kb[key * KS + 8 * c]) = olo;
+            *reinterpret_cast<u32x4 *>(&kb[key * KS + D / 2 + 8 * c]) = ohi;
         }
 #pragma unroll
-        for (int u = 0; u < NVP; ++u) {
+        for (int u = 0; u < NVC; ++u) {
             const int pi = tid + NT * u;
-            if (VPAIRS % NT != 0 && pi >= VPAIRS) break;
-            const int key0 = 2 * (pi / (D / 8)), c16 = pi % (D / 8);
-            const int col = (key0 & ~15) | swap_bits23(key0 & 15);
-#pragma unroll
-            for (int i = 0; i < 8; ++i) {
-                const uint32_t wa = v_a[u][i >> 1], wb = v_b[u][i >> 1];
-                const uint32_t word = (i & 1) ? ((wa >> 16) | (wb & 0xffff0000u)) : ((wa & 0xffffu) | (wb << 16));
-                *reinterpret_cast<uint32_t *>(&vts[buf][(8 * c16 + i) * VS + col]) = word;
-            }
+            if (VCHUNKS % NT != 0 && pi >= VCHUNKS) break;
+            const int key = pi / (D / 8), c16 = pi % (D / 8);
+            *reinterpret_cast<u32x4 *>(&vb[key * VS + 8 * c16]) = v_r[u];
         }
-        if (tid < KT) kpos_s[buf][tid] = kp_next;
+        kpos_s[t % 3][lane] = kp_stage;   // every wave writes the same 64 values
+        const unsigned bit = 1u << (t % 3);
+        mask_ring = __any(kp_stage > w.rpos_min) ? (mask_ring | bit) : (mask_ring & ~bit);
     };
 
-    floatx16 oacc[MB][NDB];
+    // S^T of one tile: two 32-key blocks, NS k-steps each
+    auto qk = [&](int t, floatx16 (&sacc)[2]) {
+        const uint16_t *kb = ks[t % 3];
 #pragma unroll
-    for (int mb = 0; mb < MB; ++mb)
+        for (int b = 0; b < 2; ++b)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) sacc[b][r] = 0.0f;
+#pragma unroll
+        for (int s = 0; s < NS; ++s)
+#pragma unroll
+            for (int b = 0; b < 2; ++b) {
+                const bf16x8 a = *reinterpret_cast<const bf16x8 *>(&kb[(b * 32 + ln) * KS + 16 * s + 8 * lg]);
+                sacc[b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, __builtin_bit_cast(bf16x8, qf[s]), sacc[b],
+                                                                   0, 0, 0);
+            }
+    };
+
+    floatx16 oacc[NDB];
+#pragma unroll
+    for (int db = 0; db < NDB; ++db)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) oacc[db][r] = 0.0f;
+    float mrow = kInitMax, lrow = 0.0f;
+
+    // online softmax, part 1: row maximum over the tile and the running maximum (moved only when
+    // it grows by more than 2^kRescaleLog2); returns the factor that rescales the running sums
+    auto softmax_max = [&](floatx16 (&sacc)[2]) -> float {
+        float mx = sacc[0][0];
+#pragma unroll
+        for (int b = 0; b < 2; ++b)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sacc[b][r]);
+        {
+            const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(mx), __float_as_uint(mx), false, false);
+            mx = fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1]));
+        }
+        const bool upd = (mx - mrow) * p.scale_log2 > kRescaleLog2;
+        const float mnew = upd ? mx : mrow;
+        const float alpha = __builtin_amdgcn_exp2f((mrow - mnew) * p.scale_log2);
+        mrow = mnew;
+        lrow *= alpha;
+        return alpha;
+    };
+
+    // part 2: exponentials, this lane's share of the row sum, bf16 P fragments for PV
+    auto softmax_exp = [&](floatx16 (&sacc)[2], u32x4 (&pf)[2][2]) {
+        const float msc = mrow * p.scale_log2;
+        float lsum = 0.0f;
+#pragma unroll
+        for (int b = 0; b < 2; ++b)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                const float e = __builtin_amdgcn_exp2f(fmaf(sacc[b][r], p.scale_log2, -msc));
+                sacc[b][r] = e;
+                lsum += e;
+            }
+        lrow += lsum;
+#pragma unroll
+        for (int b = 0; b < 2; ++b)
+#pragma unroll
+            for (int s2 = 0; s2 < 2; ++s2)
+#pragma unroll
+                for (int u = 0; u < 4; ++u)
+                    pf[b][s2][u] = pack_bf16(sacc[b][8 * s2 + 2 * u], sacc[b][8 * s2 + 2 * u + 1]);
+    };
+
+    auto apply_mask = [&](int t, floatx16 (&sacc)[2]) {
+        const int *kp = kpos_s[t % 3];
+#pragma unroll
+        for (int b = 0; b < 2; ++b)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const i32x4 kp4 = *reinterpret_cast<const i32x4 *>(&kp[b * 32 + 8 * i + 4 * lg]);
+#pragma unroll
+                for (int j = 0; j < 4; ++j)
+                    if (kp4[j] > rpos) sacc[b][4 * i + j] = -INFINITY;
+            }
+    };
+
+    auto rescale = [&](float alpha) {
+        if (__any(alpha != 1.0f)) {
+#pragma unroll
+            for (int db = 0; db < NDB; ++db)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) oacc[db][r] *= alpha;
+        }
+    };
+
+    // O^T += V^T P^T for one tile; V^T operands come from two transposing 8-byte LDS reads
+    auto pv = [&](int t, const u32x4 (&pf)[2][2]) {
+        const uint16_t *vb = vs[t & 3];
+        const int gi = lane >> 4, j = (lane >> 2) & 3, q = lane & 3;
 #pragma unroll
         for (int db = 0; db < NDB; ++db)
 #pragma unroll
-            for (int r = 0; r < 16; ++r) oacc[mb][db][r] = 0.0f;
-    float mrow[MB], lrow[MB];
+            for (int b = 0; b < 2; ++b)
 #pragma unroll
-    for (int mb = 0; mb < MB; ++mb) {
-        mrow[mb] = kInitMax;
-        lrow[mb] = 0.0f;
-    }
+                for (int s2 = 0; s2 < 2; ++s2) {
+                    const int key = b * 32 + 16 * s2 + 4 * lg + j;
+                    const int d = db * 32 + 16 * (gi & 1) + 4 * q;
+                    typedef short v4s __attribute__((ext_vector_type(4)));
+                    const v4s lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                        (__attribute__((address_space(3))) v4s *)(vb + key * VS + d));
+                    const v4s hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                        (__attribute__((address_space(3))) v4s *)(vb + (key + 8) * VS + d));
+                    const bf16x8 a = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+                    oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, __builtin_bit_cast(bf16x8, pf[b][s2]),
+                                                                       oacc[db], 0, 0, 0);
+                }
+    };
 
     const int ntiles = (w.page_end - w.page_begin + ppt - 1) / ppt;
+    const bool group_b = wave >= 4;
+    floatx16 sacc[2];
+    u32x4 pf[2][2];
+
     load_tile(0);
+    load_rope();
     store_tile(0);
+    load_tile(1);
+    load_rope();
+    store_tile(1);
     __syncthreads();
+    qk(0, sacc);
+    load_tile(2);
+    if (group_b) __syncthreads();
 
     for (int t = 0; t < ntiles; ++t) {
-        const int buf = t & 1;
-        const bool more = t + 1 < ntiles;
-        if (more) load_tile(t + 1);
-        const bool need_mask = tile_needs_mask(pg, w, w.page_begin + t * ppt, ppt, page_size);
-
-        floatx16 sacc[2][MB];
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-            for (int mb = 0; mb < MB; ++mb)
-#pragma unroll
-                for (int r = 0; r < 16; ++r) sacc[kb][mb][r] = 0.0f;
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb) {
-#pragma unroll
-            for (int s = 0; s < NS; ++s) {
-                const bf16x8 a = *reinterpret_cast<const bf16x8 *>(&ks[buf][(kb * 32 + ln) * KS + 16 * s + 8 * lg]);
-#pragma unroll
-                for (int mb = 0; mb < MB; ++mb)
-                    sacc[kb][mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-                        a, __builtin_bit_cast(bf16x8, qf[mb][s]), sacc[kb][mb], 0, 0, 0);
-            }
+        // Y(t): softmax of tile t; staging of tile t+2; loads of tile t+3
+        if (mask_ring & (1u << (t % 3))) apply_mask(t, sacc);
+        rescale(softmax_max(sacc));
+        softmax_exp(sacc, pf);
+        if (t + 2 < ntiles) {
+            load_rope();
+            store_tile(t + 2);
+            load_tile(t + 3);
         }
+        __syncthreads();
+        // X(t): PV of tile t; QK^T of tile t+1
+        pv(t, pf);
+        if (t + 1 < ntiles) qk(t + 1, sacc);
+        __syncthreads();
+    }
+    if (!group_b) __syncthreads();
 
-        u32x4 pf[MB][2][2];
-#pragma unroll
-        for (int mb = 0; mb < MB; ++mb) {
-            if (need_mask) {
-#pragma unroll
-                for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-                    for (int i = 0; i < 4; ++i) {
-                        const i32x4 kp4 = *reinterpret_cast<const i32x4 *>(&kpos_s[buf][kb * 32 + 8 * i + 4 * lg]);
-#pragma unroll
-                        for (int j = 0; j < 4; ++j)
-                            if (kp4[j] > rpos[mb]) sacc[kb][mb][4 * i + j] = -INFINITY;
-                    }
-            }
-            float mx = sacc[0][mb][0];
-#pragma unroll
-            for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-                for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sacc[kb][mb][r]);
-            mx = fmaxf(mx, __shfl_xor(mx, 32));
-            const bool upd = (mx - mrow[mb]) * p.scale_log2 > kRescaleLog2;
-            if (__any(upd)) {
-                const float mnew = upd ? mx : mrow[mb];
-                const float alpha = __builtin_amdgcn_exp2f((mrow[mb] - mnew) * p.scale_log2);
-                lrow[mb] *= alpha;
+    // ---- epilogue: normalise, write the output (or this split's partial result)
+    {
+        const int m = wave * 32 + ln;
+        const int ti = m >> p.gshift;
+        const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(lrow), __float_as_uint(lrow), false, false);
+        const float lt = __uint_as_float(sw[0]) + __uint_as_float(sw[1]);
+        const float inv = lt > 0.0f ? 1.0f / lt : 0.0f;
+        const float lse_v = lt > 0.0f ? mrow * p.scale + logf(lt) : -INFINITY;
+        if (ti < w.n_rows) {
+            const int row = w.row0 + ti;
+            const int qh = w.kv_head * G + (m & (G - 1));
+            if (w.partial < 0) {
+                uint16_t *orow = static_cast<uint16_t *>(p.out) + ((int64_t)row * p.hq + qh) * D;
 #pragma unroll
                 for (int db = 0; db < NDB; ++db)
 #pragma unroll
-                    for (int r = 0; r < 16; ++r) oacc[mb][db][r] *= alpha;
-                mrow[mb] = mnew;
+                    for (int i = 0; i < 4; ++i) {
+                        const int d0 = db * 32 + 8 * i + 4 * lg;
+                        u32x2 v;
+                        v[0] = pack_bf16(oacc[db][4 * i] * inv, oacc[db][4 * i + 1] * inv);
+                        v[1] = pack_bf16(oacc[db][4 * i + 2] * inv, oacc[db][4 * i + 3] * inv);
+                        *reinterpret_cast<u32x2 *>(orow + d0) = v;
+                    }
+                if (p.lse && lg == 0) p.lse[(int64_t)row * p.hq + qh] = lse_v;
+            } else {
+                float *po = p.part_o + ((int64_t)w.partial * TQ + m) * D;
+#pragma unroll
+                for (int db = 0; db < NDB; ++db)
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        const int d0 = db * 32 + 8 * i + 4 * lg;
+                        floatx4 v = {oacc[db][4 * i] * inv, oacc[db][4 * i + 1] * inv, oacc[db][4 * i + 2] * inv,
+                                     oacc[db][4 * i + 3] * inv};
+                        *reinterpret_cast<floatx4 *>(po + d0) = v;
+                    }
+                if (lg == 0) p.part_lse[(int64_t)w.partial * TQ + m] = lse_v;
             }
-            const float msc = mrow[mb] * p.scale_log2;
-            float lsum = 0.0f;
-#pragma unroll
-            for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-                for (int r = 0; r < 16; ++r) {
-                    const float e = __builtin_amdgcn_exp2f(fmaf(sacc[kb][mb][r], p.scale_log2, -msc));
-                    sacc[kb][mb][r] = e;
-                    lsum += e;
-                }
-            lrow[mb] += lsum;
-#pragma unroll
-            for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-                for (int s2 = 0; s2 < 2; ++s2)
-#pragma unroll
-                    for (int u = 0; u < 4; ++u)
-                        pf[mb][kb][s2][u] = pack_bf16(sacc[kb][mb][8 * s2 + 2 * u], sacc[kb][mb][8 * s2 + 2 * u + 1]);
-        }
-
-#pragma unroll
-        for (int db = 0; db < NDB; ++db)
-#pragma unroll
-            for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-                for (int s2 = 0; s2 < 2; ++s2) {
-                    const bf16x8 a = *reinterpret_cast<const bf16x8 *>(
-                        &vts[buf][(db * 32 + ln) * VS + kb * 32 + 16 * s2 + 8 * lg]);
-#pragma unroll
-                    for (int mb = 0; mb < MB; ++mb)
-                        oacc[mb][db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-                            a, __builtin_bit_cast(bf16x8, pf[mb][kb][s2]), oacc[mb][db], 0, 0, 0);
-                }
-
-        if (more) store_tile(buf ^ 1);
-        __syncthreads();
-    }
-
-    // ---- epilogue: normalise, write the output (or this split's partial result)
-#pragma unroll
-    for (int mb = 0; mb < MB; ++mb) {
-        const int m = (wave * MB + mb) * 32 + ln;
-        const int ti = m >> p.gshift;
-        const float lt = lrow[mb] + __shfl_xor(lrow[mb], 32);
-        const float inv = lt > 0.0f ? 1.0f / lt : 0.0f;
-        const float lse_v = lt > 0.0f ? mrow[mb] * p.scale + logf(lt) : -INFINITY;
-        if (ti >= w.n_rows) continue;
-        const int row = w.row0 + ti;
-        const int qh = w.kv_head * G + (m & (G - 1));
-        if (w.partial < 0) {
-            uint16_t *orow = static_cast<uint16_t *>(p.out) + ((int64_t)row * p.hq + qh) * D;
-#pragma unroll
-            for (int db = 0; db < NDB; ++db)
-#pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    const int d0 = db * 32 + 8 * i + 4 * lg;
-                    u32x2 v;
-                    v[0] = pack_bf16(oacc[mb][db][4 * i] * inv, oacc[mb][db][4 * i + 1] * inv);
-                    v[1] = pack_bf16(oacc[mb][db][4 * i + 2] * inv, oacc[mb][db][4 * i + 3] * inv);
-                    *reinterpret_cast<u32x2 *>(orow + d0) = v;
-                }
-            if (p.lse && lg == 0) p.lse[(int64_t)row * p.hq + qh] = lse_v;
-        } else {
-            float *po = p.part_o + ((int64_t)w.partial * TQ + m) * D;
-#pragma unroll
-            for (int db = 0; db < NDB; ++db)
-#pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    const int d0 = db * 32 + 8 * i + 4 * lg;
-                    floatx4 v = {oacc[mb][db][4 * i] * inv, oacc[mb][db][4 * i + 1] * inv,
-                                 oacc[mb][db][4 * i + 2] * inv, oacc[mb][db][4 * i + 3] * inv};
-                    *reinterpret_cast<floatx4 *>(po + d0) = v;
-                }
-            if (lg == 0) p.part_lse[(int64_t)w.partial * TQ + m] = lse_v;
         }
     }
 }
@@ -469,6 +506,7 @@ __global__ __launch_bounds__(kThreads, 1) void link_attention_f32(AttnParams p) 
     floatx4 k_lo[NKP], k_hi[NKP], k_c[NKP], k_s[NKP];
     floatx4 v_r[NV];
     int kp_next = kNeverAttended;
+    bool mask_next = true;
 
     auto load_tile = [&](int t) {
         const int lp0 = w.page_begin + t * ppt;
@@ -508,8 +546,9 @@ __global__ __launch_bounds__(kThreads, 1) void link_attention_f32(AttnParams p) 
             }
             v_r[u] = v;
         }
-        if (tid < KT) {
-            const int lp = lp0 + (tid >> p.pshift), slot = tid & (page_size - 1);
+        {
+            // every wave holds the position of key `lane` of the tile (64 keys, 64 lanes)
+            const int lp = lp0 + (lane >> p.pshift), slot = lane & (page_size - 1);
             int kp = kNeverAttended;
             if (lp < w.page_end) {
                 const PageDesc pd = pg[lp];
@@ -539,7 +578,9 @@ __global__ __launch_bounds__(kThreads, 1) void link_attention_f32(AttnParams p) 
             const int key = pi / (D / 4), c = pi % (D / 4);
             *reinterpret_cast<floatx4 *>(&vs[buf][key * VS + 4 * c]) = v_r[u];
         }
-        if (tid < KT) kpos_s[buf][tid] = kp_next;
+        if (wave == 0) kpos_s[buf][lane] = kp_next;
+        // the tile needs the causal/padding mask iff some key lies after the tile's first row
+        mask_next = __any(kp_next > w.rpos_min);
     };
 
     floatx16 oacc[NDB];
@@ -557,8 +598,8 @@ __global__ __launch_bounds__(kThreads, 1) void link_attention_f32(AttnParams p) 
     for (int t = 0; t < ntiles; ++t) {
         const int buf = t & 1;
         const bool more = t + 1 < ntiles;
+        const bool need_mask = mask_next;
         if (more) load_tile(t + 1);
-        const bool need_mask = tile_needs_mask(pg, w, w.page_begin + t * ppt, ppt, page_size);
 
         floatx16 sacc[2];
 #pragma unroll
@@ -802,12 +843,8 @@ hipError_t launch_attention(const LayerShape &s, const void *q, const void *k_po
     p.scale_log2 = 1.4426950408889634f / sqrtf((float)s.d);
     dim3 grid(t.n_work);
     if (s.dtype == 0) {
-        if (s.d == 128)
-            hipLaunchKernelGGL((link_attention_bf16<128, kBf16Waves, kBf16Blocks>), grid, dim3(kBf16Waves * 64), 0,
-                               stream, p);
-        else
-            hipLaunchKernelGGL((link_attention_bf16<64, kBf16Waves, kBf16Blocks>), grid, dim3(kBf16Waves * 64), 0,
-                               stream, p);
+        if (s.d == 128) hipLaunchKernelGGL(link_attention_bf16<128>, grid, dim3(512), 0, stream, p);
+        else hipLaunchKernelGGL(link_attention_bf16<64>, grid, dim3(512), 0, stream, p);
     } else {
         if (s.d == 128) hipLaunchKernelGGL(link_attention_f32<128>, grid, dim3(kThreads), 0, stream, p);
         else hipLaunchKernelGGL(link_attention_f32<64>, grid, dim3(kThreads), 0, stream, p);

@@ -54,11 +54,7 @@ struct MergeDesc {
 constexpr int kKeysPerTile = 64;   // keys staged in LDS per attention iteration
 constexpr int kThreads = 256;      // page writers, merge and the fp32 attention kernel
 
-// bf16 attention work group: kBf16Waves waves of kBf16Blocks 32-row MFMA blocks each.
-constexpr int kBf16Waves = 8;
-constexpr int kBf16Blocks = 1;
-
-// (row, head) pairs handled by one attention work group.
-constexpr int tile_qrows(int dtype) { return dtype == 0 ? kBf16Waves * kBf16Blocks * 32 : 128; }
+// (row, head) pairs handled by one attention work group: 8 waves x 32 rows (bf16), 4 x 32 (fp32).
+constexpr int tile_qrows(int dtype) { return dtype == 0 ? 256 : 128; }
 
 }  // namespace piclink
