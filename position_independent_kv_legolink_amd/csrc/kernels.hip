@@ -46,6 +46,15 @@ __device__ __forceinline__ uint32_t pack_bf16(float a, float b) {
     return __builtin_bit_cast(uint32_t, __builtin_convertvector(f, bf16x2));
 }
 
+// Work-group barrier that orders LDS only. A plain __syncthreads() also waits for every
+// outstanding global load of the wave (vmcnt(0)), which would expose the latency of loads that
+// are prefetched for later tiles and are read by their own wave only.
+__device__ __forceinline__ void lds_barrier() {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+
 __device__ __forceinline__ int swap_bits23(int x) {
     return (x & ~12) | ((x & 4) << 1) | ((x & 8) >> 1);
 }
@@ -111,9 +120,11 @@ __global__ __launch_bounds__(512, 1) void link_attention_bf16(AttnParams p) {
     constexpr int TQ = 256;
     static_assert(KT == 64, "one key per lane when deciding the tile mask");
 
-    __shared__ __attribute__((aligned(16))) uint16_t ks[3][KT * KS];
-    __shared__ __attribute__((aligned(16))) uint16_t vs[4][KT * VS];
-    __shared__ __attribute__((aligned(16))) int kpos_s[3][KT];
+    constexpr int KBUF = KT * KS, VBUF = KT * VS;
+    __shared__ __attribute__((aligned(16))) uint16_t ks[3 * KBUF];
+    __shared__ __attribute__((aligned(16))) uint16_t vs[4 * VBUF];
+    __shared__ __attribute__((aligned(16))) int kpos_s[3 * KT];
+    __shared__ int pg_phys[kMaxItemPages], pg_pos0[kMaxItemPages], pg_valid[kMaxItemPages];
 
     const WorkDesc w = p.work[blockIdx.x];
     if (w.n_rows <= 0) return;
@@ -127,7 +138,6 @@ __global__ __launch_bounds__(512, 1) void link_attention_bf16(AttnParams p) {
     const uint16_t *kpool = static_cast<const uint16_t *>(p.k_pool);
     const uint16_t *vpool = static_cast<const uint16_t *>(p.v_pool);
     const int64_t head_off = (int64_t)w.kv_head * page_size * D;
-    const int last_page = w.page_end - 1;
 
     // ---- rotated Q fragments, held for the whole key range
     u32x4 qf[NS];
@@ -167,50 +177,69 @@ __global__ __launch_bounds__(512, 1) void link_attention_bf16(AttnParams p) {
     int kp_stage = kNeverAttended;
     unsigned mask_ring = 7u;           // bit (t % 3): tile t needs the causal/padding mask
 
-    // Keys of one wave's K pieces (and of each of its V pieces) lie in one page (page >= 16
-    // tokens), so their page descriptors are wave-uniform scalar loads. Keys past the work
-    // item's range or in page padding read real, finite pool data (the last page, or the zeroed
-    // padding slots) and are removed by the mask (position kNeverAttended).
-    auto load_tile = [&](int t) {
-        const int lp0 = w.page_begin + t * ppt;
+    // The work item's page table is staged in LDS once. The descriptors of a tile's KT / page
+    // pages are read from LDS at the start of the VALU phase (their latency hides behind the
+    // softmax) and moved to SGPRs where the global loads use them. Keys of one wave's K pieces
+    // (and of each of its V pieces) lie in one page (page >= 16 tokens): each piece picks its page
+    // with a scalar select. Keys past the work item's range or in page padding read real, finite
+    // pool data (the last page, or the zeroed padding slots) and are removed by the mask
+    // (position kNeverAttended).
+    const int n_pages = w.page_end - w.page_begin;
+    for (int i = tid; i < n_pages; i += NT) {
+        const PageDesc d = pg[w.page_begin + i];
+        pg_phys[i] = d.phys;
+        pg_pos0[i] = d.pos0;
+        pg_valid[i] = d.valid;
+    }
+    lds_barrier();
+    // descriptor values read ahead from LDS: the wave's K page and V pages (uniform) and the
+    // page of key `lane` (for the mask positions)
+    int rk_phys[NKP], rk_pos0[NKP], rk_valid[NKP], rv_phys[NVC], rl_pos0, rl_valid;
+    auto load_desc = [&](int t) {
+        const int r0 = t * ppt;
         const int wv = __builtin_amdgcn_readfirstlane(wave);
+#pragma unroll
+        for (int u = 0; u < NKP; ++u) {
+            const int rq = r0 + (((NT * u + 64 * wv) / (D / 16)) >> p.pshift);
+            const int r = min(rq, n_pages - 1);
+            rk_phys[u] = pg_phys[r];
+            rk_pos0[u] = pg_pos0[r];
+            rk_valid[u] = rq < n_pages ? pg_valid[r] : 0;
+        }
+#pragma unroll
+        for (int u = 0; u < NVC; ++u)
+            rv_phys[u] = pg_phys[min(r0 + (((NT * u + 64 * wv) / (D / 8)) >> p.pshift), n_pages - 1)];
+        const int rq = r0 + (lane >> p.pshift);
+        const int r = min(rq, n_pages - 1);
+        rl_pos0 = pg_pos0[r];
+        rl_valid = rq < n_pages ? pg_valid[r] : 0;
+    };
+    auto load_tile = [&]() {
 #pragma unroll
         for (int u = 0; u < NKP; ++u) {
             const int pi = tid + NT * u;
             const int key = pi / (D / 16), c = pi % (D / 16);
-            const int lpu = lp0 + (((NT * u + 64 * wv) / (D / 16)) >> p.pshift);
-            const PageDesc pd = pg[min(lpu, last_page)];
+            const int phys = __builtin_amdgcn_readfirstlane(rk_phys[u]);
+            const int pos0 = __builtin_amdgcn_readfirstlane(rk_pos0[u]);
+            const int valid = __builtin_amdgcn_readfirstlane(rk_valid[u]);
             const int slot = key & (page_size - 1);
-            const bool ok = (KPAIRS % NT == 0 || pi < KPAIRS) && lpu <= last_page && slot < pd.valid;
-            const int64_t base = (int64_t)pd.phys * p.page_elems + head_off + (int64_t)slot * D;
+            const bool ok = (KPAIRS % NT == 0 || pi < KPAIRS) && slot < valid;
+            const int64_t base = (int64_t)phys * p.page_elems + head_off + (int64_t)slot * D;
             k_lo[u] = *reinterpret_cast<const u32x4 *>(kpool + base + 8 * c);
             k_hi[u] = *reinterpret_cast<const u32x4 *>(kpool + base + D / 2 + 8 * c);
-            k_pos[u] = ok ? pd.pos0 + slot : pd.pos0;
+            k_pos[u] = ok ? pos0 + slot : pos0;
         }
 #pragma unroll
         for (int u = 0; u < NVC; ++u) {
             const int pi = tid + NT * u;
             const int key = pi / (D / 8), c16 = pi % (D / 8);
-            const int lpu = lp0 + (((NT * u + 64 * wv) / (D / 8)) >> p.pshift);
-            const PageDesc pd = pg[min(lpu, last_page)];
             const int slot = key & (page_size - 1);
-            const int64_t base = (int64_t)pd.phys * p.page_elems + head_off + (int64_t)slot * D;
+            const int64_t base =
+                (int64_t)__builtin_amdgcn_readfirstlane(rv_phys[u]) * p.page_elems + head_off + (int64_t)slot * D;
             v_r[u] = *reinterpret_cast<const u32x4 *>(vpool + base + 8 * c16);
         }
-        {
-            // every wave holds the position of key `lane` of the tile (64 keys, 64 lanes)
-            const int q = lane >> p.pshift, slot = lane & (page_size - 1);
-            int pos0 = 0, valid = 0;
-#pragma unroll
-            for (int j = 0; j < KT / 16; ++j) {
-                const int lpj = lp0 + j;
-                const PageDesc pd = pg[min(lpj, last_page)];
-                const int vj = lpj <= last_page ? pd.valid : 0;
-                pos0 = q == j ? pd.pos0 : pos0;
-                valid = q == j ? vj : valid;
-            }
-            kp_stage = slot < valid ? pos0 + slot : kNeverAttended;
-        }
+        const int slot = lane & (page_size - 1);
+        kp_stage = slot < rl_valid ? rl_pos0 + slot : kNeverAttended;
     };
 
     // cos/sin of the staged keys; issued ahead of the MFMAs that hide their latency
@@ -227,9 +256,10 @@ __global__ __launch_bounds__(512, 1) void link_attention_bf16(AttnParams p) {
         }
     };
 
-    auto store_tile = [&](int t) {
-        uint16_t *kb = ks[t % 3];
-        uint16_t *vb = vs[t & 3];
+    // slots: K' and key positions in ring slot ksl (of 3), V in slot vsl (of 4)
+    auto store_tile = [&](int ksl, int vsl, int t) {
+        uint16_t *kb = ks + ksl * KBUF;
+        uint16_t *vb = vs + vsl * VBUF;
 #pragma unroll
         for (int u = 0; u < NKP; ++u) {
             const int pi = tid + NT * u;
@@ -247,14 +277,14 @@ __global__ __launch_bounds__(512, 1) void link_attention_bf16(AttnParams p) {
             const int key = pi / (D / 8), c16 = pi % (D / 8);
             *reinterpret_cast<u32x4 *>(&vb[key * VS + 8 * c16]) = v_r[u];
         }
-        kpos_s[t % 3][lane] = kp_stage;   // every wave writes the same 64 values
-        const unsigned bit = 1u << (t % 3);
+        kpos_s[ksl * KT + lane] = kp_stage;   // every wave writes the same 64 values
+        const unsigned bit = 1u << ksl;
         mask_ring = __any(kp_stage > w.rpos_min) ? (mask_ring | bit) : (mask_ring & ~bit);
     };
 
     // S^T of one tile: two 32-key blocks, NS k-steps each
-    auto qk = [&](int t, floatx16 (&sacc)[2]) {
-        const uint16_t *kb = ks[t % 3];
+    auto qk = [&](int ksl, floatx16 (&sacc)[2]) {
+        const uint16_t *kb = ks + ksl * KBUF;
 #pragma unroll
         for (int b = 0; b < 2; ++b)
 #pragma unroll
@@ -296,30 +326,30 @@ __global__ __launch_bounds__(512, 1) void link_attention_bf16(AttnParams p) {
         return alpha;
     };
 
-    // part 2: exponentials, this lane's share of the row sum, bf16 P fragments for PV
-    auto softmax_exp = [&](floatx16 (&sacc)[2], u32x4 (&pf)[2][2]) {
+    // part 2: exponentials straight into the bf16 P fragments; the row sum adds the rounded
+    // weights (v_dot2 against (1, 1)), i.e. exactly the weights the PV MFMA multiplies
+    auto softmax_exp = [&](const floatx16 (&sacc)[2], u32x4 (&pf)[2][2]) {
         const float msc = mrow * p.scale_log2;
-        float lsum = 0.0f;
-#pragma unroll
-        for (int b = 0; b < 2; ++b)
-#pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                const float e = __builtin_amdgcn_exp2f(fmaf(sacc[b][r], p.scale_log2, -msc));
-                sacc[b][r] = e;
-                lsum += e;
-            }
-        lrow += lsum;
+        const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
+        float lsum[2] = {0.0f, 0.0f};
 #pragma unroll
         for (int b = 0; b < 2; ++b)
 #pragma unroll
             for (int s2 = 0; s2 < 2; ++s2)
 #pragma unroll
-                for (int u = 0; u < 4; ++u)
-                    pf[b][s2][u] = pack_bf16(sacc[b][8 * s2 + 2 * u], sacc[b][8 * s2 + 2 * u + 1]);
+                for (int u = 0; u < 4; ++u) {
+                    const float e0 = __builtin_amdgcn_exp2f(fmaf(sacc[b][8 * s2 + 2 * u], p.scale_log2, -msc));
+                    const float e1 = __builtin_amdgcn_exp2f(fmaf(sacc[b][8 * s2 + 2 * u + 1], p.scale_log2, -msc));
+                    const uint32_t w2 = pack_bf16(e0, e1);
+                    pf[b][s2][u] = w2;
+                    lsum[u & 1] = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, w2), ones,
+                                                                  lsum[u & 1], false);
+                }
+        lrow += lsum[0] + lsum[1];
     };
 
-    auto apply_mask = [&](int t, floatx16 (&sacc)[2]) {
-        const int *kp = kpos_s[t % 3];
+    auto apply_mask = [&](int ksl, floatx16 (&sacc)[2]) {
+        const int *kp = kpos_s + ksl * KT;
 #pragma unroll
         for (int b = 0; b < 2; ++b)
 #pragma unroll
@@ -341,8 +371,8 @@ __global__ __launch_bounds__(512, 1) void link_attention_bf16(AttnParams p) {
     };
 
     // O^T += V^T P^T for one tile; V^T operands come from two transposing 8-byte LDS reads
-    auto pv = [&](int t, const u32x4 (&pf)[2][2]) {
-        const uint16_t *vb = vs[t & 3];
+    auto pv = [&](int vsl, const u32x4 (&pf)[2][2]) {
+        const uint16_t *vb = vs + vsl * VBUF;
         const int gi = lane >> 4, j = (lane >> 2) & 3, q = lane & 3;
 #pragma unroll
         for (int db = 0; db < NDB; ++db)
@@ -368,34 +398,49 @@ __global__ __launch_bounds__(512, 1) void link_attention_bf16(AttnParams p) {
     floatx16 sacc[2];
     u32x4 pf[2][2];
 
-    load_tile(0);
+    load_desc(0);
+    load_tile();
     load_rope();
-    store_tile(0);
-    load_tile(1);
+    store_tile(0, 0, 0);
+    load_desc(1);
+    load_tile();
     load_rope();
-    store_tile(1);
-    __syncthreads();
+    store_tile(1, 1, 1);
+    lds_barrier();
     qk(0, sacc);
-    load_tile(2);
-    if (group_b) __syncthreads();
+    load_desc(2);
+    load_tile();
+    if (group_b) lds_barrier();
 
+    // ring slots of tile t (K', positions: t % 3; V: t % 4) and of tiles t+1, t+2
+    int k_cur = 0, k_nxt = 1, k_st = 2, v_cur = 0;
     for (int t = 0; t < ntiles; ++t) {
-        // Y(t): softmax of tile t; staging of tile t+2; loads of tile t+3
-        if (mask_ring & (1u << (t % 3))) apply_mask(t, sacc);
+        // Y(t): softmax of tile t; staging of tile t+2; loads of tile t+3. The cos/sin loads of
+        // the staged keys go first so that the softmax hides their latency.
+        const bool stage = t + 2 < ntiles;
+        if (stage) {
+            load_rope();
+            load_desc(t + 3);
+        }
+        if (mask_ring & (1u << k_cur)) apply_mask(k_cur, sacc);
         rescale(softmax_max(sacc));
         softmax_exp(sacc, pf);
-        if (t + 2 < ntiles) {
-            load_rope();
-            store_tile(t + 2);
-            load_tile(t + 3);
+        if (stage) {
+            store_tile(k_st, v_cur ^ 2, t + 2);
+            load_tile();
         }
-        __syncthreads();
+        lds_barrier();
         // X(t): PV of tile t; QK^T of tile t+1
-        pv(t, pf);
-        if (t + 1 < ntiles) qk(t + 1, sacc);
-        __syncthreads();
+        pv(v_cur, pf);
+        if (t + 1 < ntiles) qk(k_nxt, sacc);
+        lds_barrier();
+        const int k_old = k_cur;
+        k_cur = k_nxt;
+        k_nxt = k_st;
+        k_st = k_old;
+        v_cur = (v_cur + 1) & 3;
     }
-    if (!group_b) __syncthreads();
+    if (!group_b) lds_barrier();
 
     // ---- epilogue: normalise, write the output (or this split's partial result)
     {

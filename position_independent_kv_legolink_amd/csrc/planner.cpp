@@ -153,6 +153,8 @@ pic_plan *build_plan(pic_store *s, const pic_request *reqs, int32_t n_reqs, cons
         // aim at about two items per compute unit, never below 8 key tiles per item
         max_pages = std::max<int64_t>(8 * ppt, align_up((total + 2 * s->num_cus - 1) / (2 * s->num_cus), ppt));
     }
+    // an item's page table is staged in LDS by the attention kernel
+    max_pages = std::min<int64_t>(max_pages, kMaxItemPages);
     std::vector<Item> split;
     for (const Item &it : items) {
         if (it.len <= max_pages) {
