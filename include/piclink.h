@@ -101,7 +101,8 @@ typedef struct {
  * pos_offset   absolute position of the first token of every request (>= 0)
  * recompute_all  select every row of every segment (full-recompute comparator)
  * split_pages  KV pages per attention work item: 0 = automatic, > 0 = at most
- *              that many, < 0 = never split a (row tile, KV head) */
+ *              that many, < 0 = split a (row tile, KV head) only where its key
+ *              range exceeds the kernel's limit of 2,048 pages per work item */
 typedef struct {
     int32_t k;
     int32_t block_level;
