@@ -234,12 +234,16 @@ def cpu_baseline(cfg, target_s):
     R = len(pos)
     q, k, v = gen.new_rows(cfg, 0, R)
     cores = int(os.environ.get("OMP_NUM_THREADS", os.cpu_count() or 1))
-    # calibrate on a few rows, then take as many evenly spread rows as fit the time target
-    probe = np.linspace(0, R - 1, 4).astype(np.int64)
-    t = time.perf_counter()
-    olink.link_attention(segs, cached, q, k, v, cfg.rope_theta, rows=probe)
-    per_row = (time.perf_counter() - t) / len(probe)
-    n = int(max(4, min(R, target_s / max(per_row, 1e-6))))
+    # calibrate on a few rows (two probe sizes remove the fixed cost of building the merged
+    # cache and rotating every key), then take as many evenly spread rows as fit the target
+    times = []
+    for n_probe in (4, 12):
+        probe = np.linspace(0, R - 1, n_probe).astype(np.int64)
+        t = time.perf_counter()
+        olink.link_attention(segs, cached, q, k, v, cfg.rope_theta, rows=probe)
+        times.append(time.perf_counter() - t)
+    per_row = max((times[1] - times[0]) / 8, 1e-6)
+    n = int(max(4, min(R, (target_s - times[0]) / per_row)))
     rows = np.unique(np.linspace(0, R - 1, n).astype(np.int64))
     t = time.perf_counter()
     olink.link_attention(segs, cached, q, k, v, cfg.rope_theta, rows=rows)
@@ -251,7 +255,7 @@ def cpu_baseline(cfg, target_s):
                        f"{cfg.num_q_heads} heads, fp64 with explicit loops; {dt:.1f} s")
 
 
-def traffic_from_profiles(attn_calls_per_step):
+def traffic_from_profiles(workload):
     """HBM bytes per attention launch from the committed counter summary, if it is current."""
     if not os.path.exists(TRAFFIC_FILE):
         return None
@@ -259,9 +263,48 @@ def traffic_from_profiles(attn_calls_per_step):
         t = json.load(open(TRAFFIC_FILE))
     except Exception:
         return None
-    if t.get("kernel_source_sha256_16") != kernel_hash():
+    if t.get("kernel_source_sha256_16") != kernel_hash() or t.get("workload") != workload:
         return None
     return t.get("hbm_bytes_per_launch")
+
+
+def _counter_rows(directory, counter):
+    import csv
+    import glob
+    files = glob.glob(os.path.join(directory, "**", "*counter_collection.csv"), recursive=True)
+    if not files:
+        raise SystemExit(f"no counter_collection.csv under {directory}")
+    out = []
+    for f in files:
+        for r in csv.DictReader(open(f)):
+            if r["Counter_Name"] == counter:
+                out.append((r["Kernel_Name"], float(r["Counter_Value"])))
+    return out
+
+
+def summarize_traffic(fetch_dir, write_dir, copy_mib, workload, out_json):
+    """Turn two rocprofv3 --pmc runs (FETCH_SIZE, WRITE_SIZE, KiB per dispatch) into HBM bytes per
+    attention launch, each scaled by what the same counter reads for the calibration copy."""
+    copy_bytes = copy_mib * (1 << 20)
+    res = {"workload": workload, "kernel_source_sha256_16": kernel_hash(), "copy_bytes": copy_bytes}
+    for name, d in (("fetch", fetch_dir), ("write", write_dir)):
+        counter = "FETCH_SIZE" if name == "fetch" else "WRITE_SIZE"
+        rows = _counter_rows(d, counter)
+        attn = [v for k, v in rows if "link_attention" in k]
+        copy = [v for k, v in rows if "elementwise" in k.lower() or "mul" in k.lower()]
+        if not attn or not copy:
+            raise SystemExit(f"{counter}: need attention and calibration-copy dispatches in {d}")
+        attn_kib = sum(attn) / len(attn)
+        copy_kib = max(copy)
+        scale = copy_bytes / (copy_kib * 1024.0)
+        res[f"{name}_kib_per_dispatch"] = round(attn_kib, 1)
+        res[f"copy_{name}_kib"] = round(copy_kib, 1)
+        res[f"{name}_scale"] = round(scale, 4)
+        res[f"{name}_bytes_per_launch"] = int(attn_kib * 1024 * scale)
+    res["hbm_bytes_per_launch"] = res["fetch_bytes_per_launch"] + res["write_bytes_per_launch"]
+    with open(out_json, "w") as f:
+        json.dump(res, f, indent=1)
+    print(json.dumps(res))
 
 
 def main():
@@ -271,11 +314,18 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="long50k_k32")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--cpu-seconds", type=float, default=20.0)
     ap.add_argument("--no-dense", action="store_true")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="also run one device copy of this size per step (counter calibration runs)")
+    ap.add_argument("--traffic-from", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
+                    help="summarise two rocprofv3 --pmc runs (FETCH_SIZE, WRITE_SIZE) into per-launch HBM bytes")
+    ap.add_argument("--traffic-out", default=TRAFFIC_FILE)
     args = ap.parse_args()
+    if args.traffic_from:
+        summarize_traffic(args.traffic_from[0], args.traffic_from[1], args.copy_probe_mib or 256, args.workload,
+                          args.traffic_out)
+        return
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
@@ -308,8 +358,9 @@ def main():
 
     ms_step, prof = time_steps(job, args.steps, args.warmup)
     if copy_src is not None:
+        # a plain elementwise kernel that reads and writes copy_probe_mib MiB each
         for _ in range(args.steps):
-            copy_dst.copy_(copy_src)
+            torch.mul(copy_src, 1.0, out=copy_dst)
         torch.cuda.synchronize()
     calls = max(prof["calls"], 1)
     attn_ms = prof["attention_ms"] / calls
@@ -321,7 +372,7 @@ def main():
     peak = PEAK_BF16_TFLOPS if cfg.dtype == "bf16" else PEAK_F32_TFLOPS
     achieved = flop / (attn_ms * 1e-3) / 1e12
     roofline = dict(bound="mfma", achieved=round(achieved, 2), peak=peak, unit="TFLOP/s",
-                    frac=round(achieved / peak, 4), traffic=traffic_from_profiles(1))
+                    frac=round(achieved / peak, 4), traffic=traffic_from_profiles(cfg.name))
 
     dense = None
     if not args.no_dense:
