@@ -73,7 +73,8 @@ typedef struct pic_plan pic_plan;
  *   head_dim      64 or 128
  *   page_size     tokens per page: 16, 32 or 64
  *   num_q_heads   a multiple of num_kv_heads, with Hq/Hkv in {1, 2, 4, 8}
- *   max_position  every linked position must be < max_position (RoPE table rows) */
+ *   max_position  every linked position must be < max_position (RoPE table rows);
+ *                 at most 4,194,304 */
 typedef struct {
     int32_t num_q_heads;
     int32_t num_kv_heads;

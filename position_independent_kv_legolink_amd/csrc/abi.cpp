@@ -58,7 +58,8 @@ void store_check_config(const pic_store_config &c) {
     if (c.num_pages <= 0) fail(PIC_ERR_INVALID, "num_pages must be positive");
     if (c.dtype != PIC_DTYPE_BF16 && c.dtype != PIC_DTYPE_F32) fail(PIC_ERR_INVALID, "dtype must be bf16 or f32");
     if (!(c.rope_theta > 0.0)) fail(PIC_ERR_INVALID, "rope_theta must be positive");
-    if (c.max_position <= 0) fail(PIC_ERR_INVALID, "max_position must be positive");
+    if (c.max_position <= 0 || c.max_position > kMaxPosition)
+        fail(PIC_ERR_INVALID, "max_position must be in [1, " + std::to_string(kMaxPosition) + "]");
 }
 
 int32_t store_alloc_page(pic_store *s) {

@@ -16,6 +16,8 @@
 #include <math.h>
 #include <stdint.h>
 
+#include <type_traits>
+
 #include "launch.h"
 
 namespace piclink {
@@ -30,12 +32,10 @@ typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef int32_t i32x4 __attribute__((ext_vector_type(4)));
 
-// Scores are kept in raw q.k units; the running maximum is only moved when a
-// row's maximum grows by more than 2^kRescaleLog2 in softmax units, so the
-// accumulator is rescaled rarely. Exact for any stale maximum: exponentials
-// stay <= 2^kRescaleLog2.
+// The running softmax maximum is moved lazily: exact for any stale maximum as long as the
+// exponentials stay bounded, here by 2^kRescaleLog2, so the output accumulator is rescaled rarely.
 constexpr float kRescaleLog2 = 8.0f;
-constexpr float kInitMax = -1.0e30f;
+constexpr float kInitMax = -1.0e30f;    // fp32 kernel: maximum before the first key
 constexpr int kNeverAttended = INT_MAX;
 
 __device__ __forceinline__ float bf_lo(uint32_t w) { return __uint_as_float(w << 16); }
@@ -77,6 +77,15 @@ struct AttnParams {
     float scale;                // 1 / sqrt(d)
 };
 
+// A callable that issues piece j of a tile's loads, with the number of pieces as a constant
+// (zero: no loads).
+template <int N, typename F>
+struct Loads {
+    static constexpr int count = N;
+    F f;
+    __device__ __forceinline__ void operator()(int j) const { f(j); }
+};
+
 // Rotate 8 bf16 pairs (x_i, x_{i+d/2}) by (cos, sin); returns rounded bf16 words.
 __device__ __forceinline__ void rope8_bf16(const u32x4 &lo, const u32x4 &hi, const floatx4 c[2],
                                            const floatx4 s[2], u32x4 &olo, u32x4 &ohi) {
@@ -100,17 +109,21 @@ __device__ __forceinline__ void rope8_bf16(const u32x4 &lo, const u32x4 &hi, con
 // Ping-pong schedule: waves 0-3 (group A, one per SIMD) and waves 4-7 (group B) run the same
 // per-tile sequence one phase apart, so that one wave's MFMA phase meets the other wave's VALU
 // phase on every SIMD:
-//   Y(t): softmax of tile t, RoPE + LDS staging of tile t+2, global loads of tile t+3  (VALU)
-//   X(t): PV of tile t, QK^T of tile t+1                                             (MFMA)
+//   Y(t): RoPE + LDS staging of tile t+2, then the softmax of tile t with the global loads of
+//         tile t+3 spread between its exponentials                                  (VALU)
+//   X(t): PV of tile t, QK^T of tile t+1 (MFMAs and their LDS operand reads only)   (MFMA)
 // with a work-group barrier after each phase; group B passes one extra barrier at the start
 // (and group A one at the end), so B's phase k overlaps A's phase k+1. Tile buffers are deep
-// enough for the one-phase skew: K' and key positions x3, V x4.
+// enough for the one-phase skew: K' and key positions x3, V x4. Q carries the softmax scale and
+// log2(e), and the running maximum enters S^T through one bias MFMA per 32-key block, so the
+// common softmax path is exp2, a row sum and the bf16 packing.
 template <int D>
 __global__ __launch_bounds__(512, 1) void link_attention_bf16(AttnParams p) {
     constexpr int NT = 512;
     constexpr int KT = kKeysPerTile;
     constexpr int KS = D + 8;          // K' row stride in LDS (bf16): conflict-free A-fragment reads
-    constexpr int VS = D + 16;         // V row stride in LDS (bf16): conflict-free transposing reads
+    constexpr int VS = D + 32;         // V row stride in LDS (bf16): 16 banks mod 64, so the 4 keys x 2 column
+                                       // halves of one transposing read cover all 64 banks
     constexpr int NS = D / 16;         // k-steps of QK^T
     constexpr int NDB = D / 32;        // 32-wide d blocks of PV
     constexpr int KPAIRS = KT * (D / 16);          // (key, 8 dims of each half) per tile
@@ -124,7 +137,7 @@ __global__ __launch_bounds__(512, 1) void link_attention_bf16(AttnParams p) {
     __shared__ __attribute__((aligned(16))) uint16_t ks[3 * KBUF];
     __shared__ __attribute__((aligned(16))) uint16_t vs[4 * VBUF];
     __shared__ __attribute__((aligned(16))) int kpos_s[3 * KT];
-    __shared__ int pg_phys[kMaxItemPages], pg_pos0[kMaxItemPages], pg_valid[kMaxItemPages];
+    __shared__ int pg_phys[kMaxItemPages], pg_pv[kMaxItemPages];
 
     const WorkDesc w = p.work[blockIdx.x];
     if (w.n_rows <= 0) return;
@@ -135,8 +148,6 @@ __global__ __launch_bounds__(512, 1) void link_attention_bf16(AttnParams p) {
     const int page_size = 1 << p.pshift;
     const int ppt = KT >> p.pshift;
     const PageDesc *pg = p.pages + w.page_base;
-    const uint16_t *kpool = static_cast<const uint16_t *>(p.k_pool);
-    const uint16_t *vpool = static_cast<const uint16_t *>(p.v_pool);
     const int64_t head_off = (int64_t)w.kv_head * page_size * D;
 
     // ---- rotated Q fragments, held for the whole key range
@@ -165,6 +176,12 @@ __global__ __launch_bounds__(512, 1) void link_attention_bf16(AttnParams p) {
             c[1] = *reinterpret_cast<const floatx4 *>(cs + e0 + 4);
             sn[0] = *reinterpret_cast<const floatx4 *>(cs + D / 2 + e0);
             sn[1] = *reinterpret_cast<const floatx4 *>(cs + D / 2 + e0 + 4);
+            // the softmax scale and log2(e) ride on Q: scores come out of the MFMA in log2 units
+#pragma unroll
+            for (int h = 0; h < 2; ++h) {
+                c[h] *= p.scale_log2;
+                sn[h] *= p.scale_log2;
+            }
             rope8_bf16(lo, hi, c, sn, qf[s], qf[s + NS / 2]);
         }
     }
@@ -174,28 +191,54 @@ __global__ __launch_bounds__(512, 1) void link_attention_bf16(AttnParams p) {
     int k_pos[NKP];
     floatx4 k_c[NKP][2], k_s[NKP][2];
     u32x4 v_r[NVC];
+    u32x4 k_olo[NKP], k_ohi[NKP];      // rotated K halves on their way to LDS
     int kp_stage = kNeverAttended;
     unsigned mask_ring = 7u;           // bit (t % 3): tile t needs the causal/padding mask
 
-    // The work item's page table is staged in LDS once. The descriptors of a tile's KT / page
-    // pages are read from LDS at the start of the VALU phase (their latency hides behind the
-    // softmax) and moved to SGPRs where the global loads use them. Keys of one wave's K pieces
-    // (and of each of its V pieces) lie in one page (page >= 16 tokens): each piece picks its page
-    // with a scalar select. Keys past the work item's range or in page padding read real, finite
-    // pool data (the last page, or the zeroed padding slots) and are removed by the mask
-    // (position kNeverAttended).
+    // Loop-invariant byte offsets of this thread's pieces inside a page (and inside a cos/sin
+    // row), so that each load is a scalar page base plus a 32-bit lane offset.
+    const char *kpool_b = static_cast<const char *>(p.k_pool);
+    const char *vpool_b = static_cast<const char *>(p.v_pool);
+    const char *rope_b = reinterpret_cast<const char *>(p.rope);
+    const uint32_t page_bytes = (uint32_t)p.page_elems * 2u;
+    uint32_t k_loff[NKP], k_cs_off[NKP], v_loff[NVC];
+    int k_slot[NKP];
+#pragma unroll
+    for (int u = 0; u < NKP; ++u) {
+        const int pi = tid + NT * u;
+        const int key = pi / (D / 16), c = pi % (D / 16);
+        k_slot[u] = key & (page_size - 1);
+        k_loff[u] = (uint32_t)(head_off + k_slot[u] * D + 8 * c) * 2u;
+        k_cs_off[u] = (uint32_t)(8 * c) * 4u;
+    }
+#pragma unroll
+    for (int u = 0; u < NVC; ++u) {
+        const int pi = tid + NT * u;
+        const int key = pi / (D / 8), c16 = pi % (D / 8);
+        v_loff[u] = (uint32_t)(head_off + (key & (page_size - 1)) * D + 8 * c16) * 2u;
+    }
+
+    // The work item's page table is staged in LDS once: the physical page, and the page's first
+    // position and valid token count packed as pos0 << 7 | valid (pos0 < 2^22, valid <= 64).
+    // The descriptors of a tile's KT / page pages are read from LDS early in the MFMA phase and
+    // moved to SGPRs where the loads of the same phase use them. Keys of one wave's K pieces (and
+    // of each of its V pieces) lie in one page (page >= 16 tokens). Keys past the work item's
+    // range or in page padding read real, finite pool data (the last page, or the zeroed padding
+    // slots) and are removed by the mask (position kNeverAttended).
     const int n_pages = w.page_end - w.page_begin;
     for (int i = tid; i < n_pages; i += NT) {
         const PageDesc d = pg[w.page_begin + i];
         pg_phys[i] = d.phys;
-        pg_pos0[i] = d.pos0;
-        pg_valid[i] = d.valid;
+        pg_pv[i] = (d.pos0 << 7) | d.valid;
     }
     lds_barrier();
     // descriptor values read ahead from LDS: the wave's K page and V pages (uniform) and the
-    // page of key `lane` (for the mask positions)
-    int rk_phys[NKP], rk_pos0[NKP], rk_valid[NKP], rv_phys[NVC], rl_pos0, rl_valid;
-    auto load_desc = [&](int t) {
+    // page of key `lane` (for the mask positions). The reads are unconditional (clamped to the
+    // last page) and the range test is applied where the values are used: a conditional read
+    // becomes a branch whose join waits for the LDS result at once.
+    int rk_phys[NKP], rk_pv[NKP], rv_phys[NVC], rl_pv;
+    bool rk_in[NKP], rl_in;
+    auto load_desc = [&](int t) __attribute__((always_inline)) {
         const int r0 = t * ppt;
         const int wv = __builtin_amdgcn_readfirstlane(wave);
 #pragma unroll
@@ -203,73 +246,96 @@ __global__ __launch_bounds__(512, 1) void link_attention_bf16(AttnParams p) {
             const int rq = r0 + (((NT * u + 64 * wv) / (D / 16)) >> p.pshift);
             const int r = min(rq, n_pages - 1);
             rk_phys[u] = pg_phys[r];
-            rk_pos0[u] = pg_pos0[r];
-            rk_valid[u] = rq < n_pages ? pg_valid[r] : 0;
+            rk_pv[u] = pg_pv[r];
+            rk_in[u] = rq < n_pages;
         }
 #pragma unroll
         for (int u = 0; u < NVC; ++u)
             rv_phys[u] = pg_phys[min(r0 + (((NT * u + 64 * wv) / (D / 8)) >> p.pshift), n_pages - 1)];
         const int rq = r0 + (lane >> p.pshift);
-        const int r = min(rq, n_pages - 1);
-        rl_pos0 = pg_pos0[r];
-        rl_valid = rq < n_pages ? pg_valid[r] : 0;
+        rl_pv = pg_pv[min(rq, n_pages - 1)];
+        rl_in = rq < n_pages;
     };
-    auto load_tile = [&]() {
+    // the loads of one tile, one instruction per piece so that they can be spread between MFMAs:
+    // piece 0 takes the page descriptors into SGPRs, sets the keys' positions and loads the K low
+    // halves, 1 the K high halves, then V, then the cos/sin rows at the keys' positions
+    constexpr int NLOAD = 2 + NVC + 4;
+    const char *k_page[NKP];
+    auto load_piece = [&](int j) __attribute__((always_inline)) {
+        if (j == 0) {
 #pragma unroll
-        for (int u = 0; u < NKP; ++u) {
-            const int pi = tid + NT * u;
-            const int key = pi / (D / 16), c = pi % (D / 16);
-            const int phys = __builtin_amdgcn_readfirstlane(rk_phys[u]);
-            const int pos0 = __builtin_amdgcn_readfirstlane(rk_pos0[u]);
-            const int valid = __builtin_amdgcn_readfirstlane(rk_valid[u]);
-            const int slot = key & (page_size - 1);
-            const bool ok = (KPAIRS % NT == 0 || pi < KPAIRS) && slot < valid;
-            const int64_t base = (int64_t)phys * p.page_elems + head_off + (int64_t)slot * D;
-            k_lo[u] = *reinterpret_cast<const u32x4 *>(kpool + base + 8 * c);
-            k_hi[u] = *reinterpret_cast<const u32x4 *>(kpool + base + D / 2 + 8 * c);
-            k_pos[u] = ok ? pos0 + slot : pos0;
-        }
+            for (int u = 0; u < NKP; ++u) {
+                const uint32_t phys = (uint32_t)__builtin_amdgcn_readfirstlane(rk_phys[u]);
+                const int pv = __builtin_amdgcn_readfirstlane(rk_pv[u]);
+                const int pos0 = pv >> 7, valid = pv & 127;
+                const int pi = tid + NT * u;
+                const bool ok = (KPAIRS % NT == 0 || pi < KPAIRS) && rk_in[u] && k_slot[u] < valid;
+                k_pos[u] = ok ? pos0 + k_slot[u] : pos0;
+                k_page[u] = kpool_b + (uint64_t)phys * page_bytes;
+                k_lo[u] = *reinterpret_cast<const u32x4 *>(k_page[u] + k_loff[u]);
+            }
+            const int slot = lane & (page_size - 1);
+            kp_stage = rl_in && slot < (rl_pv & 127) ? (rl_pv >> 7) + slot : kNeverAttended;
+        } else if (j == 1) {
 #pragma unroll
-        for (int u = 0; u < NVC; ++u) {
-            const int pi = tid + NT * u;
-            const int key = pi / (D / 8), c16 = pi % (D / 8);
-            const int slot = key & (page_size - 1);
-            const int64_t base =
-                (int64_t)__builtin_amdgcn_readfirstlane(rv_phys[u]) * p.page_elems + head_off + (int64_t)slot * D;
-            v_r[u] = *reinterpret_cast<const u32x4 *>(vpool + base + 8 * c16);
+            for (int u = 0; u < NKP; ++u) k_hi[u] = *reinterpret_cast<const u32x4 *>(k_page[u] + k_loff[u] + D);
+        } else if (j < 2 + NVC) {
+            const int u = j - 2;
+            const char *page = vpool_b + (uint64_t)(uint32_t)__builtin_amdgcn_readfirstlane(rv_phys[u]) * page_bytes;
+            v_r[u] = *reinterpret_cast<const u32x4 *>(page + v_loff[u]);
+        } else {
+            const int q = j - 2 - NVC;   // 0: cos lo, 1: cos hi, 2: sin lo, 3: sin hi
+#pragma unroll
+            for (int u = 0; u < NKP; ++u) {
+                const uint32_t off = (uint32_t)k_pos[u] * (uint32_t)(D * 4) + k_cs_off[u];
+                const floatx4 v = *reinterpret_cast<const floatx4 *>(rope_b + off + (q >> 1) * (D * 2) + (q & 1) * 16);
+                if (q < 2) k_c[u][q & 1] = v;
+                else k_s[u][q & 1] = v;
+            }
         }
-        const int slot = lane & (page_size - 1);
-        kp_stage = slot < rl_valid ? rl_pos0 + slot : kNeverAttended;
+    };
+    auto load_tile = [&]() __attribute__((always_inline)) {
+#pragma unroll
+        for (int j = 0; j < NLOAD; ++j) load_piece(j);
     };
 
-    // cos/sin of the staged keys; issued ahead of the MFMAs that hide their latency
-    auto load_rope = [&]() {
+    // staging of one tile, in pieces that fit between MFMAs: the rotation of word wd (two
+    // (x_i, x_{i+d/2}) pairs) of every K piece, then the LDS writes. K', V and key positions of a
+    // tile share ring slot sl (of 3); the mask bit of the slot records whether any key of the tile
+    // lies after the work item's first row.
+    // step k rotates pair k & 1 of word k >> 1 (the even pair is held until the odd one is ready
+    // to be packed with it)
+    float rx[NKP], ry[NKP];
+    auto rope_step = [&](int k) __attribute__((always_inline)) {
+        const int wd = k >> 1, h = k & 1;
 #pragma unroll
         for (int u = 0; u < NKP; ++u) {
-            const int pi = tid + NT * u;
-            const int c = pi % (D / 16);
-            const float *cs = p.rope + (int64_t)k_pos[u] * D + 8 * c;
-            k_c[u][0] = *reinterpret_cast<const floatx4 *>(cs);
-            k_c[u][1] = *reinterpret_cast<const floatx4 *>(cs + 4);
-            k_s[u][0] = *reinterpret_cast<const floatx4 *>(cs + D / 2);
-            k_s[u][1] = *reinterpret_cast<const floatx4 *>(cs + D / 2 + 4);
+            const float x = h ? bf_hi(k_lo[u][wd]) : bf_lo(k_lo[u][wd]);
+            const float y = h ? bf_hi(k_hi[u][wd]) : bf_lo(k_hi[u][wd]);
+            const float c = k_c[u][wd >> 1][2 * (wd & 1) + h], sn = k_s[u][wd >> 1][2 * (wd & 1) + h];
+            const float xr = fmaf(x, c, -y * sn), yr = fmaf(y, c, x * sn);
+            if (h == 0) {
+                rx[u] = xr;
+                ry[u] = yr;
+            } else {
+                k_olo[u][wd] = pack_bf16(rx[u], xr);
+                k_ohi[u][wd] = pack_bf16(ry[u], yr);
+            }
         }
     };
-
-    // slots: K' and key positions in ring slot ksl (of 3), V in slot vsl (of 4)
-    auto store_tile = [&](int ksl, int vsl, int t) {
-        uint16_t *kb = ks + ksl * KBUF;
-        uint16_t *vb = vs + vsl * VBUF;
+    auto write_k = [&](int sl) __attribute__((always_inline)) {
+        uint16_t *kb = ks + sl * KBUF;
 #pragma unroll
         for (int u = 0; u < NKP; ++u) {
             const int pi = tid + NT * u;
             if (KPAIRS % NT != 0 && pi >= KPAIRS) break;
             const int key = pi / (D / 16), c = pi % (D / 16);
-            u32x4 olo, ohi;
-            rope8_bf16(k_lo[u], k_hi[u], k_c[u], k_s[u], olo, ohi);
-            *reinterpret_cast<u32x4 *>(&kb[key * KS + 8 * c]) = olo;
-            *reinterpret_cast<u32x4 *>(&kb[key * KS + D / 2 + 8 * c]) = ohi;
+            *reinterpret_cast<u32x4 *>(&kb[key * KS + 8 * c]) = k_olo[u];
+            *reinterpret_cast<u32x4 *>(&kb[key * KS + D / 2 + 8 * c]) = k_ohi[u];
         }
+    };
+    auto write_v = [&](int vsl, int sl) __attribute__((always_inline)) {
+        uint16_t *vb = vs + vsl * VBUF;
 #pragma unroll
         for (int u = 0; u < NVC; ++u) {
             const int pi = tid + NT * u;
@@ -277,14 +343,20 @@ __global__ __launch_bounds__(512, 1) void link_attention_bf16(AttnParams p) {
             const int key = pi / (D / 8), c16 = pi % (D / 8);
             *reinterpret_cast<u32x4 *>(&vb[key * VS + 8 * c16]) = v_r[u];
         }
-        kpos_s[ksl * KT + lane] = kp_stage;   // every wave writes the same 64 values
-        const unsigned bit = 1u << ksl;
+        kpos_s[sl * KT + lane] = kp_stage;   // every wave writes the same 64 values
+        const unsigned bit = 1u << sl;
         mask_ring = __any(kp_stage > w.rpos_min) ? (mask_ring | bit) : (mask_ring & ~bit);
+    };
+    auto store_tile = [&](int sl, int vsl) __attribute__((always_inline)) {
+#pragma unroll
+        for (int r = 0; r < 8; ++r) rope_step(r);
+        write_k(sl);
+        write_v(vsl, sl);
     };
 
     // S^T of one tile: two 32-key blocks, NS k-steps each
-    auto qk = [&](int ksl, floatx16 (&sacc)[2]) {
-        const uint16_t *kb = ks + ksl * KBUF;
+    auto qk = [&](int sl, floatx16 (&sacc)[2]) {
+        const uint16_t *kb = ks + sl * KBUF;
 #pragma unroll
         for (int b = 0; b < 2; ++b)
 #pragma unroll
@@ -304,142 +376,221 @@ __global__ __launch_bounds__(512, 1) void link_attention_bf16(AttnParams p) {
     for (int db = 0; db < NDB; ++db)
 #pragma unroll
         for (int r = 0; r < 16; ++r) oacc[db][r] = 0.0f;
-    float mrow = kInitMax, lrow = 0.0f;
+    // Online softmax with a lazily moved maximum carried as an MFMA bias. mrow is the running
+    // maximum in log2 units of the scaled scores, kept on bf16 values, and one extra MFMA per
+    // 32-key block adds -mrow to every S^T entry before the K'Q'^T k-steps (A = a unit vector
+    // along one k, B = -mrow of each row along the same k), so the accumulators hold s - mrow and
+    // the weights are plain exp2 of them. mrow moves only when a lane's partial sum of one tile's
+    // weights leaves (0, 2^kRescaleLog2] (a weight may exceed 2^kRescaleLog2, or overflowed),
+    // while the row has no maximum yet, or on tiles that need the causal/padding mask.
+    float mrow = 0.0f, lrow = 0.0f;
+    bool have_max = false;
+    const bf16x8 bias_a = __builtin_bit_cast(bf16x8, u32x4{lg == 0 ? 0x3f80u : 0u, 0u, 0u, 0u});   // e_0
+    u32x4 bias_b = {0u, 0u, 0u, 0u};   // -mrow at k = 0 (lanes 0-31 hold k 0..7 of their row)
+    floatx16 sacc[2];   // S^T - mrow of the tile in flight
+    u32x4 pf[2][2];     // its bf16 softmax weights, the B operands of PV
 
-    // online softmax, part 1: row maximum over the tile and the running maximum (moved only when
-    // it grows by more than 2^kRescaleLog2); returns the factor that rescales the running sums
-    auto softmax_max = [&](floatx16 (&sacc)[2]) -> float {
-        float mx = sacc[0][0];
+    auto tile_sum = [&](const float (&e)[2][16]) -> float {
+        float part[4];
 #pragma unroll
-        for (int b = 0; b < 2; ++b)
+        for (int i = 0; i < 4; ++i) {
+            part[i] = e[i >> 1][8 * (i & 1)];
 #pragma unroll
-            for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sacc[b][r]);
-        {
-            const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(mx), __float_as_uint(mx), false, false);
-            mx = fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1]));
+            for (int r = 1; r < 8; ++r) part[i] += e[i >> 1][8 * (i & 1) + r];
         }
-        const bool upd = (mx - mrow) * p.scale_log2 > kRescaleLog2;
-        const float mnew = upd ? mx : mrow;
-        const float alpha = __builtin_amdgcn_exp2f((mrow - mnew) * p.scale_log2);
-        mrow = mnew;
-        lrow *= alpha;
-        return alpha;
+        return (part[0] + part[1]) + (part[2] + part[3]);
     };
-
-    // part 2: exponentials straight into the bf16 P fragments; the row sum adds the rounded
-    // weights (v_dot2 against (1, 1)), i.e. exactly the weights the PV MFMA multiplies
-    auto softmax_exp = [&](const floatx16 (&sacc)[2], u32x4 (&pf)[2][2]) {
-        const float msc = mrow * p.scale_log2;
-        const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
-        float lsum[2] = {0.0f, 0.0f};
-#pragma unroll
-        for (int b = 0; b < 2; ++b)
-#pragma unroll
-            for (int s2 = 0; s2 < 2; ++s2)
-#pragma unroll
-                for (int u = 0; u < 4; ++u) {
-                    const float e0 = __builtin_amdgcn_exp2f(fmaf(sacc[b][8 * s2 + 2 * u], p.scale_log2, -msc));
-                    const float e1 = __builtin_amdgcn_exp2f(fmaf(sacc[b][8 * s2 + 2 * u + 1], p.scale_log2, -msc));
-                    const uint32_t w2 = pack_bf16(e0, e1);
-                    pf[b][s2][u] = w2;
-                    lsum[u & 1] = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, w2), ones,
-                                                                  lsum[u & 1], false);
-                }
-        lrow += lsum[0] + lsum[1];
-    };
-
-    auto apply_mask = [&](int ksl, floatx16 (&sacc)[2]) {
-        const int *kp = kpos_s + ksl * KT;
+    // the row sum adds the fp32 weights with plain adds (a v_dot2 shares the matrix pipe and
+    // would stall behind the other wave's MFMAs)
+    auto apply_mask = [&](int sl) __attribute__((always_inline)) {
+        const int *kp = kpos_s + sl * KT;
 #pragma unroll
         for (int b = 0; b < 2; ++b)
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
                 const i32x4 kp4 = *reinterpret_cast<const i32x4 *>(&kp[b * 32 + 8 * i + 4 * lg]);
 #pragma unroll
-                for (int j = 0; j < 4; ++j)
-                    if (kp4[j] > rpos) sacc[b][4 * i + j] = -INFINITY;
+                for (int j = 0; j < 4; ++j) sacc[b][4 * i + j] = kp4[j] > rpos ? -INFINITY : sacc[b][4 * i + j];
             }
     };
 
-    auto rescale = [&](float alpha) {
-        if (__any(alpha != 1.0f)) {
+    // `loads(j)` issues load piece j of the next tile; the pieces are spread between the
+    // exponentials so that the wave group's loads do not queue up in the vector memory pipeline
+    auto softmax = [&](bool masked, int kc, auto loads) __attribute__((always_inline)) {
+        constexpr int NL = decltype(loads)::count;
+        float e[2][16];
+        float lsum = 0.0f;
+        bool exact = masked;
+        if (!masked) {
 #pragma unroll
-            for (int db = 0; db < NDB; ++db)
-#pragma unroll
-                for (int r = 0; r < 16; ++r) oacc[db][r] *= alpha;
+            for (int i = 0; i < 32; ++i) {
+                e[i >> 4][i & 15] = __builtin_amdgcn_exp2f(sacc[i >> 4][i & 15]);
+                if (NL > 0 && (i & 3) == 3 && (i >> 2) < NL) {
+                    loads(i >> 2);
+                    __builtin_amdgcn_sched_barrier(0);
+                }
+            }
+            lsum = tile_sum(e);
+            const bool ok = have_max && lsum <= (float)(1 << (int)kRescaleLog2);   // false for inf, NaN
+            exact = __any(!ok);
         }
-    };
-
-    // O^T += V^T P^T for one tile; V^T operands come from two transposing 8-byte LDS reads
-    auto pv = [&](int vsl, const u32x4 (&pf)[2][2]) {
-        const uint16_t *vb = vs + vsl * VBUF;
-        const int gi = lane >> 4, j = (lane >> 2) & 3, q = lane & 3;
+        if (exact) {
+            if (masked) {
 #pragma unroll
-        for (int db = 0; db < NDB; ++db)
+                for (int j = 0; j < NL; ++j) loads(j);
+                apply_mask(kc);
+            }
+            // the tile's maximum relative to mrow, over both lane halves of the row
+            float mx = sacc[0][0];
 #pragma unroll
             for (int b = 0; b < 2; ++b)
 #pragma unroll
-                for (int s2 = 0; s2 < 2; ++s2) {
-                    const int key = b * 32 + 16 * s2 + 4 * lg + j;
-                    const int d = db * 32 + 16 * (gi & 1) + 4 * q;
-                    typedef short v4s __attribute__((ext_vector_type(4)));
-                    const v4s lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                        (__attribute__((address_space(3))) v4s *)(vb + key * VS + d));
-                    const v4s hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                        (__attribute__((address_space(3))) v4s *)(vb + (key + 8) * VS + d));
-                    const bf16x8 a = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
-                    oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, __builtin_bit_cast(bf16x8, pf[b][s2]),
-                                                                       oacc[db], 0, 0, 0);
+                for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sacc[b][r]);
+            const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(mx), __float_as_uint(mx), false, false);
+            mx = fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1]));
+            float target = mrow;
+            bool first = false;
+            if (mx != -INFINITY) {            // the row sees a key of this tile
+                if (!have_max) {
+                    target = mrow + mx;       // nothing accumulated yet
+                    first = true;
+                    have_max = true;
+                } else if (mx > 0.0f) {
+                    target = mrow + mx;
                 }
+            }
+            // the new maximum is a bf16 value (it enters the MFMA as a bf16 operand); the shift
+            // between two bf16 values is exact in fp32
+            const uint32_t tb = pack_bf16(-target, 0.0f) & 0xffffu;
+            const float mnew = -bf_lo(tb);
+            const float shift = mnew - mrow;
+            const float alpha = first ? 1.0f : __builtin_amdgcn_exp2f(-shift);
+            mrow = mnew;
+            bias_b[0] = lg == 0 ? tb : 0u;
+#pragma unroll
+            for (int b = 0; b < 2; ++b)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) e[b][r] = __builtin_amdgcn_exp2f(sacc[b][r] - shift);
+            lsum = tile_sum(e);
+            lrow *= alpha;
+            if (__any(alpha != 1.0f)) {
+#pragma unroll
+                for (int db = 0; db < NDB; ++db)
+#pragma unroll
+                    for (int r = 0; r < 16; ++r) oacc[db][r] *= alpha;
+            }
+        }
+#pragma unroll
+        for (int b = 0; b < 2; ++b)
+#pragma unroll
+            for (int s2 = 0; s2 < 2; ++s2)
+#pragma unroll
+                for (int u = 0; u < 4; ++u) pf[b][s2][u] = pack_bf16(e[b][8 * s2 + 2 * u], e[b][8 * s2 + 2 * u + 1]);
+        lrow += lsum;
+    };
+
+    // X phase: O^T += V^T P^T for tile t (V^T operands from pairs of transposing 8-byte LDS
+    // reads), then S^T = K' Q'^T for tile t+1. Only MFMAs and their operand reads: a wave issues
+    // one instruction per four cycles at best, so every other instruction in this phase would
+    // delay the MFMAs. Every MFMA's LDS operand is read three MFMAs ahead; the slots are
+    // separated by scheduling barriers, so the order below is the issue order.
+    typedef short v4s __attribute__((ext_vector_type(4)));
+    constexpr int NPV = 4 * NDB;       // PV MFMAs per tile
+    constexpr int NQK = 2 * NS;        // QK^T k-step MFMAs per tile
+    constexpr int NBIAS = 2;           // bias MFMAs (one per 32-key block) ahead of them
+    constexpr int AHEAD = 3;
+    v4s vlo[NPV], vhi[NPV];
+    bf16x8 ka[NQK];
+    auto xphase = [&](int vsl, int ksl, auto with_qk) __attribute__((always_inline)) {
+        constexpr bool QK = decltype(with_qk)::value;
+        constexpr int NM = NPV + (QK ? NBIAS + NQK : 0);
+        const int gi = lane >> 4, jj = (lane >> 2) & 3, qq = lane & 3;
+        const uint16_t *vb = vs + vsl * VBUF + (4 * lg + jj) * VS + 16 * (gi & 1) + 4 * qq;
+        const uint16_t *kb = ks + ksl * KBUF + ln * KS + 8 * lg;
+        auto read = [&](int i) __attribute__((always_inline)) {
+            if (i < NPV) {
+                const int db = i >> 2, b = (i >> 1) & 1, s2 = i & 1;
+                const uint16_t *a = vb + (b * 32 + 16 * s2) * VS + db * 32;
+                vlo[i] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) v4s *)a);
+                vhi[i] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                    (__attribute__((address_space(3))) v4s *)(a + 8 * VS));
+            } else if (i >= NPV + NBIAS) {
+                const int j = i - NPV - NBIAS, s = j >> 1, b = j & 1;
+                ka[j] = *reinterpret_cast<const bf16x8 *>(kb + b * 32 * KS + 16 * s);
+            }
+        };
+        auto mma = [&](int i) __attribute__((always_inline)) {
+            if (i < NPV) {
+                const int db = i >> 2, b = (i >> 1) & 1, s2 = i & 1;
+                const bf16x8 a = __builtin_bit_cast(bf16x8, __builtin_shufflevector(vlo[i], vhi[i], 0, 1, 2, 3, 4, 5, 6, 7));
+                oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, __builtin_bit_cast(bf16x8, pf[b][s2]), oacc[db],
+                                                                   0, 0, 0);
+            } else if (i < NPV + NBIAS) {
+                const floatx16 zero = {};
+                sacc[i - NPV] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bias_a, __builtin_bit_cast(bf16x8, bias_b), zero,
+                                                                        0, 0, 0);
+            } else {
+                const int j = i - NPV - NBIAS, s = j >> 1, b = j & 1;
+                sacc[b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[j], __builtin_bit_cast(bf16x8, qf[s]), sacc[b], 0, 0, 0);
+            }
+        };
+#pragma unroll
+        for (int i = 0; i < AHEAD; ++i) read(i);
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int i = 0; i < NM; ++i) {
+            mma(i);
+            if (i + AHEAD < NM) read(i + AHEAD);
+            __builtin_amdgcn_sched_barrier(0);
+        }
     };
 
     const int ntiles = (w.page_end - w.page_begin + ppt - 1) / ppt;
     const bool group_b = wave >= 4;
-    floatx16 sacc[2];
-    u32x4 pf[2][2];
 
     load_desc(0);
     load_tile();
-    load_rope();
-    store_tile(0, 0, 0);
+    store_tile(0, 0);
     load_desc(1);
     load_tile();
-    load_rope();
-    store_tile(1, 1, 1);
+    store_tile(1, 1);
     lds_barrier();
     qk(0, sacc);
     load_desc(2);
     load_tile();
+    load_desc(3);
     if (group_b) lds_barrier();
 
-    // ring slots of tile t (K', positions: t % 3; V: t % 4) and of tiles t+1, t+2
-    int k_cur = 0, k_nxt = 1, k_st = 2, v_cur = 0;
-    for (int t = 0; t < ntiles; ++t) {
-        // Y(t): softmax of tile t; staging of tile t+2; loads of tile t+3. The cos/sin loads of
-        // the staged keys go first so that the softmax hides their latency.
-        const bool stage = t + 2 < ntiles;
-        if (stage) {
-            load_rope();
-            load_desc(t + 3);
-        }
-        if (mask_ring & (1u << k_cur)) apply_mask(k_cur, sacc);
-        rescale(softmax_max(sacc));
-        softmax_exp(sacc, pf);
-        if (stage) {
-            store_tile(k_st, v_cur ^ 2, t + 2);
-            load_tile();
-        }
+    // ring slots of tiles t, t+1, t+2: K' and key positions in a ring of 3, V in a ring of 4 (the
+    // one-phase skew between the wave groups keeps a V tile in use one phase longer)
+    int kc = 0, kn = 1, ks2 = 2, vc = 0;
+    // one tile. Y(t): RoPE + LDS staging of tile t+2 from the registers loaded one step earlier,
+    // the loads of tile t+3 into the freed registers (a whole step ahead of their use), then the
+    // softmax of tile t. X(t): PV of tile t, QK^T of tile t+1, and the page descriptors of the
+    // next step's loads.
+    auto step = [&](int t, auto next_qk, auto staging, auto next_staging) __attribute__((always_inline)) {
+        constexpr bool STAGE = decltype(staging)::value;
+        if constexpr (STAGE) store_tile(ks2, (vc + 2) & 3);
+        softmax((mask_ring >> kc) & 1u, kc, Loads<STAGE ? NLOAD : 0, decltype(load_piece) &>{load_piece});
+        __builtin_amdgcn_sched_barrier(0);
         lds_barrier();
-        // X(t): PV of tile t; QK^T of tile t+1
-        pv(v_cur, pf);
-        if (t + 1 < ntiles) qk(k_nxt, sacc);
+        xphase(vc, kn, next_qk);
+        if constexpr (decltype(next_staging)::value) load_desc(t + 4);
+        __builtin_amdgcn_sched_barrier(0);
         lds_barrier();
-        const int k_old = k_cur;
-        k_cur = k_nxt;
-        k_nxt = k_st;
-        k_st = k_old;
-        v_cur = (v_cur + 1) & 3;
-    }
+        const int old = kc;
+        kc = kn;
+        kn = ks2;
+        ks2 = old;
+        vc = (vc + 1) & 3;
+    };
+    using yes = std::integral_constant<bool, true>;
+    using no = std::integral_constant<bool, false>;
+    int t = 0;
+    for (; t + 3 < ntiles; ++t) step(t, yes{}, yes{}, yes{});
+    if (t + 2 < ntiles) step(t++, yes{}, yes{}, no{});
+    if (t + 1 < ntiles) step(t++, yes{}, no{}, no{});
+    if (t < ntiles) step(t, no{}, no{}, no{});
     if (!group_b) lds_barrier();
 
     // ---- epilogue: normalise, write the output (or this split's partial result)
@@ -449,7 +600,7 @@ __global__ __launch_bounds__(512, 1) void link_attention_bf16(AttnParams p) {
         const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(lrow), __float_as_uint(lrow), false, false);
         const float lt = __uint_as_float(sw[0]) + __uint_as_float(sw[1]);
         const float inv = lt > 0.0f ? 1.0f / lt : 0.0f;
-        const float lse_v = lt > 0.0f ? mrow * p.scale + logf(lt) : -INFINITY;
+        const float lse_v = lt > 0.0f ? (mrow + __builtin_amdgcn_logf(lt)) * 0.6931471805599453f : -INFINITY;
         if (ti < w.n_rows) {
             const int row = w.row0 + ti;
             const int qh = w.kv_head * G + (m & (G - 1));

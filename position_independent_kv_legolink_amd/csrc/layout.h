@@ -53,6 +53,9 @@ struct MergeDesc {
 
 constexpr int kKeysPerTile = 64;   // keys staged in LDS per attention iteration
 constexpr int kMaxItemPages = 2048;  // longest KV range of one attention work item (its page table sits in LDS)
+// Positions are packed with a page's valid count into one 32-bit word (pos0 << 7 | valid) and
+// cos/sin rows are addressed with 32-bit byte offsets: both hold below this bound.
+constexpr int kMaxPosition = 1 << 22;
 constexpr int kThreads = 256;      // page writers, merge and the fp32 attention kernel
 
 // (row, head) pairs handled by one attention work group: 8 waves x 32 rows (bf16), 4 x 32 (fp32).
