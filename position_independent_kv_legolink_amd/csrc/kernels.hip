@@ -902,11 +902,14 @@ template <typename T, int D>
 __global__ __launch_bounds__(kThreads) void link_merge(const MergeDesc *merge, const float *part_o,
                                                        const float *part_lse, T *out, float *lse, int hq,
                                                        int gshift, int tq) {
+    // grid: (split tile, block of kThreads / (D / 4) M-rows); one thread per (M-row, 4 dims)
+    constexpr int RPB = kThreads / (D / 4);
     const MergeDesc md = merge[blockIdx.x];
     const int G = 1 << gshift;
     const int mrows = md.n_rows << gshift;
-    for (int idx = threadIdx.x; idx < mrows * (D / 4); idx += kThreads) {
-        const int m = idx / (D / 4), d4 = idx % (D / 4);
+    {
+        const int m = blockIdx.y * RPB + (int)threadIdx.x / (D / 4), d4 = (int)threadIdx.x % (D / 4);
+        if (m >= mrows) return;
         float L = -INFINITY;
         for (int s = 0; s < md.n_split; ++s) L = fmaxf(L, part_lse[(int64_t)(md.slot0 + s) * tq + m]);
         floatx4 acc = {0, 0, 0, 0};
@@ -1052,7 +1055,7 @@ hipError_t launch_merge(const LayerShape &s, const AttnTables &t, void *out, flo
     if (t.n_merge <= 0) return hipSuccess;
     const int gshift = log2_exact(s.hq / s.hkv);
     const int tq = tile_qrows(s.dtype);
-    dim3 grid(t.n_merge);
+    dim3 grid(t.n_merge, tq / (kThreads / (s.d / 4)));
     if (s.dtype == 0) {
         typedef uint16_t T;
         if (s.d == 128)
