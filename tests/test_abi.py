@@ -41,11 +41,15 @@ def meta(**over):
 
 @pytest.mark.parametrize("bad", [dict(head_dim=96), dict(page_size=8), dict(num_q_heads=6),
                                  dict(num_q_heads=32, num_kv_heads=2), dict(num_pages=0), dict(rope_theta=0.0),
-                                 dict(max_position=0)])
+                                 dict(max_position=0), dict(max_position=(1 << 22) + 1)])
 def test_store_config_validation(bad):
     with pytest.raises(pic.PicError) as e:
         meta(**bad)
     assert e.value.status == -1
+
+
+def test_store_accepts_the_largest_max_position():
+    meta(max_position=1 << 22).close()
 
 
 def test_store_and_plan_errors():

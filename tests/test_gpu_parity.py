@@ -163,6 +163,36 @@ def test_edge_cases_all_rows(name):
     check(cfg, got, want, ex, name)
 
 
+def test_large_scores():
+    """Scores spread over several units of log2(e): the running maximum moves often, and the
+    exponentials of stale maxima overflow fp32 on some tiles, so the exact softmax path runs."""
+    cfg = small_cfg(q_scale=2.0, kv_scale=1.0, chunk_len=150, k=12)
+    got, want, ex = run_workload(cfg)
+    check(cfg, got, want, ex, "large scores")
+
+
+def test_growing_scores():
+    """Keys of later chunks scaled up: every chunk brings a new row maximum."""
+    cfg = small_cfg(chunk_len=200, chunks_per_request=6, k=8, n_requests=1, prefix_len=0)
+    wl = Workload(cfg)
+    order = {c: i for i, c in enumerate(wl.draws[0])}
+    cached = {c: (k * np.float32(1.0 + 0.6 * order[c]), v) for c, (k, v) in wl.cached().items()}
+    cached = {c: (gen.round_bf16(k), v) for c, (k, v) in cached.items()}
+    segs = wl.segments(k=cfg.k)
+    store = gpu_store(cfg, cached, num_pages=400, max_position=4096)
+    plan = store.link_plan(wl.link_requests(), k=cfg.k)
+    rows = wl.new_rows(segs)
+    q, kn, vn = (torch.from_numpy(np.concatenate([r[i] for r in rows])).to("cuda", torch.bfloat16).contiguous()
+                 for i in range(3))
+    plan.upload()
+    lse_t = torch.empty((plan.rows, cfg.num_q_heads), dtype=torch.float32, device="cuda")
+    out = pic.link_attend(store, plan, q, kn, vn, lse=lse_t)
+    torch.cuda.synchronize()
+    want = oracle_outputs(segs, cached, rows, cfg.rope_theta)
+    check(cfg, out.float().cpu().numpy(), want,
+          dict(export=plan.export(), sample=None, lse=lse_t.cpu().numpy()), "growing scores")
+
+
 @pytest.mark.parametrize("split", [-1, 4, 12])
 def test_split_and_merge(split):
     cfg = small_cfg(chunk_len=300, chunks_per_request=6, k=20, n_requests=2)
