@@ -103,17 +103,27 @@ typedef struct {
  * recompute_all  select every row of every segment (full-recompute comparator)
  * split_pages  KV pages per attention work item: 0 = automatic, > 0 = at most
  *              that many, < 0 = split a (row tile, KV head) only where its key
- *              range exceeds the kernel's limit of 2,048 pages per work item */
+ *              range exceeds the kernel's limit of 2,048 pages per work item
+ * rope_keys    where the keys get their RoPE rotation (MEPIC abstract: inside
+ *              attention): 1 = in the attention kernel, for every key tile a work
+ *              item reads; 2 = once per link call, every logical page's keys into
+ *              the workspace, before attention (bfloat16 stores only; the results
+ *              are bit-identical to 1); 0 = automatic: 2 for bfloat16 stores when
+ *              the work list reads each key page at least 8 times on average,
+ *              else 1. Other values: PIC_ERR_INVALID. */
 typedef struct {
     int32_t k;
     int32_t block_level;
     int32_t pos_offset;
     int32_t recompute_all;
     int32_t split_pages;
+    int32_t rope_keys;
 } pic_link_options;
 
 /* Sizes of a plan. rows = selected rows R over all requests (the first dim of
- * q_new/k_new/v_new/out); pages = logical pages over all requests. */
+ * q_new/k_new/v_new/out); pages = logical pages over all requests;
+ * rotated_pages = logical pages whose keys pic_link_attend rotates into the
+ * workspace before attention (0: keys are rotated inside attention). */
 typedef struct {
     int64_t rows;
     int64_t pages;
@@ -123,6 +133,7 @@ typedef struct {
     int64_t split_items;
     int64_t workspace_bytes;
     int64_t requests;
+    int64_t rotated_pages;
 } pic_plan_sizes;
 
 /* Device bytes the caller must provide: each K and V pool
@@ -208,9 +219,11 @@ pic_status pic_plan_upload(pic_store *store, pic_plan *plan, void *workspace, in
  *   lse    [rows][Hq]      optional float32 natural-log softmax denominators
  * 1. scatter: every private page gets the new rows it holds, the cached rows
  *    copied from its stored page (copy-on-write) and zeroed padding;
- * 2. attention: every selected row attends causally over its request's linked
+ * 2. key rotation, when the plan has rotated_pages: the keys of every logical
+ *    page rotated at their absolute positions into the workspace;
+ * 3. attention: every selected row attends causally over its request's linked
  *    pages with RoPE applied at each token's absolute position;
- * 3. merge of split KV ranges (log-sum-exp weighted), when the plan split.
+ * 4. merge of split KV ranges (log-sum-exp weighted), when the plan split.
  * workspace must be the one the plan was uploaded to. Asynchronous. */
 pic_status pic_link_attend(pic_store *store, const pic_plan *plan, const void *q_new, const void *k_new,
                            const void *v_new, void *out, float *lse, void *workspace, int64_t workspace_bytes,
@@ -221,10 +234,11 @@ pic_status pic_link_attend(pic_store *store, const pic_plan *plan, const void *q
 pic_status pic_plan_free(pic_store *store, pic_plan *plan);
 
 /* Per-kernel timing of pic_link_attend with HIP events on the call's stream.
- * While enabled, every call records events around the scatter, attention and
- * merge launches. pic_profile_read synchronises on the recorded events and
- * returns the summed milliseconds of each stage (ms[0..2]) and the number of
- * calls since enabling; enabling again resets the sums. */
+ * While enabled, every call records events around the scatter, key rotation,
+ * attention and merge launches. pic_profile_read synchronises on the recorded
+ * events and returns the summed milliseconds of each stage in ms[0..3]
+ * (scatter, attention, merge, key rotation; ms needs room for 4) and the number
+ * of calls since enabling; enabling again resets the sums. */
 pic_status pic_profile_enable(pic_store *store, int32_t on);
 pic_status pic_profile_read(pic_store *store, double *ms, int32_t *calls);
 

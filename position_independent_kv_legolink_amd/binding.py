@@ -48,14 +48,15 @@ class Request(ctypes.Structure):
 
 class LinkOptions(ctypes.Structure):
     _fields_ = [("k", ctypes.c_int32), ("block_level", ctypes.c_int32), ("pos_offset", ctypes.c_int32),
-                ("recompute_all", ctypes.c_int32), ("split_pages", ctypes.c_int32)]
+                ("recompute_all", ctypes.c_int32), ("split_pages", ctypes.c_int32),
+                ("rope_keys", ctypes.c_int32)]
 
 
 class PlanSizes(ctypes.Structure):
     _fields_ = [("rows", ctypes.c_int64), ("pages", ctypes.c_int64), ("private_pages", ctypes.c_int64),
                 ("cow_pages", ctypes.c_int64), ("work_items", ctypes.c_int64),
                 ("split_items", ctypes.c_int64), ("workspace_bytes", ctypes.c_int64),
-                ("requests", ctypes.c_int64)]
+                ("requests", ctypes.c_int64), ("rotated_pages", ctypes.c_int64)]
 
 
 _lib = None
@@ -192,7 +193,7 @@ class Store:
         return dict(free_pages=f.value, chunks=c.value, plans=p.value)
 
     def link_plan(self, requests, *, k=0, block_level=False, pos_offset=0, recompute_all=False,
-                  split_pages=0):
+                  split_pages=0, rope_keys=0):
         n = len(requests)
         reqs = (Request * max(n, 1))()
         keep = []
@@ -203,7 +204,7 @@ class Store:
                               ctypes.cast(ids, ctypes.POINTER(ctypes.c_uint64)), len(r.chunk_ids),
                               int(r.suffix_len))
         opts = LinkOptions(int(k), int(bool(block_level)), int(pos_offset), int(bool(recompute_all)),
-                           int(split_pages))
+                           int(split_pages), int(rope_keys))
         h = ctypes.c_void_p()
         _check(lib().pic_link_plan(self.handle, reqs, n, ctypes.byref(opts), ctypes.byref(h)))
         return Plan(self, h)
@@ -212,10 +213,10 @@ class Store:
         _check(lib().pic_profile_enable(self.handle, int(bool(on))))
 
     def profile_read(self):
-        ms = (ctypes.c_double * 3)()
+        ms = (ctypes.c_double * 4)()
         calls = ctypes.c_int32()
         _check(lib().pic_profile_read(self.handle, ms, ctypes.byref(calls)))
-        return dict(scatter_ms=ms[0], attention_ms=ms[1], merge_ms=ms[2], calls=calls.value)
+        return dict(scatter_ms=ms[0], attention_ms=ms[1], merge_ms=ms[2], rotate_ms=ms[3], calls=calls.value)
 
 
 class Plan:

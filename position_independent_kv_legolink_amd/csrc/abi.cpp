@@ -248,6 +248,7 @@ pic_status pic_plan_info(const pic_plan *plan, pic_plan_sizes *sz) {
         sz->split_items = plan->n_split_items;
         sz->workspace_bytes = plan->workspace_bytes;
         sz->requests = plan->n_requests;
+        sz->rotated_pages = plan->rotate_keys ? (int64_t)plan->pages.size() : 0;
     });
 }
 
@@ -321,11 +322,12 @@ pic_status pic_link_attend(pic_store *s, const pic_plan *plan, const void *q_new
         t.n_merge = (int)plan->merge.size();
         t.part_o = reinterpret_cast<float *>(ws + plan->off_part_o);
         t.part_lse = reinterpret_cast<float *>(ws + plan->off_part_lse);
+        if (plan->rotate_keys) t.k_rot = ws + plan->off_k_rot;
 
         ProfileMarks marks{};
         const bool prof = s->profiling;
         if (prof) {
-            for (int i = 0; i < 4; ++i) {
+            for (int i = 0; i < 5; ++i) {
                 if (!s->spare_events.empty()) {
                     marks.ev[i] = s->spare_events.back();
                     s->spare_events.pop_back();
@@ -340,12 +342,17 @@ pic_status pic_link_attend(pic_store *s, const pic_plan *plan, const void *q_new
                                  (int)plan->scatter.size(), stream),
                   "scatter launch");
         if (prof) check_hip(hipEventRecord(marks.ev[1], stream), "hipEventRecord");
+        if (plan->rotate_keys)
+            check_hip(launch_rotate_keys(s->shape, s->k_pool, s->rope, t.pages, (int)plan->pages.size(),
+                                         const_cast<void *>(t.k_rot), stream),
+                      "key rotation launch");
+        if (prof) check_hip(hipEventRecord(marks.ev[2], stream), "hipEventRecord");
         check_hip(launch_attention(s->shape, q_new, s->k_pool, s->v_pool, s->rope, t, out, lse, stream),
                   "attention launch");
-        if (prof) check_hip(hipEventRecord(marks.ev[2], stream), "hipEventRecord");
+        if (prof) check_hip(hipEventRecord(marks.ev[3], stream), "hipEventRecord");
         check_hip(launch_merge(s->shape, t, out, lse, stream), "merge launch");
         if (prof) {
-            check_hip(hipEventRecord(marks.ev[3], stream), "hipEventRecord");
+            check_hip(hipEventRecord(marks.ev[4], stream), "hipEventRecord");
             s->pending.push_back(marks);
         }
     });
@@ -367,7 +374,7 @@ pic_status pic_profile_enable(pic_store *s, int32_t on) {
         s->pending.clear();
         s->profiling = on != 0;
         s->profiled_calls = 0;
-        s->profiled_ms[0] = s->profiled_ms[1] = s->profiled_ms[2] = 0.0;
+        for (double &m : s->profiled_ms) m = 0.0;
     });
 }
 
@@ -375,18 +382,20 @@ pic_status pic_profile_read(pic_store *s, double *ms, int32_t *calls) {
     return guarded([&] {
         if (!s) fail(PIC_ERR_INVALID, "null store");
         for (auto &m : s->pending) {
-            check_hip(hipEventSynchronize(m.ev[3]), "hipEventSynchronize");
-            for (int i = 0; i < 3; ++i) {
+            check_hip(hipEventSynchronize(m.ev[4]), "hipEventSynchronize");
+            // event intervals: scatter, key rotation, attention, merge
+            static const int kStage[4] = {0, 3, 1, 2};
+            for (int i = 0; i < 4; ++i) {
                 float t = 0.0f;
                 check_hip(hipEventElapsedTime(&t, m.ev[i], m.ev[i + 1]), "hipEventElapsedTime");
-                s->profiled_ms[i] += t;
+                s->profiled_ms[kStage[i]] += t;
             }
             s->profiled_calls += 1;
             for (hipEvent_t e : m.ev) s->spare_events.push_back(e);
         }
         s->pending.clear();
         if (ms)
-            for (int i = 0; i < 3; ++i) ms[i] = s->profiled_ms[i];
+            for (int i = 0; i < 4; ++i) ms[i] = s->profiled_ms[i];
         if (calls) *calls = s->profiled_calls;
     });
 }

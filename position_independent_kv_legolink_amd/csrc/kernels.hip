@@ -2,6 +2,8 @@
 //
 //   store_fill     chunk K/V [n][Hkv][d] -> page-aligned pool pages (compile-step product in)
 //   link_scatter   recomputed rows' K/V -> request-private pages, copy-on-write of cached rows
+//   rotate_keys    optional: K of every logical page rotated once at its absolute positions, for
+//                  link calls whose key tiles are read by many row tiles
 //   link_attention causal attention of the selected rows over their request's linked pages,
 //                  RoPE applied in registers at each token's absolute position, grouped-query
 //                  rows of one KV head per work group, MFMA for QK^T and PV, online softmax
@@ -64,6 +66,7 @@ struct AttnParams {
     const void *k_pool;
     const void *v_pool;
     const float *rope;          // [max_position][d]: d/2 cosines, then d/2 sines
+    const void *k_rot;          // pre-rotated keys [logical page][Hkv][page][d], or null
     const PageDesc *pages;
     const int32_t *row_pos;
     const WorkDesc *work;
@@ -117,7 +120,9 @@ __device__ __forceinline__ void rope8_bf16(const u32x4 &lo, const u32x4 &hi, con
 // enough for the one-phase skew: K' and key positions x3, V x4. Q carries the softmax scale and
 // log2(e), and the running maximum enters S^T through one bias MFMA per 32-key block, so the
 // common softmax path is exp2, a row sum and the bf16 packing.
-template <int D>
+// KR: keys come pre-rotated (rotate_keys, indexed by logical page) and are staged as loaded;
+// otherwise they are rotated here, with the same table values and arithmetic.
+template <int D, bool KR>
 __global__ __launch_bounds__(512, 1) void link_attention_bf16(AttnParams p) {
     constexpr int NT = 512;
     constexpr int KT = kKeysPerTile;
@@ -197,10 +202,11 @@ __global__ __launch_bounds__(512, 1) void link_attention_bf16(AttnParams p) {
 
     // Loop-invariant byte offsets of this thread's pieces inside a page (and inside a cos/sin
     // row), so that each load is a scalar page base plus a 32-bit lane offset.
-    const char *kpool_b = static_cast<const char *>(p.k_pool);
+    const char *kpool_b = static_cast<const char *>(KR ? p.k_rot : p.k_pool);
     const char *vpool_b = static_cast<const char *>(p.v_pool);
     const char *rope_b = reinterpret_cast<const char *>(p.rope);
     const uint32_t page_bytes = (uint32_t)p.page_elems * 2u;
+    const int lpage0 = w.page_base + w.page_begin;   // logical page of the item's first page
     uint32_t k_loff[NKP], k_cs_off[NKP], v_loff[NVC];
     int k_slot[NKP];
 #pragma unroll
@@ -245,9 +251,13 @@ __global__ __launch_bounds__(512, 1) void link_attention_bf16(AttnParams p) {
         for (int u = 0; u < NKP; ++u) {
             const int rq = r0 + (((NT * u + 64 * wv) / (D / 16)) >> p.pshift);
             const int r = min(rq, n_pages - 1);
-            rk_phys[u] = pg_phys[r];
-            rk_pv[u] = pg_pv[r];
-            rk_in[u] = rq < n_pages;
+            if constexpr (KR) {
+                rk_phys[u] = lpage0 + r;
+            } else {
+                rk_phys[u] = pg_phys[r];
+                rk_pv[u] = pg_pv[r];
+                rk_in[u] = rq < n_pages;
+            }
         }
 #pragma unroll
         for (int u = 0; u < NVC; ++u)
@@ -258,19 +268,22 @@ __global__ __launch_bounds__(512, 1) void link_attention_bf16(AttnParams p) {
     };
     // the loads of one tile, one instruction per piece so that they can be spread between MFMAs:
     // piece 0 takes the page descriptors into SGPRs, sets the keys' positions and loads the K low
-    // halves, 1 the K high halves, then V, then the cos/sin rows at the keys' positions
-    constexpr int NLOAD = 2 + NVC + 4;
+    // halves, 1 the K high halves, then V, then (keys rotated here) the cos/sin rows at the keys'
+    // positions
+    constexpr int NLOAD = 2 + NVC + (KR ? 0 : 4);
     const char *k_page[NKP];
     auto load_piece = [&](int j) __attribute__((always_inline)) {
         if (j == 0) {
 #pragma unroll
             for (int u = 0; u < NKP; ++u) {
                 const uint32_t phys = (uint32_t)__builtin_amdgcn_readfirstlane(rk_phys[u]);
-                const int pv = __builtin_amdgcn_readfirstlane(rk_pv[u]);
-                const int pos0 = pv >> 7, valid = pv & 127;
-                const int pi = tid + NT * u;
-                const bool ok = (KPAIRS % NT == 0 || pi < KPAIRS) && rk_in[u] && k_slot[u] < valid;
-                k_pos[u] = ok ? pos0 + k_slot[u] : pos0;
+                if constexpr (!KR) {
+                    const int pv = __builtin_amdgcn_readfirstlane(rk_pv[u]);
+                    const int pos0 = pv >> 7, valid = pv & 127;
+                    const int pi = tid + NT * u;
+                    const bool ok = (KPAIRS % NT == 0 || pi < KPAIRS) && rk_in[u] && k_slot[u] < valid;
+                    k_pos[u] = ok ? pos0 + k_slot[u] : pos0;
+                }
                 k_page[u] = kpool_b + (uint64_t)phys * page_bytes;
                 k_lo[u] = *reinterpret_cast<const u32x4 *>(k_page[u] + k_loff[u]);
             }
@@ -348,8 +361,16 @@ __global__ __launch_bounds__(512, 1) void link_attention_bf16(AttnParams p) {
         mask_ring = __any(kp_stage > w.rpos_min) ? (mask_ring | bit) : (mask_ring & ~bit);
     };
     auto store_tile = [&](int sl, int vsl) __attribute__((always_inline)) {
+        if constexpr (KR) {
 #pragma unroll
-        for (int r = 0; r < 8; ++r) rope_step(r);
+            for (int u = 0; u < NKP; ++u) {
+                k_olo[u] = k_lo[u];
+                k_ohi[u] = k_hi[u];
+            }
+        } else {
+#pragma unroll
+            for (int r = 0; r < 8; ++r) rope_step(r);
+        }
         write_k(sl);
         write_v(vsl, sl);
     };
@@ -988,6 +1009,41 @@ __global__ __launch_bounds__(kThreads) void link_scatter(const ScatterDesc *tabl
     }
 }
 
+// Keys of every logical page of a plan rotated once at the page's absolute positions, with the
+// attention kernel's table values and arithmetic, into the pool's page layout indexed by logical
+// page ([page][Hkv][page_size][d]); padding slots are written as zeros (the pools hold zeros
+// there, which rotate to zeros). One work group per logical page; a thread takes 8 (x_i,
+// x_{i+d/2}) pairs of one (head, slot) per pass, consecutive threads consecutive pairs of a row.
+template <int D>
+__global__ __launch_bounds__(kThreads) void rotate_keys_bf16(const PageDesc *pages, const uint8_t *k_pool,
+                                                             const float *rope, uint8_t *k_rot, int hkv, int pshift,
+                                                             int64_t page_bytes) {
+    const PageDesc pd = pages[blockIdx.x];
+    const int page_size = 1 << pshift;
+    constexpr int PPR = D / 16;   // pieces per row
+    const uint8_t *src = k_pool + (int64_t)pd.phys * page_bytes;
+    uint8_t *dst = k_rot + (int64_t)blockIdx.x * page_bytes;
+    for (int i = threadIdx.x; i < hkv * page_size * PPR; i += kThreads) {
+        const int c = i % PPR, row = i / PPR;   // row = head * page_size + slot
+        const int slot = row & (page_size - 1);
+        const int64_t off = (int64_t)row * D * 2 + c * 16;
+        u32x4 olo = {0, 0, 0, 0}, ohi = {0, 0, 0, 0};
+        if (slot < pd.valid) {
+            const u32x4 lo = *reinterpret_cast<const u32x4 *>(src + off);
+            const u32x4 hi = *reinterpret_cast<const u32x4 *>(src + off + D);
+            const float *cs = rope + (int64_t)(pd.pos0 + slot) * D + 8 * c;
+            floatx4 co[2], sn[2];
+            co[0] = *reinterpret_cast<const floatx4 *>(cs);
+            co[1] = *reinterpret_cast<const floatx4 *>(cs + 4);
+            sn[0] = *reinterpret_cast<const floatx4 *>(cs + D / 2);
+            sn[1] = *reinterpret_cast<const floatx4 *>(cs + D / 2 + 4);
+            rope8_bf16(lo, hi, co, sn, olo, ohi);
+        }
+        *reinterpret_cast<u32x4 *>(dst + off) = olo;
+        *reinterpret_cast<u32x4 *>(dst + off + D) = ohi;
+    }
+}
+
 int log2_exact(int x) {
     int s = 0;
     while ((1 << s) < x) ++s;
@@ -1018,14 +1074,33 @@ hipError_t launch_scatter(const LayerShape &s, void *k_pool, void *v_pool, const
     return hipGetLastError();
 }
 
+hipError_t launch_rotate_keys(const LayerShape &s, const void *k_pool, const float *rope, const PageDesc *pages,
+                              int n_pages, void *k_rot, hipStream_t stream) {
+    if (n_pages <= 0) return hipSuccess;
+    if (s.dtype != 0) return hipErrorInvalidValue;
+    const int pshift = log2_exact(s.page_size);
+    const int64_t page_bytes = s.page_elems * 2;
+    if (s.d == 128)
+        hipLaunchKernelGGL(rotate_keys_bf16<128>, dim3(n_pages), dim3(kThreads), 0, stream, pages,
+                           static_cast<const uint8_t *>(k_pool), rope, static_cast<uint8_t *>(k_rot), s.hkv, pshift,
+                           page_bytes);
+    else
+        hipLaunchKernelGGL(rotate_keys_bf16<64>, dim3(n_pages), dim3(kThreads), 0, stream, pages,
+                           static_cast<const uint8_t *>(k_pool), rope, static_cast<uint8_t *>(k_rot), s.hkv, pshift,
+                           page_bytes);
+    return hipGetLastError();
+}
+
 hipError_t launch_attention(const LayerShape &s, const void *q, const void *k_pool, const void *v_pool,
                             const float *rope, const AttnTables &t, void *out, float *lse, hipStream_t stream) {
     if (t.n_work <= 0) return hipSuccess;
+    if (t.k_rot && s.dtype != 0) return hipErrorInvalidValue;
     AttnParams p;
     p.q = q;
     p.k_pool = k_pool;
     p.v_pool = v_pool;
     p.rope = rope;
+    p.k_rot = t.k_rot;
     p.pages = t.pages;
     p.row_pos = t.row_pos;
     p.work = t.work;
@@ -1042,8 +1117,13 @@ hipError_t launch_attention(const LayerShape &s, const void *q, const void *k_po
     p.scale_log2 = 1.4426950408889634f / sqrtf((float)s.d);
     dim3 grid(t.n_work);
     if (s.dtype == 0) {
-        if (s.d == 128) hipLaunchKernelGGL(link_attention_bf16<128>, grid, dim3(512), 0, stream, p);
-        else hipLaunchKernelGGL(link_attention_bf16<64>, grid, dim3(512), 0, stream, p);
+        if (t.k_rot) {
+            if (s.d == 128) hipLaunchKernelGGL((link_attention_bf16<128, true>), grid, dim3(512), 0, stream, p);
+            else hipLaunchKernelGGL((link_attention_bf16<64, true>), grid, dim3(512), 0, stream, p);
+        } else {
+            if (s.d == 128) hipLaunchKernelGGL((link_attention_bf16<128, false>), grid, dim3(512), 0, stream, p);
+            else hipLaunchKernelGGL((link_attention_bf16<64, false>), grid, dim3(512), 0, stream, p);
+        }
     } else {
         if (s.d == 128) hipLaunchKernelGGL(link_attention_f32<128>, grid, dim3(kThreads), 0, stream, p);
         else hipLaunchKernelGGL(link_attention_f32<64>, grid, dim3(kThreads), 0, stream, p);

@@ -30,6 +30,11 @@ hipError_t launch_store_fill(const LayerShape &s, void *k_pool, void *v_pool, co
 hipError_t launch_scatter(const LayerShape &s, void *k_pool, void *v_pool, const void *k_new, const void *v_new,
                           const ScatterDesc *table, int n, hipStream_t stream);
 
+// K of `n_pages` logical pages (device PageDesc table) rotated at their positions into k_rot
+// ([logical page][Hkv][page][d]); bfloat16 layers only.
+hipError_t launch_rotate_keys(const LayerShape &s, const void *k_pool, const float *rope, const PageDesc *pages,
+                              int n_pages, void *k_rot, hipStream_t stream);
+
 struct AttnTables {
     const PageDesc *pages;
     const int32_t *row_pos;
@@ -39,6 +44,7 @@ struct AttnTables {
     int n_merge;
     float *part_o;
     float *part_lse;
+    const void *k_rot = nullptr;   // pre-rotated keys (bf16), or null: keys rotated inside attention
 };
 
 hipError_t launch_attention(const LayerShape &s, const void *q, const void *k_pool, const void *v_pool,

@@ -37,6 +37,9 @@ pic_plan *build_plan(pic_store *s, const pic_request *reqs, int32_t n_reqs, cons
     if (n_reqs < 0 || (n_reqs > 0 && !reqs)) fail(PIC_ERR_INVALID, "bad request array");
     if (o.k < 0) fail(PIC_ERR_INVALID, "k must be >= 0");
     if (o.pos_offset < 0) fail(PIC_ERR_INVALID, "pos_offset must be >= 0");
+    if (o.rope_keys < 0 || o.rope_keys > 2) fail(PIC_ERR_INVALID, "rope_keys must be 0, 1 or 2");
+    if (o.rope_keys == 2 && cfg.dtype != PIC_DTYPE_BF16)
+        fail(PIC_ERR_INVALID, "keys are rotated ahead of attention for bfloat16 stores only");
 
     // ---- pass 1: segments, validation and private-page count
     std::vector<std::vector<Seg>> all(n_reqs);
@@ -144,6 +147,14 @@ pic_plan *build_plan(pic_store *s, const pic_request *reqs, int32_t n_reqs, cons
             }
         }
     }
+    // where the keys are rotated: a key page is read once per (row tile, KV head) item that
+    // covers it, and rotating it once ahead of attention pays when that happens often
+    const int64_t page_heads = (int64_t)plan->pages.size() * cfg.num_kv_heads;
+    if (!items.empty()) {
+        if (o.rope_keys == 2) plan->rotate_keys = true;
+        else if (o.rope_keys == 0)
+            plan->rotate_keys = cfg.dtype == PIC_DTYPE_BF16 && total >= (int64_t)kRotateReuse * page_heads;
+    }
     int64_t max_pages;
     if (o.split_pages > 0) {
         max_pages = align_up(o.split_pages, ppt);
@@ -209,6 +220,8 @@ pic_plan *build_plan(pic_store *s, const pic_request *reqs, int32_t n_reqs, cons
     const int64_t tq = tile_qrows(cfg.dtype);
     plan->off_part_o = place((int64_t)plan->n_slots * tq * cfg.head_dim * sizeof(float));
     plan->off_part_lse = place((int64_t)plan->n_slots * tq * sizeof(float));
+    const int64_t elem = cfg.dtype == PIC_DTYPE_BF16 ? 2 : 4;
+    plan->off_k_rot = place(plan->rotate_keys ? (int64_t)plan->pages.size() * s->shape.page_elems * elem : 0);
     plan->workspace_bytes = std::max<int64_t>(off, 256);
     return plan;
 }

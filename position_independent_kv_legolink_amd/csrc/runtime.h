@@ -28,7 +28,7 @@ struct Chunk {
 };
 
 struct ProfileMarks {
-    hipEvent_t ev[4];   // before scatter, before attention, before merge, after merge
+    hipEvent_t ev[5];   // before scatter, before key rotation, before attention, before merge, after merge
 };
 
 }  // namespace piclink
@@ -46,7 +46,7 @@ struct pic_store {
     int32_t num_cus = 256;              // compute units used by the work-list split policy
     bool profiling = false;
     int32_t profiled_calls = 0;
-    double profiled_ms[3] = {0, 0, 0};
+    double profiled_ms[4] = {0, 0, 0, 0};   // scatter, attention, merge, key rotation
     std::vector<piclink::ProfileMarks> pending;
     std::vector<hipEvent_t> spare_events;
 };
@@ -66,6 +66,8 @@ struct pic_plan {
     // workspace layout (byte offsets)
     int64_t off_pages = 0, off_row_pos = 0, off_scatter = 0, off_work = 0, off_merge = 0;
     int64_t off_part_o = 0, off_part_lse = 0, table_bytes = 0, workspace_bytes = 0;
+    bool rotate_keys = false;           // keys rotated into the workspace before attention
+    int64_t off_k_rot = 0;
     void *uploaded_to = nullptr;
 };
 

@@ -131,3 +131,40 @@ def test_plan_sizes_report_workspace():
     assert z["rows"] == 66 and z["pages"] == 36 and z["private_pages"] == 5 and z["cow_pages"] == 1
     assert z["workspace_bytes"] % 256 == 0 and z["workspace_bytes"] >= 36 * 16
     plan.free()
+
+
+def test_rope_keys_option_is_validated():
+    s = meta()
+    s.store_chunk(1, n_tokens=40)
+    for bad in (-1, 3):
+        with pytest.raises(pic.PicError) as e:
+            s.link_plan([pic.LinkRequest([1], 5)], k=2, rope_keys=bad)
+        assert e.value.status == -1
+    s.close()
+    f = meta(dtype="f32", head_dim=64)
+    f.store_chunk(1, n_tokens=40)
+    with pytest.raises(pic.PicError) as e:
+        f.link_plan([pic.LinkRequest([1], 5)], k=2, rope_keys=2)   # bf16 stores only
+    assert e.value.status == -1
+    for rk in (0, 1):
+        plan = f.link_plan([pic.LinkRequest([1], 5)], k=2, rope_keys=rk)
+        assert plan.sizes["rotated_pages"] == 0
+        plan.free()
+    assert f.stats()["plans"] == 0
+
+
+def test_rotated_keys_take_one_page_per_logical_page_of_workspace():
+    """rope_keys=2 adds the rotated keys of every logical page (Hkv x page x d bf16 each) to the
+    workspace; rope_keys=1 adds nothing; a plan without rows rotates nothing."""
+    s = meta()
+    s.store_chunk(1, n_tokens=512)
+    fused = s.link_plan([pic.LinkRequest([1], 64)], k=2, rope_keys=1)
+    rot = s.link_plan([pic.LinkRequest([1], 64)], k=2, rope_keys=2)
+    assert fused.sizes["rotated_pages"] == 0
+    assert rot.sizes["rotated_pages"] == rot.sizes["pages"] == 36
+    page_bytes = 2 * 16 * 128 * 2
+    assert rot.sizes["workspace_bytes"] - fused.sizes["workspace_bytes"] == 36 * page_bytes
+    empty = s.link_plan([pic.LinkRequest([1], 0)], k=0, rope_keys=2)
+    assert empty.sizes["rows"] == 0 and empty.sizes["rotated_pages"] == 0
+    for p in (fused, rot, empty):
+        p.free()

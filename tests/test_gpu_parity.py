@@ -38,8 +38,9 @@ def _need_gpu():
 
 
 def run_workload(cfg, *, n_requests=None, sample_rows=None, pos_offset=0, split_pages=0, k=None,
-                 recompute_all=False, seed=0, check_plan=True, repeat=1, lse=True, num_pages=None):
-    """Link a config's requests on the GPU; return (gpu outs, oracle outs, extras)."""
+                 recompute_all=False, seed=0, check_plan=True, repeat=1, lse=True, num_pages=None, rope_keys=0,
+                 with_oracle=True):
+    """Link a config's requests on the GPU; return (gpu outs, oracle outs or None, extras)."""
     wl = Workload(cfg, n_requests=n_requests)
     kk = cfg.k if k is None else k
     segs = wl.segments(pos_offset=pos_offset, recompute_all=recompute_all, k=kk)
@@ -51,7 +52,7 @@ def run_workload(cfg, *, n_requests=None, sample_rows=None, pos_offset=0, split_
     store = gpu_store(cfg, cached, num_pages=num_pages or (stored + private + 8),
                       max_position=pos_offset + n_tokens + 1)
     plan = store.link_plan(wl.link_requests(), k=kk, block_level=cfg.block_level, pos_offset=pos_offset,
-                           recompute_all=recompute_all, split_pages=split_pages)
+                           recompute_all=recompute_all, split_pages=split_pages, rope_keys=rope_keys)
     if check_plan:
         compare_plan(store, plan, segs, B)
     rows = wl.new_rows(segs)
@@ -76,7 +77,7 @@ def run_workload(cfg, *, n_requests=None, sample_rows=None, pos_offset=0, split_
             R = len(oplan.selected_positions(s))
             pick = {0, R - 1, R // 2} | set(int(x) for x in g.integers(0, R, size=max(0, sample_rows - 3)))
             sample[i] = np.array(sorted(x for x in pick if 0 <= x < R), dtype=np.int64)
-    want = oracle_outputs(segs, cached, rows, cfg.rope_theta, sample=sample)
+    want = oracle_outputs(segs, cached, rows, cfg.rope_theta, sample=sample) if with_oracle else None
     extras = dict(store=store, plan=plan, export=ex, segs=segs, cached=cached, rows=rows, sample=sample,
                   lse=got_lse, outs=outs)
     return outs[0], want, extras
@@ -119,6 +120,8 @@ def test_batched_k16_sampled():
 def test_long50k_k32_sampled():
     cfg = CONFIGS["long50k_k32"]
     got, want, ex = run_workload(cfg, sample_rows=40, repeat=2)
+    # its 50 row tiles per KV head read every key page many times: keys are rotated ahead
+    assert ex["plan"].sizes["rotated_pages"] == ex["plan"].sizes["pages"]
     check(cfg, got, want, ex, "long50k_k32")
     assert np.array_equal(ex["outs"][0], ex["outs"][1]), "run-to-run results differ"
 
@@ -292,3 +295,46 @@ def test_page_placement_does_not_change_results():
     plan.upload()
     b = pic.link_attend(store, plan, q, kn, vn).float().cpu().numpy()
     assert np.array_equal(a, b)
+
+
+# ------------------------------------------------------------------ keys rotated ahead of attention
+ROTATED = {n: c for n, c in EDGE.items() if c.get("dtype", "bf16") == "bf16"}
+
+
+@pytest.mark.parametrize("name", list(ROTATED))
+def test_edge_cases_rotated_keys(name):
+    cfg = small_cfg(**ROTATED[name])
+    _say(f"edge case {name}, keys rotated ahead of attention")
+    got, want, ex = run_workload(cfg, rope_keys=2)
+    assert ex["plan"].sizes["rotated_pages"] == ex["plan"].sizes["pages"]
+    check(cfg, got, want, ex, f"{name} rotated keys")
+
+
+@pytest.mark.parametrize("name,sample", [("llama3_k2", None), ("batched_k16", 12), ("block_zipf", 4)])
+def test_workloads_rotated_keys(name, sample):
+    cfg = CONFIGS[name]
+    _say(f"{name}, keys rotated ahead of attention")
+    got, want, ex = run_workload(cfg, sample_rows=sample, rope_keys=2)
+    assert ex["plan"].sizes["rotated_pages"] == ex["plan"].sizes["pages"]
+    check(cfg, got, want, ex, f"{name} rotated keys")
+
+
+ROTATION_CASES = {
+    "llama3_k2": lambda: (CONFIGS["llama3_k2"], {}),
+    "long50k_k32": lambda: (CONFIGS["long50k_k32"], {}),
+    "split_offset": lambda: (small_cfg(chunk_len=300, chunks_per_request=6, k=20), dict(split_pages=4, pos_offset=4097)),
+    "page64_d64": lambda: (small_cfg(page_size=64, head_dim=64, num_q_heads=8, num_kv_heads=2, k=40), {}),
+}
+
+
+@pytest.mark.parametrize("case", list(ROTATION_CASES))
+def test_rotation_modes_are_bit_identical(case):
+    """Keys rotated once ahead of attention and keys rotated inside attention use the same table
+    values and arithmetic, so outputs and log-sum-exps agree bit for bit."""
+    cfg, kw = ROTATION_CASES[case]()
+    _say(f"rotation modes, {case}")
+    a, _, ex_a = run_workload(cfg, rope_keys=1, with_oracle=False, check_plan=False, **kw)
+    b, _, ex_b = run_workload(cfg, rope_keys=2, with_oracle=False, check_plan=False, **kw)
+    assert ex_a["plan"].sizes["rotated_pages"] == 0 and ex_b["plan"].sizes["rotated_pages"] > 0
+    assert np.array_equal(a, b)
+    assert np.array_equal(ex_a["lse"], ex_b["lse"])

@@ -120,3 +120,42 @@ def test_split_options():
             # only tiles whose key range exceeds 2,048 pages split, each into two pieces
             assert s["split_items"] < s["work_items"]
         plan.free()
+
+
+@pytest.mark.parametrize("name", ["llama3_k2", "batched_k16", "long50k_k32", "block_zipf"])
+def test_automatic_key_rotation_follows_key_reuse(name):
+    """rope_keys=0 rotates the keys ahead of attention exactly when the work list reads the key
+    pages at least 8 times each on average: the 50k request's 50 row tiles do, the short and
+    batched requests (at most 8 row tiles each) do not."""
+    cfg = CONFIGS[name]
+    wl = Workload(cfg)
+    B = cfg.page_size
+    segs = wl.segments()
+    pages_needed = sum(-(-cfg.chunk_len // B) for _ in wl.chunk_ids)
+    pages_needed += len(wl.requests) * -(-cfg.prefix_len // B) + plan_private(segs, B)
+    store = meta_store(cfg, pages_needed)
+    for c in wl.chunk_ids:
+        store.store_chunk(c, n_tokens=cfg.chunk_len)
+    if cfg.prefix_len:
+        for r in wl.requests:
+            store.store_chunk(cfg.prefix_id(r), n_tokens=cfg.prefix_len)
+    plan = store.link_plan(wl.link_requests(), k=cfg.k, block_level=cfg.block_level, split_pages=-1)
+    # reads of key pages: one per (row tile of 64 rows, KV head) and page up to the tile's last row
+    G = cfg.num_q_heads // cfg.num_kv_heads
+    tile = 256 // G
+    reads = 0
+    ex = plan.export()
+    pos_map = ex["pos_map"].reshape(-1, B)
+    cu_rows, cu_pages = ex["cu_rows"], ex["cu_pages"]
+    for r in range(len(cu_rows) - 1):
+        rp = ex["row_pos"][cu_rows[r]:cu_rows[r + 1]]
+        pm = pos_map[cu_pages[r]:cu_pages[r + 1]]
+        first = pm[:, 0]   # slot 0 of every page holds a token
+        for t0 in range(0, len(rp), tile):
+            last = rp[min(t0 + tile, len(rp)) - 1]
+            reads += int(np.sum(first <= last))
+    reads *= cfg.num_kv_heads
+    expect = reads >= 8 * plan.sizes["pages"] * cfg.num_kv_heads
+    assert (plan.sizes["rotated_pages"] > 0) == expect
+    assert expect == (name == "long50k_k32")
+    plan.free()
