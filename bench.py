@@ -72,7 +72,7 @@ def algorithmic_counts(cfg, export, sizes, n_tokens_per_request):
 class LinkJob:
     """Store, requests and device tensors of one workload."""
 
-    def __init__(self, cfg, *, dense_pages=0):
+    def __init__(self, cfg, *, dense_pages=0, rope_keys=0):
         import torch
 
         import position_independent_kv_legolink_amd as pic
@@ -106,7 +106,7 @@ class LinkJob:
             self.requests.append(pic.LinkRequest(ids, cfg.suffix_len, pid))
         torch.cuda.synchronize()
         log(f"stored {len(chunk_ids)} chunks in {time.time() - t:.1f}s")
-        self.plan_kw = dict(k=cfg.k, block_level=cfg.block_level)
+        self.plan_kw = dict(k=cfg.k, block_level=cfg.block_level, rope_keys=rope_keys)
         plan = self.store.link_plan(self.requests, **self.plan_kw)
         self.sizes = dict(plan.sizes)
         self.export = plan.export()
@@ -159,7 +159,7 @@ def dense_comparator(job, reps=3):
     from workloads import gen
 
     torch, cfg = job.torch, job.cfg
-    plan = job.store.link_plan(job.requests, k=cfg.k, recompute_all=True)
+    plan = job.store.link_plan(job.requests, k=cfg.k, recompute_all=True, rope_keys=job.plan_kw["rope_keys"])
     sizes, ex = dict(plan.sizes), plan.export()
     R = sizes["rows"]
     B = cfg.page_size
@@ -316,6 +316,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=20.0)
     ap.add_argument("--no-dense", action="store_true")
+    ap.add_argument("--rope-keys", type=int, default=0, choices=(0, 1, 2),
+                    help="key rotation: 0 automatic, 1 inside attention, 2 once ahead of attention")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="also run one device copy of this size per step (counter calibration runs)")
     ap.add_argument("--traffic-from", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
@@ -346,7 +348,7 @@ def main():
     cfg = CONFIGS[args.workload]
     dense_pages = 0 if args.no_dense else (-(-(cfg.prefix_len + cfg.chunks_per_request * cfg.chunk_len +
                                                  cfg.suffix_len) // cfg.page_size)) * cfg.n_requests
-    job = LinkJob(cfg, dense_pages=dense_pages)
+    job = LinkJob(cfg, dense_pages=dense_pages, rope_keys=args.rope_keys)
     flop, attn_bytes, total_bytes = algorithmic_counts(cfg, job.export, job.sizes, job.n_tokens)
     log(f"{cfg.name}: rows {job.sizes['rows']}, pages {job.sizes['pages']}, work items {job.sizes['work_items']} "
         f"({job.sizes['split_items']} split), {flop / 1e9:.1f} GFLOP, {total_bytes / 1e6:.1f} MB")
@@ -366,8 +368,15 @@ def main():
     attn_ms = prof["attention_ms"] / calls
     scatter_ms = prof["scatter_ms"] / calls
     merge_ms = prof["merge_ms"] / calls
-    link_ms = scatter_ms + attn_ms + merge_ms
-    log(f"step {ms_step:.3f} ms; scatter {scatter_ms:.4f} attention {attn_ms:.4f} merge {merge_ms:.4f} ms")
+    rotate_ms = prof["rotate_ms"] / calls
+    link_ms = scatter_ms + rotate_ms + attn_ms + merge_ms
+    log(f"step {ms_step:.3f} ms; scatter {scatter_ms:.4f} key rotation {rotate_ms:.4f} attention {attn_ms:.4f} "
+        f"merge {merge_ms:.4f} ms")
+    # key rotation pass: every rotated page's keys read and written, its cos/sin rows read once
+    rot_pages = job.sizes["rotated_pages"]
+    elem = 2 if cfg.dtype == "bf16" else 4
+    rot_bytes = rot_pages * (2 * cfg.num_kv_heads * cfg.page_size * cfg.head_dim * elem
+                             + cfg.page_size * cfg.head_dim * 4)
 
     peak = PEAK_BF16_TFLOPS if cfg.dtype == "bf16" else PEAK_F32_TFLOPS
     achieved = flop / (attn_ms * 1e-3) / 1e12
@@ -406,6 +415,9 @@ def main():
         "attention_ms": round(attn_ms, 4),
         "scatter_ms": round(scatter_ms, 4),
         "merge_ms": round(merge_ms, 4),
+        "keys_rotated_ahead": rot_pages > 0,
+        "rotate_ms": round(rotate_ms, 4),
+        "rotate_gbps": round(rot_bytes / (rotate_ms * 1e-3) / 1e9, 1) if rotate_ms > 0 else None,
         "algorithmic_gflop": round(flop / 1e9, 3),
         "algorithmic_mb": round(total_bytes / 1e6, 2),
         "hbm_gbps": round(total_bytes / (link_ms * 1e-3) / 1e9, 1),
