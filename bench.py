@@ -72,7 +72,7 @@ def algorithmic_counts(cfg, export, sizes, n_tokens_per_request):
 class LinkJob:
     """Store, requests and device tensors of one workload."""
 
-    def __init__(self, cfg, *, dense_pages=0, rope_keys=0):
+    def __init__(self, cfg, *, dense_pages=0, rope_keys=0, split_pages=0):
         import torch
 
         import position_independent_kv_legolink_amd as pic
@@ -106,7 +106,7 @@ class LinkJob:
             self.requests.append(pic.LinkRequest(ids, cfg.suffix_len, pid))
         torch.cuda.synchronize()
         log(f"stored {len(chunk_ids)} chunks in {time.time() - t:.1f}s")
-        self.plan_kw = dict(k=cfg.k, block_level=cfg.block_level, rope_keys=rope_keys)
+        self.plan_kw = dict(k=cfg.k, block_level=cfg.block_level, rope_keys=rope_keys, split_pages=split_pages)
         plan = self.store.link_plan(self.requests, **self.plan_kw)
         self.sizes = dict(plan.sizes)
         self.export = plan.export()
@@ -318,6 +318,9 @@ def main():
     ap.add_argument("--no-dense", action="store_true")
     ap.add_argument("--rope-keys", type=int, default=0, choices=(0, 1, 2),
                     help="key rotation: 0 automatic, 1 inside attention, 2 once ahead of attention")
+    ap.add_argument("--split-pages", type=int, default=0,
+                    help="KV pages per attention work item: 0 automatic, > 0 at most that many, "
+                         "< 0 only where the kernel's limit requires")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="also run one device copy of this size per step (counter calibration runs)")
     ap.add_argument("--traffic-from", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
@@ -348,7 +351,7 @@ def main():
     cfg = CONFIGS[args.workload]
     dense_pages = 0 if args.no_dense else (-(-(cfg.prefix_len + cfg.chunks_per_request * cfg.chunk_len +
                                                  cfg.suffix_len) // cfg.page_size)) * cfg.n_requests
-    job = LinkJob(cfg, dense_pages=dense_pages, rope_keys=args.rope_keys)
+    job = LinkJob(cfg, dense_pages=dense_pages, rope_keys=args.rope_keys, split_pages=args.split_pages)
     flop, attn_bytes, total_bytes = algorithmic_counts(cfg, job.export, job.sizes, job.n_tokens)
     log(f"{cfg.name}: rows {job.sizes['rows']}, pages {job.sizes['pages']}, work items {job.sizes['work_items']} "
         f"({job.sizes['split_items']} split), {flop / 1e9:.1f} GFLOP, {total_bytes / 1e6:.1f} MB")

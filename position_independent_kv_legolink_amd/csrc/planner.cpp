@@ -9,8 +9,9 @@
 //     with the store; the others are private to the request and, when they also keep cached
 //     rows, are filled copy-on-write from their stored page.
 // The attention work list then cuts each request's rows into tiles of tile_qrows / G rows,
-// one work item per (tile, KV head), splits long key ranges and orders the items longest
-// first, grouped so that one KV head's items land on one XCD.
+// one work item per (tile, KV head), splits key ranges longer than a compute unit's average
+// load (or the kernel's page-table limit) and orders the items longest first, grouped so that
+// one KV head's items land on one XCD.
 #include <algorithm>
 #include <numeric>
 
@@ -161,8 +162,10 @@ pic_plan *build_plan(pic_store *s, const pic_request *reqs, int32_t n_reqs, cons
     } else if (o.split_pages < 0) {
         max_pages = INT32_MAX;
     } else {
-        // aim at about two items per compute unit, never below 8 key tiles per item
-        max_pages = std::max<int64_t>(8 * ppt, align_up((total + 2 * s->num_cus - 1) / (2 * s->num_cus), ppt));
+        // split only items longer than the average load of a compute unit: the longest-first
+        // schedule then ends within about one item of the average, and shorter pieces would only
+        // add merge work. Never below 8 key tiles per item.
+        max_pages = std::max<int64_t>(8 * ppt, align_up((total + s->num_cus - 1) / s->num_cus, ppt));
     }
     // an item's page table is staged in LDS by the attention kernel
     max_pages = std::min<int64_t>(max_pages, kMaxItemPages);
