@@ -191,6 +191,12 @@ __global__ __launch_bounds__(512, 1) void link_attention_bf16(AttnParams p) {
         }
     }
 
+    // position of the wave's first row: its rows are consecutive selected rows of one request, in
+    // increasing position, so a key tile needs no mask for this wave when no key lies after it (a
+    // wave without rows never needs the mask: its outputs are not written)
+    const int rpos0 = __builtin_amdgcn_readfirstlane(rpos);
+    const int wave_rpos0 = rpos0 < 0 ? INT_MAX : rpos0;
+
     // ---- staging registers of one key tile (global -> registers -> LDS)
     u32x4 k_lo[NKP], k_hi[NKP];
     int k_pos[NKP];
@@ -315,7 +321,7 @@ __global__ __launch_bounds__(512, 1) void link_attention_bf16(AttnParams p) {
     // staging of one tile, in pieces that fit between MFMAs: the rotation of word wd (two
     // (x_i, x_{i+d/2}) pairs) of every K piece, then the LDS writes. K', V and key positions of a
     // tile share ring slot sl (of 3); the mask bit of the slot records whether any key of the tile
-    // lies after the work item's first row.
+    // lies after the wave's first row.
     // step k rotates pair k & 1 of word k >> 1 (the even pair is held until the odd one is ready
     // to be packed with it)
     float rx[NKP], ry[NKP];
@@ -358,7 +364,7 @@ __global__ __launch_bounds__(512, 1) void link_attention_bf16(AttnParams p) {
         }
         kpos_s[sl * KT + lane] = kp_stage;   // every wave writes the same 64 values
         const unsigned bit = 1u << sl;
-        mask_ring = __any(kp_stage > w.rpos_min) ? (mask_ring | bit) : (mask_ring & ~bit);
+        mask_ring = __any(kp_stage > wave_rpos0) ? (mask_ring | bit) : (mask_ring & ~bit);
     };
     auto store_tile = [&](int sl, int vsl) __attribute__((always_inline)) {
         if constexpr (KR) {
@@ -720,6 +726,11 @@ __global__ __launch_bounds__(kThreads, 1) void link_attention_f32(AttnParams p) 
         }
     }
 
+    // position of the wave's first row (rows of one request in increasing position; a wave
+    // without rows never needs the mask)
+    const int rpos0 = __builtin_amdgcn_readfirstlane(rpos);
+    const int wave_rpos0 = rpos0 < 0 ? INT_MAX : rpos0;
+
     floatx4 k_lo[NKP], k_hi[NKP], k_c[NKP], k_s[NKP];
     floatx4 v_r[NV];
     int kp_next = kNeverAttended;
@@ -796,8 +807,9 @@ __global__ __launch_bounds__(kThreads, 1) void link_attention_f32(AttnParams p) 
             *reinterpret_cast<floatx4 *>(&vs[buf][key * VS + 4 * c]) = v_r[u];
         }
         if (wave == 0) kpos_s[buf][lane] = kp_next;
-        // the tile needs the causal/padding mask iff some key lies after the tile's first row
-        mask_next = __any(kp_next > w.rpos_min);
+        // the tile needs the causal/padding mask for this wave iff some key lies after the wave's
+        // first row
+        mask_next = __any(kp_next > wave_rpos0);
     };
 
     floatx16 oacc[NDB];

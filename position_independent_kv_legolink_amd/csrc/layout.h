@@ -38,7 +38,7 @@ struct WorkDesc {
     int32_t n_rows;      // selected rows in the tile; 0 = empty slot, exit
     int32_t kv_head;
     int32_t partial;     // -1: final output; else partial-result slot of this split
-    int32_t rpos_min;    // position of the tile's first row
+    int32_t pad;
 };
 
 // Combine the partial results of the splits of one (row tile, KV head).

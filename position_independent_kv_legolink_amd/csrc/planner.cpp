@@ -143,7 +143,7 @@ pic_plan *build_plan(pic_store *s, const pic_request *reqs, int32_t n_reqs, cons
             const int32_t n = std::min(tile_rows, plan->cu_rows[r + 1] - t0);
             const int32_t need = row_page[t0 + n - 1] + 1;
             for (int h = 0; h < cfg.num_kv_heads; ++h) {
-                items.push_back({{plan->cu_pages[r], 0, need, t0, n, h, -1, plan->row_pos[t0]}, need});
+                items.push_back({{plan->cu_pages[r], 0, need, t0, n, h, -1, 0}, need});
                 total += need;
             }
         }
