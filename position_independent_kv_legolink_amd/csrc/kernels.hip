@@ -196,6 +196,11 @@ __global__ __launch_bounds__(512, 1) void link_attention_bf16(AttnParams p) {
     // wave without rows never needs the mask: its outputs are not written)
     const int rpos0 = __builtin_amdgcn_readfirstlane(rpos);
     const int wave_rpos0 = rpos0 < 0 ? INT_MAX : rpos0;
+    // ... and of its last row (-1: no rows)
+    int rlast = rpos;
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) rlast = max(rlast, __shfl_xor(rlast, o));
+    const int wave_rpos1 = __builtin_amdgcn_readfirstlane(rlast);
 
     // ---- staging registers of one key tile (global -> registers -> LDS)
     u32x4 k_lo[NKP], k_hi[NKP];
@@ -574,6 +579,19 @@ __global__ __launch_bounds__(512, 1) void link_attention_bf16(AttnParams p) {
 
     const int ntiles = (w.page_end - w.page_begin + ppt - 1) / ppt;
     const bool group_b = wave >= 4;
+    // Key tiles this wave attends: those whose first key is at or before its last row, a prefix
+    // [0, n_act) of the item's tiles (page positions increase). Past it the wave only stages tiles
+    // for the other waves, and its SIMD partner runs alone.
+    int n_act;
+    {
+        int lo = 0, hi = n_pages;   // first page whose first position lies after the last row
+        while (lo < hi) {
+            const int mid = (lo + hi) >> 1;
+            if ((pg_pv[mid] >> 7) <= wave_rpos1) lo = mid + 1;
+            else hi = mid;
+        }
+        n_act = __builtin_amdgcn_readfirstlane((lo + ppt - 1) / ppt);
+    }
 
     load_desc(0);
     load_tile();
@@ -611,13 +629,46 @@ __global__ __launch_bounds__(512, 1) void link_attention_bf16(AttnParams p) {
         ks2 = old;
         vc = (vc + 1) & 3;
     };
+    // a step of a wave past its last key tile: the staging of tile t+2 and the loads of tile t+3,
+    // with the same two barriers as `step`
+    auto idle_step = [&](int t, auto staging, auto next_staging) __attribute__((always_inline)) {
+        if constexpr (decltype(staging)::value) {
+            store_tile(ks2, (vc + 2) & 3);
+#pragma unroll
+            for (int j = 0; j < NLOAD; ++j) load_piece(j);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+        lds_barrier();
+        if constexpr (decltype(next_staging)::value) load_desc(t + 4);
+        __builtin_amdgcn_sched_barrier(0);
+        lds_barrier();
+        const int old = kc;
+        kc = kn;
+        kn = ks2;
+        ks2 = old;
+        vc = (vc + 1) & 3;
+    };
     using yes = std::integral_constant<bool, true>;
     using no = std::integral_constant<bool, false>;
+    // every wave passes 2 barriers per tile for all ntiles tiles, active or not
     int t = 0;
-    for (; t + 3 < ntiles; ++t) step(t, yes{}, yes{}, yes{});
-    if (t + 2 < ntiles) step(t++, yes{}, yes{}, no{});
-    if (t + 1 < ntiles) step(t++, yes{}, no{}, no{});
-    if (t < ntiles) step(t, no{}, no{}, no{});
+    const int t_main = min(n_act, ntiles - 3);
+    for (; t < t_main; ++t) step(t, yes{}, yes{}, yes{});
+    for (; t + 3 < ntiles; ++t) idle_step(t, yes{}, yes{});
+    if (t + 2 < ntiles) {
+        if (t < n_act) step(t, yes{}, yes{}, no{});
+        else idle_step(t, yes{}, no{});
+        ++t;
+    }
+    if (t + 1 < ntiles) {
+        if (t < n_act) step(t, yes{}, no{}, no{});
+        else idle_step(t, no{}, no{});
+        ++t;
+    }
+    if (t < ntiles) {
+        if (t < n_act) step(t, no{}, no{}, no{});
+        else idle_step(t, no{}, no{});
+    }
     if (!group_b) lds_barrier();
 
     // ---- epilogue: normalise, write the output (or this split's partial result)
