@@ -35,7 +35,9 @@
  *     1/sqrt(d); a row at position p sees every linked token at position
  *     <= p.
  *   - All device memory belongs to the caller. The library allocates none:
- *     no hipMalloc, no device-side buffers. It owns host metadata only.
+ *     no hipMalloc, no device-side buffers. It owns host metadata and one
+ *     pinned host buffer per store (hipHostMalloc) that plan tables are
+ *     uploaded from, grown as needed and freed by pic_store_destroy.
  *   - Device work is enqueued on the caller's stream and returns
  *     asynchronously; execution faults surface at the caller's next
  *     synchronisation. One thread at a time per store.
@@ -206,9 +208,12 @@ pic_status pic_plan_export(const pic_plan *plan, int32_t *row_pos, int32_t *row_
                            int32_t *cow_dst);
 
 /* Copy the plan's device tables into the caller's workspace (device memory
- * of at least sizes.workspace_bytes, 256-byte aligned). Blocking: returns
- * after the copy on `stream` has completed, so the plan's host memory is free
- * to go. Must precede pic_link_attend with the same workspace. */
+ * of at least sizes.workspace_bytes, 256-byte aligned). Stream-ordered: the
+ * tables are staged into the store's pinned host buffer and the copy is
+ * enqueued on `stream`; the call waits only for the previous upload's copy
+ * out of that buffer. Work already enqueued on `stream` that reads the same
+ * workspace (an earlier link call) runs before the copy. Must precede
+ * pic_link_attend with the same workspace, on the same stream. */
 pic_status pic_plan_upload(pic_store *store, pic_plan *plan, void *workspace, int64_t workspace_bytes,
                            hipStream_t stream);
 
@@ -230,7 +235,10 @@ pic_status pic_link_attend(pic_store *store, const pic_plan *plan, const void *q
                            hipStream_t stream);
 
 /* Free a plan and drop its page references (its private pages return to the
- * pool). Device work that uses the plan must have completed. */
+ * pool, where a later plan may take them). Device work that uses the plan must
+ * have completed, or every later device call on the store must use the same
+ * stream as that work: stream order then keeps the freed pages from being
+ * rewritten before that work has read them. */
 pic_status pic_plan_free(pic_store *store, pic_plan *plan);
 
 /* Per-kernel timing of pic_link_attend with HIP events on the call's stream.

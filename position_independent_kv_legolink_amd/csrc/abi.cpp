@@ -157,6 +157,11 @@ pic_status pic_store_destroy(pic_store *s) {
         for (auto &m : s->pending)
             for (hipEvent_t e : m.ev) (void)hipEventDestroy(e);
         for (hipEvent_t e : s->spare_events) (void)hipEventDestroy(e);
+        if (s->staging_done) {
+            (void)hipEventSynchronize(s->staging_done);
+            (void)hipEventDestroy(s->staging_done);
+        }
+        if (s->staging) (void)hipHostFree(s->staging);
         delete s;
     });
 }
@@ -282,19 +287,33 @@ pic_status pic_plan_upload(pic_store *s, pic_plan *plan, void *workspace, int64_
         if (!workspace || workspace_bytes < plan->workspace_bytes)
             fail(PIC_ERR_WORKSPACE, "workspace needs " + std::to_string(plan->workspace_bytes) + " bytes");
         if (reinterpret_cast<uintptr_t>(workspace) % 256 != 0) fail(PIC_ERR_WORKSPACE, "workspace must be 256-byte aligned");
-        std::vector<uint8_t> blob(plan->table_bytes, 0);
-        auto put = [&](int64_t off, const void *src, size_t bytes) {
-            if (bytes) memcpy(blob.data() + off, src, bytes);
-        };
-        put(plan->off_pages, plan->pages.data(), plan->pages.size() * sizeof(PageDesc));
-        put(plan->off_row_pos, plan->row_pos.data(), plan->row_pos.size() * sizeof(int32_t));
-        put(plan->off_scatter, plan->scatter.data(), plan->scatter.size() * sizeof(ScatterDesc));
-        put(plan->off_work, plan->work.data(), plan->work.size() * sizeof(WorkDesc));
-        put(plan->off_merge, plan->merge.data(), plan->merge.size() * sizeof(MergeDesc));
-        if (!blob.empty()) {
-            check_hip(hipMemcpyAsync(workspace, blob.data(), blob.size(), hipMemcpyHostToDevice, stream),
+        // the tables go through the store's pinned staging buffer, so the copy is asynchronous;
+        // the previous upload's copy out of the buffer must have finished before it is rewritten
+        if (plan->table_bytes > 0) {
+            if (s->staging_done) check_hip(hipEventSynchronize(s->staging_done), "staging buffer wait");
+            if (s->staging_bytes < plan->table_bytes) {
+                const int64_t cap = std::max<int64_t>({plan->table_bytes, 2 * s->staging_bytes, 1 << 16});
+                if (s->staging) check_hip(hipHostFree(s->staging), "hipHostFree");
+                s->staging = nullptr;
+                s->staging_bytes = 0;
+                check_hip(hipHostMalloc(&s->staging, (size_t)cap, hipHostMallocDefault), "hipHostMalloc");
+                s->staging_bytes = cap;
+            }
+            if (!s->staging_done)
+                check_hip(hipEventCreateWithFlags(&s->staging_done, hipEventDisableTiming), "hipEventCreate");
+            uint8_t *blob = static_cast<uint8_t *>(s->staging);
+            memset(blob, 0, (size_t)plan->table_bytes);
+            auto put = [&](int64_t off, const void *src, size_t bytes) {
+                if (bytes) memcpy(blob + off, src, bytes);
+            };
+            put(plan->off_pages, plan->pages.data(), plan->pages.size() * sizeof(PageDesc));
+            put(plan->off_row_pos, plan->row_pos.data(), plan->row_pos.size() * sizeof(int32_t));
+            put(plan->off_scatter, plan->scatter.data(), plan->scatter.size() * sizeof(ScatterDesc));
+            put(plan->off_work, plan->work.data(), plan->work.size() * sizeof(WorkDesc));
+            put(plan->off_merge, plan->merge.data(), plan->merge.size() * sizeof(MergeDesc));
+            check_hip(hipMemcpyAsync(workspace, blob, (size_t)plan->table_bytes, hipMemcpyHostToDevice, stream),
                       "plan upload");
-            check_hip(hipStreamSynchronize(stream), "plan upload");
+            check_hip(hipEventRecord(s->staging_done, stream), "hipEventRecord");
         }
         plan->uploaded_to = workspace;
     });

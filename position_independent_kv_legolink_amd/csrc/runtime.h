@@ -49,6 +49,11 @@ struct pic_store {
     double profiled_ms[4] = {0, 0, 0, 0};   // scatter, attention, merge, key rotation
     std::vector<piclink::ProfileMarks> pending;
     std::vector<hipEvent_t> spare_events;
+    // pinned host buffer the plan tables are uploaded from, and the event recorded after the last
+    // upload's copy out of it
+    void *staging = nullptr;
+    int64_t staging_bytes = 0;
+    hipEvent_t staging_done = nullptr;
 };
 
 struct pic_plan {

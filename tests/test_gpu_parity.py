@@ -338,3 +338,44 @@ def test_rotation_modes_are_bit_identical(case):
     assert ex_a["plan"].sizes["rotated_pages"] == 0 and ex_b["plan"].sizes["rotated_pages"] > 0
     assert np.array_equal(a, b)
     assert np.array_equal(ex_a["lse"], ex_b["lse"])
+
+
+def test_back_to_back_uploads_share_one_workspace():
+    """Plan uploads are stream-ordered: uploading a plan into the workspace that a queued link call
+    still reads does not disturb that call, and the store's staging buffer grows for a plan whose
+    tables exceed it. Outputs match synchronised runs with their own workspaces bit for bit."""
+    cfg = small_cfg(n_requests=24, chunks_per_request=24, chunk_len=100, k=4, pool_size=30)
+    wl_b = Workload(cfg)
+    wl_s = Workload(cfg, n_requests=1)
+    cached = wl_b.cached()
+    B = cfg.page_size
+    jobs = []
+    for wl in (wl_s, wl_b):
+        segs = wl.segments(k=cfg.k)
+        rows = wl.new_rows(segs)
+        jobs.append((wl, segs, rows))
+    private = sum(p.private for _, segs, _ in jobs for s in segs for p in oplan.logical_pages(s, B))
+    stored = sum(-(-v[0].shape[0] // B) for v in cached.values())
+    n_tokens = max(oplan.total_tokens(s) for _, segs, _ in jobs for s in segs)
+    store = gpu_store(cfg, cached, num_pages=stored + private + 8, max_position=n_tokens + 1)
+    plans, tensors = [], []
+    for wl, segs, rows in jobs:
+        plans.append(store.link_plan(wl.link_requests(), k=cfg.k, split_pages=-1))
+        tensors.append([torch.from_numpy(np.concatenate([r[i] for r in rows])).to("cuda", torch.bfloat16).contiguous()
+                        for i in range(3)])
+    assert plans[1].sizes["workspace_bytes"] > 1 << 16
+    refs = []
+    for plan, (q, kn, vn) in zip(plans, tensors):
+        plan.upload()
+        refs.append(pic.link_attend(store, plan, q, kn, vn).float().cpu().numpy())
+    torch.cuda.synchronize()
+    ws = torch.empty(max(p.sizes["workspace_bytes"] for p in plans), dtype=torch.uint8, device="cuda")
+    outs = []
+    for i in (0, 1, 0, 1):
+        plans[i].upload(ws)
+        outs.append((i, pic.link_attend(store, plans[i], *tensors[i])))
+    torch.cuda.synchronize()
+    for i, o in outs:
+        assert np.array_equal(o.float().cpu().numpy(), refs[i])
+    for p in plans:
+        p.free()
