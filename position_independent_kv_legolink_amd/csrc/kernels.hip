@@ -112,14 +112,16 @@ __device__ __forceinline__ void rope8_bf16(const u32x4 &lo, const u32x4 &hi, con
 // Ping-pong schedule: waves 0-3 (group A, one per SIMD) and waves 4-7 (group B) run the same
 // per-tile sequence one phase apart, so that one wave's MFMA phase meets the other wave's VALU
 // phase on every SIMD:
-//   Y(t): RoPE + LDS staging of tile t+2, then the softmax of tile t with the global loads of
-//         tile t+3 spread between its exponentials                                  (VALU)
+//   Y(t): LDS staging of tile t+2 (with the RoPE rotation of its keys unless KR), then the
+//         softmax of tile t with the global loads of tile t+3 spread between its
+//         exponentials                                                              (VALU)
 //   X(t): PV of tile t, QK^T of tile t+1 (MFMAs and their LDS operand reads only)   (MFMA)
 // with a work-group barrier after each phase; group B passes one extra barrier at the start
 // (and group A one at the end), so B's phase k overlaps A's phase k+1. Tile buffers are deep
 // enough for the one-phase skew: K' and key positions x3, V x4. Q carries the softmax scale and
 // log2(e), and the running maximum enters S^T through one bias MFMA per 32-key block, so the
-// common softmax path is exp2, a row sum and the bf16 packing.
+// common softmax path is exp2, a row sum and the bf16 packing. A wave past the last key tile its
+// rows attend keeps staging tiles for the others, with the same barriers, and computes nothing.
 // KR: keys come pre-rotated (rotate_keys, indexed by logical page) and are staged as loaded;
 // otherwise they are rotated here, with the same table values and arithmetic.
 template <int D, bool KR>
@@ -609,7 +611,7 @@ __global__ __launch_bounds__(512, 1) void link_attention_bf16(AttnParams p) {
     // ring slots of tiles t, t+1, t+2: K' and key positions in a ring of 3, V in a ring of 4 (the
     // one-phase skew between the wave groups keeps a V tile in use one phase longer)
     int kc = 0, kn = 1, ks2 = 2, vc = 0;
-    // one tile. Y(t): RoPE + LDS staging of tile t+2 from the registers loaded one step earlier,
+    // one tile. Y(t): LDS staging of tile t+2 from the registers loaded one step earlier,
     // the loads of tile t+3 into the freed registers (a whole step ahead of their use), then the
     // softmax of tile t. X(t): PV of tile t, QK^T of tile t+1, and the page descriptors of the
     // next step's loads.
