@@ -1,17 +1,20 @@
 """Link-step benchmark on one MI355X.
 
 A step is one pass of the whole link path over one batch: link_plan (host),
-plan upload, copy-on-write scatter, attention, and split merge. The default
-workload is the 50,304-token request (64-token prefix + 98 x 512-token chunks
-+ 64-token suffix, LegoLink-32, Llama-3-8B layer shape, bf16). Its chunk KV and
-new rows are seeded synthetic data, resident in HBM before timing starts.
+plan upload, copy-on-write scatter, key rotation (when the plan rotates keys
+ahead of attention), attention, and split merge. The default workload is the
+50,304-token request (64-token prefix + 98 x 512-token chunks + 64-token
+suffix, LegoLink-32, Llama-3-8B layer shape, bf16). Its chunk KV and new rows
+are seeded synthetic data, resident in HBM before timing starts.
 
 Output: one JSON line with the step throughput (algorithmic TFLOP/s), the
 attention kernel's roofline position (timed live with HIP events on the
-stream it runs on), the dense full-recompute comparator on the same inputs,
-and the fp64 CPU oracle timed on a bounded sample of rows.
+stream it runs on), the same step with the 256 MiB MALL evicted before each
+step ("cold"), the dense full-recompute comparator on the same inputs, and
+the fp64 CPU oracle timed on a bounded sample of rows.
 
     python bench.py [--steps K] [--warmup W] [--workload NAME] [--no-cpu-baseline] [--no-dense]
+                    [--cold-steps N] [--rope-keys 0|1|2] [--split-pages P]
 """
 from __future__ import annotations
 
@@ -147,6 +150,27 @@ def time_steps(job, steps, warmup):
     prof = job.store.profile_read()
     job.store.profile_enable(False)
     return (t1 - t0) * 1e3 / steps, prof
+
+
+def time_steps_cold(job, steps, evict_mib=512):
+    """Each step after a write of evict_mib MiB of scratch (the 256 MiB MALL holds none of the
+    link step's data afterwards), timed on its own between synchronisations; the eviction is
+    outside the timed interval. Returns (mean ms per step, per-kernel profile)."""
+    torch = job.torch
+    scratch = torch.empty(evict_mib << 20, dtype=torch.uint8, device="cuda")
+    job.store.profile_enable(True)
+    total = 0.0
+    for i in range(steps):
+        scratch.fill_(i & 0xff)
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        job.step()
+        torch.cuda.synchronize()
+        total += time.perf_counter() - t0
+    prof = job.store.profile_read()
+    job.store.profile_enable(False)
+    del scratch
+    return total * 1e3 / steps, prof
 
 
 def dense_comparator(job, reps=3):
@@ -316,6 +340,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=20.0)
     ap.add_argument("--no-dense", action="store_true")
+    ap.add_argument("--cold-steps", type=int, default=10,
+                    help="extra steps, each after evicting the MALL, reported under 'cold' (0: none)")
     ap.add_argument("--rope-keys", type=int, default=0, choices=(0, 1, 2),
                     help="key rotation: 0 automatic, 1 inside attention, 2 once ahead of attention")
     ap.add_argument("--split-pages", type=int, default=0,
@@ -386,6 +412,17 @@ def main():
     roofline = dict(bound="mfma", achieved=round(achieved, 2), peak=peak, unit="TFLOP/s",
                     frac=round(achieved / peak, 4), traffic=traffic_from_profiles(cfg.name))
 
+    cold = None
+    if args.cold_steps > 0:
+        c_ms, c_prof = time_steps_cold(job, args.cold_steps)
+        cc = max(c_prof["calls"], 1)
+        c_attn = c_prof["attention_ms"] / cc
+        cold = {"steps": args.cold_steps, "evict_mib": 512, "ms_per_step": round(c_ms, 4),
+                "attention_ms": round(c_attn, 4), "attention_tflops": round(flop / (c_attn * 1e-3) / 1e12, 2),
+                "rotate_ms": round(c_prof["rotate_ms"] / cc, 4), "scatter_ms": round(c_prof["scatter_ms"] / cc, 4),
+                "merge_ms": round(c_prof["merge_ms"] / cc, 4)}
+        log(f"cold (MALL evicted before each step, steps not overlapped with planning): {cold}")
+
     dense = None
     if not args.no_dense:
         dense = dense_comparator(job)
@@ -427,6 +464,7 @@ def main():
         "hbm_frac": round(total_bytes / (link_ms * 1e-3) / 1e9 / PEAK_HBM_GBPS, 4),
         "mfma_frac_step": round(flop / (ms_step * 1e-3) / 1e12 / peak, 4),
         "roofline": roofline,
+        "cold": cold,
         "dense_comparator": dense,
         "cpu_baseline": cpu,
         "kernel_source_sha256_16": kernel_hash(),
