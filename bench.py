@@ -379,6 +379,18 @@ def main():
                                                  cfg.suffix_len) // cfg.page_size)) * cfg.n_requests
     job = LinkJob(cfg, dense_pages=dense_pages, rope_keys=args.rope_keys, split_pages=args.split_pages)
     flop, attn_bytes, total_bytes = algorithmic_counts(cfg, job.export, job.sizes, job.n_tokens)
+    # page sharing: logical pages the requests read vs the distinct physical pages behind them
+    elem = 2 if cfg.dtype == "bf16" else 4
+    page_bytes = cfg.num_kv_heads * cfg.page_size * cfg.head_dim * elem
+    logical = int(job.sizes["pages"])
+    distinct = int(np.unique(job.export["block_table"]).size)
+    kv_pages = {"logical": logical, "distinct": distinct, "sharing_ratio": round(logical / max(distinct, 1), 3),
+                "unique_kv_mb": round(2 * distinct * page_bytes / 1e6, 1),
+                "logical_kv_mb": round(2 * logical * page_bytes / 1e6, 1)}
+    t = time.perf_counter()
+    for _ in range(10):
+        job.store.link_plan(job.requests, **job.plan_kw).free()
+    plan_ms = (time.perf_counter() - t) * 1e3 / 10
     log(f"{cfg.name}: rows {job.sizes['rows']}, pages {job.sizes['pages']}, work items {job.sizes['work_items']} "
         f"({job.sizes['split_items']} split), {flop / 1e9:.1f} GFLOP, {total_bytes / 1e6:.1f} MB")
 
@@ -403,7 +415,6 @@ def main():
         f"merge {merge_ms:.4f} ms")
     # key rotation pass: every rotated page's keys read and written, its cos/sin rows read once
     rot_pages = job.sizes["rotated_pages"]
-    elem = 2 if cfg.dtype == "bf16" else 4
     rot_bytes = rot_pages * (2 * cfg.num_kv_heads * cfg.page_size * cfg.head_dim * elem
                              + cfg.page_size * cfg.head_dim * 4)
 
@@ -458,6 +469,8 @@ def main():
         "keys_rotated_ahead": rot_pages > 0,
         "rotate_ms": round(rotate_ms, 4),
         "rotate_gbps": round(rot_bytes / (rotate_ms * 1e-3) / 1e9, 1) if rotate_ms > 0 else None,
+        "link_plan_host_ms": round(plan_ms, 4),
+        "kv_pages": kv_pages,
         "algorithmic_gflop": round(flop / 1e9, 3),
         "algorithmic_mb": round(total_bytes / 1e6, 2),
         "hbm_gbps": round(total_bytes / (link_ms * 1e-3) / 1e9, 1),
