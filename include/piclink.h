@@ -112,7 +112,9 @@ typedef struct {
  *              the workspace, before attention (bfloat16 stores only; the results
  *              are bit-identical to 1); 0 = automatic: 2 for bfloat16 stores when
  *              the work list reads each key page at least 8 times on average,
- *              else 1. Other values: PIC_ERR_INVALID. */
+ *              else 1. Other values: PIC_ERR_INVALID.
+ * decode       1: also prepare pic_link_decode (bfloat16 stores; keys are then always
+ *              rotated ahead, so rope_keys must be 0 or 2); 0: link only */
 typedef struct {
     int32_t k;
     int32_t block_level;
@@ -120,12 +122,14 @@ typedef struct {
     int32_t recompute_all;
     int32_t split_pages;
     int32_t rope_keys;
+    int32_t decode;
 } pic_link_options;
 
 /* Sizes of a plan. rows = selected rows R over all requests (the first dim of
  * q_new/k_new/v_new/out); pages = logical pages over all requests;
  * rotated_pages = logical pages whose keys pic_link_attend rotates into the
- * workspace before attention (0: keys are rotated inside attention). */
+ * workspace before attention (0: keys are rotated inside attention);
+ * decode_items = split-KV work items of pic_link_decode (0: plan not made for decode). */
 typedef struct {
     int64_t rows;
     int64_t pages;
@@ -136,6 +140,7 @@ typedef struct {
     int64_t workspace_bytes;
     int64_t requests;
     int64_t rotated_pages;
+    int64_t decode_items;
 } pic_plan_sizes;
 
 /* Device bytes the caller must provide: each K and V pool
@@ -233,6 +238,23 @@ pic_status pic_plan_upload(pic_store *store, pic_plan *plan, void *workspace, in
 pic_status pic_link_attend(pic_store *store, const pic_plan *plan, const void *q_new, const void *k_new,
                            const void *v_new, void *out, float *lse, void *workspace, int64_t workspace_bytes,
                            hipStream_t stream);
+
+/* Decode after link: one generation step per request (EPIC digest, abstract: chunks are
+ * compiled, then linked, then the request generates; MEPIC abstract: the paged, shared cache
+ * serves the request). For every request r of a plan made with opts.decode = 1, after
+ * pic_link_attend ran on the same workspace: the new token at position p_r, the position after
+ * the request's last linked token, attends over the request's linked cache (all positions
+ * < p_r, with the recomputed rows' K/V that pic_link_attend scattered) and over itself.
+ *   q      [n_req][Hq][d]   the new tokens' queries, pre-RoPE
+ *   k, v   [n_req][Hkv][d]  their keys (pre-RoPE) and values; read, not written to the pool
+ *   out    [n_req][Hq][d]   attention output, store dtype
+ *   lse    [n_req][Hq]      optional float32 natural-log softmax denominators
+ * The cache's keys are read as pic_link_attend rotated them into the workspace. Split-KV: every
+ * (request, KV head) is cut into page ranges whose partial results are merged with the new
+ * token's own score. Errors: PIC_ERR_STATE (plan not made for decode, or not attended on this
+ * workspace), PIC_ERR_WORKSPACE, PIC_ERR_INVALID (null tensor). Asynchronous on `stream`. */
+pic_status pic_link_decode(pic_store *store, const pic_plan *plan, const void *q, const void *k, const void *v,
+                           void *out, float *lse, void *workspace, int64_t workspace_bytes, hipStream_t stream);
 
 /* Free a plan and drop its page references (its private pages return to the
  * pool, where a later plan may take them). Device work that uses the plan must

@@ -23,7 +23,8 @@ DTYPES = {"bf16": 0, "f32": 1}
 
 EXPORTS = ["pic_store_sizes", "pic_store_create", "pic_store_destroy", "pic_store_chunk",
            "pic_store_chunk_pages", "pic_store_release", "pic_store_stats", "pic_link_plan",
-           "pic_plan_info", "pic_plan_export", "pic_plan_upload", "pic_link_attend", "pic_plan_free",
+           "pic_plan_info", "pic_plan_export", "pic_plan_upload", "pic_link_attend", "pic_link_decode",
+           "pic_plan_free",
            "pic_profile_enable", "pic_profile_read", "pic_last_error"]
 
 
@@ -49,14 +50,14 @@ class Request(ctypes.Structure):
 class LinkOptions(ctypes.Structure):
     _fields_ = [("k", ctypes.c_int32), ("block_level", ctypes.c_int32), ("pos_offset", ctypes.c_int32),
                 ("recompute_all", ctypes.c_int32), ("split_pages", ctypes.c_int32),
-                ("rope_keys", ctypes.c_int32)]
+                ("rope_keys", ctypes.c_int32), ("decode", ctypes.c_int32)]
 
 
 class PlanSizes(ctypes.Structure):
     _fields_ = [("rows", ctypes.c_int64), ("pages", ctypes.c_int64), ("private_pages", ctypes.c_int64),
                 ("cow_pages", ctypes.c_int64), ("work_items", ctypes.c_int64),
                 ("split_items", ctypes.c_int64), ("workspace_bytes", ctypes.c_int64),
-                ("requests", ctypes.c_int64), ("rotated_pages", ctypes.c_int64)]
+                ("requests", ctypes.c_int64), ("rotated_pages", ctypes.c_int64), ("decode_items", ctypes.c_int64)]
 
 
 _lib = None
@@ -85,6 +86,7 @@ def lib():
             "pic_plan_export": [vp, vp, vp, vp, vp, vp, vp, vp, vp],
             "pic_plan_upload": [vp, vp, vp, i64, vp],
             "pic_link_attend": [vp, vp, vp, vp, vp, vp, vp, vp, i64, vp],
+            "pic_link_decode": [vp, vp, vp, vp, vp, vp, vp, vp, i64, vp],
             "pic_plan_free": [vp, vp],
             "pic_profile_enable": [vp, i32],
             "pic_profile_read": [vp, P(ctypes.c_double), P(i32)],
@@ -193,7 +195,7 @@ class Store:
         return dict(free_pages=f.value, chunks=c.value, plans=p.value)
 
     def link_plan(self, requests, *, k=0, block_level=False, pos_offset=0, recompute_all=False,
-                  split_pages=0, rope_keys=0):
+                  split_pages=0, rope_keys=0, decode=False):
         n = len(requests)
         reqs = (Request * max(n, 1))()
         keep = []
@@ -204,7 +206,7 @@ class Store:
                               ctypes.cast(ids, ctypes.POINTER(ctypes.c_uint64)), len(r.chunk_ids),
                               int(r.suffix_len))
         opts = LinkOptions(int(k), int(bool(block_level)), int(pos_offset), int(bool(recompute_all)),
-                           int(split_pages), int(rope_keys))
+                           int(split_pages), int(rope_keys), int(bool(decode)))
         h = ctypes.c_void_p()
         _check(lib().pic_link_plan(self.handle, reqs, n, ctypes.byref(opts), ctypes.byref(h)))
         return Plan(self, h)
@@ -283,4 +285,30 @@ def link_attend(store: Store, plan: Plan, q_new, k_new, v_new, out=None, lse=Non
     ws = plan.workspace
     _check(lib().pic_link_attend(store.handle, plan.handle, _ptr(q_new), _ptr(k_new), _ptr(v_new), _ptr(out),
                                  _ptr(lse), _ptr(ws), ws.numel(), _stream()))
+    return out
+
+
+def link_decode(store: Store, plan: Plan, q, k, v, out=None, lse=None):
+    """One decode step after link_attend with the same plan and workspace: every request's new
+    token ([n_req][Hq][d] queries, [n_req][Hkv][d] keys and values, pre-RoPE) attends over the
+    request's linked cache and itself. Returns ``out`` [n_req][Hq][d]."""
+    import torch
+    c = store.cfg
+    n = plan.sizes["requests"]
+    tdt = store.k_pool.dtype
+    for name, t, h in (("q", q, c.num_q_heads), ("k", k, c.num_kv_heads), ("v", v, c.num_kv_heads)):
+        if tuple(t.shape) != (n, h, c.head_dim) or t.dtype != tdt or not t.is_contiguous() or t.device.type != "cuda":
+            raise ValueError(f"{name} must be a contiguous {tdt} device tensor of shape {(n, h, c.head_dim)}")
+    if out is None:
+        out = torch.empty((n, c.num_q_heads, c.head_dim), dtype=tdt, device=q.device)
+    if tuple(out.shape) != (n, c.num_q_heads, c.head_dim) or out.dtype != tdt or not out.is_contiguous():
+        raise ValueError("out has the wrong shape or dtype")
+    if lse is not None and (tuple(lse.shape) != (n, c.num_q_heads) or lse.dtype != torch.float32
+                            or not lse.is_contiguous()):
+        raise ValueError("lse must be a contiguous float32 tensor [n_req][Hq]")
+    if plan.workspace is None:
+        raise RuntimeError("upload the plan and run link_attend before link_decode")
+    ws = plan.workspace
+    _check(lib().pic_link_decode(store.handle, plan.handle, _ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse),
+                                 _ptr(ws), ws.numel(), _stream()))
     return out

@@ -254,6 +254,7 @@ pic_status pic_plan_info(const pic_plan *plan, pic_plan_sizes *sz) {
         sz->workspace_bytes = plan->workspace_bytes;
         sz->requests = plan->n_requests;
         sz->rotated_pages = plan->rotate_keys ? (int64_t)plan->pages.size() : 0;
+        sz->decode_items = (int64_t)plan->dec_work.size();
     });
 }
 
@@ -311,6 +312,9 @@ pic_status pic_plan_upload(pic_store *s, pic_plan *plan, void *workspace, int64_
             put(plan->off_scatter, plan->scatter.data(), plan->scatter.size() * sizeof(ScatterDesc));
             put(plan->off_work, plan->work.data(), plan->work.size() * sizeof(WorkDesc));
             put(plan->off_merge, plan->merge.data(), plan->merge.size() * sizeof(MergeDesc));
+            put(plan->off_dec_pos, plan->dec_pos.data(), plan->dec_pos.size() * sizeof(int32_t));
+            put(plan->off_dec_work, plan->dec_work.data(), plan->dec_work.size() * sizeof(DecodeDesc));
+            put(plan->off_dec_merge, plan->dec_merge.data(), plan->dec_merge.size() * sizeof(DecodeMergeDesc));
             check_hip(hipMemcpyAsync(workspace, blob, (size_t)plan->table_bytes, hipMemcpyHostToDevice, stream),
                       "plan upload");
             check_hip(hipEventRecord(s->staging_done, stream), "hipEventRecord");
@@ -370,10 +374,40 @@ pic_status pic_link_attend(pic_store *s, const pic_plan *plan, const void *q_new
                   "attention launch");
         if (prof) check_hip(hipEventRecord(marks.ev[3], stream), "hipEventRecord");
         check_hip(launch_merge(s->shape, t, out, lse, stream), "merge launch");
+        const_cast<pic_plan *>(plan)->attended_ws = workspace;
         if (prof) {
             check_hip(hipEventRecord(marks.ev[4], stream), "hipEventRecord");
             s->pending.push_back(marks);
         }
+    });
+}
+
+pic_status pic_link_decode(pic_store *s, const pic_plan *plan, const void *q, const void *k, const void *v,
+                           void *out, float *lse, void *workspace, int64_t workspace_bytes, hipStream_t stream) {
+    return guarded([&] {
+        if (!s || !plan) fail(PIC_ERR_INVALID, "null argument");
+        if (plan->owner != s) fail(PIC_ERR_INVALID, "plan belongs to another store");
+        if (!s->k_pool) fail(PIC_ERR_STATE, "metadata-only store has no device");
+        if (!plan->decode) fail(PIC_ERR_STATE, "plan was not made for decode (opts.decode)");
+        if (!plan->uploaded_to || plan->uploaded_to != workspace)
+            fail(PIC_ERR_WORKSPACE, "workspace is not the one this plan was uploaded to");
+        if (workspace_bytes < plan->workspace_bytes) fail(PIC_ERR_WORKSPACE, "workspace too small");
+        if (plan->attended_ws != workspace)
+            fail(PIC_ERR_STATE, "run pic_link_attend on this workspace first (it rotates the keys decode reads)");
+        if (plan->n_requests == 0) return;
+        if (!q || !k || !v || !out) fail(PIC_ERR_INVALID, "null tensor");
+        uint8_t *ws = static_cast<uint8_t *>(workspace);
+        DecodeTables t;
+        t.pages = reinterpret_cast<const PageDesc *>(ws + plan->off_pages);
+        t.dec_pos = reinterpret_cast<const int32_t *>(ws + plan->off_dec_pos);
+        t.work = reinterpret_cast<const DecodeDesc *>(ws + plan->off_dec_work);
+        t.n_work = (int)plan->dec_work.size();
+        t.merge = reinterpret_cast<const DecodeMergeDesc *>(ws + plan->off_dec_merge);
+        t.n_merge = (int)plan->dec_merge.size();
+        t.part_o = reinterpret_cast<float *>(ws + plan->off_dec_o);
+        t.part_lse = reinterpret_cast<float *>(ws + plan->off_dec_lse);
+        t.k_rot = plan->rotate_keys ? ws + plan->off_k_rot : nullptr;
+        check_hip(launch_decode(s->shape, q, k, v, s->v_pool, s->rope, t, out, lse, stream), "decode launch");
     });
 }
 

@@ -8,6 +8,8 @@
 //                  RoPE applied in registers at each token's absolute position, grouped-query
 //                  rows of one KV head per work group, MFMA for QK^T and PV, online softmax
 //   link_merge     log-sum-exp combination of split KV ranges
+//   link_decode    decode after link: each request's new token over its linked pages (split-KV),
+//                  then the merge of the ranges with the token's own key
 //
 // Method: EPIC (atlas.scime.ai summary, "Approach": chunks compiled from position 0, the first
 // k tokens of every chunk recomputed at link time) and MEPIC (searcharxiv.org abstract:
@@ -1109,6 +1111,269 @@ __global__ __launch_bounds__(kThreads) void rotate_keys_bf16(const PageDesc *pag
     }
 }
 
+// ---------------------------------------------------------------------------------------------
+// Decode after link (bf16). One work group (4 waves) per DecodeDesc item: the new token's G query
+// heads of one KV head over a page range of its request. The G heads take the columns of the
+// 32x32 MFMA blocks (lanes of rows G..31 hold zero queries), so the arithmetic is that of
+// link_attention_bf16 with one 32-key block at a time:
+//   S^T = K' Q'^T   (A = 32 keys loaded from the rotated-key workspace straight into registers)
+//   O^T += V^T P^T  (A = V^T from transposing LDS reads of the block's values, staged per wave)
+// Wave w takes the item's 32-key blocks w, w+4, ... with its own online softmax (fp32, log2
+// units; every key of the cache lies before the new token, so only padding is masked). The four
+// waves' results are merged through LDS into the item's partial slot: the normalised output and
+// its log2-sum-exp.
+struct DecodeParams {
+    const void *q;
+    const void *k_rot;
+    const void *v_pool;
+    const float *rope;
+    const PageDesc *pages;
+    const int32_t *dec_pos;
+    const DecodeDesc *work;
+    float *part_o;
+    float *part_lse;
+    int hq, hkv, gshift, pshift;
+    int64_t page_elems;
+    float scale_log2;
+};
+
+template <int D>
+__global__ __launch_bounds__(256, 2) void link_decode_bf16(DecodeParams p) {
+    constexpr int NS = D / 16;          // k-steps of QK^T; also 16-byte V pieces per lane
+    constexpr int NDB = D / 32;
+    constexpr int VS = D + 32;          // V row stride in LDS, as in link_attention_bf16
+    constexpr int NW = 4;
+    constexpr int MAXG = 8;
+    __shared__ __attribute__((aligned(16))) uint16_t vbuf[NW * 32 * VS];
+    __shared__ __attribute__((aligned(16))) int kval[NW * 32];
+    __shared__ float obuf[NW * MAXG * D];
+    __shared__ float mbuf[NW * MAXG], lbuf[NW * MAXG];
+
+    const DecodeDesc w = p.work[blockIdx.x];
+    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, ln = lane & 31, lg = lane >> 5;
+    const int G = 1 << p.gshift;
+    const int page_size = 1 << p.pshift;
+    const int n_pages = w.page_end - w.page_begin;
+    const int lpage0 = w.page_base + w.page_begin;
+    const int64_t head_off = (int64_t)w.kv_head * page_size * D;   // elements
+    const uint32_t page_bytes = (uint32_t)p.page_elems * 2u;
+
+    // rotated, scaled query fragments of head ln (zero beyond the G heads)
+    u32x4 qf[NS];
+    {
+        const bool valid = ln < G;
+        const int qpos = p.dec_pos[w.request];
+        const uint16_t *qrow =
+            static_cast<const uint16_t *>(p.q) + ((int64_t)w.request * p.hq + w.kv_head * G + (valid ? ln : 0)) * D;
+        const float *cs = p.rope + (int64_t)qpos * D;
+#pragma unroll
+        for (int s = 0; s < NS / 2; ++s) {
+            const int e0 = 16 * s + 8 * lg;
+            u32x4 lo = {0, 0, 0, 0}, hi = {0, 0, 0, 0};
+            if (valid) {
+                lo = *reinterpret_cast<const u32x4 *>(qrow + e0);
+                hi = *reinterpret_cast<const u32x4 *>(qrow + D / 2 + e0);
+            }
+            floatx4 c[2], sn[2];
+            c[0] = *reinterpret_cast<const floatx4 *>(cs + e0);
+            c[1] = *reinterpret_cast<const floatx4 *>(cs + e0 + 4);
+            sn[0] = *reinterpret_cast<const floatx4 *>(cs + D / 2 + e0);
+            sn[1] = *reinterpret_cast<const floatx4 *>(cs + D / 2 + e0 + 4);
+#pragma unroll
+            for (int h = 0; h < 2; ++h) {
+                c[h] *= p.scale_log2;
+                sn[h] *= p.scale_log2;
+            }
+            rope8_bf16(lo, hi, c, sn, qf[s], qf[s + NS / 2]);
+        }
+    }
+
+    floatx16 oacc[NDB];
+#pragma unroll
+    for (int db = 0; db < NDB; ++db) oacc[db] = (floatx16)(0.0f);
+    float m_run = -INFINITY, l_run = 0.0f;
+
+    uint16_t *vb = vbuf + wave * 32 * VS;
+    int *kv = kval + wave * 32;
+    const char *krot_b = static_cast<const char *>(p.k_rot);
+    const char *vpool_b = static_cast<const char *>(p.v_pool);
+    const int nblk = (n_pages * page_size + 31) >> 5;
+    for (int blk = wave; blk < nblk; blk += NW) {
+        // the lane's key (both lane halves hold key ln: the A operand's row and half of its V row)
+        const int kk = blk * 32 + ln;
+        const int rel = kk >> p.pshift;
+        const int slot = kk & (page_size - 1);
+        const bool in_range = rel < n_pages;
+        const int lp = lpage0 + (in_range ? rel : n_pages - 1);
+        const PageDesc pd = p.pages[lp];
+        const bool ok = in_range && slot < pd.valid;
+        const uint32_t row_off = (uint32_t)(head_off + slot * D) * 2u;
+        const char *krow = krot_b + (uint64_t)(uint32_t)lp * page_bytes + row_off;
+        const char *vrow = vpool_b + (uint64_t)(uint32_t)pd.phys * page_bytes + row_off;
+        // K: NS 16-byte pieces of the A operand; V: the lane half's D/2 values, NS pieces of 8
+        bf16x8 ka[NS];
+        u32x4 vr[NS];
+#pragma unroll
+        for (int s = 0; s < NS; ++s) ka[s] = *reinterpret_cast<const bf16x8 *>(krow + (16 * s + 8 * lg) * 2);
+#pragma unroll
+        for (int i = 0; i < NS; ++i) vr[i] = *reinterpret_cast<const u32x4 *>(vrow + (lg * D / 2 + 8 * i) * 2);
+        // the previous block's transposing reads of this wave's V buffer are complete
+        __builtin_amdgcn_s_waitcnt(0xc07f);   // lgkmcnt(0)
+        __builtin_amdgcn_wave_barrier();
+#pragma unroll
+        for (int i = 0; i < NS; ++i) *reinterpret_cast<u32x4 *>(&vb[ln * VS + lg * D / 2 + 8 * i]) = vr[i];
+        if (lg == 0) kv[ln] = ok ? 1 : 0;
+
+        floatx16 sacc = (floatx16)(0.0f);
+#pragma unroll
+        for (int s = 0; s < NS; ++s)
+            sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[s], __builtin_bit_cast(bf16x8, qf[s]), sacc, 0, 0, 0);
+        __builtin_amdgcn_s_waitcnt(0xc07f);
+        __builtin_amdgcn_wave_barrier();
+        // S^T lane layout: column ln (head), rows 8 (r / 4) + 4 lg + r % 4 (keys of the block)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const i32x4 k4 = *reinterpret_cast<const i32x4 *>(&kv[8 * i + 4 * lg]);
+#pragma unroll
+            for (int j = 0; j < 4; ++j) sacc[4 * i + j] = k4[j] ? sacc[4 * i + j] : -INFINITY;
+        }
+        float mx = sacc[0];
+#pragma unroll
+        for (int r = 1; r < 16; ++r) mx = fmaxf(mx, sacc[r]);
+        const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(mx), __float_as_uint(mx), false, false);
+        mx = fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1]));
+        const float m_new = fmaxf(m_run, mx);
+        const float base = m_new == -INFINITY ? 0.0f : m_new;
+        const float alpha = __builtin_amdgcn_exp2f(m_run - base);
+        float e[16];
+        float lsum = 0.0f;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+            e[r] = __builtin_amdgcn_exp2f(sacc[r] - base);
+            lsum += e[r];
+        }
+        const auto sl = __builtin_amdgcn_permlane32_swap(__float_as_uint(lsum), __float_as_uint(lsum), false, false);
+        lsum = __uint_as_float(sl[0]) + __uint_as_float(sl[1]);
+        l_run = l_run * alpha + lsum;
+        m_run = m_new;
+        u32x4 pf[2];
+#pragma unroll
+        for (int s2 = 0; s2 < 2; ++s2)
+#pragma unroll
+            for (int u = 0; u < 4; ++u) pf[s2][u] = pack_bf16(e[8 * s2 + 2 * u], e[8 * s2 + 2 * u + 1]);
+        // O^T += V^T P^T over the block's 32 keys (two k-steps of 16)
+        typedef short v4s __attribute__((ext_vector_type(4)));
+        const int gi = lane >> 4, jj = (lane >> 2) & 3, qq = lane & 3;
+        const uint16_t *vt = vb + (4 * lg + jj) * VS + 16 * (gi & 1) + 4 * qq;
+#pragma unroll
+        for (int db = 0; db < NDB; ++db) {
+            oacc[db] *= alpha;
+#pragma unroll
+            for (int s2 = 0; s2 < 2; ++s2) {
+                const uint16_t *a = vt + (16 * s2) * VS + db * 32;
+                const v4s lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) v4s *)a);
+                const v4s hi =
+                    __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) v4s *)(a + 8 * VS));
+                const bf16x8 av = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+                oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, __builtin_bit_cast(bf16x8, pf[s2]), oacc[db], 0,
+                                                                   0, 0);
+            }
+        }
+    }
+
+    // the four waves' (m, l, O) of every head, merged through LDS
+    if (ln < G) {
+        if (lg == 0) {
+            mbuf[wave * MAXG + ln] = m_run;
+            lbuf[wave * MAXG + ln] = l_run;
+        }
+#pragma unroll
+        for (int db = 0; db < NDB; ++db)
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+#pragma unroll
+                for (int j = 0; j < 4; ++j) obuf[(wave * MAXG + ln) * D + db * 32 + 8 * i + 4 * lg + j] = oacc[db][4 * i + j];
+    }
+    __syncthreads();
+    for (int t = tid; t < G * D; t += 256) {
+        const int h = t / D, d = t % D;
+        float m = -INFINITY;
+#pragma unroll
+        for (int v = 0; v < NW; ++v) m = fmaxf(m, mbuf[v * MAXG + h]);
+        float l = 0.0f, o = 0.0f;
+        if (m != -INFINITY) {
+#pragma unroll
+            for (int v = 0; v < NW; ++v) {
+                const float f = __builtin_amdgcn_exp2f(mbuf[v * MAXG + h] - m);
+                l += lbuf[v * MAXG + h] * f;
+                o += obuf[(v * MAXG + h) * D + d] * f;
+            }
+        }
+        const bool any = l > 0.0f;
+        p.part_o[((int64_t)w.partial * G + h) * D + d] = any ? o / l : 0.0f;
+        if (d == 0) p.part_lse[(int64_t)w.partial * G + h] = any ? m + __builtin_amdgcn_logf(l) : -INFINITY;
+    }
+}
+
+// Decode merge: one wave per (request, query head). The new token's own score (its rotated query
+// against its rotated key, both rounded to bf16 as the attention kernels round them) joins the
+// partial results of the request's page ranges; the output is their log-sum-exp weighted mean.
+struct DecodeMergeParams {
+    const void *q, *k, *v;
+    const float *rope;
+    const int32_t *dec_pos;
+    const DecodeMergeDesc *merge;
+    const float *part_o;
+    const float *part_lse;
+    void *out;
+    float *lse;
+    int hq, hkv, gshift;
+    float scale_log2;
+};
+
+template <int D>
+__global__ __launch_bounds__(64) void link_decode_merge(DecodeMergeParams p) {
+    const int G = 1 << p.gshift;
+    const DecodeMergeDesc md = p.merge[blockIdx.x >> p.gshift];
+    const int hl = blockIdx.x & (G - 1), h = md.kv_head * G + hl;
+    const int lane = threadIdx.x;
+    const int i = lane & (D / 2 - 1);   // rotation pair (i, i + D/2); lanes past D/2 repeat it
+    const bool owner = lane < D / 2;
+    const int pos = p.dec_pos[md.request];
+    const float c = p.rope[(int64_t)pos * D + i], sn = p.rope[(int64_t)pos * D + D / 2 + i];
+    const uint16_t *qr = static_cast<const uint16_t *>(p.q) + ((int64_t)md.request * p.hq + h) * D;
+    const uint16_t *kr = static_cast<const uint16_t *>(p.k) + ((int64_t)md.request * p.hkv + md.kv_head) * D;
+    const uint16_t *vr = static_cast<const uint16_t *>(p.v) + ((int64_t)md.request * p.hkv + md.kv_head) * D;
+    const float qx = bf_lo(qr[i]), qy = bf_lo(qr[i + D / 2]);
+    const float kx = bf_lo(kr[i]), ky = bf_lo(kr[i + D / 2]);
+    const float cq = c * p.scale_log2, sq = sn * p.scale_log2;
+    const uint32_t qp = pack_bf16(fmaf(qx, cq, -qy * sq), fmaf(qy, cq, qx * sq));
+    const uint32_t kp = pack_bf16(fmaf(kx, c, -ky * sn), fmaf(ky, c, kx * sn));
+    float dot = owner ? bf_lo(qp) * bf_lo(kp) + bf_hi(qp) * bf_hi(kp) : 0.0f;
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) dot += __shfl_xor(dot, o);
+    const float s_new = dot;   // log2 units
+    float m = s_new;
+    for (int j = 0; j < md.n_split; ++j) m = fmaxf(m, p.part_lse[(int64_t)(md.slot0 + j) * G + hl]);
+    const float f_new = __builtin_amdgcn_exp2f(s_new - m);
+    float den = f_new, o0 = f_new * bf_lo(vr[i]), o1 = f_new * bf_lo(vr[i + D / 2]);
+    for (int j = 0; j < md.n_split; ++j) {
+        const int64_t sl = (int64_t)(md.slot0 + j) * G + hl;
+        const float f = __builtin_amdgcn_exp2f(p.part_lse[sl] - m);
+        den += f;
+        o0 += f * p.part_o[sl * D + i];
+        o1 += f * p.part_o[sl * D + i + D / 2];
+    }
+    if (owner) {
+        uint16_t *orow = static_cast<uint16_t *>(p.out) + ((int64_t)md.request * p.hq + h) * D;
+        const uint32_t w = pack_bf16(o0 / den, o1 / den);
+        orow[i] = (uint16_t)(w & 0xffffu);
+        orow[i + D / 2] = (uint16_t)(w >> 16);
+        if (lane == 0 && p.lse)
+            p.lse[(int64_t)md.request * p.hq + h] = (m + __builtin_amdgcn_logf(den)) * 0.6931471805599453f;
+    }
+}
+
 int log2_exact(int x) {
     int s = 0;
     while ((1 << s) < x) ++s;
@@ -1193,6 +1458,56 @@ hipError_t launch_attention(const LayerShape &s, const void *q, const void *k_po
         if (s.d == 128) hipLaunchKernelGGL(link_attention_f32<128>, grid, dim3(kThreads), 0, stream, p);
         else hipLaunchKernelGGL(link_attention_f32<64>, grid, dim3(kThreads), 0, stream, p);
     }
+    return hipGetLastError();
+}
+
+hipError_t launch_decode(const LayerShape &s, const void *q, const void *k, const void *v, const void *v_pool,
+                         const float *rope, const DecodeTables &t, void *out, float *lse, hipStream_t stream) {
+    if (s.dtype != 0) return hipErrorInvalidValue;
+    const int gshift = log2_exact(s.hq / s.hkv);
+    const float scale_log2 = 1.4426950408889634f / sqrtf((float)s.d);
+    if (t.n_work > 0) {
+        if (!t.k_rot) return hipErrorInvalidValue;
+        DecodeParams p;
+        p.q = q;
+        p.k_rot = t.k_rot;
+        p.v_pool = v_pool;
+        p.rope = rope;
+        p.pages = t.pages;
+        p.dec_pos = t.dec_pos;
+        p.work = t.work;
+        p.part_o = t.part_o;
+        p.part_lse = t.part_lse;
+        p.hq = s.hq;
+        p.hkv = s.hkv;
+        p.gshift = gshift;
+        p.pshift = log2_exact(s.page_size);
+        p.page_elems = s.page_elems;
+        p.scale_log2 = scale_log2;
+        if (s.d == 128) hipLaunchKernelGGL(link_decode_bf16<128>, dim3(t.n_work), dim3(256), 0, stream, p);
+        else hipLaunchKernelGGL(link_decode_bf16<64>, dim3(t.n_work), dim3(256), 0, stream, p);
+        const hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+    }
+    if (t.n_merge <= 0) return hipSuccess;
+    DecodeMergeParams m;
+    m.q = q;
+    m.k = k;
+    m.v = v;
+    m.rope = rope;
+    m.dec_pos = t.dec_pos;
+    m.merge = t.merge;
+    m.part_o = t.part_o;
+    m.part_lse = t.part_lse;
+    m.out = out;
+    m.lse = lse;
+    m.hq = s.hq;
+    m.hkv = s.hkv;
+    m.gshift = gshift;
+    m.scale_log2 = scale_log2;
+    const dim3 grid(t.n_merge << gshift);
+    if (s.d == 128) hipLaunchKernelGGL(link_decode_merge<128>, grid, dim3(64), 0, stream, m);
+    else hipLaunchKernelGGL(link_decode_merge<64>, grid, dim3(64), 0, stream, m);
     return hipGetLastError();
 }
 

@@ -51,6 +51,27 @@ struct MergeDesc {
     int32_t pad0, pad1, pad2;
 };
 
+// One decode work item: the new token of request `request` (the G query heads of KV head
+// kv_head) over the logical pages [page_begin, page_end) of that request. Every item writes a
+// partial result into slot `partial`.
+struct DecodeDesc {
+    int32_t page_base;   // index of the request's logical page 0 in the PageDesc table
+    int32_t page_begin;
+    int32_t page_end;
+    int32_t request;
+    int32_t kv_head;
+    int32_t partial;
+    int32_t pad0, pad1;
+};
+
+// Combine the partial results of one (request, KV head) with the new token's own key.
+struct DecodeMergeDesc {
+    int32_t request;
+    int32_t kv_head;
+    int32_t n_split;
+    int32_t slot0;
+};
+
 constexpr int kKeysPerTile = 64;   // keys staged in LDS per attention iteration
 constexpr int kMaxItemPages = 2048;  // longest KV range of one attention work item (its page table sits in LDS)
 // Positions are packed with a page's valid count into one 32-bit word (pos0 << 7 | valid) and

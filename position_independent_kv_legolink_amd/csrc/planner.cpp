@@ -41,9 +41,14 @@ pic_plan *build_plan(pic_store *s, const pic_request *reqs, int32_t n_reqs, cons
     if (o.rope_keys < 0 || o.rope_keys > 2) fail(PIC_ERR_INVALID, "rope_keys must be 0, 1 or 2");
     if (o.rope_keys == 2 && cfg.dtype != PIC_DTYPE_BF16)
         fail(PIC_ERR_INVALID, "keys are rotated ahead of attention for bfloat16 stores only");
+    if (o.decode != 0 && o.decode != 1) fail(PIC_ERR_INVALID, "decode must be 0 or 1");
+    if (o.decode && cfg.dtype != PIC_DTYPE_BF16) fail(PIC_ERR_INVALID, "decode after link needs a bfloat16 store");
+    if (o.decode && o.rope_keys == 1)
+        fail(PIC_ERR_INVALID, "decode reads keys rotated ahead of attention: rope_keys must be 0 or 2");
 
     // ---- pass 1: segments, validation and private-page count
     std::vector<std::vector<Seg>> all(n_reqs);
+    std::vector<int32_t> ends(n_reqs);   // position after each request's last token
     int64_t private_needed = 0;
     for (int r = 0; r < n_reqs; ++r) {
         const pic_request &q = reqs[r];
@@ -72,6 +77,10 @@ pic_plan *build_plan(pic_store *s, const pic_request *reqs, int32_t n_reqs, cons
         if (pos > cfg.max_position)
             fail(PIC_ERR_INVALID, "request " + std::to_string(r) + " reaches position " + std::to_string(pos - 1) +
                                       " but the store's RoPE table ends at " + std::to_string(cfg.max_position - 1));
+        if (o.decode && pos >= cfg.max_position)
+            fail(PIC_ERR_INVALID, "request " + std::to_string(r) + ": its decode token at position " +
+                                      std::to_string(pos) + " lies beyond the store's RoPE table");
+        ends[r] = (int32_t)pos;
         for (const Seg &g : segs) {
             if (g.suffix) private_needed += (g.length + B - 1) / B;
             else private_needed += (g.recompute + B - 1) / B;
@@ -156,6 +165,8 @@ pic_plan *build_plan(pic_store *s, const pic_request *reqs, int32_t n_reqs, cons
         else if (o.rope_keys == 0)
             plan->rotate_keys = cfg.dtype == PIC_DTYPE_BF16 && total >= (int64_t)kRotateReuse * page_heads;
     }
+    // decode reads every key page once per step: its keys are rotated once, at link time
+    if (o.decode) plan->rotate_keys = !plan->pages.empty();
     int64_t max_pages;
     if (o.split_pages > 0) {
         max_pages = align_up(o.split_pages, ppt);
@@ -207,6 +218,28 @@ pic_plan *build_plan(pic_store *s, const pic_request *reqs, int32_t n_reqs, cons
         for (const Item &it : split) plan->work.push_back(it.w);
     }
 
+    // ---- decode work list: every (request, KV head) cut into page ranges, about two items per
+    // compute unit over the whole batch; each range's partial result goes to its own slot
+    if (o.decode) {
+        plan->decode = true;
+        plan->dec_pos = ends;
+        const int64_t per_item = std::max<int64_t>(4, (page_heads + 2 * s->num_cus - 1) / (2 * s->num_cus));
+        for (int r = 0; r < n_reqs; ++r) {
+            const int32_t n = plan->cu_pages[r + 1] - plan->cu_pages[r];
+            for (int h = 0; h < cfg.num_kv_heads; ++h) {
+                const int32_t slot0 = (int32_t)plan->dec_work.size();
+                if (n > 0) {
+                    const int32_t n_split = (int32_t)((n + per_item - 1) / per_item);
+                    const int32_t step = (n + n_split - 1) / n_split;
+                    for (int32_t b = 0; b < n; b += step)
+                        plan->dec_work.push_back({plan->cu_pages[r], b, std::min(n, b + step), r, h,
+                                                  (int32_t)plan->dec_work.size(), 0, 0});
+                }
+                plan->dec_merge.push_back({r, h, (int32_t)plan->dec_work.size() - slot0, slot0});
+            }
+        }
+    }
+
     // ---- workspace layout
     int64_t off = 0;
     auto place = [&](int64_t bytes) {
@@ -219,12 +252,17 @@ pic_plan *build_plan(pic_store *s, const pic_request *reqs, int32_t n_reqs, cons
     plan->off_scatter = place((int64_t)plan->scatter.size() * sizeof(ScatterDesc));
     plan->off_work = place((int64_t)plan->work.size() * sizeof(WorkDesc));
     plan->off_merge = place((int64_t)plan->merge.size() * sizeof(MergeDesc));
+    plan->off_dec_pos = place((int64_t)plan->dec_pos.size() * sizeof(int32_t));
+    plan->off_dec_work = place((int64_t)plan->dec_work.size() * sizeof(DecodeDesc));
+    plan->off_dec_merge = place((int64_t)plan->dec_merge.size() * sizeof(DecodeMergeDesc));
     plan->table_bytes = off;
     const int64_t tq = tile_qrows(cfg.dtype);
     plan->off_part_o = place((int64_t)plan->n_slots * tq * cfg.head_dim * sizeof(float));
     plan->off_part_lse = place((int64_t)plan->n_slots * tq * sizeof(float));
     const int64_t elem = cfg.dtype == PIC_DTYPE_BF16 ? 2 : 4;
     plan->off_k_rot = place(plan->rotate_keys ? (int64_t)plan->pages.size() * s->shape.page_elems * elem : 0);
+    plan->off_dec_o = place((int64_t)plan->dec_work.size() * G * cfg.head_dim * sizeof(float));
+    plan->off_dec_lse = place((int64_t)plan->dec_work.size() * G * sizeof(float));
     plan->workspace_bytes = std::max<int64_t>(off, 256);
     return plan;
 }

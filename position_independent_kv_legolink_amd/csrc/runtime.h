@@ -73,6 +73,13 @@ struct pic_plan {
     int64_t off_part_o = 0, off_part_lse = 0, table_bytes = 0, workspace_bytes = 0;
     bool rotate_keys = false;           // keys rotated into the workspace before attention
     int64_t off_k_rot = 0;
+    // decode after link (plans made with opts.decode)
+    bool decode = false;
+    std::vector<int32_t> dec_pos;       // per request: position of the new token
+    std::vector<piclink::DecodeDesc> dec_work;
+    std::vector<piclink::DecodeMergeDesc> dec_merge;
+    int64_t off_dec_pos = 0, off_dec_work = 0, off_dec_merge = 0, off_dec_o = 0, off_dec_lse = 0;
+    const void *attended_ws = nullptr;  // workspace of the last pic_link_attend (holds the rotated keys)
     void *uploaded_to = nullptr;
 };
 

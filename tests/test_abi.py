@@ -168,3 +168,34 @@ def test_rotated_keys_take_one_page_per_logical_page_of_workspace():
     assert empty.sizes["rows"] == 0 and empty.sizes["rotated_pages"] == 0
     for p in (fused, rot, empty):
         p.free()
+
+
+def test_decode_option_is_validated():
+    """decode=1 rotates every key page ahead and builds one decode item per (request, KV head)
+    range; it needs a bf16 store, keys rotated ahead (rope_keys 0 or 2) and a RoPE table row for
+    the new token's position."""
+    s = meta()
+    s.store_chunk(1, n_tokens=40)
+    plan = s.link_plan([pic.LinkRequest([1], 5)], k=2, decode=True)
+    assert plan.sizes["decode_items"] == 2            # 1 request x 2 KV heads, 4 pages each
+    assert plan.sizes["rotated_pages"] == plan.sizes["pages"] == 4
+    plan.free()
+    plain = s.link_plan([pic.LinkRequest([1], 5)], k=2)
+    assert plain.sizes["decode_items"] == 0
+    plain.free()
+    with pytest.raises(pic.PicError) as e:
+        s.link_plan([pic.LinkRequest([1], 5)], k=2, decode=True, rope_keys=1)
+    assert e.value.status == -1
+    # the request ends at position 4095 = the last table row: linking is fine, the decode token
+    # at 4096 has no row
+    s.link_plan([pic.LinkRequest([1], 5)], k=2, pos_offset=4096 - 45).free()
+    with pytest.raises(pic.PicError) as e:
+        s.link_plan([pic.LinkRequest([1], 5)], k=2, pos_offset=4096 - 45, decode=True)
+    assert e.value.status == -1
+    assert s.stats()["plans"] == 0
+    s.close()
+    f = meta(dtype="f32", head_dim=64)
+    f.store_chunk(1, n_tokens=40)
+    with pytest.raises(pic.PicError) as e:
+        f.link_plan([pic.LinkRequest([1], 5)], k=2, decode=True)
+    assert e.value.status == -1
