@@ -173,6 +173,44 @@ def time_steps_cold(job, steps, evict_mib=512):
     return total * 1e3 / steps, prof
 
 
+def decode_measure(job, steps=20, warmup=3):
+    """Decode after link on the same requests: a plan made for decode, one link call to rotate
+    its keys, then `steps` decode steps timed with HIP events on the stream they run on. Bytes:
+    every request's logical K' and V pages (shared pages count once per request that reads
+    them) plus the new tokens' q, k, v and outputs."""
+    torch, cfg = job.torch, job.cfg
+    kw = dict(job.plan_kw)
+    kw["rope_keys"] = 0
+    plan = job.store.link_plan(job.requests, decode=True, **kw)
+    ws = torch.empty(plan.sizes["workspace_bytes"], dtype=torch.uint8, device="cuda")
+    plan.upload(ws)
+    job.pic.link_attend(job.store, plan, job.q, job.k, job.v)
+    n = len(job.requests)
+    g = np.random.default_rng(7)
+    mk = lambda h: torch.from_numpy(g.standard_normal((n, h, cfg.head_dim), dtype=np.float32)).to(
+        "cuda", job.tdt).contiguous()
+    q, k, v = mk(cfg.num_q_heads), mk(cfg.num_kv_heads), mk(cfg.num_kv_heads)
+    out = torch.empty_like(q)
+    for _ in range(warmup):
+        job.pic.link_decode(job.store, plan, q, k, v, out=out)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(steps):
+        job.pic.link_decode(job.store, plan, q, k, v, out=out)
+    e1.record()
+    e1.synchronize()
+    ms = e0.elapsed_time(e1) / steps
+    elem = 2 if cfg.dtype == "bf16" else 4
+    page_bytes = cfg.num_kv_heads * cfg.page_size * cfg.head_dim * elem
+    nbytes = 2 * plan.sizes["pages"] * page_bytes + n * (2 * cfg.num_q_heads + 2 * cfg.num_kv_heads) * cfg.head_dim * elem
+    items = plan.sizes["decode_items"]
+    plan.free()
+    gbps = nbytes / (ms * 1e-3) / 1e9
+    return {"requests": n, "ms": round(ms, 4), "work_items": items, "algorithmic_mb": round(nbytes / 1e6, 1),
+            "gbps": round(gbps, 1), "hbm_frac": round(gbps / PEAK_HBM_GBPS, 4)}
+
+
 def dense_comparator(job, reps=3):
     """Full recompute of every token (prefix and suffix included) on the same inputs.
 
@@ -342,6 +380,7 @@ def main():
     ap.add_argument("--no-dense", action="store_true")
     ap.add_argument("--cold-steps", type=int, default=10,
                     help="extra steps, each after evicting the MALL, reported under 'cold' (0: none)")
+    ap.add_argument("--no-decode", action="store_true", help="skip the decode-after-link measurement")
     ap.add_argument("--rope-keys", type=int, default=0, choices=(0, 1, 2),
                     help="key rotation: 0 automatic, 1 inside attention, 2 once ahead of attention")
     ap.add_argument("--split-pages", type=int, default=0,
@@ -434,6 +473,11 @@ def main():
                 "merge_ms": round(c_prof["merge_ms"] / cc, 4)}
         log(f"cold (MALL evicted before each step, steps not overlapped with planning): {cold}")
 
+    decode = None
+    if not args.no_decode and cfg.dtype == "bf16":
+        decode = decode_measure(job)
+        log(f"decode after link: {decode}")
+
     dense = None
     if not args.no_dense:
         dense = dense_comparator(job)
@@ -478,6 +522,7 @@ def main():
         "mfma_frac_step": round(flop / (ms_step * 1e-3) / 1e12 / peak, 4),
         "roofline": roofline,
         "cold": cold,
+        "decode": decode,
         "dense_comparator": dense,
         "cpu_baseline": cpu,
         "kernel_source_sha256_16": kernel_hash(),

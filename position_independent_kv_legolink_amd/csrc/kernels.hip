@@ -1315,9 +1315,11 @@ __global__ __launch_bounds__(256, 2) void link_decode_bf16(DecodeParams p) {
     }
 }
 
-// Decode merge: one wave per (request, query head). The new token's own score (its rotated query
-// against its rotated key, both rounded to bf16 as the attention kernels round them) joins the
-// partial results of the request's page ranges; the output is their log-sum-exp weighted mean.
+// Decode merge: one work group per (request, query head). The new token's own score (its rotated
+// query against its rotated key, both rounded to bf16 as the attention kernels round them) joins
+// the partial results of the request's page ranges; the output is their log-sum-exp weighted
+// mean. The ranges' weights are formed in parallel and staged in LDS; groups of D threads then
+// sum disjoint sets of ranges, one output dimension per thread.
 struct DecodeMergeParams {
     const void *q, *k, *v;
     const float *rope;
@@ -1332,45 +1334,78 @@ struct DecodeMergeParams {
 };
 
 template <int D>
-__global__ __launch_bounds__(64) void link_decode_merge(DecodeMergeParams p) {
+__global__ __launch_bounds__(512) void link_decode_merge(DecodeMergeParams p) {
+    constexpr int NT = 512, NWV = NT / 64, NG = NT / D;
+    constexpr int FB = 1024;            // range weights staged per round
+    __shared__ float fbuf[FB];
+    __shared__ float acc[NG * D];
+    __shared__ float red[NWV];
+    __shared__ float s_new_sh;
     const int G = 1 << p.gshift;
     const DecodeMergeDesc md = p.merge[blockIdx.x >> p.gshift];
     const int hl = blockIdx.x & (G - 1), h = md.kv_head * G + hl;
-    const int lane = threadIdx.x;
-    const int i = lane & (D / 2 - 1);   // rotation pair (i, i + D/2); lanes past D/2 repeat it
-    const bool owner = lane < D / 2;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int pos = p.dec_pos[md.request];
-    const float c = p.rope[(int64_t)pos * D + i], sn = p.rope[(int64_t)pos * D + D / 2 + i];
-    const uint16_t *qr = static_cast<const uint16_t *>(p.q) + ((int64_t)md.request * p.hq + h) * D;
-    const uint16_t *kr = static_cast<const uint16_t *>(p.k) + ((int64_t)md.request * p.hkv + md.kv_head) * D;
-    const uint16_t *vr = static_cast<const uint16_t *>(p.v) + ((int64_t)md.request * p.hkv + md.kv_head) * D;
-    const float qx = bf_lo(qr[i]), qy = bf_lo(qr[i + D / 2]);
-    const float kx = bf_lo(kr[i]), ky = bf_lo(kr[i + D / 2]);
-    const float cq = c * p.scale_log2, sq = sn * p.scale_log2;
-    const uint32_t qp = pack_bf16(fmaf(qx, cq, -qy * sq), fmaf(qy, cq, qx * sq));
-    const uint32_t kp = pack_bf16(fmaf(kx, c, -ky * sn), fmaf(ky, c, kx * sn));
-    float dot = owner ? bf_lo(qp) * bf_lo(kp) + bf_hi(qp) * bf_hi(kp) : 0.0f;
+    const float *lse_r = p.part_lse + (int64_t)md.slot0 * G + hl;   // range j at lse_r[j * G]
+    if (wave == 0) {
+        const int i = lane & (D / 2 - 1);   // rotation pair (i, i + D/2); lanes past D/2 repeat it
+        const float c = p.rope[(int64_t)pos * D + i], sn = p.rope[(int64_t)pos * D + D / 2 + i];
+        const uint16_t *qr = static_cast<const uint16_t *>(p.q) + ((int64_t)md.request * p.hq + h) * D;
+        const uint16_t *kr = static_cast<const uint16_t *>(p.k) + ((int64_t)md.request * p.hkv + md.kv_head) * D;
+        const float qx = bf_lo(qr[i]), qy = bf_lo(qr[i + D / 2]);
+        const float kx = bf_lo(kr[i]), ky = bf_lo(kr[i + D / 2]);
+        const float cq = c * p.scale_log2, sq = sn * p.scale_log2;
+        const uint32_t qp = pack_bf16(fmaf(qx, cq, -qy * sq), fmaf(qy, cq, qx * sq));
+        const uint32_t kp = pack_bf16(fmaf(kx, c, -ky * sn), fmaf(ky, c, kx * sn));
+        float dot = lane < D / 2 ? bf_lo(qp) * bf_lo(kp) + bf_hi(qp) * bf_hi(kp) : 0.0f;
 #pragma unroll
-    for (int o = 32; o > 0; o >>= 1) dot += __shfl_xor(dot, o);
-    const float s_new = dot;   // log2 units
-    float m = s_new;
-    for (int j = 0; j < md.n_split; ++j) m = fmaxf(m, p.part_lse[(int64_t)(md.slot0 + j) * G + hl]);
-    const float f_new = __builtin_amdgcn_exp2f(s_new - m);
-    float den = f_new, o0 = f_new * bf_lo(vr[i]), o1 = f_new * bf_lo(vr[i + D / 2]);
-    for (int j = 0; j < md.n_split; ++j) {
-        const int64_t sl = (int64_t)(md.slot0 + j) * G + hl;
-        const float f = __builtin_amdgcn_exp2f(p.part_lse[sl] - m);
-        den += f;
-        o0 += f * p.part_o[sl * D + i];
-        o1 += f * p.part_o[sl * D + i + D / 2];
+        for (int o = 32; o > 0; o >>= 1) dot += __shfl_xor(dot, o);
+        if (lane == 0) s_new_sh = dot;   // log2 units
     }
-    if (owner) {
+    float mloc = -INFINITY;
+    for (int j = tid; j < md.n_split; j += NT) mloc = fmaxf(mloc, lse_r[(int64_t)j * G]);
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) mloc = fmaxf(mloc, __shfl_xor(mloc, o));
+    if (lane == 0) red[wave] = mloc;
+    __syncthreads();
+    const float s_new = s_new_sh;
+    float m = s_new;
+#pragma unroll
+    for (int w = 0; w < NWV; ++w) m = fmaxf(m, red[w]);
+    __syncthreads();
+    const int d = tid % D, grp = tid / D;
+    float o = 0.0f, den = 0.0f;
+    for (int j0 = 0; j0 < md.n_split; j0 += FB) {
+        const int nj = min(FB, md.n_split - j0);
+        for (int j = tid; j < nj; j += NT) {
+            const float f = __builtin_amdgcn_exp2f(lse_r[(int64_t)(j0 + j) * G] - m);
+            fbuf[j] = f;
+            den += f;
+        }
+        __syncthreads();
+        const float *po = p.part_o + ((int64_t)(md.slot0 + j0) * G + hl) * D + d;
+#pragma unroll 4
+        for (int j = grp; j < nj; j += NG) o += fbuf[j] * po[(int64_t)j * G * D];
+        __syncthreads();
+    }
+#pragma unroll
+    for (int k = 32; k > 0; k >>= 1) den += __shfl_xor(den, k);
+    if (lane == 0) red[wave] = den;
+    acc[grp * D + d] = o;
+    __syncthreads();
+    if (tid < D) {
+        const float f_new = __builtin_amdgcn_exp2f(s_new - m);
+        float dsum = f_new, osum = 0.0f;
+#pragma unroll
+        for (int w = 0; w < NWV; ++w) dsum += red[w];
+#pragma unroll
+        for (int g = 0; g < NG; ++g) osum += acc[g * D + tid];
+        const uint16_t *vr = static_cast<const uint16_t *>(p.v) + ((int64_t)md.request * p.hkv + md.kv_head) * D;
+        osum += f_new * bf_lo(vr[tid]);
         uint16_t *orow = static_cast<uint16_t *>(p.out) + ((int64_t)md.request * p.hq + h) * D;
-        const uint32_t w = pack_bf16(o0 / den, o1 / den);
-        orow[i] = (uint16_t)(w & 0xffffu);
-        orow[i + D / 2] = (uint16_t)(w >> 16);
-        if (lane == 0 && p.lse)
-            p.lse[(int64_t)md.request * p.hq + h] = (m + __builtin_amdgcn_logf(den)) * 0.6931471805599453f;
+        orow[tid] = (uint16_t)(pack_bf16(osum / dsum, 0.0f) & 0xffffu);
+        if (tid == 0 && p.lse)
+            p.lse[(int64_t)md.request * p.hq + h] = (m + __builtin_amdgcn_logf(dsum)) * 0.6931471805599453f;
     }
 }
 
@@ -1506,8 +1541,8 @@ hipError_t launch_decode(const LayerShape &s, const void *q, const void *k, cons
     m.gshift = gshift;
     m.scale_log2 = scale_log2;
     const dim3 grid(t.n_merge << gshift);
-    if (s.d == 128) hipLaunchKernelGGL(link_decode_merge<128>, grid, dim3(64), 0, stream, m);
-    else hipLaunchKernelGGL(link_decode_merge<64>, grid, dim3(64), 0, stream, m);
+    if (s.d == 128) hipLaunchKernelGGL(link_decode_merge<128>, grid, dim3(512), 0, stream, m);
+    else hipLaunchKernelGGL(link_decode_merge<64>, grid, dim3(512), 0, stream, m);
     return hipGetLastError();
 }
 
