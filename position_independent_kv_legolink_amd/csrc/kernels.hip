@@ -1148,6 +1148,7 @@ __global__ __launch_bounds__(256, 2) void link_decode_bf16(DecodeParams p) {
     __shared__ __attribute__((aligned(16))) int kval[NW * 32];
     __shared__ float obuf[NW * MAXG * D];
     __shared__ float mbuf[NW * MAXG], lbuf[NW * MAXG];
+    __shared__ int dpg_phys[kMaxItemPages], dpg_valid[kMaxItemPages];
 
     const DecodeDesc w = p.work[blockIdx.x];
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, ln = lane & 31, lg = lane >> 5;
@@ -1157,6 +1158,13 @@ __global__ __launch_bounds__(256, 2) void link_decode_bf16(DecodeParams p) {
     const int lpage0 = w.page_base + w.page_begin;
     const int64_t head_off = (int64_t)w.kv_head * page_size * D;   // elements
     const uint32_t page_bytes = (uint32_t)p.page_elems * 2u;
+    // the range's page table, staged once (physical page and valid count of every page)
+    for (int i = tid; i < n_pages; i += 256) {
+        const PageDesc d = p.pages[lpage0 + i];
+        dpg_phys[i] = d.phys;
+        dpg_valid[i] = d.valid;
+    }
+    __syncthreads();
 
     // rotated, scaled query fragments of head ln (zero beyond the G heads)
     u32x4 qf[NS];
@@ -1199,29 +1207,34 @@ __global__ __launch_bounds__(256, 2) void link_decode_bf16(DecodeParams p) {
     const char *vpool_b = static_cast<const char *>(p.v_pool);
     const int nblk = (n_pages * page_size + 31) >> 5;
     for (int blk = wave; blk < nblk; blk += NW) {
-        // the lane's key (both lane halves hold key ln: the A operand's row and half of its V row)
+        // the lane's key for the A operand (both lane halves hold key ln)
         const int kk = blk * 32 + ln;
         const int rel = kk >> p.pshift;
         const int slot = kk & (page_size - 1);
         const bool in_range = rel < n_pages;
-        const int lp = lpage0 + (in_range ? rel : n_pages - 1);
-        const PageDesc pd = p.pages[lp];
-        const bool ok = in_range && slot < pd.valid;
-        const uint32_t row_off = (uint32_t)(head_off + slot * D) * 2u;
-        const char *krow = krot_b + (uint64_t)(uint32_t)lp * page_bytes + row_off;
-        const char *vrow = vpool_b + (uint64_t)(uint32_t)pd.phys * page_bytes + row_off;
-        // K: NS 16-byte pieces of the A operand; V: the lane half's D/2 values, NS pieces of 8
+        const int rc = in_range ? rel : n_pages - 1;
+        const bool ok = in_range && slot < dpg_valid[rc];
+        const char *krow = krot_b + (uint64_t)(uint32_t)(lpage0 + rc) * page_bytes + (uint32_t)(head_off + slot * D) * 2u;
+        // K: NS 16-byte pieces of the A operand. V: NS loads, each a contiguous run of RPI rows of
+        // the block (a page holds whole runs: RPI <= 8 <= page size), lane = (row, 16-byte chunk)
+        constexpr int RPI = 512 / D, CPR = D / 8;
         bf16x8 ka[NS];
         u32x4 vr[NS];
 #pragma unroll
         for (int s = 0; s < NS; ++s) ka[s] = *reinterpret_cast<const bf16x8 *>(krow + (16 * s + 8 * lg) * 2);
 #pragma unroll
-        for (int i = 0; i < NS; ++i) vr[i] = *reinterpret_cast<const u32x4 *>(vrow + (lg * D / 2 + 8 * i) * 2);
+        for (int i = 0; i < NS; ++i) {
+            const int vk = blk * 32 + i * RPI + lane / CPR;
+            const int vrel = min(vk >> p.pshift, n_pages - 1);
+            const char *vrow = vpool_b + (uint64_t)(uint32_t)dpg_phys[vrel] * page_bytes +
+                               (uint32_t)(head_off + (vk & (page_size - 1)) * D) * 2u;
+            vr[i] = *reinterpret_cast<const u32x4 *>(vrow + (lane % CPR) * 16);
+        }
         // the previous block's transposing reads of this wave's V buffer are complete
         __builtin_amdgcn_s_waitcnt(0xc07f);   // lgkmcnt(0)
         __builtin_amdgcn_wave_barrier();
 #pragma unroll
-        for (int i = 0; i < NS; ++i) *reinterpret_cast<u32x4 *>(&vb[ln * VS + lg * D / 2 + 8 * i]) = vr[i];
+        for (int i = 0; i < NS; ++i) *reinterpret_cast<u32x4 *>(&vb[(i * RPI + lane / CPR) * VS + (lane % CPR) * 8]) = vr[i];
         if (lg == 0) kv[ln] = ok ? 1 : 0;
 
         floatx16 sacc = (floatx16)(0.0f);

@@ -223,7 +223,9 @@ pic_plan *build_plan(pic_store *s, const pic_request *reqs, int32_t n_reqs, cons
     if (o.decode) {
         plan->decode = true;
         plan->dec_pos = ends;
-        const int64_t per_item = std::max<int64_t>(4, (page_heads + 2 * s->num_cus - 1) / (2 * s->num_cus));
+        // a range's page table sits in LDS: at most kMaxItemPages pages
+        const int64_t per_item = std::min<int64_t>(
+            kMaxItemPages, std::max<int64_t>(4, (page_heads + 2 * s->num_cus - 1) / (2 * s->num_cus)));
         for (int r = 0; r < n_reqs; ++r) {
             const int32_t n = plan->cu_pages[r + 1] - plan->cu_pages[r];
             for (int h = 0; h < cfg.num_kv_heads; ++h) {
