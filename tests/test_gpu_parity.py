@@ -155,6 +155,11 @@ EDGE = {
     "d64_f32_g8": dict(head_dim=64, num_q_heads=8, num_kv_heads=1, dtype="f32", kv_scale=1.0),
     "g2_many_requests": dict(num_q_heads=4, num_kv_heads=2, n_requests=5, chunk_len=33),
     "hkv8_xcd_buckets": dict(num_q_heads=32, num_kv_heads=8, chunk_len=140, k=20),
+    "g8_bf16": dict(num_q_heads=16, num_kv_heads=2),
+    "one_token_chunks": dict(chunk_len=1, chunks_per_request=40, pool_size=60, k=1, prefix_len=3, suffix_len=5),
+    "prefix_and_suffix_only": dict(prefix_len=300, chunks_per_request=0, suffix_len=7),
+    "single_head_d64": dict(num_q_heads=1, num_kv_heads=1, head_dim=64),
+    "page32_d64_k33": dict(page_size=32, head_dim=64, num_q_heads=4, num_kv_heads=2, k=33, chunk_len=90),
 }
 
 
