@@ -34,6 +34,8 @@ METRIC = "link-step attention TFLOP/s + HBM GB/s (% MI355X peak); link latency @
 PEAK_BF16_TFLOPS = 2500.0     # MI355X dense bf16 MFMA
 PEAK_F32_TFLOPS = 157.3       # MI355X fp32
 PEAK_HBM_GBPS = 8000.0        # MI355X HBM3E
+DECODE_WARMUP, DECODE_STEPS = 3, 20
+DECODE_SLOTS = DECODE_WARMUP + DECODE_STEPS
 KERNEL_SOURCE = os.path.join(ROOT, "position_independent_kv_legolink_amd", "csrc", "kernels.hip")
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "attention_traffic.json")
 
@@ -91,9 +93,13 @@ class LinkJob:
         private = len(draws) * (cfg.chunks_per_request * -(-max(cfg.k, B if cfg.block_level else 0) // B)
                                 + -(-cfg.suffix_len // B))
         self.n_tokens = cfg.prefix_len + cfg.chunks_per_request * cfg.chunk_len + cfg.suffix_len
+        # room for the decode measurement's plan: its private pages plus DECODE_SLOTS decode slots per
+        # request, and the RoPE rows of those positions
+        decode_pages = private + len(draws) * (-(-DECODE_SLOTS // B) + 1)
         self.store = pic.Store(num_q_heads=cfg.num_q_heads, num_kv_heads=cfg.num_kv_heads, head_dim=cfg.head_dim,
-                               page_size=B, num_pages=pages + private + dense_pages + 64, dtype=cfg.dtype,
-                               rope_theta=cfg.rope_theta, max_position=self.n_tokens + 1)
+                               page_size=B, num_pages=pages + private + max(dense_pages, decode_pages) + 64,
+                               dtype=cfg.dtype, rope_theta=cfg.rope_theta,
+                               max_position=self.n_tokens + DECODE_SLOTS + 1)
         self.tdt = torch.bfloat16 if cfg.dtype == "bf16" else torch.float32
         t = time.time()
         for c in chunk_ids:
@@ -173,15 +179,16 @@ def time_steps_cold(job, steps, evict_mib=512):
     return total * 1e3 / steps, prof
 
 
-def decode_measure(job, steps=20, warmup=3):
-    """Decode after link on the same requests: a plan made for decode, one link call to rotate
-    its keys, then `steps` decode steps timed with HIP events on the stream they run on. Bytes:
-    every request's logical K' and V pages (shared pages count once per request that reads
+def decode_measure(job, steps=DECODE_STEPS, warmup=DECODE_WARMUP):
+    """Decode after link on the same requests: a plan with warmup + steps decode slots per
+    request, one link call (it rotates the keys), then consecutive decode steps, the last
+    `steps` timed with HIP events on the stream they run on (each appends its token). Bytes per
+    step: every request's logical K' and V pages (shared pages count once per request that reads
     them) plus the new tokens' q, k, v and outputs."""
     torch, cfg = job.torch, job.cfg
     kw = dict(job.plan_kw)
     kw["rope_keys"] = 0
-    plan = job.store.link_plan(job.requests, decode=True, **kw)
+    plan = job.store.link_plan(job.requests, decode=warmup + steps, **kw)
     ws = torch.empty(plan.sizes["workspace_bytes"], dtype=torch.uint8, device="cuda")
     plan.upload(ws)
     job.pic.link_attend(job.store, plan, job.q, job.k, job.v)

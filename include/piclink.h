@@ -113,8 +113,12 @@ typedef struct {
  *              are bit-identical to 1); 0 = automatic: 2 for bfloat16 stores when
  *              the work list reads each key page at least 8 times on average,
  *              else 1. Other values: PIC_ERR_INVALID.
- * decode       1: also prepare pic_link_decode (bfloat16 stores; keys are then always
- *              rotated ahead, so rope_keys must be 0 or 2); 0: link only */
+ * decode       T > 0: also prepare T steps of pic_link_decode (bfloat16 stores; keys are
+ *              then always rotated ahead, so rope_keys must be 0 or 2). Every request gets T
+ *              decode slots after its last token, positions end .. end + T - 1: the tail of
+ *              its suffix's last page and further private pages (a private segment of their
+ *              own when the request has no suffix). They count toward max_position and the
+ *              page pool, and show in pic_plan_export as valid slots. 0: link only */
 typedef struct {
     int32_t k;
     int32_t block_level;
@@ -241,18 +245,21 @@ pic_status pic_link_attend(pic_store *store, const pic_plan *plan, const void *q
 
 /* Decode after link: one generation step per request (EPIC digest, abstract: chunks are
  * compiled, then linked, then the request generates; MEPIC abstract: the paged, shared cache
- * serves the request). For every request r of a plan made with opts.decode = 1, after
- * pic_link_attend ran on the same workspace: the new token at position p_r, the position after
- * the request's last linked token, attends over the request's linked cache (all positions
- * < p_r, with the recomputed rows' K/V that pic_link_attend scattered) and over itself.
- *   q      [n_req][Hq][d]   the new tokens' queries, pre-RoPE
- *   k, v   [n_req][Hkv][d]  their keys (pre-RoPE) and values; read, not written to the pool
+ * serves the request). For a plan made with opts.decode = T, after pic_link_attend ran on the
+ * same workspace, call i (i = 0 .. T-1) is decode step i: every request's token at position
+ * p = end + i (end = the position after its last linked token) attends over the request's
+ * linked cache (positions < end, with the recomputed rows' K/V that pic_link_attend
+ * scattered), over the tokens of steps 0 .. i-1 and over itself; the step then writes the
+ * token's key and value into its decode slot, for the later steps.
+ *   q      [n_req][Hq][d]   the tokens' queries, pre-RoPE
+ *   k, v   [n_req][Hkv][d]  their keys (pre-RoPE) and values
  *   out    [n_req][Hq][d]   attention output, store dtype
  *   lse    [n_req][Hq]      optional float32 natural-log softmax denominators
- * The cache's keys are read as pic_link_attend rotated them into the workspace. Split-KV: every
- * (request, KV head) is cut into page ranges whose partial results are merged with the new
- * token's own score. Errors: PIC_ERR_STATE (plan not made for decode, or not attended on this
- * workspace), PIC_ERR_WORKSPACE, PIC_ERR_INVALID (null tensor). Asynchronous on `stream`. */
+ * The cache's keys are read as the link call rotated them into the workspace. Split-KV: every
+ * (request, KV head) is cut into page ranges whose partial results are merged with the token's
+ * own score. pic_link_attend zeroes the decode slots and restarts at step 0. Errors:
+ * PIC_ERR_STATE (plan not made for decode, not attended on this workspace, or all T steps
+ * used), PIC_ERR_WORKSPACE, PIC_ERR_INVALID (null tensor). Asynchronous on `stream`. */
 pic_status pic_link_decode(pic_store *store, const pic_plan *plan, const void *q, const void *k, const void *v,
                            void *out, float *lse, void *workspace, int64_t workspace_bytes, hipStream_t stream);
 

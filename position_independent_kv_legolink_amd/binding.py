@@ -195,7 +195,7 @@ class Store:
         return dict(free_pages=f.value, chunks=c.value, plans=p.value)
 
     def link_plan(self, requests, *, k=0, block_level=False, pos_offset=0, recompute_all=False,
-                  split_pages=0, rope_keys=0, decode=False):
+                  split_pages=0, rope_keys=0, decode=0):
         n = len(requests)
         reqs = (Request * max(n, 1))()
         keep = []
@@ -206,7 +206,7 @@ class Store:
                               ctypes.cast(ids, ctypes.POINTER(ctypes.c_uint64)), len(r.chunk_ids),
                               int(r.suffix_len))
         opts = LinkOptions(int(k), int(bool(block_level)), int(pos_offset), int(bool(recompute_all)),
-                           int(split_pages), int(rope_keys), int(bool(decode)))
+                           int(split_pages), int(rope_keys), int(decode))
         h = ctypes.c_void_p()
         _check(lib().pic_link_plan(self.handle, reqs, n, ctypes.byref(opts), ctypes.byref(h)))
         return Plan(self, h)

@@ -312,7 +312,7 @@ pic_status pic_plan_upload(pic_store *s, pic_plan *plan, void *workspace, int64_
             put(plan->off_scatter, plan->scatter.data(), plan->scatter.size() * sizeof(ScatterDesc));
             put(plan->off_work, plan->work.data(), plan->work.size() * sizeof(WorkDesc));
             put(plan->off_merge, plan->merge.data(), plan->merge.size() * sizeof(MergeDesc));
-            put(plan->off_dec_pos, plan->dec_pos.data(), plan->dec_pos.size() * sizeof(int32_t));
+            put(plan->off_dec_req, plan->dec_req.data(), plan->dec_req.size() * sizeof(DecodeReq));
             put(plan->off_dec_work, plan->dec_work.data(), plan->dec_work.size() * sizeof(DecodeDesc));
             put(plan->off_dec_merge, plan->dec_merge.data(), plan->dec_merge.size() * sizeof(DecodeMergeDesc));
             check_hip(hipMemcpyAsync(workspace, blob, (size_t)plan->table_bytes, hipMemcpyHostToDevice, stream),
@@ -375,6 +375,7 @@ pic_status pic_link_attend(pic_store *s, const pic_plan *plan, const void *q_new
         if (prof) check_hip(hipEventRecord(marks.ev[3], stream), "hipEventRecord");
         check_hip(launch_merge(s->shape, t, out, lse, stream), "merge launch");
         const_cast<pic_plan *>(plan)->attended_ws = workspace;
+        const_cast<pic_plan *>(plan)->dec_next = 0;   // the scatter zeroed the decode slots
         if (prof) {
             check_hip(hipEventRecord(marks.ev[4], stream), "hipEventRecord");
             s->pending.push_back(marks);
@@ -394,12 +395,15 @@ pic_status pic_link_decode(pic_store *s, const pic_plan *plan, const void *q, co
         if (workspace_bytes < plan->workspace_bytes) fail(PIC_ERR_WORKSPACE, "workspace too small");
         if (plan->attended_ws != workspace)
             fail(PIC_ERR_STATE, "run pic_link_attend on this workspace first (it rotates the keys decode reads)");
+        if (plan->dec_next >= plan->dec_steps)
+            fail(PIC_ERR_STATE, "all " + std::to_string(plan->dec_steps) + " reserved decode steps are used");
         if (plan->n_requests == 0) return;
         if (!q || !k || !v || !out) fail(PIC_ERR_INVALID, "null tensor");
         uint8_t *ws = static_cast<uint8_t *>(workspace);
         DecodeTables t;
         t.pages = reinterpret_cast<const PageDesc *>(ws + plan->off_pages);
-        t.dec_pos = reinterpret_cast<const int32_t *>(ws + plan->off_dec_pos);
+        t.dec_req = reinterpret_cast<const DecodeReq *>(ws + plan->off_dec_req);
+        t.step = plan->dec_next;
         t.work = reinterpret_cast<const DecodeDesc *>(ws + plan->off_dec_work);
         t.n_work = (int)plan->dec_work.size();
         t.merge = reinterpret_cast<const DecodeMergeDesc *>(ws + plan->off_dec_merge);
@@ -407,7 +411,9 @@ pic_status pic_link_decode(pic_store *s, const pic_plan *plan, const void *q, co
         t.part_o = reinterpret_cast<float *>(ws + plan->off_dec_o);
         t.part_lse = reinterpret_cast<float *>(ws + plan->off_dec_lse);
         t.k_rot = plan->rotate_keys ? ws + plan->off_k_rot : nullptr;
-        check_hip(launch_decode(s->shape, q, k, v, s->v_pool, s->rope, t, out, lse, stream), "decode launch");
+        check_hip(launch_decode(s->shape, q, k, v, s->k_pool, s->v_pool, s->rope, t, out, lse, stream),
+                  "decode launch");
+        const_cast<pic_plan *>(plan)->dec_next += 1;
     });
 }
 

@@ -1128,11 +1128,11 @@ struct DecodeParams {
     const void *v_pool;
     const float *rope;
     const PageDesc *pages;
-    const int32_t *dec_pos;
+    const DecodeReq *dec_req;
     const DecodeDesc *work;
     float *part_o;
     float *part_lse;
-    int hq, hkv, gshift, pshift;
+    int hq, hkv, gshift, pshift, step;
     int64_t page_elems;
     float scale_log2;
 };
@@ -1148,7 +1148,7 @@ __global__ __launch_bounds__(256, 2) void link_decode_bf16(DecodeParams p) {
     __shared__ __attribute__((aligned(16))) int kval[NW * 32];
     __shared__ float obuf[NW * MAXG * D];
     __shared__ float mbuf[NW * MAXG], lbuf[NW * MAXG];
-    __shared__ int dpg_phys[kMaxItemPages], dpg_valid[kMaxItemPages];
+    __shared__ int dpg_phys[kMaxItemPages], dpg_pv[kMaxItemPages];
 
     const DecodeDesc w = p.work[blockIdx.x];
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, ln = lane & 31, lg = lane >> 5;
@@ -1158,19 +1158,22 @@ __global__ __launch_bounds__(256, 2) void link_decode_bf16(DecodeParams p) {
     const int lpage0 = w.page_base + w.page_begin;
     const int64_t head_off = (int64_t)w.kv_head * page_size * D;   // elements
     const uint32_t page_bytes = (uint32_t)p.page_elems * 2u;
-    // the range's page table, staged once (physical page and valid count of every page)
+    // the range's page table, staged once: the physical page, and the first position and valid
+    // count packed as pos0 << 7 | valid (positions below 2^22, valid <= 64)
     for (int i = tid; i < n_pages; i += 256) {
         const PageDesc d = p.pages[lpage0 + i];
         dpg_phys[i] = d.phys;
-        dpg_valid[i] = d.valid;
+        dpg_pv[i] = (d.pos0 << 7) | d.valid;
     }
     __syncthreads();
+    // the new token's position: keys at or after it (this step's token and later decode slots) are
+    // masked; the merge adds the token itself
+    const int qpos = p.dec_req[w.request].pos + p.step;
 
     // rotated, scaled query fragments of head ln (zero beyond the G heads)
     u32x4 qf[NS];
     {
         const bool valid = ln < G;
-        const int qpos = p.dec_pos[w.request];
         const uint16_t *qrow =
             static_cast<const uint16_t *>(p.q) + ((int64_t)w.request * p.hq + w.kv_head * G + (valid ? ln : 0)) * D;
         const float *cs = p.rope + (int64_t)qpos * D;
@@ -1213,7 +1216,8 @@ __global__ __launch_bounds__(256, 2) void link_decode_bf16(DecodeParams p) {
         const int slot = kk & (page_size - 1);
         const bool in_range = rel < n_pages;
         const int rc = in_range ? rel : n_pages - 1;
-        const bool ok = in_range && slot < dpg_valid[rc];
+        const int pv = dpg_pv[rc];
+        const bool ok = in_range && slot < (pv & 127) && (pv >> 7) + slot < qpos;
         const char *krow = krot_b + (uint64_t)(uint32_t)(lpage0 + rc) * page_bytes + (uint32_t)(head_off + slot * D) * 2u;
         // K: NS 16-byte pieces of the A operand. V: NS loads, each a contiguous run of RPI rows of
         // the block (a page holds whole runs: RPI <= 8 <= page size), lane = (row, 16-byte chunk)
@@ -1336,13 +1340,16 @@ __global__ __launch_bounds__(256, 2) void link_decode_bf16(DecodeParams p) {
 struct DecodeMergeParams {
     const void *q, *k, *v;
     const float *rope;
-    const int32_t *dec_pos;
+    const DecodeReq *dec_req;
     const DecodeMergeDesc *merge;
+    const PageDesc *pages;
     const float *part_o;
     const float *part_lse;
     void *out;
     float *lse;
-    int hq, hkv, gshift;
+    void *k_pool, *v_pool, *k_rot;   // the token's decode slot is written here
+    int hq, hkv, gshift, pshift, step;
+    int64_t page_elems;
     float scale_log2;
 };
 
@@ -1358,7 +1365,8 @@ __global__ __launch_bounds__(512) void link_decode_merge(DecodeMergeParams p) {
     const DecodeMergeDesc md = p.merge[blockIdx.x >> p.gshift];
     const int hl = blockIdx.x & (G - 1), h = md.kv_head * G + hl;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const int pos = p.dec_pos[md.request];
+    const DecodeReq dr = p.dec_req[md.request];
+    const int pos = dr.pos + p.step;
     const float *lse_r = p.part_lse + (int64_t)md.slot0 * G + hl;   // range j at lse_r[j * G]
     if (wave == 0) {
         const int i = lane & (D / 2 - 1);   // rotation pair (i, i + D/2); lanes past D/2 repeat it
@@ -1374,6 +1382,25 @@ __global__ __launch_bounds__(512) void link_decode_merge(DecodeMergeParams p) {
 #pragma unroll
         for (int o = 32; o > 0; o >>= 1) dot += __shfl_xor(dot, o);
         if (lane == 0) s_new_sh = dot;   // log2 units
+        // the first query head of the KV head writes the token into its decode slot, for the
+        // later steps: its key and value into the pools, its rotated key into the rotated keys
+        if (hl == 0 && lane < D / 2) {
+            const int page_size = 1 << p.pshift;
+            const int lp = dr.lpage0 + ((dr.off + p.step) >> p.pshift);
+            const int slot = (dr.off + p.step) & (page_size - 1);
+            const int64_t row = (int64_t)(md.kv_head * page_size + slot) * D;
+            const int64_t phys_row = (int64_t)p.pages[lp].phys * p.page_elems + row;
+            const int64_t rot_row = (int64_t)lp * p.page_elems + row;
+            const uint16_t *vr = static_cast<const uint16_t *>(p.v) + ((int64_t)md.request * p.hkv + md.kv_head) * D;
+            uint16_t *kp_ = static_cast<uint16_t *>(p.k_pool), *vp_ = static_cast<uint16_t *>(p.v_pool);
+            uint16_t *kr_ = static_cast<uint16_t *>(p.k_rot);
+            kp_[phys_row + i] = kr[i];
+            kp_[phys_row + i + D / 2] = kr[i + D / 2];
+            vp_[phys_row + i] = vr[i];
+            vp_[phys_row + i + D / 2] = vr[i + D / 2];
+            kr_[rot_row + i] = (uint16_t)(kp & 0xffffu);
+            kr_[rot_row + i + D / 2] = (uint16_t)(kp >> 16);
+        }
     }
     float mloc = -INFINITY;
     for (int j = tid; j < md.n_split; j += NT) mloc = fmaxf(mloc, lse_r[(int64_t)j * G]);
@@ -1509,9 +1536,10 @@ hipError_t launch_attention(const LayerShape &s, const void *q, const void *k_po
     return hipGetLastError();
 }
 
-hipError_t launch_decode(const LayerShape &s, const void *q, const void *k, const void *v, const void *v_pool,
+hipError_t launch_decode(const LayerShape &s, const void *q, const void *k, const void *v, void *k_pool, void *v_pool,
                          const float *rope, const DecodeTables &t, void *out, float *lse, hipStream_t stream) {
     if (s.dtype != 0) return hipErrorInvalidValue;
+    if (t.n_merge > 0 && !t.k_rot) return hipErrorInvalidValue;
     const int gshift = log2_exact(s.hq / s.hkv);
     const float scale_log2 = 1.4426950408889634f / sqrtf((float)s.d);
     if (t.n_work > 0) {
@@ -1522,7 +1550,8 @@ hipError_t launch_decode(const LayerShape &s, const void *q, const void *k, cons
         p.v_pool = v_pool;
         p.rope = rope;
         p.pages = t.pages;
-        p.dec_pos = t.dec_pos;
+        p.dec_req = t.dec_req;
+        p.step = t.step;
         p.work = t.work;
         p.part_o = t.part_o;
         p.part_lse = t.part_lse;
@@ -1543,8 +1572,15 @@ hipError_t launch_decode(const LayerShape &s, const void *q, const void *k, cons
     m.k = k;
     m.v = v;
     m.rope = rope;
-    m.dec_pos = t.dec_pos;
+    m.dec_req = t.dec_req;
     m.merge = t.merge;
+    m.pages = t.pages;
+    m.k_pool = k_pool;
+    m.v_pool = v_pool;
+    m.k_rot = t.k_rot;
+    m.pshift = log2_exact(s.page_size);
+    m.step = t.step;
+    m.page_elems = s.page_elems;
     m.part_o = t.part_o;
     m.part_lse = t.part_lse;
     m.out = out;

@@ -54,19 +54,21 @@ hipError_t launch_merge(const LayerShape &s, const AttnTables &t, void *out, flo
 
 struct DecodeTables {
     const PageDesc *pages;
-    const int32_t *dec_pos;          // per request: position of the new token
+    const DecodeReq *dec_req;        // per request: decode token positions and slots
+    int step;                        // decode step: token `step` of every request
     const DecodeDesc *work;
     int n_work;
     const DecodeMergeDesc *merge;    // one per (request, KV head)
     int n_merge;
     float *part_o;                   // [item][G][d]: normalised partial outputs
     float *part_lse;                 // [item][G]: their log2-sum-exp (scores in log2 units)
-    const void *k_rot;               // pre-rotated keys [logical page][Hkv][page][d]
+    void *k_rot;                     // pre-rotated keys [logical page][Hkv][page][d]
 };
 
 // Decode attention (split-KV over the pre-rotated keys and the pool's values), then the merge of
-// each (request, KV head)'s partial results with the new token's own key and value (bf16 only).
-hipError_t launch_decode(const LayerShape &s, const void *q, const void *k, const void *v, const void *v_pool,
+// each (request, KV head)'s partial results with the new token's own key and value, which the
+// merge also writes into the token's decode slot (pools and rotated keys) for later steps (bf16).
+hipError_t launch_decode(const LayerShape &s, const void *q, const void *k, const void *v, void *k_pool, void *v_pool,
                          const float *rope, const DecodeTables &t, void *out, float *lse, hipStream_t stream);
 
 }  // namespace piclink

@@ -64,6 +64,15 @@ struct DecodeDesc {
     int32_t pad0, pad1;
 };
 
+// Decode slots of one request: its first decode token's position and where its decode tokens
+// are written (token i at logical page lpage0 + (off + i) / page, slot (off + i) % page).
+struct DecodeReq {
+    int32_t pos;
+    int32_t lpage0;
+    int32_t off;
+    int32_t pad;
+};
+
 // Combine the partial results of one (request, KV head) with the new token's own key.
 struct DecodeMergeDesc {
     int32_t request;

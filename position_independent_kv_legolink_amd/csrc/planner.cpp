@@ -41,7 +41,7 @@ pic_plan *build_plan(pic_store *s, const pic_request *reqs, int32_t n_reqs, cons
     if (o.rope_keys < 0 || o.rope_keys > 2) fail(PIC_ERR_INVALID, "rope_keys must be 0, 1 or 2");
     if (o.rope_keys == 2 && cfg.dtype != PIC_DTYPE_BF16)
         fail(PIC_ERR_INVALID, "keys are rotated ahead of attention for bfloat16 stores only");
-    if (o.decode != 0 && o.decode != 1) fail(PIC_ERR_INVALID, "decode must be 0 or 1");
+    if (o.decode < 0 || o.decode > kMaxPosition) fail(PIC_ERR_INVALID, "decode must be in [0, max_position]");
     if (o.decode && cfg.dtype != PIC_DTYPE_BF16) fail(PIC_ERR_INVALID, "decode after link needs a bfloat16 store");
     if (o.decode && o.rope_keys == 1)
         fail(PIC_ERR_INVALID, "decode reads keys rotated ahead of attention: rope_keys must be 0 or 2");
@@ -74,13 +74,17 @@ pic_plan *build_plan(pic_store *s, const pic_request *reqs, int32_t n_reqs, cons
             segs.push_back({nullptr, q.suffix_len, pos, q.suffix_len, true});
             pos += q.suffix_len;
         }
+        ends[r] = (int32_t)std::min<int64_t>(pos, INT32_MAX);
+        if (o.decode > 0) {
+            // decode slots after the last token: the suffix's tail and pages, or a private segment
+            if (!segs.empty() && segs.back().suffix) segs.back().length += o.decode;
+            else segs.push_back({nullptr, o.decode, pos, 0, true});
+            pos += o.decode;
+        }
         if (pos > cfg.max_position)
             fail(PIC_ERR_INVALID, "request " + std::to_string(r) + " reaches position " + std::to_string(pos - 1) +
                                       " but the store's RoPE table ends at " + std::to_string(cfg.max_position - 1));
-        if (o.decode && pos >= cfg.max_position)
-            fail(PIC_ERR_INVALID, "request " + std::to_string(r) + ": its decode token at position " +
-                                      std::to_string(pos) + " lies beyond the store's RoPE table");
-        ends[r] = (int32_t)pos;
+
         for (const Seg &g : segs) {
             if (g.suffix) private_needed += (g.length + B - 1) / B;
             else private_needed += (g.recompute + B - 1) / B;
@@ -117,7 +121,8 @@ pic_plan *build_plan(pic_store *s, const pic_request *reqs, int32_t n_reqs, cons
                         store_ref(s, src);
                         plan->page_refs.push_back(src);
                     }
-                    plan->scatter.push_back({dst, src, n_new, seg_row0 + q * B, valid, 0, 0, 0});
+                    // slots past the new rows are copied from the stored page, or zeroed
+                    plan->scatter.push_back({dst, src, n_new, seg_row0 + q * B, src >= 0 ? valid : n_new, 0, 0, 0});
                     phys[q] = dst;
                 } else {
                     phys[q] = g.chunk->pages[q];
@@ -222,7 +227,13 @@ pic_plan *build_plan(pic_store *s, const pic_request *reqs, int32_t n_reqs, cons
     // compute unit over the whole batch; each range's partial result goes to its own slot
     if (o.decode) {
         plan->decode = true;
-        plan->dec_pos = ends;
+        plan->dec_steps = o.decode;
+        for (int r = 0; r < n_reqs; ++r) {
+            // the decode tokens sit in the request's last segment, after its suffix rows
+            const Seg &g = all[r].back();
+            const int32_t seg_pages = (g.length + B - 1) / B;
+            plan->dec_req.push_back({ends[r], plan->cu_pages[r + 1] - seg_pages, g.length - o.decode, 0});
+        }
         // a range's page table sits in LDS: at most kMaxItemPages pages
         const int64_t per_item = std::min<int64_t>(
             kMaxItemPages, std::max<int64_t>(4, (page_heads + 2 * s->num_cus - 1) / (2 * s->num_cus)));
@@ -254,7 +265,7 @@ pic_plan *build_plan(pic_store *s, const pic_request *reqs, int32_t n_reqs, cons
     plan->off_scatter = place((int64_t)plan->scatter.size() * sizeof(ScatterDesc));
     plan->off_work = place((int64_t)plan->work.size() * sizeof(WorkDesc));
     plan->off_merge = place((int64_t)plan->merge.size() * sizeof(MergeDesc));
-    plan->off_dec_pos = place((int64_t)plan->dec_pos.size() * sizeof(int32_t));
+    plan->off_dec_req = place((int64_t)plan->dec_req.size() * sizeof(DecodeReq));
     plan->off_dec_work = place((int64_t)plan->dec_work.size() * sizeof(DecodeDesc));
     plan->off_dec_merge = place((int64_t)plan->dec_merge.size() * sizeof(DecodeMergeDesc));
     plan->table_bytes = off;

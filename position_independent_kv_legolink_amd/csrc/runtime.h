@@ -75,10 +75,12 @@ struct pic_plan {
     int64_t off_k_rot = 0;
     // decode after link (plans made with opts.decode)
     bool decode = false;
-    std::vector<int32_t> dec_pos;       // per request: position of the new token
+    int32_t dec_steps = 0;              // decode steps reserved per request
+    int32_t dec_next = 0;               // the next decode step (reset by pic_link_attend)
+    std::vector<piclink::DecodeReq> dec_req;
     std::vector<piclink::DecodeDesc> dec_work;
     std::vector<piclink::DecodeMergeDesc> dec_merge;
-    int64_t off_dec_pos = 0, off_dec_work = 0, off_dec_merge = 0, off_dec_o = 0, off_dec_lse = 0;
+    int64_t off_dec_req = 0, off_dec_work = 0, off_dec_merge = 0, off_dec_o = 0, off_dec_lse = 0;
     const void *attended_ws = nullptr;  // workspace of the last pic_link_attend (holds the rotated keys)
     void *uploaded_to = nullptr;
 };

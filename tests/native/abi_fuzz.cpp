@@ -103,7 +103,7 @@ int main(int argc, char **argv) {
             o.recompute_all = U(0, 7) == 0;
             o.split_pages = U(0, 3) == 0 ? U(1, 200) : U(-1, 0);
             o.rope_keys = U(0, 15) == 0 ? 3 : U(0, 2);
-            o.decode = U(0, 15) == 0 ? 2 : U(0, 1);
+            o.decode = U(0, 15) == 0 ? -1 : U(0, 2) == 0 ? U(1, 40) : 0;
             pic_plan *plan = nullptr;
             const pic_status st = pic_link_plan(s, reqs.data(), n_req, &o, &plan);
             if (st == PIC_OK) {

@@ -1,11 +1,13 @@
 """Decode after link on the GPU against the fp64 oracle (needs an MI355X).
 
-After link_attend, every request's new token at the position after its last
-linked token attends over the linked cache and itself. For the oracle that
-token is one more row of the request's suffix (a suffix of one row when the
-request has none): its output is the oracle's attention of that row, computed
-from the pages' definition over the merged cache. Tolerance as for the link
-step: |gpu - oracle| <= 2e-2 + 1e-2 |oracle| in bf16.
+After link_attend, decode step i gives every request's token i, at the i-th
+position after its last linked token, attention over the linked cache, the
+tokens of the earlier steps (which the library appended to the request's
+reserved decode slots) and itself. For the oracle the decode tokens are more
+rows of the request's suffix (a suffix of their own when the request has
+none): step i's output is the oracle's attention of the (i+1)-th added row,
+computed from the pages' definition over the merged cache. Tolerance as for
+the link step: |gpu - oracle| <= 2e-2 + 1e-2 |oracle| in bf16.
 """
 from __future__ import annotations
 
@@ -46,8 +48,8 @@ def with_decode_row(segs):
     return segs + [oplan.Segment("suffix", None, 1, last.start + last.length, 1)]
 
 
-def decode_rows(cfg, n, seed):
-    g = np.random.default_rng([seed, 4242])
+def decode_rows(cfg, n, seed, step=0):
+    g = np.random.default_rng([seed, 4242, step])
     d = cfg.head_dim
     q = gen.round_bf16(g.standard_normal((n, cfg.num_q_heads, d), dtype=np.float32) * np.float32(cfg.q_scale))
     k = gen.round_bf16(g.standard_normal((n, cfg.num_kv_heads, d), dtype=np.float32) * np.float32(cfg.kv_scale))
@@ -55,7 +57,7 @@ def decode_rows(cfg, n, seed):
     return q, k, v
 
 
-def run_decode(cfg, *, n_requests=None, pos_offset=0, repeat=1, with_oracle=True):
+def run_decode(cfg, *, n_requests=None, pos_offset=0, repeat=1, with_oracle=True, steps=1):
     wl = Workload(cfg, n_requests=n_requests)
     segs = wl.segments(pos_offset=pos_offset, k=cfg.k)
     cached = wl.cached()
@@ -64,40 +66,55 @@ def run_decode(cfg, *, n_requests=None, pos_offset=0, repeat=1, with_oracle=True
     private = sum(p.private for s in segs for p in oplan.logical_pages(s, B))
     stored = sum(-(-v[0].shape[0] // B) for v in cached.values())
     n_tokens = max(oplan.total_tokens(s) for s in segs)
-    store = gpu_store(cfg, cached, num_pages=stored + private + 8, max_position=pos_offset + n_tokens + 2)
+    decode_pages = len(segs) * (-(-steps // B) + 1)
+    store = gpu_store(cfg, cached, num_pages=stored + private + decode_pages + 8,
+                      max_position=pos_offset + n_tokens + steps + 1)
     plan = store.link_plan(wl.link_requests(), k=cfg.k, block_level=cfg.block_level, pos_offset=pos_offset,
-                           decode=True)
+                           decode=steps)
     n = len(segs)
     assert plan.sizes["decode_items"] > 0 and plan.sizes["rotated_pages"] == plan.sizes["pages"]
     dev = lambda a: torch.from_numpy(np.ascontiguousarray(a)).to("cuda", torch.bfloat16).contiguous()
     q, kn, vn = (dev(np.concatenate([r[i] for r in rows])) for i in range(3))
-    plan.upload()
-    pic.link_attend(store, plan, q, kn, vn)
-    dq, dk, dv = decode_rows(cfg, n, cfg.seed)
-    outs = []
-    lse = torch.empty((n, cfg.num_q_heads), dtype=torch.float32, device="cuda")
+    tokens = [decode_rows(cfg, n, cfg.seed, i) for i in range(steps)]
+    results = []   # per step: (outputs of each repeat, lse, oracle)
     for _ in range(repeat):
-        out = pic.link_decode(store, plan, dev(dq), dev(dk), dev(dv), lse=lse)
-        torch.cuda.synchronize()
-        outs.append(out.float().cpu().numpy())
-    want = None
+        # a link call zeroes the decode slots and restarts the steps
+        plan.upload()
+        pic.link_attend(store, plan, q, kn, vn)
+        for i, (dq, dk, dv) in enumerate(tokens):
+            lse = torch.empty((n, cfg.num_q_heads), dtype=torch.float32, device="cuda")
+            out = pic.link_decode(store, plan, dev(dq), dev(dk), dev(dv), lse=lse)
+            torch.cuda.synchronize()
+            if len(results) <= i:
+                results.append([[], None, None])
+            results[i][0].append(out.float().cpu().numpy())
+            results[i][1] = lse.cpu().numpy()
     if with_oracle:
-        ext = [with_decode_row(s) for s in segs]
-        ext_rows = [(np.concatenate([r[0], dq[i:i + 1]]), np.concatenate([r[1], dk[i:i + 1]]),
-                     np.concatenate([r[2], dv[i:i + 1]])) for i, r in enumerate(rows)]
-        sample = {i: np.array([len(oplan.selected_positions(s)) - 1]) for i, s in enumerate(ext)}
-        want = oracle_outputs(ext, cached, ext_rows, cfg.rope_theta, sample=sample)
+        for i in range(steps):
+            ext = list(segs)
+            for _ in range(i + 1):
+                ext = [with_decode_row(s) for s in ext]
+            ext_rows = [tuple(np.concatenate([r[c]] + [tokens[j][c][a:a + 1] for j in range(i + 1)])
+                              for c in range(3)) for a, r in enumerate(rows)]
+            sample = {a: np.array([len(oplan.selected_positions(s)) - 1]) for a, s in enumerate(ext)}
+            results[i][2] = oracle_outputs(ext, cached, ext_rows, cfg.rope_theta, sample=sample)
+    with pytest.raises(pic.PicError) as e:   # every reserved step is used
+        pic.link_decode(store, plan, *(dev(t) for t in tokens[-1]))
+    assert e.value.status == -7
     plan.free()
-    return outs, lse.cpu().numpy(), want
+    return results
 
 
-def check(cfg, outs, lse, want, what):
+def check(cfg, results, what):
     atol, rtol = TOLERANCE[cfg.dtype]
     worst = 0.0
-    for i, (wo, wl) in enumerate(want):
-        worst = max(worst, assert_close(outs[0][i:i + 1], wo, atol, rtol, f"{what} request {i} out"))
-        assert_close(lse[i:i + 1], wl, atol, rtol, f"{what} request {i} lse")
-    _say(f"{what}: max abs err {worst:.3e}")
+    for step, (outs, lse, want) in enumerate(results):
+        for i, (wo, wl) in enumerate(want):
+            worst = max(worst, assert_close(outs[0][i:i + 1], wo, atol, rtol, f"{what} step {step} request {i} out"))
+            assert_close(lse[i:i + 1], wl, atol, rtol, f"{what} step {step} request {i} lse")
+        for o in outs[1:]:
+            assert np.array_equal(o, outs[0]), f"{what} step {step}: run-to-run results differ"
+    _say(f"{what}: {len(results)} steps, max abs err {worst:.3e}")
 
 
 DECODE_EDGE = {n: c for n, c in EDGE.items() if c.get("dtype", "bf16") == "bf16"}
@@ -107,22 +124,27 @@ DECODE_EDGE = {n: c for n, c in EDGE.items() if c.get("dtype", "bf16") == "bf16"
 def test_decode_edge_cases(name):
     cfg = small_cfg(**DECODE_EDGE[name])
     _say(f"decode, edge case {name}")
-    outs, lse, want = run_decode(cfg)
-    check(cfg, outs, lse, want, f"decode {name}")
+    check(cfg, run_decode(cfg, steps=3), f"decode {name}")
 
 
 @pytest.mark.parametrize("name", ["llama3_k2", "batched_k16", "long50k_k32", "block_zipf"])
 def test_decode_workloads(name):
     cfg = CONFIGS[name]
     _say(f"decode, {name}")
-    outs, lse, want = run_decode(cfg, repeat=2)
-    check(cfg, outs, lse, want, f"decode {name}")
-    assert np.array_equal(outs[0], outs[1]), "run-to-run results differ"
+    check(cfg, run_decode(cfg, repeat=2, steps=2), f"decode {name}")
 
 
 @pytest.mark.parametrize("offset", [1, 100000])
 def test_decode_position_offset(offset):
     cfg = small_cfg(chunk_len=64)
     _say(f"decode, pos_offset {offset}")
-    outs, lse, want = run_decode(cfg, pos_offset=offset)
-    check(cfg, outs, lse, want, f"decode offset {offset}")
+    check(cfg, run_decode(cfg, pos_offset=offset, steps=2), f"decode offset {offset}")
+
+
+@pytest.mark.parametrize("suffix_len,steps", [(15, 4), (16, 3), (0, 18), (5, 40)])
+def test_decode_steps_cross_pages(suffix_len, steps):
+    """Decode tokens fill the suffix's last page, then new pages (page 16): a suffix one short of
+    a page, a full page, no suffix (the tokens get pages of their own) and 40 steps."""
+    cfg = small_cfg(suffix_len=suffix_len, n_requests=2, chunk_len=50)
+    _say(f"decode, suffix {suffix_len}, {steps} steps")
+    check(cfg, run_decode(cfg, steps=steps), f"decode suffix {suffix_len}")
