@@ -998,10 +998,13 @@ __global__ __launch_bounds__(kThreads) void link_merge(const MergeDesc *merge, c
     {
         const int m = blockIdx.y * RPB + (int)threadIdx.x / (D / 4), d4 = (int)threadIdx.x % (D / 4);
         if (m >= mrows) return;
+        // the splits' loads are independent: unrolled, several are in flight at once
         float L = -INFINITY;
+#pragma unroll 4
         for (int s = 0; s < md.n_split; ++s) L = fmaxf(L, part_lse[(int64_t)(md.slot0 + s) * tq + m]);
         floatx4 acc = {0, 0, 0, 0};
         float wsum = 0.0f;
+#pragma unroll 4
         for (int s = 0; s < md.n_split; ++s) {
             const float ls = part_lse[(int64_t)(md.slot0 + s) * tq + m];
             const float wgt = ls == -INFINITY ? 0.0f : expf(ls - L);
