@@ -185,6 +185,31 @@ pic_status pic_store_chunk_pages(const pic_store *store, uint64_t id, int32_t *p
  * plan references them. */
 pic_status pic_store_release(pic_store *store, uint64_t id);
 
+/* Store lifecycle: evict least recently used chunks until at least target_free_pages pages
+ * of the pool are free (EPIC digest, 关键设计 / key design: the cache replacement policy, LRU for
+ * example, and the cache size are key parameters). A chunk's use is its ingest and every
+ * pic_link_plan that links it (as a prefix or a chunk). Only chunks whose pages no live plan
+ * holds are candidates, since releasing the others frees nothing until those plans are freed.
+ * *evicted (may be NULL) receives the number of chunks released. Errors: PIC_ERR_INVALID
+ * (target outside [0, num_pages]), PIC_ERR_OOM (the target cannot be reached; nothing is
+ * evicted then). */
+pic_status pic_store_evict(pic_store *store, int32_t target_free_pages, int32_t *evicted);
+
+/* Footprint of a store's pool: every page is free, held by a stored chunk (shared by every plan
+ * that links it), or held only by live plans (their private pages, and pages of chunks released
+ * while plans still use them). */
+typedef struct {
+    int64_t pages_total;
+    int64_t pages_free;
+    int64_t pages_chunks;
+    int64_t pages_plans_only;
+    int64_t chunks;
+    int64_t plans;
+    int64_t evictions;   /* chunks released by pic_store_evict since the store was created */
+} pic_store_usage_info;
+
+pic_status pic_store_usage(const pic_store *store, pic_store_usage_info *usage);
+
 /* Free pages in the pool, stored chunks, live plans. Any pointer may be NULL. */
 pic_status pic_store_stats(const pic_store *store, int32_t *free_pages, int32_t *chunks, int32_t *plans);
 

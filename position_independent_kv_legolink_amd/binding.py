@@ -22,7 +22,8 @@ STATUS_NAMES = {-1: "PIC_ERR_INVALID", -2: "PIC_ERR_OOM", -3: "PIC_ERR_NOT_FOUND
 DTYPES = {"bf16": 0, "f32": 1}
 
 EXPORTS = ["pic_store_sizes", "pic_store_create", "pic_store_destroy", "pic_store_chunk",
-           "pic_store_chunk_pages", "pic_store_release", "pic_store_stats", "pic_link_plan",
+           "pic_store_chunk_pages", "pic_store_release", "pic_store_evict", "pic_store_usage", "pic_store_stats",
+           "pic_link_plan",
            "pic_plan_info", "pic_plan_export", "pic_plan_upload", "pic_link_attend", "pic_link_decode",
            "pic_plan_free",
            "pic_profile_enable", "pic_profile_read", "pic_last_error"]
@@ -53,6 +54,12 @@ class LinkOptions(ctypes.Structure):
                 ("rope_keys", ctypes.c_int32), ("decode", ctypes.c_int32)]
 
 
+class StoreUsage(ctypes.Structure):
+    _fields_ = [("pages_total", ctypes.c_int64), ("pages_free", ctypes.c_int64), ("pages_chunks", ctypes.c_int64),
+                ("pages_plans_only", ctypes.c_int64), ("chunks", ctypes.c_int64), ("plans", ctypes.c_int64),
+                ("evictions", ctypes.c_int64)]
+
+
 class PlanSizes(ctypes.Structure):
     _fields_ = [("rows", ctypes.c_int64), ("pages", ctypes.c_int64), ("private_pages", ctypes.c_int64),
                 ("cow_pages", ctypes.c_int64), ("work_items", ctypes.c_int64),
@@ -81,6 +88,8 @@ def lib():
             "pic_store_chunk_pages": [vp, u64, vp, i32, P(i32), P(i32)],
             "pic_store_release": [vp, u64],
             "pic_store_stats": [vp, P(i32), P(i32), P(i32)],
+            "pic_store_evict": [vp, i32, P(i32)],
+            "pic_store_usage": [vp, P(StoreUsage)],
             "pic_link_plan": [vp, P(Request), i32, P(LinkOptions), P(vp)],
             "pic_plan_info": [vp, P(PlanSizes)],
             "pic_plan_export": [vp, vp, vp, vp, vp, vp, vp, vp, vp],
@@ -193,6 +202,17 @@ class Store:
         f, c, p = ctypes.c_int32(), ctypes.c_int32(), ctypes.c_int32()
         _check(lib().pic_store_stats(self.handle, ctypes.byref(f), ctypes.byref(c), ctypes.byref(p)))
         return dict(free_pages=f.value, chunks=c.value, plans=p.value)
+
+    def evict(self, target_free_pages: int) -> int:
+        """Release least recently used chunks until target_free_pages pages are free; returns how many."""
+        n = ctypes.c_int32()
+        _check(lib().pic_store_evict(self.handle, int(target_free_pages), ctypes.byref(n)))
+        return n.value
+
+    def usage(self):
+        u = StoreUsage()
+        _check(lib().pic_store_usage(self.handle, ctypes.byref(u)))
+        return {f: getattr(u, f) for f, _ in StoreUsage._fields_}
 
     def link_plan(self, requests, *, k=0, block_level=False, pos_offset=0, recompute_all=False,
                   split_pages=0, rope_keys=0, decode=0):

@@ -181,6 +181,7 @@ pic_status pic_store_chunk(pic_store *s, uint64_t id, const void *k, const void 
                                   std::to_string(s->free_pages.size()) + " free");
         Chunk c;
         c.n_tokens = n_tokens;
+        c.last_use = ++s->use_clock;
         for (int i = 0; i < n_pages; ++i) c.pages.push_back(store_alloc_page(s));
         if (k) {
             for (int32_t first = 0; first < n_pages; first += kMaxFillPages) {
@@ -221,6 +222,57 @@ pic_status pic_store_release(pic_store *s, uint64_t id) {
         if (it == s->chunks.end()) fail(PIC_ERR_NOT_FOUND, "chunk " + std::to_string(id) + " is not stored");
         for (int32_t p : it->second.pages) store_unref(s, p);
         s->chunks.erase(it);
+    });
+}
+
+pic_status pic_store_evict(pic_store *s, int32_t target_free_pages, int32_t *evicted) {
+    return guarded([&] {
+        if (!s) fail(PIC_ERR_INVALID, "null store");
+        if (evicted) *evicted = 0;
+        if (target_free_pages < 0 || target_free_pages > s->cfg.num_pages)
+            fail(PIC_ERR_INVALID, "target_free_pages must be in [0, num_pages]");
+        // candidates: chunks whose pages only the chunk table holds, least recently used first
+        std::vector<std::pair<uint64_t, uint64_t>> order;   // (last use, id)
+        int64_t reclaimable = 0;
+        for (const auto &kv : s->chunks) {
+            bool only_table = true;
+            for (int32_t p : kv.second.pages) only_table = only_table && s->refs[p] == 1;
+            if (only_table) {
+                order.push_back({kv.second.last_use, kv.first});
+                reclaimable += (int64_t)kv.second.pages.size();
+            }
+        }
+        const int64_t free_now = (int64_t)s->free_pages.size();
+        if (free_now >= target_free_pages) return;
+        if (free_now + reclaimable < target_free_pages)
+            fail(PIC_ERR_OOM, "only " + std::to_string(free_now + reclaimable) + " pages can be freed (" +
+                                  std::to_string(target_free_pages) + " asked): the rest are held by live plans");
+        std::sort(order.begin(), order.end());
+        int32_t n = 0;
+        for (const auto &c : order) {
+            if ((int64_t)s->free_pages.size() >= target_free_pages) break;
+            auto it = s->chunks.find(c.second);
+            for (int32_t p : it->second.pages) store_unref(s, p);
+            s->chunks.erase(it);
+            ++n;
+        }
+        s->evictions += n;
+        if (evicted) *evicted = n;
+    });
+}
+
+pic_status pic_store_usage(const pic_store *s, pic_store_usage_info *u) {
+    return guarded([&] {
+        if (!s || !u) fail(PIC_ERR_INVALID, "null argument");
+        int64_t chunk_pages = 0;
+        for (const auto &kv : s->chunks) chunk_pages += (int64_t)kv.second.pages.size();
+        u->pages_total = s->cfg.num_pages;
+        u->pages_free = (int64_t)s->free_pages.size();
+        u->pages_chunks = chunk_pages;
+        u->pages_plans_only = u->pages_total - u->pages_free - chunk_pages;
+        u->chunks = (int64_t)s->chunks.size();
+        u->plans = s->live_plans;
+        u->evictions = s->evictions;
     });
 }
 

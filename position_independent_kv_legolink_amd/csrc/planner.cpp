@@ -141,6 +141,16 @@ pic_plan *build_plan(pic_store *s, const pic_request *reqs, int32_t n_reqs, cons
         plan->cu_pages.push_back((int32_t)plan->pages.size());
     }
     s->live_plans += 1;
+    // the chunks this plan links are the store's most recently used ones now
+    const uint64_t now = ++s->use_clock;
+    auto touch = [&](uint64_t id) {
+        auto it = s->chunks.find(id);
+        if (it != s->chunks.end()) it->second.last_use = now;
+    };
+    for (int r = 0; r < n_reqs; ++r) {
+        if (reqs[r].has_prefix) touch(reqs[r].prefix_id);
+        for (int i = 0; i < reqs[r].n_chunks; ++i) touch(reqs[r].chunk_ids[i]);
+    }
 
     // ---- attention work list
     const int G = cfg.num_q_heads / cfg.num_kv_heads;

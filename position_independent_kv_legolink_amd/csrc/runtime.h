@@ -25,6 +25,7 @@ struct Error {
 struct Chunk {
     int32_t n_tokens = 0;
     std::vector<int32_t> pages;
+    uint64_t last_use = 0;   // store clock at ingest or at the last plan that linked it
 };
 
 struct ProfileMarks {
@@ -43,6 +44,8 @@ struct pic_store {
     std::set<int32_t> free_pages;       // lowest id first
     std::unordered_map<uint64_t, piclink::Chunk> chunks;
     int32_t live_plans = 0;
+    uint64_t use_clock = 0;             // advanced by every chunk ingest and every link plan
+    int64_t evictions = 0;              // chunks released by pic_store_evict
     int32_t num_cus = 256;              // compute units used by the work-list split policy
     bool profiling = false;
     int32_t profiled_calls = 0;

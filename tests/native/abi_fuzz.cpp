@@ -115,6 +115,30 @@ int main(int argc, char **argv) {
                 CHECK(st == PIC_ERR_INVALID || st == PIC_ERR_NOT_FOUND || st == PIC_ERR_OOM);
                 ++errors_seen;
             }
+            // evict towards a random free-page target: success reaches it, failure changes nothing
+            if (U(0, 4) == 0) {
+                const int target = U(-1, cfg.num_pages + 1);
+                int32_t f0 = 0, c0 = 0, f1 = 0, c1 = 0, n = -1;
+                CHECK(pic_store_stats(s, &f0, &c0, nullptr) == PIC_OK);
+                const pic_status es = pic_store_evict(s, target, &n);
+                CHECK(pic_store_stats(s, &f1, &c1, nullptr) == PIC_OK);
+                if (es == PIC_OK) {
+                    CHECK(f1 >= target && c0 - c1 == n && n >= 0);
+                } else {
+                    CHECK((es == PIC_ERR_INVALID || es == PIC_ERR_OOM) && f1 == f0 && c1 == c0);
+                    ++errors_seen;
+                }
+                // chunks that eviction released are gone from the id list
+                std::vector<uint64_t> kept;
+                for (uint64_t id : ids) {
+                    int32_t np = 0, nt = 0;
+                    if (pic_store_chunk_pages(s, id, nullptr, 0, &np, &nt) == PIC_OK) kept.push_back(id);
+                }
+                ids = kept;
+                pic_store_usage_info u;
+                CHECK(pic_store_usage(s, &u) == PIC_OK);
+                CHECK(u.pages_free + u.pages_chunks + u.pages_plans_only == u.pages_total && u.pages_plans_only >= 0);
+            }
             // release a chunk that live plans may still reference
             if (!ids.empty() && U(0, 3) == 0) {
                 const int i = U(0, (int)ids.size() - 1);

@@ -199,3 +199,66 @@ def test_decode_option_is_validated():
     with pytest.raises(pic.PicError) as e:
         f.link_plan([pic.LinkRequest([1], 5)], k=2, decode=True)
     assert e.value.status == -1
+
+
+def _usage_consistent(s):
+    u = s.usage()
+    assert u["pages_free"] + u["pages_chunks"] + u["pages_plans_only"] == u["pages_total"]
+    assert u["pages_free"] == s.stats()["free_pages"] and u["chunks"] == s.stats()["chunks"]
+    return u
+
+
+def test_evict_releases_least_recently_used_chunks():
+    """Chunks age by ingest and by the plans that link them; eviction frees the oldest first."""
+    s = meta(num_pages=6)
+    for cid in (1, 2, 3):
+        s.store_chunk(cid, n_tokens=32)              # 2 pages each: the pool is full
+    assert _usage_consistent(s)["pages_chunks"] == 6
+    s.link_plan([pic.LinkRequest([1], 0)], k=0).free()   # chunk 1 is now the most recent
+    assert s.evict(2) == 1                           # chunk 2: ingested before 3, never linked since
+    with pytest.raises(pic.PicError) as e:
+        s.chunk_pages(2)
+    assert e.value.status == -3
+    assert s.evict(2) == 0                           # already 2 free pages
+    assert s.evict(4) == 1                           # then chunk 3
+    u = _usage_consistent(s)
+    assert u["chunks"] == 1 and u["evictions"] == 2 and u["pages_free"] == 4
+    s.close()
+
+
+def test_evict_skips_chunks_that_live_plans_hold():
+    """A chunk whose pages a live plan holds frees nothing when released, so eviction passes it
+    by; a target that only such chunks could meet fails without evicting anything."""
+    s = meta(num_pages=8)
+    for cid in (1, 2, 3):
+        s.store_chunk(cid, n_tokens=32)
+    plan = s.link_plan([pic.LinkRequest([1], 0)], k=0)   # holds chunk 1's pages; touches it last
+    with pytest.raises(pic.PicError) as e:
+        s.evict(8)                                   # 2 free + 4 of chunks 2 and 3 < 8
+    assert e.value.status == -2
+    assert s.stats()["chunks"] == 3 and s.usage()["evictions"] == 0
+    assert s.evict(6) == 2                           # chunks 2 and 3; chunk 1 stays
+    assert s.stats()["chunks"] == 1
+    plan.free()
+    assert s.evict(8) == 1
+    assert _usage_consistent(s)["pages_free"] == 8
+    with pytest.raises(pic.PicError) as e:
+        s.evict(9)
+    assert e.value.status == -1
+    s.close()
+
+
+def test_usage_counts_pages_held_only_by_plans():
+    """Private pages, and the pages of a chunk released while a plan uses it, are held by plans
+    only; they return to the pool with the plan."""
+    s = meta(num_pages=16)
+    s.store_chunk(1, n_tokens=40)                    # 3 pages
+    plan = s.link_plan([pic.LinkRequest([1], 20)], k=2)   # private: chunk page 0 (copy-on-write) + 2 suffix pages
+    u = _usage_consistent(s)
+    assert u["pages_chunks"] == 3 and u["pages_plans_only"] == 3 and u["plans"] == 1
+    s.release(1)
+    u = _usage_consistent(s)
+    assert u["pages_chunks"] == 0 and u["pages_plans_only"] == 6
+    plan.free()
+    assert _usage_consistent(s)["pages_free"] == 16
+    s.close()
