@@ -12,7 +12,12 @@
  *   - keys are stored without positional encoding and rotary position
  *     embedding is applied at the linked position at attention time (MEPIC,
  *     searcharxiv.org abstract: positional encodings removed from stored KV,
- *     RoPE fused into attention);
+ *     RoPE fused into attention): key t is rotated by key_rot[t], which is
+ *     key_pos[t] for such a key (key_rot NULL). A key that already carries a
+ *     rotation at its position s inside its segment, as a chunk compiled from
+ *     position 0 leaves it (EPIC, atlas.scime.ai summary, "Approach"), is
+ *     rotated by the segment's linked start instead; the two rotations
+ *     compose to one at the key's absolute position;
  *   - rotation pairs dimension i with i + d/2 ("rotate half"), angle
  *     pos * theta^(-2i/d), no frequency scaling;
  *   - row r, query head h attends key head g = h / (Hq/Hkv) over every key
@@ -44,7 +49,7 @@ static void rotate(const double *x, double *y, int d, int64_t pos, const double 
 /* Returns 0 on success, -1 on invalid arguments, -2 when memory runs out. */
 int oracle_link_attention(int n_keys, int n_kv_heads, int n_q_heads, int head_dim,
                           const double *k, const double *v, const int64_t *key_pos,
-                          int n_rows, const double *q, const int64_t *row_pos,
+                          const int64_t *key_rot, int n_rows, const double *q, const int64_t *row_pos,
                           double rope_theta, double *out, double *lse)
 {
     if (n_keys < 0 || n_rows < 0 || n_kv_heads <= 0 || n_q_heads <= 0 || head_dim <= 0 ||
@@ -68,7 +73,7 @@ int oracle_link_attention(int n_keys, int n_kv_heads, int n_q_heads, int head_di
     for (int t = 0; t < n_keys; ++t)
         for (int g = 0; g < n_kv_heads; ++g)
             rotate(k + ((size_t)t * n_kv_heads + g) * d, k_rot + ((size_t)t * n_kv_heads + g) * d,
-                   d, key_pos[t], inv_freq);
+                   d, key_rot ? key_rot[t] : key_pos[t], inv_freq);
 
     const double inv_sqrt_d = 1.0 / sqrt((double)d);
     int failed = 0;

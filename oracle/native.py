@@ -33,7 +33,7 @@ def load(path: str):
     f = L.oracle_link_attention
     f.restype = ctypes.c_int
     f.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int,
-                  ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
+                  ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
                   ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p,
                   ctypes.c_double, ctypes.c_void_p, ctypes.c_void_p]
     f._keepalive = L
@@ -48,13 +48,21 @@ def lib():
     return _lib
 
 
-def attention(k, v, key_pos, q, row_pos, rope_theta, entry=None):
-    """fp64 causal RoPE attention; see attention.c. Returns (out [R][Hq][d], lse [R][Hq])."""
+def attention(k, v, key_pos, q, row_pos, rope_theta, entry=None, key_rot=None):
+    """fp64 causal RoPE attention; see attention.c. Returns (out [R][Hq][d], lse [R][Hq]).
+
+    ``key_rot`` (optional, [n_keys]) is the position each key is rotated by; by
+    default its absolute position ``key_pos``.
+    """
     k = np.ascontiguousarray(k, dtype=np.float64)
     v = np.ascontiguousarray(v, dtype=np.float64)
     q = np.ascontiguousarray(q, dtype=np.float64)
     key_pos = np.ascontiguousarray(key_pos, dtype=np.int64)
     row_pos = np.ascontiguousarray(row_pos, dtype=np.int64)
+    if key_rot is not None:
+        key_rot = np.ascontiguousarray(key_rot, dtype=np.int64)
+        if key_rot.shape != key_pos.shape:
+            raise ValueError("shape mismatch")
     n_keys, hkv, d = k.shape
     n_rows, hq, dq = q.shape
     if v.shape != k.shape or dq != d or key_pos.shape != (n_keys,) or row_pos.shape != (n_rows,):
@@ -63,7 +71,8 @@ def attention(k, v, key_pos, q, row_pos, rope_theta, entry=None):
     lse = np.empty((n_rows, hq), dtype=np.float64)
     fn = entry if entry is not None else lib()
     rc = fn(n_keys, hkv, hq, d, k.ctypes.data, v.ctypes.data,
-                                     key_pos.ctypes.data, n_rows, q.ctypes.data,
+                                     key_pos.ctypes.data, None if key_rot is None else key_rot.ctypes.data,
+                                     n_rows, q.ctypes.data,
                                      row_pos.ctypes.data, float(rope_theta),
                                      out.ctypes.data, lse.ctypes.data)
     if rc != 0:

@@ -197,6 +197,26 @@ def test_matches_brute_force(case):
     assert np.abs(lse - bl).max() < 1e-12
 
 
+# ------------------------------------------- keys compiled from position 0
+@pytest.mark.parametrize("case", range(len(CASES)))
+def test_keys_compiled_from_zero_equal_position_free(case):
+    """Cached keys handed over rotated at 0..L-1 of their own segment (EPIC: every chunk encoded
+    from position 0) and re-rotated by the segment's start give the position-free result:
+    R(start) R(j) = R(start + j). The compiled form is made here by complex multiplication."""
+    req = tiny_request(300 + case, **CASES[case])
+    base, base_lse = run_oracle(req)
+    compiled = {cid: (_rotate_complex(k, np.arange(k.shape[0]), req["theta"]), v)
+                for cid, (k, v) in req["cached"].items()}
+    out, lse = olink.link_attention(req["segs"], compiled, req["q"], req["k"], req["v"], req["theta"],
+                                    key_layout="segment_rope")
+    assert np.abs(out - base).max() < 1e-12
+    assert np.abs(lse - base_lse).max() < 1e-12
+    if any(s.kind != "suffix" and s.start > 0 and s.recompute < s.length for s in req["segs"]) and len(base):
+        # read as position-free, the compiled keys would give another result
+        wrong, _ = olink.link_attention(req["segs"], compiled, req["q"], req["k"], req["v"], req["theta"])
+        assert np.abs(wrong - base).max() > 1e-3
+
+
 def test_first_chunk_rows_ignore_cached_values():
     req = tiny_request(7, prefix_len=0, chunk_lens=(10, 12), k=4, page_size=4)
     base, _ = run_oracle(req)

@@ -3,7 +3,8 @@
 Each case compiles a copy of oracle/attention.c with one plausible mistake
 (a flipped rotation sign, a wrong pairing frequency, a dropped scale, an
 exclusive causal bound, a wrong GQA head map, a one-pass softmax without the
-maximum) into a temporary directory and runs the closed-form and dense-case
+maximum, a key rotation that ignores the per-key rotation position) into a
+temporary directory and runs the closed-form, dense-case and compiled-from-0
 pins against it. Every mutant has to fail at least one of them; the
 unmodified source has to pass all of them.
 """
@@ -29,6 +30,7 @@ MUTANTS = {
     "gqa_modulo": ("int g = h / group;", "int g = h % n_kv_heads;"),
     "value_head": ("const double *vt = v + ((size_t)t * n_kv_heads + g) * d;",
                    "const double *vt = v + ((size_t)t * n_kv_heads + 0) * d;"),
+    "rotation_position_ignored": ("key_rot ? key_rot[t] : key_pos[t]", "key_pos[t]"),
 }
 
 
@@ -65,21 +67,31 @@ def _causal_ok(fn):
     return bool(np.isfinite(out).all() and np.allclose(out[0, 0], [1.0, 0.0], atol=0, rtol=0))
 
 
-def _dense_ok(fn):
+def _dense_ok(fn, compiled_from_zero=False):
+    """One segment at offset 5, every row attending: scaled_dot_product_attention over tensors
+    rotated by complex multiplication. With compiled_from_zero the keys are handed over
+    rotated at 0..L-1 (a chunk encoded on its own) and rotated by the segment's start."""
     g = np.random.default_rng(0)
     L, hq, hkv, d, theta = 23, 4, 2, 16, 1e4
     q = g.standard_normal((L, hq, d))
     k = g.standard_normal((L, hkv, d))
     v = g.standard_normal((L, hkv, d))
     pos = np.arange(L) + 5
-    out, _ = native.attention(k, v, pos, q, pos, theta, entry=fn)
     h = d // 2
     freq = theta ** (-2.0 * np.arange(h) / d)
-    ph = np.exp(1j * pos[:, None] * freq[None, :])[:, None, :]
+
+    def rot_at(x, at):
+        z = (x[..., :h] + 1j * x[..., h:]) * np.exp(1j * at[:, None] * freq[None, :])[:, None, :]
+        return np.concatenate([z.real, z.imag], -1)
+
+    if compiled_from_zero:
+        out, _ = native.attention(rot_at(k, np.arange(L)), v, pos, q, pos, theta, entry=fn,
+                                  key_rot=np.full(L, 5))
+    else:
+        out, _ = native.attention(k, v, pos, q, pos, theta, entry=fn)
 
     def rot(x):
-        z = (x[..., :h] + 1j * x[..., h:]) * ph
-        return torch.from_numpy(np.concatenate([z.real, z.imag], -1)).permute(1, 0, 2)
+        return torch.from_numpy(rot_at(x, pos)).permute(1, 0, 2)
 
     ref = torch.nn.functional.scaled_dot_product_attention(
         rot(q)[None], rot(k).repeat_interleave(hq // hkv, 0)[None],
@@ -91,7 +103,7 @@ def _dense_ok(fn):
 @pytest.mark.parametrize("name", list(MUTANTS))
 def test_pins_catch_planted_mistakes(tmp_path, name):
     fn = _build(tmp_path, name)
-    verdicts = [_closed_form_ok(fn), _causal_ok(fn), _dense_ok(fn)]
+    verdicts = [_closed_form_ok(fn), _causal_ok(fn), _dense_ok(fn), _dense_ok(fn, compiled_from_zero=True)]
     if name == "original":
         assert all(verdicts)
     else:
