@@ -68,6 +68,12 @@ typedef int32_t pic_status;
 #define PIC_DTYPE_BF16 0
 #define PIC_DTYPE_F32 1
 
+/* How stored keys carry position (pic_store_config.key_layout). */
+#define PIC_KEYS_POSITION_FREE 0   /* pre-RoPE keys (MEPIC abstract: positional encodings removed) */
+#define PIC_KEYS_SEGMENT_ROPE 1    /* keys rotated at their position inside their own segment, as a
+                                      chunk compiled from position 0 leaves them (EPIC summary,
+                                      "Approach") */
+
 typedef struct pic_store pic_store;
 typedef struct pic_plan pic_plan;
 
@@ -76,7 +82,12 @@ typedef struct pic_plan pic_plan;
  *   page_size     tokens per page: 16, 32 or 64
  *   num_q_heads   a multiple of num_kv_heads, with Hq/Hkv in {1, 2, 4, 8}
  *   max_position  every linked position must be < max_position (RoPE table rows);
- *                 at most 4,194,304 */
+ *                 at most 4,194,304
+ *   key_layout    PIC_KEYS_POSITION_FREE: stored keys are pre-RoPE and each key is rotated at
+ *                 its absolute linked position t. PIC_KEYS_SEGMENT_ROPE: a key stored at
+ *                 position s of its segment holds R(s)k, and is re-rotated by the segment's
+ *                 linked start a (R(a)R(s)k = R(a + s)k, the RoPE composition rule). Both give
+ *                 the same attention up to rounding. Other values: PIC_ERR_INVALID. */
 typedef struct {
     int32_t num_q_heads;
     int32_t num_kv_heads;
@@ -86,6 +97,7 @@ typedef struct {
     int32_t dtype;
     double rope_theta;
     int32_t max_position;
+    int32_t key_layout;
 } pic_store_config;
 
 /* One prompt to link: [prefix] chunk_ids[0..n_chunks) [suffix of suffix_len new tokens].
@@ -165,10 +177,13 @@ pic_status pic_store_create(const pic_store_config *cfg, void *k_pool, void *v_p
 /* Destroy a store. Outstanding plans must be freed first (PIC_ERR_STATE otherwise). */
 pic_status pic_store_destroy(pic_store *store);
 
-/* Compile-step product in: store the position-free K and V of one chunk
- * (EPIC summary, "Approach": each chunk compiled independently from
- * position 0; MEPIC abstract: KV kept without positional encoding, page
- * aligned). k, v: device [n_tokens][Hkv][d] of the store dtype, pre-RoPE.
+/* Compile-step product in: store the K and V of one chunk (EPIC summary,
+ * "Approach": each chunk compiled independently from position 0; MEPIC
+ * abstract: KV kept without positional encoding, page aligned).
+ * k, v: device [n_tokens][Hkv][d] of the store dtype. K is pre-RoPE in a
+ * PIC_KEYS_POSITION_FREE store; in a PIC_KEYS_SEGMENT_ROPE store token j's key
+ * is already rotated at position j (rotate-half pairs (i, i + d/2), angle
+ * j * theta^(-2i/d)), as compiling the chunk from position 0 produces it.
  * Takes ceil(n_tokens / page_size) pages, lowest free ids first; the last
  * page's padding slots are zero-filled. NULL k and v reserve the pages
  * without writing (metadata-only use). Errors: PIC_ERR_EXISTS,
@@ -257,11 +272,15 @@ pic_status pic_plan_upload(pic_store *store, pic_plan *plan, void *workspace, in
  *   out    [rows][Hq][d]   attention output, store dtype
  *   lse    [rows][Hq]      optional float32 natural-log softmax denominators
  * 1. scatter: every private page gets the new rows it holds, the cached rows
- *    copied from its stored page (copy-on-write) and zeroed padding;
+ *    copied from its stored page (copy-on-write) and zeroed padding; in a
+ *    PIC_KEYS_SEGMENT_ROPE store a new row's key is written rotated at its
+ *    position inside its segment, the store's key form;
  * 2. key rotation, when the plan has rotated_pages: the keys of every logical
- *    page rotated at their absolute positions into the workspace;
+ *    page rotated to their absolute positions into the workspace (by the
+ *    key's position, or by its segment's start in a PIC_KEYS_SEGMENT_ROPE
+ *    store);
  * 3. attention: every selected row attends causally over its request's linked
- *    pages with RoPE applied at each token's absolute position;
+ *    pages with every key rotated to its absolute position;
  * 4. merge of split KV ranges (log-sum-exp weighted), when the plan split.
  * workspace must be the one the plan was uploaded to. Asynchronous. */
 pic_status pic_link_attend(pic_store *store, const pic_plan *plan, const void *q_new, const void *k_new,
@@ -275,7 +294,8 @@ pic_status pic_link_attend(pic_store *store, const pic_plan *plan, const void *q
  * p = end + i (end = the position after its last linked token) attends over the request's
  * linked cache (positions < end, with the recomputed rows' K/V that pic_link_attend
  * scattered), over the tokens of steps 0 .. i-1 and over itself; the step then writes the
- * token's key and value into its decode slot, for the later steps.
+ * token's key and value into its decode slot, for the later steps (the key in the store's
+ * key form: rotated at its position inside its segment in a PIC_KEYS_SEGMENT_ROPE store).
  *   q      [n_req][Hq][d]   the tokens' queries, pre-RoPE
  *   k, v   [n_req][Hkv][d]  their keys (pre-RoPE) and values
  *   out    [n_req][Hq][d]   attention output, store dtype

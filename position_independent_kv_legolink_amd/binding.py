@@ -39,7 +39,12 @@ class StoreConfig(ctypes.Structure):
     _fields_ = [("num_q_heads", ctypes.c_int32), ("num_kv_heads", ctypes.c_int32),
                 ("head_dim", ctypes.c_int32), ("page_size", ctypes.c_int32),
                 ("num_pages", ctypes.c_int32), ("dtype", ctypes.c_int32),
-                ("rope_theta", ctypes.c_double), ("max_position", ctypes.c_int32)]
+                ("rope_theta", ctypes.c_double), ("max_position", ctypes.c_int32),
+                ("key_layout", ctypes.c_int32)]
+
+
+# how stored keys carry position: pre-RoPE, or rotated at their position inside their segment
+KEY_LAYOUTS = {"position_free": 0, "segment_rope": 1}
 
 
 class Request(ctypes.Structure):
@@ -135,13 +140,17 @@ class Store:
     """Paged chunk-KV store over caller-owned torch device pools.
 
     With ``device=None`` the store holds metadata only (host planning, tests
-    without a GPU).
+    without a GPU). ``key_layout`` is "position_free" (stored keys are pre-RoPE)
+    or "segment_rope" (a chunk's token j holds its key rotated at position j).
     """
 
     def __init__(self, *, num_q_heads, num_kv_heads, head_dim, page_size, num_pages, dtype,
-                 rope_theta, max_position, device="cuda"):
+                 rope_theta, max_position, device="cuda", key_layout="position_free"):
+        if key_layout not in KEY_LAYOUTS:
+            raise ValueError(f"key_layout must be one of {sorted(KEY_LAYOUTS)}")
         self.cfg = StoreConfig(num_q_heads, num_kv_heads, head_dim, page_size, num_pages, DTYPES[dtype],
-                               float(rope_theta), max_position)
+                               float(rope_theta), max_position, KEY_LAYOUTS[key_layout])
+        self.key_layout = key_layout
         self.dtype = dtype
         self.device = device
         self.k_pool = self.v_pool = self.rope_table = None
@@ -176,7 +185,7 @@ class Store:
             pass
 
     def store_chunk(self, chunk_id: int, k=None, v=None, n_tokens: int | None = None):
-        """k, v: device tensors [n][Hkv][d] of the store dtype (position-free); or n_tokens only."""
+        """k, v: device tensors [n][Hkv][d] of the store dtype, keys in the store's key form; or n_tokens only."""
         if k is not None:
             n_tokens = k.shape[0]
             exp = (n_tokens, self.cfg.num_kv_heads, self.cfg.head_dim)

@@ -60,6 +60,8 @@ void store_check_config(const pic_store_config &c) {
     if (!(c.rope_theta > 0.0)) fail(PIC_ERR_INVALID, "rope_theta must be positive");
     if (c.max_position <= 0 || c.max_position > kMaxPosition)
         fail(PIC_ERR_INVALID, "max_position must be in [1, " + std::to_string(kMaxPosition) + "]");
+    if (c.key_layout != PIC_KEYS_POSITION_FREE && c.key_layout != PIC_KEYS_SEGMENT_ROPE)
+        fail(PIC_ERR_INVALID, "key_layout must be PIC_KEYS_POSITION_FREE or PIC_KEYS_SEGMENT_ROPE");
 }
 
 int32_t store_alloc_page(pic_store *s) {
@@ -113,7 +115,7 @@ pic_status pic_store_create(const pic_store_config *cfg, void *k_pool, void *v_p
         pic_store *s = new pic_store();
         s->cfg = *cfg;
         s->shape = {cfg->num_q_heads, cfg->num_kv_heads, cfg->head_dim, cfg->page_size, cfg->dtype,
-                    (int64_t)cfg->num_kv_heads * cfg->page_size * cfg->head_dim};
+                    (int64_t)cfg->num_kv_heads * cfg->page_size * cfg->head_dim, cfg->key_layout};
         s->k_pool = k_pool;
         s->v_pool = v_pool;
         s->rope = static_cast<float *>(rope_table);
@@ -412,7 +414,7 @@ pic_status pic_link_attend(pic_store *s, const pic_plan *plan, const void *q_new
             }
             check_hip(hipEventRecord(marks.ev[0], stream), "hipEventRecord");
         }
-        check_hip(launch_scatter(s->shape, s->k_pool, s->v_pool, k_new, v_new,
+        check_hip(launch_scatter(s->shape, s->k_pool, s->v_pool, k_new, v_new, s->rope,
                                  reinterpret_cast<const ScatterDesc *>(ws + plan->off_scatter),
                                  (int)plan->scatter.size(), stream),
                   "scatter launch");

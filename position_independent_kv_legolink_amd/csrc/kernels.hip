@@ -80,6 +80,7 @@ struct AttnParams {
     int64_t page_elems;
     float scale_log2;           // log2(e) / sqrt(d)
     float scale;                // 1 / sqrt(d)
+    int seg_keys;               // keys stored rotated inside their segment: rotate by its start
 };
 
 // A callable that issues piece j of a tile's loads, with the number of pieces as a constant
@@ -125,9 +126,12 @@ __device__ __forceinline__ void rope8_bf16(const u32x4 &lo, const u32x4 &hi, con
 // common softmax path is exp2, a row sum and the bf16 packing. A wave past the last key tile its
 // rows attend keeps staging tiles for the others, with the same barriers, and computes nothing.
 // KR: keys come pre-rotated (rotate_keys, indexed by logical page) and are staged as loaded;
-// otherwise they are rotated here, with the same table values and arithmetic.
-template <int D, bool KR>
+// otherwise they are rotated here, with the same table values and arithmetic: by each key's
+// absolute position, or (SEG: the store holds keys rotated at their position inside their
+// segment) by the start of the key's segment, one cos/sin row per page.
+template <int D, bool KR, bool SEG>
 __global__ __launch_bounds__(512, 1) void link_attention_bf16(AttnParams p) {
+    static_assert(!(KR && SEG), "pre-rotated keys need no segment starts");
     constexpr int NT = 512;
     constexpr int KT = kKeysPerTile;
     constexpr int KS = D + 8;          // K' row stride in LDS (bf16): conflict-free A-fragment reads
@@ -147,6 +151,7 @@ __global__ __launch_bounds__(512, 1) void link_attention_bf16(AttnParams p) {
     __shared__ __attribute__((aligned(16))) uint16_t vs[4 * VBUF];
     __shared__ __attribute__((aligned(16))) int kpos_s[3 * KT];
     __shared__ int pg_phys[kMaxItemPages], pg_pv[kMaxItemPages];
+    __shared__ int pg_seg[SEG ? kMaxItemPages : 1];
 
     const WorkDesc w = p.work[blockIdx.x];
     if (w.n_rows <= 0) return;
@@ -251,13 +256,14 @@ __global__ __launch_bounds__(512, 1) void link_attention_bf16(AttnParams p) {
         const PageDesc d = pg[w.page_begin + i];
         pg_phys[i] = d.phys;
         pg_pv[i] = (d.pos0 << 7) | d.valid;
+        if constexpr (SEG) pg_seg[i] = d.seg0;
     }
     lds_barrier();
     // descriptor values read ahead from LDS: the wave's K page and V pages (uniform) and the
     // page of key `lane` (for the mask positions). The reads are unconditional (clamped to the
     // last page) and the range test is applied where the values are used: a conditional read
     // becomes a branch whose join waits for the LDS result at once.
-    int rk_phys[NKP], rk_pv[NKP], rv_phys[NVC], rl_pv;
+    int rk_phys[NKP], rk_pv[NKP], rk_seg[NKP], rv_phys[NVC], rl_pv;
     bool rk_in[NKP], rl_in;
     auto load_desc = [&](int t) __attribute__((always_inline)) {
         const int r0 = t * ppt;
@@ -271,6 +277,7 @@ __global__ __launch_bounds__(512, 1) void link_attention_bf16(AttnParams p) {
             } else {
                 rk_phys[u] = pg_phys[r];
                 rk_pv[u] = pg_pv[r];
+                if constexpr (SEG) rk_seg[u] = pg_seg[r];
                 rk_in[u] = rq < n_pages;
             }
         }
@@ -297,7 +304,10 @@ __global__ __launch_bounds__(512, 1) void link_attention_bf16(AttnParams p) {
                     const int pos0 = pv >> 7, valid = pv & 127;
                     const int pi = tid + NT * u;
                     const bool ok = (KPAIRS % NT == 0 || pi < KPAIRS) && rk_in[u] && k_slot[u] < valid;
-                    k_pos[u] = ok ? pos0 + k_slot[u] : pos0;
+                    // the cos/sin row of the key's rotation (padding slots hold zeros, which
+                    // rotate to zeros with any row)
+                    if constexpr (SEG) k_pos[u] = __builtin_amdgcn_readfirstlane(rk_seg[u]);
+                    else k_pos[u] = ok ? pos0 + k_slot[u] : pos0;
                 }
                 k_page[u] = kpool_b + (uint64_t)phys * page_bytes;
                 k_lo[u] = *reinterpret_cast<const u32x4 *>(k_page[u] + k_loff[u]);
@@ -805,7 +815,7 @@ __global__ __launch_bounds__(kThreads, 1) void link_attention_f32(AttnParams p) 
                 const PageDesc pd = pg[lp];
                 if (slot < pd.valid) {
                     ok = true;
-                    pos = pd.pos0 + slot;
+                    pos = p.seg_keys ? pd.seg0 : pd.pos0 + slot;   // cos/sin row of the rotation
                     base = (int64_t)pd.phys * p.page_elems + head_off + (int64_t)slot * D;
                 }
             }
@@ -1053,14 +1063,19 @@ __global__ __launch_bounds__(kThreads) void store_fill(FillPages pages, uint8_t 
     }
 }
 
+// In a store of keys rotated at their position inside their segment (rotate_new), a new row's
+// key is written in that form: rotated at slot position local0 + slot, with the table values and
+// the fp32 arithmetic of the attention kernels' key rotation. Cached rows are copied as stored.
 __global__ __launch_bounds__(kThreads) void link_scatter(const ScatterDesc *table, uint8_t *k_pool, uint8_t *v_pool,
-                                                         const uint8_t *k_new, const uint8_t *v_new, int hkv,
-                                                         int page_size, int row_bytes, int64_t page_bytes) {
+                                                         const uint8_t *k_new, const uint8_t *v_new, const float *rope,
+                                                         int rotate_new, int elem, int hkv, int page_size,
+                                                         int row_bytes, int64_t page_bytes) {
     const ScatterDesc sd = table[blockIdx.x];
     const int h = blockIdx.y;
     const int pieces_per_row = row_bytes / 16;
     const int64_t head_bytes = (int64_t)h * page_size * row_bytes;
     const int64_t dst0 = (int64_t)sd.dst * page_bytes + head_bytes;
+    const int n_rot = rotate_new ? sd.n_new : 0;   // new rows whose keys are written rotated below
     for (int c = threadIdx.x; c < page_size * pieces_per_row; c += kThreads) {
         const int slot = c / pieces_per_row, piece = c % pieces_per_row;
         u32x4 a = {0, 0, 0, 0}, b = {0, 0, 0, 0};
@@ -1074,20 +1089,59 @@ __global__ __launch_bounds__(kThreads) void link_scatter(const ScatterDesc *tabl
             b = *reinterpret_cast<const u32x4 *>(v_pool + src);
         }
         const int64_t dst = dst0 + (int64_t)slot * row_bytes + piece * 16;
-        *reinterpret_cast<u32x4 *>(k_pool + dst) = a;
+        if (slot >= n_rot) *reinterpret_cast<u32x4 *>(k_pool + dst) = a;
         *reinterpret_cast<u32x4 *>(v_pool + dst) = b;
+    }
+    if (n_rot > 0) {
+        // a thread takes pieces c and c + half of one new key: the rotation pairs (i, i + d/2)
+        const int half = pieces_per_row / 2, d = row_bytes / elem;
+        for (int c = threadIdx.x; c < n_rot * half; c += kThreads) {
+            const int slot = c / half, piece = c % half;
+            const int64_t src = ((int64_t)(sd.row0 + slot) * hkv + h) * row_bytes + piece * 16;
+            const u32x4 lo = *reinterpret_cast<const u32x4 *>(k_new + src);
+            const u32x4 hi = *reinterpret_cast<const u32x4 *>(k_new + src + row_bytes / 2);
+            const float *cs = rope + (int64_t)(sd.local0 + slot) * d;
+            u32x4 olo, ohi;
+            if (elem == 2) {
+                const int e0 = piece * 8;
+                floatx4 co[2], sn[2];
+                co[0] = *reinterpret_cast<const floatx4 *>(cs + e0);
+                co[1] = *reinterpret_cast<const floatx4 *>(cs + e0 + 4);
+                sn[0] = *reinterpret_cast<const floatx4 *>(cs + d / 2 + e0);
+                sn[1] = *reinterpret_cast<const floatx4 *>(cs + d / 2 + e0 + 4);
+                rope8_bf16(lo, hi, co, sn, olo, ohi);
+            } else {
+                const int e0 = piece * 4;
+                const floatx4 co = *reinterpret_cast<const floatx4 *>(cs + e0);
+                const floatx4 sn = *reinterpret_cast<const floatx4 *>(cs + d / 2 + e0);
+                const floatx4 x = __builtin_bit_cast(floatx4, lo), y = __builtin_bit_cast(floatx4, hi);
+                floatx4 xr, yr;
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    xr[j] = fmaf(x[j], co[j], -y[j] * sn[j]);
+                    yr[j] = fmaf(y[j], co[j], x[j] * sn[j]);
+                }
+                olo = __builtin_bit_cast(u32x4, xr);
+                ohi = __builtin_bit_cast(u32x4, yr);
+            }
+            const int64_t dst = dst0 + (int64_t)slot * row_bytes + piece * 16;
+            *reinterpret_cast<u32x4 *>(k_pool + dst) = olo;
+            *reinterpret_cast<u32x4 *>(k_pool + dst + row_bytes / 2) = ohi;
+        }
     }
 }
 
-// Keys of every logical page of a plan rotated once at the page's absolute positions, with the
+// Keys of every logical page of a plan rotated once to the page's absolute positions, with the
 // attention kernel's table values and arithmetic, into the pool's page layout indexed by logical
 // page ([page][Hkv][page_size][d]); padding slots are written as zeros (the pools hold zeros
-// there, which rotate to zeros). One work group per logical page; a thread takes 8 (x_i,
-// x_{i+d/2}) pairs of one (head, slot) per pass, consecutive threads consecutive pairs of a row.
+// there, which rotate to zeros). A position-free key is rotated by its position; a key stored
+// rotated at its position inside its segment (seg_keys) by the segment's start. One work group
+// per logical page; a thread takes 8 (x_i, x_{i+d/2}) pairs of one (head, slot) per pass,
+// consecutive threads consecutive pairs of a row.
 template <int D>
 __global__ __launch_bounds__(kThreads) void rotate_keys_bf16(const PageDesc *pages, const uint8_t *k_pool,
                                                              const float *rope, uint8_t *k_rot, int hkv, int pshift,
-                                                             int64_t page_bytes) {
+                                                             int64_t page_bytes, int seg_keys) {
     const PageDesc pd = pages[blockIdx.x];
     const int page_size = 1 << pshift;
     constexpr int PPR = D / 16;   // pieces per row
@@ -1101,7 +1155,7 @@ __global__ __launch_bounds__(kThreads) void rotate_keys_bf16(const PageDesc *pag
         if (slot < pd.valid) {
             const u32x4 lo = *reinterpret_cast<const u32x4 *>(src + off);
             const u32x4 hi = *reinterpret_cast<const u32x4 *>(src + off + D);
-            const float *cs = rope + (int64_t)(pd.pos0 + slot) * D + 8 * c;
+            const float *cs = rope + (int64_t)(seg_keys ? pd.seg0 : pd.pos0 + slot) * D + 8 * c;
             floatx4 co[2], sn[2];
             co[0] = *reinterpret_cast<const floatx4 *>(cs);
             co[1] = *reinterpret_cast<const floatx4 *>(cs + 4);
@@ -1354,6 +1408,7 @@ struct DecodeMergeParams {
     int hq, hkv, gshift, pshift, step;
     int64_t page_elems;
     float scale_log2;
+    int seg_keys;                    // the pool holds keys rotated at their position in their segment
 };
 
 template <int D>
@@ -1397,8 +1452,17 @@ __global__ __launch_bounds__(512) void link_decode_merge(DecodeMergeParams p) {
             const uint16_t *vr = static_cast<const uint16_t *>(p.v) + ((int64_t)md.request * p.hkv + md.kv_head) * D;
             uint16_t *kp_ = static_cast<uint16_t *>(p.k_pool), *vp_ = static_cast<uint16_t *>(p.v_pool);
             uint16_t *kr_ = static_cast<uint16_t *>(p.k_rot);
-            kp_[phys_row + i] = kr[i];
-            kp_[phys_row + i + D / 2] = kr[i + D / 2];
+            if (p.seg_keys) {
+                // the pool's form: rotated at the token's position inside its segment
+                const float *cl = p.rope + (int64_t)(pos - dr.seg0) * D;
+                const float c2 = cl[i], s2 = cl[D / 2 + i];
+                const uint32_t kl = pack_bf16(fmaf(kx, c2, -ky * s2), fmaf(ky, c2, kx * s2));
+                kp_[phys_row + i] = (uint16_t)(kl & 0xffffu);
+                kp_[phys_row + i + D / 2] = (uint16_t)(kl >> 16);
+            } else {
+                kp_[phys_row + i] = kr[i];
+                kp_[phys_row + i + D / 2] = kr[i + D / 2];
+            }
             vp_[phys_row + i] = vr[i];
             vp_[phys_row + i + D / 2] = vr[i + D / 2];
             kr_[rot_row + i] = (uint16_t)(kp & 0xffffu);
@@ -1472,13 +1536,14 @@ hipError_t launch_store_fill(const LayerShape &s, void *k_pool, void *v_pool, co
 }
 
 hipError_t launch_scatter(const LayerShape &s, void *k_pool, void *v_pool, const void *k_new, const void *v_new,
-                          const ScatterDesc *table, int n, hipStream_t stream) {
+                          const float *rope, const ScatterDesc *table, int n, hipStream_t stream) {
     if (n <= 0) return hipSuccess;
     const int elem = s.dtype == 0 ? 2 : 4;
     dim3 grid(n, s.hkv);
     hipLaunchKernelGGL(link_scatter, grid, dim3(kThreads), 0, stream, table, static_cast<uint8_t *>(k_pool),
                        static_cast<uint8_t *>(v_pool), static_cast<const uint8_t *>(k_new),
-                       static_cast<const uint8_t *>(v_new), s.hkv, s.page_size, s.d * elem, s.page_elems * elem);
+                       static_cast<const uint8_t *>(v_new), rope, s.key_layout, elem, s.hkv, s.page_size, s.d * elem,
+                       s.page_elems * elem);
     return hipGetLastError();
 }
 
@@ -1491,11 +1556,11 @@ hipError_t launch_rotate_keys(const LayerShape &s, const void *k_pool, const flo
     if (s.d == 128)
         hipLaunchKernelGGL(rotate_keys_bf16<128>, dim3(n_pages), dim3(kThreads), 0, stream, pages,
                            static_cast<const uint8_t *>(k_pool), rope, static_cast<uint8_t *>(k_rot), s.hkv, pshift,
-                           page_bytes);
+                           page_bytes, s.key_layout);
     else
         hipLaunchKernelGGL(rotate_keys_bf16<64>, dim3(n_pages), dim3(kThreads), 0, stream, pages,
                            static_cast<const uint8_t *>(k_pool), rope, static_cast<uint8_t *>(k_rot), s.hkv, pshift,
-                           page_bytes);
+                           page_bytes, s.key_layout);
     return hipGetLastError();
 }
 
@@ -1523,14 +1588,18 @@ hipError_t launch_attention(const LayerShape &s, const void *q, const void *k_po
     p.page_elems = s.page_elems;
     p.scale = 1.0f / sqrtf((float)s.d);
     p.scale_log2 = 1.4426950408889634f / sqrtf((float)s.d);
+    p.seg_keys = s.key_layout;
     dim3 grid(t.n_work);
     if (s.dtype == 0) {
         if (t.k_rot) {
-            if (s.d == 128) hipLaunchKernelGGL((link_attention_bf16<128, true>), grid, dim3(512), 0, stream, p);
-            else hipLaunchKernelGGL((link_attention_bf16<64, true>), grid, dim3(512), 0, stream, p);
+            if (s.d == 128) hipLaunchKernelGGL((link_attention_bf16<128, true, false>), grid, dim3(512), 0, stream, p);
+            else hipLaunchKernelGGL((link_attention_bf16<64, true, false>), grid, dim3(512), 0, stream, p);
+        } else if (s.key_layout) {
+            if (s.d == 128) hipLaunchKernelGGL((link_attention_bf16<128, false, true>), grid, dim3(512), 0, stream, p);
+            else hipLaunchKernelGGL((link_attention_bf16<64, false, true>), grid, dim3(512), 0, stream, p);
         } else {
-            if (s.d == 128) hipLaunchKernelGGL((link_attention_bf16<128, false>), grid, dim3(512), 0, stream, p);
-            else hipLaunchKernelGGL((link_attention_bf16<64, false>), grid, dim3(512), 0, stream, p);
+            if (s.d == 128) hipLaunchKernelGGL((link_attention_bf16<128, false, false>), grid, dim3(512), 0, stream, p);
+            else hipLaunchKernelGGL((link_attention_bf16<64, false, false>), grid, dim3(512), 0, stream, p);
         }
     } else {
         if (s.d == 128) hipLaunchKernelGGL(link_attention_f32<128>, grid, dim3(kThreads), 0, stream, p);
@@ -1592,6 +1661,7 @@ hipError_t launch_decode(const LayerShape &s, const void *q, const void *k, cons
     m.hkv = s.hkv;
     m.gshift = gshift;
     m.scale_log2 = scale_log2;
+    m.seg_keys = s.key_layout;
     const dim3 grid(t.n_merge << gshift);
     if (s.d == 128) hipLaunchKernelGGL(link_decode_merge<128>, grid, dim3(512), 0, stream, m);
     else hipLaunchKernelGGL(link_decode_merge<64>, grid, dim3(512), 0, stream, m);

@@ -11,6 +11,7 @@ namespace piclink {
 struct LayerShape {
     int hq, hkv, d, page_size, dtype;
     int64_t page_elems;   // elements of one page in one pool: Hkv * page_size * d
+    int key_layout;       // PIC_KEYS_POSITION_FREE or PIC_KEYS_SEGMENT_ROPE
 };
 
 constexpr int kMaxFillPages = 480;
@@ -26,12 +27,14 @@ struct FillPages {
 hipError_t launch_store_fill(const LayerShape &s, void *k_pool, void *v_pool, const void *k, const void *v,
                              const FillPages &pages, hipStream_t stream);
 
-// Scatter kernel over `n` private pages described in `table` (device).
+// Scatter kernel over `n` private pages described in `table` (device). In a store of
+// segment-rotated keys, new keys are rotated at their position inside their segment (rope).
 hipError_t launch_scatter(const LayerShape &s, void *k_pool, void *v_pool, const void *k_new, const void *v_new,
-                          const ScatterDesc *table, int n, hipStream_t stream);
+                          const float *rope, const ScatterDesc *table, int n, hipStream_t stream);
 
-// K of `n_pages` logical pages (device PageDesc table) rotated at their positions into k_rot
-// ([logical page][Hkv][page][d]); bfloat16 layers only.
+// K of `n_pages` logical pages (device PageDesc table) rotated to their absolute positions into
+// k_rot ([logical page][Hkv][page][d]): by each key's position, or by its segment's start when
+// the store's keys are rotated inside their segment; bfloat16 layers only.
 hipError_t launch_rotate_keys(const LayerShape &s, const void *k_pool, const float *rope, const PageDesc *pages,
                               int n_pages, void *k_rot, hipStream_t stream);
 

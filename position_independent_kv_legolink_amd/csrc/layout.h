@@ -12,19 +12,22 @@ struct PageDesc {
     int32_t phys;    // physical page id in the pools
     int32_t pos0;    // absolute position of slot 0
     int32_t valid;   // slots [0, valid) hold tokens, the rest are padding
-    int32_t pad;
+    int32_t seg0;    // absolute position of the first token of the page's segment
 };
 
 // One private page written by the scatter kernel before attention:
 // slots [0, n_new) take new rows row0.., slots [n_new, n_valid) are copied
 // from page `src` (copy-on-write, src >= 0), slots [n_valid, page) are zeroed.
+// local0 is slot 0's position inside its segment (the rotation of new keys in a
+// store whose keys are rotated at their position inside their segment).
 struct ScatterDesc {
     int32_t dst;
     int32_t src;
     int32_t n_new;
     int32_t row0;
     int32_t n_valid;
-    int32_t pad0, pad1, pad2;
+    int32_t local0;
+    int32_t pad1, pad2;
 };
 
 // One attention work item: a tile of consecutive selected rows of one request
@@ -70,7 +73,7 @@ struct DecodeReq {
     int32_t pos;
     int32_t lpage0;
     int32_t off;
-    int32_t pad;
+    int32_t seg0;    // absolute position of the first token of the segment holding the slots
 };
 
 // Combine the partial results of one (request, KV head) with the new token's own key.

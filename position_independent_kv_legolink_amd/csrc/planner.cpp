@@ -7,7 +7,10 @@
 //     block-level variant, and every suffix token; a prefix is cached and not recomputed;
 //   - every segment starts on a fresh page; pages that hold no recomputed row stay shared
 //     with the store; the others are private to the request and, when they also keep cached
-//     rows, are filled copy-on-write from their stored page.
+//     rows, are filled copy-on-write from their stored page;
+//   - every page carries its segment's start, the rotation of keys stored as a chunk compiled
+//     from position 0 leaves them, and every private page its first slot's position inside the
+//     segment, where the scatter rotates new keys to in such a store.
 // The attention work list then cuts each request's rows into tiles of tile_qrows / G rows,
 // one work item per (tile, KV head), splits key ranges longer than a compute unit's average
 // load (or the kernel's page-table limit) and orders the items longest first, grouped so that
@@ -122,14 +125,14 @@ pic_plan *build_plan(pic_store *s, const pic_request *reqs, int32_t n_reqs, cons
                         plan->page_refs.push_back(src);
                     }
                     // slots past the new rows are copied from the stored page, or zeroed
-                    plan->scatter.push_back({dst, src, n_new, seg_row0 + q * B, src >= 0 ? valid : n_new, 0, 0, 0});
+                    plan->scatter.push_back({dst, src, n_new, seg_row0 + q * B, src >= 0 ? valid : n_new, q * B, 0, 0});
                     phys[q] = dst;
                 } else {
                     phys[q] = g.chunk->pages[q];
                     store_ref(s, phys[q]);
                 }
                 plan->page_refs.push_back(phys[q]);
-                plan->pages.push_back({phys[q], (int32_t)(g.start + (int64_t)q * B), valid, 0});
+                plan->pages.push_back({phys[q], (int32_t)(g.start + (int64_t)q * B), valid, (int32_t)g.start});
             }
             for (int j = 0; j < g.recompute; ++j) {
                 plan->row_pos.push_back((int32_t)(g.start + j));
@@ -242,7 +245,7 @@ pic_plan *build_plan(pic_store *s, const pic_request *reqs, int32_t n_reqs, cons
             // the decode tokens sit in the request's last segment, after its suffix rows
             const Seg &g = all[r].back();
             const int32_t seg_pages = (g.length + B - 1) / B;
-            plan->dec_req.push_back({ends[r], plan->cu_pages[r + 1] - seg_pages, g.length - o.decode, 0});
+            plan->dec_req.push_back({ends[r], plan->cu_pages[r + 1] - seg_pages, g.length - o.decode, (int32_t)g.start});
         }
         // a range's page table sits in LDS: at most kMaxItemPages pages
         const int64_t per_item = std::min<int64_t>(

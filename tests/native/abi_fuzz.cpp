@@ -61,7 +61,9 @@ int main(int argc, char **argv) {
         cfg.dtype = U(0, 3) ? PIC_DTYPE_BF16 : PIC_DTYPE_F32;
         cfg.rope_theta = U(0, 1) ? 5e5 : 1e4;
         cfg.max_position = U(1, 1 << 14);
+        cfg.key_layout = U(0, 1) ? PIC_KEYS_SEGMENT_ROPE : PIC_KEYS_POSITION_FREE;
         if (U(0, 15) == 0) cfg.head_dim = 96;   // invalid
+        if (U(0, 31) == 0) cfg.key_layout = U(0, 1) ? 2 : -1;   // invalid
         pic_store *s = nullptr;
         const pic_status cs = pic_store_create(&cfg, nullptr, nullptr, nullptr, nullptr, &s);
         if (cs != PIC_OK) {

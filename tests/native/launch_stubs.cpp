@@ -10,8 +10,8 @@ hipError_t launch_store_fill(const LayerShape &, void *, void *, const void *, c
                              hipStream_t) {
     return hipErrorNotSupported;
 }
-hipError_t launch_scatter(const LayerShape &, void *, void *, const void *, const void *, const ScatterDesc *, int,
-                          hipStream_t) {
+hipError_t launch_scatter(const LayerShape &, void *, void *, const void *, const void *, const float *,
+                          const ScatterDesc *, int, hipStream_t) {
     return hipErrorNotSupported;
 }
 hipError_t launch_rotate_keys(const LayerShape &, const void *, const float *, const PageDesc *, int, void *,

@@ -5,6 +5,7 @@ import ctypes
 import re
 import subprocess
 
+import numpy as np
 import pytest
 
 import position_independent_kv_legolink_amd as pic
@@ -50,6 +51,32 @@ def test_store_config_validation(bad):
 
 def test_store_accepts_the_largest_max_position():
     meta(max_position=1 << 22).close()
+
+
+def test_key_layout_is_validated():
+    """The binding names the two key forms; the C ABI rejects any other value."""
+    meta(key_layout="segment_rope").close()
+    with pytest.raises(ValueError):
+        meta(key_layout="rotated")
+    cfg = pic.binding.StoreConfig(8, 2, 128, 16, 64, 0, 5e5, 4096, 2)
+    h = ctypes.c_void_p()
+    assert pic.lib().pic_store_create(ctypes.byref(cfg), None, None, None, None, ctypes.byref(h)) == -1
+    assert b"key_layout" in pic.lib().pic_last_error()
+
+
+def test_plans_of_both_key_layouts_are_identical():
+    """The key form changes only how keys are rotated, not the plan."""
+    ex = []
+    for layout in ("position_free", "segment_rope"):
+        st = meta(key_layout=layout)
+        for c in range(3):
+            st.store_chunk(c, None, None, n_tokens=50)
+        plan = st.link_plan([pic.LinkRequest(chunk_ids=[2, 0, 1], suffix_len=9)], k=5)
+        ex.append(plan.export())
+        plan.free()
+        st.close()
+    for key in ex[0]:
+        assert np.array_equal(ex[0][key], ex[1][key]), key
 
 
 def test_store_and_plan_errors():

@@ -57,7 +57,16 @@ def decode_rows(cfg, n, seed, step=0):
     return q, k, v
 
 
-def run_decode(cfg, *, n_requests=None, pos_offset=0, repeat=1, with_oracle=True, steps=1):
+def rotate_at(x, pos, theta):
+    """RoPE of x [..][d] at one position, as complex multiplication (fp64)."""
+    d = x.shape[-1]
+    h = d // 2
+    z = (x[..., :h] + 1j * x[..., h:]) * np.exp(1j * pos * theta ** (-2.0 * np.arange(h) / d))
+    return np.concatenate([z.real, z.imag], axis=-1)
+
+
+def run_decode(cfg, *, n_requests=None, pos_offset=0, repeat=1, with_oracle=True, steps=1,
+               key_layout="position_free"):
     wl = Workload(cfg, n_requests=n_requests)
     segs = wl.segments(pos_offset=pos_offset, k=cfg.k)
     cached = wl.cached()
@@ -68,7 +77,7 @@ def run_decode(cfg, *, n_requests=None, pos_offset=0, repeat=1, with_oracle=True
     n_tokens = max(oplan.total_tokens(s) for s in segs)
     decode_pages = len(segs) * (-(-steps // B) + 1)
     store = gpu_store(cfg, cached, num_pages=stored + private + decode_pages + 8,
-                      max_position=pos_offset + n_tokens + steps + 1)
+                      max_position=pos_offset + n_tokens + steps + 1, key_layout=key_layout)
     plan = store.link_plan(wl.link_requests(), k=cfg.k, block_level=cfg.block_level, pos_offset=pos_offset,
                            decode=steps)
     n = len(segs)
@@ -97,7 +106,27 @@ def run_decode(cfg, *, n_requests=None, pos_offset=0, repeat=1, with_oracle=True
             ext_rows = [tuple(np.concatenate([r[c]] + [tokens[j][c][a:a + 1] for j in range(i + 1)])
                               for c in range(3)) for a, r in enumerate(rows)]
             sample = {a: np.array([len(oplan.selected_positions(s)) - 1]) for a, s in enumerate(ext)}
-            results[i][2] = oracle_outputs(ext, cached, ext_rows, cfg.rope_theta, sample=sample)
+            results[i][2] = oracle_outputs(ext, cached, ext_rows, cfg.rope_theta, sample=sample,
+                                           key_layout=key_layout)
+    # every step wrote its token's key into the token's decode slot of the pool, in the store's
+    # key form: pre-RoPE, or rotated at the token's position inside its segment
+    ex = plan.export()
+    kp = store.k_pool.float().cpu().numpy()
+    B = cfg.page_size
+    for a, sg in enumerate(segs):
+        end = sg[-1].start + sg[-1].length
+        seg0 = sg[-1].start if sg[-1].kind == "suffix" else end
+        pm = ex["pos_map"][ex["cu_pages"][a] * B:ex["cu_pages"][a + 1] * B]
+        for i in range(steps):
+            slot = int(np.nonzero(pm == end + i)[0][0])
+            phys = int(ex["block_table"][ex["cu_pages"][a] + slot // B])
+            got = kp[phys, :, slot % B]
+            want = tokens[i][1][a].astype(np.float64)
+            if key_layout == "segment_rope":
+                want = rotate_at(want, end + i - seg0, cfg.rope_theta)
+                assert np.all(np.abs(got - want) <= 2.0 ** -8 * np.abs(want) + 1e-6), f"decode slot {a}/{i}"
+            else:
+                assert np.array_equal(got, want), f"decode slot {a}/{i}"
     with pytest.raises(pic.PicError) as e:   # every reserved step is used
         pic.link_decode(store, plan, *(dev(t) for t in tokens[-1]))
     assert e.value.status == -7
