@@ -19,6 +19,7 @@ the fp64 CPU oracle timed on a bounded sample of rows.
 from __future__ import annotations
 
 import argparse
+import gc
 import hashlib
 import json
 import os
@@ -77,7 +78,7 @@ def algorithmic_counts(cfg, export, sizes, n_tokens_per_request):
 class LinkJob:
     """Store, requests and device tensors of one workload."""
 
-    def __init__(self, cfg, *, dense_pages=0, rope_keys=0, split_pages=0):
+    def __init__(self, cfg, *, dense_pages=0, rope_keys=0, split_pages=0, key_layout="position_free"):
         import torch
 
         import position_independent_kv_legolink_amd as pic
@@ -99,7 +100,8 @@ class LinkJob:
         self.store = pic.Store(num_q_heads=cfg.num_q_heads, num_kv_heads=cfg.num_kv_heads, head_dim=cfg.head_dim,
                                page_size=B, num_pages=pages + private + max(dense_pages, decode_pages) + 64,
                                dtype=cfg.dtype, rope_theta=cfg.rope_theta,
-                               max_position=self.n_tokens + DECODE_SLOTS + 1)
+                               max_position=self.n_tokens + DECODE_SLOTS + 1, key_layout=key_layout)
+        self.key_layout = key_layout
         self.tdt = torch.bfloat16 if cfg.dtype == "bf16" else torch.float32
         t = time.time()
         for c in chunk_ids:
@@ -141,6 +143,20 @@ class LinkJob:
         plan.free()
 
 
+class NoGC:
+    """Python's cyclic collector is off inside timed regions: one full collection over the
+    objects a workload's setup leaves (about 170,000 for the 64-request workload) stalls the host
+    for 40-65 ms, which a 10-step interval would count as 4-6 ms per step."""
+
+    def __enter__(self):
+        self.was = gc.isenabled()
+        gc.disable()
+
+    def __exit__(self, *exc):
+        if self.was:
+            gc.enable()
+
+
 def time_steps(job, steps, warmup):
     torch = job.torch
     for _ in range(warmup):
@@ -148,11 +164,12 @@ def time_steps(job, steps, warmup):
     torch.cuda.synchronize()
     job.store.profile_enable(True)
     torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for _ in range(steps):
-        job.step()
-    torch.cuda.synchronize()
-    t1 = time.perf_counter()
+    with NoGC():
+        t0 = time.perf_counter()
+        for _ in range(steps):
+            job.step()
+        torch.cuda.synchronize()
+        t1 = time.perf_counter()
     prof = job.store.profile_read()
     job.store.profile_enable(False)
     return (t1 - t0) * 1e3 / steps, prof
@@ -169,10 +186,11 @@ def time_steps_cold(job, steps, evict_mib=512):
     for i in range(steps):
         scratch.fill_(i & 0xff)
         torch.cuda.synchronize()
-        t0 = time.perf_counter()
-        job.step()
-        torch.cuda.synchronize()
-        total += time.perf_counter() - t0
+        with NoGC():
+            t0 = time.perf_counter()
+            job.step()
+            torch.cuda.synchronize()
+            total += time.perf_counter() - t0
     prof = job.store.profile_read()
     job.store.profile_enable(False)
     del scratch
@@ -202,11 +220,12 @@ def decode_measure(job, steps=DECODE_STEPS, warmup=DECODE_WARMUP):
         job.pic.link_decode(job.store, plan, q, k, v, out=out)
     torch.cuda.synchronize()
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    e0.record()
-    for _ in range(steps):
-        job.pic.link_decode(job.store, plan, q, k, v, out=out)
-    e1.record()
-    e1.synchronize()
+    with NoGC():
+        e0.record()
+        for _ in range(steps):
+            job.pic.link_decode(job.store, plan, q, k, v, out=out)
+        e1.record()
+        e1.synchronize()
     ms = e0.elapsed_time(e1) / steps
     elem = 2 if cfg.dtype == "bf16" else 4
     page_bytes = cfg.num_kv_heads * cfg.page_size * cfg.head_dim * elem
@@ -267,11 +286,12 @@ def dense_comparator(job, reps=3):
     job.pic.link_attend(job.store, plan, q, k_all, v_all, out=out)
     torch.cuda.synchronize()
     job.store.profile_enable(True)
-    t0 = time.perf_counter()
-    for _ in range(reps):
-        job.pic.link_attend(job.store, plan, q, k_all, v_all, out=out)
-    torch.cuda.synchronize()
-    wall = (time.perf_counter() - t0) * 1e3 / reps
+    with NoGC():
+        t0 = time.perf_counter()
+        for _ in range(reps):
+            job.pic.link_attend(job.store, plan, q, k_all, v_all, out=out)
+        torch.cuda.synchronize()
+        wall = (time.perf_counter() - t0) * 1e3 / reps
     prof = job.store.profile_read()
     job.store.profile_enable(False)
     flop, attn_bytes, _ = algorithmic_counts(cfg, ex, sizes, job.n_tokens)
@@ -285,7 +305,7 @@ def dense_comparator(job, reps=3):
                 attention_tflops=round(flop / attn_ms / 1e9, 2), max_abs_diff_at_link_rows=diff)
 
 
-def cpu_baseline(cfg, target_s):
+def cpu_baseline(cfg, target_s, key_layout="position_free"):
     """The fp64 oracle on a bounded, evenly spread sample of the same workload's rows."""
     from oracle import link as olink
     from oracle import plan as oplan
@@ -309,13 +329,13 @@ def cpu_baseline(cfg, target_s):
     for n_probe in (4, 12):
         probe = np.linspace(0, R - 1, n_probe).astype(np.int64)
         t = time.perf_counter()
-        olink.link_attention(segs, cached, q, k, v, cfg.rope_theta, rows=probe)
+        olink.link_attention(segs, cached, q, k, v, cfg.rope_theta, rows=probe, key_layout=key_layout)
         times.append(time.perf_counter() - t)
     per_row = max((times[1] - times[0]) / 8, 1e-6)
     n = int(max(4, min(R, (target_s - times[0]) / per_row)))
     rows = np.unique(np.linspace(0, R - 1, n).astype(np.int64))
     t = time.perf_counter()
-    olink.link_attention(segs, cached, q, k, v, cfg.rope_theta, rows=rows)
+    olink.link_attention(segs, cached, q, k, v, cfg.rope_theta, rows=rows, key_layout=key_layout)
     dt = time.perf_counter() - t
     first = segs[0].start
     flop = int(4 * cfg.head_dim * cfg.num_q_heads * (pos[rows] - first + 1).sum())
@@ -324,7 +344,7 @@ def cpu_baseline(cfg, target_s):
                        f"{cfg.num_q_heads} heads, fp64 with explicit loops; {dt:.1f} s")
 
 
-def traffic_from_profiles(workload):
+def traffic_from_profiles(workload, key_layout="position_free"):
     """HBM bytes per attention launch from the committed counter summary, if it is current."""
     if not os.path.exists(TRAFFIC_FILE):
         return None
@@ -332,7 +352,8 @@ def traffic_from_profiles(workload):
         t = json.load(open(TRAFFIC_FILE))
     except Exception:
         return None
-    if t.get("kernel_source_sha256_16") != kernel_hash() or t.get("workload") != workload:
+    if (t.get("kernel_source_sha256_16") != kernel_hash() or t.get("workload") != workload
+            or t.get("key_layout", "position_free") != key_layout):
         return None
     return t.get("hbm_bytes_per_launch")
 
@@ -351,11 +372,12 @@ def _counter_rows(directory, counter):
     return out
 
 
-def summarize_traffic(fetch_dir, write_dir, copy_mib, workload, out_json):
+def summarize_traffic(fetch_dir, write_dir, copy_mib, workload, out_json, key_layout="position_free"):
     """Turn two rocprofv3 --pmc runs (FETCH_SIZE, WRITE_SIZE, KiB per dispatch) into HBM bytes per
     attention launch, each scaled by what the same counter reads for the calibration copy."""
     copy_bytes = copy_mib * (1 << 20)
-    res = {"workload": workload, "kernel_source_sha256_16": kernel_hash(), "copy_bytes": copy_bytes}
+    res = {"workload": workload, "key_layout": key_layout, "kernel_source_sha256_16": kernel_hash(),
+           "copy_bytes": copy_bytes}
     for name, d in (("fetch", fetch_dir), ("write", write_dir)):
         counter = "FETCH_SIZE" if name == "fetch" else "WRITE_SIZE"
         rows = _counter_rows(d, counter)
@@ -390,6 +412,9 @@ def main():
     ap.add_argument("--no-decode", action="store_true", help="skip the decode-after-link measurement")
     ap.add_argument("--rope-keys", type=int, default=0, choices=(0, 1, 2),
                     help="key rotation: 0 automatic, 1 inside attention, 2 once ahead of attention")
+    ap.add_argument("--key-layout", default="position_free", choices=("position_free", "segment_rope"),
+                    help="stored key form: pre-RoPE, or rotated at the position inside the segment "
+                         "(a chunk compiled from position 0)")
     ap.add_argument("--split-pages", type=int, default=0,
                     help="KV pages per attention work item: 0 automatic, > 0 at most that many, "
                          "< 0 only where the kernel's limit requires")
@@ -401,7 +426,7 @@ def main():
     args = ap.parse_args()
     if args.traffic_from:
         summarize_traffic(args.traffic_from[0], args.traffic_from[1], args.copy_probe_mib or 256, args.workload,
-                          args.traffic_out)
+                          args.traffic_out, args.key_layout)
         return
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -423,7 +448,11 @@ def main():
     cfg = CONFIGS[args.workload]
     dense_pages = 0 if args.no_dense else (-(-(cfg.prefix_len + cfg.chunks_per_request * cfg.chunk_len +
                                                  cfg.suffix_len) // cfg.page_size)) * cfg.n_requests
-    job = LinkJob(cfg, dense_pages=dense_pages, rope_keys=args.rope_keys, split_pages=args.split_pages)
+    job = LinkJob(cfg, dense_pages=dense_pages, rope_keys=args.rope_keys, split_pages=args.split_pages,
+                  key_layout=args.key_layout)
+    # the setup's objects are never garbage: keep the collector from scanning them again
+    gc.collect()
+    gc.freeze()
     flop, attn_bytes, total_bytes = algorithmic_counts(cfg, job.export, job.sizes, job.n_tokens)
     # page sharing: logical pages the requests read vs the distinct physical pages behind them
     elem = 2 if cfg.dtype == "bf16" else 4
@@ -459,15 +488,17 @@ def main():
     link_ms = scatter_ms + rotate_ms + attn_ms + merge_ms
     log(f"step {ms_step:.3f} ms; scatter {scatter_ms:.4f} key rotation {rotate_ms:.4f} attention {attn_ms:.4f} "
         f"merge {merge_ms:.4f} ms")
-    # key rotation pass: every rotated page's keys read and written, its cos/sin rows read once
+    # key rotation pass: every rotated page's keys read and written, its cos/sin rows read once (one
+    # row per slot for position-free keys, one per page for keys rotated inside their segment)
     rot_pages = job.sizes["rotated_pages"]
+    cs_rows = cfg.page_size if args.key_layout == "position_free" else 1
     rot_bytes = rot_pages * (2 * cfg.num_kv_heads * cfg.page_size * cfg.head_dim * elem
-                             + cfg.page_size * cfg.head_dim * 4)
+                             + cs_rows * cfg.head_dim * 4)
 
     peak = PEAK_BF16_TFLOPS if cfg.dtype == "bf16" else PEAK_F32_TFLOPS
     achieved = flop / (attn_ms * 1e-3) / 1e12
     roofline = dict(bound="mfma", achieved=round(achieved, 2), peak=peak, unit="TFLOP/s",
-                    frac=round(achieved / peak, 4), traffic=traffic_from_profiles(cfg.name))
+                    frac=round(achieved / peak, 4), traffic=traffic_from_profiles(cfg.name, args.key_layout))
 
     cold = None
     if args.cold_steps > 0:
@@ -493,7 +524,7 @@ def main():
 
     cpu = None
     if not args.no_cpu_baseline:
-        cpu = cpu_baseline(cfg, args.cpu_seconds)
+        cpu = cpu_baseline(cfg, args.cpu_seconds, args.key_layout)
         log(f"cpu oracle: {cpu}")
 
     result = {
@@ -512,7 +543,7 @@ def main():
         "config": {"workload": cfg.name, "tokens_per_request": job.n_tokens, "requests": cfg.n_requests,
                    "selected_rows": job.sizes["rows"], "q_heads": cfg.num_q_heads, "kv_heads": cfg.num_kv_heads,
                    "head_dim": cfg.head_dim, "page_size": cfg.page_size, "k": cfg.k,
-                   "block_level": cfg.block_level, "parallelism": "single GPU"},
+                   "block_level": cfg.block_level, "key_layout": args.key_layout, "parallelism": "single GPU"},
         "link_latency_ms": round(link_ms, 4),
         "attention_ms": round(attn_ms, 4),
         "scatter_ms": round(scatter_ms, 4),
