@@ -1136,35 +1136,57 @@ __global__ __launch_bounds__(kThreads) void link_scatter(const ScatterDesc *tabl
 // page ([page][Hkv][page_size][d]); padding slots are written as zeros (the pools hold zeros
 // there, which rotate to zeros). A position-free key is rotated by its position; a key stored
 // rotated at its position inside its segment (seg_keys) by the segment's start. One work group
-// per logical page; a thread takes 8 (x_i, x_{i+d/2}) pairs of one (head, slot) per pass,
-// consecutive threads consecutive pairs of a row.
+// per logical page. A thread takes 8 (x_i, x_{i+d/2}) pairs of one slot, loads their cos/sin
+// once, and rotates them in every head of its head group (heads hg, hg + n_hg, ...), loading
+// up to HB heads' keys before the first store; consecutive threads take consecutive pairs of a
+// row, so every key row is read and written in whole 128-byte runs.
 template <int D>
-__global__ __launch_bounds__(kThreads) void rotate_keys_bf16(const PageDesc *pages, const uint8_t *k_pool,
-                                                             const float *rope, uint8_t *k_rot, int hkv, int pshift,
-                                                             int64_t page_bytes, int seg_keys) {
+__global__ __launch_bounds__(kThreads) void rotate_keys_bf16(const PageDesc *pages, const uint8_t *__restrict__ k_pool,
+                                                             const float *__restrict__ rope, uint8_t *__restrict__ k_rot,
+                                                             int hkv, int pshift, int64_t page_bytes, int seg_keys) {
+    constexpr int PPR = D / 16;   // pieces of 8 pairs per row
+    constexpr int HB = 4;         // heads loaded ahead of their stores
     const PageDesc pd = pages[blockIdx.x];
     const int page_size = 1 << pshift;
-    constexpr int PPR = D / 16;   // pieces per row
+    const int items = page_size * PPR;                           // (slot, piece) of one head
+    const int n_hg = max(1, min(hkv, kThreads / items));         // head groups side by side
     const uint8_t *src = k_pool + (int64_t)pd.phys * page_bytes;
     uint8_t *dst = k_rot + (int64_t)blockIdx.x * page_bytes;
-    for (int i = threadIdx.x; i < hkv * page_size * PPR; i += kThreads) {
-        const int c = i % PPR, row = i / PPR;   // row = head * page_size + slot
-        const int slot = row & (page_size - 1);
-        const int64_t off = (int64_t)row * D * 2 + c * 16;
-        u32x4 olo = {0, 0, 0, 0}, ohi = {0, 0, 0, 0};
-        if (slot < pd.valid) {
-            const u32x4 lo = *reinterpret_cast<const u32x4 *>(src + off);
-            const u32x4 hi = *reinterpret_cast<const u32x4 *>(src + off + D);
+    for (int i = threadIdx.x; i < items * n_hg; i += kThreads) {
+        const int c = i % PPR, slot = (i / PPR) & (page_size - 1), hg = i / items;
+        const bool valid = slot < pd.valid;
+        floatx4 co[2] = {}, sn[2] = {};
+        if (valid) {
             const float *cs = rope + (int64_t)(seg_keys ? pd.seg0 : pd.pos0 + slot) * D + 8 * c;
-            floatx4 co[2], sn[2];
             co[0] = *reinterpret_cast<const floatx4 *>(cs);
             co[1] = *reinterpret_cast<const floatx4 *>(cs + 4);
             sn[0] = *reinterpret_cast<const floatx4 *>(cs + D / 2);
             sn[1] = *reinterpret_cast<const floatx4 *>(cs + D / 2 + 4);
-            rope8_bf16(lo, hi, co, sn, olo, ohi);
         }
-        *reinterpret_cast<u32x4 *>(dst + off) = olo;
-        *reinterpret_cast<u32x4 *>(dst + off + D) = ohi;
+        for (int h0 = hg; h0 < hkv; h0 += HB * n_hg) {
+            u32x4 lo[HB], hi[HB];
+#pragma unroll
+            for (int j = 0; j < HB; ++j) {
+                const int h = h0 + j * n_hg;
+                lo[j] = u32x4{0, 0, 0, 0};
+                hi[j] = u32x4{0, 0, 0, 0};
+                if (valid && h < hkv) {
+                    const int64_t off = ((int64_t)h * page_size + slot) * D * 2 + c * 16;
+                    lo[j] = *reinterpret_cast<const u32x4 *>(src + off);
+                    hi[j] = *reinterpret_cast<const u32x4 *>(src + off + D);
+                }
+            }
+#pragma unroll
+            for (int j = 0; j < HB; ++j) {
+                const int h = h0 + j * n_hg;
+                if (h >= hkv) break;
+                u32x4 olo = {0, 0, 0, 0}, ohi = {0, 0, 0, 0};
+                if (valid) rope8_bf16(lo[j], hi[j], co, sn, olo, ohi);
+                const int64_t off = ((int64_t)h * page_size + slot) * D * 2 + c * 16;
+                *reinterpret_cast<u32x4 *>(dst + off) = olo;
+                *reinterpret_cast<u32x4 *>(dst + off + D) = ohi;
+            }
+        }
     }
 }
 
