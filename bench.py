@@ -175,6 +175,19 @@ def time_steps(job, steps, warmup):
     return (t1 - t0) * 1e3 / steps, prof
 
 
+def time_steps_no_events(job, steps):
+    """The same steps without the per-kernel events: each event pair costs the GPU about 5 us,
+    which matters for the short workloads."""
+    torch = job.torch
+    torch.cuda.synchronize()
+    with NoGC():
+        t0 = time.perf_counter()
+        for _ in range(steps):
+            job.step()
+        torch.cuda.synchronize()
+        return (time.perf_counter() - t0) * 1e3 / steps
+
+
 def time_steps_cold(job, steps, evict_mib=512):
     """Each step after a write of evict_mib MiB of scratch (the 256 MiB MALL holds none of the
     link step's data afterwards), timed on its own between synchronisations; the eviction is
@@ -475,6 +488,7 @@ def main():
         copy_dst = torch.empty_like(copy_src)
 
     ms_step, prof = time_steps(job, args.steps, args.warmup)
+    ms_step_bare = time_steps_no_events(job, args.steps)
     if copy_src is not None:
         # a plain elementwise kernel that reads and writes copy_probe_mib MiB each
         for _ in range(args.steps):
@@ -535,6 +549,7 @@ def main():
         "steps": args.steps,
         "warmup": args.warmup,
         "ms_per_step": round(ms_step, 4),
+        "ms_per_step_without_kernel_events": round(ms_step_bare, 4),
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
