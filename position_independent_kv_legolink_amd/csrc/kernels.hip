@@ -553,9 +553,12 @@ __global__ __launch_bounds__(512, 1) void link_attention_bf16(AttnParams p) {
         const int gi = lane >> 4, jj = (lane >> 2) & 3, qq = lane & 3;
         const uint16_t *vb = vs + vsl * VBUF + (4 * lg + jj) * VS + 16 * (gi & 1) + 4 * qq;
         const uint16_t *kb = ks + ksl * KBUF + ln * KS + 8 * lg;
+        // PV MFMA i takes d block i % NDB and k-step i / NDB (32-key block b, half s2), so that
+        // consecutive MFMAs accumulate into different output blocks; each block still takes its
+        // k-steps in the same order
         auto read = [&](int i) __attribute__((always_inline)) {
             if (i < NPV) {
-                const int db = i >> 2, b = (i >> 1) & 1, s2 = i & 1;
+                const int db = i % NDB, b = (i / NDB) >> 1, s2 = (i / NDB) & 1;
                 const uint16_t *a = vb + (b * 32 + 16 * s2) * VS + db * 32;
                 vlo[i] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) v4s *)a);
                 vhi[i] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
@@ -567,7 +570,7 @@ __global__ __launch_bounds__(512, 1) void link_attention_bf16(AttnParams p) {
         };
         auto mma = [&](int i) __attribute__((always_inline)) {
             if (i < NPV) {
-                const int db = i >> 2, b = (i >> 1) & 1, s2 = i & 1;
+                const int db = i % NDB, b = (i / NDB) >> 1, s2 = (i / NDB) & 1;
                 const bf16x8 a = __builtin_bit_cast(bf16x8, __builtin_shufflevector(vlo[i], vhi[i], 0, 1, 2, 3, 4, 5, 6, 7));
                 oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, __builtin_bit_cast(bf16x8, pf[b][s2]), oacc[db],
                                                                    0, 0, 0);
