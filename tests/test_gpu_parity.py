@@ -241,10 +241,13 @@ def test_empty_plan_is_a_noop():
     assert out.shape[0] == 0
 
 
-def test_scatter_writes_private_pages_exactly():
-    """Private pages hold new rows, copied cached rows and zero padding, byte for byte."""
+@pytest.mark.parametrize("rope_keys", [1, 2])
+def test_scatter_writes_private_pages_exactly(rope_keys):
+    """Private pages hold new rows, copied cached rows and zero padding, byte for byte, with the
+    keys rotated inside attention or ahead of it."""
     cfg = small_cfg(k=3, chunk_len=45)
-    got, want, ex = run_workload(cfg)
+    got, want, ex = run_workload(cfg, rope_keys=rope_keys)
+    check(cfg, got, want, ex, f"scatter rope_keys {rope_keys}")
     store, segs, rows, cached = ex["store"], ex["segs"], ex["rows"], ex["cached"]
     exp_ = ex["export"]
     B = cfg.page_size

@@ -91,13 +91,14 @@ def test_split_and_offset(split, offset):
     check(cfg, got, want, ex, f"segment keys split {split} offset {offset}")
 
 
-@pytest.mark.parametrize("dtype", ["bf16", "f32"])
-def test_scatter_writes_new_keys_rotated_inside_their_segment(dtype):
+@pytest.mark.parametrize("dtype,rope_keys", [("bf16", 1), ("bf16", 2), ("f32", 1)])
+def test_scatter_writes_new_keys_rotated_inside_their_segment(dtype, rope_keys):
     """Private pages hold the new rows' keys rotated at their position inside their segment
     (within one bf16 rounding of the exact rotation; fp32 within 1e-6 relative + 4e-6), cached rows copied as
     stored, values as given, and zero padding."""
     cfg = small_cfg(k=3, chunk_len=45, **({"dtype": "f32", "kv_scale": 1.0} if dtype == "f32" else {}))
-    got, want, ex = run_workload(cfg, key_layout=SEG, pos_offset=333)
+    got, want, ex = run_workload(cfg, key_layout=SEG, pos_offset=333, rope_keys=rope_keys)
+    check(cfg, got, want, ex, f"segment keys scatter {dtype} rope_keys {rope_keys}")
     store, segs, rows, cached = ex["store"], ex["segs"], ex["rows"], ex["cached"]
     exp_ = ex["export"]
     B = cfg.page_size
