@@ -314,8 +314,14 @@ def dense_comparator(job, reps=3):
     diff = float((out[idx].float() - job.out.float()).abs().max())
     del q, k_all, v_all, ws, out
     attn_ms = prof["attention_ms"] / max(prof["calls"], 1)
-    return dict(rows=R, gflop=round(flop / 1e9, 1), ms=round(wall, 4), attention_ms=round(attn_ms, 4),
-                attention_tflops=round(flop / attn_ms / 1e9, 2), max_abs_diff_at_link_rows=diff)
+    res = dict(rows=R, gflop=round(flop / 1e9, 1), ms=round(wall, 4), attention_ms=round(attn_ms, 4),
+               attention_tflops=round(flop / attn_ms / 1e9, 2), max_abs_diff_at_link_rows=diff)
+    if job.key_layout != "position_free":
+        # every token enters as a new, position-free row here, while the cached keys of this
+        # store are compiled from position 0: the timing holds, the comparison does not
+        res["max_abs_diff_at_link_rows"] = None
+        res["note"] = "cached keys re-entered as new rows without undoing their rotation: no output comparison"
+    return res
 
 
 def cpu_baseline(cfg, target_s, key_layout="position_free"):
