@@ -179,11 +179,13 @@ def test_decode_steps_cross_pages(suffix_len, steps):
     check(cfg, run_decode(cfg, steps=steps), f"decode suffix {suffix_len}")
 
 
-def test_decode_positions_at_the_limit():
+@pytest.mark.parametrize("key_layout", ["position_free", "segment_rope"])
+def test_decode_positions_at_the_limit(key_layout):
     """Decode tokens at the last positions below 2^22, the largest max_position a store takes."""
     cfg = small_cfg(chunk_len=64, n_requests=1)
     steps = 3
     n_tokens = oplan.total_tokens(Workload(cfg, n_requests=1).segments()[0])
     offset = (1 << 22) - n_tokens - steps - 1
-    _say(f"decode, positions up to {offset + n_tokens + steps - 1}")
-    check(cfg, run_decode(cfg, pos_offset=offset, steps=steps), "decode positions at 2^22")
+    _say(f"decode, positions up to {offset + n_tokens + steps - 1}, {key_layout} keys")
+    check(cfg, run_decode(cfg, pos_offset=offset, steps=steps, key_layout=key_layout),
+          f"decode positions at 2^22, {key_layout} keys")

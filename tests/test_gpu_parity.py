@@ -391,24 +391,28 @@ def test_back_to_back_uploads_share_one_workspace():
 
 
 # ------------------------------------------------------------------ the kernels' size limits
+@pytest.mark.parametrize("key_layout", ["position_free", "segment_rope"])
 @pytest.mark.parametrize("rope_keys", [1, 2])
-def test_item_at_the_page_table_limit(rope_keys):
+def test_item_at_the_page_table_limit(rope_keys, key_layout):
     """64 chunks of 512 tokens, LegoLink-32, no prefix: the row tile of chunks 62 and 63 reads
     exactly 2,048 pages, the most one work item's LDS page table holds; the suffix tile reads
     2,049 and is split in two (for each KV head)."""
     cfg = small_cfg(chunk_len=512, chunks_per_request=64, pool_size=64, k=32, prefix_len=0, suffix_len=16,
                     n_requests=1)
-    _say(f"2,048-page work item, rope_keys {rope_keys}")
-    got, want, ex = run_workload(cfg, split_pages=-1, sample_rows=24, rope_keys=rope_keys, check_plan=False)
+    _say(f"2,048-page work item, rope_keys {rope_keys}, {key_layout} keys")
+    got, want, ex = run_workload(cfg, split_pages=-1, sample_rows=24, rope_keys=rope_keys, check_plan=False,
+                                 key_layout=key_layout)
     assert ex["plan"].sizes["split_items"] == 2 * cfg.num_kv_heads   # the suffix tile of each KV head
     rows = np.concatenate([ex["sample"][0], [2047, 2048, 2063]])   # rows of the last chunk pair and the suffix
     ex["sample"] = {0: np.unique(rows)}
-    want = oracle_outputs(ex["segs"], ex["cached"], ex["rows"], cfg.rope_theta, sample=ex["sample"])
-    check(cfg, got, want, ex, f"2,048-page item, rope_keys {rope_keys}")
+    want = oracle_outputs(ex["segs"], ex["cached"], ex["rows"], cfg.rope_theta, sample=ex["sample"],
+                          key_layout=key_layout)
+    check(cfg, got, want, ex, f"2,048-page item, rope_keys {rope_keys}, {key_layout} keys")
 
 
+@pytest.mark.parametrize("key_layout", ["position_free", "segment_rope"])
 @pytest.mark.parametrize("rope_keys", [1, 2])
-def test_positions_at_the_limit(rope_keys):
+def test_positions_at_the_limit(rope_keys, key_layout):
     """The request's last positions end just below 2^22, the largest max_position a store takes
     (positions are packed with a page's valid count, and cos/sin rows addressed with 32-bit
     offsets, up to there)."""
@@ -416,6 +420,6 @@ def test_positions_at_the_limit(rope_keys):
     wl = Workload(cfg, n_requests=1)
     n_tokens = oplan.total_tokens(wl.segments()[0])
     offset = (1 << 22) - n_tokens - 1
-    _say(f"positions up to {offset + n_tokens - 1}, rope_keys {rope_keys}")
-    got, want, ex = run_workload(cfg, pos_offset=offset, rope_keys=rope_keys)
-    check(cfg, got, want, ex, f"positions at 2^22, rope_keys {rope_keys}")
+    _say(f"positions up to {offset + n_tokens - 1}, rope_keys {rope_keys}, {key_layout} keys")
+    got, want, ex = run_workload(cfg, pos_offset=offset, rope_keys=rope_keys, key_layout=key_layout)
+    check(cfg, got, want, ex, f"positions at 2^22, rope_keys {rope_keys}, {key_layout} keys")
