@@ -151,3 +151,13 @@ def test_decode_long50k():
     cfg = CONFIGS["long50k_k32"]
     _say("decode, long50k_k32, segment-rotated keys")
     check_decode(cfg, run_decode(cfg, steps=2, key_layout=SEG), "decode long50k segment keys")
+
+
+@pytest.mark.parametrize("rope_keys", [1, 2])
+def test_dense_recompute_all(rope_keys):
+    """Every row recomputed: every page is private and every key arrives position-free, so the
+    scatter writes all of them into the store's form before attention rotates them back out."""
+    cfg = small_cfg(chunk_len=100, chunks_per_request=3, n_requests=1)
+    got, want, ex = run_workload(cfg, recompute_all=True, rope_keys=rope_keys, key_layout=SEG)
+    assert ex["plan"].sizes["cow_pages"] == 0
+    check(cfg, got, want, ex, f"segment keys recompute_all rope_keys {rope_keys}")
