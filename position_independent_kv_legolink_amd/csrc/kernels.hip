@@ -117,7 +117,9 @@ __device__ __forceinline__ void rope8_bf16(const u32x4 &lo, const u32x4 &hi, con
 // phase on every SIMD:
 //   Y(t): LDS staging of tile t+2 (with the RoPE rotation of its keys unless KR), then the
 //         softmax of tile t with the global loads of tile t+3 spread between its
-//         exponentials                                                              (VALU)
+//         exponentials; with pre-rotated keys (KR) each staged piece is written to LDS just
+//         before the load that reuses its registers, so the staging writes are spread over
+//         the exponentials too instead of meeting the other wave's operand reads at once (VALU)
 //   X(t): PV of tile t, QK^T of tile t+1 (MFMAs and their LDS operand reads only)   (MFMA)
 // with a work-group barrier after each phase; group B passes one extra barrier at the start
 // (and group A one at the end), so B's phase k overlaps A's phase k+1. Tile buffers are deep
@@ -385,6 +387,37 @@ __global__ __launch_bounds__(512, 1) void link_attention_bf16(AttnParams p) {
         const unsigned bit = 1u << sl;
         mask_ring = __any(kp_stage > wave_rpos0) ? (mask_ring | bit) : (mask_ring & ~bit);
     };
+    auto write_piece = [&](int j, int sl, int vsl) __attribute__((always_inline)) {
+        if (j == 0) {
+            kpos_s[sl * KT + lane] = kp_stage;
+            const unsigned bit = 1u << sl;
+            mask_ring = __any(kp_stage > wave_rpos0) ? (mask_ring | bit) : (mask_ring & ~bit);
+            uint16_t *kb = ks + sl * KBUF;
+#pragma unroll
+            for (int u = 0; u < NKP; ++u) {
+                const int pi = tid + NT * u;
+                if (KPAIRS % NT != 0 && pi >= KPAIRS) break;
+                const int key = pi / (D / 16), c = pi % (D / 16);
+                *reinterpret_cast<u32x4 *>(&kb[key * KS + 8 * c]) = k_lo[u];
+            }
+        } else if (j == 1) {
+            uint16_t *kb = ks + sl * KBUF;
+#pragma unroll
+            for (int u = 0; u < NKP; ++u) {
+                const int pi = tid + NT * u;
+                if (KPAIRS % NT != 0 && pi >= KPAIRS) break;
+                const int key = pi / (D / 16), c = pi % (D / 16);
+                *reinterpret_cast<u32x4 *>(&kb[key * KS + D / 2 + 8 * c]) = k_hi[u];
+            }
+        } else {
+            const int u = j - 2;
+            const int pi = tid + NT * u;
+            if (VCHUNKS % NT == 0 || pi < VCHUNKS) {
+                const int key = pi / (D / 8), c16 = pi % (D / 8);
+                *reinterpret_cast<u32x4 *>(&(vs + vsl * VBUF)[key * VS + 8 * c16]) = v_r[u];
+            }
+        }
+    };
     auto store_tile = [&](int sl, int vsl) __attribute__((always_inline)) {
         if constexpr (KR) {
 #pragma unroll
@@ -626,14 +659,26 @@ __global__ __launch_bounds__(512, 1) void link_attention_bf16(AttnParams p) {
     // ring slots of tiles t, t+1, t+2: K' and key positions in a ring of 3, V in a ring of 4 (the
     // one-phase skew between the wave groups keeps a V tile in use one phase longer)
     int kc = 0, kn = 1, ks2 = 2, vc = 0;
-    // one tile. Y(t): LDS staging of tile t+2 from the registers loaded one step earlier,
-    // the loads of tile t+3 into the freed registers (a whole step ahead of their use), then the
+    // one tile. Y(t): LDS staging of tile t+2 from the registers loaded one step earlier and
+    // the loads of tile t+3 into the freed registers (a whole step ahead of their use), with the
     // softmax of tile t. X(t): PV of tile t, QK^T of tile t+1, and the page descriptors of the
     // next step's loads.
     auto step = [&](int t, auto next_qk, auto staging, auto next_staging) __attribute__((always_inline)) {
         constexpr bool STAGE = decltype(staging)::value;
-        if constexpr (STAGE) store_tile(ks2, (vc + 2) & 3);
-        softmax((mask_ring >> kc) & 1u, kc, Loads<STAGE ? NLOAD : 0, decltype(load_piece) &>{load_piece});
+        if constexpr (KR) {
+            // each staged piece goes to LDS just before the load that reuses its registers, so the
+            // tile's LDS writes are spread over the exponentials
+            const int wsl = ks2, wvsl = (vc + 2) & 3;
+            const bool masked = (mask_ring >> kc) & 1u;   // read before piece 0 updates the ring
+            auto stage_load = [&](int j) __attribute__((always_inline)) {
+                write_piece(j, wsl, wvsl);
+                load_piece(j);
+            };
+            softmax(masked, kc, Loads<STAGE ? NLOAD : 0, decltype(stage_load) &>{stage_load});
+        } else {
+            if constexpr (STAGE) store_tile(ks2, (vc + 2) & 3);
+            softmax((mask_ring >> kc) & 1u, kc, Loads<STAGE ? NLOAD : 0, decltype(load_piece) &>{load_piece});
+        }
         __builtin_amdgcn_sched_barrier(0);
         lds_barrier();
         xphase(vc, kn, next_qk);
