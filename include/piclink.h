@@ -123,7 +123,7 @@ typedef struct {
  *              item reads; 2 = once per link call, every logical page's keys into
  *              the workspace, before attention (bfloat16 stores only; the results
  *              are bit-identical to 1); 0 = automatic: 2 for bfloat16 stores when
- *              the work list reads each key page at least 8 times on average,
+ *              the work list reads each key page at least 5 times on average,
  *              else 1. Other values: PIC_ERR_INVALID.
  * decode       T > 0: also prepare T steps of pic_link_decode (bfloat16 stores; keys are
  *              then always rotated ahead, so rope_keys must be 0 or 2). Every request gets T

@@ -91,8 +91,9 @@ constexpr int kMaxItemPages = 2048;  // longest KV range of one attention work i
 constexpr int kMaxPosition = 1 << 22;
 constexpr int kThreads = 256;      // page writers, merge and the fp32 attention kernel
 // Automatic key rotation mode: rotate once per link call when the work list reads each key page
-// at least this many times on average (else inside attention).
-constexpr int kRotateReuse = 8;
+// at least this many times on average (else inside attention). The rotation pass costs about as
+// much as 5 reads' worth of rotation inside attention.
+constexpr int kRotateReuse = 5;
 
 // (row, head) pairs handled by one attention work group: 8 waves x 32 rows (bf16), 4 x 32 (fp32).
 constexpr int tile_qrows(int dtype) { return dtype == 0 ? 256 : 128; }

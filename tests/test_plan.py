@@ -125,8 +125,9 @@ def test_split_options():
 @pytest.mark.parametrize("name", ["llama3_k2", "batched_k16", "long50k_k32", "block_zipf"])
 def test_automatic_key_rotation_follows_key_reuse(name):
     """rope_keys=0 rotates the keys ahead of attention exactly when the work list reads the key
-    pages at least 8 times each on average: the 50k request's 50 row tiles do, the short and
-    batched requests (at most 8 row tiles each) do not."""
+    pages at least 5 times each on average: the 50k request's 50 row tiles do (25.5 reads per
+    page), and so do the batched requests' 8 row tiles (5.2); the short request and the Zipf
+    batch (3 row tiles per request, 2.0 and 2.2) do not."""
     cfg = CONFIGS[name]
     wl = Workload(cfg)
     B = cfg.page_size
@@ -155,7 +156,7 @@ def test_automatic_key_rotation_follows_key_reuse(name):
             last = rp[min(t0 + tile, len(rp)) - 1]
             reads += int(np.sum(first <= last))
     reads *= cfg.num_kv_heads
-    expect = reads >= 8 * plan.sizes["pages"] * cfg.num_kv_heads
+    expect = reads >= 5 * plan.sizes["pages"] * cfg.num_kv_heads
     assert (plan.sizes["rotated_pages"] > 0) == expect
-    assert expect == (name == "long50k_k32")
+    assert expect == (name in ("long50k_k32", "batched_k16"))
     plan.free()
