@@ -9,12 +9,14 @@ are seeded synthetic data, resident in HBM before timing starts.
 
 Output: one JSON line with the step throughput (algorithmic TFLOP/s), the
 attention kernel's roofline position (timed live with HIP events on the
-stream it runs on), the same step with the 256 MiB MALL evicted before each
-step ("cold"), the dense full-recompute comparator on the same inputs, and
-the fp64 CPU oracle timed on a bounded sample of rows.
+stream it runs on), the link latency (each step alone between
+synchronisations: 10th, 50th and 90th percentile), the same step with the
+256 MiB MALL evicted before each step ("cold"), decode after link, the dense
+full-recompute comparator on the same inputs, and the fp64 CPU oracle timed
+on a bounded sample of rows.
 
     python bench.py [--steps K] [--warmup W] [--workload NAME] [--no-cpu-baseline] [--no-dense]
-                    [--cold-steps N] [--rope-keys 0|1|2] [--split-pages P]
+                    [--cold-steps N] [--rope-keys 0|1|2] [--key-layout L] [--split-pages P]
 """
 from __future__ import annotations
 
@@ -188,14 +190,35 @@ def time_steps_no_events(job, steps):
         return (time.perf_counter() - t0) * 1e3 / steps
 
 
+def time_steps_latency(job, steps):
+    """Link latency: each step (planning on the host, table upload and the kernels) timed alone
+    between synchronisations, so nothing overlaps it. Returns the per-step times in ms."""
+    torch = job.torch
+    times = []
+    with NoGC():
+        for _ in range(steps):
+            torch.cuda.synchronize()
+            t0 = time.perf_counter()
+            job.step()
+            torch.cuda.synchronize()
+            times.append((time.perf_counter() - t0) * 1e3)
+    return times
+
+
+def percentiles(times):
+    a = np.asarray(times, dtype=np.float64)
+    return {"p10": round(float(np.percentile(a, 10)), 4), "p50": round(float(np.percentile(a, 50)), 4),
+            "p90": round(float(np.percentile(a, 90)), 4)}
+
+
 def time_steps_cold(job, steps, evict_mib=512):
     """Each step after a write of evict_mib MiB of scratch (the 256 MiB MALL holds none of the
     link step's data afterwards), timed on its own between synchronisations; the eviction is
-    outside the timed interval. Returns (mean ms per step, per-kernel profile)."""
+    outside the timed interval. Returns (ms of each step, per-kernel profile)."""
     torch = job.torch
     scratch = torch.empty(evict_mib << 20, dtype=torch.uint8, device="cuda")
     job.store.profile_enable(True)
-    total = 0.0
+    times = []
     for i in range(steps):
         scratch.fill_(i & 0xff)
         torch.cuda.synchronize()
@@ -203,11 +226,11 @@ def time_steps_cold(job, steps, evict_mib=512):
             t0 = time.perf_counter()
             job.step()
             torch.cuda.synchronize()
-            total += time.perf_counter() - t0
+            times.append((time.perf_counter() - t0) * 1e3)
     prof = job.store.profile_read()
     job.store.profile_enable(False)
     del scratch
-    return total * 1e3 / steps, prof
+    return times, prof
 
 
 def decode_measure(job, steps=DECODE_STEPS, warmup=DECODE_WARMUP):
@@ -496,6 +519,8 @@ def main():
 
     ms_step, prof = time_steps(job, args.steps, args.warmup)
     ms_step_bare = time_steps_no_events(job, args.steps)
+    lat = time_steps_latency(job, args.steps)
+    latency = dict(steps=len(lat), **percentiles(lat))
     if copy_src is not None:
         # a plain elementwise kernel that reads and writes copy_probe_mib MiB each
         for _ in range(args.steps):
@@ -523,10 +548,11 @@ def main():
 
     cold = None
     if args.cold_steps > 0:
-        c_ms, c_prof = time_steps_cold(job, args.cold_steps)
+        c_times, c_prof = time_steps_cold(job, args.cold_steps)
+        c_ms = float(np.mean(c_times))
         cc = max(c_prof["calls"], 1)
         c_attn = c_prof["attention_ms"] / cc
-        cold = {"steps": args.cold_steps, "evict_mib": 512, "ms_per_step": round(c_ms, 4),
+        cold = {"steps": args.cold_steps, "evict_mib": 512, "ms_per_step": round(c_ms, 4), **percentiles(c_times),
                 "attention_ms": round(c_attn, 4), "attention_tflops": round(flop / (c_attn * 1e-3) / 1e12, 2),
                 "rotate_ms": round(c_prof["rotate_ms"] / cc, 4), "scatter_ms": round(c_prof["scatter_ms"] / cc, 4),
                 "merge_ms": round(c_prof["merge_ms"] / cc, 4)}
@@ -567,6 +593,7 @@ def main():
                    "head_dim": cfg.head_dim, "page_size": cfg.page_size, "k": cfg.k,
                    "block_level": cfg.block_level, "key_layout": args.key_layout, "parallelism": "single GPU"},
         "link_latency_ms": round(link_ms, 4),
+        "link_latency_wall_ms": latency,
         "attention_ms": round(attn_ms, 4),
         "scatter_ms": round(scatter_ms, 4),
         "merge_ms": round(merge_ms, 4),

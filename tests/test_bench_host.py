@@ -58,3 +58,8 @@ def test_traffic_applies_only_to_its_kernel_source_workload_and_key_form(tmp_pat
     f.write_text(json.dumps(dict(base, kernel_source_sha256_16="0" * 16)))
     assert bench.traffic_from_profiles("long50k_k32") is None
 
+
+
+def test_percentiles_of_step_times():
+    p = bench.percentiles([float(x) for x in range(1, 12)])
+    assert p == {"p10": 2.0, "p50": 6.0, "p90": 10.0}
