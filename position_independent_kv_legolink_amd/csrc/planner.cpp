@@ -193,9 +193,11 @@ pic_plan *build_plan(pic_store *s, const pic_request *reqs, int32_t n_reqs, cons
     } else {
         // split only items longer than the average load of a compute unit: the longest-first
         // schedule then ends within about one item of the average, and shorter pieces would only
-        // add merge work. Never below 6 key tiles per item, so that a piece's set-up (query
-        // rotation, page table, the first two staged tiles) stays a small part of it.
-        max_pages = std::max<int64_t>(6 * ppt, align_up((total + s->num_cus - 1) / s->num_cus, ppt));
+        // add merge work. A bf16 piece keeps at least 6 key tiles, so that its set-up (query
+        // rotation, page table, the first two staged tiles) stays a small part of it; an fp32
+        // key tile takes several times longer (fp32 MFMAs), and one tile is enough.
+        const int64_t min_tiles = cfg.dtype == PIC_DTYPE_BF16 ? 6 : 1;
+        max_pages = std::max<int64_t>(min_tiles * ppt, align_up((total + s->num_cus - 1) / s->num_cus, ppt));
     }
     // an item's page table is staged in LDS by the attention kernel
     max_pages = std::min<int64_t>(max_pages, kMaxItemPages);
