@@ -160,3 +160,38 @@ def test_automatic_key_rotation_follows_key_reuse(name):
     assert (plan.sizes["rotated_pages"] > 0) == expect
     assert expect == (name in ("long50k_k32", "batched_k16"))
     plan.free()
+
+
+@pytest.mark.parametrize("name,min_tiles", [("tiny", 1), ("llama3_k2", 6)])
+def test_automatic_split_keeps_the_smallest_piece(name, min_tiles):
+    """The automatic split never cuts a key range into pieces shorter than min_tiles key tiles
+    (6 for bf16, 1 for fp32), apart from a range's last piece; above that floor it aims at the
+    average load of a compute unit. Both short requests reach the floor: every item is split."""
+    cfg = CONFIGS[name]
+    wl = Workload(cfg)
+    B = cfg.page_size
+    segs = wl.segments()
+    pages_needed = sum(-(-cfg.chunk_len // B) for _ in wl.chunk_ids)
+    pages_needed += len(wl.requests) * -(-cfg.prefix_len // B) + plan_private(segs, B)
+    store = meta_store(cfg, pages_needed)
+    for c in wl.chunk_ids:
+        store.store_chunk(c, n_tokens=cfg.chunk_len)
+    if cfg.prefix_len:
+        for r in wl.requests:
+            store.store_chunk(cfg.prefix_id(r), n_tokens=cfg.prefix_len)
+    plan = store.link_plan(wl.link_requests(), k=cfg.k, block_level=cfg.block_level)
+    ppt = 64 // B
+    G = cfg.num_q_heads // cfg.num_kv_heads
+    ex = plan.export()
+    pm = ex["pos_map"].reshape(-1, B)
+    n_items = 0
+    for r in range(len(ex["cu_rows"]) - 1):
+        rp = ex["row_pos"][ex["cu_rows"][r]:ex["cu_rows"][r + 1]]
+        first = pm[ex["cu_pages"][r]:ex["cu_pages"][r + 1], 0]
+        for t0 in range(0, len(rp), 256 // G):
+            need = int(np.sum(first <= rp[min(t0 + 256 // G, len(rp)) - 1]))
+            n_split = -(-need // (min_tiles * ppt))
+            step = -(-(-(-need // n_split)) // ppt) * ppt
+            n_items += cfg.num_kv_heads * -(-need // step)
+    s = plan.sizes
+    assert s["work_items"] == s["split_items"] == n_items
