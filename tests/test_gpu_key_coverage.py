@@ -113,3 +113,57 @@ def test_zero_queries_weigh_every_key_once(name, rope_keys, key_layout, pos_offs
             want = np.repeat(mean, G, axis=0)                                  # [Hq][d]
             assert_close(got[r_base + r], want, atol, rtol, f"{name} request {i} row {r} mean")
         r_base += R
+
+
+@pytest.mark.parametrize("name,key_layout", [("llama3_k2", "position_free"), ("batched_k16", "segment_rope"),
+                                             ("long50k_k32", "position_free"), ("block_zipf", "position_free")])
+def test_zero_queries_decode_weighs_every_key_once(name, key_layout):
+    """Decode step i of a request with n linked tokens: its token weighs the n linked keys, the i
+    earlier decode tokens and itself, so lse = ln(n + i + 1) and the output is their values' mean."""
+    cfg = CONFIGS[name]
+    steps = 3
+    _say(f"{name}: zero-query decode, {steps} steps, {key_layout}")
+    wl = Workload(cfg)
+    segs = wl.segments()
+    cached = wl.cached()
+    B = cfg.page_size
+    private = sum(p.private for s in segs for p in oplan.logical_pages(s, B))
+    stored = sum(-(-v[0].shape[0] // B) for v in cached.values())
+    n_tokens = max(oplan.total_tokens(s) for s in segs)
+    store = gpu_store(cfg, cached, num_pages=stored + private + len(segs) * 2 + 8,
+                      max_position=n_tokens + steps + 1, key_layout=key_layout)
+    plan = store.link_plan(wl.link_requests(), k=cfg.k, block_level=cfg.block_level, decode=steps)
+    rows = wl.new_rows(segs)
+    dev = lambda a: torch.from_numpy(np.ascontiguousarray(a)).to("cuda", torch.bfloat16).contiguous()
+    q, kn, vn = (dev(np.concatenate([r[i] for r in rows])) for i in range(3))
+    plan.upload()
+    pic.link_attend(store, plan, q, kn, vn)
+    n_req = len(segs)
+    g = np.random.default_rng(7)
+    means = []
+    for a, s in enumerate(segs):
+        vals = merged_values(s, cached, rows[a][2])
+        means.append([vals.sum(axis=0), vals.shape[0]])
+    for i in range(steps):
+        dk = (0.5 * g.standard_normal((n_req, cfg.num_kv_heads, cfg.head_dim))).astype(np.float32)
+        dv = (0.5 * g.standard_normal((n_req, cfg.num_kv_heads, cfg.head_dim))).astype(np.float32)
+        dq = np.zeros((n_req, cfg.num_q_heads, cfg.head_dim), dtype=np.float32)
+        dvb = torch.from_numpy(dv).to(torch.bfloat16).float().numpy().astype(np.float64)
+        lse = torch.empty((n_req, cfg.num_q_heads), dtype=torch.float32, device="cuda")
+        out = pic.link_decode(store, plan, dev(dq), dev(dk), dev(dv), lse=lse)
+        torch.cuda.synchronize()
+        got_lse = lse.cpu().numpy().astype(np.float64)
+        got = out.float().cpu().numpy()
+        G = cfg.num_q_heads // cfg.num_kv_heads
+        for a, s in enumerate(segs):
+            means[a][0] = means[a][0] + dvb[a]
+            means[a][1] += 1
+            cnt = means[a][1]
+            assert cnt == oplan.total_tokens(s) + i + 1
+            want_lse = np.log(cnt)
+            err = np.abs(got_lse[a] - want_lse)
+            assert np.all(err <= 2e-6 + 1e-6 * want_lse), (a, i, float(err.max()))
+            want = np.repeat(means[a][0] / cnt, G, axis=0)
+            assert_close(got[a], want, 2e-2, 1e-2, f"{name} decode step {i} request {a} mean")
+        _say(f"  step {i}: max |lse - ln n| {np.abs(got_lse - np.log([m[1] for m in means])[:, None]).max():.2e}")
+    plan.free()
