@@ -129,6 +129,17 @@ def _ptr(t):
     return None if t is None else ctypes.c_void_p(t.data_ptr())
 
 
+def _on_device(t, what):
+    """Device memory the kernels read or write: a host tensor here would hand the GPU a host
+    address, so it is refused before any library call."""
+    if t.device.type != "cuda" or not t.is_contiguous():
+        raise ValueError(f"{what} must be a contiguous device tensor")
+
+
+def _nbytes(t):
+    return t.numel() * t.element_size()
+
+
 @dataclass
 class LinkRequest:
     chunk_ids: list
@@ -193,6 +204,8 @@ class Store:
                 raise ValueError(f"chunk K/V must be contiguous {exp}")
             if k.dtype != self.k_pool.dtype or v.dtype != self.k_pool.dtype:
                 raise ValueError("chunk K/V dtype differs from the store's")
+            _on_device(k, "chunk K")
+            _on_device(v, "chunk V")
         _check(lib().pic_store_chunk(self.handle, chunk_id, _ptr(k), _ptr(v), int(n_tokens),
                                      _stream() if k is not None else None))
 
@@ -281,8 +294,9 @@ class Plan:
         import torch
         if workspace is None:
             workspace = torch.empty(self.sizes["workspace_bytes"], dtype=torch.uint8, device=self.store.device)
+        _on_device(workspace, "workspace")
         _check(lib().pic_plan_upload(self.store.handle, self.handle, _ptr(workspace),
-                                     workspace.numel(), _stream()))
+                                     _nbytes(workspace), _stream()))
         self.workspace = workspace
         return workspace
 
@@ -304,16 +318,18 @@ def link_attend(store: Store, plan: Plan, q_new, k_new, v_new, out=None, lse=Non
             raise ValueError(f"{name} must be a contiguous {tdt} device tensor of shape {(R, h, c.head_dim)}")
     if out is None:
         out = torch.empty((R, c.num_q_heads, c.head_dim), dtype=tdt, device=q_new.device)
-    if tuple(out.shape) != (R, c.num_q_heads, c.head_dim) or out.dtype != tdt or not out.is_contiguous():
+    if tuple(out.shape) != (R, c.num_q_heads, c.head_dim) or out.dtype != tdt:
         raise ValueError("out has the wrong shape or dtype")
-    if lse is not None and (tuple(lse.shape) != (R, c.num_q_heads) or lse.dtype != torch.float32
-                            or not lse.is_contiguous()):
-        raise ValueError("lse must be a contiguous float32 tensor [R][Hq]")
+    _on_device(out, "out")
+    if lse is not None:
+        if tuple(lse.shape) != (R, c.num_q_heads) or lse.dtype != torch.float32:
+            raise ValueError("lse must be a float32 tensor [R][Hq]")
+        _on_device(lse, "lse")
     if plan.workspace is None:
         raise RuntimeError("upload the plan before link_attend")
     ws = plan.workspace
     _check(lib().pic_link_attend(store.handle, plan.handle, _ptr(q_new), _ptr(k_new), _ptr(v_new), _ptr(out),
-                                 _ptr(lse), _ptr(ws), ws.numel(), _stream()))
+                                 _ptr(lse), _ptr(ws), _nbytes(ws), _stream()))
     return out
 
 
@@ -330,14 +346,16 @@ def link_decode(store: Store, plan: Plan, q, k, v, out=None, lse=None):
             raise ValueError(f"{name} must be a contiguous {tdt} device tensor of shape {(n, h, c.head_dim)}")
     if out is None:
         out = torch.empty((n, c.num_q_heads, c.head_dim), dtype=tdt, device=q.device)
-    if tuple(out.shape) != (n, c.num_q_heads, c.head_dim) or out.dtype != tdt or not out.is_contiguous():
+    if tuple(out.shape) != (n, c.num_q_heads, c.head_dim) or out.dtype != tdt:
         raise ValueError("out has the wrong shape or dtype")
-    if lse is not None and (tuple(lse.shape) != (n, c.num_q_heads) or lse.dtype != torch.float32
-                            or not lse.is_contiguous()):
-        raise ValueError("lse must be a contiguous float32 tensor [n_req][Hq]")
+    _on_device(out, "out")
+    if lse is not None:
+        if tuple(lse.shape) != (n, c.num_q_heads) or lse.dtype != torch.float32:
+            raise ValueError("lse must be a float32 tensor [n_req][Hq]")
+        _on_device(lse, "lse")
     if plan.workspace is None:
         raise RuntimeError("upload the plan and run link_attend before link_decode")
     ws = plan.workspace
     _check(lib().pic_link_decode(store.handle, plan.handle, _ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse),
-                                 _ptr(ws), ws.numel(), _stream()))
+                                 _ptr(ws), _nbytes(ws), _stream()))
     return out

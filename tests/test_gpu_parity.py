@@ -423,3 +423,31 @@ def test_positions_at_the_limit(rope_keys, key_layout):
     _say(f"positions up to {offset + n_tokens - 1}, rope_keys {rope_keys}, {key_layout} keys")
     got, want, ex = run_workload(cfg, pos_offset=offset, rope_keys=rope_keys, key_layout=key_layout)
     check(cfg, got, want, ex, f"positions at 2^22, rope_keys {rope_keys}, {key_layout} keys")
+
+
+def test_host_tensors_are_refused_before_any_library_call():
+    """A host tensor where the kernels expect device memory is refused by the binding (a kernel
+    would otherwise be handed a host address)."""
+    cfg = small_cfg(k=3, chunk_len=45)
+    wl = Workload(cfg, n_requests=1)
+    cached = wl.cached()
+    store = gpu_store(cfg, cached, num_pages=64, max_position=1024)
+    k, v = next(iter(cached.values()))
+    host = torch.from_numpy(np.ascontiguousarray(k)).to(torch.bfloat16)
+    with pytest.raises(ValueError):
+        store.store_chunk(10 ** 6, host, host)
+    plan = store.link_plan(wl.link_requests(), k=cfg.k)
+    with pytest.raises(ValueError):
+        plan.upload(torch.empty(plan.sizes["workspace_bytes"], dtype=torch.uint8))
+    plan.upload()
+    R = plan.rows
+    dev = torch.zeros((R, cfg.num_q_heads, cfg.head_dim), dtype=torch.bfloat16, device="cuda")
+    kv = torch.zeros((R, cfg.num_kv_heads, cfg.head_dim), dtype=torch.bfloat16, device="cuda")
+    with pytest.raises(ValueError):
+        pic.link_attend(store, plan, dev, kv, kv, out=torch.empty_like(dev, device="cpu"))
+    with pytest.raises(ValueError):
+        pic.link_attend(store, plan, dev, kv, kv, lse=torch.empty((R, cfg.num_q_heads), dtype=torch.float32))
+    with pytest.raises(ValueError):
+        pic.link_attend(store, plan, dev.cpu(), kv, kv)
+    torch.cuda.synchronize()
+    plan.free()
