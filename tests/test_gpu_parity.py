@@ -17,7 +17,8 @@ import pytest
 
 import position_independent_kv_legolink_amd as pic
 from oracle import plan as oplan
-from tests.harness import (TOLERANCE, Workload, assert_close, compare_plan, gpu_store, oracle_outputs)
+from tests.harness import (RESULTS, TOLERANCE, Workload, assert_close, check_rows, compare_plan, gpu_store,
+                           oracle_outputs)
 from workloads import CONFIGS, gen
 
 pytestmark = pytest.mark.gpu
@@ -84,18 +85,24 @@ def run_workload(cfg, *, n_requests=None, sample_rows=None, pos_offset=0, split_
     return outs[0], want, extras
 
 
-def check(cfg, got, want, extras, what):
+def check(cfg, got, want, extras, what, normwise=None):
+    """Element-wise tolerance on outputs and lse, and the norm-wise bound per (row, head) on the
+    outputs. The norm-wise bound assumes score spreads of the Llama-shaped inputs
+    (q_scale * kv_scale <= 1); other inputs record their norm-wise error without the bound."""
     atol, rtol = TOLERANCE[cfg.dtype]
+    if normwise is None:
+        normwise = cfg.q_scale * cfg.kv_scale <= 1.0
     ex = extras["export"]
     worst = 0.0
     for i, (wo, wl) in enumerate(want):
         r0 = ex["cu_rows"][i]
         idx = np.arange(wo.shape[0]) if extras["sample"] is None else extras["sample"][i]
         g = got[r0 + idx]
-        worst = max(worst, assert_close(g, wo, atol, rtol, f"{what} request {i} out"))
+        worst = max(worst, check_rows(g, wo, cfg.dtype, what, normwise=normwise))
         if extras["lse"] is not None:
             assert_close(extras["lse"][r0 + idx], wl, atol, rtol, f"{what} request {i} lse")
-    _say(f"{what}: max abs err {worst:.3e}")
+    nw = RESULTS[what][1] if what in RESULTS else 0.0
+    _say(f"{what}: max abs err {worst:.3e}, worst norm-wise {nw:.3e}")
     return worst
 
 
@@ -198,8 +205,9 @@ def test_growing_scores():
     out = pic.link_attend(store, plan, q, kn, vn, lse=lse_t)
     torch.cuda.synchronize()
     want = oracle_outputs(segs, cached, rows, cfg.rope_theta)
+    # keys of the later chunks are scaled up to 4x: score spreads beyond the norm-wise bound's premise
     check(cfg, out.float().cpu().numpy(), want,
-          dict(export=plan.export(), sample=None, lse=lse_t.cpu().numpy()), "growing scores")
+          dict(export=plan.export(), sample=None, lse=lse_t.cpu().numpy()), "growing scores", normwise=False)
 
 
 @pytest.mark.parametrize("split", [-1, 4, 12])

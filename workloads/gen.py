@@ -108,3 +108,26 @@ def request_chunks(cfg: LinkConfig) -> list[list[int]]:
 def used_chunks(cfg: LinkConfig) -> list[int]:
     """Distinct chunk ids referenced by any request, ascending."""
     return sorted({c for ids in request_chunks(cfg) for c in ids})
+
+
+def structured_values(ident: int, n: int, hkv: int, d: int, new: bool = False) -> np.ndarray:
+    """Values [n][Hkv][d] whose every entry is a multiple of 1/16 below 4 in magnitude, so that
+    bfloat16 holds them and float32 sums of up to 2^18 of them exactly.
+
+    Entry (token j, head g, dim e) of a stored segment ``ident``:
+    (A(g, e) + B(g, e) * U(ident) + W(j)) / 16, with A = (7g + 3e) mod 11 - 5,
+    B = (5g + e) mod 7 - 3, U = 37 * ident mod 29 - 14 and W = j mod 5 - 2; recomputed rows
+    (``new``, ``ident`` = request) take (A + 4B - 1) / 16. A mean over any long run of tokens then
+    keeps an O(1) part that differs between heads, dimensions and sets of segments.
+    """
+    g = np.arange(hkv)[:, None]
+    e = np.arange(d)[None, :]
+    a = (7 * g + 3 * e) % 11 - 5
+    b = (5 * g + e) % 7 - 3
+    if new:
+        base = (a + 4 * b - 1)[None].repeat(n, axis=0)
+    else:
+        u = (37 * int(ident)) % 29 - 14
+        w = np.arange(n) % 5 - 2
+        base = (a + b * u)[None] + w[:, None, None]
+    return (base / 16.0).astype(np.float32)
