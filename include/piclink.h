@@ -62,7 +62,7 @@ typedef int32_t pic_status;
 #define PIC_ERR_NOT_FOUND (-3)  /* unknown chunk id */
 #define PIC_ERR_EXISTS (-4)     /* chunk id already stored */
 #define PIC_ERR_DEVICE (-5)     /* HIP runtime error or kernel launch failure */
-#define PIC_ERR_WORKSPACE (-6)  /* workspace too small or not the uploaded one */
+#define PIC_ERR_WORKSPACE (-6)  /* workspace too small, misaligned, or not holding the plan */
 #define PIC_ERR_STATE (-7)      /* call out of order (e.g. attend before upload) */
 
 #define PIC_DTYPE_BF16 0
@@ -261,8 +261,13 @@ pic_status pic_plan_export(const pic_plan *plan, int32_t *row_pos, int32_t *row_
  * tables are staged into the store's pinned host buffer and the copy is
  * enqueued on `stream`; the call waits only for the previous upload's copy
  * out of that buffer. Work already enqueued on `stream` that reads the same
- * workspace (an earlier link call) runs before the copy. Must precede
- * pic_link_attend with the same workspace, on the same stream. */
+ * workspace (an earlier link call) runs before the copy.
+ * Workspace ownership: the region [workspace, workspace + sizes.workspace_bytes)
+ * now holds this plan, and no longer holds any other plan whose region it
+ * overlaps; a plan holds one region at a time. pic_link_attend uploads the
+ * plan itself when the workspace does not hold it, so this call is needed
+ * only to copy the tables ahead of time (for example while the previous link
+ * call runs). Errors: PIC_ERR_WORKSPACE (too small, misaligned). */
 pic_status pic_plan_upload(pic_store *store, pic_plan *plan, void *workspace, int64_t workspace_bytes,
                            hipStream_t stream);
 
@@ -282,7 +287,13 @@ pic_status pic_plan_upload(pic_store *store, pic_plan *plan, void *workspace, in
  * 3. attention: every selected row attends causally over its request's linked
  *    pages with every key rotated to its absolute position;
  * 4. merge of split KV ranges (log-sum-exp weighted), when the plan split.
- * workspace must be the one the plan was uploaded to. Asynchronous. */
+ * workspace: device memory of at least sizes.workspace_bytes, 256-byte aligned.
+ * When it does not hold this plan's tables (pic_plan_upload), they are copied in
+ * first, on `stream`, as pic_plan_upload does. Errors: PIC_ERR_WORKSPACE (too
+ * small, misaligned), PIC_ERR_INVALID (null row tensor with rows > 0),
+ * PIC_ERR_STATE (metadata-only store), PIC_ERR_DEVICE (launch failure).
+ * Asynchronous; no kernel is launched when an error is returned before the
+ * first launch. */
 pic_status pic_link_attend(pic_store *store, const pic_plan *plan, const void *q_new, const void *k_new,
                            const void *v_new, void *out, float *lse, void *workspace, int64_t workspace_bytes,
                            hipStream_t stream);
@@ -302,9 +313,13 @@ pic_status pic_link_attend(pic_store *store, const pic_plan *plan, const void *q
  *   lse    [n_req][Hq]      optional float32 natural-log softmax denominators
  * The cache's keys are read as the link call rotated them into the workspace. Split-KV: every
  * (request, KV head) is cut into page ranges whose partial results are merged with the token's
- * own score. pic_link_attend zeroes the decode slots and restarts at step 0. Errors:
- * PIC_ERR_STATE (plan not made for decode, not attended on this workspace, or all T steps
- * used), PIC_ERR_WORKSPACE, PIC_ERR_INVALID (null tensor). Asynchronous on `stream`. */
+ * own score. pic_link_attend zeroes the decode slots and restarts at step 0. The workspace
+ * must still hold this plan (no other plan uploaded over it since pic_link_attend), because
+ * the rotated keys and decode tables live there. Errors, each returned before any launch:
+ * PIC_ERR_WORKSPACE (too small, or the workspace does not hold this plan's tables),
+ * PIC_ERR_STATE (plan not made for decode, pic_link_attend not run on this workspace since
+ * its last upload, or all T steps used), PIC_ERR_INVALID (null tensor). Asynchronous on
+ * `stream`. */
 pic_status pic_link_decode(pic_store *store, const pic_plan *plan, const void *q, const void *k, const void *v,
                            void *out, float *lse, void *workspace, int64_t workspace_bytes, hipStream_t stream);
 

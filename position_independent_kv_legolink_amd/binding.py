@@ -326,8 +326,10 @@ def link_attend(store: Store, plan: Plan, q_new, k_new, v_new, out=None, lse=Non
             raise ValueError("lse must be a float32 tensor [R][Hq]")
         _on_device(lse, "lse")
     if plan.workspace is None:
-        raise RuntimeError("upload the plan before link_attend")
+        # the library copies the plan's tables in itself when the workspace does not hold them
+        plan.workspace = torch.empty(plan.sizes["workspace_bytes"], dtype=torch.uint8, device=q_new.device)
     ws = plan.workspace
+    _on_device(ws, "workspace")
     _check(lib().pic_link_attend(store.handle, plan.handle, _ptr(q_new), _ptr(k_new), _ptr(v_new), _ptr(out),
                                  _ptr(lse), _ptr(ws), _nbytes(ws), _stream()))
     return out

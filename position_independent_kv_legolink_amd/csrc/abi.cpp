@@ -84,6 +84,53 @@ const Chunk &store_find(const pic_store *s, uint64_t id) {
     return it->second;
 }
 
+
+// The plan's device tables, laid out as the workspace holds them (offsets from the planner).
+void pack_tables(const pic_plan &plan, uint8_t *blob) {
+    memset(blob, 0, (size_t)plan.table_bytes);
+    auto put = [&](int64_t off, const void *src, size_t bytes) {
+        if (bytes) memcpy(blob + off, src, bytes);
+    };
+    put(plan.off_pages, plan.pages.data(), plan.pages.size() * sizeof(PageDesc));
+    put(plan.off_row_pos, plan.row_pos.data(), plan.row_pos.size() * sizeof(int32_t));
+    put(plan.off_scatter, plan.scatter.data(), plan.scatter.size() * sizeof(ScatterDesc));
+    put(plan.off_work, plan.work.data(), plan.work.size() * sizeof(WorkDesc));
+    put(plan.off_merge, plan.merge.data(), plan.merge.size() * sizeof(MergeDesc));
+    put(plan.off_dec_req, plan.dec_req.data(), plan.dec_req.size() * sizeof(DecodeReq));
+    put(plan.off_dec_work, plan.dec_work.data(), plan.dec_work.size() * sizeof(DecodeDesc));
+    put(plan.off_dec_merge, plan.dec_merge.data(), plan.dec_merge.size() * sizeof(DecodeMergeDesc));
+}
+
+// Stage a plan's tables in the store's pinned buffer and enqueue their copy into the workspace on
+// `stream`; the workspace region then holds this plan (the ledger), and the plan has not yet been
+// attended there.
+void upload_tables(pic_store *s, pic_plan *plan, void *workspace, int64_t workspace_bytes, hipStream_t stream) {
+    if (!workspace || workspace_bytes < plan->workspace_bytes)
+        fail(PIC_ERR_WORKSPACE, "workspace needs " + std::to_string(plan->workspace_bytes) + " bytes");
+    if (reinterpret_cast<uintptr_t>(workspace) % 256 != 0) fail(PIC_ERR_WORKSPACE, "workspace must be 256-byte aligned");
+    // the previous upload's copy out of the staging buffer must have finished before it is rewritten
+    if (plan->table_bytes > 0) {
+        if (s->staging_done) check_hip(hipEventSynchronize(s->staging_done), "staging buffer wait");
+        if (s->staging_bytes < plan->table_bytes) {
+            const int64_t cap = std::max<int64_t>({plan->table_bytes, 2 * s->staging_bytes, 1 << 16});
+            if (s->staging) check_hip(hipHostFree(s->staging), "hipHostFree");
+            s->staging = nullptr;
+            s->staging_bytes = 0;
+            check_hip(hipHostMalloc(&s->staging, (size_t)cap, hipHostMallocDefault), "hipHostMalloc");
+            s->staging_bytes = cap;
+        }
+        if (!s->staging_done)
+            check_hip(hipEventCreateWithFlags(&s->staging_done, hipEventDisableTiming), "hipEventCreate");
+        pack_tables(*plan, static_cast<uint8_t *>(s->staging));
+        check_hip(hipMemcpyAsync(workspace, s->staging, (size_t)plan->table_bytes, hipMemcpyHostToDevice, stream),
+                  "plan upload");
+        check_hip(hipEventRecord(s->staging_done, stream), "hipEventRecord");
+    }
+    s->ledger.claim(plan, workspace, plan->workspace_bytes);
+    plan->attended_ws = nullptr;
+    plan->dec_next = 0;
+}
+
 }  // namespace piclink
 
 using namespace piclink;
@@ -339,41 +386,7 @@ pic_status pic_plan_upload(pic_store *s, pic_plan *plan, void *workspace, int64_
         if (!s || !plan) fail(PIC_ERR_INVALID, "null argument");
         if (plan->owner != s) fail(PIC_ERR_INVALID, "plan belongs to another store");
         if (!s->k_pool) fail(PIC_ERR_STATE, "metadata-only store has no device");
-        if (!workspace || workspace_bytes < plan->workspace_bytes)
-            fail(PIC_ERR_WORKSPACE, "workspace needs " + std::to_string(plan->workspace_bytes) + " bytes");
-        if (reinterpret_cast<uintptr_t>(workspace) % 256 != 0) fail(PIC_ERR_WORKSPACE, "workspace must be 256-byte aligned");
-        // the tables go through the store's pinned staging buffer, so the copy is asynchronous;
-        // the previous upload's copy out of the buffer must have finished before it is rewritten
-        if (plan->table_bytes > 0) {
-            if (s->staging_done) check_hip(hipEventSynchronize(s->staging_done), "staging buffer wait");
-            if (s->staging_bytes < plan->table_bytes) {
-                const int64_t cap = std::max<int64_t>({plan->table_bytes, 2 * s->staging_bytes, 1 << 16});
-                if (s->staging) check_hip(hipHostFree(s->staging), "hipHostFree");
-                s->staging = nullptr;
-                s->staging_bytes = 0;
-                check_hip(hipHostMalloc(&s->staging, (size_t)cap, hipHostMallocDefault), "hipHostMalloc");
-                s->staging_bytes = cap;
-            }
-            if (!s->staging_done)
-                check_hip(hipEventCreateWithFlags(&s->staging_done, hipEventDisableTiming), "hipEventCreate");
-            uint8_t *blob = static_cast<uint8_t *>(s->staging);
-            memset(blob, 0, (size_t)plan->table_bytes);
-            auto put = [&](int64_t off, const void *src, size_t bytes) {
-                if (bytes) memcpy(blob + off, src, bytes);
-            };
-            put(plan->off_pages, plan->pages.data(), plan->pages.size() * sizeof(PageDesc));
-            put(plan->off_row_pos, plan->row_pos.data(), plan->row_pos.size() * sizeof(int32_t));
-            put(plan->off_scatter, plan->scatter.data(), plan->scatter.size() * sizeof(ScatterDesc));
-            put(plan->off_work, plan->work.data(), plan->work.size() * sizeof(WorkDesc));
-            put(plan->off_merge, plan->merge.data(), plan->merge.size() * sizeof(MergeDesc));
-            put(plan->off_dec_req, plan->dec_req.data(), plan->dec_req.size() * sizeof(DecodeReq));
-            put(plan->off_dec_work, plan->dec_work.data(), plan->dec_work.size() * sizeof(DecodeDesc));
-            put(plan->off_dec_merge, plan->dec_merge.data(), plan->dec_merge.size() * sizeof(DecodeMergeDesc));
-            check_hip(hipMemcpyAsync(workspace, blob, (size_t)plan->table_bytes, hipMemcpyHostToDevice, stream),
-                      "plan upload");
-            check_hip(hipEventRecord(s->staging_done, stream), "hipEventRecord");
-        }
-        plan->uploaded_to = workspace;
+        upload_tables(s, plan, workspace, workspace_bytes, stream);
     });
 }
 
@@ -384,11 +397,12 @@ pic_status pic_link_attend(pic_store *s, const pic_plan *plan, const void *q_new
         if (!s || !plan) fail(PIC_ERR_INVALID, "null argument");
         if (plan->owner != s) fail(PIC_ERR_INVALID, "plan belongs to another store");
         if (!s->k_pool) fail(PIC_ERR_STATE, "metadata-only store has no device");
-        if (!plan->uploaded_to || plan->uploaded_to != workspace)
-            fail(PIC_ERR_WORKSPACE, "workspace is not the one this plan was uploaded to");
         if (workspace_bytes < plan->workspace_bytes) fail(PIC_ERR_WORKSPACE, "workspace too small");
         const bool has_rows = !plan->row_pos.empty();
         if (has_rows && (!q_new || !k_new || !v_new || !out)) fail(PIC_ERR_INVALID, "null row tensor");
+        // the plan's tables are copied in first unless this workspace region still holds them
+        if (!s->ledger.holds(plan, workspace))
+            upload_tables(s, const_cast<pic_plan *>(plan), workspace, workspace_bytes, stream);
         uint8_t *ws = static_cast<uint8_t *>(workspace);
         AttnTables t;
         t.pages = reinterpret_cast<const PageDesc *>(ws + plan->off_pages);
@@ -444,9 +458,10 @@ pic_status pic_link_decode(pic_store *s, const pic_plan *plan, const void *q, co
         if (plan->owner != s) fail(PIC_ERR_INVALID, "plan belongs to another store");
         if (!s->k_pool) fail(PIC_ERR_STATE, "metadata-only store has no device");
         if (!plan->decode) fail(PIC_ERR_STATE, "plan was not made for decode (opts.decode)");
-        if (!plan->uploaded_to || plan->uploaded_to != workspace)
-            fail(PIC_ERR_WORKSPACE, "workspace is not the one this plan was uploaded to");
         if (workspace_bytes < plan->workspace_bytes) fail(PIC_ERR_WORKSPACE, "workspace too small");
+        if (!s->ledger.holds(plan, workspace))
+            fail(PIC_ERR_WORKSPACE, "the workspace does not hold this plan's tables (never uploaded there, or "
+                                    "another plan was uploaded over them)");
         if (plan->attended_ws != workspace)
             fail(PIC_ERR_STATE, "run pic_link_attend on this workspace first (it rotates the keys decode reads)");
         if (plan->dec_next >= plan->dec_steps)
@@ -475,6 +490,7 @@ pic_status pic_plan_free(pic_store *s, pic_plan *plan) {
     return guarded([&] {
         if (!s || !plan) fail(PIC_ERR_INVALID, "null argument");
         if (plan->owner != s) fail(PIC_ERR_INVALID, "plan belongs to another store");
+        s->ledger.drop(plan);
         release_plan(s, plan);
     });
 }

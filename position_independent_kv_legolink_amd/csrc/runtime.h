@@ -11,6 +11,7 @@
 #include "../../include/piclink.h"
 #include "launch.h"
 #include "layout.h"
+#include "ledger.h"
 
 namespace piclink {
 
@@ -57,6 +58,7 @@ struct pic_store {
     void *staging = nullptr;
     int64_t staging_bytes = 0;
     hipEvent_t staging_done = nullptr;
+    piclink::WorkspaceLedger<pic_plan> ledger;   // which plan's tables each workspace region holds
 };
 
 struct pic_plan {
@@ -84,8 +86,7 @@ struct pic_plan {
     std::vector<piclink::DecodeDesc> dec_work;
     std::vector<piclink::DecodeMergeDesc> dec_merge;
     int64_t off_dec_req = 0, off_dec_work = 0, off_dec_merge = 0, off_dec_o = 0, off_dec_lse = 0;
-    const void *attended_ws = nullptr;  // workspace of the last pic_link_attend (holds the rotated keys)
-    void *uploaded_to = nullptr;
+    const void *attended_ws = nullptr;  // workspace of the last pic_link_attend since the last upload
 };
 
 namespace piclink {
