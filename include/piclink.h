@@ -298,6 +298,28 @@ pic_status pic_link_attend(pic_store *store, const pic_plan *plan, const void *q
                            const void *v_new, void *out, float *lse, void *workspace, int64_t workspace_bytes,
                            hipStream_t stream);
 
+/* Bytes of the library's static device scratch: the largest plan workspace that
+ * pic_link_attend_static takes. */
+#define PIC_STATIC_SCRATCH_BYTES (64ll << 20)
+
+/* pic_link_attend without a caller workspace, for callers that cannot allocate device
+ * memory: code under HIP graph capture, tight serving loops, harnesses that forbid hipMalloc.
+ * The library keeps one static device array of PIC_STATIC_SCRATCH_BYTES (64 MiB) per GPU,
+ * held until the process ends; the plan's tables are copied into it from the plan's host
+ * arrays (plain hipMemcpyAsync, no staging buffer) and the link step's kernels use it as
+ * their workspace (tables, split partials, rotated keys). The caller still passes the row
+ * tensors and the outputs, as for pic_link_attend, whose results it reproduces bit for bit.
+ * The call allocates nothing: no hipMalloc, hipFree, hipHostMalloc or other allocating
+ * routine. Every call on one GPU shares that GPU's array, which keeps the last call's
+ * contents: calls whose device work overlaps on one GPU (other streams, other threads) race
+ * and must be ordered by the caller. After it, the plan's tables are in the scratch, not in
+ * its earlier workspace: a later pic_link_attend copies them in again, and pic_link_decode
+ * needs a pic_link_attend first. Errors, before any copy or launch: PIC_ERR_WORKSPACE (the
+ * plan's sizes.workspace_bytes exceeds PIC_STATIC_SCRATCH_BYTES), and those of
+ * pic_link_attend. */
+pic_status pic_link_attend_static(pic_store *store, const pic_plan *plan, const void *q_new, const void *k_new,
+                                  const void *v_new, void *out, float *lse, hipStream_t stream);
+
 /* Decode after link: one generation step per request (EPIC digest, abstract: chunks are
  * compiled, then linked, then the request generates; MEPIC abstract: the paged, shared cache
  * serves the request). For a plan made with opts.decode = T, after pic_link_attend ran on the

@@ -24,7 +24,8 @@ DTYPES = {"bf16": 0, "f32": 1}
 EXPORTS = ["pic_store_sizes", "pic_store_create", "pic_store_destroy", "pic_store_chunk",
            "pic_store_chunk_pages", "pic_store_release", "pic_store_evict", "pic_store_usage", "pic_store_stats",
            "pic_link_plan",
-           "pic_plan_info", "pic_plan_export", "pic_plan_upload", "pic_link_attend", "pic_link_decode",
+           "pic_plan_info", "pic_plan_export", "pic_plan_upload", "pic_link_attend", "pic_link_attend_static",
+           "pic_link_decode",
            "pic_plan_free",
            "pic_profile_enable", "pic_profile_read", "pic_last_error"]
 
@@ -100,6 +101,7 @@ def lib():
             "pic_plan_export": [vp, vp, vp, vp, vp, vp, vp, vp, vp],
             "pic_plan_upload": [vp, vp, vp, i64, vp],
             "pic_link_attend": [vp, vp, vp, vp, vp, vp, vp, vp, i64, vp],
+            "pic_link_attend_static": [vp, vp, vp, vp, vp, vp, vp, vp],
             "pic_link_decode": [vp, vp, vp, vp, vp, vp, vp, vp, i64, vp],
             "pic_plan_free": [vp, vp],
             "pic_profile_enable": [vp, i32],
@@ -332,6 +334,40 @@ def link_attend(store: Store, plan: Plan, q_new, k_new, v_new, out=None, lse=Non
     _on_device(ws, "workspace")
     _check(lib().pic_link_attend(store.handle, plan.handle, _ptr(q_new), _ptr(k_new), _ptr(v_new), _ptr(out),
                                  _ptr(lse), _ptr(ws), _nbytes(ws), _stream()))
+    return out
+
+
+STATIC_SCRATCH_BYTES = 64 << 20
+
+
+def _link_args(store: Store, plan: Plan, q_new, k_new, v_new, out, lse):
+    import torch
+    c = store.cfg
+    R = plan.rows
+    tdt = store.k_pool.dtype
+    for name, t, h in (("q_new", q_new, c.num_q_heads), ("k_new", k_new, c.num_kv_heads),
+                       ("v_new", v_new, c.num_kv_heads)):
+        if tuple(t.shape) != (R, h, c.head_dim) or t.dtype != tdt or not t.is_contiguous() or t.device.type != "cuda":
+            raise ValueError(f"{name} must be a contiguous {tdt} device tensor of shape {(R, h, c.head_dim)}")
+    if out is None:
+        out = torch.empty((R, c.num_q_heads, c.head_dim), dtype=tdt, device=q_new.device)
+    if tuple(out.shape) != (R, c.num_q_heads, c.head_dim) or out.dtype != tdt:
+        raise ValueError("out has the wrong shape or dtype")
+    _on_device(out, "out")
+    if lse is not None:
+        if tuple(lse.shape) != (R, c.num_q_heads) or lse.dtype != torch.float32:
+            raise ValueError("lse must be a float32 tensor [R][Hq]")
+        _on_device(lse, "lse")
+    return out
+
+
+def link_attend_static(store: Store, plan: Plan, q_new, k_new, v_new, out=None, lse=None):
+    """The link step on the library's static device scratch instead of a workspace
+    (pic_link_attend_static: allocates nothing when ``out`` is given). Plans whose workspace
+    exceeds STATIC_SCRATCH_BYTES are refused. Returns ``out``."""
+    out = _link_args(store, plan, q_new, k_new, v_new, out, lse)
+    _check(lib().pic_link_attend_static(store.handle, plan.handle, _ptr(q_new), _ptr(k_new), _ptr(v_new), _ptr(out),
+                                        _ptr(lse), _stream()))
     return out
 
 

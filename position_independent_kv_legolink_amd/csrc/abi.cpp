@@ -9,6 +9,8 @@
 
 #include "runtime.h"
 
+static_assert(piclink::kStaticScratchBytes == PIC_STATIC_SCRATCH_BYTES, "scratch size differs from the header");
+
 namespace piclink {
 
 thread_local std::string g_last_error;
@@ -129,6 +131,67 @@ void upload_tables(pic_store *s, pic_plan *plan, void *workspace, int64_t worksp
     s->ledger.claim(plan, workspace, plan->workspace_bytes);
     plan->attended_ws = nullptr;
     plan->dec_next = 0;
+}
+
+
+// Argument checks shared by the link calls; every failure is raised before any launch.
+void check_link_call(pic_store *s, const pic_plan *plan, const void *q_new, const void *k_new, const void *v_new,
+                     const void *out) {
+    if (!s || !plan) fail(PIC_ERR_INVALID, "null argument");
+    if (plan->owner != s) fail(PIC_ERR_INVALID, "plan belongs to another store");
+    if (!s->k_pool) fail(PIC_ERR_STATE, "metadata-only store has no device");
+    if (!plan->row_pos.empty() && (!q_new || !k_new || !v_new || !out)) fail(PIC_ERR_INVALID, "null row tensor");
+}
+
+// The device link step over a workspace that holds the plan's tables: scatter, key rotation (when
+// the plan rotates ahead), attention and the merge of split ranges, with per-kernel events when
+// `prof`.
+void launch_link(pic_store *s, const pic_plan *plan, const void *q_new, const void *k_new, const void *v_new,
+                 void *out, float *lse, uint8_t *ws, bool prof, hipStream_t stream) {
+    AttnTables t;
+    t.pages = reinterpret_cast<const PageDesc *>(ws + plan->off_pages);
+    t.row_pos = reinterpret_cast<const int32_t *>(ws + plan->off_row_pos);
+    t.work = reinterpret_cast<const WorkDesc *>(ws + plan->off_work);
+    t.n_work = (int)plan->work.size();
+    t.merge = reinterpret_cast<const MergeDesc *>(ws + plan->off_merge);
+    t.n_merge = (int)plan->merge.size();
+    t.part_o = reinterpret_cast<float *>(ws + plan->off_part_o);
+    t.part_lse = reinterpret_cast<float *>(ws + plan->off_part_lse);
+    if (plan->rotate_keys) t.k_rot = ws + plan->off_k_rot;
+
+    ProfileMarks marks{};
+    if (prof) {
+        for (int i = 0; i < 5; ++i) {
+            if (!s->spare_events.empty()) {
+                marks.ev[i] = s->spare_events.back();
+                s->spare_events.pop_back();
+            } else {
+                check_hip(hipEventCreate(&marks.ev[i]), "hipEventCreate");
+            }
+        }
+        check_hip(hipEventRecord(marks.ev[0], stream), "hipEventRecord");
+    }
+    check_hip(launch_scatter(s->shape, s->k_pool, s->v_pool, k_new, v_new, s->rope,
+                             reinterpret_cast<const ScatterDesc *>(ws + plan->off_scatter), (int)plan->scatter.size(),
+                             stream),
+              "scatter launch");
+    if (prof) check_hip(hipEventRecord(marks.ev[1], stream), "hipEventRecord");
+    if (plan->rotate_keys)
+        check_hip(launch_rotate_keys(s->shape, s->k_pool, s->rope, t.pages, (int)plan->pages.size(),
+                                     const_cast<void *>(t.k_rot), stream),
+                  "key rotation launch");
+    if (prof) check_hip(hipEventRecord(marks.ev[2], stream), "hipEventRecord");
+    check_hip(launch_attention(s->shape, q_new, s->k_pool, s->v_pool, s->rope, t, out, lse, stream),
+              "attention launch");
+    if (prof) check_hip(hipEventRecord(marks.ev[3], stream), "hipEventRecord");
+    check_hip(launch_merge(s->shape, t, out, lse, stream), "merge launch");
+    pic_plan *mp = const_cast<pic_plan *>(plan);
+    mp->attended_ws = ws;
+    mp->dec_next = 0;   // the scatter zeroed the decode slots
+    if (prof) {
+        check_hip(hipEventRecord(marks.ev[4], stream), "hipEventRecord");
+        s->pending.push_back(marks);
+    }
 }
 
 }  // namespace piclink
@@ -394,60 +457,43 @@ pic_status pic_link_attend(pic_store *s, const pic_plan *plan, const void *q_new
                            const void *v_new, void *out, float *lse, void *workspace, int64_t workspace_bytes,
                            hipStream_t stream) {
     return guarded([&] {
-        if (!s || !plan) fail(PIC_ERR_INVALID, "null argument");
-        if (plan->owner != s) fail(PIC_ERR_INVALID, "plan belongs to another store");
-        if (!s->k_pool) fail(PIC_ERR_STATE, "metadata-only store has no device");
+        check_link_call(s, plan, q_new, k_new, v_new, out);
         if (workspace_bytes < plan->workspace_bytes) fail(PIC_ERR_WORKSPACE, "workspace too small");
-        const bool has_rows = !plan->row_pos.empty();
-        if (has_rows && (!q_new || !k_new || !v_new || !out)) fail(PIC_ERR_INVALID, "null row tensor");
         // the plan's tables are copied in first unless this workspace region still holds them
         if (!s->ledger.holds(plan, workspace))
             upload_tables(s, const_cast<pic_plan *>(plan), workspace, workspace_bytes, stream);
-        uint8_t *ws = static_cast<uint8_t *>(workspace);
-        AttnTables t;
-        t.pages = reinterpret_cast<const PageDesc *>(ws + plan->off_pages);
-        t.row_pos = reinterpret_cast<const int32_t *>(ws + plan->off_row_pos);
-        t.work = reinterpret_cast<const WorkDesc *>(ws + plan->off_work);
-        t.n_work = (int)plan->work.size();
-        t.merge = reinterpret_cast<const MergeDesc *>(ws + plan->off_merge);
-        t.n_merge = (int)plan->merge.size();
-        t.part_o = reinterpret_cast<float *>(ws + plan->off_part_o);
-        t.part_lse = reinterpret_cast<float *>(ws + plan->off_part_lse);
-        if (plan->rotate_keys) t.k_rot = ws + plan->off_k_rot;
+        launch_link(s, plan, q_new, k_new, v_new, out, lse, static_cast<uint8_t *>(workspace), s->profiling, stream);
+    });
+}
 
-        ProfileMarks marks{};
-        const bool prof = s->profiling;
-        if (prof) {
-            for (int i = 0; i < 5; ++i) {
-                if (!s->spare_events.empty()) {
-                    marks.ev[i] = s->spare_events.back();
-                    s->spare_events.pop_back();
-                } else {
-                    check_hip(hipEventCreate(&marks.ev[i]), "hipEventCreate");
-                }
-            }
-            check_hip(hipEventRecord(marks.ev[0], stream), "hipEventRecord");
-        }
-        check_hip(launch_scatter(s->shape, s->k_pool, s->v_pool, k_new, v_new, s->rope,
-                                 reinterpret_cast<const ScatterDesc *>(ws + plan->off_scatter),
-                                 (int)plan->scatter.size(), stream),
-                  "scatter launch");
-        if (prof) check_hip(hipEventRecord(marks.ev[1], stream), "hipEventRecord");
-        if (plan->rotate_keys)
-            check_hip(launch_rotate_keys(s->shape, s->k_pool, s->rope, t.pages, (int)plan->pages.size(),
-                                         const_cast<void *>(t.k_rot), stream),
-                      "key rotation launch");
-        if (prof) check_hip(hipEventRecord(marks.ev[2], stream), "hipEventRecord");
-        check_hip(launch_attention(s->shape, q_new, s->k_pool, s->v_pool, s->rope, t, out, lse, stream),
-                  "attention launch");
-        if (prof) check_hip(hipEventRecord(marks.ev[3], stream), "hipEventRecord");
-        check_hip(launch_merge(s->shape, t, out, lse, stream), "merge launch");
-        const_cast<pic_plan *>(plan)->attended_ws = workspace;
-        const_cast<pic_plan *>(plan)->dec_next = 0;   // the scatter zeroed the decode slots
-        if (prof) {
-            check_hip(hipEventRecord(marks.ev[4], stream), "hipEventRecord");
-            s->pending.push_back(marks);
-        }
+pic_status pic_link_attend_static(pic_store *s, const pic_plan *plan, const void *q_new, const void *k_new,
+                                  const void *v_new, void *out, float *lse, hipStream_t stream) {
+    return guarded([&] {
+        check_link_call(s, plan, q_new, k_new, v_new, out);
+        if (plan->workspace_bytes > kStaticScratchBytes)
+            fail(PIC_ERR_WORKSPACE, "the plan needs " + std::to_string(plan->workspace_bytes) +
+                                        " bytes of workspace; the static scratch holds " +
+                                        std::to_string(kStaticScratchBytes));
+        void *scratch = nullptr;
+        check_hip(static_scratch(&scratch), "static scratch address");
+        // the tables go straight from the plan's host arrays (pageable memory: each copy has read
+        // its source when it returns), so no staging buffer is needed
+        uint8_t *ws = static_cast<uint8_t *>(scratch);
+        auto put = [&](int64_t off, const void *src, size_t bytes) {
+            if (bytes)
+                check_hip(hipMemcpyAsync(ws + off, src, bytes, hipMemcpyHostToDevice, stream), "plan table copy");
+        };
+        put(plan->off_pages, plan->pages.data(), plan->pages.size() * sizeof(PageDesc));
+        put(plan->off_row_pos, plan->row_pos.data(), plan->row_pos.size() * sizeof(int32_t));
+        put(plan->off_scatter, plan->scatter.data(), plan->scatter.size() * sizeof(ScatterDesc));
+        put(plan->off_work, plan->work.data(), plan->work.size() * sizeof(WorkDesc));
+        put(plan->off_merge, plan->merge.data(), plan->merge.size() * sizeof(MergeDesc));
+        put(plan->off_dec_req, plan->dec_req.data(), plan->dec_req.size() * sizeof(DecodeReq));
+        put(plan->off_dec_work, plan->dec_work.data(), plan->dec_work.size() * sizeof(DecodeDesc));
+        put(plan->off_dec_merge, plan->dec_merge.data(), plan->dec_merge.size() * sizeof(DecodeMergeDesc));
+        pic_plan *mp = const_cast<pic_plan *>(plan);
+        s->ledger.claim(mp, scratch, plan->workspace_bytes);   // its caller workspace no longer holds it
+        launch_link(s, plan, q_new, k_new, v_new, out, lse, ws, false, stream);
     });
 }
 

@@ -20,6 +20,7 @@
 #include <math.h>
 #include <stdint.h>
 
+#include <mutex>
 #include <type_traits>
 
 #include "launch.h"
@@ -1736,6 +1737,32 @@ hipError_t launch_decode(const LayerShape &s, const void *q, const void *k, cons
     if (s.d == 128) hipLaunchKernelGGL(link_decode_merge<128>, grid, dim3(512), 0, stream, m);
     else hipLaunchKernelGGL(link_decode_merge<64>, grid, dim3(512), 0, stream, m);
     return hipGetLastError();
+}
+
+// Device scratch of the allocation-free link call (pic_link_attend_static): the plan tables, split
+// partials and rotated keys of one call. Each GPU the library runs on holds its own copy, at its own
+// address, until the process ends. In host code `scratch` names a host-side stand-in: its device
+// address comes from hipGetSymbolAddress, once per device, and only that address is used.
+static __device__ __align__(256) uint8_t scratch[kStaticScratchBytes];
+
+hipError_t static_scratch(void **ptr) {
+    constexpr int kMaxDevices = 64;
+    static std::mutex lock;
+    static void *address[kMaxDevices] = {};
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+    std::lock_guard<std::mutex> hold(lock);
+    if (!address[dev]) {
+        void *p = nullptr;
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess) return e;
+        if (!p) return hipErrorInvalidSymbol;
+        address[dev] = p;
+    }
+    *ptr = address[dev];
+    return hipSuccess;
 }
 
 hipError_t launch_merge(const LayerShape &s, const AttnTables &t, void *out, float *lse, hipStream_t stream) {

@@ -74,4 +74,8 @@ struct DecodeTables {
 hipError_t launch_decode(const LayerShape &s, const void *q, const void *k, const void *v, void *k_pool, void *v_pool,
                          const float *rope, const DecodeTables &t, void *out, float *lse, hipStream_t stream);
 
+// Address, on the current device, of the library's static device scratch (kStaticScratchBytes,
+// one array per GPU, held until the process ends), looked up once per device.
+hipError_t static_scratch(void **ptr);
+
 }  // namespace piclink

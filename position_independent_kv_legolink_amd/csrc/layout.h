@@ -95,6 +95,9 @@ constexpr int kThreads = 256;      // page writers, merge and the fp32 attention
 // much as 5 reads' worth of rotation inside attention.
 constexpr int kRotateReuse = 5;
 
+// Device scratch of the allocation-free link call: the largest plan workspace it takes.
+constexpr int64_t kStaticScratchBytes = int64_t(64) << 20;
+
 // (row, head) pairs handled by one attention work group: 8 waves x 32 rows (bf16), 4 x 32 (fp32).
 constexpr int tile_qrows(int dtype) { return dtype == 0 ? 256 : 128; }
 
