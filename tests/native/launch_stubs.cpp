@@ -25,6 +25,7 @@ hipError_t launch_attention(const LayerShape &, const void *, const void *, cons
 hipError_t launch_merge(const LayerShape &, const AttnTables &, void *, float *, hipStream_t) {
     return hipErrorNotSupported;
 }
+hipError_t static_scratch(void **) { return hipErrorNotSupported; }
 hipError_t launch_decode(const LayerShape &, const void *, const void *, const void *, void *, void *, const float *,
                          const DecodeTables &, void *, float *, hipStream_t) {
     return hipErrorNotSupported;
