@@ -267,10 +267,13 @@ def decode_measure(job, steps=DECODE_STEPS, warmup=DECODE_WARMUP):
     page_bytes = cfg.num_kv_heads * cfg.page_size * cfg.head_dim * elem
     nbytes = 2 * plan.sizes["pages"] * page_bytes + n * (2 * cfg.num_q_heads + 2 * cfg.num_kv_heads) * cfg.head_dim * elem
     items = plan.sizes["decode_items"]
+    ws_mb = plan.sizes["workspace_bytes"] / 1e6
+    rot_mb = plan.sizes["rotated_key_bytes"] / 1e6
     plan.free()
     gbps = nbytes / (ms * 1e-3) / 1e9
     return {"requests": n, "ms": round(ms, 4), "work_items": items, "algorithmic_mb": round(nbytes / 1e6, 1),
-            "gbps": round(gbps, 1), "hbm_frac": round(gbps / PEAK_HBM_GBPS, 4)}
+            "gbps": round(gbps, 1), "hbm_frac": round(gbps / PEAK_HBM_GBPS, 4),
+            "workspace_mb": round(ws_mb, 1), "rotated_keys_mb": round(rot_mb, 1)}
 
 
 def dense_comparator(job, reps=3):
@@ -502,9 +505,18 @@ def main():
     page_bytes = cfg.num_kv_heads * cfg.page_size * cfg.head_dim * elem
     logical = int(job.sizes["pages"])
     distinct = int(np.unique(job.export["block_table"]).size)
+    # live device bytes of the link step: the K/V pages it reads (each distinct page once) plus the
+    # plan's workspace, whose rotated keys are a per-request copy of every logical key page
+    unique_kv = 2 * distinct * page_bytes
+    ws = job.sizes["workspace_bytes"]
     kv_pages = {"logical": logical, "distinct": distinct, "sharing_ratio": round(logical / max(distinct, 1), 3),
-                "unique_kv_mb": round(2 * distinct * page_bytes / 1e6, 1),
-                "logical_kv_mb": round(2 * logical * page_bytes / 1e6, 1)}
+                "unique_kv_mb": round(unique_kv / 1e6, 1),
+                "logical_kv_mb": round(2 * logical * page_bytes / 1e6, 1),
+                "workspace_mb": round(ws / 1e6, 1),
+                "rotated_keys_mb": round(job.sizes["rotated_key_bytes"] / 1e6, 1),
+                "partials_mb": round(job.sizes["partial_bytes"] / 1e6, 1),
+                "live_mb": round((unique_kv + ws) / 1e6, 1),
+                "live_saving": round(2 * logical * page_bytes / max(unique_kv + ws, 1), 3)}
     t = time.perf_counter()
     for _ in range(10):
         job.store.link_plan(job.requests, **job.plan_kw).free()

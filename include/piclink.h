@@ -145,7 +145,11 @@ typedef struct {
  * q_new/k_new/v_new/out); pages = logical pages over all requests;
  * rotated_pages = logical pages whose keys pic_link_attend rotates into the
  * workspace before attention (0: keys are rotated inside attention);
- * decode_items = split-KV work items of pic_link_decode (0: plan not made for decode). */
+ * decode_items = split-KV work items of pic_link_decode (0: plan not made for decode);
+ * workspace_bytes = table_bytes (the uploaded tables) + partial_bytes (float32 partial
+ * results of split key ranges, link and decode) + rotated_key_bytes (the keys of every logical
+ * page rotated ahead of attention: a per-request copy of shared pages, 0 when keys are rotated
+ * inside attention) + alignment. */
 typedef struct {
     int64_t rows;
     int64_t pages;
@@ -157,6 +161,9 @@ typedef struct {
     int64_t requests;
     int64_t rotated_pages;
     int64_t decode_items;
+    int64_t table_bytes;
+    int64_t partial_bytes;
+    int64_t rotated_key_bytes;
 } pic_plan_sizes;
 
 /* Device bytes the caller must provide: each K and V pool

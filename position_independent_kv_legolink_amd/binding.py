@@ -70,7 +70,9 @@ class PlanSizes(ctypes.Structure):
     _fields_ = [("rows", ctypes.c_int64), ("pages", ctypes.c_int64), ("private_pages", ctypes.c_int64),
                 ("cow_pages", ctypes.c_int64), ("work_items", ctypes.c_int64),
                 ("split_items", ctypes.c_int64), ("workspace_bytes", ctypes.c_int64),
-                ("requests", ctypes.c_int64), ("rotated_pages", ctypes.c_int64), ("decode_items", ctypes.c_int64)]
+                ("requests", ctypes.c_int64), ("rotated_pages", ctypes.c_int64), ("decode_items", ctypes.c_int64),
+                ("table_bytes", ctypes.c_int64), ("partial_bytes", ctypes.c_int64),
+                ("rotated_key_bytes", ctypes.c_int64)]
 
 
 _lib = None

@@ -419,6 +419,9 @@ pic_status pic_plan_info(const pic_plan *plan, pic_plan_sizes *sz) {
         sz->requests = plan->n_requests;
         sz->rotated_pages = plan->rotate_keys ? (int64_t)plan->pages.size() : 0;
         sz->decode_items = (int64_t)plan->dec_work.size();
+        sz->table_bytes = plan->table_bytes;
+        sz->partial_bytes = (plan->off_k_rot - plan->off_part_o) + (plan->off_end - plan->off_dec_o);
+        sz->rotated_key_bytes = plan->off_dec_o - plan->off_k_rot;
     });
 }
 

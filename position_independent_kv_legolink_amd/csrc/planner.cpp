@@ -292,6 +292,7 @@ pic_plan *build_plan(pic_store *s, const pic_request *reqs, int32_t n_reqs, cons
     plan->off_k_rot = place(plan->rotate_keys ? (int64_t)plan->pages.size() * s->shape.page_elems * elem : 0);
     plan->off_dec_o = place((int64_t)plan->dec_work.size() * G * cfg.head_dim * sizeof(float));
     plan->off_dec_lse = place((int64_t)plan->dec_work.size() * G * sizeof(float));
+    plan->off_end = off;
     plan->workspace_bytes = std::max<int64_t>(off, 256);
     return plan;
 }

@@ -85,7 +85,7 @@ struct pic_plan {
     std::vector<piclink::DecodeReq> dec_req;
     std::vector<piclink::DecodeDesc> dec_work;
     std::vector<piclink::DecodeMergeDesc> dec_merge;
-    int64_t off_dec_req = 0, off_dec_work = 0, off_dec_merge = 0, off_dec_o = 0, off_dec_lse = 0;
+    int64_t off_dec_req = 0, off_dec_work = 0, off_dec_merge = 0, off_dec_o = 0, off_dec_lse = 0, off_end = 0;
     const void *attended_ws = nullptr;  // workspace of the last pic_link_attend since the last upload
 };
 

@@ -160,6 +160,29 @@ def test_plan_sizes_report_workspace():
     plan.free()
 
 
+def test_workspace_breakdown_adds_up():
+    """table_bytes + partial_bytes + rotated_key_bytes (+ 256-byte alignment) = workspace_bytes;
+    the rotated keys are one page of keys per logical page, the partials one float32 row per
+    split slot (link) or decode item."""
+    s = meta(num_pages=400)
+    for c in range(6):
+        s.store_chunk(c, n_tokens=300)
+    req = [pic.LinkRequest(list(range(6)), 40)]
+    for kw in (dict(rope_keys=1), dict(rope_keys=2), dict(rope_keys=1, split_pages=4), dict(decode=3)):
+        plan = s.link_plan(req, k=3, **kw)
+        z = plan.sizes
+        parts = z["table_bytes"] + z["partial_bytes"] + z["rotated_key_bytes"]
+        assert parts <= z["workspace_bytes"] <= parts + 8 * 256, (kw, z)
+        page_bytes = 2 * 16 * 128 * 2          # Hkv 2, page 16, d 128, bf16
+        assert z["rotated_key_bytes"] >= z["rotated_pages"] * page_bytes
+        assert z["rotated_key_bytes"] < z["rotated_pages"] * page_bytes + 256
+        if z["split_items"] == 0 and z["decode_items"] == 0:
+            assert z["partial_bytes"] == 0
+        else:
+            assert z["partial_bytes"] > 0
+        plan.free()
+
+
 def test_rope_keys_option_is_validated():
     s = meta()
     s.store_chunk(1, n_tokens=40)
