@@ -13,7 +13,8 @@
  *     embedding is applied at the linked position at attention time (MEPIC,
  *     searcharxiv.org abstract: positional encodings removed from stored KV,
  *     RoPE fused into attention): key t is rotated by key_rot[t], which is
- *     key_pos[t] for such a key (key_rot NULL). A key that already carries a
+ *     key_pos[t] for such a key (key_rot NULL); key_rot may be negative, a
+ *     rotation by a negative angle. A key that already carries a
  *     rotation at its position s inside its segment, as a chunk compiled from
  *     position 0 leaves it (EPIC, atlas.scime.ai summary, "Approach"), is
  *     rotated by the segment's linked start instead; the two rotations

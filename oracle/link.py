@@ -12,8 +12,14 @@ Cached keys come in one of two forms. Position-free keys (MEPIC abstract) are
 rotated at each token's absolute position. Keys compiled from position 0 (EPIC
 summary, "Approach": a chunk is encoded on its own, so token j of a segment
 carries the rotation of position j) are re-rotated by the segment's linked
-start, the offset the chunk is moved by. New rows are always given
-position-free and are rotated at their absolute position.
+start, the offset the chunk is moved by. A chunk compiled after c leading
+tokens whose KV is then dropped (EPIC summary, "Measured effects" table: the
+LegoLink-0 ablation prepends four dummy tokens during compilation and discards
+them; read here as the dummies taking positions 0..c-1, so token j of the chunk
+was encoded at position c + j) carries the rotation of c + j, and moves by the
+segment's start minus c, which is negative for a chunk linked before position
+c. New rows are always given position-free and are rotated at their absolute
+position.
 """
 from __future__ import annotations
 
@@ -26,14 +32,15 @@ from .plan import selected_positions, token_positions
 KEY_LAYOUTS = ("position_free", "segment_rope")
 
 
-def merged_cache(segs, cached: dict, k_new, v_new, key_layout="position_free"):
+def merged_cache(segs, cached: dict, k_new, v_new, key_layout="position_free", compile_offset=0):
     """Token-level K, V [N][Hkv][d] (fp64), absolute positions [N] and the
     position each key is rotated by [N] of one request.
 
     ``cached`` maps a segment's store id to its cached (K, V), each
     [length][Hkv][d], with keys in the form ``key_layout`` names;
     ``k_new``/``v_new`` hold the recomputed rows (position-free keys) in the
-    order of ``selected_positions(segs)``.
+    order of ``selected_positions(segs)``. With ``key_layout="segment_rope"``,
+    cached token j of a segment carries the rotation of ``compile_offset + j``.
     """
     if key_layout not in KEY_LAYOUTS:
         raise ValueError(f"unknown key layout {key_layout!r}")
@@ -61,7 +68,7 @@ def merged_cache(segs, cached: dict, k_new, v_new, key_layout="position_free"):
         # position 0, which move by the segment's start
         pos = s.start + np.arange(s.length, dtype=np.int64)
         if key_layout == "segment_rope" and s.kind != "suffix":
-            pos[s.recompute:] = s.start
+            pos[s.recompute:] = s.start - compile_offset
         rot.append(pos)
     if r != k_new.shape[0]:
         raise ValueError("number of new rows does not match the plan")
@@ -73,13 +80,15 @@ def merged_cache(segs, cached: dict, k_new, v_new, key_layout="position_free"):
 
 
 def link_attention(segs, cached: dict, q_new, k_new, v_new, rope_theta, rows=None,
-                   key_layout="position_free"):
+                   key_layout="position_free", compile_offset=0):
     """Outputs [R'][Hq][d] and lse [R'][Hq] (fp64) of the recomputed rows.
 
     ``rows`` optionally restricts the computation to a subset of row indices
     (for sampled checks at full size); the merged cache is always complete.
     """
-    k, v, key_pos, key_rot = merged_cache(segs, cached, k_new, v_new, key_layout)
+    if compile_offset < 0:
+        raise ValueError("compile_offset must be >= 0")
+    k, v, key_pos, key_rot = merged_cache(segs, cached, k_new, v_new, key_layout, compile_offset)
     row_pos = np.asarray(selected_positions(segs), dtype=np.int64)
     q = np.asarray(q_new, dtype=np.float64)
     if rows is not None:

@@ -217,6 +217,30 @@ def test_keys_compiled_from_zero_equal_position_free(case):
         assert np.abs(wrong - base).max() > 1e-3
 
 
+@pytest.mark.parametrize("offset", [4, 7])
+@pytest.mark.parametrize("case", [0, 1, 3, 4, 6, 8])
+def test_keys_compiled_after_dummy_tokens_equal_position_free(case, offset):
+    """LegoLink-0's compile step puts c dummy tokens first and drops their KV (EPIC summary,
+    "Measured effects" table), so token j of a chunk is encoded at position c + j. Keys handed
+    over rotated at c + j (complex multiplication here) and re-rotated by the segment's start
+    minus c, negative for a chunk linked before position c, give the position-free result:
+    R(start - c) R(c + j) = R(start + j). Read with c = 0 they give another."""
+    req = tiny_request(700 + case, **CASES[case])
+    base, base_lse = run_oracle(req)
+    compiled = {cid: (_rotate_complex(k, offset + np.arange(k.shape[0]), req["theta"]), v)
+                for cid, (k, v) in req["cached"].items()}
+    out, lse = olink.link_attention(req["segs"], compiled, req["q"], req["k"], req["v"], req["theta"],
+                                    key_layout="segment_rope", compile_offset=offset)
+    assert np.abs(out - base).max() < 1e-12
+    assert np.abs(lse - base_lse).max() < 1e-12
+    cached_pos = [s.start + j for s in req["segs"] if s.kind != "suffix" for j in range(s.recompute, s.length)]
+    sel = oplan.selected_positions(req["segs"])
+    if cached_pos and sel and min(cached_pos) <= max(sel):      # some row attends a cached key
+        wrong, _ = olink.link_attention(req["segs"], compiled, req["q"], req["k"], req["v"], req["theta"],
+                                        key_layout="segment_rope")
+        assert np.abs(wrong - base).max() > 1e-3
+
+
 def test_first_chunk_rows_ignore_cached_values():
     req = tiny_request(7, prefix_len=0, chunk_lens=(10, 12), k=4, page_size=4)
     base, _ = run_oracle(req)
