@@ -87,7 +87,15 @@ typedef struct pic_plan pic_plan;
  *                 its absolute linked position t. PIC_KEYS_SEGMENT_ROPE: a key stored at
  *                 position s of its segment holds R(s)k, and is re-rotated by the segment's
  *                 linked start a (R(a)R(s)k = R(a + s)k, the RoPE composition rule). Both give
- *                 the same attention up to rounding. Other values: PIC_ERR_INVALID. */
+ *                 the same attention up to rounding. Other values: PIC_ERR_INVALID.
+ *   compile_offset  PIC_KEYS_SEGMENT_ROPE stores: the position of a chunk's first token when it
+ *                 was compiled, c in [0, 4096]. A compile step that puts c leading tokens first and
+ *                 drops their KV (LegoLink-0 prepends four dummy tokens: EPIC summary, "Measured
+ *                 effects" table) leaves token j's key rotated at c + j; the link step then
+ *                 re-rotates a segment's keys by its start a minus c, a negative angle when
+ *                 a < c, and writes new keys rotated at c + their position in the segment.
+ *                 Every segment's c + length must stay below max_position. No effect in a
+ *                 PIC_KEYS_POSITION_FREE store (its keys carry no position). */
 typedef struct {
     int32_t num_q_heads;
     int32_t num_kv_heads;
@@ -98,6 +106,7 @@ typedef struct {
     double rope_theta;
     int32_t max_position;
     int32_t key_layout;
+    int32_t compile_offset;
 } pic_store_config;
 
 /* One prompt to link: [prefix] chunk_ids[0..n_chunks) [suffix of suffix_len new tokens].

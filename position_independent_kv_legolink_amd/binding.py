@@ -41,7 +41,7 @@ class StoreConfig(ctypes.Structure):
                 ("head_dim", ctypes.c_int32), ("page_size", ctypes.c_int32),
                 ("num_pages", ctypes.c_int32), ("dtype", ctypes.c_int32),
                 ("rope_theta", ctypes.c_double), ("max_position", ctypes.c_int32),
-                ("key_layout", ctypes.c_int32)]
+                ("key_layout", ctypes.c_int32), ("compile_offset", ctypes.c_int32)]
 
 
 # how stored keys carry position: pre-RoPE, or rotated at their position inside their segment
@@ -156,15 +156,17 @@ class Store:
 
     With ``device=None`` the store holds metadata only (host planning, tests
     without a GPU). ``key_layout`` is "position_free" (stored keys are pre-RoPE)
-    or "segment_rope" (a chunk's token j holds its key rotated at position j).
+    or "segment_rope" (a chunk's token j holds its key rotated at position
+    ``compile_offset + j``: 0 for a chunk compiled from position 0, 4 for
+    LegoLink-0's four dummy tokens).
     """
 
     def __init__(self, *, num_q_heads, num_kv_heads, head_dim, page_size, num_pages, dtype,
-                 rope_theta, max_position, device="cuda", key_layout="position_free"):
+                 rope_theta, max_position, device="cuda", key_layout="position_free", compile_offset=0):
         if key_layout not in KEY_LAYOUTS:
             raise ValueError(f"key_layout must be one of {sorted(KEY_LAYOUTS)}")
         self.cfg = StoreConfig(num_q_heads, num_kv_heads, head_dim, page_size, num_pages, DTYPES[dtype],
-                               float(rope_theta), max_position, KEY_LAYOUTS[key_layout])
+                               float(rope_theta), max_position, KEY_LAYOUTS[key_layout], int(compile_offset))
         self.key_layout = key_layout
         self.dtype = dtype
         self.device = device

@@ -64,6 +64,9 @@ void store_check_config(const pic_store_config &c) {
         fail(PIC_ERR_INVALID, "max_position must be in [1, " + std::to_string(kMaxPosition) + "]");
     if (c.key_layout != PIC_KEYS_POSITION_FREE && c.key_layout != PIC_KEYS_SEGMENT_ROPE)
         fail(PIC_ERR_INVALID, "key_layout must be PIC_KEYS_POSITION_FREE or PIC_KEYS_SEGMENT_ROPE");
+    if (c.compile_offset < 0 || c.compile_offset > kMaxCompileOffset || c.compile_offset >= c.max_position)
+        fail(PIC_ERR_INVALID, "compile_offset must be in [0, " + std::to_string(kMaxCompileOffset) +
+                                  "] and below max_position");
 }
 
 int32_t store_alloc_page(pic_store *s) {

@@ -217,6 +217,7 @@ __global__ __launch_bounds__(512, 1) void link_attention_bf16(AttnParams p) {
     // ---- staging registers of one key tile (global -> registers -> LDS)
     u32x4 k_lo[NKP], k_hi[NKP];
     int k_pos[NKP];
+    uint32_t k_sgn[NKP];               // SEG: sign bit of the rotation (a negative angle flips the sines)
     floatx4 k_c[NKP][2], k_s[NKP][2];
     u32x4 v_r[NVC];
     u32x4 k_olo[NKP], k_ohi[NKP];      // rotated K halves on their way to LDS
@@ -309,8 +310,15 @@ __global__ __launch_bounds__(512, 1) void link_attention_bf16(AttnParams p) {
                     const bool ok = (KPAIRS % NT == 0 || pi < KPAIRS) && rk_in[u] && k_slot[u] < valid;
                     // the cos/sin row of the key's rotation (padding slots hold zeros, which
                     // rotate to zeros with any row)
-                    if constexpr (SEG) k_pos[u] = __builtin_amdgcn_readfirstlane(rk_seg[u]);
-                    else k_pos[u] = ok ? pos0 + k_slot[u] : pos0;
+                    if constexpr (SEG) {
+                        // the segment's rotation may be negative (keys compiled after leading tokens
+                        // linked before them): the row of its magnitude, sines negated
+                        const int r = __builtin_amdgcn_readfirstlane(rk_seg[u]);
+                        k_pos[u] = r < 0 ? -r : r;
+                        k_sgn[u] = r < 0 ? 0x80000000u : 0u;
+                    } else {
+                        k_pos[u] = ok ? pos0 + k_slot[u] : pos0;
+                    }
                 }
                 k_page[u] = kpool_b + (uint64_t)phys * page_bytes;
                 k_lo[u] = *reinterpret_cast<const u32x4 *>(k_page[u] + k_loff[u]);
@@ -329,9 +337,13 @@ __global__ __launch_bounds__(512, 1) void link_attention_bf16(AttnParams p) {
 #pragma unroll
             for (int u = 0; u < NKP; ++u) {
                 const uint32_t off = (uint32_t)k_pos[u] * (uint32_t)(D * 4) + k_cs_off[u];
-                const floatx4 v = *reinterpret_cast<const floatx4 *>(rope_b + off + (q >> 1) * (D * 2) + (q & 1) * 16);
-                if (q < 2) k_c[u][q & 1] = v;
-                else k_s[u][q & 1] = v;
+                floatx4 v = *reinterpret_cast<const floatx4 *>(rope_b + off + (q >> 1) * (D * 2) + (q & 1) * 16);
+                if (q < 2) {
+                    k_c[u][q & 1] = v;
+                } else {
+                    if constexpr (SEG) v = __builtin_bit_cast(floatx4, __builtin_bit_cast(u32x4, v) ^ k_sgn[u]);
+                    k_s[u][q & 1] = v;
+                }
             }
         }
     };
@@ -864,15 +876,17 @@ __global__ __launch_bounds__(kThreads, 1) void link_attention_f32(AttnParams p) 
                 const PageDesc pd = pg[lp];
                 if (slot < pd.valid) {
                     ok = true;
-                    pos = p.seg_keys ? pd.seg0 : pd.pos0 + slot;   // cos/sin row of the rotation
+                    pos = p.seg_keys ? pd.seg0 : pd.pos0 + slot;   // the rotation (negative: see below)
                     base = (int64_t)pd.phys * p.page_elems + head_off + (int64_t)slot * D;
                 }
             }
             k_lo[u] = ok ? *reinterpret_cast<const floatx4 *>(kpool + base + 4 * c) : floatx4{0, 0, 0, 0};
             k_hi[u] = ok ? *reinterpret_cast<const floatx4 *>(kpool + base + D / 2 + 4 * c) : floatx4{0, 0, 0, 0};
-            const float *cs = p.rope + (int64_t)pos * D + 4 * c;
+            // a negative rotation takes the row of its magnitude with the sines negated
+            const float *cs = p.rope + (int64_t)(pos < 0 ? -pos : pos) * D + 4 * c;
             k_c[u] = *reinterpret_cast<const floatx4 *>(cs);
             k_s[u] = *reinterpret_cast<const floatx4 *>(cs + D / 2);
+            if (pos < 0) k_s[u] = -k_s[u];
         }
 #pragma unroll
         for (int u = 0; u < NV; ++u) {
@@ -1206,11 +1220,18 @@ __global__ __launch_bounds__(kThreads) void rotate_keys_bf16(const PageDesc *pag
         const bool valid = slot < pd.valid;
         floatx4 co[2] = {}, sn[2] = {};
         if (valid) {
-            const float *cs = rope + (int64_t)(seg_keys ? pd.seg0 : pd.pos0 + slot) * D + 8 * c;
+            // a negative rotation (keys compiled after leading tokens, linked before them) takes the
+            // row of its magnitude with the sines negated, as the attention kernels do
+            const int rot = seg_keys ? pd.seg0 : pd.pos0 + slot;
+            const float *cs = rope + (int64_t)(rot < 0 ? -rot : rot) * D + 8 * c;
             co[0] = *reinterpret_cast<const floatx4 *>(cs);
             co[1] = *reinterpret_cast<const floatx4 *>(cs + 4);
             sn[0] = *reinterpret_cast<const floatx4 *>(cs + D / 2);
             sn[1] = *reinterpret_cast<const floatx4 *>(cs + D / 2 + 4);
+            if (rot < 0) {
+                sn[0] = -sn[0];
+                sn[1] = -sn[1];
+            }
         }
         for (int h0 = hg; h0 < hkv; h0 += HB * n_hg) {
             u32x4 lo[HB], hi[HB];

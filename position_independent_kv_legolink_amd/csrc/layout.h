@@ -12,14 +12,16 @@ struct PageDesc {
     int32_t phys;    // physical page id in the pools
     int32_t pos0;    // absolute position of slot 0
     int32_t valid;   // slots [0, valid) hold tokens, the rest are padding
-    int32_t seg0;    // absolute position of the first token of the page's segment
+    int32_t seg0;    // keys rotated inside their segment: the rotation that places them, the
+                     // segment's start minus the store's compile offset (negative when the segment
+                     // starts before that offset)
 };
 
 // One private page written by the scatter kernel before attention:
 // slots [0, n_new) take new rows row0.., slots [n_new, n_valid) are copied
 // from page `src` (copy-on-write, src >= 0), slots [n_valid, page) are zeroed.
-// local0 is slot 0's position inside its segment (the rotation of new keys in a
-// store whose keys are rotated at their position inside their segment).
+// local0 is the rotation of slot 0's new key in a store whose keys are rotated at their position
+// inside their segment: that position plus the store's compile offset.
 struct ScatterDesc {
     int32_t dst;
     int32_t src;
@@ -73,7 +75,9 @@ struct DecodeReq {
     int32_t pos;
     int32_t lpage0;
     int32_t off;
-    int32_t seg0;    // absolute position of the first token of the segment holding the slots
+    int32_t seg0;    // start of the segment holding the slots minus the store's compile offset: a decode
+                     // key at position p is written rotated at p - seg0 in a store of keys rotated
+                     // inside their segment
 };
 
 // Combine the partial results of one (request, KV head) with the new token's own key.
@@ -89,6 +93,8 @@ constexpr int kMaxItemPages = 2048;  // longest KV range of one attention work i
 // Positions are packed with a page's valid count into one 32-bit word (pos0 << 7 | valid) and
 // cos/sin rows are addressed with 32-bit byte offsets: both hold below this bound.
 constexpr int kMaxPosition = 1 << 22;
+// Largest compile offset (leading tokens a chunk was compiled after) a store takes.
+constexpr int kMaxCompileOffset = 4096;
 constexpr int kThreads = 256;      // page writers, merge and the fp32 attention kernel
 // Automatic key rotation mode: rotate once per link call when the work list reads each key page
 // at least this many times on average (else inside attention). The rotation pass costs about as

@@ -49,6 +49,9 @@ pic_plan *build_plan(pic_store *s, const pic_request *reqs, int32_t n_reqs, cons
     if (o.decode && o.rope_keys == 1)
         fail(PIC_ERR_INVALID, "decode reads keys rotated ahead of attention: rope_keys must be 0 or 2");
 
+    // keys rotated inside their segment carry the compile offset on top of their position there
+    const int32_t c_off = cfg.key_layout == PIC_KEYS_SEGMENT_ROPE ? cfg.compile_offset : 0;
+
     // ---- pass 1: segments, validation and private-page count
     std::vector<std::vector<Seg>> all(n_reqs);
     std::vector<int32_t> ends(n_reqs);   // position after each request's last token
@@ -87,6 +90,11 @@ pic_plan *build_plan(pic_store *s, const pic_request *reqs, int32_t n_reqs, cons
         if (pos > cfg.max_position)
             fail(PIC_ERR_INVALID, "request " + std::to_string(r) + " reaches position " + std::to_string(pos - 1) +
                                       " but the store's RoPE table ends at " + std::to_string(cfg.max_position - 1));
+        for (const Seg &g : segs)
+            if ((int64_t)c_off + g.length > cfg.max_position)
+                fail(PIC_ERR_INVALID, "request " + std::to_string(r) + ": a segment of " + std::to_string(g.length) +
+                                          " tokens after the compile offset " + std::to_string(c_off) +
+                                          " passes the store's RoPE table");
 
         for (const Seg &g : segs) {
             if (g.suffix) private_needed += (g.length + B - 1) / B;
@@ -125,14 +133,15 @@ pic_plan *build_plan(pic_store *s, const pic_request *reqs, int32_t n_reqs, cons
                         plan->page_refs.push_back(src);
                     }
                     // slots past the new rows are copied from the stored page, or zeroed
-                    plan->scatter.push_back({dst, src, n_new, seg_row0 + q * B, src >= 0 ? valid : n_new, q * B, 0, 0});
+                    plan->scatter.push_back(
+                        {dst, src, n_new, seg_row0 + q * B, src >= 0 ? valid : n_new, q * B + c_off, 0, 0});
                     phys[q] = dst;
                 } else {
                     phys[q] = g.chunk->pages[q];
                     store_ref(s, phys[q]);
                 }
                 plan->page_refs.push_back(phys[q]);
-                plan->pages.push_back({phys[q], (int32_t)(g.start + (int64_t)q * B), valid, (int32_t)g.start});
+                plan->pages.push_back({phys[q], (int32_t)(g.start + (int64_t)q * B), valid, (int32_t)(g.start - c_off)});
             }
             for (int j = 0; j < g.recompute; ++j) {
                 plan->row_pos.push_back((int32_t)(g.start + j));
@@ -248,7 +257,8 @@ pic_plan *build_plan(pic_store *s, const pic_request *reqs, int32_t n_reqs, cons
             // the decode tokens sit in the request's last segment, after its suffix rows
             const Seg &g = all[r].back();
             const int32_t seg_pages = (g.length + B - 1) / B;
-            plan->dec_req.push_back({ends[r], plan->cu_pages[r + 1] - seg_pages, g.length - o.decode, (int32_t)g.start});
+            plan->dec_req.push_back(
+                {ends[r], plan->cu_pages[r + 1] - seg_pages, g.length - o.decode, (int32_t)(g.start - c_off)});
         }
         // a range's page table sits in LDS: at most kMaxItemPages pages
         const int64_t per_item = std::min<int64_t>(

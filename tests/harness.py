@@ -115,14 +115,16 @@ class Workload:
         return rows
 
 
-def gpu_store(cfg, cached: dict, *, num_pages, max_position, device="cuda", key_layout="position_free"):
+def gpu_store(cfg, cached: dict, *, num_pages, max_position, device="cuda", key_layout="position_free",
+              compile_offset=0):
     """A store holding ``cached``. With key_layout "segment_rope" the same seeded keys are
-    taken as keys compiled from position 0 (already rotated inside their segment)."""
+    taken as keys compiled from position ``compile_offset`` (already rotated inside their
+    segment)."""
     import torch
     store = pic.Store(num_q_heads=cfg.num_q_heads, num_kv_heads=cfg.num_kv_heads, head_dim=cfg.head_dim,
                       page_size=cfg.page_size, num_pages=num_pages, dtype=cfg.dtype,
                       rope_theta=cfg.rope_theta, max_position=max_position, device=device,
-                      key_layout=key_layout)
+                      key_layout=key_layout, compile_offset=compile_offset)
     tdt = torch.bfloat16 if cfg.dtype == "bf16" else torch.float32
     for cid, (k, v) in cached.items():
         store.store_chunk(cid, torch.from_numpy(k).to(device=device, dtype=tdt).contiguous(),
@@ -130,12 +132,13 @@ def gpu_store(cfg, cached: dict, *, num_pages, max_position, device="cuda", key_
     return store
 
 
-def oracle_outputs(seg_lists, cached, rows, theta, sample=None, key_layout="position_free"):
+def oracle_outputs(seg_lists, cached, rows, theta, sample=None, key_layout="position_free", compile_offset=0):
     """fp64 oracle outputs per request; ``sample`` maps request index -> row indices."""
     outs = []
     for i, (segs, (q, k, v)) in enumerate(zip(seg_lists, rows)):
         sel = None if sample is None else sample.get(i)
-        outs.append(olink.link_attention(segs, cached, q, k, v, theta, rows=sel, key_layout=key_layout))
+        outs.append(olink.link_attention(segs, cached, q, k, v, theta, rows=sel, key_layout=key_layout,
+                                         compile_offset=compile_offset))
     return outs
 
 

@@ -312,3 +312,24 @@ def test_usage_counts_pages_held_only_by_plans():
     plan.free()
     assert _usage_consistent(s)["pages_free"] == 16
     s.close()
+
+
+def test_compile_offset_is_validated():
+    """A store's compile offset (keys compiled after leading tokens) must lie in [0, 4096] and below
+    max_position, and no segment may reach past the RoPE table once it is added."""
+    for bad in (-1, 4097):
+        with pytest.raises(pic.PicError):
+            meta(key_layout="segment_rope", compile_offset=bad)
+    with pytest.raises(pic.PicError):
+        meta(key_layout="segment_rope", compile_offset=4, max_position=4)
+    s = meta(key_layout="segment_rope", compile_offset=70, max_position=130)
+    s.store_chunk(1, n_tokens=64)
+    s.store_chunk(2, n_tokens=60)
+    with pytest.raises(pic.PicError):          # 70 + 64 > 130: the scatter would pass the table
+        s.link_plan([pic.LinkRequest([1], 0)], k=2)
+    plan = s.link_plan([pic.LinkRequest([2], 0)], k=2)   # 70 + 60 = 130 fits
+    plan.free()
+    # no effect on position-free stores beyond validation
+    p = meta(compile_offset=4)
+    p.store_chunk(1, n_tokens=64)
+    p.link_plan([pic.LinkRequest([1], 10)], k=2).free()

@@ -66,7 +66,7 @@ def rotate_at(x, pos, theta):
 
 
 def run_decode(cfg, *, n_requests=None, pos_offset=0, repeat=1, with_oracle=True, steps=1,
-               key_layout="position_free"):
+               key_layout="position_free", compile_offset=0):
     wl = Workload(cfg, n_requests=n_requests)
     segs = wl.segments(pos_offset=pos_offset, k=cfg.k)
     cached = wl.cached()
@@ -77,7 +77,8 @@ def run_decode(cfg, *, n_requests=None, pos_offset=0, repeat=1, with_oracle=True
     n_tokens = max(oplan.total_tokens(s) for s in segs)
     decode_pages = len(segs) * (-(-steps // B) + 1)
     store = gpu_store(cfg, cached, num_pages=stored + private + decode_pages + 8,
-                      max_position=pos_offset + n_tokens + steps + 1, key_layout=key_layout)
+                      max_position=pos_offset + n_tokens + steps + compile_offset + 1, key_layout=key_layout,
+                      compile_offset=compile_offset)
     plan = store.link_plan(wl.link_requests(), k=cfg.k, block_level=cfg.block_level, pos_offset=pos_offset,
                            decode=steps)
     n = len(segs)
@@ -107,7 +108,7 @@ def run_decode(cfg, *, n_requests=None, pos_offset=0, repeat=1, with_oracle=True
                               for c in range(3)) for a, r in enumerate(rows)]
             sample = {a: np.array([len(oplan.selected_positions(s)) - 1]) for a, s in enumerate(ext)}
             results[i][2] = oracle_outputs(ext, cached, ext_rows, cfg.rope_theta, sample=sample,
-                                           key_layout=key_layout)
+                                           key_layout=key_layout, compile_offset=compile_offset)
     # every step wrote its token's key into the token's decode slot of the pool, in the store's
     # key form: pre-RoPE, or rotated at the token's position inside its segment
     ex = plan.export()
@@ -123,7 +124,7 @@ def run_decode(cfg, *, n_requests=None, pos_offset=0, repeat=1, with_oracle=True
             got = kp[phys, :, slot % B]
             want = tokens[i][1][a].astype(np.float64)
             if key_layout == "segment_rope":
-                want = rotate_at(want, end + i - seg0, cfg.rope_theta)
+                want = rotate_at(want, end + i - seg0 + compile_offset, cfg.rope_theta)
                 assert np.all(np.abs(got - want) <= 2.0 ** -8 * np.abs(want) + 1e-6), f"decode slot {a}/{i}"
             else:
                 assert np.array_equal(got, want), f"decode slot {a}/{i}"

@@ -40,7 +40,7 @@ def _need_gpu():
 
 def run_workload(cfg, *, n_requests=None, sample_rows=None, pos_offset=0, split_pages=0, k=None,
                  recompute_all=False, seed=0, check_plan=True, repeat=1, lse=True, num_pages=None, rope_keys=0,
-                 with_oracle=True, key_layout="position_free"):
+                 with_oracle=True, key_layout="position_free", compile_offset=0):
     """Link a config's requests on the GPU; return (gpu outs, oracle outs or None, extras)."""
     wl = Workload(cfg, n_requests=n_requests)
     kk = cfg.k if k is None else k
@@ -51,7 +51,8 @@ def run_workload(cfg, *, n_requests=None, sample_rows=None, pos_offset=0, split_
     stored = sum(-(-v[0].shape[0] // B) for v in cached.values())
     n_tokens = max(oplan.total_tokens(s) for s in segs)
     store = gpu_store(cfg, cached, num_pages=num_pages or (stored + private + 8),
-                      max_position=pos_offset + n_tokens + 1, key_layout=key_layout)
+                      max_position=pos_offset + n_tokens + compile_offset + 1, key_layout=key_layout,
+                      compile_offset=compile_offset)
     plan = store.link_plan(wl.link_requests(), k=kk, block_level=cfg.block_level, pos_offset=pos_offset,
                            recompute_all=recompute_all, split_pages=split_pages, rope_keys=rope_keys)
     if check_plan:
@@ -78,8 +79,8 @@ def run_workload(cfg, *, n_requests=None, sample_rows=None, pos_offset=0, split_
             R = len(oplan.selected_positions(s))
             pick = {0, R - 1, R // 2} | set(int(x) for x in g.integers(0, R, size=max(0, sample_rows - 3)))
             sample[i] = np.array(sorted(x for x in pick if 0 <= x < R), dtype=np.int64)
-    want = (oracle_outputs(segs, cached, rows, cfg.rope_theta, sample=sample, key_layout=key_layout)
-            if with_oracle else None)
+    want = (oracle_outputs(segs, cached, rows, cfg.rope_theta, sample=sample, key_layout=key_layout,
+                           compile_offset=compile_offset) if with_oracle else None)
     extras = dict(store=store, plan=plan, export=ex, segs=segs, cached=cached, rows=rows, sample=sample,
                   lse=got_lse, outs=outs)
     return outs[0], want, extras
