@@ -13,18 +13,66 @@ import numpy as np
 _HERE = os.path.dirname(os.path.abspath(__file__))
 SOURCE = os.path.join(_HERE, "attention.c")
 LIBRARY = os.path.join(_HERE, "liboracle_attention.so")
+MODEL_SOURCE = os.path.join(_HERE, "model.c")
+MODEL_LIBRARY = os.path.join(_HERE, "liboracle_model.so")
 _lib = None
+_model = None
+
+
+def _compile(source, library, force):
+    if not force and os.path.exists(library) and os.path.getmtime(library) >= os.path.getmtime(source):
+        return library
+    tmp = library + ".tmp"
+    subprocess.run(["gcc", "-O2", "-fopenmp", "-fPIC", "-shared", "-std=c11", "-Wall",
+                    "-o", tmp, source, "-lm"], check=True)
+    os.replace(tmp, library)
+    return library
 
 
 def build(force: bool = True) -> str:
     """Compile the oracle with gcc (-O2, OpenMP, no fast-math) into oracle/."""
-    if not force and os.path.exists(LIBRARY) and os.path.getmtime(LIBRARY) >= os.path.getmtime(SOURCE):
-        return LIBRARY
-    tmp = LIBRARY + ".tmp"
-    subprocess.run(["gcc", "-O2", "-fopenmp", "-fPIC", "-shared", "-std=c11", "-Wall",
-                    "-o", tmp, SOURCE, "-lm"], check=True)
-    os.replace(tmp, LIBRARY)
-    return LIBRARY
+    _compile(MODEL_SOURCE, MODEL_LIBRARY, force)
+    return _compile(SOURCE, LIBRARY, force)
+
+
+def model_lib():
+    global _model
+    if _model is None:
+        _compile(MODEL_SOURCE, MODEL_LIBRARY, False)
+        L = ctypes.CDLL(MODEL_LIBRARY)
+        L.oracle_linear.restype = None
+        L.oracle_linear.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p,
+                                    ctypes.c_void_p]
+        L.oracle_rmsnorm.restype = None
+        L.oracle_rmsnorm.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_double,
+                                     ctypes.c_void_p]
+        _model = L
+    return _model
+
+
+def linear(a, w):
+    """y = a W^T in fp64 with explicit loops (oracle/model.c): a [m][k], w [n][k] -> [m][n]."""
+    a = np.ascontiguousarray(a, dtype=np.float64)
+    w = np.ascontiguousarray(w, dtype=np.float64)
+    m, k = a.shape
+    n, k2 = w.shape
+    if k != k2:
+        raise ValueError("shape mismatch")
+    out = np.empty((m, n), dtype=np.float64)
+    model_lib().oracle_linear(m, n, k, a.ctypes.data, w.ctypes.data, out.ctypes.data)
+    return out
+
+
+def rmsnorm(x, w, eps):
+    """x / sqrt(mean(x^2) + eps) * w per row, fp64 (oracle/model.c)."""
+    x = np.ascontiguousarray(x, dtype=np.float64)
+    w = np.ascontiguousarray(w, dtype=np.float64)
+    rows, dm = x.shape
+    if w.shape != (dm,):
+        raise ValueError("shape mismatch")
+    out = np.empty_like(x)
+    model_lib().oracle_rmsnorm(rows, dm, x.ctypes.data, w.ctypes.data, float(eps), out.ctypes.data)
+    return out
 
 
 def load(path: str):
