@@ -95,7 +95,10 @@ typedef struct pic_plan pic_plan;
  *                 re-rotates a segment's keys by its start a minus c, a negative angle when
  *                 a < c, and writes new keys rotated at c + their position in the segment.
  *                 Every segment's c + length must stay below max_position. No effect in a
- *                 PIC_KEYS_POSITION_FREE store (its keys carry no position). */
+ *                 PIC_KEYS_POSITION_FREE store (its keys carry no position).
+ *   num_layers    decoder layers the store holds K/V for, in [0, 1024] (0 means 1). Each pool is
+ *                 [num_layers][num_pages][Hkv][page][d]: every layer holds a chunk's tokens on the
+ *                 same page ids, so one plan serves every layer. */
 typedef struct {
     int32_t num_q_heads;
     int32_t num_kv_heads;
@@ -107,6 +110,7 @@ typedef struct {
     int32_t max_position;
     int32_t key_layout;
     int32_t compile_offset;
+    int32_t num_layers;
 } pic_store_config;
 
 /* One prompt to link: [prefix] chunk_ids[0..n_chunks) [suffix of suffix_len new tokens].
@@ -196,7 +200,8 @@ pic_status pic_store_destroy(pic_store *store);
 /* Compile-step product in: store the K and V of one chunk (EPIC summary,
  * "Approach": each chunk compiled independently from position 0; MEPIC
  * abstract: KV kept without positional encoding, page aligned).
- * k, v: device [n_tokens][Hkv][d] of the store dtype. K is pre-RoPE in a
+ * k, v: device [num_layers][n_tokens][Hkv][d] of the store dtype (every layer's K/V
+ * of the chunk; [n_tokens][Hkv][d] for a single-layer store). K is pre-RoPE in a
  * PIC_KEYS_POSITION_FREE store; in a PIC_KEYS_SEGMENT_ROPE store token j's key
  * is already rotated at position j (rotate-half pairs (i, i + d/2), angle
  * j * theta^(-2i/d)), as compiling the chunk from position 0 produces it.
@@ -313,6 +318,65 @@ pic_status pic_plan_upload(pic_store *store, pic_plan *plan, void *workspace, in
 pic_status pic_link_attend(pic_store *store, const pic_plan *plan, const void *q_new, const void *k_new,
                            const void *v_new, void *out, float *lse, void *workspace, int64_t workspace_bytes,
                            hipStream_t stream);
+
+/* pic_link_attend on one layer of a multi-layer store: the same steps over that layer's K/V
+ * pools (the plan's pages, private pages and rotated keys are those of the layer).
+ * pic_link_attend is layer 0. Errors: PIC_ERR_INVALID (layer outside [0, num_layers)) and
+ * those of pic_link_attend. */
+pic_status pic_link_attend_layer(pic_store *store, const pic_plan *plan, int32_t layer, const void *q_new,
+                                 const void *k_new, const void *v_new, void *out, float *lse, void *workspace,
+                                 int64_t workspace_bytes, hipStream_t stream);
+
+/* ---- Decoder layers around the link step (synthetic weights; EPIC summary, "Key results"
+ * and "Limitations": the recomputed rows run through a 7-9B Llama-class model).
+ * The selected rows' hidden states go through every layer of the store:
+ *   h = RMSNorm(x) * attn_norm;  q, k, v = h W_qkv^T (split by heads);
+ *   a = link attention of the layer (scatter of k, v; causal RoPE attention of q over the layer's
+ *       linked cache);  x = x + a W_o^T;
+ *   h = RMSNorm(x) * mlp_norm;  x = x + (SiLU(h W_gate^T) * (h W_up^T)) W_down^T.
+ * RMSNorm(x) = x / sqrt(mean(x^2) + norm_eps). Every tensor is bfloat16 in device memory,
+ * row-major; products accumulate in float32 and are rounded to bfloat16 once per output. */
+typedef struct {
+    int32_t d_model;   /* hidden size: num_q_heads * head_dim, a multiple of 128 */
+    int32_t d_ff;      /* MLP width, a multiple of 64 */
+    float norm_eps;
+} pic_model_config;
+
+/* One layer's weights, device bfloat16, each [out features][in features]. */
+typedef struct {
+    const void *attn_norm;   /* [d_model] */
+    const void *w_qkv;       /* [(Hq + 2 Hkv) d][d_model]: query heads, then key heads, then value heads */
+    const void *w_o;         /* [d_model][Hq d] */
+    const void *mlp_norm;    /* [d_model] */
+    const void *w_gate_up;   /* [2 d_ff][d_model]: rows alternate 32 gate rows and 32 up rows */
+    const void *w_down;      /* [d_model][d_ff] */
+} pic_layer_weights;
+
+/* Device bytes pic_link_forward needs: the plan's workspace, then the activations of the
+ * selected rows (normed input, q, k, v, attention output, MLP hidden). */
+pic_status pic_forward_workspace(const pic_store *store, const pic_plan *plan, const pic_model_config *model,
+                                 int64_t *bytes);
+
+/* Every layer of a bfloat16 store over the plan's selected rows, in order. x [rows][d_model]
+ * holds the rows' hidden states entering layer 0 and is overwritten with those leaving the last
+ * layer. layers: num_layers entries (host array of device pointers). workspace: at least
+ * pic_forward_workspace bytes, 256-byte aligned; its first bytes serve as the plan's workspace
+ * (the tables are copied in when it does not hold them). Errors, before any launch:
+ * PIC_ERR_INVALID (shapes the kernels do not take, null weights, float32 store),
+ * PIC_ERR_WORKSPACE, PIC_ERR_STATE (metadata-only store). Asynchronous on `stream`. */
+pic_status pic_link_forward(pic_store *store, const pic_plan *plan, const pic_model_config *model,
+                            const pic_layer_weights *layers, void *x, void *workspace, int64_t workspace_bytes,
+                            hipStream_t stream);
+
+/* The layers' building blocks, on their own (bfloat16, device, row-major, asynchronous):
+ * out [m][n] = a [m][k] w^T (w [n][k]) with epilogue 0: nothing, 1: + residual [m][n] (may be
+ * out), 2: w's rows alternate 32 gate and 32 up rows and out [m][n/2] = SiLU(gate) * up;
+ * n a multiple of 128, k of 64. PIC_ERR_INVALID otherwise. */
+pic_status pic_linear(const void *a, const void *w, void *out, int32_t m, int32_t n, int32_t k, int32_t epilogue,
+                      const void *residual, hipStream_t stream);
+/* y [rows][dm] = x / sqrt(mean(x^2) + eps) * w; dm a multiple of 8, at most 8,192. */
+pic_status pic_rmsnorm(const void *x, const void *w, void *y, int32_t rows, int32_t dm, float eps,
+                       hipStream_t stream);
 
 /* Bytes of the library's static device scratch: the largest plan workspace that
  * pic_link_attend_static takes. */

@@ -24,8 +24,9 @@ DTYPES = {"bf16": 0, "f32": 1}
 EXPORTS = ["pic_store_sizes", "pic_store_create", "pic_store_destroy", "pic_store_chunk",
            "pic_store_chunk_pages", "pic_store_release", "pic_store_evict", "pic_store_usage", "pic_store_stats",
            "pic_link_plan",
-           "pic_plan_info", "pic_plan_export", "pic_plan_upload", "pic_link_attend", "pic_link_attend_static",
-           "pic_link_decode",
+           "pic_plan_info", "pic_plan_export", "pic_plan_upload", "pic_link_attend", "pic_link_attend_layer",
+           "pic_link_attend_static", "pic_link_decode", "pic_forward_workspace", "pic_link_forward", "pic_linear",
+           "pic_rmsnorm",
            "pic_plan_free",
            "pic_profile_enable", "pic_profile_read", "pic_last_error"]
 
@@ -41,11 +42,21 @@ class StoreConfig(ctypes.Structure):
                 ("head_dim", ctypes.c_int32), ("page_size", ctypes.c_int32),
                 ("num_pages", ctypes.c_int32), ("dtype", ctypes.c_int32),
                 ("rope_theta", ctypes.c_double), ("max_position", ctypes.c_int32),
-                ("key_layout", ctypes.c_int32), ("compile_offset", ctypes.c_int32)]
+                ("key_layout", ctypes.c_int32), ("compile_offset", ctypes.c_int32),
+                ("num_layers", ctypes.c_int32)]
 
 
 # how stored keys carry position: pre-RoPE, or rotated at their position inside their segment
 KEY_LAYOUTS = {"position_free": 0, "segment_rope": 1}
+
+
+class ModelConfig(ctypes.Structure):
+    _fields_ = [("d_model", ctypes.c_int32), ("d_ff", ctypes.c_int32), ("norm_eps", ctypes.c_float)]
+
+
+class LayerWeights(ctypes.Structure):
+    _fields_ = [("attn_norm", ctypes.c_void_p), ("w_qkv", ctypes.c_void_p), ("w_o", ctypes.c_void_p),
+                ("mlp_norm", ctypes.c_void_p), ("w_gate_up", ctypes.c_void_p), ("w_down", ctypes.c_void_p)]
 
 
 class Request(ctypes.Structure):
@@ -104,6 +115,11 @@ def lib():
             "pic_plan_upload": [vp, vp, vp, i64, vp],
             "pic_link_attend": [vp, vp, vp, vp, vp, vp, vp, vp, i64, vp],
             "pic_link_attend_static": [vp, vp, vp, vp, vp, vp, vp, vp],
+            "pic_link_attend_layer": [vp, vp, i32, vp, vp, vp, vp, vp, vp, i64, vp],
+            "pic_forward_workspace": [vp, vp, P(ModelConfig), P(i64)],
+            "pic_link_forward": [vp, vp, P(ModelConfig), vp, vp, vp, i64, vp],
+            "pic_linear": [vp, vp, vp, i32, i32, i32, i32, vp, vp],
+            "pic_rmsnorm": [vp, vp, vp, i32, i32, ctypes.c_float, vp],
             "pic_link_decode": [vp, vp, vp, vp, vp, vp, vp, vp, i64, vp],
             "pic_plan_free": [vp, vp],
             "pic_profile_enable": [vp, i32],
@@ -162,11 +178,14 @@ class Store:
     """
 
     def __init__(self, *, num_q_heads, num_kv_heads, head_dim, page_size, num_pages, dtype,
-                 rope_theta, max_position, device="cuda", key_layout="position_free", compile_offset=0):
+                 rope_theta, max_position, device="cuda", key_layout="position_free", compile_offset=0,
+                 num_layers=1):
         if key_layout not in KEY_LAYOUTS:
             raise ValueError(f"key_layout must be one of {sorted(KEY_LAYOUTS)}")
         self.cfg = StoreConfig(num_q_heads, num_kv_heads, head_dim, page_size, num_pages, DTYPES[dtype],
-                               float(rope_theta), max_position, KEY_LAYOUTS[key_layout], int(compile_offset))
+                               float(rope_theta), max_position, KEY_LAYOUTS[key_layout], int(compile_offset),
+                               int(num_layers))
+        self.num_layers = max(1, int(num_layers))
         self.key_layout = key_layout
         self.dtype = dtype
         self.device = device
@@ -178,6 +197,8 @@ class Store:
             _check(L.pic_store_sizes(ctypes.byref(self.cfg), ctypes.byref(pool_bytes), ctypes.byref(rope_bytes)))
             tdt = torch.bfloat16 if dtype == "bf16" else torch.float32
             shape = (num_pages, num_kv_heads, page_size, head_dim)
+            if self.num_layers > 1:
+                shape = (self.num_layers,) + shape
             self.k_pool = torch.empty(shape, dtype=tdt, device=device)
             self.v_pool = torch.empty(shape, dtype=tdt, device=device)
             self.rope_table = torch.empty((max_position, head_dim), dtype=torch.float32, device=device)
@@ -202,10 +223,13 @@ class Store:
             pass
 
     def store_chunk(self, chunk_id: int, k=None, v=None, n_tokens: int | None = None):
-        """k, v: device tensors [n][Hkv][d] of the store dtype, keys in the store's key form; or n_tokens only."""
+        """k, v: device tensors [n][Hkv][d] ([num_layers][n][Hkv][d] for a multi-layer store) of the
+        store dtype, keys in the store's key form; or n_tokens only."""
         if k is not None:
-            n_tokens = k.shape[0]
+            n_tokens = k.shape[1] if self.num_layers > 1 else k.shape[0]
             exp = (n_tokens, self.cfg.num_kv_heads, self.cfg.head_dim)
+            if self.num_layers > 1:
+                exp = (self.num_layers,) + exp
             if tuple(k.shape) != exp or tuple(v.shape) != exp or not k.is_contiguous() or not v.is_contiguous():
                 raise ValueError(f"chunk K/V must be contiguous {exp}")
             if k.dtype != self.k_pool.dtype or v.dtype != self.k_pool.dtype:
@@ -372,6 +396,112 @@ def link_attend_static(store: Store, plan: Plan, q_new, k_new, v_new, out=None, 
     out = _link_args(store, plan, q_new, k_new, v_new, out, lse)
     _check(lib().pic_link_attend_static(store.handle, plan.handle, _ptr(q_new), _ptr(k_new), _ptr(v_new), _ptr(out),
                                         _ptr(lse), _stream()))
+    return out
+
+
+def link_attend_layer(store: Store, plan: Plan, layer: int, q_new, k_new, v_new, out=None, lse=None):
+    """The link step on one layer of a multi-layer store; returns ``out``."""
+    import torch
+    out = _link_args(store, plan, q_new, k_new, v_new, out, lse)
+    if plan.workspace is None:
+        plan.workspace = torch.empty(plan.sizes["workspace_bytes"], dtype=torch.uint8, device=q_new.device)
+    ws = plan.workspace
+    _on_device(ws, "workspace")
+    _check(lib().pic_link_attend_layer(store.handle, plan.handle, int(layer), _ptr(q_new), _ptr(k_new), _ptr(v_new),
+                                       _ptr(out), _ptr(lse), _ptr(ws), _nbytes(ws), _stream()))
+    return out
+
+
+@dataclass
+class Model:
+    """Decoder layers around the link step: d_model = num_q_heads * head_dim, the MLP width
+    d_ff, the RMSNorm epsilon, and per layer a dict of device bf16 weights attn_norm [d_model],
+    w_qkv [(Hq + 2 Hkv) d][d_model], w_o [d_model][Hq d], mlp_norm [d_model],
+    w_gate_up [2 d_ff][d_model] (rows alternate 32 gate and 32 up rows), w_down [d_model][d_ff]."""
+    d_model: int
+    d_ff: int
+    norm_eps: float
+    layers: list
+
+    def config(self):
+        return ModelConfig(int(self.d_model), int(self.d_ff), float(self.norm_eps))
+
+    def weights(self):
+        arr = (LayerWeights * len(self.layers))()
+        for i, w in enumerate(self.layers):
+            for name in ("attn_norm", "w_qkv", "w_o", "mlp_norm", "w_gate_up", "w_down"):
+                t = w[name]
+                _on_device(t, name)
+                setattr(arr[i], name, t.data_ptr())
+        return arr
+
+
+def forward_workspace_bytes(store: Store, plan: Plan, model: Model) -> int:
+    n = ctypes.c_int64()
+    cfg = model.config()
+    _check(lib().pic_forward_workspace(store.handle, plan.handle, ctypes.byref(cfg), ctypes.byref(n)))
+    return n.value
+
+
+def link_forward(store: Store, plan: Plan, model: Model, x, workspace=None):
+    """The plan's selected rows through every layer of the store (pic_link_forward): ``x``
+    [rows][d_model] bf16 on the device, overwritten with the last layer's output. Returns
+    (x, workspace)."""
+    import torch
+    if len(model.layers) != store.num_layers:
+        raise ValueError("one weight set per store layer")
+    if tuple(x.shape) != (plan.rows, model.d_model) or x.dtype != torch.bfloat16 or not x.is_contiguous():
+        raise ValueError(f"x must be a contiguous bf16 tensor of shape {(plan.rows, model.d_model)}")
+    _on_device(x, "x")
+    need = forward_workspace_bytes(store, plan, model)
+    if workspace is None:
+        workspace = torch.empty(need, dtype=torch.uint8, device=x.device)
+    _on_device(workspace, "workspace")
+    cfg = model.config()
+    weights = model.weights()
+    _check(lib().pic_link_forward(store.handle, plan.handle, ctypes.byref(cfg), weights, _ptr(x), _ptr(workspace),
+                                  _nbytes(workspace), _stream()))
+    return x, workspace
+
+
+def linear(a, w, epilogue=0, residual=None, out=None):
+    """out = a w^T (epilogue 0), + residual (1), or SiLU(gate) * up of w's interleaved rows (2);
+    bf16 device tensors a [m][k], w [n][k]."""
+    import torch
+    m, k = a.shape
+    n = w.shape[0]
+    for name, t in (("a", a), ("w", w)):
+        if t.dtype != torch.bfloat16 or not t.is_contiguous():
+            raise ValueError(f"{name} must be a contiguous bf16 tensor")
+        _on_device(t, name)
+    if w.shape[1] != k:
+        raise ValueError("a and w disagree on k")
+    width = n // 2 if epilogue == 2 else n
+    if out is None:
+        out = torch.empty((m, width), dtype=torch.bfloat16, device=a.device)
+    if tuple(out.shape) != (m, width) or out.dtype != torch.bfloat16:
+        raise ValueError("out has the wrong shape or dtype")
+    _on_device(out, "out")
+    if residual is not None:
+        if tuple(residual.shape) != (m, n) or residual.dtype != torch.bfloat16 or not residual.is_contiguous():
+            raise ValueError("residual must be a contiguous bf16 tensor [m][n]")
+        _on_device(residual, "residual")
+    _check(lib().pic_linear(_ptr(a), _ptr(w), _ptr(out), m, n, k, int(epilogue), _ptr(residual), _stream()))
+    return out
+
+
+def rmsnorm(x, w, eps, out=None):
+    """x / sqrt(mean(x^2) + eps) * w per row, bf16 device tensors."""
+    import torch
+    rows, dm = x.shape
+    for name, t in (("x", x), ("w", w)):
+        if t.dtype != torch.bfloat16 or not t.is_contiguous():
+            raise ValueError(f"{name} must be a contiguous bf16 tensor")
+        _on_device(t, name)
+    if out is None:
+        out = torch.empty_like(x)
+    _on_device(out, "out")
+    _check(lib().pic_rmsnorm(_ptr(x), _ptr(w), _ptr(out), rows, dm, float(eps), _stream()))
     return out
 
 

@@ -8,7 +8,7 @@ import sys
 HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 LIBRARY = os.path.join(HERE, "libpiclink.so")
-SOURCES = ["kernels.hip", "planner.cpp", "abi.cpp"]
+SOURCES = ["kernels.hip", "model.hip", "planner.cpp", "abi.cpp", "forward.cpp"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 # Packed fp32 VALU forms are switched off for every device pass.

@@ -17,31 +17,11 @@ thread_local std::string g_last_error;
 
 void fail(pic_status status, const std::string &message) { throw Error{status, message}; }
 
-namespace {
-
-template <typename F>
-pic_status guarded(F &&f) {
-    try {
-        f();
-        return PIC_OK;
-    } catch (const Error &e) {
-        g_last_error = e.message;
-        return e.status;
-    } catch (const std::bad_alloc &) {
-        g_last_error = "host allocation failed";
-        return PIC_ERR_OOM;
-    } catch (const std::exception &e) {
-        g_last_error = e.what();
-        return PIC_ERR_INVALID;
-    } catch (...) {
-        g_last_error = "unknown error";
-        return PIC_ERR_INVALID;
-    }
-}
-
 void check_hip(hipError_t e, const char *what) {
     if (e != hipSuccess) fail(PIC_ERR_DEVICE, std::string(what) + ": " + hipGetErrorString(e));
 }
+
+namespace {
 
 int64_t elem_bytes(int32_t dtype) { return dtype == PIC_DTYPE_BF16 ? 2 : 4; }
 
@@ -64,6 +44,8 @@ void store_check_config(const pic_store_config &c) {
         fail(PIC_ERR_INVALID, "max_position must be in [1, " + std::to_string(kMaxPosition) + "]");
     if (c.key_layout != PIC_KEYS_POSITION_FREE && c.key_layout != PIC_KEYS_SEGMENT_ROPE)
         fail(PIC_ERR_INVALID, "key_layout must be PIC_KEYS_POSITION_FREE or PIC_KEYS_SEGMENT_ROPE");
+    if (c.num_layers < 0 || c.num_layers > kMaxLayers)
+        fail(PIC_ERR_INVALID, "num_layers must be in [0, " + std::to_string(kMaxLayers) + "] (0 means 1)");
     if (c.compile_offset < 0 || c.compile_offset > kMaxCompileOffset || c.compile_offset >= c.max_position)
         fail(PIC_ERR_INVALID, "compile_offset must be in [0, " + std::to_string(kMaxCompileOffset) +
                                   "] and below max_position");
@@ -149,8 +131,12 @@ void check_link_call(pic_store *s, const pic_plan *plan, const void *q_new, cons
 // The device link step over a workspace that holds the plan's tables: scatter, key rotation (when
 // the plan rotates ahead), attention and the merge of split ranges, with per-kernel events when
 // `prof`.
-void launch_link(pic_store *s, const pic_plan *plan, const void *q_new, const void *k_new, const void *v_new,
-                 void *out, float *lse, uint8_t *ws, bool prof, hipStream_t stream) {
+void launch_link(pic_store *s, const pic_plan *plan, int layer, const void *q_new, const void *k_new,
+                 const void *v_new, void *out, float *lse, uint8_t *ws, bool prof, hipStream_t stream) {
+    // the layer's pools: every layer holds the same pages at the same ids
+    const int64_t layer_bytes = s->shape.page_elems * s->cfg.num_pages * elem_bytes(s->cfg.dtype);
+    void *k_pool = static_cast<uint8_t *>(s->k_pool) + layer * layer_bytes;
+    void *v_pool = static_cast<uint8_t *>(s->v_pool) + layer * layer_bytes;
     AttnTables t;
     t.pages = reinterpret_cast<const PageDesc *>(ws + plan->off_pages);
     t.row_pos = reinterpret_cast<const int32_t *>(ws + plan->off_row_pos);
@@ -174,17 +160,17 @@ void launch_link(pic_store *s, const pic_plan *plan, const void *q_new, const vo
         }
         check_hip(hipEventRecord(marks.ev[0], stream), "hipEventRecord");
     }
-    check_hip(launch_scatter(s->shape, s->k_pool, s->v_pool, k_new, v_new, s->rope,
+    check_hip(launch_scatter(s->shape, k_pool, v_pool, k_new, v_new, s->rope,
                              reinterpret_cast<const ScatterDesc *>(ws + plan->off_scatter), (int)plan->scatter.size(),
                              stream),
               "scatter launch");
     if (prof) check_hip(hipEventRecord(marks.ev[1], stream), "hipEventRecord");
     if (plan->rotate_keys)
-        check_hip(launch_rotate_keys(s->shape, s->k_pool, s->rope, t.pages, (int)plan->pages.size(),
+        check_hip(launch_rotate_keys(s->shape, k_pool, s->rope, t.pages, (int)plan->pages.size(),
                                      const_cast<void *>(t.k_rot), stream),
                   "key rotation launch");
     if (prof) check_hip(hipEventRecord(marks.ev[2], stream), "hipEventRecord");
-    check_hip(launch_attention(s->shape, q_new, s->k_pool, s->v_pool, s->rope, t, out, lse, stream),
+    check_hip(launch_attention(s->shape, q_new, k_pool, v_pool, s->rope, t, out, lse, stream),
               "attention launch");
     if (prof) check_hip(hipEventRecord(marks.ev[3], stream), "hipEventRecord");
     check_hip(launch_merge(s->shape, t, out, lse, stream), "merge launch");
@@ -210,8 +196,8 @@ pic_status pic_store_sizes(const pic_store_config *cfg, int64_t *pool_bytes, int
         if (!cfg) fail(PIC_ERR_INVALID, "null config");
         store_check_config(*cfg);
         if (pool_bytes)
-            *pool_bytes = (int64_t)cfg->num_pages * cfg->num_kv_heads * cfg->page_size * cfg->head_dim *
-                          elem_bytes(cfg->dtype);
+            *pool_bytes = (int64_t)std::max(1, cfg->num_layers) * cfg->num_pages * cfg->num_kv_heads *
+                          cfg->page_size * cfg->head_dim * elem_bytes(cfg->dtype);
         if (rope_table_bytes) *rope_table_bytes = (int64_t)cfg->max_position * cfg->head_dim * 4;
     });
 }
@@ -227,6 +213,7 @@ pic_status pic_store_create(const pic_store_config *cfg, void *k_pool, void *v_p
             fail(PIC_ERR_INVALID, "k_pool, v_pool and rope_table must all be given or all be NULL");
         pic_store *s = new pic_store();
         s->cfg = *cfg;
+        s->cfg.num_layers = std::max(1, cfg->num_layers);
         s->shape = {cfg->num_q_heads, cfg->num_kv_heads, cfg->head_dim, cfg->page_size, cfg->dtype,
                     (int64_t)cfg->num_kv_heads * cfg->page_size * cfg->head_dim, cfg->key_layout};
         s->k_pool = k_pool;
@@ -299,16 +286,26 @@ pic_status pic_store_chunk(pic_store *s, uint64_t id, const void *k, const void 
         c.last_use = ++s->use_clock;
         for (int i = 0; i < n_pages; ++i) c.pages.push_back(store_alloc_page(s));
         if (k) {
-            for (int32_t first = 0; first < n_pages; first += kMaxFillPages) {
-                FillPages fp;
-                fp.count = std::min<int32_t>(kMaxFillPages, n_pages - first);
-                fp.first_token = first * B;
-                fp.n_tokens = n_tokens;
-                for (int i = 0; i < fp.count; ++i) fp.ids[i] = c.pages[first + i];
-                const hipError_t e = launch_store_fill(s->shape, s->k_pool, s->v_pool, k, v, fp, stream);
-                if (e != hipSuccess) {
-                    for (int32_t p : c.pages) store_unref(s, p);
-                    check_hip(e, "store_fill launch");
+            // k, v hold every layer: [num_layers][n_tokens][Hkv][d]
+            const int64_t elem = elem_bytes(s->cfg.dtype);
+            const int64_t layer_bytes = s->shape.page_elems * s->cfg.num_pages * elem;
+            const int64_t src_bytes = (int64_t)n_tokens * s->cfg.num_kv_heads * s->cfg.head_dim * elem;
+            for (int l = 0; l < s->cfg.num_layers; ++l) {
+                for (int32_t first = 0; first < n_pages; first += kMaxFillPages) {
+                    FillPages fp;
+                    fp.count = std::min<int32_t>(kMaxFillPages, n_pages - first);
+                    fp.first_token = first * B;
+                    fp.n_tokens = n_tokens;
+                    for (int i = 0; i < fp.count; ++i) fp.ids[i] = c.pages[first + i];
+                    const hipError_t e = launch_store_fill(
+                        s->shape, static_cast<uint8_t *>(s->k_pool) + l * layer_bytes,
+                        static_cast<uint8_t *>(s->v_pool) + l * layer_bytes,
+                        static_cast<const uint8_t *>(k) + l * src_bytes, static_cast<const uint8_t *>(v) + l * src_bytes,
+                        fp, stream);
+                    if (e != hipSuccess) {
+                        for (int32_t p : c.pages) store_unref(s, p);
+                        check_hip(e, "store_fill launch");
+                    }
                 }
             }
         }
@@ -468,7 +465,22 @@ pic_status pic_link_attend(pic_store *s, const pic_plan *plan, const void *q_new
         // the plan's tables are copied in first unless this workspace region still holds them
         if (!s->ledger.holds(plan, workspace))
             upload_tables(s, const_cast<pic_plan *>(plan), workspace, workspace_bytes, stream);
-        launch_link(s, plan, q_new, k_new, v_new, out, lse, static_cast<uint8_t *>(workspace), s->profiling, stream);
+        launch_link(s, plan, 0, q_new, k_new, v_new, out, lse, static_cast<uint8_t *>(workspace), s->profiling, stream);
+    });
+}
+
+pic_status pic_link_attend_layer(pic_store *s, const pic_plan *plan, int32_t layer, const void *q_new,
+                                 const void *k_new, const void *v_new, void *out, float *lse, void *workspace,
+                                 int64_t workspace_bytes, hipStream_t stream) {
+    return guarded([&] {
+        check_link_call(s, plan, q_new, k_new, v_new, out);
+        if (layer < 0 || layer >= s->cfg.num_layers)
+            fail(PIC_ERR_INVALID, "layer must be in [0, " + std::to_string(s->cfg.num_layers) + ")");
+        if (workspace_bytes < plan->workspace_bytes) fail(PIC_ERR_WORKSPACE, "workspace too small");
+        if (!s->ledger.holds(plan, workspace))
+            upload_tables(s, const_cast<pic_plan *>(plan), workspace, workspace_bytes, stream);
+        launch_link(s, plan, layer, q_new, k_new, v_new, out, lse, static_cast<uint8_t *>(workspace), s->profiling,
+                    stream);
     });
 }
 
@@ -499,7 +511,7 @@ pic_status pic_link_attend_static(pic_store *s, const pic_plan *plan, const void
         put(plan->off_dec_merge, plan->dec_merge.data(), plan->dec_merge.size() * sizeof(DecodeMergeDesc));
         pic_plan *mp = const_cast<pic_plan *>(plan);
         s->ledger.claim(mp, scratch, plan->workspace_bytes);   // its caller workspace no longer holds it
-        launch_link(s, plan, q_new, k_new, v_new, out, lse, ws, false, stream);
+        launch_link(s, plan, 0, q_new, k_new, v_new, out, lse, ws, false, stream);
     });
 }
 
@@ -510,6 +522,7 @@ pic_status pic_link_decode(pic_store *s, const pic_plan *plan, const void *q, co
         if (plan->owner != s) fail(PIC_ERR_INVALID, "plan belongs to another store");
         if (!s->k_pool) fail(PIC_ERR_STATE, "metadata-only store has no device");
         if (!plan->decode) fail(PIC_ERR_STATE, "plan was not made for decode (opts.decode)");
+        if (s->cfg.num_layers != 1) fail(PIC_ERR_STATE, "decode after link runs on single-layer stores");
         if (workspace_bytes < plan->workspace_bytes) fail(PIC_ERR_WORKSPACE, "workspace too small");
         if (!s->ledger.holds(plan, workspace))
             fail(PIC_ERR_WORKSPACE, "the workspace does not hold this plan's tables (never uploaded there, or "

@@ -95,6 +95,8 @@ constexpr int kMaxItemPages = 2048;  // longest KV range of one attention work i
 constexpr int kMaxPosition = 1 << 22;
 // Largest compile offset (leading tokens a chunk was compiled after) a store takes.
 constexpr int kMaxCompileOffset = 4096;
+// Most decoder layers a store holds K/V pools for.
+constexpr int kMaxLayers = 1024;
 constexpr int kThreads = 256;      // page writers, merge and the fp32 attention kernel
 // Automatic key rotation mode: rotate once per link call when the work list reads each key page
 // at least this many times on average (else inside attention). The rotation pass costs about as

@@ -1,0 +1,279 @@
+// HIP kernels of the decoder layers around the link step, for gfx950 (CDNA4).
+//
+//   linear_bf16   C = A W^T for the selected rows: A [M][K] activations, W [N][K] weights, fp32
+//                 accumulation on MFMA, with the epilogue of its place in the layer: the q/k/v
+//                 split of the QKV projection, the residual add of the output and down
+//                 projections, or SiLU(gate) * up of the MLP's gate and up projections
+//   rmsnorm_bf16  y = x / sqrt(mean(x^2) + eps) * w per row
+//
+// Only the selected rows of a link go through these layers: the cached chunks' K/V of every layer
+// come from the compile step (EPIC, atlas.scime.ai summary, "Approach": the first k tokens of each
+// chunk, and the suffix, are recomputed through the model; the rest of the chunk is reused).
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "model.h"
+
+namespace piclink {
+namespace {
+
+typedef float floatx4 __attribute__((ext_vector_type(4)));
+typedef float floatx16 __attribute__((ext_vector_type(16)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ float bf_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+
+__device__ __forceinline__ uint32_t pack_bf16(float a, float b) {
+    typedef float floatx2 __attribute__((ext_vector_type(2)));
+    floatx2 f = {a, b};
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector(f, bf16x2));
+}
+
+// ---------------------------------------------------------------------------------------------
+// linear_bf16. Work group = 4 waves, tile BM x BN = 128 x 128 of C over K in steps of BK = 64.
+// Wave (wm, wn) owns C rows [64 wm, 64 wm + 64) and columns [64 wn, 64 wn + 64) of the tile, as
+// 2 x 2 blocks of 32 x 32. Each block is computed transposed, C^T = W A^T, with
+// v_mfma_f32_32x32x16_bf16 (A operand: 32 rows of W, B operand: 32 rows of A; both K-contiguous,
+// read with one 16-byte LDS load per lane), so that a lane holds four consecutive columns of one
+// row of C per group of accumulators and writes them with one 8-byte store.
+// A and W tiles are double-buffered in LDS (row stride BK + 8: conflict-free fragment reads); the
+// next K step's tiles are loaded into registers while the current one is multiplied.
+constexpr int BM = 128, BN = 128, BK = 64, KS = BK + 8, NT = 256;
+
+struct LinearParams {
+    const uint16_t *a;        // [M][K]
+    const uint16_t *w;        // [N][K]
+    int m, n, k;
+    int epilogue;             // LinearEpilogue
+    uint16_t *out[3];         // outputs; kSplit3: column ranges [0, n0), [n0, n0 + n1), [n0 + n1, n)
+    int ld_out[3];            // row stride of each output (elements)
+    int split0, split1;       // kSplit3: columns of the first and second output
+    const uint16_t *residual; // kResidual: [M][N] added to the product (may alias out[0])
+    int tiles_m, tiles_n;
+};
+
+__global__ __launch_bounds__(NT, 2) void linear_bf16(LinearParams p) {
+    __shared__ __attribute__((aligned(16))) uint16_t as[2][BM * KS];
+    __shared__ __attribute__((aligned(16))) uint16_t ws[2][BN * KS];
+
+    // work groups are dealt round-robin over the 8 XCDs: give each XCD a contiguous run of tiles,
+    // N-major, so that the work groups sharing one W tile run on one XCD and share its L2
+    const int tiles = p.tiles_m * p.tiles_n;
+    const int per_xcd = (tiles + 7) / 8;
+    const int t = (blockIdx.x % 8) * per_xcd + blockIdx.x / 8;
+    if (t >= tiles) return;
+    const int tn = t / p.tiles_m, tm = t % p.tiles_m;
+    const int m0 = tm * BM, n0 = tn * BN;
+
+    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, ln = lane & 31, lg = lane >> 5;
+    const int wm = wave >> 1, wn = wave & 1;
+
+    // global -> register staging: 4 pieces of 16 bytes of A and 4 of W per thread per K step
+    // (row = tid / 8 + 32 i, 8 elements at column 8 (tid % 8)); rows of A past M read row M - 1
+    const int srow = tid >> 3, scol = (tid & 7) * 8;
+    const uint16_t *a_src[4];
+    const uint16_t *w_src[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const int r = min(m0 + srow + 32 * i, p.m - 1);
+        a_src[i] = p.a + (int64_t)r * p.k + scol;
+        w_src[i] = p.w + (int64_t)(n0 + srow + 32 * i) * p.k + scol;
+    }
+    u32x4 a_reg[4], w_reg[4];
+    auto load = [&](int kt) __attribute__((always_inline)) {
+        const int k0 = kt * BK;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            a_reg[i] = *reinterpret_cast<const u32x4 *>(a_src[i] + k0);
+            w_reg[i] = *reinterpret_cast<const u32x4 *>(w_src[i] + k0);
+        }
+    };
+    auto store = [&](int buf) __attribute__((always_inline)) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            *reinterpret_cast<u32x4 *>(&as[buf][(srow + 32 * i) * KS + scol]) = a_reg[i];
+            *reinterpret_cast<u32x4 *>(&ws[buf][(srow + 32 * i) * KS + scol]) = w_reg[i];
+        }
+    };
+
+    floatx16 acc[2][2];   // [n block][m block]
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int j = 0; j < 2; ++j)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
+
+    const int n_kt = p.k / BK;
+    load(0);
+    store(0);
+    __syncthreads();
+    for (int kt = 0; kt < n_kt; ++kt) {
+        const int buf = kt & 1;
+        if (kt + 1 < n_kt) load(kt + 1);
+        const uint16_t *wb = &ws[buf][(64 * wn + ln) * KS + 8 * lg];
+        const uint16_t *ab = &as[buf][(64 * wm + ln) * KS + 8 * lg];
+#pragma unroll
+        for (int s = 0; s < BK / 16; ++s) {
+            bf16x8 wf[2], af[2];
+#pragma unroll
+            for (int i = 0; i < 2; ++i) {
+                wf[i] = *reinterpret_cast<const bf16x8 *>(wb + 32 * i * KS + 16 * s);
+                af[i] = *reinterpret_cast<const bf16x8 *>(ab + 32 * i * KS + 16 * s);
+            }
+#pragma unroll
+            for (int i = 0; i < 2; ++i)
+#pragma unroll
+                for (int j = 0; j < 2; ++j)
+                    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(wf[i], af[j], acc[i][j], 0, 0, 0);
+        }
+        if (kt + 1 < n_kt) store(buf ^ 1);
+        __syncthreads();
+    }
+
+    // epilogue: lane (ln, lg) of block (i, j) holds C[row][col .. col + 3] in accumulators
+    // 4g .. 4g + 3, row = m0 + 64 wm + 32 j + ln, col = n0 + 64 wn + 32 i + 8 g + 4 lg
+    if (p.epilogue == kSwiGlu) {
+        // W rows alternate 32 gate rows and 32 up rows: block i = 0 holds gate, i = 1 up, for the
+        // output columns (n0 + 64 wn) / 2 + 8 g + 4 lg .. + 3
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+            const int row = m0 + 64 * wm + 32 * j + ln;
+            if (row >= p.m) continue;
+            uint16_t *orow = p.out[0] + (int64_t)row * p.ld_out[0] + (n0 + 64 * wn) / 2;
+#pragma unroll
+            for (int g = 0; g < 4; ++g) {
+                float v[4];
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const float gt = acc[0][j][4 * g + e], up = acc[1][j][4 * g + e];
+                    v[e] = gt / (1.0f + __expf(-gt)) * up;
+                }
+                u32x2 o = {pack_bf16(v[0], v[1]), pack_bf16(v[2], v[3])};
+                *reinterpret_cast<u32x2 *>(orow + 8 * g + 4 * lg) = o;
+            }
+        }
+        return;
+    }
+    // column ranges of the split outputs (a 32-column block never straddles two of them)
+    int which = 0, col_base = 0;
+    if (p.epilogue == kSplit3) {
+        const int c0 = n0 + 64 * wn;
+        which = c0 >= p.split0 + p.split1 ? 2 : c0 >= p.split0 ? 1 : 0;
+        col_base = which == 2 ? p.split0 + p.split1 : which == 1 ? p.split0 : 0;
+    }
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+        const int row = m0 + 64 * wm + 32 * j + ln;
+        if (row >= p.m) continue;
+#pragma unroll
+        for (int i = 0; i < 2; ++i) {
+            const int col = n0 + 64 * wn + 32 * i - col_base;
+            uint16_t *orow = p.out[which] + (int64_t)row * p.ld_out[which] + col;
+            const uint16_t *rrow = p.residual ? p.residual + (int64_t)row * p.n + n0 + 64 * wn + 32 * i : nullptr;
+#pragma unroll
+            for (int g = 0; g < 4; ++g) {
+                float v[4];
+#pragma unroll
+                for (int e = 0; e < 4; ++e) v[e] = acc[i][j][4 * g + e];
+                if (p.epilogue == kResidual) {
+                    const u32x2 r = *reinterpret_cast<const u32x2 *>(rrow + 8 * g + 4 * lg);
+                    v[0] += bf_lo(r[0]);
+                    v[1] += bf_hi(r[0]);
+                    v[2] += bf_lo(r[1]);
+                    v[3] += bf_hi(r[1]);
+                }
+                u32x2 o = {pack_bf16(v[0], v[1]), pack_bf16(v[2], v[3])};
+                *reinterpret_cast<u32x2 *>(orow + 8 * g + 4 * lg) = o;
+            }
+        }
+    }
+}
+
+// ---------------------------------------------------------------------------------------------
+// rmsnorm_bf16: one wave per row. y = x * rsqrt(mean(x^2) + eps) * w, the sum of squares in fp32.
+template <int PER_LANE>
+__global__ __launch_bounds__(256) void rmsnorm_bf16(const uint16_t *x, const uint16_t *w, uint16_t *y, int rows,
+                                                    int dm, float eps) {
+    const int row = blockIdx.x * 4 + (threadIdx.x >> 6);
+    const int lane = threadIdx.x & 63;
+    if (row >= rows) return;
+    const uint16_t *xr = x + (int64_t)row * dm;
+    u32x4 v[PER_LANE];
+    float ss = 0.0f;
+#pragma unroll
+    for (int i = 0; i < PER_LANE; ++i) {
+        const int c = (i * 64 + lane) * 8;
+        v[i] = c < dm ? *reinterpret_cast<const u32x4 *>(xr + c) : u32x4{0, 0, 0, 0};
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const float a = bf_lo(v[i][e]), b = bf_hi(v[i][e]);
+            ss = fmaf(a, a, ss);
+            ss = fmaf(b, b, ss);
+        }
+    }
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) ss += __shfl_xor(ss, o);
+    const float inv = rsqrtf(ss / (float)dm + eps);
+    uint16_t *yr = y + (int64_t)row * dm;
+#pragma unroll
+    for (int i = 0; i < PER_LANE; ++i) {
+        const int c = (i * 64 + lane) * 8;
+        if (c >= dm) continue;
+        const u32x4 wv = *reinterpret_cast<const u32x4 *>(w + c);
+        u32x4 o;
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+            o[e] = pack_bf16(bf_lo(v[i][e]) * inv * bf_lo(wv[e]), bf_hi(v[i][e]) * inv * bf_hi(wv[e]));
+        *reinterpret_cast<u32x4 *>(yr + c) = o;
+    }
+}
+
+}  // namespace
+
+hipError_t launch_linear(const LinearCall &c, hipStream_t stream) {
+    if (c.m <= 0) return hipSuccess;
+    if (c.n % BN != 0 || c.k % BK != 0 || c.k <= 0) return hipErrorInvalidValue;
+    LinearParams p{};
+    p.a = static_cast<const uint16_t *>(c.a);
+    p.w = static_cast<const uint16_t *>(c.w);
+    p.m = c.m;
+    p.n = c.n;
+    p.k = c.k;
+    p.epilogue = c.epilogue;
+    for (int i = 0; i < 3; ++i) {
+        p.out[i] = static_cast<uint16_t *>(c.out[i]);
+        p.ld_out[i] = c.ld_out[i];
+    }
+    p.split0 = c.split0;
+    p.split1 = c.split1;
+    p.residual = static_cast<const uint16_t *>(c.residual);
+    p.tiles_m = (c.m + BM - 1) / BM;
+    p.tiles_n = c.n / BN;
+    const int tiles = p.tiles_m * p.tiles_n;
+    const int grid = 8 * ((tiles + 7) / 8);
+    hipLaunchKernelGGL(linear_bf16, dim3(grid), dim3(NT), 0, stream, p);
+    return hipGetLastError();
+}
+
+hipError_t launch_rmsnorm(const void *x, const void *w, void *y, int rows, int dm, float eps, hipStream_t stream) {
+    if (rows <= 0) return hipSuccess;
+    if (dm % 8 != 0 || dm > 64 * 8 * 16) return hipErrorInvalidValue;
+    const dim3 grid((rows + 3) / 4);
+    const int per_lane = (dm + 511) / 512;
+    auto *xp = static_cast<const uint16_t *>(x);
+    auto *wp = static_cast<const uint16_t *>(w);
+    auto *yp = static_cast<uint16_t *>(y);
+    if (per_lane <= 1) hipLaunchKernelGGL(rmsnorm_bf16<1>, grid, dim3(256), 0, stream, xp, wp, yp, rows, dm, eps);
+    else if (per_lane <= 2) hipLaunchKernelGGL(rmsnorm_bf16<2>, grid, dim3(256), 0, stream, xp, wp, yp, rows, dm, eps);
+    else if (per_lane <= 4) hipLaunchKernelGGL(rmsnorm_bf16<4>, grid, dim3(256), 0, stream, xp, wp, yp, rows, dm, eps);
+    else if (per_lane <= 8) hipLaunchKernelGGL(rmsnorm_bf16<8>, grid, dim3(256), 0, stream, xp, wp, yp, rows, dm, eps);
+    else hipLaunchKernelGGL(rmsnorm_bf16<16>, grid, dim3(256), 0, stream, xp, wp, yp, rows, dm, eps);
+    return hipGetLastError();
+}
+
+}  // namespace piclink

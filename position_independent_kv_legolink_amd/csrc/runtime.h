@@ -3,7 +3,9 @@
 
 #include <stdint.h>
 
+#include <new>
 #include <set>
+#include <stdexcept>
 #include <string>
 #include <unordered_map>
 #include <vector>
@@ -22,6 +24,31 @@ struct Error {
 };
 
 [[noreturn]] void fail(pic_status status, const std::string &message);
+void check_hip(hipError_t e, const char *what);
+
+extern thread_local std::string g_last_error;
+
+// Runs f, turning every C++ exception into a status and the thread's last-error message; no
+// exception crosses the C ABI.
+template <typename F>
+pic_status guarded(F &&f) {
+    try {
+        f();
+        return PIC_OK;
+    } catch (const Error &e) {
+        g_last_error = e.message;
+        return e.status;
+    } catch (const std::bad_alloc &) {
+        g_last_error = "host allocation failed";
+        return PIC_ERR_OOM;
+    } catch (const std::exception &e) {
+        g_last_error = e.what();
+        return PIC_ERR_INVALID;
+    } catch (...) {
+        g_last_error = "unknown error";
+        return PIC_ERR_INVALID;
+    }
+}
 
 struct Chunk {
     int32_t n_tokens = 0;
@@ -99,5 +126,12 @@ const Chunk &store_find(const pic_store *s, uint64_t id);
 
 pic_plan *build_plan(pic_store *s, const pic_request *reqs, int32_t n_reqs, const pic_link_options &opts);
 void release_plan(pic_store *s, pic_plan *plan);
+
+// Shared by the link calls (abi.cpp) and the layer executor (forward.cpp).
+void upload_tables(pic_store *s, pic_plan *plan, void *workspace, int64_t workspace_bytes, hipStream_t stream);
+void check_link_call(pic_store *s, const pic_plan *plan, const void *q_new, const void *k_new, const void *v_new,
+                     const void *out);
+void launch_link(pic_store *s, const pic_plan *plan, int layer, const void *q_new, const void *k_new,
+                 const void *v_new, void *out, float *lse, uint8_t *ws, bool prof, hipStream_t stream);
 
 }  // namespace piclink

@@ -96,3 +96,33 @@ CONFIGS: dict[str, LinkConfig] = {
 
 # Order used when the configs are listed: the small parity tier first.
 CONFIG_ORDER = ["tiny", "llama3_k2", "batched_k16", "long50k_k32", "block_zipf"]
+
+
+@dataclass(frozen=True)
+class ModelShape:
+    """Decoder layers around the link step, with seeded random weights (no trained model)."""
+    name: str
+    description: str
+    n_layers: int
+    d_ff: int
+    norm_eps: float = 1e-5
+    weight_seed: int = 0
+
+
+# A reduced configuration the fp64 oracle runs in seconds, for parity; and the Llama-3-8B shape
+# (32 layers, d_ff 14,336) that the latency figure uses (EPIC summary, "Limitations": 7-9B models).
+MODEL_SHAPES: dict[str, ModelShape] = {
+    "small2": ModelShape("small2", "2 layers, d_model 512 (8 q / 2 kv heads x 64), d_ff 1,024", n_layers=2,
+                         d_ff=1024, weight_seed=2001),
+    "llama3_8b": ModelShape("llama3_8b", "32 layers, d_model 4,096 (32 q / 8 kv heads x 128), d_ff 14,336",
+                            n_layers=32, d_ff=14336, weight_seed=2002),
+}
+
+# the link workload the reduced model runs on: two requests over a shared pool, LegoLink-4
+MODEL_LINK = LinkConfig(
+    name="model_small",
+    description="8 q / 2 kv heads, head_dim 64, bf16, theta 5e5; 2 requests of a 32-token prefix + 6 x 96-token "
+                "chunks (uniform draw from 8) + 40-token suffix, k=4",
+    num_q_heads=8, num_kv_heads=2, head_dim=64, dtype="bf16", rope_theta=5e5, page_size=16, k=4,
+    block_level=False, prefix_len=32, chunk_len=96, chunks_per_request=6, suffix_len=40, n_requests=2,
+    pool_size=8, pool_draw="uniform", q_scale=1.0, kv_scale=1.0, seed=1101)

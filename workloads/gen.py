@@ -26,8 +26,14 @@ KIND_DRAW = 8
 KIND_Q_ALL = 9
 
 
-def rng(seed: int, kind: int, ident: int) -> np.random.Generator:
-    return np.random.Generator(np.random.PCG64(np.random.SeedSequence([seed, kind, ident])))
+KIND_WEIGHT = 10
+KIND_HIDDEN = 11
+
+
+def rng(seed: int, kind: int, ident: int, layer: int = 0) -> np.random.Generator:
+    """PCG64 keyed by (seed, kind, id) — and the decoder layer for layers after the first."""
+    key = [seed, kind, ident] + ([layer] if layer else [])
+    return np.random.Generator(np.random.PCG64(np.random.SeedSequence(key)))
 
 
 def round_bf16(x: np.ndarray) -> np.ndarray:
@@ -45,8 +51,8 @@ def round_bf16(x: np.ndarray) -> np.ndarray:
     return out
 
 
-def normal(seed: int, kind: int, ident: int, shape, scale: float, dtype: str) -> np.ndarray:
-    a = rng(seed, kind, ident).standard_normal(shape, dtype=np.float32)
+def normal(seed: int, kind: int, ident: int, shape, scale: float, dtype: str, layer: int = 0) -> np.ndarray:
+    a = rng(seed, kind, ident, layer).standard_normal(shape, dtype=np.float32)
     if scale != 1.0:
         a *= np.float32(scale)
     if dtype == "bf16":
@@ -54,18 +60,42 @@ def normal(seed: int, kind: int, ident: int, shape, scale: float, dtype: str) ->
     return a
 
 
-def chunk_kv(cfg: LinkConfig, chunk_id: int) -> tuple[np.ndarray, np.ndarray]:
-    """Position-free K and V of one pooled chunk, each [chunk_len][Hkv][d]."""
+def chunk_kv(cfg: LinkConfig, chunk_id: int, layer: int = 0) -> tuple[np.ndarray, np.ndarray]:
+    """Position-free K and V of one pooled chunk at one decoder layer, each [chunk_len][Hkv][d]."""
     shape = (cfg.chunk_len, cfg.num_kv_heads, cfg.head_dim)
-    return (normal(cfg.seed, KIND_CHUNK_K, chunk_id, shape, cfg.kv_scale, cfg.dtype),
-            normal(cfg.seed, KIND_CHUNK_V, chunk_id, shape, cfg.kv_scale, cfg.dtype))
+    return (normal(cfg.seed, KIND_CHUNK_K, chunk_id, shape, cfg.kv_scale, cfg.dtype, layer),
+            normal(cfg.seed, KIND_CHUNK_V, chunk_id, shape, cfg.kv_scale, cfg.dtype, layer))
 
 
-def prefix_kv(cfg: LinkConfig, request: int) -> tuple[np.ndarray, np.ndarray]:
-    """Cached K and V of a request's prefix, each [prefix_len][Hkv][d]."""
+def prefix_kv(cfg: LinkConfig, request: int, layer: int = 0) -> tuple[np.ndarray, np.ndarray]:
+    """Cached K and V of a request's prefix at one decoder layer, each [prefix_len][Hkv][d]."""
     shape = (cfg.prefix_len, cfg.num_kv_heads, cfg.head_dim)
-    return (normal(cfg.seed, KIND_PREFIX_K, request, shape, cfg.kv_scale, cfg.dtype),
-            normal(cfg.seed, KIND_PREFIX_V, request, shape, cfg.kv_scale, cfg.dtype))
+    return (normal(cfg.seed, KIND_PREFIX_K, request, shape, cfg.kv_scale, cfg.dtype, layer),
+            normal(cfg.seed, KIND_PREFIX_V, request, shape, cfg.kv_scale, cfg.dtype, layer))
+
+
+def layer_weights(seed: int, layer: int, *, d_model: int, d_ff: int, num_q_heads: int, num_kv_heads: int,
+                  head_dim: int) -> dict:
+    """Random bf16 weights of one decoder layer (float32 arrays of bf16 values): projections
+    N(0, 1/fan_in) as [out][in], norm weights 1 + 0.1 N(0, 1)."""
+    qd, kvd = num_q_heads * head_dim, num_kv_heads * head_dim
+    shapes = dict(attn_norm=(d_model,), w_qkv=(qd + 2 * kvd, d_model), w_o=(d_model, qd), mlp_norm=(d_model,),
+                  w_gate_up=(2 * d_ff, d_model), w_down=(d_model, d_ff))
+    out = {}
+    for i, (name, shape) in enumerate(shapes.items()):
+        g = rng(seed, KIND_WEIGHT, i, layer + 1)
+        a = g.standard_normal(shape, dtype=np.float32)
+        if len(shape) == 1:
+            a = np.float32(1.0) + np.float32(0.1) * a
+        else:
+            a *= np.float32(1.0 / np.sqrt(shape[1]))
+        out[name] = round_bf16(a)
+    return out
+
+
+def hidden_states(seed: int, request: int, n_rows: int, d_model: int) -> np.ndarray:
+    """Hidden states [n][d_model] of a request's selected rows entering the first layer, N(0, 1), bf16."""
+    return normal(seed, KIND_HIDDEN, request, (n_rows, d_model), 1.0, "bf16")
 
 
 def new_rows(cfg: LinkConfig, request: int, n_rows: int):
