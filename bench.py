@@ -276,6 +276,116 @@ def decode_measure(job, steps=DECODE_STEPS, warmup=DECODE_WARMUP):
             "workspace_mb": round(ws_mb, 1), "rotated_keys_mb": round(rot_mb, 1)}
 
 
+def model_measure(cfg, shape_name="llama3_8b", steps=5, warmup=2, gemm_reps=10):
+    """TTFT-shaped latency: the request's selected rows through every layer of a Llama-3-8B-shaped
+    model with seeded random weights (pic_link_forward: per layer RMSNorm, QKV projection, the
+    link step over that layer's cached K/V, output projection, RMSNorm, gate/up + SwiGLU, down
+    projection), each forward timed alone with HIP events after resetting the rows' hidden states.
+    The layers' cached K/V and weights are drawn on the GPU (torch's seeded generator). The hand-
+    written GEMM is also timed on its own at each projection shape of the layer."""
+    import torch
+
+    import position_independent_kv_legolink_amd as pic
+    from workloads import MODEL_SHAPES, gen
+
+    shape = MODEL_SHAPES[shape_name]
+    L, dff, eps = shape.n_layers, shape.d_ff, shape.norm_eps
+    hq, hkv, hd, B = cfg.num_q_heads, cfg.num_kv_heads, cfg.head_dim, cfg.page_size
+    dm, qd, kvd = hq * hd, hq * hd, hkv * hd
+    draws = gen.request_chunks(cfg)
+    chunk_ids = sorted({c for ids in draws for c in ids})
+    n_tokens = cfg.prefix_len + cfg.chunks_per_request * cfg.chunk_len + cfg.suffix_len
+    pages = len(chunk_ids) * -(-cfg.chunk_len // B) + len(draws) * (-(-cfg.prefix_len // B))
+    private = len(draws) * (cfg.chunks_per_request * -(-max(cfg.k, B if cfg.block_level else 0) // B)
+                            + -(-cfg.suffix_len // B))
+    store = pic.Store(num_q_heads=hq, num_kv_heads=hkv, head_dim=hd, page_size=B, num_pages=pages + private + 16,
+                      dtype="bf16", rope_theta=cfg.rope_theta, max_position=n_tokens + 1, num_layers=L)
+    g = torch.Generator(device="cuda")
+    g.manual_seed(shape.weight_seed)
+
+    def randn(*size, scale=1.0):
+        return (torch.randn(*size, generator=g, device="cuda", dtype=torch.float32) * scale).to(torch.bfloat16)
+
+    requests = []
+    for c in chunk_ids:
+        store.store_chunk(c, randn(L, cfg.chunk_len, hkv, hd, scale=cfg.kv_scale),
+                          randn(L, cfg.chunk_len, hkv, hd, scale=cfg.kv_scale))
+    for r, ids in enumerate(draws):
+        pid = None
+        if cfg.prefix_len:
+            pid = cfg.prefix_id(r)
+            store.store_chunk(pid, randn(L, cfg.prefix_len, hkv, hd, scale=cfg.kv_scale),
+                              randn(L, cfg.prefix_len, hkv, hd, scale=cfg.kv_scale))
+        requests.append(pic.LinkRequest(ids, cfg.suffix_len, pid))
+    layers = []
+    for _ in range(L):
+        layers.append(dict(attn_norm=(1.0 + 0.1 * randn(dm).float()).to(torch.bfloat16),
+                           w_qkv=randn(qd + 2 * kvd, dm, scale=dm ** -0.5), w_o=randn(dm, qd, scale=qd ** -0.5),
+                           mlp_norm=(1.0 + 0.1 * randn(dm).float()).to(torch.bfloat16),
+                           w_gate_up=randn(2 * dff, dm, scale=dm ** -0.5), w_down=randn(dm, dff, scale=dff ** -0.5)))
+    model = pic.Model(d_model=dm, d_ff=dff, norm_eps=eps, layers=layers)
+    plan = store.link_plan(requests, k=cfg.k, block_level=cfg.block_level)
+    R = plan.rows
+    x0 = randn(R, dm)
+    x = torch.empty_like(x0)
+    ws = torch.empty(pic.forward_workspace_bytes(store, plan, model), dtype=torch.uint8, device="cuda")
+    torch.cuda.synchronize()
+    times = []
+    with NoGC():
+        for i in range(warmup + steps):
+            x.copy_(x0)
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            pic.link_forward(store, plan, model, x, workspace=ws)
+            e1.record()
+            e1.synchronize()
+            if i >= warmup:
+                times.append(e0.elapsed_time(e1))
+    assert torch.isfinite(x.float()).all(), "non-finite hidden states"
+    ms = float(np.median(times))
+    # the projections alone, at the layer's shapes (same kernel, same grid)
+    a_dm, a_q, a_ff = randn(R, dm), randn(R, qd), randn(R, dff)
+    gemms = {"qkv": (a_dm, layers[0]["w_qkv"], 0), "o": (a_q, layers[0]["w_o"], 1),
+             "gate_up_swiglu": (a_dm, layers[0]["w_gate_up"], 2), "down": (a_ff, layers[0]["w_down"], 1)}
+    gemm_out = {}
+    gemm_ms_total, gemm_flop_total = 0.0, 0.0
+    for name, (a, w, epi) in gemms.items():
+        res = torch.empty((R, w.shape[0]), dtype=torch.bfloat16, device="cuda") if epi == 1 else None
+        out = torch.empty((R, w.shape[0] // 2 if epi == 2 else w.shape[0]), dtype=torch.bfloat16, device="cuda")
+        for _ in range(3):
+            pic.linear(a, w, epi, residual=res, out=out)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(gemm_reps):
+            pic.linear(a, w, epi, residual=res, out=out)
+        e1.record()
+        e1.synchronize()
+        gms = e0.elapsed_time(e1) / gemm_reps
+        flop = 2.0 * R * w.shape[0] * w.shape[1]
+        gemm_ms_total += gms
+        gemm_flop_total += flop
+        gemm_out[name] = {"m": R, "n": int(w.shape[0]), "k": int(w.shape[1]), "ms": round(gms, 4),
+                          "tflops": round(flop / (gms * 1e-3) / 1e12, 1),
+                          "frac": round(flop / (gms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4)}
+    ex = plan.export()
+    attn_flop = 0.0
+    for r in range(len(requests)):
+        p = ex["row_pos"][ex["cu_rows"][r]:ex["cu_rows"][r + 1]].astype(np.float64)
+        attn_flop += 4.0 * hd * hq * float(np.sum(p + 1))     # positions start at 0
+    layer_flop = gemm_flop_total + attn_flop
+    plan.free()
+    store.close()
+    gemm_tflops = gemm_flop_total / (gemm_ms_total * 1e-3) / 1e12
+    return {"model": shape_name, "layers": L, "d_model": dm, "d_ff": dff, "rows": R, "tokens_per_request": n_tokens,
+            "ms": round(ms, 3), "ms_p10_p90": [round(float(np.quantile(times, 0.1)), 3),
+                                               round(float(np.quantile(times, 0.9)), 3)],
+            "ms_per_layer": round(ms / L, 4), "gflop_per_layer": round(layer_flop / 1e9, 1),
+            "tflops": round(L * layer_flop / (ms * 1e-3) / 1e12, 1),
+            "gemm": gemm_out, "gemm_ms_per_layer": round(gemm_ms_total, 4),
+            "gemm_tflops": round(gemm_tflops, 1), "gemm_frac": round(gemm_tflops / PEAK_BF16_TFLOPS, 4),
+            "weights": "random N(0, 1/fan_in), bf16", "data": "synthetic"}
+
+
 def dense_comparator(job, reps=3):
     """Full recompute of every token (prefix and suffix included) on the same inputs.
 
@@ -456,6 +566,8 @@ def main():
     ap.add_argument("--cold-steps", type=int, default=10,
                     help="extra steps, each after evicting the MALL, reported under 'cold' (0: none)")
     ap.add_argument("--no-decode", action="store_true", help="skip the decode-after-link measurement")
+    ap.add_argument("--no-model", action="store_true",
+                    help="skip the 32-layer forward (TTFT-shaped latency) of the request's selected rows")
     ap.add_argument("--rope-keys", type=int, default=0, choices=(0, 1, 2),
                     help="key rotation: 0 automatic, 1 inside attention, 2 once ahead of attention")
     ap.add_argument("--key-layout", default="position_free", choices=("position_free", "segment_rope"),
@@ -575,6 +687,11 @@ def main():
         decode = decode_measure(job)
         log(f"decode after link: {decode}")
 
+    model = None
+    if not args.no_model and cfg.dtype == "bf16":
+        model = model_measure(cfg)
+        log(f"32-layer forward: {model}")
+
     dense = None
     if not args.no_dense:
         dense = dense_comparator(job)
@@ -622,6 +739,7 @@ def main():
         "roofline": roofline,
         "cold": cold,
         "decode": decode,
+        "model_forward": model,
         "dense_comparator": dense,
         "cpu_baseline": cpu,
         "kernel_source_sha256_16": kernel_hash(),

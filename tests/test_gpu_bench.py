@@ -33,7 +33,8 @@ def test_bench_line_has_every_field():
                "--cpu-seconds", "1")
     for key in ("metric", "value", "unit", "n_gpus", "steps", "warmup", "ms_per_step", "higher_is_better",
                 "scaling", "vs_baseline", "dtype", "data", "config", "roofline", "cpu_baseline",
-                "link_latency_wall_ms", "cold", "decode", "dense_comparator", "kernel_source_sha256_16"):
+                "link_latency_wall_ms", "cold", "decode", "model_forward", "dense_comparator",
+                "kernel_source_sha256_16"):
         assert key in d, key
     assert d["n_gpus"] == 1 and d["steps"] == 3 and d["warmup"] == 2 and d["dtype"] == "bf16"
     assert d["config"]["workload"] == "llama3_k2" and d["config"]["selected_rows"] == 84
@@ -47,6 +48,9 @@ def test_bench_line_has_every_field():
     assert lat["steps"] == 3 and 0 < lat["p10"] <= lat["p50"] <= lat["p90"]
     assert d["cold"]["steps"] == 2 and d["cold"]["p10"] <= d["cold"]["p90"]
     assert d["decode"]["ms"] > 0
+    m = d["model_forward"]                 # 32 Llama-3-8B-shaped layers over the 84 selected rows
+    assert m["layers"] == 32 and m["rows"] == 84 and m["ms"] > 0 and 0 < m["gemm_frac"] < 1
+    assert set(m["gemm"]) == {"qkv", "o", "gate_up_swiglu", "down"}
     # the dense comparator's outputs agree with the link step's at the link rows (bf16 tolerance)
     assert d["dense_comparator"]["max_abs_diff_at_link_rows"] <= 2e-2
 
