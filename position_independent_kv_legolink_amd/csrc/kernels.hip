@@ -788,6 +788,566 @@ __global__ __launch_bounds__(512, 1) void link_attention_bf16(AttnParams p) {
 }
 
 // ---------------------------------------------------------------------------------------------
+// bf16 attention over keys rotated ahead (KR), d = 128: the schedule of link_attention_bf16 with
+// the K' and V tiles loaded straight from global memory into LDS (global_load_lds_dwordx4: lane i
+// of an instruction writes the 16 bytes it loads at the instruction's LDS base + 16 i). Staging
+// then costs no registers, no LDS writes and no VALU work in the softmax phase.
+//   - Rows are unpadded (256 bytes per key) and XOR-swizzled per 16-byte chunk so that the MFMA
+//     operand reads stay free of bank conflicts: K' row r holds chunk c at c ^ (r & 15), so the 16
+//     lanes of one b128 read take 16 rows at 16 distinct chunks; V row r holds it at c ^ 4 (r & 3),
+//     so the 4 keys x 4 chunks that 32 lanes of one transposing b64 read touch are distinct. Each
+//     lane fetches the global chunk that lands in its LDS position.
+//   - K', V and key positions use rings of 4 slots; the K' and V slots are separate arrays and the
+//     main loop is unrolled by 4, so that every slot is a compile-time constant and the compiler
+//     keeps the loads of later tiles in flight past the operand reads of the current ones.
+//   - Slot lifetimes under the one-phase skew of the wave groups: K' of tile t+3 is loaded in
+//     Y(t) (its slot held tile t-1, read by both groups' QK^T before A's X(t-1)); V of tile t+3 in
+//     X(t) (its slot held tile t-1, read by B's PV during A's Y(t)). Per wave and tile: 2 K' and 2
+//     V load instructions of 1 KiB.
+//   - Before the barrier that opens group A's X(t), every wave waits for its own loads of K'(t+1)
+//     and V(t): group A at the end of Y(t) (8 later load instructions may stay in flight), group B
+//     at the end of its X(t-1) (6 may).
+// Work-group barrier of the direct-load kernel: this wave's LDS operations complete (lgkmcnt), then
+// s_barrier; the memory clobber keeps the compiler from moving memory accesses across it. A memory
+// fence would also wait for every direct load in flight (they are LDS writes to the memory model)
+// and expose their latency at every barrier: the loads a barrier has to cover are waited for with
+// an explicit vmcnt before it.
+__device__ __forceinline__ void barrier_dl() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
+
+// One direct load: 16 bytes per lane from `src` into LDS at byte lds + 16 * lane (global_load_lds
+// with its LDS base in M0). Issued from asm, so the compiler does not track it: the kernel waits
+// for its loads itself (vmcnt) before the barriers that publish them. Loads the compiler does not
+// count can only make its own vmcnt waits for other loads stricter, never too weak (they
+// complete in order).
+__device__ __forceinline__ void dma16(const void *src, uint32_t lds) {
+    asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(src), "s"(lds) : "memory", "m0");
+}
+
+// LDS byte address of a __shared__ location.
+__device__ __forceinline__ uint32_t lds_addr(const void *p) {
+    return (uint32_t)(uintptr_t)(const void __attribute__((address_space(3))) *)p;
+}
+
+template <typename T>
+struct IsSlot : std::false_type {};
+template <int V>
+struct IsSlot<std::integral_constant<int, V>> : std::true_type {};
+
+template <int D>
+__global__ __launch_bounds__(512, 1) void link_attention_bf16_dl(AttnParams p) {
+    static_assert(D == 128, "16 chunks of 16 bytes per key row");
+    constexpr int NT = 512;
+    constexpr int KT = kKeysPerTile;
+    constexpr int NS = D / 16;         // k-steps of QK^T
+    constexpr int NDB = D / 32;        // 32-wide d blocks of PV
+    constexpr int TQ = 256;
+    constexpr int TILE = KT * D;       // elements of one K' or V tile (16 KiB)
+    static_assert(KT == 64, "one key per lane when deciding the tile mask");
+
+    __shared__ __attribute__((aligned(16))) uint16_t k0[TILE], k1[TILE], k2[TILE], k3[TILE];
+    __shared__ __attribute__((aligned(16))) uint16_t v0[TILE], v1[TILE], v2[TILE], v3[TILE];
+    __shared__ __attribute__((aligned(16))) int kpos_s[4 * KT];
+    __shared__ int pg_phys[kMaxItemPages], pg_pv[kMaxItemPages];
+
+    const WorkDesc w = p.work[blockIdx.x];
+    if (w.n_rows <= 0) return;
+
+    const int tid = threadIdx.x;
+    const int wave = tid >> 6, lane = tid & 63, ln = lane & 31, lg = lane >> 5;
+    const int wv = __builtin_amdgcn_readfirstlane(wave);
+    const int G = 1 << p.gshift;
+    const int page_size = 1 << p.pshift;
+    const int ppt = KT >> p.pshift;
+    const PageDesc *pg = p.pages + w.page_base;
+    const int64_t head_off = (int64_t)w.kv_head * page_size * D;
+
+    // slots: compile-time (std::integral_constant) in the unrolled main loop, else run-time
+    auto kslot = [&](auto s) -> uint16_t * {
+        if constexpr (IsSlot<decltype(s)>::value) {
+            constexpr int S = decltype(s)::value;
+            if constexpr (S == 0) return k0;
+            else if constexpr (S == 1) return k1;
+            else if constexpr (S == 2) return k2;
+            else return k3;
+        } else {
+            const int S = s & 3;
+            return S == 0 ? k0 : S == 1 ? k1 : S == 2 ? k2 : k3;
+        }
+    };
+    auto vslot = [&](auto s) -> uint16_t * {
+        if constexpr (IsSlot<decltype(s)>::value) {
+            constexpr int S = decltype(s)::value;
+            if constexpr (S == 0) return v0;
+            else if constexpr (S == 1) return v1;
+            else if constexpr (S == 2) return v2;
+            else return v3;
+        } else {
+            const int S = s & 3;
+            return S == 0 ? v0 : S == 1 ? v1 : S == 2 ? v2 : v3;
+        }
+    };
+    auto slot_plus = [](auto s, auto k) {
+        if constexpr (IsSlot<decltype(s)>::value)
+            return std::integral_constant<int, (decltype(s)::value + decltype(k)::value) & 3>{};
+        else
+            return (int)((s + decltype(k)::value) & 3);
+    };
+    using one = std::integral_constant<int, 1>;
+    using three = std::integral_constant<int, 3>;
+
+    // ---- rotated Q fragments, held for the whole key range
+    u32x4 qf[NS];
+    int rpos;
+    {
+        const int m = wave * 32 + ln;
+        const int ti = m >> p.gshift;
+        const bool valid = ti < w.n_rows;
+        const int row = w.row0 + (valid ? ti : 0);
+        const int qh = w.kv_head * G + (m & (G - 1));
+        const int rp = valid ? p.row_pos[row] : -1;
+        rpos = rp;
+        const uint16_t *qrow = static_cast<const uint16_t *>(p.q) + ((int64_t)row * p.hq + qh) * D;
+        const float *cs = p.rope + (int64_t)(valid ? rp : 0) * D;
+#pragma unroll
+        for (int s = 0; s < NS / 2; ++s) {
+            const int e0 = 16 * s + 8 * lg;
+            u32x4 lo = {0, 0, 0, 0}, hi = {0, 0, 0, 0};
+            if (valid) {
+                lo = *reinterpret_cast<const u32x4 *>(qrow + e0);
+                hi = *reinterpret_cast<const u32x4 *>(qrow + D / 2 + e0);
+            }
+            floatx4 c[2], sn[2];
+            c[0] = *reinterpret_cast<const floatx4 *>(cs + e0);
+            c[1] = *reinterpret_cast<const floatx4 *>(cs + e0 + 4);
+            sn[0] = *reinterpret_cast<const floatx4 *>(cs + D / 2 + e0);
+            sn[1] = *reinterpret_cast<const floatx4 *>(cs + D / 2 + e0 + 4);
+#pragma unroll
+            for (int h = 0; h < 2; ++h) {
+                c[h] *= p.scale_log2;
+                sn[h] *= p.scale_log2;
+            }
+            rope8_bf16(lo, hi, c, sn, qf[s], qf[s + NS / 2]);
+        }
+    }
+    const int rpos0 = __builtin_amdgcn_readfirstlane(rpos);
+    const int wave_rpos0 = rpos0 < 0 ? INT_MAX : rpos0;
+    int rlast = rpos;
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) rlast = max(rlast, __shfl_xor(rlast, o));
+    const int wave_rpos1 = __builtin_amdgcn_readfirstlane(rlast);
+
+    // ---- the item's page table in LDS: physical page, and pos0 << 7 | valid
+    const int n_pages = w.page_end - w.page_begin;
+    for (int i = tid; i < n_pages; i += NT) {
+        const PageDesc d = pg[w.page_begin + i];
+        pg_phys[i] = d.phys;
+        pg_pv[i] = (d.pos0 << 7) | d.valid;
+    }
+    barrier_dl();
+
+    // ---- direct loads. Instruction m (0, 1) of wave wv covers key rows 8 wv + 4 m .. + 3 of a tile
+    // (one page: pages hold at least 16 keys); lane i fetches the global chunk that lands at LDS
+    // chunk position i % 16 of row 8 wv + 4 m + i / 16.
+    const char *kpool_b = static_cast<const char *>(p.k_rot);
+    const char *vpool_b = static_cast<const char *>(p.v_pool);
+    const uint32_t page_bytes = (uint32_t)p.page_elems * 2u;
+    const int lpage0 = w.page_base + w.page_begin;   // logical page of the item's first page
+    const int pg_in_tile = (8 * wv) >> p.pshift;
+    uint32_t k_doff[2], v_doff[2];
+#pragma unroll
+    for (int m = 0; m < 2; ++m) {
+        const int r = 8 * wave + 4 * m + (lane >> 4);
+        const int pc = lane & 15;
+        const uint32_t row_off = (uint32_t)(head_off + (int64_t)(r & (page_size - 1)) * D) * 2u;
+        k_doff[m] = row_off + (uint32_t)((pc ^ (r & 15)) * 16);
+        v_doff[m] = row_off + (uint32_t)((pc ^ (4 * (r & 3))) * 16);
+    }
+    // page of this wave's rows of tile t (keys past the item's range read its last page; the mask
+    // removes them)
+    auto tile_page = [&](int t) { return min(t * ppt + pg_in_tile, n_pages - 1); };
+    auto dma_k = [&](int t, uint16_t *dst, int m) __attribute__((always_inline)) {
+        const uint32_t phys = (uint32_t)(lpage0 + tile_page(t));
+        const char *src = kpool_b + (uint64_t)phys * page_bytes + k_doff[m];
+        dma16(src, lds_addr(dst + (8 * wv + 4 * m) * D));
+    };
+    int v_phys_next = 0;   // V page of the next V tile this wave loads (read from LDS one phase ahead)
+    auto dma_v = [&](uint16_t *dst, int m) __attribute__((always_inline)) {
+        const uint32_t phys = (uint32_t)__builtin_amdgcn_readfirstlane(v_phys_next);
+        const char *src = vpool_b + (uint64_t)phys * page_bytes + v_doff[m];
+        dma16(src, lds_addr(dst + (8 * wv + 4 * m) * D));
+    };
+    // key positions of tile t into ring slot sl, and the wave's mask bit of the slot
+    unsigned mask_ring = 15u;          // bit sl: the tile in slot sl needs the causal/padding mask
+    auto stage_kpos = [&](int t, int sl) __attribute__((always_inline)) {
+        const int rq = t * ppt + (lane >> p.pshift);
+        const int pv = pg_pv[min(rq, n_pages - 1)];
+        const int slot = lane & (page_size - 1);
+        const int kp = rq < n_pages && slot < (pv & 127) ? (pv >> 7) + slot : kNeverAttended;
+        kpos_s[sl * KT + lane] = kp;   // every wave writes the same 64 values
+        const unsigned bit = 1u << sl;
+        mask_ring = __any(kp > wave_rpos0) ? (mask_ring | bit) : (mask_ring & ~bit);
+    };
+    auto wait_loads = [&](auto n) __attribute__((always_inline)) {
+        // s_waitcnt vmcnt(n): lgkmcnt and expcnt left at their maxima
+        __builtin_amdgcn_s_waitcnt((decltype(n)::value & 15) | ((decltype(n)::value >> 4) << 14) | (7 << 4) |
+                                   (15 << 8));
+    };
+
+    // per-lane LDS fragment offsets (elements) of the swizzled rows. K' k-step s of key row ln reads
+    // chunk (2s + lg) ^ (ln & 15): offset kfo0 ^ 16 s, since the XOR only touches bits 4-6. V^T
+    // d block db of key row 4 lg + jj reads chunk (4 db + 2 (gi & 1) + qq / 2) ^ 4 jj: offset
+    // vfo0 ^ 32 db (bits 5-6). Written as XORs of a per-lane base, they cost one VALU each where the
+    // compiler does not keep them in registers.
+    const uint32_t kfo0 = (uint32_t)(ln * D + 8 * (lg ^ (ln & 1)) + 16 * ((ln & 15) >> 1));
+    auto kfo = [&](int s) { return kfo0 ^ (uint32_t)(16 * s); };
+    const int gi = lane >> 4, jj = (lane >> 2) & 3, qq = lane & 3;
+    const uint32_t vfo0 = (uint32_t)((4 * lg + jj) * D + 32 * jj + 16 * (gi & 1) + 4 * qq);
+    auto vfo = [&](int db) { return vfo0 ^ (uint32_t)(32 * db); };
+
+    auto qk = [&](auto ksl, floatx16 (&sacc)[2]) {
+        const uint16_t *kb = kslot(ksl);
+#pragma unroll
+        for (int b = 0; b < 2; ++b)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) sacc[b][r] = 0.0f;
+#pragma unroll
+        for (int s = 0; s < NS; ++s)
+#pragma unroll
+            for (int b = 0; b < 2; ++b) {
+                const bf16x8 a = *reinterpret_cast<const bf16x8 *>(kb + kfo(s) + b * 32 * D);
+                sacc[b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, __builtin_bit_cast(bf16x8, qf[s]), sacc[b],
+                                                                   0, 0, 0);
+            }
+    };
+
+    floatx16 oacc[NDB];
+#pragma unroll
+    for (int db = 0; db < NDB; ++db)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) oacc[db][r] = 0.0f;
+    float mrow = 0.0f, lrow = 0.0f;
+    bool have_max = false;
+    const bf16x8 bias_a = __builtin_bit_cast(bf16x8, u32x4{lg == 0 ? 0x3f80u : 0u, 0u, 0u, 0u});   // e_0
+    u32x4 bias_b = {0u, 0u, 0u, 0u};
+    floatx16 sacc[2];
+    u32x4 pf[2][2];
+
+    auto tile_sum = [&](const float (&e)[2][16]) -> float {
+        float part[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            part[i] = e[i >> 1][8 * (i & 1)];
+#pragma unroll
+            for (int r = 1; r < 8; ++r) part[i] += e[i >> 1][8 * (i & 1) + r];
+        }
+        return (part[0] + part[1]) + (part[2] + part[3]);
+    };
+    auto apply_mask = [&](int sl) __attribute__((always_inline)) {
+        const int *kp = kpos_s + sl * KT;
+#pragma unroll
+        for (int b = 0; b < 2; ++b)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const i32x4 kp4 = *reinterpret_cast<const i32x4 *>(&kp[b * 32 + 8 * i + 4 * lg]);
+#pragma unroll
+                for (int j = 0; j < 4; ++j) sacc[b][4 * i + j] = kp4[j] > rpos ? -INFINITY : sacc[b][4 * i + j];
+            }
+    };
+    // the softmax of one tile (as link_attention_bf16); `loads(j)` issues load j of a later tile,
+    // spread between the exponentials
+    auto softmax = [&](bool masked, int kc, auto loads) __attribute__((always_inline)) {
+        constexpr int NL = decltype(loads)::count;
+        float e[2][16];
+        float lsum = 0.0f;
+        bool exact = masked;
+        if (!masked) {
+#pragma unroll
+            for (int i = 0; i < 32; ++i) {
+                e[i >> 4][i & 15] = __builtin_amdgcn_exp2f(sacc[i >> 4][i & 15]);
+                if (NL > 0 && (i & 7) == 7 && (i >> 3) < NL) {
+                    loads(i >> 3);
+                    __builtin_amdgcn_sched_barrier(0);
+                }
+            }
+            lsum = tile_sum(e);
+            const bool ok = have_max && lsum <= (float)(1 << (int)kRescaleLog2);   // false for inf, NaN
+            exact = __any(!ok);
+        }
+        if (exact) {
+            if (masked) {
+#pragma unroll
+                for (int j = 0; j < NL; ++j) loads(j);
+                apply_mask(kc);
+            }
+            float mx = sacc[0][0];
+#pragma unroll
+            for (int b = 0; b < 2; ++b)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sacc[b][r]);
+            const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(mx), __float_as_uint(mx), false, false);
+            mx = fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1]));
+            float target = mrow;
+            bool first = false;
+            if (mx != -INFINITY) {
+                if (!have_max) {
+                    target = mrow + mx;
+                    first = true;
+                    have_max = true;
+                } else if (mx > 0.0f) {
+                    target = mrow + mx;
+                }
+            }
+            const uint32_t tb = pack_bf16(-target, 0.0f) & 0xffffu;
+            const float mnew = -bf_lo(tb);
+            const float shift = mnew - mrow;
+            const float alpha = first ? 1.0f : __builtin_amdgcn_exp2f(-shift);
+            mrow = mnew;
+            bias_b[0] = lg == 0 ? tb : 0u;
+#pragma unroll
+            for (int b = 0; b < 2; ++b)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) e[b][r] = __builtin_amdgcn_exp2f(sacc[b][r] - shift);
+            lsum = tile_sum(e);
+            lrow *= alpha;
+            if (__any(alpha != 1.0f)) {
+#pragma unroll
+                for (int db = 0; db < NDB; ++db)
+#pragma unroll
+                    for (int r = 0; r < 16; ++r) oacc[db][r] *= alpha;
+            }
+        }
+#pragma unroll
+        for (int b = 0; b < 2; ++b)
+#pragma unroll
+            for (int s2 = 0; s2 < 2; ++s2)
+#pragma unroll
+                for (int u = 0; u < 4; ++u) pf[b][s2][u] = pack_bf16(e[b][8 * s2 + 2 * u], e[b][8 * s2 + 2 * u + 1]);
+        lrow += lsum;
+    };
+
+    // X phase: PV of the tile in V slot vsl, QK^T of the tile in K' slot ksl, MFMAs and their
+    // operand reads only (operands read three MFMAs ahead), plus `vloads` (V of a later tile) after
+    // the first operand reads
+    typedef short v4s __attribute__((ext_vector_type(4)));
+    constexpr int NPV = 4 * NDB;
+    constexpr int NQK = 2 * NS;
+    constexpr int NBIAS = 2;
+    constexpr int AHEAD = 3;
+    v4s vlo[NPV], vhi[NPV];
+    bf16x8 ka[NQK];
+    auto xphase = [&](auto vsl, auto ksl, auto with_qk, auto vloads) __attribute__((always_inline)) {
+        constexpr bool QK = decltype(with_qk)::value;
+        constexpr int NM = NPV + (QK ? NBIAS + NQK : 0);
+        const uint16_t *vb = vslot(vsl);
+        const uint16_t *kb = kslot(ksl);
+        auto read = [&](int i) __attribute__((always_inline)) {
+            if (i < NPV) {
+                const int db = i % NDB, b = (i / NDB) >> 1, s2 = (i / NDB) & 1;
+                const uint16_t *a = vb + vfo(db) + (b * 32 + 16 * s2) * D;
+                vlo[i] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) v4s *)a);
+                vhi[i] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) v4s *)(a + 8 * D));
+            } else if (i >= NPV + NBIAS) {
+                const int j = i - NPV - NBIAS, s = j >> 1, b = j & 1;
+                ka[j] = *reinterpret_cast<const bf16x8 *>(kb + kfo(s) + b * 32 * D);
+            }
+        };
+        auto mma = [&](int i) __attribute__((always_inline)) {
+            if (i < NPV) {
+                const int db = i % NDB, b = (i / NDB) >> 1, s2 = (i / NDB) & 1;
+                const bf16x8 a = __builtin_bit_cast(bf16x8, __builtin_shufflevector(vlo[i], vhi[i], 0, 1, 2, 3, 4, 5, 6, 7));
+                oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, __builtin_bit_cast(bf16x8, pf[b][s2]), oacc[db],
+                                                                   0, 0, 0);
+            } else if (i < NPV + NBIAS) {
+                const floatx16 zero = {};
+                sacc[i - NPV] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bias_a, __builtin_bit_cast(bf16x8, bias_b), zero,
+                                                                        0, 0, 0);
+            } else {
+                const int j = i - NPV - NBIAS, s = j >> 1, b = j & 1;
+                sacc[b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[j], __builtin_bit_cast(bf16x8, qf[s]), sacc[b], 0, 0, 0);
+            }
+        };
+#pragma unroll
+        for (int i = 0; i < AHEAD; ++i) read(i);
+        __builtin_amdgcn_sched_barrier(0);
+        vloads();
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int i = 0; i < NM; ++i) {
+            mma(i);
+            if (i + AHEAD < NM) read(i + AHEAD);
+            __builtin_amdgcn_sched_barrier(0);
+        }
+    };
+
+    const int ntiles = (n_pages + ppt - 1) / ppt;
+    const bool group_b = wave >= 4;
+    int n_act;
+    {
+        int lo = 0, hi = n_pages;
+        while (lo < hi) {
+            const int mid = (lo + hi) >> 1;
+            if ((pg_pv[mid] >> 7) <= wave_rpos1) lo = mid + 1;
+            else hi = mid;
+        }
+        n_act = __builtin_amdgcn_readfirstlane((lo + ppt - 1) / ppt);
+    }
+
+    using yes = std::integral_constant<bool, true>;
+    using no = std::integral_constant<bool, false>;
+    using S0 = std::integral_constant<int, 0>;
+    using S1 = std::integral_constant<int, 1>;
+    using S2 = std::integral_constant<int, 2>;
+    using S3 = std::integral_constant<int, 3>;
+    using W6 = std::integral_constant<int, 6>;
+    using W8 = std::integral_constant<int, 8>;
+    using W10 = std::integral_constant<int, 10>;
+    using W0 = std::integral_constant<int, 0>;
+
+    // ---- prologue: tiles 0, 1, 2 (K', V, positions) in slots 0, 1, 2; QK^T of tile 0
+    auto v_page = [&](int t) { return pg_phys[tile_page(t)]; };
+    auto prologue_tile = [&](int t, auto sl) __attribute__((always_inline)) {
+        dma_k(t, kslot(sl), 0);
+        dma_k(t, kslot(sl), 1);
+        v_phys_next = v_page(t);
+        dma_v(vslot(sl), 0);
+        dma_v(vslot(sl), 1);
+        stage_kpos(t, decltype(sl)::value);
+    };
+    prologue_tile(0, S0{});
+    if (ntiles > 1) prologue_tile(1, S1{});
+    if (ntiles > 2) prologue_tile(2, S2{});
+    if (ntiles > 3) v_phys_next = v_page(3);
+    if (ntiles > 2) wait_loads(W10{});
+    else wait_loads(W0{});
+    barrier_dl();
+    qk(S0{}, sacc);
+    if (group_b) {
+        // A's X(0) needs K'(1) and V(0) of every wave
+        if (ntiles > 2) wait_loads(W6{});
+        else wait_loads(W0{});
+        barrier_dl();
+    }
+
+    // one tile. Y(t): softmax of tile t with K'(t+3) loaded between its exponentials, positions of
+    // tile t+3; X(t): PV of tile t, QK^T of tile t+1, V(t+3) loaded. `stage`: tile t+3 exists.
+    auto step = [&](int t, auto sl, auto next_qk, auto stage, auto active) __attribute__((always_inline)) {
+        constexpr bool STAGE = decltype(stage)::value;
+        constexpr bool ACT = decltype(active)::value;
+        const auto sl1 = slot_plus(sl, one{});
+        const auto sl3 = slot_plus(sl, three{});
+        uint16_t *kdst = kslot(sl3);
+        if constexpr (ACT) {
+            const bool masked = (mask_ring >> (int)sl) & 1u;
+            auto kload = [&](int j) __attribute__((always_inline)) {
+                if constexpr (STAGE) dma_k(t + 3, kdst, j);
+            };
+            softmax(masked, (int)sl, Loads<STAGE ? 2 : 0, decltype(kload) &>{kload});
+        } else if constexpr (STAGE) {
+            dma_k(t + 3, kdst, 0);
+            dma_k(t + 3, kdst, 1);
+        }
+        if constexpr (STAGE) stage_kpos(t + 3, (int)sl3);
+        __builtin_amdgcn_sched_barrier(0);
+        // group A's X(t) needs K'(t+1) (8 later loads may be in flight); B's X(t) follows this
+        // barrier too and needs the same
+        if constexpr (STAGE) wait_loads(W8{});
+        else wait_loads(W0{});
+        barrier_dl();
+        uint16_t *vdst = vslot(sl3);
+        auto vload = [&]() __attribute__((always_inline)) {
+            if constexpr (STAGE) {
+                dma_v(vdst, 0);
+                dma_v(vdst, 1);
+            }
+        };
+        if constexpr (ACT) {
+            xphase(sl, sl1, next_qk, vload);
+        } else {
+            vload();
+        }
+        // the V page of the next tile this wave loads, read from LDS ahead of its use
+        if constexpr (STAGE) {
+            if (t + 4 < ntiles) v_phys_next = v_page(t + 4);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+        // the barrier that ends B's X(t) opens A's X(t+1), which needs K'(t+2) (6 later loads may be
+        // in flight); for A this is one phase early
+        if constexpr (STAGE) wait_loads(W6{});
+        else wait_loads(W0{});
+        barrier_dl();
+    };
+
+    int t = 0;
+    const int t_main = min(n_act, ntiles - 3);
+    for (; t + 4 <= t_main; t += 4) {
+        step(t, S0{}, yes{}, yes{}, yes{});
+        step(t + 1, S1{}, yes{}, yes{}, yes{});
+        step(t + 2, S2{}, yes{}, yes{}, yes{});
+        step(t + 3, S3{}, yes{}, yes{}, yes{});
+    }
+    if (t < t_main) step(t++, S0{}, yes{}, yes{}, yes{});
+    if (t < t_main) step(t++, S1{}, yes{}, yes{}, yes{});
+    if (t < t_main) step(t++, S2{}, yes{}, yes{}, yes{});
+    // waves past their last key tile keep loading tiles for the others
+    for (; t + 3 < ntiles; ++t) step(t, t & 3, no{}, yes{}, no{});
+    if (t + 2 < ntiles) {
+        if (t < n_act) step(t, t & 3, yes{}, no{}, yes{});
+        else step(t, t & 3, no{}, no{}, no{});
+        ++t;
+    }
+    if (t + 1 < ntiles) {
+        if (t < n_act) step(t, t & 3, yes{}, no{}, yes{});
+        else step(t, t & 3, no{}, no{}, no{});
+        ++t;
+    }
+    if (t < ntiles) {
+        if (t < n_act) step(t, t & 3, no{}, no{}, yes{});
+        else step(t, t & 3, no{}, no{}, no{});
+    }
+    if (!group_b) barrier_dl();
+
+    // ---- epilogue: normalise, write the output (or this split's partial result)
+    {
+        const int m = wave * 32 + ln;
+        const int ti = m >> p.gshift;
+        const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(lrow), __float_as_uint(lrow), false, false);
+        const float lt = __uint_as_float(sw[0]) + __uint_as_float(sw[1]);
+        const float inv = lt > 0.0f ? 1.0f / lt : 0.0f;
+        const float lse_v = lt > 0.0f ? (mrow + __builtin_amdgcn_logf(lt)) * 0.6931471805599453f : -INFINITY;
+        if (ti < w.n_rows) {
+            const int row = w.row0 + ti;
+            const int qh = w.kv_head * G + (m & (G - 1));
+            if (w.partial < 0) {
+                uint16_t *orow = static_cast<uint16_t *>(p.out) + ((int64_t)row * p.hq + qh) * D;
+#pragma unroll
+                for (int db = 0; db < NDB; ++db)
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        const int d0 = db * 32 + 8 * i + 4 * lg;
+                        u32x2 v;
+                        v[0] = pack_bf16(oacc[db][4 * i] * inv, oacc[db][4 * i + 1] * inv);
+                        v[1] = pack_bf16(oacc[db][4 * i + 2] * inv, oacc[db][4 * i + 3] * inv);
+                        *reinterpret_cast<u32x2 *>(orow + d0) = v;
+                    }
+                if (p.lse && lg == 0) p.lse[(int64_t)row * p.hq + qh] = lse_v;
+            } else {
+                float *po = p.part_o + ((int64_t)w.partial * TQ + m) * D;
+#pragma unroll
+                for (int db = 0; db < NDB; ++db)
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        const int d0 = db * 32 + 8 * i + 4 * lg;
+                        floatx4 v = {oacc[db][4 * i] * inv, oacc[db][4 * i + 1] * inv, oacc[db][4 * i + 2] * inv,
+                                     oacc[db][4 * i + 3] * inv};
+                        *reinterpret_cast<floatx4 *>(po + d0) = v;
+                    }
+                if (lg == 0) p.part_lse[(int64_t)w.partial * TQ + m] = lse_v;
+            }
+        }
+    }
+}
+
+// ---------------------------------------------------------------------------------------------
 // fp32 attention. Work group = 4 waves of one 32-row MFMA block each (128 M-rows).
 //   S^T = K' Q'^T   (v_mfma_f32_32x32x2f32; lane group lg supplies dimension 8(s/4) + 4lg + s%4
 //                    at k-step s, so each lane reads 4 consecutive dimensions per 4 steps)
@@ -1684,7 +2244,7 @@ hipError_t launch_attention(const LayerShape &s, const void *q, const void *k_po
     dim3 grid(t.n_work);
     if (s.dtype == 0) {
         if (t.k_rot) {
-            if (s.d == 128) hipLaunchKernelGGL((link_attention_bf16<128, true, false>), grid, dim3(512), 0, stream, p);
+            if (s.d == 128) hipLaunchKernelGGL(link_attention_bf16_dl<128>, grid, dim3(512), 0, stream, p);
             else hipLaunchKernelGGL((link_attention_bf16<64, true, false>), grid, dim3(512), 0, stream, p);
         } else if (s.key_layout) {
             if (s.d == 128) hipLaunchKernelGGL((link_attention_bf16<128, false, true>), grid, dim3(512), 0, stream, p);
