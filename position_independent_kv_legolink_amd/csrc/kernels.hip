@@ -1126,8 +1126,8 @@ __global__ __launch_bounds__(512, 1) void link_attention_bf16_dl(AttnParams p) {
     };
 
     // X phase: PV of the tile in V slot vsl, QK^T of the tile in K' slot ksl, MFMAs and their
-    // operand reads only (operands read three MFMAs ahead), plus `vloads` (V of a later tile) after
-    // the first operand reads
+    // operand reads only (operands read three MFMAs ahead), then `vloads` (V of a later tile). The
+    // V loads go last: issued at the start they slowed the operand reads of the same phase.
     typedef short v4s __attribute__((ext_vector_type(4)));
     constexpr int NPV = 4 * NDB;
     constexpr int NQK = 2 * NS;
@@ -1169,14 +1169,14 @@ __global__ __launch_bounds__(512, 1) void link_attention_bf16_dl(AttnParams p) {
 #pragma unroll
         for (int i = 0; i < AHEAD; ++i) read(i);
         __builtin_amdgcn_sched_barrier(0);
-        vloads();
-        __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
         for (int i = 0; i < NM; ++i) {
             mma(i);
             if (i + AHEAD < NM) read(i + AHEAD);
             __builtin_amdgcn_sched_barrier(0);
         }
+        vloads();
+        __builtin_amdgcn_sched_barrier(0);
     };
 
     const int ntiles = (n_pages + ppt - 1) / ppt;
