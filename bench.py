@@ -269,11 +269,13 @@ def decode_measure(job, steps=DECODE_STEPS, warmup=DECODE_WARMUP):
     items = plan.sizes["decode_items"]
     ws_mb = plan.sizes["workspace_bytes"] / 1e6
     rot_mb = plan.sizes["rotated_key_bytes"] / 1e6
+    # decode reads the link call's rotated copy when it made one, else rotates the pool's keys
+    keys = "rotated copy" if plan.sizes["rotated_pages"] else "pool, rotated in the kernel"
     plan.free()
     gbps = nbytes / (ms * 1e-3) / 1e9
     return {"requests": n, "ms": round(ms, 4), "work_items": items, "algorithmic_mb": round(nbytes / 1e6, 1),
             "gbps": round(gbps, 1), "hbm_frac": round(gbps / PEAK_HBM_GBPS, 4),
-            "workspace_mb": round(ws_mb, 1), "rotated_keys_mb": round(rot_mb, 1)}
+            "workspace_mb": round(ws_mb, 1), "rotated_keys_mb": round(rot_mb, 1), "keys": keys}
 
 
 def model_measure(cfg, shape_name="llama3_8b", steps=5, warmup=2, gemm_reps=10):

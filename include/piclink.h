@@ -138,8 +138,9 @@ typedef struct {
  *              are bit-identical to 1); 0 = automatic: 2 for bfloat16 stores when
  *              the work list reads each key page at least 5 times on average,
  *              else 1. Other values: PIC_ERR_INVALID.
- * decode       T > 0: also prepare T steps of pic_link_decode (bfloat16 stores; keys are
- *              then always rotated ahead, so rope_keys must be 0 or 2). Every request gets T
+ * decode       T > 0: also prepare T steps of pic_link_decode (bfloat16 stores; any
+ *              rope_keys: decode reads the keys rotated ahead when the link call rotates them
+ *              ahead, else rotates the pool's keys itself). Every request gets T
  *              decode slots after its last token, positions end .. end + T - 1: the tail of
  *              its suffix's last page and further private pages (a private segment of their
  *              own when the request has no suffix). They count toward max_position and the
@@ -159,10 +160,13 @@ typedef struct {
  * rotated_pages = logical pages whose keys pic_link_attend rotates into the
  * workspace before attention (0: keys are rotated inside attention);
  * decode_items = split-KV work items of pic_link_decode (0: plan not made for decode);
- * workspace_bytes = table_bytes (the uploaded tables) + partial_bytes (float32 partial
- * results of split key ranges, link and decode) + rotated_key_bytes (the keys of every logical
- * page rotated ahead of attention: a per-request copy of shared pages, 0 when keys are rotated
- * inside attention) + alignment. */
+ * workspace_bytes = table_bytes (the uploaded tables) + the larger of the link call's scratch,
+ * partial_bytes (float32 partial results of split key ranges) + rotated_key_bytes (the keys of
+ * every logical page rotated ahead of attention: a per-request copy of shared pages, 0 when keys
+ * are rotated inside attention), and decode's, decode_partial_bytes (float32 partial results of
+ * decode's page ranges), + alignment. Both scratch regions start at the same offset when the keys
+ * are rotated inside attention (decode runs after the link call and needs none of its scratch);
+ * with rotated_pages, decode reads the rotated keys and its partials follow them. */
 typedef struct {
     int64_t rows;
     int64_t pages;
@@ -177,6 +181,7 @@ typedef struct {
     int64_t table_bytes;
     int64_t partial_bytes;
     int64_t rotated_key_bytes;
+    int64_t decode_partial_bytes;
 } pic_plan_sizes;
 
 /* Device bytes the caller must provide: each K and V pool
@@ -413,11 +418,17 @@ pic_status pic_link_attend_static(pic_store *store, const pic_plan *plan, const 
  *   k, v   [n_req][Hkv][d]  their keys (pre-RoPE) and values
  *   out    [n_req][Hq][d]   attention output, store dtype
  *   lse    [n_req][Hq]      optional float32 natural-log softmax denominators
- * The cache's keys are read as the link call rotated them into the workspace. Split-KV: every
+ * The cache's keys: when the plan has rotated_pages (the link call rotated every page's keys
+ * into the workspace), decode reads that copy, and each step adds its token's rotated key to it;
+ * else decode reads the pools as stored and rotates the keys itself (by their position, or by
+ * their segment's start in a PIC_KEYS_SEGMENT_ROPE store), and the plan keeps no rotated copy:
+ * the choice between speed and workspace is the link call's rope_keys. Split-KV: every
  * (request, KV head) is cut into page ranges whose partial results are merged with the token's
- * own score. pic_link_attend zeroes the decode slots and restarts at step 0. The workspace
- * must still hold this plan (no other plan uploaded over it since pic_link_attend), because
- * the rotated keys and decode tables live there. Errors, each returned before any launch:
+ * own score. pic_link_attend zeroes the decode slots and restarts at step 0. Decode must run after
+ * that pic_link_attend in stream order (it reads the rows the link call scattered, and its partial
+ * results may reuse the link call's workspace scratch). The workspace must still hold this plan
+ * (no other plan uploaded over it since pic_link_attend), because the decode tables (and rotated
+ * keys) live there. Errors, each returned before any launch:
  * PIC_ERR_WORKSPACE (too small, or the workspace does not hold this plan's tables),
  * PIC_ERR_STATE (plan not made for decode, pic_link_attend not run on this workspace since
  * its last upload, or all T steps used), PIC_ERR_INVALID (null tensor). Asynchronous on

@@ -83,7 +83,7 @@ class PlanSizes(ctypes.Structure):
                 ("split_items", ctypes.c_int64), ("workspace_bytes", ctypes.c_int64),
                 ("requests", ctypes.c_int64), ("rotated_pages", ctypes.c_int64), ("decode_items", ctypes.c_int64),
                 ("table_bytes", ctypes.c_int64), ("partial_bytes", ctypes.c_int64),
-                ("rotated_key_bytes", ctypes.c_int64)]
+                ("rotated_key_bytes", ctypes.c_int64), ("decode_partial_bytes", ctypes.c_int64)]
 
 
 _lib = None

@@ -418,10 +418,11 @@ pic_status pic_plan_info(const pic_plan *plan, pic_plan_sizes *sz) {
         sz->workspace_bytes = plan->workspace_bytes;
         sz->requests = plan->n_requests;
         sz->rotated_pages = plan->rotate_keys ? (int64_t)plan->pages.size() : 0;
-        sz->decode_items = (int64_t)plan->dec_work.size();
+        sz->decode_items = plan->n_dec_slots;
         sz->table_bytes = plan->table_bytes;
-        sz->partial_bytes = (plan->off_k_rot - plan->off_part_o) + (plan->off_end - plan->off_dec_o);
-        sz->rotated_key_bytes = plan->off_dec_o - plan->off_k_rot;
+        sz->partial_bytes = plan->off_k_rot - plan->off_part_o;
+        sz->rotated_key_bytes = plan->off_link_end - plan->off_k_rot;
+        sz->decode_partial_bytes = plan->off_dec_end - plan->off_dec_o;
     });
 }
 
@@ -528,7 +529,8 @@ pic_status pic_link_decode(pic_store *s, const pic_plan *plan, const void *q, co
             fail(PIC_ERR_WORKSPACE, "the workspace does not hold this plan's tables (never uploaded there, or "
                                     "another plan was uploaded over them)");
         if (plan->attended_ws != workspace)
-            fail(PIC_ERR_STATE, "run pic_link_attend on this workspace first (it rotates the keys decode reads)");
+            fail(PIC_ERR_STATE, "run pic_link_attend on this workspace first (it writes the recomputed rows and "
+                                "clears the decode slots that decode reads)");
         if (plan->dec_next >= plan->dec_steps)
             fail(PIC_ERR_STATE, "all " + std::to_string(plan->dec_steps) + " reserved decode steps are used");
         if (plan->n_requests == 0) return;
@@ -544,6 +546,7 @@ pic_status pic_link_decode(pic_store *s, const pic_plan *plan, const void *q, co
         t.n_merge = (int)plan->dec_merge.size();
         t.part_o = reinterpret_cast<float *>(ws + plan->off_dec_o);
         t.part_lse = reinterpret_cast<float *>(ws + plan->off_dec_lse);
+        t.max_pos = s->cfg.max_position;
         t.k_rot = plan->rotate_keys ? ws + plan->off_k_rot : nullptr;
         check_hip(launch_decode(s->shape, q, k, v, s->k_pool, s->v_pool, s->rope, t, out, lse, stream),
                   "decode launch");

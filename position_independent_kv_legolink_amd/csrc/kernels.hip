@@ -1825,15 +1825,25 @@ __global__ __launch_bounds__(kThreads) void rotate_keys_bf16(const PageDesc *pag
 // heads of one KV head over a page range of its request. The G heads take the columns of the
 // 32x32 MFMA blocks (lanes of rows G..31 hold zero queries), so the arithmetic is that of
 // link_attention_bf16 with one 32-key block at a time:
-//   S^T = K' Q'^T   (A = 32 keys loaded from the rotated-key workspace straight into registers)
+//   S^T = K' Q'^T   (A = 32 keys loaded from the pool straight into registers and rotated there:
+//                    lane pieces s and s + NS/2 hold the rotation pairs (e, e + d/2) of one key)
 //   O^T += V^T P^T  (A = V^T from transposing LDS reads of the block's values, staged per wave)
+// Keys come from the link call's rotated copy when it made one (read as they are), else from the
+// pools, read as stored and rotated here, so that decode needs no per-request copy of shared
+// pages. A key of a store of keys rotated inside their segment turns by its segment's rotation (one
+// cos/sin row per page, as rotate_keys_bf16 turns it). A position-free key at position t = b + o
+// (b = its page's first position plus its slot rounded down to 16, o = slot mod 16) turns by
+// R(b) R(o): the cos/sin of t come from rows b and o by the angle-addition formulas, so a 32-key
+// block reads two rows of the table (one per 16-key group, staged through LDS) and the 16 rows of
+// o sit in LDS, instead of one row per key.
 // Wave w takes the item's 32-key blocks w, w+4, ... with its own online softmax (fp32, log2
 // units; every key of the cache lies before the new token, so only padding is masked). The four
 // waves' results are merged through LDS into the item's partial slot: the normalised output and
 // its log2-sum-exp.
 struct DecodeParams {
     const void *q;
-    const void *k_rot;
+    const void *k_rot;               // keys rotated ahead [logical page][Hkv][page][d], or null
+    const void *k_pool;
     const void *v_pool;
     const float *rope;
     const PageDesc *pages;
@@ -1844,10 +1854,14 @@ struct DecodeParams {
     int hq, hkv, gshift, pshift, step;
     int64_t page_elems;
     float scale_log2;
+    int max_pos;                     // rows of the RoPE table
 };
 
-template <int D>
+constexpr int kDecRotated = 0, kDecPosition = 1, kDecSegment = 2;   // where decode's keys come from
+
+template <int D, int KM>
 __global__ __launch_bounds__(256, 2) void link_decode_bf16(DecodeParams p) {
+    constexpr bool KR = KM == kDecRotated, SEG = KM == kDecSegment;
     constexpr int NS = D / 16;          // k-steps of QK^T; also 16-byte V pieces per lane
     constexpr int NDB = D / 32;
     constexpr int VS = D + 32;          // V row stride in LDS, as in link_attention_bf16
@@ -1857,9 +1871,12 @@ __global__ __launch_bounds__(256, 2) void link_decode_bf16(DecodeParams p) {
     __shared__ __attribute__((aligned(16))) int kval[NW * 32];
     __shared__ float obuf[NW * MAXG * D];
     __shared__ float mbuf[NW * MAXG], lbuf[NW * MAXG];
-    __shared__ int dpg_phys[kMaxItemPages], dpg_pv[kMaxItemPages];
+    __shared__ int dpg_phys[kMaxDecodePages], dpg_pv[kMaxDecodePages];
+    __shared__ __attribute__((aligned(16))) float slot_cs[KM == kDecPosition ? 16 * D : 4];   // table rows 0..15
+    __shared__ __attribute__((aligned(16))) float base_cs[KR ? 4 : NW * 2 * D];   // per wave: the block's 2 rows
 
     const DecodeDesc w = p.work[blockIdx.x];
+    if (w.partial < 0) return;   // empty slot of the work list
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, ln = lane & 31, lg = lane >> 5;
     const int G = 1 << p.gshift;
     const int page_size = 1 << p.pshift;
@@ -1873,6 +1890,9 @@ __global__ __launch_bounds__(256, 2) void link_decode_bf16(DecodeParams p) {
         const PageDesc d = p.pages[lpage0 + i];
         dpg_phys[i] = d.phys;
         dpg_pv[i] = (d.pos0 << 7) | d.valid;
+    }
+    if constexpr (KM == kDecPosition) {
+        for (int i = tid; i < 16 * D; i += 256) slot_cs[i] = i / D < p.max_pos ? p.rope[i] : 0.0f;
     }
     __syncthreads();
     // the new token's position: keys at or after it (this step's token and later decode slots) are
@@ -1915,8 +1935,9 @@ __global__ __launch_bounds__(256, 2) void link_decode_bf16(DecodeParams p) {
 
     uint16_t *vb = vbuf + wave * 32 * VS;
     int *kv = kval + wave * 32;
-    const char *krot_b = static_cast<const char *>(p.k_rot);
+    const char *kpool_b = static_cast<const char *>(p.k_pool);
     const char *vpool_b = static_cast<const char *>(p.v_pool);
+    const char *rope_b = reinterpret_cast<const char *>(p.rope);
     const int nblk = (n_pages * page_size + 31) >> 5;
     for (int blk = wave; blk < nblk; blk += NW) {
         // the lane's key for the A operand (both lane halves hold key ln)
@@ -1926,15 +1947,42 @@ __global__ __launch_bounds__(256, 2) void link_decode_bf16(DecodeParams p) {
         const bool in_range = rel < n_pages;
         const int rc = in_range ? rel : n_pages - 1;
         const int pv = dpg_pv[rc];
-        const bool ok = in_range && slot < (pv & 127) && (pv >> 7) + slot < qpos;
-        const char *krow = krot_b + (uint64_t)(uint32_t)(lpage0 + rc) * page_bytes + (uint32_t)(head_off + slot * D) * 2u;
+        const bool filled = in_range && slot < (pv & 127);
+        const bool ok = filled && (pv >> 7) + slot < qpos;
+        const uint32_t kpage = KR ? (uint32_t)(lpage0 + rc) : (uint32_t)dpg_phys[rc];
+        const char *krow = (KR ? static_cast<const char *>(p.k_rot) : kpool_b) + (uint64_t)kpage * page_bytes +
+                           (uint32_t)(head_off + slot * D) * 2u;
+        // the cos/sin row of each 16-key group of the block (padding slots hold zeros, which rotate
+        // to zeros with any row): its segment's rotation (negative: the row of its magnitude, sines
+        // negated), or b, the position of the group's first slot; row o = slot mod 16 of a key's
+        // position comes from slot_cs. One 16-byte piece per lane, through LDS.
+        constexpr int LPR = D / 4;   // lanes per row
+        u32x4 brow_piece = {0u, 0u, 0u, 0u};
+        const int bg = lane / LPR;
+        if (!KR && bg < 2) {
+            const int gk = blk * 32 + 16 * bg;
+            const int grc = min(gk >> p.pshift, n_pages - 1);
+            int row;
+            uint32_t neg = 0u;
+            if constexpr (SEG) {
+                const int r = p.pages[lpage0 + grc].seg0;
+                row = r < 0 ? -r : r;
+                neg = r < 0 && (lane % LPR) >= LPR / 2 ? 0x80000000u : 0u;   // the sine half
+            } else {
+                row = min((dpg_pv[grc] >> 7) + (gk & (page_size - 1)), p.max_pos - 1);
+            }
+            brow_piece = *reinterpret_cast<const u32x4 *>(rope_b + (uint64_t)(uint32_t)row * (uint32_t)(D * 4) +
+                                                          (lane % LPR) * 16);
+#pragma unroll
+            for (int u = 0; u < 4; ++u) brow_piece[u] ^= neg;
+        }
         // K: NS 16-byte pieces of the A operand. V: NS loads, each a contiguous run of RPI rows of
         // the block (a page holds whole runs: RPI <= 8 <= page size), lane = (row, 16-byte chunk)
         constexpr int RPI = 512 / D, CPR = D / 8;
-        bf16x8 ka[NS];
+        u32x4 kr[NS];
         u32x4 vr[NS];
 #pragma unroll
-        for (int s = 0; s < NS; ++s) ka[s] = *reinterpret_cast<const bf16x8 *>(krow + (16 * s + 8 * lg) * 2);
+        for (int s = 0; s < NS; ++s) kr[s] = *reinterpret_cast<const u32x4 *>(krow + (16 * s + 8 * lg) * 2);
 #pragma unroll
         for (int i = 0; i < NS; ++i) {
             const int vk = blk * 32 + i * RPI + lane / CPR;
@@ -1943,13 +1991,56 @@ __global__ __launch_bounds__(256, 2) void link_decode_bf16(DecodeParams p) {
                                (uint32_t)(head_off + (vk & (page_size - 1)) * D) * 2u;
             vr[i] = *reinterpret_cast<const u32x4 *>(vrow + (lane % CPR) * 16);
         }
-        // the previous block's transposing reads of this wave's V buffer are complete
+        // the previous block's reads of this wave's LDS buffers are complete
         __builtin_amdgcn_s_waitcnt(0xc07f);   // lgkmcnt(0)
         __builtin_amdgcn_wave_barrier();
+        float *bcs = base_cs + wave * 2 * D;
+        if (!KR && bg < 2) *reinterpret_cast<u32x4 *>(&bcs[bg * D + (lane % LPR) * 4]) = brow_piece;
 #pragma unroll
         for (int i = 0; i < NS; ++i) *reinterpret_cast<u32x4 *>(&vb[(i * RPI + lane / CPR) * VS + (lane % CPR) * 8]) = vr[i];
         if (lg == 0) kv[ln] = ok ? 1 : 0;
-
+        __builtin_amdgcn_s_waitcnt(0xc07f);
+        __builtin_amdgcn_wave_barrier();
+        const float *cs_row = bcs + (ln >> 4) * D;   // the lane's key's group
+        const int orow = ln & 15;                    // its slot mod 16
+        bf16x8 ka[NS];
+#pragma unroll
+        for (int s = 0; s < NS / 2 && KR; ++s) {
+            ka[s] = __builtin_bit_cast(bf16x8, kr[s]);
+            ka[s + NS / 2] = __builtin_bit_cast(bf16x8, kr[s + NS / 2]);
+        }
+#pragma unroll
+        for (int s = 0; s < NS / 2 && !KR; ++s) {
+            const int e0 = 16 * s + 8 * lg;
+            floatx4 c[2], sn[2];
+#pragma unroll
+            for (int h = 0; h < 2; ++h) {
+                c[h] = *reinterpret_cast<const floatx4 *>(&cs_row[e0 + 4 * h]);
+                sn[h] = *reinterpret_cast<const floatx4 *>(&cs_row[D / 2 + e0 + 4 * h]);
+            }
+            if constexpr (KM == kDecPosition) {
+                // cos/sin(b + o) from the rows of b and of o
+#pragma unroll
+                for (int h = 0; h < 2; ++h) {
+                    const floatx4 c2 = *reinterpret_cast<const floatx4 *>(&slot_cs[orow * D + e0 + 4 * h]);
+                    const floatx4 s2 = *reinterpret_cast<const floatx4 *>(&slot_cs[orow * D + D / 2 + e0 + 4 * h]);
+                    floatx4 cc, ss;
+#pragma unroll
+                    for (int u = 0; u < 4; ++u) {
+                        cc[u] = fmaf(c[h][u], c2[u], -(sn[h][u] * s2[u]));
+                        ss[u] = fmaf(sn[h][u], c2[u], c[h][u] * s2[u]);
+                    }
+                    c[h] = cc;
+                    sn[h] = ss;
+                }
+            }
+            u32x4 lo, hi;
+            rope8_bf16(kr[s], kr[s + NS / 2], c, sn, lo, hi);
+            ka[s] = __builtin_bit_cast(bf16x8, lo);
+            ka[s + NS / 2] = __builtin_bit_cast(bf16x8, hi);
+            // one step's cos/sin live at a time
+            __builtin_amdgcn_sched_barrier(0);
+        }
         floatx16 sacc = (floatx16)(0.0f);
 #pragma unroll
         for (int s = 0; s < NS; ++s)
@@ -2056,7 +2147,7 @@ struct DecodeMergeParams {
     const float *part_lse;
     void *out;
     float *lse;
-    void *k_pool, *v_pool, *k_rot;   // the token's decode slot is written here
+    void *k_pool, *v_pool, *k_rot;   // the token's decode slot is written here (k_rot: when present)
     int hq, hkv, gshift, pshift, step;
     int64_t page_elems;
     float scale_log2;
@@ -2093,32 +2184,43 @@ __global__ __launch_bounds__(512) void link_decode_merge(DecodeMergeParams p) {
         for (int o = 32; o > 0; o >>= 1) dot += __shfl_xor(dot, o);
         if (lane == 0) s_new_sh = dot;   // log2 units
         // the first query head of the KV head writes the token into its decode slot, for the
-        // later steps: its key and value into the pools, its rotated key into the rotated keys
+        // later steps: its key (in the pool's key form) and value into the pools, and its rotated
+        // key into the rotated copy when decode reads keys from there
         if (hl == 0 && lane < D / 2) {
             const int page_size = 1 << p.pshift;
             const int lp = dr.lpage0 + ((dr.off + p.step) >> p.pshift);
             const int slot = (dr.off + p.step) & (page_size - 1);
             const int64_t row = (int64_t)(md.kv_head * page_size + slot) * D;
             const int64_t phys_row = (int64_t)p.pages[lp].phys * p.page_elems + row;
-            const int64_t rot_row = (int64_t)lp * p.page_elems + row;
             const uint16_t *vr = static_cast<const uint16_t *>(p.v) + ((int64_t)md.request * p.hkv + md.kv_head) * D;
             uint16_t *kp_ = static_cast<uint16_t *>(p.k_pool), *vp_ = static_cast<uint16_t *>(p.v_pool);
-            uint16_t *kr_ = static_cast<uint16_t *>(p.k_rot);
+            uint32_t krot = kp;   // the rotated copy's form: as the link call rotates the pool's key
             if (p.seg_keys) {
-                // the pool's form: rotated at the token's position inside its segment
+                // the pool's form: rotated at the token's position inside its segment; the copy
+                // turns that by the segment's rotation (negative: the row of its magnitude, sines
+                // negated), as the link call turns every stored key
                 const float *cl = p.rope + (int64_t)(pos - dr.seg0) * D;
                 const float c2 = cl[i], s2 = cl[D / 2 + i];
                 const uint32_t kl = pack_bf16(fmaf(kx, c2, -ky * s2), fmaf(ky, c2, kx * s2));
                 kp_[phys_row + i] = (uint16_t)(kl & 0xffffu);
                 kp_[phys_row + i + D / 2] = (uint16_t)(kl >> 16);
+                const int r = dr.seg0;
+                const float *cr = p.rope + (int64_t)(r < 0 ? -r : r) * D;
+                const float c3 = cr[i], s3 = r < 0 ? -cr[D / 2 + i] : cr[D / 2 + i];
+                const float lx = bf_lo(kl), ly = bf_hi(kl);
+                krot = pack_bf16(fmaf(lx, c3, -ly * s3), fmaf(ly, c3, lx * s3));
             } else {
                 kp_[phys_row + i] = kr[i];
                 kp_[phys_row + i + D / 2] = kr[i + D / 2];
             }
             vp_[phys_row + i] = vr[i];
             vp_[phys_row + i + D / 2] = vr[i + D / 2];
-            kr_[rot_row + i] = (uint16_t)(kp & 0xffffu);
-            kr_[rot_row + i + D / 2] = (uint16_t)(kp >> 16);
+            if (p.k_rot) {
+                uint16_t *kr_ = static_cast<uint16_t *>(p.k_rot);
+                const int64_t rot_row = (int64_t)lp * p.page_elems + row;
+                kr_[rot_row + i] = (uint16_t)(krot & 0xffffu);
+                kr_[rot_row + i + D / 2] = (uint16_t)(krot >> 16);
+            }
         }
     }
     float mloc = -INFINITY;
@@ -2263,14 +2365,13 @@ hipError_t launch_attention(const LayerShape &s, const void *q, const void *k_po
 hipError_t launch_decode(const LayerShape &s, const void *q, const void *k, const void *v, void *k_pool, void *v_pool,
                          const float *rope, const DecodeTables &t, void *out, float *lse, hipStream_t stream) {
     if (s.dtype != 0) return hipErrorInvalidValue;
-    if (t.n_merge > 0 && !t.k_rot) return hipErrorInvalidValue;
     const int gshift = log2_exact(s.hq / s.hkv);
     const float scale_log2 = 1.4426950408889634f / sqrtf((float)s.d);
     if (t.n_work > 0) {
-        if (!t.k_rot) return hipErrorInvalidValue;
         DecodeParams p;
         p.q = q;
         p.k_rot = t.k_rot;
+        p.k_pool = k_pool;
         p.v_pool = v_pool;
         p.rope = rope;
         p.pages = t.pages;
@@ -2285,8 +2386,18 @@ hipError_t launch_decode(const LayerShape &s, const void *q, const void *k, cons
         p.pshift = log2_exact(s.page_size);
         p.page_elems = s.page_elems;
         p.scale_log2 = scale_log2;
-        if (s.d == 128) hipLaunchKernelGGL(link_decode_bf16<128>, dim3(t.n_work), dim3(256), 0, stream, p);
-        else hipLaunchKernelGGL(link_decode_bf16<64>, dim3(t.n_work), dim3(256), 0, stream, p);
+        p.max_pos = t.max_pos;
+        const dim3 grid(t.n_work);
+        if (t.k_rot) {
+            if (s.d == 128) hipLaunchKernelGGL((link_decode_bf16<128, kDecRotated>), grid, dim3(256), 0, stream, p);
+            else hipLaunchKernelGGL((link_decode_bf16<64, kDecRotated>), grid, dim3(256), 0, stream, p);
+        } else if (s.key_layout) {
+            if (s.d == 128) hipLaunchKernelGGL((link_decode_bf16<128, kDecSegment>), grid, dim3(256), 0, stream, p);
+            else hipLaunchKernelGGL((link_decode_bf16<64, kDecSegment>), grid, dim3(256), 0, stream, p);
+        } else {
+            if (s.d == 128) hipLaunchKernelGGL((link_decode_bf16<128, kDecPosition>), grid, dim3(256), 0, stream, p);
+            else hipLaunchKernelGGL((link_decode_bf16<64, kDecPosition>), grid, dim3(256), 0, stream, p);
+        }
         const hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
     }

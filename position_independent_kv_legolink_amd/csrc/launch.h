@@ -65,7 +65,9 @@ struct DecodeTables {
     int n_merge;
     float *part_o;                   // [item][G][d]: normalised partial outputs
     float *part_lse;                 // [item][G]: their log2-sum-exp (scores in log2 units)
-    void *k_rot;                     // pre-rotated keys [logical page][Hkv][page][d]
+    int max_pos;                     // rows of the RoPE table
+    void *k_rot;                     // keys rotated ahead [logical page][Hkv][page][d], or null: decode
+                                     // then rotates the pool's keys itself
 };
 
 // Decode attention (split-KV over the pre-rotated keys and the pool's values), then the merge of

@@ -58,7 +58,7 @@ struct MergeDesc {
 
 // One decode work item: the new token of request `request` (the G query heads of KV head
 // kv_head) over the logical pages [page_begin, page_end) of that request. Every item writes a
-// partial result into slot `partial`.
+// partial result into slot `partial` (-1: an empty slot of the work list, which does nothing).
 struct DecodeDesc {
     int32_t page_base;   // index of the request's logical page 0 in the PageDesc table
     int32_t page_begin;
@@ -90,6 +90,7 @@ struct DecodeMergeDesc {
 
 constexpr int kKeysPerTile = 64;   // keys staged in LDS per attention iteration
 constexpr int kMaxItemPages = 2048;  // longest KV range of one attention work item (its page table sits in LDS)
+constexpr int kMaxDecodePages = 1024;  // longest KV range of one decode work item (its page table sits in LDS)
 // Positions are packed with a page's valid count into one 32-bit word (pos0 << 7 | valid) and
 // cos/sin rows are addressed with 32-bit byte offsets: both hold below this bound.
 constexpr int kMaxPosition = 1 << 22;

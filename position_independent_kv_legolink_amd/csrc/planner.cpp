@@ -46,8 +46,6 @@ pic_plan *build_plan(pic_store *s, const pic_request *reqs, int32_t n_reqs, cons
         fail(PIC_ERR_INVALID, "keys are rotated ahead of attention for bfloat16 stores only");
     if (o.decode < 0 || o.decode > kMaxPosition) fail(PIC_ERR_INVALID, "decode must be in [0, max_position]");
     if (o.decode && cfg.dtype != PIC_DTYPE_BF16) fail(PIC_ERR_INVALID, "decode after link needs a bfloat16 store");
-    if (o.decode && o.rope_keys == 1)
-        fail(PIC_ERR_INVALID, "decode reads keys rotated ahead of attention: rope_keys must be 0 or 2");
 
     // keys rotated inside their segment carry the compile offset on top of their position there
     const int32_t c_off = cfg.key_layout == PIC_KEYS_SEGMENT_ROPE ? cfg.compile_offset : 0;
@@ -192,8 +190,6 @@ pic_plan *build_plan(pic_store *s, const pic_request *reqs, int32_t n_reqs, cons
         else if (o.rope_keys == 0)
             plan->rotate_keys = cfg.dtype == PIC_DTYPE_BF16 && total >= (int64_t)kRotateReuse * page_heads;
     }
-    // decode reads every key page once per step: its keys are rotated once, at link time
-    if (o.decode) plan->rotate_keys = !plan->pages.empty();
     int64_t max_pages;
     if (o.split_pages > 0) {
         max_pages = align_up(o.split_pages, ppt);
@@ -260,23 +256,48 @@ pic_plan *build_plan(pic_store *s, const pic_request *reqs, int32_t n_reqs, cons
             plan->dec_req.push_back(
                 {ends[r], plan->cu_pages[r + 1] - seg_pages, g.length - o.decode, (int32_t)(g.start - c_off)});
         }
-        // a range's page table sits in LDS: at most kMaxItemPages pages
+        // a range's page table sits in LDS: at most kMaxDecodePages pages
         const int64_t per_item = std::min<int64_t>(
-            kMaxItemPages, std::max<int64_t>(4, (page_heads + 2 * s->num_cus - 1) / (2 * s->num_cus)));
+            kMaxDecodePages, std::max<int64_t>(4, (page_heads + 2 * s->num_cus - 1) / (2 * s->num_cus)));
+        // partial slots: (request, KV head) major, ranges in order, as the merge reads them
+        std::vector<std::vector<DecodeDesc>> by_range;   // [request's range][KV head]
+        int32_t n_slots = 0;
         for (int r = 0; r < n_reqs; ++r) {
             const int32_t n = plan->cu_pages[r + 1] - plan->cu_pages[r];
+            const int32_t n_split = n > 0 ? (int32_t)((n + per_item - 1) / per_item) : 0;
+            const int32_t step = n_split > 0 ? (n + n_split - 1) / n_split : 1;
+            const size_t g0 = by_range.size();
+            for (int32_t b = 0; b < n; b += step) by_range.emplace_back();
+            const int32_t used = (int32_t)(by_range.size() - g0);
             for (int h = 0; h < cfg.num_kv_heads; ++h) {
-                const int32_t slot0 = (int32_t)plan->dec_work.size();
-                if (n > 0) {
-                    const int32_t n_split = (int32_t)((n + per_item - 1) / per_item);
-                    const int32_t step = (n + n_split - 1) / n_split;
-                    for (int32_t b = 0; b < n; b += step)
-                        plan->dec_work.push_back({plan->cu_pages[r], b, std::min(n, b + step), r, h,
-                                                  (int32_t)plan->dec_work.size(), 0, 0});
-                }
-                plan->dec_merge.push_back({r, h, (int32_t)plan->dec_work.size() - slot0, slot0});
+                plan->dec_merge.push_back({r, h, used, n_slots});
+                int32_t i = 0;
+                for (int32_t b = 0; b < n; b += step, ++i)
+                    by_range[g0 + i].push_back({plan->cu_pages[r], b, std::min(n, b + step), r, h, n_slots + i, 0, 0});
+                n_slots += used;
             }
         }
+        // work groups are dispatched round-robin over the XCDs (slot i on XCD i % 8): the KV heads
+        // of one page range go to one XCD, one after another, so that the cos/sin rows of the
+        // range's keys are read into that XCD's L2 once. Empty slots (partial -1) exit at once.
+        constexpr int kXcds = 8;
+        std::vector<std::vector<DecodeDesc>> bucket(kXcds);
+        for (size_t g = 0; g < by_range.size(); ++g)
+            for (const DecodeDesc &d : by_range[g]) bucket[g % kXcds].push_back(d);
+        size_t depth = 0;
+        for (auto &b : bucket) depth = std::max(depth, b.size());
+        int n_used = 0;
+        for (auto &b : bucket) n_used += b.empty() ? 0 : 1;
+        if (n_used == 1 || (int64_t)depth * kXcds > 2 * (int64_t)n_slots) {
+            // too few ranges to fill the XCDs evenly: plain order
+            for (auto &b : by_range)
+                for (const DecodeDesc &d : b) plan->dec_work.push_back(d);
+        } else {
+            plan->dec_work.assign(depth * kXcds, DecodeDesc{0, 0, 0, 0, 0, -1, 0, 0});
+            for (int x = 0; x < kXcds; ++x)
+                for (size_t i = 0; i < bucket[x].size(); ++i) plan->dec_work[i * kXcds + x] = bucket[x][i];
+        }
+        plan->n_dec_slots = n_slots;
     }
 
     // ---- workspace layout
@@ -295,13 +316,21 @@ pic_plan *build_plan(pic_store *s, const pic_request *reqs, int32_t n_reqs, cons
     plan->off_dec_work = place((int64_t)plan->dec_work.size() * sizeof(DecodeDesc));
     plan->off_dec_merge = place((int64_t)plan->dec_merge.size() * sizeof(DecodeMergeDesc));
     plan->table_bytes = off;
+    // the link call's scratch (split partials, rotated keys) and decode's partials share one
+    // region: decode runs after the link call, in stream order, and reads neither, unless the keys
+    // are rotated ahead: decode then reads the rotated copy, and its partials follow it
+    const int64_t scratch0 = off;
     const int64_t tq = tile_qrows(cfg.dtype);
     plan->off_part_o = place((int64_t)plan->n_slots * tq * cfg.head_dim * sizeof(float));
     plan->off_part_lse = place((int64_t)plan->n_slots * tq * sizeof(float));
     const int64_t elem = cfg.dtype == PIC_DTYPE_BF16 ? 2 : 4;
     plan->off_k_rot = place(plan->rotate_keys ? (int64_t)plan->pages.size() * s->shape.page_elems * elem : 0);
-    plan->off_dec_o = place((int64_t)plan->dec_work.size() * G * cfg.head_dim * sizeof(float));
-    plan->off_dec_lse = place((int64_t)plan->dec_work.size() * G * sizeof(float));
+    plan->off_link_end = off;
+    if (!plan->rotate_keys) off = scratch0;
+    plan->off_dec_o = place((int64_t)plan->n_dec_slots * G * cfg.head_dim * sizeof(float));
+    plan->off_dec_lse = place((int64_t)plan->n_dec_slots * G * sizeof(float));
+    plan->off_dec_end = off;
+    off = std::max(plan->off_link_end, plan->off_dec_end);
     plan->off_end = off;
     plan->workspace_bytes = std::max<int64_t>(off, 256);
     return plan;

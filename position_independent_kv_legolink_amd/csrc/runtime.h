@@ -112,7 +112,11 @@ struct pic_plan {
     std::vector<piclink::DecodeReq> dec_req;
     std::vector<piclink::DecodeDesc> dec_work;
     std::vector<piclink::DecodeMergeDesc> dec_merge;
+    int32_t n_dec_slots = 0;            // decode partial slots: the items of dec_work that are not empty
     int64_t off_dec_req = 0, off_dec_work = 0, off_dec_merge = 0, off_dec_o = 0, off_dec_lse = 0, off_end = 0;
+    // the link call's scratch [off_part_o, off_link_end) and decode's partials [off_dec_o,
+    // off_dec_end) start at the same offset
+    int64_t off_link_end = 0, off_dec_end = 0;
     const void *attended_ws = nullptr;  // workspace of the last pic_link_attend since the last upload
 };
 

@@ -161,25 +161,35 @@ def test_plan_sizes_report_workspace():
 
 
 def test_workspace_breakdown_adds_up():
-    """table_bytes + partial_bytes + rotated_key_bytes (+ 256-byte alignment) = workspace_bytes;
-    the rotated keys are one page of keys per logical page, the partials one float32 row per
-    split slot (link) or decode item."""
+    """table_bytes + max(partial_bytes + rotated_key_bytes, decode_partial_bytes) (+ 256-byte
+    alignment) = workspace_bytes: the link call's scratch and decode's partials share one region,
+    except when the keys are rotated ahead (decode then reads them and its partials follow).
+    The rotated keys are one page of keys per logical page, the link partials one float32 row per
+    split slot, the decode partials one per decode item and query head."""
     s = meta(num_pages=400)
     for c in range(6):
         s.store_chunk(c, n_tokens=300)
     req = [pic.LinkRequest(list(range(6)), 40)]
-    for kw in (dict(rope_keys=1), dict(rope_keys=2), dict(rope_keys=1, split_pages=4), dict(decode=3)):
+    page_bytes = 2 * 16 * 128 * 2          # Hkv 2, page 16, d 128, bf16
+    for kw in (dict(rope_keys=1), dict(rope_keys=2), dict(rope_keys=1, split_pages=4), dict(decode=3),
+               dict(decode=3, rope_keys=2), dict(decode=3, rope_keys=1, split_pages=4)):
         plan = s.link_plan(req, k=3, **kw)
         z = plan.sizes
-        parts = z["table_bytes"] + z["partial_bytes"] + z["rotated_key_bytes"]
+        link = z["partial_bytes"] + z["rotated_key_bytes"]
+        if z["rotated_pages"]:   # decode reads the rotated keys: its partials follow them
+            parts = z["table_bytes"] + link + z["decode_partial_bytes"]
+        else:
+            parts = z["table_bytes"] + max(link, z["decode_partial_bytes"])
         assert parts <= z["workspace_bytes"] <= parts + 8 * 256, (kw, z)
-        page_bytes = 2 * 16 * 128 * 2          # Hkv 2, page 16, d 128, bf16
         assert z["rotated_key_bytes"] >= z["rotated_pages"] * page_bytes
         assert z["rotated_key_bytes"] < z["rotated_pages"] * page_bytes + 256
-        if z["split_items"] == 0 and z["decode_items"] == 0:
-            assert z["partial_bytes"] == 0
+        assert (z["partial_bytes"] > 0) == (z["split_items"] > 0), (kw, z)
+        if kw.get("decode"):
+            # 1 request, 2 KV heads, G = 4 query heads: d floats and one lse per head and item
+            assert z["decode_items"] > 0
+            assert z["decode_partial_bytes"] >= z["decode_items"] * 4 * (128 + 1) * 4
         else:
-            assert z["partial_bytes"] > 0
+            assert z["decode_items"] == 0 and z["decode_partial_bytes"] == 0
         plan.free()
 
 
@@ -221,21 +231,25 @@ def test_rotated_keys_take_one_page_per_logical_page_of_workspace():
 
 
 def test_decode_option_is_validated():
-    """decode=1 rotates every key page ahead and builds one decode item per (request, KV head)
-    range; it needs a bf16 store, keys rotated ahead (rope_keys 0 or 2) and a RoPE table row for
-    the new token's position."""
+    """decode=1 builds one decode item per (request, KV head) range and rotates nothing ahead for
+    decode (the decode kernel rotates the keys it reads), with either rope_keys mode of the link
+    call; it needs a bf16 store and a RoPE table row for the new token's position."""
     s = meta()
     s.store_chunk(1, n_tokens=40)
     plan = s.link_plan([pic.LinkRequest([1], 5)], k=2, decode=True)
     assert plan.sizes["decode_items"] == 2            # 1 request x 2 KV heads, 4 pages each
-    assert plan.sizes["rotated_pages"] == plan.sizes["pages"] == 4
-    plan.free()
+    assert plan.sizes["pages"] == 4
     plain = s.link_plan([pic.LinkRequest([1], 5)], k=2)
     assert plain.sizes["decode_items"] == 0
+    # the same link choice as without decode
+    assert plan.sizes["rotated_pages"] == plain.sizes["rotated_pages"]
+    plan.free()
     plain.free()
-    with pytest.raises(pic.PicError) as e:
-        s.link_plan([pic.LinkRequest([1], 5)], k=2, decode=True, rope_keys=1)
-    assert e.value.status == -1
+    for rk in (1, 2):
+        p = s.link_plan([pic.LinkRequest([1], 5)], k=2, decode=True, rope_keys=rk)
+        assert p.sizes["decode_items"] == 2
+        assert p.sizes["rotated_pages"] == (4 if rk == 2 else 0)
+        p.free()
     # the request ends at position 4095 = the last table row: linking is fine, the decode token
     # at 4096 has no row
     s.link_plan([pic.LinkRequest([1], 5)], k=2, pos_offset=4096 - 45).free()

@@ -66,7 +66,7 @@ def rotate_at(x, pos, theta):
 
 
 def run_decode(cfg, *, n_requests=None, pos_offset=0, repeat=1, with_oracle=True, steps=1,
-               key_layout="position_free", compile_offset=0):
+               key_layout="position_free", compile_offset=0, rope_keys=0):
     wl = Workload(cfg, n_requests=n_requests)
     segs = wl.segments(pos_offset=pos_offset, k=cfg.k)
     cached = wl.cached()
@@ -80,9 +80,11 @@ def run_decode(cfg, *, n_requests=None, pos_offset=0, repeat=1, with_oracle=True
                       max_position=pos_offset + n_tokens + steps + compile_offset + 1, key_layout=key_layout,
                       compile_offset=compile_offset)
     plan = store.link_plan(wl.link_requests(), k=cfg.k, block_level=cfg.block_level, pos_offset=pos_offset,
-                           decode=steps)
+                           decode=steps, rope_keys=rope_keys)
     n = len(segs)
-    assert plan.sizes["decode_items"] > 0 and plan.sizes["rotated_pages"] == plan.sizes["pages"]
+    assert plan.sizes["decode_items"] > 0
+    if rope_keys:
+        assert plan.sizes["rotated_pages"] == (plan.sizes["pages"] if rope_keys == 2 else 0)
     dev = lambda a: torch.from_numpy(np.ascontiguousarray(a)).to("cuda", torch.bfloat16).contiguous()
     q, kn, vn = (dev(np.concatenate([r[i] for r in rows])) for i in range(3))
     tokens = [decode_rows(cfg, n, cfg.seed, i) for i in range(steps)]
@@ -191,3 +193,20 @@ def test_decode_positions_at_the_limit(key_layout):
     _say(f"decode, positions up to {offset + n_tokens + steps - 1}, {key_layout} keys")
     check(cfg, run_decode(cfg, pos_offset=offset, steps=steps, key_layout=key_layout),
           f"decode positions at 2^22, {key_layout} keys")
+
+
+@pytest.mark.parametrize("key_layout", ["position_free", "segment_rope"])
+def test_decode_does_not_depend_on_the_link_rotation_mode(key_layout):
+    """Decode reads the rotated copy when the link call rotated the keys ahead of attention
+    (rope_keys 2), else the pools, rotating the keys itself (rope_keys 1): both match the oracle,
+    and for keys rotated inside their segment (one cos/sin row per page either way) they agree bit
+    for bit. Position-free keys are rotated from one row per key ahead and from two rows (angle
+    addition) in decode, which may round differently."""
+    cfg = small_cfg(chunk_len=80, n_requests=3, suffix_len=7)
+    _say(f"decode after both link rotation modes, {key_layout} keys")
+    runs = {rk: run_decode(cfg, steps=3, key_layout=key_layout, rope_keys=rk) for rk in (1, 2)}
+    for rk, res in runs.items():
+        check(cfg, res, f"decode after rope_keys {rk}, {key_layout} keys")
+    if key_layout == "segment_rope":
+        for (o1, l1, _), (o2, l2, _) in zip(runs[1], runs[2]):
+            assert np.array_equal(o1[0], o2[0]) and np.array_equal(l1, l2)
