@@ -683,6 +683,10 @@ def main():
                 "rotate_ms": round(c_prof["rotate_ms"] / cc, 4), "scatter_ms": round(c_prof["scatter_ms"] / cc, 4),
                 "merge_ms": round(c_prof["merge_ms"] / cc, 4)}
         log(f"cold (MALL evicted before each step, steps not overlapped with planning): {cold}")
+        # the same kernel with its K/V out of the MALL: launches of the cold leg
+        achieved_cold = flop / (c_attn * 1e-3) / 1e12
+        roofline["achieved_cold"] = round(achieved_cold, 2)
+        roofline["frac_cold"] = round(achieved_cold / peak, 4)
 
     decode = None
     if not args.no_decode and cfg.dtype == "bf16":
