@@ -91,6 +91,7 @@ struct DecodeMergeDesc {
 constexpr int kKeysPerTile = 64;   // keys staged in LDS per attention iteration
 constexpr int kMaxItemPages = 2048;  // longest KV range of one attention work item (its page table sits in LDS)
 constexpr int kMaxDecodePages = 1024;  // longest KV range of one decode work item (its page table sits in LDS)
+constexpr int kDecodeMinPages = 96;    // decode ranges shorter than this give way to one range per compute unit
 // Positions are packed with a page's valid count into one 32-bit word (pos0 << 7 | valid) and
 // cos/sin rows are addressed with 32-bit byte offsets: both hold below this bound.
 constexpr int kMaxPosition = 1 << 22;

@@ -256,9 +256,14 @@ pic_plan *build_plan(pic_store *s, const pic_request *reqs, int32_t n_reqs, cons
             plan->dec_req.push_back(
                 {ends[r], plan->cu_pages[r + 1] - seg_pages, g.length - o.decode, (int32_t)(g.start - c_off)});
         }
-        // a range's page table sits in LDS: at most kMaxDecodePages pages
-        const int64_t per_item = std::min<int64_t>(
-            kMaxDecodePages, std::max<int64_t>(4, (page_heads + 2 * s->num_cus - 1) / (2 * s->num_cus)));
+        // about two ranges per compute unit over the batch; where that makes ranges shorter than
+        // kDecodeMinPages and one per unit still fills every unit, one per unit, so that fewer,
+        // longer ranges carry the set-up and the merge has fewer partial results. A range's page
+        // table sits in LDS: at most kMaxDecodePages pages.
+        int64_t per_item = (page_heads + 2 * s->num_cus - 1) / (2 * s->num_cus);
+        if (per_item < kDecodeMinPages && page_heads >= (int64_t)kDecodeMinPages * s->num_cus)
+            per_item = (page_heads + s->num_cus - 1) / s->num_cus;
+        per_item = std::min<int64_t>(kMaxDecodePages, std::max<int64_t>(4, per_item));
         // partial slots: (request, KV head) major, ranges in order, as the merge reads them
         std::vector<std::vector<DecodeDesc>> by_range;   // [request's range][KV head]
         int32_t n_slots = 0;
