@@ -2135,8 +2135,9 @@ __global__ __launch_bounds__(256, 2) void link_decode_bf16(DecodeParams p) {
 // Decode merge: one work group per (request, query head). The new token's own score (its rotated
 // query against its rotated key, both rounded to bf16 as the attention kernels round them) joins
 // the partial results of the request's page ranges; the output is their log-sum-exp weighted
-// mean. The ranges' weights are formed in parallel and staged in LDS; groups of D threads then
-// sum disjoint sets of ranges, one output dimension per thread.
+// mean. Thread (g, d) folds ranges g, g + NG, ... of output dimension d into a running
+// (maximum, weight sum, weighted sum), loading R ranges at a time before using them, so the merge
+// waits for memory about once; one LDS round then combines the NG groups with the token's score.
 struct DecodeMergeParams {
     const void *q, *k, *v;
     const float *rope;
@@ -2156,32 +2157,70 @@ struct DecodeMergeParams {
 
 template <int D>
 __global__ __launch_bounds__(512) void link_decode_merge(DecodeMergeParams p) {
-    constexpr int NT = 512, NWV = NT / 64, NG = NT / D;
-    constexpr int FB = 1024;            // range weights staged per round
-    __shared__ float fbuf[FB];
-    __shared__ float acc[NG * D];
-    __shared__ float red[NWV];
+    constexpr int NT = 512, NG = NT / D;
+    constexpr int R = 8;                // ranges a thread loads before folding them in
+    __shared__ float part_m[NG * D], part_l[NG * D], part_s[NG * D];
     __shared__ float s_new_sh;
     const int G = 1 << p.gshift;
     const DecodeMergeDesc md = p.merge[blockIdx.x >> p.gshift];
     const int hl = blockIdx.x & (G - 1), h = md.kv_head * G + hl;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int d = tid % D, grp = tid / D;
     const DecodeReq dr = p.dec_req[md.request];
     const int pos = dr.pos + p.step;
-    const float *lse_r = p.part_lse + (int64_t)md.slot0 * G + hl;   // range j at lse_r[j * G]
+    // the token's rows, loaded ahead of the ranges (wave 0 forms its score from them)
+    const int i = lane & (D / 2 - 1);   // rotation pair (i, i + D/2); lanes past D/2 repeat it
+    const uint16_t *qr = static_cast<const uint16_t *>(p.q) + ((int64_t)md.request * p.hq + h) * D;
+    const uint16_t *kr = static_cast<const uint16_t *>(p.k) + ((int64_t)md.request * p.hkv + md.kv_head) * D;
+    const uint16_t *vr = static_cast<const uint16_t *>(p.v) + ((int64_t)md.request * p.hkv + md.kv_head) * D;
+    float c = 0.0f, sn = 0.0f, qx = 0.0f, qy = 0.0f, kx = 0.0f, ky = 0.0f;
     if (wave == 0) {
-        const int i = lane & (D / 2 - 1);   // rotation pair (i, i + D/2); lanes past D/2 repeat it
-        const float c = p.rope[(int64_t)pos * D + i], sn = p.rope[(int64_t)pos * D + D / 2 + i];
-        const uint16_t *qr = static_cast<const uint16_t *>(p.q) + ((int64_t)md.request * p.hq + h) * D;
-        const uint16_t *kr = static_cast<const uint16_t *>(p.k) + ((int64_t)md.request * p.hkv + md.kv_head) * D;
-        const float qx = bf_lo(qr[i]), qy = bf_lo(qr[i + D / 2]);
-        const float kx = bf_lo(kr[i]), ky = bf_lo(kr[i + D / 2]);
+        c = p.rope[(int64_t)pos * D + i];
+        sn = p.rope[(int64_t)pos * D + D / 2 + i];
+        qx = bf_lo(qr[i]);
+        qy = bf_lo(qr[i + D / 2]);
+        kx = bf_lo(kr[i]);
+        ky = bf_lo(kr[i + D / 2]);
+    }
+
+    const float *lse_r = p.part_lse + (int64_t)md.slot0 * G + hl;              // range j at lse_r[j * G]
+    const float *po = p.part_o + ((int64_t)md.slot0 * G + hl) * D + d;         // range j at po[j * G * D]
+    float m = -INFINITY, l = 0.0f, o = 0.0f;
+    for (int j0 = grp; j0 < md.n_split; j0 += NG * R) {
+        float lv[R], ov[R];
+#pragma unroll
+        for (int u = 0; u < R; ++u) {
+            const int j = j0 + u * NG;
+            const bool in = j < md.n_split;
+            lv[u] = in ? lse_r[(int64_t)j * G] : -INFINITY;
+            ov[u] = in ? po[(int64_t)j * G * D] : 0.0f;
+        }
+        float mx = m;
+#pragma unroll
+        for (int u = 0; u < R; ++u) mx = fmaxf(mx, lv[u]);
+        if (mx != -INFINITY) {
+            const float sc = __builtin_amdgcn_exp2f(m - mx);   // 0 while m is -inf
+            l *= sc;
+            o *= sc;
+#pragma unroll
+            for (int u = 0; u < R; ++u) {
+                const float f = __builtin_amdgcn_exp2f(lv[u] - mx);
+                l += f;
+                o += f * ov[u];
+            }
+            m = mx;
+        }
+    }
+    part_m[grp * D + d] = m;
+    part_l[grp * D + d] = l;
+    part_s[grp * D + d] = o;
+    if (wave == 0) {
         const float cq = c * p.scale_log2, sq = sn * p.scale_log2;
         const uint32_t qp = pack_bf16(fmaf(qx, cq, -qy * sq), fmaf(qy, cq, qx * sq));
         const uint32_t kp = pack_bf16(fmaf(kx, c, -ky * sn), fmaf(ky, c, kx * sn));
         float dot = lane < D / 2 ? bf_lo(qp) * bf_lo(kp) + bf_hi(qp) * bf_hi(kp) : 0.0f;
 #pragma unroll
-        for (int o = 32; o > 0; o >>= 1) dot += __shfl_xor(dot, o);
+        for (int o2 = 32; o2 > 0; o2 >>= 1) dot += __shfl_xor(dot, o2);
         if (lane == 0) s_new_sh = dot;   // log2 units
         // the first query head of the KV head writes the token into its decode slot, for the
         // later steps: its key (in the pool's key form) and value into the pools, and its rotated
@@ -2192,7 +2231,6 @@ __global__ __launch_bounds__(512) void link_decode_merge(DecodeMergeParams p) {
             const int slot = (dr.off + p.step) & (page_size - 1);
             const int64_t row = (int64_t)(md.kv_head * page_size + slot) * D;
             const int64_t phys_row = (int64_t)p.pages[lp].phys * p.page_elems + row;
-            const uint16_t *vr = static_cast<const uint16_t *>(p.v) + ((int64_t)md.request * p.hkv + md.kv_head) * D;
             uint16_t *kp_ = static_cast<uint16_t *>(p.k_pool), *vp_ = static_cast<uint16_t *>(p.v_pool);
             uint32_t krot = kp;   // the rotated copy's form: as the link call rotates the pool's key
             if (p.seg_keys) {
@@ -2223,50 +2261,24 @@ __global__ __launch_bounds__(512) void link_decode_merge(DecodeMergeParams p) {
             }
         }
     }
-    float mloc = -INFINITY;
-    for (int j = tid; j < md.n_split; j += NT) mloc = fmaxf(mloc, lse_r[(int64_t)j * G]);
-#pragma unroll
-    for (int o = 32; o > 0; o >>= 1) mloc = fmaxf(mloc, __shfl_xor(mloc, o));
-    if (lane == 0) red[wave] = mloc;
-    __syncthreads();
-    const float s_new = s_new_sh;
-    float m = s_new;
-#pragma unroll
-    for (int w = 0; w < NWV; ++w) m = fmaxf(m, red[w]);
-    __syncthreads();
-    const int d = tid % D, grp = tid / D;
-    float o = 0.0f, den = 0.0f;
-    for (int j0 = 0; j0 < md.n_split; j0 += FB) {
-        const int nj = min(FB, md.n_split - j0);
-        for (int j = tid; j < nj; j += NT) {
-            const float f = __builtin_amdgcn_exp2f(lse_r[(int64_t)(j0 + j) * G] - m);
-            fbuf[j] = f;
-            den += f;
-        }
-        __syncthreads();
-        const float *po = p.part_o + ((int64_t)(md.slot0 + j0) * G + hl) * D + d;
-#pragma unroll 4
-        for (int j = grp; j < nj; j += NG) o += fbuf[j] * po[(int64_t)j * G * D];
-        __syncthreads();
-    }
-#pragma unroll
-    for (int k = 32; k > 0; k >>= 1) den += __shfl_xor(den, k);
-    if (lane == 0) red[wave] = den;
-    acc[grp * D + d] = o;
     __syncthreads();
     if (tid < D) {
-        const float f_new = __builtin_amdgcn_exp2f(s_new - m);
-        float dsum = f_new, osum = 0.0f;
+        const float s_new = s_new_sh;
+        float mm = s_new;
 #pragma unroll
-        for (int w = 0; w < NWV; ++w) dsum += red[w];
+        for (int g = 0; g < NG; ++g) mm = fmaxf(mm, part_m[g * D + tid]);
+        const float f_new = __builtin_amdgcn_exp2f(s_new - mm);
+        float den = f_new, osum = f_new * bf_lo(vr[tid]);
 #pragma unroll
-        for (int g = 0; g < NG; ++g) osum += acc[g * D + tid];
-        const uint16_t *vr = static_cast<const uint16_t *>(p.v) + ((int64_t)md.request * p.hkv + md.kv_head) * D;
-        osum += f_new * bf_lo(vr[tid]);
+        for (int g = 0; g < NG; ++g) {
+            const float f = __builtin_amdgcn_exp2f(part_m[g * D + tid] - mm);   // 0 for a group without ranges
+            den += part_l[g * D + tid] * f;
+            osum += part_s[g * D + tid] * f;
+        }
         uint16_t *orow = static_cast<uint16_t *>(p.out) + ((int64_t)md.request * p.hq + h) * D;
-        orow[tid] = (uint16_t)(pack_bf16(osum / dsum, 0.0f) & 0xffffu);
+        orow[tid] = (uint16_t)(pack_bf16(osum / den, 0.0f) & 0xffffu);
         if (tid == 0 && p.lse)
-            p.lse[(int64_t)md.request * p.hq + h] = (m + __builtin_amdgcn_logf(dsum)) * 0.6931471805599453f;
+            p.lse[(int64_t)md.request * p.hq + h] = (mm + __builtin_amdgcn_logf(den)) * 0.6931471805599453f;
     }
 }
 
