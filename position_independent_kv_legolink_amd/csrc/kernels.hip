@@ -1166,13 +1166,23 @@ __global__ __launch_bounds__(512, 1) void link_attention_bf16_dl(AttnParams p) {
                 sacc[b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[j], __builtin_bit_cast(bf16x8, qf[s]), sacc[b], 0, 0, 0);
             }
         };
+        // issue order: the bias MFMAs first, then PV and QK^T alternating, so that each QK^T MFMA
+        // follows the previous one on its accumulator four MFMAs later (two when they ran back to
+        // back): 1.25% shorter at the 50k-token request. Each accumulator keeps its order, so the
+        // results are those of the plain order bit for bit.
+        auto op = [&](int k) -> int {
+            if constexpr (!QK) return k;
+            if (k < NBIAS) return NPV + k;
+            const int r = k - NBIAS;
+            return (r & 1) ? NPV + NBIAS + (r >> 1) : (r >> 1);
+        };
 #pragma unroll
-        for (int i = 0; i < AHEAD; ++i) read(i);
+        for (int k = 0; k < AHEAD; ++k) read(op(k));
         __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-        for (int i = 0; i < NM; ++i) {
-            mma(i);
-            if (i + AHEAD < NM) read(i + AHEAD);
+        for (int k = 0; k < NM; ++k) {
+            mma(op(k));
+            if (k + AHEAD < NM) read(op(k + AHEAD));
             __builtin_amdgcn_sched_barrier(0);
         }
         vloads();
