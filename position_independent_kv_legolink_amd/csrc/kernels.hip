@@ -24,6 +24,7 @@
 #include <type_traits>
 
 #include "launch.h"
+#include "lds_dma.h"
 
 namespace piclink {
 namespace {
@@ -807,27 +808,6 @@ __global__ __launch_bounds__(512, 1) void link_attention_bf16(AttnParams p) {
 //   - Before the barrier that opens group A's X(t), every wave waits for its own loads of K'(t+1)
 //     and V(t): group A at the end of Y(t) (8 later load instructions may stay in flight), group B
 //     at the end of its X(t-1) (6 may).
-// Work-group barrier of the direct-load kernel: this wave's LDS operations complete (lgkmcnt), then
-// s_barrier; the memory clobber keeps the compiler from moving memory accesses across it. A memory
-// fence would also wait for every direct load in flight (they are LDS writes to the memory model)
-// and expose their latency at every barrier: the loads a barrier has to cover are waited for with
-// an explicit vmcnt before it.
-__device__ __forceinline__ void barrier_dl() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
-
-// One direct load: 16 bytes per lane from `src` into LDS at byte lds + 16 * lane (global_load_lds
-// with its LDS base in M0). Issued from asm, so the compiler does not track it: the kernel waits
-// for its loads itself (vmcnt) before the barriers that publish them. Loads the compiler does not
-// count can only make its own vmcnt waits for other loads stricter, never too weak (they
-// complete in order).
-__device__ __forceinline__ void dma16(const void *src, uint32_t lds) {
-    asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(src), "s"(lds) : "memory", "m0");
-}
-
-// LDS byte address of a __shared__ location.
-__device__ __forceinline__ uint32_t lds_addr(const void *p) {
-    return (uint32_t)(uintptr_t)(const void __attribute__((address_space(3))) *)p;
-}
-
 template <typename T>
 struct IsSlot : std::false_type {};
 template <int V>

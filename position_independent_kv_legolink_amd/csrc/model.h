@@ -15,6 +15,7 @@ enum LinearEpilogue : int {
 
 // C = A W^T over bf16 operands with fp32 accumulation: A [m][k], W [n][k] (both row-major, k
 // contiguous); n a multiple of 128, k a multiple of 64 (kSplit3: split0 and split1 multiples of 64).
+// n a multiple of 256 runs the kernel whose operand tiles are loaded straight into LDS.
 struct LinearCall {
     const void *a;
     const void *w;

@@ -12,6 +12,7 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "lds_dma.h"
 #include "model.h"
 
 namespace piclink {
@@ -55,6 +56,69 @@ struct LinearParams {
     const uint16_t *residual; // kResidual: [M][N] added to the product (may alias out[0])
     int tiles_m, tiles_n;
 };
+
+// The epilogue of both GEMM kernels: the wave's 64 x 64 slice of C at rows m0 + 64 wm, columns
+// n0 + 64 wn, from its 2 x 2 accumulator blocks (n block i, m block j).
+__device__ __forceinline__ void store_tile(const LinearParams &p, const floatx16 (&acc)[2][2], int m0, int n0, int wm,
+                                           int wn, int ln, int lg) {
+    // epilogue: lane (ln, lg) of block (i, j) holds C[row][col .. col + 3] in accumulators
+    // 4g .. 4g + 3, row = m0 + 64 wm + 32 j + ln, col = n0 + 64 wn + 32 i + 8 g + 4 lg
+    if (p.epilogue == kSwiGlu) {
+        // W rows alternate 32 gate rows and 32 up rows: block i = 0 holds gate, i = 1 up, for the
+        // output columns (n0 + 64 wn) / 2 + 8 g + 4 lg .. + 3
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+            const int row = m0 + 64 * wm + 32 * j + ln;
+            if (row >= p.m) continue;
+            uint16_t *orow = p.out[0] + (int64_t)row * p.ld_out[0] + (n0 + 64 * wn) / 2;
+#pragma unroll
+            for (int g = 0; g < 4; ++g) {
+                float v[4];
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const float gt = acc[0][j][4 * g + e], up = acc[1][j][4 * g + e];
+                    v[e] = gt / (1.0f + __expf(-gt)) * up;
+                }
+                u32x2 o = {pack_bf16(v[0], v[1]), pack_bf16(v[2], v[3])};
+                *reinterpret_cast<u32x2 *>(orow + 8 * g + 4 * lg) = o;
+            }
+        }
+        return;
+    }
+    // column ranges of the split outputs (a 32-column block never straddles two of them)
+    int which = 0, col_base = 0;
+    if (p.epilogue == kSplit3) {
+        const int c0 = n0 + 64 * wn;
+        which = c0 >= p.split0 + p.split1 ? 2 : c0 >= p.split0 ? 1 : 0;
+        col_base = which == 2 ? p.split0 + p.split1 : which == 1 ? p.split0 : 0;
+    }
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+        const int row = m0 + 64 * wm + 32 * j + ln;
+        if (row >= p.m) continue;
+#pragma unroll
+        for (int i = 0; i < 2; ++i) {
+            const int col = n0 + 64 * wn + 32 * i - col_base;
+            uint16_t *orow = p.out[which] + (int64_t)row * p.ld_out[which] + col;
+            const uint16_t *rrow = p.residual ? p.residual + (int64_t)row * p.n + n0 + 64 * wn + 32 * i : nullptr;
+#pragma unroll
+            for (int g = 0; g < 4; ++g) {
+                float v[4];
+#pragma unroll
+                for (int e = 0; e < 4; ++e) v[e] = acc[i][j][4 * g + e];
+                if (p.epilogue == kResidual) {
+                    const u32x2 r = *reinterpret_cast<const u32x2 *>(rrow + 8 * g + 4 * lg);
+                    v[0] += bf_lo(r[0]);
+                    v[1] += bf_hi(r[0]);
+                    v[2] += bf_lo(r[1]);
+                    v[3] += bf_hi(r[1]);
+                }
+                u32x2 o = {pack_bf16(v[0], v[1]), pack_bf16(v[2], v[3])};
+                *reinterpret_cast<u32x2 *>(orow + 8 * g + 4 * lg) = o;
+            }
+        }
+    }
+}
 
 __global__ __launch_bounds__(NT, 2) void linear_bf16(LinearParams p) {
     __shared__ __attribute__((aligned(16))) uint16_t as[2][BM * KS];
@@ -135,63 +199,98 @@ __global__ __launch_bounds__(NT, 2) void linear_bf16(LinearParams p) {
         __syncthreads();
     }
 
-    // epilogue: lane (ln, lg) of block (i, j) holds C[row][col .. col + 3] in accumulators
-    // 4g .. 4g + 3, row = m0 + 64 wm + 32 j + ln, col = n0 + 64 wn + 32 i + 8 g + 4 lg
-    if (p.epilogue == kSwiGlu) {
-        // W rows alternate 32 gate rows and 32 up rows: block i = 0 holds gate, i = 1 up, for the
-        // output columns (n0 + 64 wn) / 2 + 8 g + 4 lg .. + 3
+    store_tile(p, acc, m0, n0, wm, wn, ln, lg);
+}
+
+// ---------------------------------------------------------------------------------------------
+// linear_bf16_dl: the same product and epilogues with a tile of 128 rows of A x 256 rows of W
+// (8 waves, each the 64 x 64 slice of linear_bf16) whose operand tiles are loaded straight from
+// global memory into LDS (global_load_lds_dwordx4: lane i of an instruction writes its 16 bytes at
+// the instruction's LDS base + 16 i), in a ring of 3 K steps of 64 loaded two steps ahead.
+//   - Rows are unpadded (128 bytes) and chunk c of row r sits at c ^ ((r >> 1) & 7): the 16 lanes
+//     of one fragment read take 16 consecutive rows at 16 distinct 16-byte bank groups. Each lane
+//     of a load fetches the global chunk that lands at its LDS position.
+//   - A K step is 48 load instructions of 8 rows (32 of W, 16 of A), 6 per wave. Before the one
+//     barrier of step kt each wave waits for its own loads of step kt (the 6 of step kt+1 may stay
+//     in flight); after it, step kt+2's loads go into the slot that step kt-1 used.
+constexpr int DBM = 128, DBN = 256, DNT = 512, DSTAGES = 3, DLOADS = 6;
+
+__global__ __launch_bounds__(DNT, 1) void linear_bf16_dl(LinearParams p) {
+    __shared__ __attribute__((aligned(16))) uint16_t wsm[DSTAGES][DBN * BK];
+    __shared__ __attribute__((aligned(16))) uint16_t asm_[DSTAGES][DBM * BK];
+
+    const int tiles = p.tiles_m * p.tiles_n;
+    const int per_xcd = (tiles + 7) / 8;
+    const int t = (blockIdx.x % 8) * per_xcd + blockIdx.x / 8;
+    if (t >= tiles) return;
+    const int tn = t / p.tiles_m, tm = t % p.tiles_m;
+    const int m0 = tm * DBM, n0 = tn * DBN;
+
+    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, ln = lane & 31, lg = lane >> 5;
+    const int wn = wave & 3, wm = wave >> 2;
+    const int wv = __builtin_amdgcn_readfirstlane(wave);
+
+    // this wave's loads: instruction i is 8-row group q = 6 wave + i (q < 32: W rows 8q..; else A
+    // rows 8 (q - 32)..); lane -> row 8q + lane / 8, LDS chunk lane % 8, global chunk swizzled
+    const char *src[DLOADS];
 #pragma unroll
-        for (int j = 0; j < 2; ++j) {
-            const int row = m0 + 64 * wm + 32 * j + ln;
-            if (row >= p.m) continue;
-            uint16_t *orow = p.out[0] + (int64_t)row * p.ld_out[0] + (n0 + 64 * wn) / 2;
+    for (int i = 0; i < DLOADS; ++i) {
+        const int q = DLOADS * wv + i;
+        const bool is_w = q < DBN / 8;
+        const int r = 8 * (is_w ? q : q - DBN / 8) + (lane >> 3);
+        const int gc = (lane & 7) ^ ((r >> 1) & 7);
+        const uint16_t *row = is_w ? p.w + (int64_t)(n0 + r) * p.k : p.a + (int64_t)min(m0 + r, p.m - 1) * p.k;
+        src[i] = reinterpret_cast<const char *>(row + 8 * gc);
+    }
+    auto issue = [&](int kt, int st) __attribute__((always_inline)) {
 #pragma unroll
-            for (int g = 0; g < 4; ++g) {
-                float v[4];
-#pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    const float gt = acc[0][j][4 * g + e], up = acc[1][j][4 * g + e];
-                    v[e] = gt / (1.0f + __expf(-gt)) * up;
-                }
-                u32x2 o = {pack_bf16(v[0], v[1]), pack_bf16(v[2], v[3])};
-                *reinterpret_cast<u32x2 *>(orow + 8 * g + 4 * lg) = o;
-            }
+        for (int i = 0; i < DLOADS; ++i) {
+            const int q = DLOADS * wv + i;
+            uint16_t *dst = q < DBN / 8 ? &wsm[st][q * 8 * BK] : &asm_[st][(q - DBN / 8) * 8 * BK];
+            dma16(src[i] + (int64_t)kt * BK * 2, lds_addr(dst));
         }
-        return;
-    }
-    // column ranges of the split outputs (a 32-column block never straddles two of them)
-    int which = 0, col_base = 0;
-    if (p.epilogue == kSplit3) {
-        const int c0 = n0 + 64 * wn;
-        which = c0 >= p.split0 + p.split1 ? 2 : c0 >= p.split0 ? 1 : 0;
-        col_base = which == 2 ? p.split0 + p.split1 : which == 1 ? p.split0 : 0;
-    }
+    };
+
+    // fragment reads: rows 64 wn + 32 i + ln of W and 64 wm + 32 j + ln of A, chunk 2 s + lg at
+    // (2 s + lg) ^ ((row >> 1) & 7) = x0 ^ 2 s (the row's bits 1-3 are those of ln)
+    const int x0 = lg ^ ((ln >> 1) & 7);
+    floatx16 acc[2][2];
 #pragma unroll
-    for (int j = 0; j < 2; ++j) {
-        const int row = m0 + 64 * wm + 32 * j + ln;
-        if (row >= p.m) continue;
+    for (int i = 0; i < 2; ++i)
 #pragma unroll
-        for (int i = 0; i < 2; ++i) {
-            const int col = n0 + 64 * wn + 32 * i - col_base;
-            uint16_t *orow = p.out[which] + (int64_t)row * p.ld_out[which] + col;
-            const uint16_t *rrow = p.residual ? p.residual + (int64_t)row * p.n + n0 + 64 * wn + 32 * i : nullptr;
+        for (int j = 0; j < 2; ++j)
 #pragma unroll
-            for (int g = 0; g < 4; ++g) {
-                float v[4];
+            for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
+
+    const int n_kt = p.k / BK;
+    issue(0, 0);
+    if (n_kt > 1) issue(1, 1);
+    int st = 0;
+    for (int kt = 0; kt < n_kt; ++kt) {
+        if (kt + 1 < n_kt) wait_vmcnt<DLOADS>();
+        else wait_vmcnt<0>();
+        barrier_dl();
+        if (kt + 2 < n_kt) issue(kt + 2, st == 0 ? 2 : st - 1);
+        const uint16_t *wb = &wsm[st][(64 * wn + ln) * BK];
+        const uint16_t *ab = &asm_[st][(64 * wm + ln) * BK];
+        bf16x8 wf[4][2], af[4][2];
 #pragma unroll
-                for (int e = 0; e < 4; ++e) v[e] = acc[i][j][4 * g + e];
-                if (p.epilogue == kResidual) {
-                    const u32x2 r = *reinterpret_cast<const u32x2 *>(rrow + 8 * g + 4 * lg);
-                    v[0] += bf_lo(r[0]);
-                    v[1] += bf_hi(r[0]);
-                    v[2] += bf_lo(r[1]);
-                    v[3] += bf_hi(r[1]);
-                }
-                u32x2 o = {pack_bf16(v[0], v[1]), pack_bf16(v[2], v[3])};
-                *reinterpret_cast<u32x2 *>(orow + 8 * g + 4 * lg) = o;
+        for (int s = 0; s < BK / 16; ++s)
+#pragma unroll
+            for (int i = 0; i < 2; ++i) {
+                wf[s][i] = *reinterpret_cast<const bf16x8 *>(wb + 32 * i * BK + 8 * (x0 ^ (2 * s)));
+                af[s][i] = *reinterpret_cast<const bf16x8 *>(ab + 32 * i * BK + 8 * (x0 ^ (2 * s)));
             }
-        }
+#pragma unroll
+        for (int s = 0; s < BK / 16; ++s)
+#pragma unroll
+            for (int i = 0; i < 2; ++i)
+#pragma unroll
+                for (int j = 0; j < 2; ++j)
+                    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(wf[s][i], af[s][j], acc[i][j], 0, 0, 0);
+        st = st == 2 ? 0 : st + 1;
     }
+    store_tile(p, acc, m0, n0, wm, wn, ln, lg);
 }
 
 // ---------------------------------------------------------------------------------------------
@@ -252,6 +351,13 @@ hipError_t launch_linear(const LinearCall &c, hipStream_t stream) {
     p.split0 = c.split0;
     p.split1 = c.split1;
     p.residual = static_cast<const uint16_t *>(c.residual);
+    if (c.n % DBN == 0) {
+        p.tiles_m = (c.m + DBM - 1) / DBM;
+        p.tiles_n = c.n / DBN;
+        const int grid = 8 * ((p.tiles_m * p.tiles_n + 7) / 8);
+        hipLaunchKernelGGL(linear_bf16_dl, dim3(grid), dim3(DNT), 0, stream, p);
+        return hipGetLastError();
+    }
     p.tiles_m = (c.m + BM - 1) / BM;
     p.tiles_n = c.n / BN;
     const int tiles = p.tiles_m * p.tiles_n;
