@@ -294,6 +294,103 @@ __global__ __launch_bounds__(DNT, 1) void linear_bf16_dl(LinearParams p) {
 }
 
 // ---------------------------------------------------------------------------------------------
+// linear_bf16_big: the same product and epilogues for large grids, with a tile of 256 rows of A x
+// 256 rows of W (8 waves, each 64 columns x 128 rows: 2 x 4 blocks of 32 x 32), so that each byte
+// loaded into LDS feeds 1.5 times the MFMA work of linear_bf16_dl. Operand tiles go straight
+// into LDS in a ring of 4 K steps of 32, loaded three steps ahead.
+//   - Rows of a K step are 64 bytes (4 chunks); chunk c of row r sits at c ^ ((r >> 2) & 3), so the
+//     16 lanes of one fragment read (16 consecutive rows) take 16 distinct 16-byte bank groups.
+//   - A K step is 32 load instructions of 16 rows (16 of W, 16 of A), 4 per wave; each wave waits
+//     for its own loads of step kt before the step's barrier (those of the later steps in flight
+//     may stay), and issues step kt+3 into the slot that step kt-1 used after it.
+constexpr int GBM = 256, GBN = 256, GBK = 32, GNT = 512, GSTAGES = 4, GLOADS = 4;
+
+__global__ __launch_bounds__(GNT, 1) void linear_bf16_big(LinearParams p) {
+    __shared__ __attribute__((aligned(16))) uint16_t wsm[GSTAGES][GBN * GBK];
+    __shared__ __attribute__((aligned(16))) uint16_t asm_[GSTAGES][GBM * GBK];
+
+    const int tiles = p.tiles_m * p.tiles_n;
+    const int per_xcd = (tiles + 7) / 8;
+    const int t = (blockIdx.x % 8) * per_xcd + blockIdx.x / 8;
+    if (t >= tiles) return;
+    const int tn = t / p.tiles_m, tm = t % p.tiles_m;
+    const int m0 = tm * GBM, n0 = tn * GBN;
+
+    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, ln = lane & 31, lg = lane >> 5;
+    const int wn = wave & 3, wm = wave >> 2;
+    const int wv = __builtin_amdgcn_readfirstlane(wave);
+
+    // this wave's loads: instruction i is 16-row group q = 4 wave + i (q < 16: W rows 16q..; else
+    // A rows 16 (q - 16)..); lane -> row 16q + lane / 4, LDS chunk lane % 4, global chunk swizzled
+    const char *src[GLOADS];
+#pragma unroll
+    for (int i = 0; i < GLOADS; ++i) {
+        const int q = GLOADS * wv + i;
+        const bool is_w = q < GBN / 16;
+        const int r = 16 * (is_w ? q : q - GBN / 16) + (lane >> 2);
+        const int gc = (lane & 3) ^ ((r >> 2) & 3);
+        const uint16_t *row = is_w ? p.w + (int64_t)(n0 + r) * p.k : p.a + (int64_t)min(m0 + r, p.m - 1) * p.k;
+        src[i] = reinterpret_cast<const char *>(row + 8 * gc);
+    }
+    auto issue = [&](int kt, int st) __attribute__((always_inline)) {
+#pragma unroll
+        for (int i = 0; i < GLOADS; ++i) {
+            const int q = GLOADS * wv + i;
+            uint16_t *dst = q < GBN / 16 ? &wsm[st][q * 16 * GBK] : &asm_[st][(q - GBN / 16) * 16 * GBK];
+            dma16(src[i] + (int64_t)kt * GBK * 2, lds_addr(dst));
+        }
+    };
+
+    // fragment reads: rows 64 wn + 32 i + ln of W and 128 wm + 32 j + ln of A, chunk 2 s + lg at
+    // (2 s + lg) ^ ((row >> 2) & 3) = x0 ^ 2 s (the row's bits 2-3 are those of ln)
+    const int x0 = lg ^ ((ln >> 2) & 3);
+    floatx16 acc[2][4];
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
+
+    const int n_kt = p.k / GBK;
+#pragma unroll
+    for (int k = 0; k < GSTAGES - 1; ++k)
+        if (k < n_kt) issue(k, k);
+    int st = 0;
+    for (int kt = 0; kt < n_kt; ++kt) {
+        // loads of later steps this wave has in flight: steps kt+1, kt+2 when they exist
+        const int later = min(GSTAGES - 2, n_kt - 1 - kt);
+        if (later >= 2) wait_vmcnt<2 * GLOADS>();
+        else if (later == 1) wait_vmcnt<GLOADS>();
+        else wait_vmcnt<0>();
+        barrier_dl();
+        if (kt + GSTAGES - 1 < n_kt) issue(kt + GSTAGES - 1, st == 0 ? GSTAGES - 1 : st - 1);
+        const uint16_t *wb = &wsm[st][(64 * wn + ln) * GBK];
+        const uint16_t *ab = &asm_[st][(128 * wm + ln) * GBK];
+#pragma unroll
+        for (int s = 0; s < GBK / 16; ++s) {
+            bf16x8 wf[2], af[4];
+#pragma unroll
+            for (int i = 0; i < 2; ++i) wf[i] = *reinterpret_cast<const bf16x8 *>(wb + 32 * i * GBK + 8 * (x0 ^ (2 * s)));
+#pragma unroll
+            for (int j = 0; j < 4; ++j) af[j] = *reinterpret_cast<const bf16x8 *>(ab + 32 * j * GBK + 8 * (x0 ^ (2 * s)));
+#pragma unroll
+            for (int i = 0; i < 2; ++i)
+#pragma unroll
+                for (int j = 0; j < 4; ++j)
+                    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(wf[i], af[j], acc[i][j], 0, 0, 0);
+        }
+        st = st == GSTAGES - 1 ? 0 : st + 1;
+    }
+    // the wave's 128 rows as two 64-row slices of the shared epilogue
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+        const floatx16 sub[2][2] = {{acc[0][2 * h], acc[0][2 * h + 1]}, {acc[1][2 * h], acc[1][2 * h + 1]}};
+        store_tile(p, sub, m0 + 128 * wm + 64 * h, n0, 0, wn, ln, lg);
+    }
+}
+
+// ---------------------------------------------------------------------------------------------
 // rmsnorm_bf16: one wave per row. y = x * rsqrt(mean(x^2) + eps) * w, the sum of squares in fp32.
 template <int PER_LANE>
 __global__ __launch_bounds__(256) void rmsnorm_bf16(const uint16_t *x, const uint16_t *w, uint16_t *y, int rows,
@@ -351,6 +448,15 @@ hipError_t launch_linear(const LinearCall &c, hipStream_t stream) {
     p.split0 = c.split0;
     p.split1 = c.split1;
     p.residual = static_cast<const uint16_t *>(c.residual);
+    // large grids: the 256 x 256 tile, where its tiles fill the GPU's compute units at least four
+    // times over (fewer, larger tiles leave units idle in the last round)
+    if (c.n % GBN == 0 && (int64_t)((c.m + GBM - 1) / GBM) * (c.n / GBN) >= 4 * 256) {
+        p.tiles_m = (c.m + GBM - 1) / GBM;
+        p.tiles_n = c.n / GBN;
+        const int grid = 8 * ((p.tiles_m * p.tiles_n + 7) / 8);
+        hipLaunchKernelGGL(linear_bf16_big, dim3(grid), dim3(GNT), 0, stream, p);
+        return hipGetLastError();
+    }
     if (c.n % DBN == 0) {
         p.tiles_m = (c.m + DBM - 1) / DBM;
         p.tiles_n = c.n / DBN;

@@ -81,6 +81,33 @@ def test_linear(m, n, k, epilogue):
     one_rounding(host(got), want, f"linear epilogue {epilogue}")
 
 
+@pytest.mark.parametrize("epilogue", [0, 1, 2])
+def test_linear_large_grid(epilogue):
+    """A grid of at least 4 x 256 tiles of 256 x 256 (300 rows: 2 row tiles, the last partial; 131,072
+    columns: 512 column tiles) runs the large-tile kernel; 512 sampled output columns (for SwiGLU:
+    their gate and up rows of W) are checked against the oracle."""
+    m, n, k = 300, 131072, 64
+    g = np.random.default_rng([m, n, k, epilogue, 1])
+    a = gen.round_bf16(g.standard_normal((m, k), dtype=np.float32))
+    w = gen.round_bf16(g.standard_normal((n, k), dtype=np.float32) / np.float32(np.sqrt(k)))
+    n_out = n // 2 if epilogue == 2 else n
+    cols = np.sort(g.choice(n_out, 512, replace=False))
+    if epilogue == 2:
+        wg, wu = omodel.split_gate_up(w)
+        want = omodel.silu(native.linear(a, wg[cols])) * native.linear(a, wu[cols])
+        got = pic.linear(dev(a), dev(w), 2)
+    elif epilogue == 1:
+        r = gen.round_bf16(g.standard_normal((m, n), dtype=np.float32))
+        want = native.linear(a, w[cols]) + r[:, cols]
+        got = pic.linear(dev(a), dev(w), 1, residual=dev(r))
+    else:
+        want = native.linear(a, w[cols])
+        got = pic.linear(dev(a), dev(w), 0)
+    torch.cuda.synchronize()
+    assert tuple(got.shape) == (m, n_out)
+    one_rounding(host(got[:, torch.as_tensor(cols, device="cuda")]), want, f"linear, large grid, epilogue {epilogue}")
+
+
 def test_linear_residual_in_place():
     g = np.random.default_rng(5)
     a = gen.round_bf16(g.standard_normal((200, 256), dtype=np.float32))
