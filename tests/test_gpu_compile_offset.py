@@ -109,8 +109,13 @@ def test_new_keys_are_written_at_the_offset(rope_keys):
     assert n_checked > 0
 
 
+@pytest.mark.parametrize("rope_keys", [1, 2])
 @pytest.mark.parametrize("name", ["ragged_bf16", "no_prefix_no_suffix"])
-def test_decode_after_link(name):
+def test_decode_after_link(name, rope_keys):
+    """Decode over keys rotated at C + j, whose first segments link before C (negative rotations):
+    from the pools, rotated in the decode kernel (rope_keys 1), and from the link call's rotated copy,
+    which each step extends with its token's key (rope_keys 2)."""
     cfg = small_cfg(**EDGE[name])
-    _say(f"decode, edge case {name}, compile offset {C}")
-    check_decode(cfg, run_decode(cfg, steps=3, key_layout=SEG, compile_offset=C), f"decode {name} compile offset {C}")
+    _say(f"decode, edge case {name}, compile offset {C}, rope_keys {rope_keys}")
+    check_decode(cfg, run_decode(cfg, steps=3, key_layout=SEG, compile_offset=C, rope_keys=rope_keys),
+                 f"decode {name} compile offset {C} rope_keys {rope_keys}")
