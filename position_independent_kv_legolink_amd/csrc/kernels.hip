@@ -338,13 +338,9 @@ __global__ __launch_bounds__(512, 1) void link_attention_bf16(AttnParams p) {
 #pragma unroll
             for (int u = 0; u < NKP; ++u) {
                 const uint32_t off = (uint32_t)k_pos[u] * (uint32_t)(D * 4) + k_cs_off[u];
-                floatx4 v = *reinterpret_cast<const floatx4 *>(rope_b + off + (q >> 1) * (D * 2) + (q & 1) * 16);
-                if (q < 2) {
-                    k_c[u][q & 1] = v;
-                } else {
-                    if constexpr (SEG) v = __builtin_bit_cast(floatx4, __builtin_bit_cast(u32x4, v) ^ k_sgn[u]);
-                    k_s[u][q & 1] = v;
-                }
+                const floatx4 v = *reinterpret_cast<const floatx4 *>(rope_b + off + (q >> 1) * (D * 2) + (q & 1) * 16);
+                if (q < 2) k_c[u][q & 1] = v;
+                else k_s[u][q & 1] = v;
             }
         }
     };
@@ -362,6 +358,18 @@ __global__ __launch_bounds__(512, 1) void link_attention_bf16(AttnParams p) {
     float rx[NKP], ry[NKP];
     auto rope_step = [&](int k) __attribute__((always_inline)) {
         const int wd = k >> 1, h = k & 1;
+        if constexpr (SEG) {
+            // a negative rotation: sines negated here, where the rotation first needs them (done
+            // right after their load it would wait for the load there); k_sgn is wave-uniform
+            if (k == 0) {
+#pragma unroll
+                for (int u = 0; u < NKP; ++u)
+                    if (k_sgn[u])
+#pragma unroll
+                        for (int i = 0; i < 2; ++i)
+                            k_s[u][i] = __builtin_bit_cast(floatx4, __builtin_bit_cast(u32x4, k_s[u][i]) ^ k_sgn[u]);
+            }
+        }
 #pragma unroll
         for (int u = 0; u < NKP; ++u) {
             const float x = h ? bf_hi(k_lo[u][wd]) : bf_lo(k_lo[u][wd]);
@@ -1408,6 +1416,7 @@ __global__ __launch_bounds__(kThreads, 1) void link_attention_f32(AttnParams p) 
     const int wave_rpos0 = rpos0 < 0 ? INT_MAX : rpos0;
 
     floatx4 k_lo[NKP], k_hi[NKP], k_c[NKP], k_s[NKP];
+    uint32_t k_sgn[NKP];   // sign bit of the rotation: a negative angle flips the sines
     floatx4 v_r[NV];
     int kp_next = kNeverAttended;
     bool mask_next = true;
@@ -1432,11 +1441,12 @@ __global__ __launch_bounds__(kThreads, 1) void link_attention_f32(AttnParams p) 
             }
             k_lo[u] = ok ? *reinterpret_cast<const floatx4 *>(kpool + base + 4 * c) : floatx4{0, 0, 0, 0};
             k_hi[u] = ok ? *reinterpret_cast<const floatx4 *>(kpool + base + D / 2 + 4 * c) : floatx4{0, 0, 0, 0};
-            // a negative rotation takes the row of its magnitude with the sines negated
+            // a negative rotation takes the row of its magnitude with the sines negated (when the
+            // rotation uses them: negated here, they would wait for their load here)
             const float *cs = p.rope + (int64_t)(pos < 0 ? -pos : pos) * D + 4 * c;
             k_c[u] = *reinterpret_cast<const floatx4 *>(cs);
             k_s[u] = *reinterpret_cast<const floatx4 *>(cs + D / 2);
-            if (pos < 0) k_s[u] = -k_s[u];
+            k_sgn[u] = pos < 0 ? 0x80000000u : 0u;
         }
 #pragma unroll
         for (int u = 0; u < NV; ++u) {
@@ -1470,10 +1480,11 @@ __global__ __launch_bounds__(kThreads, 1) void link_attention_f32(AttnParams p) 
             const int pi = tid + kThreads * u;
             const int key = pi / (D / 8), c = pi % (D / 8);
             floatx4 olo, ohi;
+            const floatx4 sn = __builtin_bit_cast(floatx4, __builtin_bit_cast(u32x4, k_s[u]) ^ k_sgn[u]);
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
-                olo[j] = fmaf(k_lo[u][j], k_c[u][j], -k_hi[u][j] * k_s[u][j]);
-                ohi[j] = fmaf(k_hi[u][j], k_c[u][j], k_lo[u][j] * k_s[u][j]);
+                olo[j] = fmaf(k_lo[u][j], k_c[u][j], -k_hi[u][j] * sn[j]);
+                ohi[j] = fmaf(k_hi[u][j], k_c[u][j], k_lo[u][j] * sn[j]);
             }
             *reinterpret_cast<floatx4 *>(&ks[buf][key * KS + 4 * c]) = olo;
             *reinterpret_cast<floatx4 *>(&ks[buf][key * KS + D / 2 + 4 * c]) = ohi;
