@@ -448,9 +448,14 @@ hipError_t launch_linear(const LinearCall &c, hipStream_t stream) {
     p.split0 = c.split0;
     p.split1 = c.split1;
     p.residual = static_cast<const uint16_t *>(c.residual);
-    // large grids: the 256 x 256 tile, where its tiles fill the GPU's compute units at least four
-    // times over (fewer, larger tiles leave units idle in the last round)
-    if (c.n % GBN == 0 && (int64_t)((c.m + GBM - 1) / GBM) * (c.n / GBN) >= 4 * 256) {
+    // the 256 x 256 tile where it needs fewer rounds of the 256 compute units, each round weighed
+    // 1.7 times a round of 128 x 256 tiles (twice the work at 1.5 times the MFMA work per byte
+    // loaded: 15% faster per FLOP). At 3,200 rows that picks it for the output and down
+    // projections (208 tiles: one round against two, 12% and 9% faster) and for gate/up, and
+    // keeps 128 x 256 for the QKV projection (two rounds against three; 256 x 256 was 9% slower)
+    const int64_t big_rounds = ((int64_t)((c.m + GBM - 1) / GBM) * (c.n / GBN) + 255) / 256;
+    const int64_t dl_rounds = ((int64_t)((c.m + DBM - 1) / DBM) * (c.n / DBN) + 255) / 256;
+    if (c.n % GBN == 0 && 17 * big_rounds < 10 * dl_rounds) {
         p.tiles_m = (c.m + GBM - 1) / GBM;
         p.tiles_n = c.n / GBN;
         const int grid = 8 * ((p.tiles_m * p.tiles_n + 7) / 8);

@@ -83,10 +83,11 @@ def test_linear(m, n, k, epilogue):
 
 @pytest.mark.parametrize("epilogue", [0, 1, 2])
 def test_linear_large_grid(epilogue):
-    """A grid of at least 4 x 256 tiles of 256 x 256 (300 rows: 2 row tiles, the last partial; 131,072
-    columns: 512 column tiles) runs the large-tile kernel; 512 sampled output columns (for SwiGLU:
-    their gate and up rows of W) are checked against the oracle."""
-    m, n, k = 300, 131072, 64
+    """A grid on which 256 x 256 tiles need fewer rounds of the compute units (500 rows: 2 row
+    tiles, the last partial, against 4 of 128 rows; 65,536 columns: 256 column tiles) runs the
+    large-tile kernel; 512 sampled output columns (for SwiGLU: their gate and up rows of W) are
+    checked against the oracle."""
+    m, n, k = 500, 65536, 64
     g = np.random.default_rng([m, n, k, epilogue, 1])
     a = gen.round_bf16(g.standard_normal((m, k), dtype=np.float32))
     w = gen.round_bf16(g.standard_normal((n, k), dtype=np.float32) / np.float32(np.sqrt(k)))
