@@ -1632,19 +1632,36 @@ __global__ __launch_bounds__(kThreads) void link_merge(const MergeDesc *merge, c
     {
         const int m = blockIdx.y * RPB + (int)threadIdx.x / (D / 4), d4 = (int)threadIdx.x % (D / 4);
         if (m >= mrows) return;
-        // the splits' loads are independent: unrolled, several are in flight at once
-        float L = -INFINITY;
-#pragma unroll 4
-        for (int s = 0; s < md.n_split; ++s) L = fmaxf(L, part_lse[(int64_t)(md.slot0 + s) * tq + m]);
+        // one pass over the splits, four at a time: the loads of a group (its log-sum-exps and
+        // partial outputs) are all issued before any of them is used, then folded into a running
+        // maximum L, weight sum and output (rescaled when L moves)
+        constexpr int R = 4;
+        float L = -INFINITY, wsum = 0.0f;
         floatx4 acc = {0, 0, 0, 0};
-        float wsum = 0.0f;
-#pragma unroll 4
-        for (int s = 0; s < md.n_split; ++s) {
-            const float ls = part_lse[(int64_t)(md.slot0 + s) * tq + m];
-            const float wgt = ls == -INFINITY ? 0.0f : expf(ls - L);
-            const floatx4 o = *reinterpret_cast<const floatx4 *>(part_o + ((int64_t)(md.slot0 + s) * tq + m) * D + 4 * d4);
-            acc += wgt * o;
-            wsum += wgt;
+        for (int s0 = 0; s0 < md.n_split; s0 += R) {
+            float ls[R];
+            floatx4 o[R];
+#pragma unroll
+            for (int u = 0; u < R; ++u) {
+                const int s = s0 + u;
+                const int64_t slot = (int64_t)(md.slot0 + min(s, md.n_split - 1)) * tq + m;
+                ls[u] = s < md.n_split ? part_lse[slot] : -INFINITY;
+                o[u] = *reinterpret_cast<const floatx4 *>(part_o + slot * D + 4 * d4);
+            }
+            float mx = L;
+#pragma unroll
+            for (int u = 0; u < R; ++u) mx = fmaxf(mx, ls[u]);
+            if (mx == -INFINITY) continue;
+            const float sc = expf(L - mx);   // 0 while L is still -inf
+            acc *= sc;
+            wsum *= sc;
+#pragma unroll
+            for (int u = 0; u < R; ++u) {
+                const float wgt = ls[u] == -INFINITY ? 0.0f : expf(ls[u] - mx);
+                acc += wgt * o[u];
+                wsum += wgt;
+            }
+            L = mx;
         }
         const float inv = wsum > 0.0f ? 1.0f / wsum : 0.0f;
         const int row = md.row0 + (m >> gshift);
