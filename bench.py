@@ -21,6 +21,7 @@ on a bounded sample of rows.
 from __future__ import annotations
 
 import argparse
+import dataclasses
 import gc
 import hashlib
 import json
@@ -575,6 +576,10 @@ def main():
     ap.add_argument("--key-layout", default="position_free", choices=("position_free", "segment_rope"),
                     help="stored key form: pre-RoPE, or rotated at the position inside the segment "
                          "(a chunk compiled from position 0)")
+    ap.add_argument("--value-scale", type=float, default=1.0,
+                    help="scale the workload's synthetic Q, K and V by this factor (0: all zeros); the MFMA "
+                         "clock depends on the operand values, so this shows how much of the attention time "
+                         "is power rather than schedule")
     ap.add_argument("--split-pages", type=int, default=0,
                     help="KV pages per attention work item: 0 automatic, > 0 at most that many, "
                          "< 0 only where the kernel's limit requires")
@@ -606,6 +611,9 @@ def main():
         sys.exit(1)
     torch.cuda.set_device(0)
     cfg = CONFIGS[args.workload]
+    if args.value_scale != 1.0:
+        cfg = dataclasses.replace(cfg, q_scale=cfg.q_scale * args.value_scale,
+                                  kv_scale=cfg.kv_scale * args.value_scale)
     dense_pages = 0 if args.no_dense else (-(-(cfg.prefix_len + cfg.chunks_per_request * cfg.chunk_len +
                                                  cfg.suffix_len) // cfg.page_size)) * cfg.n_requests
     job = LinkJob(cfg, dense_pages=dense_pages, rope_keys=args.rope_keys, split_pages=args.split_pages,
@@ -726,7 +734,8 @@ def main():
         "config": {"workload": cfg.name, "tokens_per_request": job.n_tokens, "requests": cfg.n_requests,
                    "selected_rows": job.sizes["rows"], "q_heads": cfg.num_q_heads, "kv_heads": cfg.num_kv_heads,
                    "head_dim": cfg.head_dim, "page_size": cfg.page_size, "k": cfg.k,
-                   "block_level": cfg.block_level, "key_layout": args.key_layout, "parallelism": "single GPU"},
+                   "block_level": cfg.block_level, "key_layout": args.key_layout, "parallelism": "single GPU",
+                   **({"value_scale": args.value_scale} if args.value_scale != 1.0 else {})},
         "link_latency_ms": round(link_ms, 4),
         "link_latency_wall_ms": latency,
         "attention_ms": round(attn_ms, 4),
