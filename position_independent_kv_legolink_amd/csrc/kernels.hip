@@ -52,6 +52,13 @@ __device__ __forceinline__ uint32_t pack_bf16(float a, float b) {
     return __builtin_bit_cast(uint32_t, __builtin_convertvector(f, bf16x2));
 }
 
+// A page (or any block under 4 GiB) as a buffer resource: base address and size in SGPRs, so that
+// loads from it take a 32-bit per-lane offset (no per-load 64-bit address add); reads at offsets
+// at or past `bytes` return zeros. Data format 32, the format of untyped loads.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t page_rsrc(const char *base, uint32_t bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<char *>(base), (short)0, (int)bytes, 0x00020000);
+}
+
 // Work-group barrier that orders LDS only. A plain __syncthreads() also waits for every
 // outstanding global load of the wave (vmcnt(0)), which would expose the latency of loads that
 // are prefetched for later tiles and are read by their own wave only.
@@ -298,7 +305,7 @@ __global__ __launch_bounds__(512, 1) void link_attention_bf16(AttnParams p) {
     // halves, 1 the K high halves, then V, then (keys rotated here) the cos/sin rows at the keys'
     // positions
     constexpr int NLOAD = 2 + NVC + (KR ? 0 : 4);
-    const char *k_page[NKP];
+    __amdgpu_buffer_rsrc_t k_page[NKP];   // the key pages of this thread's pieces, as buffers
     auto load_piece = [&](int j) __attribute__((always_inline)) {
         if (j == 0) {
 #pragma unroll
@@ -321,18 +328,19 @@ __global__ __launch_bounds__(512, 1) void link_attention_bf16(AttnParams p) {
                         k_pos[u] = ok ? pos0 + k_slot[u] : pos0;
                     }
                 }
-                k_page[u] = kpool_b + (uint64_t)phys * page_bytes;
-                k_lo[u] = *reinterpret_cast<const u32x4 *>(k_page[u] + k_loff[u]);
+                k_page[u] = page_rsrc(kpool_b + (uint64_t)phys * page_bytes, page_bytes);
+                k_lo[u] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(k_page[u], (int)k_loff[u], 0, 0));
             }
             const int slot = lane & (page_size - 1);
             kp_stage = rl_in && slot < (rl_pv & 127) ? (rl_pv >> 7) + slot : kNeverAttended;
         } else if (j == 1) {
 #pragma unroll
-            for (int u = 0; u < NKP; ++u) k_hi[u] = *reinterpret_cast<const u32x4 *>(k_page[u] + k_loff[u] + D);
+            for (int u = 0; u < NKP; ++u)
+                k_hi[u] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(k_page[u], (int)(k_loff[u] + D), 0, 0));
         } else if (j < 2 + NVC) {
             const int u = j - 2;
             const char *page = vpool_b + (uint64_t)(uint32_t)__builtin_amdgcn_readfirstlane(rv_phys[u]) * page_bytes;
-            v_r[u] = *reinterpret_cast<const u32x4 *>(page + v_loff[u]);
+            v_r[u] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(page_rsrc(page, page_bytes), (int)v_loff[u], 0, 0));
         } else {
             const int q = j - 2 - NVC;   // 0: cos lo, 1: cos hi, 2: sin lo, 3: sin hi
 #pragma unroll
