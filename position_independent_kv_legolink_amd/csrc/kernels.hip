@@ -2192,7 +2192,7 @@ __global__ __launch_bounds__(512) void link_decode_merge(DecodeMergeParams p) {
     const int hl = blockIdx.x & (G - 1), h = md.kv_head * G + hl;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int d = tid % D, grp = tid / D;
-    const DecodeReq dr = p.dec_req[md.request];
+    const DecodeReq dr = md.req;
     const int pos = dr.pos + p.step;
     // the token's rows, loaded ahead of the ranges (wave 0 forms its score from them)
     const int i = lane & (D / 2 - 1);   // rotation pair (i, i + D/2); lanes past D/2 repeat it

@@ -80,12 +80,14 @@ struct DecodeReq {
                      // inside their segment
 };
 
-// Combine the partial results of one (request, KV head) with the new token's own key.
+// Combine the partial results of one (request, KV head) with the new token's own key. `req` is a
+// copy of the request's DecodeReq, so that the merge starts its loads after one descriptor read.
 struct DecodeMergeDesc {
     int32_t request;
     int32_t kv_head;
     int32_t n_split;
     int32_t slot0;
+    DecodeReq req;
 };
 
 constexpr int kKeysPerTile = 64;   // keys staged in LDS per attention iteration

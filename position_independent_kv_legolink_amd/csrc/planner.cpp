@@ -275,7 +275,7 @@ pic_plan *build_plan(pic_store *s, const pic_request *reqs, int32_t n_reqs, cons
             for (int32_t b = 0; b < n; b += step) by_range.emplace_back();
             const int32_t used = (int32_t)(by_range.size() - g0);
             for (int h = 0; h < cfg.num_kv_heads; ++h) {
-                plan->dec_merge.push_back({r, h, used, n_slots});
+                plan->dec_merge.push_back({r, h, used, n_slots, plan->dec_req[r]});
                 int32_t i = 0;
                 for (int32_t b = 0; b < n; b += step, ++i)
                     by_range[g0 + i].push_back({plan->cu_pages[r], b, std::min(n, b + step), r, h, n_slots + i, 0, 0});
