@@ -83,7 +83,6 @@ void pack_tables(const pic_plan &plan, uint8_t *blob) {
     put(plan.off_scatter, plan.scatter.data(), plan.scatter.size() * sizeof(ScatterDesc));
     put(plan.off_work, plan.work.data(), plan.work.size() * sizeof(WorkDesc));
     put(plan.off_merge, plan.merge.data(), plan.merge.size() * sizeof(MergeDesc));
-    put(plan.off_dec_req, plan.dec_req.data(), plan.dec_req.size() * sizeof(DecodeReq));
     put(plan.off_dec_work, plan.dec_work.data(), plan.dec_work.size() * sizeof(DecodeDesc));
     put(plan.off_dec_merge, plan.dec_merge.data(), plan.dec_merge.size() * sizeof(DecodeMergeDesc));
 }
@@ -507,7 +506,6 @@ pic_status pic_link_attend_static(pic_store *s, const pic_plan *plan, const void
         put(plan->off_scatter, plan->scatter.data(), plan->scatter.size() * sizeof(ScatterDesc));
         put(plan->off_work, plan->work.data(), plan->work.size() * sizeof(WorkDesc));
         put(plan->off_merge, plan->merge.data(), plan->merge.size() * sizeof(MergeDesc));
-        put(plan->off_dec_req, plan->dec_req.data(), plan->dec_req.size() * sizeof(DecodeReq));
         put(plan->off_dec_work, plan->dec_work.data(), plan->dec_work.size() * sizeof(DecodeDesc));
         put(plan->off_dec_merge, plan->dec_merge.data(), plan->dec_merge.size() * sizeof(DecodeMergeDesc));
         pic_plan *mp = const_cast<pic_plan *>(plan);
@@ -538,7 +536,6 @@ pic_status pic_link_decode(pic_store *s, const pic_plan *plan, const void *q, co
         uint8_t *ws = static_cast<uint8_t *>(workspace);
         DecodeTables t;
         t.pages = reinterpret_cast<const PageDesc *>(ws + plan->off_pages);
-        t.dec_req = reinterpret_cast<const DecodeReq *>(ws + plan->off_dec_req);
         t.step = plan->dec_next;
         t.work = reinterpret_cast<const DecodeDesc *>(ws + plan->off_dec_work);
         t.n_work = (int)plan->dec_work.size();

@@ -1873,7 +1873,6 @@ struct DecodeParams {
     const void *v_pool;
     const float *rope;
     const PageDesc *pages;
-    const DecodeReq *dec_req;
     const DecodeDesc *work;
     float *part_o;
     float *part_lse;
@@ -1923,7 +1922,7 @@ __global__ __launch_bounds__(256, 2) void link_decode_bf16(DecodeParams p) {
     __syncthreads();
     // the new token's position: keys at or after it (this step's token and later decode slots) are
     // masked; the merge adds the token itself
-    const int qpos = p.dec_req[w.request].pos + p.step;
+    const int qpos = w.pos + p.step;
 
     // rotated, scaled query fragments of head ln (zero beyond the G heads)
     u32x4 qf[NS];
@@ -2167,7 +2166,6 @@ __global__ __launch_bounds__(256, 2) void link_decode_bf16(DecodeParams p) {
 struct DecodeMergeParams {
     const void *q, *k, *v;
     const float *rope;
-    const DecodeReq *dec_req;
     const DecodeMergeDesc *merge;
     const PageDesc *pages;
     const float *part_o;
@@ -2413,7 +2411,6 @@ hipError_t launch_decode(const LayerShape &s, const void *q, const void *k, cons
         p.v_pool = v_pool;
         p.rope = rope;
         p.pages = t.pages;
-        p.dec_req = t.dec_req;
         p.step = t.step;
         p.work = t.work;
         p.part_o = t.part_o;
@@ -2445,7 +2442,6 @@ hipError_t launch_decode(const LayerShape &s, const void *q, const void *k, cons
     m.k = k;
     m.v = v;
     m.rope = rope;
-    m.dec_req = t.dec_req;
     m.merge = t.merge;
     m.pages = t.pages;
     m.k_pool = k_pool;

@@ -57,7 +57,6 @@ hipError_t launch_merge(const LayerShape &s, const AttnTables &t, void *out, flo
 
 struct DecodeTables {
     const PageDesc *pages;
-    const DecodeReq *dec_req;        // per request: decode token positions and slots
     int step;                        // decode step: token `step` of every request
     const DecodeDesc *work;
     int n_work;

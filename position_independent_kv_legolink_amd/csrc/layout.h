@@ -66,7 +66,8 @@ struct DecodeDesc {
     int32_t request;
     int32_t kv_head;
     int32_t partial;
-    int32_t pad0, pad1;
+    int32_t pos;         // the request's first decode position (its DecodeReq's), read with the rest
+    int32_t pad0;
 };
 
 // Decode slots of one request: its first decode token's position and where its decode tokens

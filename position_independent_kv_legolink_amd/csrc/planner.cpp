@@ -278,7 +278,8 @@ pic_plan *build_plan(pic_store *s, const pic_request *reqs, int32_t n_reqs, cons
                 plan->dec_merge.push_back({r, h, used, n_slots, plan->dec_req[r]});
                 int32_t i = 0;
                 for (int32_t b = 0; b < n; b += step, ++i)
-                    by_range[g0 + i].push_back({plan->cu_pages[r], b, std::min(n, b + step), r, h, n_slots + i, 0, 0});
+                    by_range[g0 + i].push_back(
+                        {plan->cu_pages[r], b, std::min(n, b + step), r, h, n_slots + i, plan->dec_req[r].pos, 0});
                 n_slots += used;
             }
         }
@@ -317,7 +318,6 @@ pic_plan *build_plan(pic_store *s, const pic_request *reqs, int32_t n_reqs, cons
     plan->off_scatter = place((int64_t)plan->scatter.size() * sizeof(ScatterDesc));
     plan->off_work = place((int64_t)plan->work.size() * sizeof(WorkDesc));
     plan->off_merge = place((int64_t)plan->merge.size() * sizeof(MergeDesc));
-    plan->off_dec_req = place((int64_t)plan->dec_req.size() * sizeof(DecodeReq));
     plan->off_dec_work = place((int64_t)plan->dec_work.size() * sizeof(DecodeDesc));
     plan->off_dec_merge = place((int64_t)plan->dec_merge.size() * sizeof(DecodeMergeDesc));
     plan->table_bytes = off;

@@ -109,11 +109,11 @@ struct pic_plan {
     bool decode = false;
     int32_t dec_steps = 0;              // decode steps reserved per request
     int32_t dec_next = 0;               // the next decode step (reset by pic_link_attend)
-    std::vector<piclink::DecodeReq> dec_req;
+    std::vector<piclink::DecodeReq> dec_req;   // host only: copied into the decode and merge descriptors
     std::vector<piclink::DecodeDesc> dec_work;
     std::vector<piclink::DecodeMergeDesc> dec_merge;
     int32_t n_dec_slots = 0;            // decode partial slots: the items of dec_work that are not empty
-    int64_t off_dec_req = 0, off_dec_work = 0, off_dec_merge = 0, off_dec_o = 0, off_dec_lse = 0, off_end = 0;
+    int64_t off_dec_work = 0, off_dec_merge = 0, off_dec_o = 0, off_dec_lse = 0, off_end = 0;
     // the link call's scratch [off_part_o, off_link_end) and decode's partials [off_dec_o,
     // off_dec_end) start at the same offset
     int64_t off_link_end = 0, off_dec_end = 0;
