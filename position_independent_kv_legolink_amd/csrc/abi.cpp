@@ -141,6 +141,9 @@ void launch_link(pic_store *s, const pic_plan *plan, int layer, const void *q_ne
     t.row_pos = reinterpret_cast<const int32_t *>(ws + plan->off_row_pos);
     t.work = reinterpret_cast<const WorkDesc *>(ws + plan->off_work);
     t.n_work = (int)plan->work.size();
+    t.ticket = reinterpret_cast<uint32_t *>(ws + plan->off_ticket);
+    t.n_queues = plan->work_queues;
+    t.n_groups = std::min<int>(t.n_work, s->num_cus);
     t.merge = reinterpret_cast<const MergeDesc *>(ws + plan->off_merge);
     t.n_merge = (int)plan->merge.size();
     t.part_o = reinterpret_cast<float *>(ws + plan->off_part_o);
@@ -506,6 +509,8 @@ pic_status pic_link_attend_static(pic_store *s, const pic_plan *plan, const void
         put(plan->off_scatter, plan->scatter.data(), plan->scatter.size() * sizeof(ScatterDesc));
         put(plan->off_work, plan->work.data(), plan->work.size() * sizeof(WorkDesc));
         put(plan->off_merge, plan->merge.data(), plan->merge.size() * sizeof(MergeDesc));
+        static const uint32_t zero_tickets[kMaxWorkQueues + 1] = {};
+        put(plan->off_ticket, zero_tickets, sizeof(zero_tickets));
         put(plan->off_dec_work, plan->dec_work.data(), plan->dec_work.size() * sizeof(DecodeDesc));
         put(plan->off_dec_merge, plan->dec_merge.data(), plan->dec_merge.size() * sizeof(DecodeMergeDesc));
         pic_plan *mp = const_cast<pic_plan *>(plan);

@@ -81,6 +81,10 @@ struct AttnParams {
     const PageDesc *pages;
     const int32_t *row_pos;
     const WorkDesc *work;
+    uint32_t *ticket;           // n_queues + 1 work counters: zero at launch, left at zero
+    int n_work;                 // a multiple of n_queues
+    int n_queues;
+    int persistent;             // one work group per compute unit over the queues, else one per item
     void *out;
     float *lse;
     float *part_o;
@@ -91,6 +95,56 @@ struct AttnParams {
     float scale;                // 1 / sqrt(d)
     int seg_keys;               // keys stored rotated inside their segment: rotate by its start
 };
+
+// Work items of an attention launch. With more items than compute units the launch is persistent
+// (p.persistent: one work group per compute unit). The list then holds p.n_queues queues
+// interleaved: item i of queue q is p.work[i * n_queues + q], each queue longest first, with its
+// counter in ticket[q]. A work group takes items from the queue of its XCD (work groups are
+// dispatched round-robin over the 8 XCDs, and the planner puts one KV head's items in one queue,
+// so that they share that XCD's L2) and, once that queue is empty, from the queue with the most
+// items left: compute units that run faster take more items. Otherwise work group i runs item i
+// alone. `state` is the caller's (thread 0's): 0 before its first item, 1 while its own queue
+// has items, 2 after. Returns -1 when the work group is done.
+__device__ __forceinline__ int next_work_item(const AttnParams &p, int &state) {
+    if (!p.persistent) return state++ == 0 ? (int)blockIdx.x : -1;
+    const int nq = p.n_queues;
+    const uint32_t depth = (uint32_t)(p.n_work / nq);
+    const int home = (int)(blockIdx.x % (uint32_t)nq);
+    if (state < 2) {
+        state = 1;
+        const uint32_t t = atomicAdd(p.ticket + home, 1u);
+        if (t < depth) return (int)t * nq + home;
+        state = 2;
+    }
+    // every counter read at once; an item from the fullest queue, or none left. Counters only
+    // grow, so this ends.
+    for (;;) {
+        uint32_t c[kMaxWorkQueues];
+#pragma unroll
+        for (int q = 0; q < kMaxWorkQueues; ++q)
+            c[q] = q < nq ? __hip_atomic_load(p.ticket + q, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) : depth;
+        uint32_t least = depth;
+        int best = -1;
+#pragma unroll
+        for (int q = 0; q < kMaxWorkQueues; ++q)
+            if (c[q] < least) {
+                least = c[q];
+                best = q;
+            }
+        if (best < 0) return -1;
+        const uint32_t t = atomicAdd(p.ticket + best, 1u);
+        if (t < depth) return (int)t * nq + best;
+    }
+}
+
+// End of a persistent launch (thread 0 of each work group, after its last item): the last work
+// group to get here puts the queue counters and the exit count (ticket[n_queues]) back to zero
+// for the next launch.
+__device__ __forceinline__ void release_work_queues(const AttnParams &p) {
+    if (!p.persistent) return;
+    if (atomicAdd(p.ticket + p.n_queues, 1u) == gridDim.x - 1)
+        for (int q = 0; q <= p.n_queues; ++q) atomicExch(p.ticket + q, 0u);
+}
 
 // A callable that issues piece j of a tile's loads, with the number of pieces as a constant
 // (zero: no loads).
@@ -164,644 +218,668 @@ __global__ __launch_bounds__(512, 1) void link_attention_bf16(AttnParams p) {
     __shared__ int pg_phys[kMaxItemPages], pg_pv[kMaxItemPages];
     __shared__ int pg_seg[SEG ? kMaxItemPages : 1];
 
-    const WorkDesc w = p.work[blockIdx.x];
-    if (w.n_rows <= 0) return;
+    // the work group's items, one after the other (next_work_item)
+    __shared__ int item_s;
+    int wstate = 0;   // thread 0's
+    for (;;) {
+        __syncthreads();   // every wave is done with the previous item's LDS, item_s included
+        if (threadIdx.x == 0) item_s = next_work_item(p, wstate);
+        __syncthreads();
+        const int item = __builtin_amdgcn_readfirstlane(item_s);
+        if (item < 0) break;
+        const WorkDesc w = p.work[item];
+        if (w.n_rows <= 0) continue;
 
-    const int tid = threadIdx.x;
-    const int wave = tid >> 6, lane = tid & 63, ln = lane & 31, lg = lane >> 5;
-    const int G = 1 << p.gshift;
-    const int page_size = 1 << p.pshift;
-    const int ppt = KT >> p.pshift;
-    const PageDesc *pg = p.pages + w.page_base;
-    const int64_t head_off = (int64_t)w.kv_head * page_size * D;
+        // the lane's index as an opaque value per item: values derived from it are computed inside
+        // the loop instead of being held in registers across it
+        int tid = threadIdx.x;
+        asm volatile("" : "+v"(tid));
 
-    // ---- rotated Q fragments, held for the whole key range
-    u32x4 qf[NS];
-    int rpos;
-    {
-        const int m = wave * 32 + ln;
-        const int ti = m >> p.gshift;
-        const bool valid = ti < w.n_rows;
-        const int row = w.row0 + (valid ? ti : 0);
-        const int qh = w.kv_head * G + (m & (G - 1));
-        const int rp = valid ? p.row_pos[row] : -1;
-        rpos = rp;
-        const uint16_t *qrow = static_cast<const uint16_t *>(p.q) + ((int64_t)row * p.hq + qh) * D;
-        const float *cs = p.rope + (int64_t)(valid ? rp : 0) * D;
-#pragma unroll
-        for (int s = 0; s < NS / 2; ++s) {
-            const int e0 = 16 * s + 8 * lg;
-            u32x4 lo = {0, 0, 0, 0}, hi = {0, 0, 0, 0};
-            if (valid) {
-                lo = *reinterpret_cast<const u32x4 *>(qrow + e0);
-                hi = *reinterpret_cast<const u32x4 *>(qrow + D / 2 + e0);
-            }
-            floatx4 c[2], sn[2];
-            c[0] = *reinterpret_cast<const floatx4 *>(cs + e0);
-            c[1] = *reinterpret_cast<const floatx4 *>(cs + e0 + 4);
-            sn[0] = *reinterpret_cast<const floatx4 *>(cs + D / 2 + e0);
-            sn[1] = *reinterpret_cast<const floatx4 *>(cs + D / 2 + e0 + 4);
-            // the softmax scale and log2(e) ride on Q: scores come out of the MFMA in log2 units
-#pragma unroll
-            for (int h = 0; h < 2; ++h) {
-                c[h] *= p.scale_log2;
-                sn[h] *= p.scale_log2;
-            }
-            rope8_bf16(lo, hi, c, sn, qf[s], qf[s + NS / 2]);
-        }
-    }
+        const int wave = tid >> 6, lane = tid & 63, ln = lane & 31, lg = lane >> 5;
+        const int G = 1 << p.gshift;
+        const int page_size = 1 << p.pshift;
+        const int ppt = KT >> p.pshift;
+        const PageDesc *pg = p.pages + w.page_base;
+        const int64_t head_off = (int64_t)w.kv_head * page_size * D;
 
-    // position of the wave's first row: its rows are consecutive selected rows of one request, in
-    // increasing position, so a key tile needs no mask for this wave when no key lies after it (a
-    // wave without rows never needs the mask: its outputs are not written)
-    const int rpos0 = __builtin_amdgcn_readfirstlane(rpos);
-    const int wave_rpos0 = rpos0 < 0 ? INT_MAX : rpos0;
-    // ... and of its last row (-1: no rows)
-    int rlast = rpos;
+        // ---- rotated Q fragments, held for the whole key range
+        u32x4 qf[NS];
+        int rpos;
+        {
+            const int m = wave * 32 + ln;
+            const int ti = m >> p.gshift;
+            const bool valid = ti < w.n_rows;
+            const int row = w.row0 + (valid ? ti : 0);
+            const int qh = w.kv_head * G + (m & (G - 1));
+            const int rp = valid ? p.row_pos[row] : -1;
+            rpos = rp;
+            const uint16_t *qrow = static_cast<const uint16_t *>(p.q) + ((int64_t)row * p.hq + qh) * D;
+            const float *cs = p.rope + (int64_t)(valid ? rp : 0) * D;
 #pragma unroll
-    for (int o = 32; o > 0; o >>= 1) rlast = max(rlast, __shfl_xor(rlast, o));
-    const int wave_rpos1 = __builtin_amdgcn_readfirstlane(rlast);
-
-    // ---- staging registers of one key tile (global -> registers -> LDS)
-    u32x4 k_lo[NKP], k_hi[NKP];
-    int k_pos[NKP];
-    uint32_t k_sgn[NKP];               // SEG: sign bit of the rotation (a negative angle flips the sines)
-    floatx4 k_c[NKP][2], k_s[NKP][2];
-    u32x4 v_r[NVC];
-    u32x4 k_olo[NKP], k_ohi[NKP];      // rotated K halves on their way to LDS
-    int kp_stage = kNeverAttended;
-    unsigned mask_ring = 7u;           // bit (t % 3): tile t needs the causal/padding mask
-
-    // Loop-invariant byte offsets of this thread's pieces inside a page (and inside a cos/sin
-    // row), so that each load is a scalar page base plus a 32-bit lane offset.
-    const char *kpool_b = static_cast<const char *>(KR ? p.k_rot : p.k_pool);
-    const char *vpool_b = static_cast<const char *>(p.v_pool);
-    const char *rope_b = reinterpret_cast<const char *>(p.rope);
-    const uint32_t page_bytes = (uint32_t)p.page_elems * 2u;
-    const int lpage0 = w.page_base + w.page_begin;   // logical page of the item's first page
-    uint32_t k_loff[NKP], k_cs_off[NKP], v_loff[NVC];
-    int k_slot[NKP];
-#pragma unroll
-    for (int u = 0; u < NKP; ++u) {
-        const int pi = tid + NT * u;
-        const int key = pi / (D / 16), c = pi % (D / 16);
-        k_slot[u] = key & (page_size - 1);
-        k_loff[u] = (uint32_t)(head_off + k_slot[u] * D + 8 * c) * 2u;
-        k_cs_off[u] = (uint32_t)(8 * c) * 4u;
-    }
-#pragma unroll
-    for (int u = 0; u < NVC; ++u) {
-        const int pi = tid + NT * u;
-        const int key = pi / (D / 8), c16 = pi % (D / 8);
-        v_loff[u] = (uint32_t)(head_off + (key & (page_size - 1)) * D + 8 * c16) * 2u;
-    }
-
-    // The work item's page table is staged in LDS once: the physical page, and the page's first
-    // position and valid token count packed as pos0 << 7 | valid (pos0 < 2^22, valid <= 64).
-    // The descriptors of a tile's KT / page pages are read from LDS early in the MFMA phase and
-    // moved to SGPRs where the loads of the same phase use them. Keys of one wave's K pieces (and
-    // of each of its V pieces) lie in one page (page >= 16 tokens). Keys past the work item's
-    // range or in page padding read real, finite pool data (the last page, or the zeroed padding
-    // slots) and are removed by the mask (position kNeverAttended).
-    const int n_pages = w.page_end - w.page_begin;
-    for (int i = tid; i < n_pages; i += NT) {
-        const PageDesc d = pg[w.page_begin + i];
-        pg_phys[i] = d.phys;
-        pg_pv[i] = (d.pos0 << 7) | d.valid;
-        if constexpr (SEG) pg_seg[i] = d.seg0;
-    }
-    lds_barrier();
-    // descriptor values read ahead from LDS: the wave's K page and V pages (uniform) and the
-    // page of key `lane` (for the mask positions). The reads are unconditional (clamped to the
-    // last page) and the range test is applied where the values are used: a conditional read
-    // becomes a branch whose join waits for the LDS result at once.
-    int rk_phys[NKP], rk_pv[NKP], rk_seg[NKP], rv_phys[NVC], rl_pv;
-    bool rk_in[NKP], rl_in;
-    auto load_desc = [&](int t) __attribute__((always_inline)) {
-        const int r0 = t * ppt;
-        const int wv = __builtin_amdgcn_readfirstlane(wave);
-#pragma unroll
-        for (int u = 0; u < NKP; ++u) {
-            const int rq = r0 + (((NT * u + 64 * wv) / (D / 16)) >> p.pshift);
-            const int r = min(rq, n_pages - 1);
-            if constexpr (KR) {
-                rk_phys[u] = lpage0 + r;
-            } else {
-                rk_phys[u] = pg_phys[r];
-                rk_pv[u] = pg_pv[r];
-                if constexpr (SEG) rk_seg[u] = pg_seg[r];
-                rk_in[u] = rq < n_pages;
-            }
-        }
-#pragma unroll
-        for (int u = 0; u < NVC; ++u)
-            rv_phys[u] = pg_phys[min(r0 + (((NT * u + 64 * wv) / (D / 8)) >> p.pshift), n_pages - 1)];
-        const int rq = r0 + (lane >> p.pshift);
-        rl_pv = pg_pv[min(rq, n_pages - 1)];
-        rl_in = rq < n_pages;
-    };
-    // the loads of one tile, one instruction per piece so that they can be spread between MFMAs:
-    // piece 0 takes the page descriptors into SGPRs, sets the keys' positions and loads the K low
-    // halves, 1 the K high halves, then V, then (keys rotated here) the cos/sin rows at the keys'
-    // positions
-    constexpr int NLOAD = 2 + NVC + (KR ? 0 : 4);
-    __amdgpu_buffer_rsrc_t k_page[NKP];   // the key pages of this thread's pieces, as buffers
-    auto load_piece = [&](int j) __attribute__((always_inline)) {
-        if (j == 0) {
-#pragma unroll
-            for (int u = 0; u < NKP; ++u) {
-                const uint32_t phys = (uint32_t)__builtin_amdgcn_readfirstlane(rk_phys[u]);
-                if constexpr (!KR) {
-                    const int pv = __builtin_amdgcn_readfirstlane(rk_pv[u]);
-                    const int pos0 = pv >> 7, valid = pv & 127;
-                    const int pi = tid + NT * u;
-                    const bool ok = (KPAIRS % NT == 0 || pi < KPAIRS) && rk_in[u] && k_slot[u] < valid;
-                    // the cos/sin row of the key's rotation (padding slots hold zeros, which
-                    // rotate to zeros with any row)
-                    if constexpr (SEG) {
-                        // the segment's rotation may be negative (keys compiled after leading tokens
-                        // linked before them): the row of its magnitude, sines negated
-                        const int r = __builtin_amdgcn_readfirstlane(rk_seg[u]);
-                        k_pos[u] = r < 0 ? -r : r;
-                        k_sgn[u] = r < 0 ? 0x80000000u : 0u;
-                    } else {
-                        k_pos[u] = ok ? pos0 + k_slot[u] : pos0;
-                    }
+            for (int s = 0; s < NS / 2; ++s) {
+                const int e0 = 16 * s + 8 * lg;
+                u32x4 lo = {0, 0, 0, 0}, hi = {0, 0, 0, 0};
+                if (valid) {
+                    lo = *reinterpret_cast<const u32x4 *>(qrow + e0);
+                    hi = *reinterpret_cast<const u32x4 *>(qrow + D / 2 + e0);
                 }
-                k_page[u] = page_rsrc(kpool_b + (uint64_t)phys * page_bytes, page_bytes);
-                k_lo[u] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(k_page[u], (int)k_loff[u], 0, 0));
-            }
-            const int slot = lane & (page_size - 1);
-            kp_stage = rl_in && slot < (rl_pv & 127) ? (rl_pv >> 7) + slot : kNeverAttended;
-        } else if (j == 1) {
+                floatx4 c[2], sn[2];
+                c[0] = *reinterpret_cast<const floatx4 *>(cs + e0);
+                c[1] = *reinterpret_cast<const floatx4 *>(cs + e0 + 4);
+                sn[0] = *reinterpret_cast<const floatx4 *>(cs + D / 2 + e0);
+                sn[1] = *reinterpret_cast<const floatx4 *>(cs + D / 2 + e0 + 4);
+                // the softmax scale and log2(e) ride on Q: scores come out of the MFMA in log2 units
 #pragma unroll
-            for (int u = 0; u < NKP; ++u)
-                k_hi[u] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(k_page[u], (int)(k_loff[u] + D), 0, 0));
-        } else if (j < 2 + NVC) {
-            const int u = j - 2;
-            const char *page = vpool_b + (uint64_t)(uint32_t)__builtin_amdgcn_readfirstlane(rv_phys[u]) * page_bytes;
-            v_r[u] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(page_rsrc(page, page_bytes), (int)v_loff[u], 0, 0));
-        } else {
-            const int q = j - 2 - NVC;   // 0: cos lo, 1: cos hi, 2: sin lo, 3: sin hi
-#pragma unroll
-            for (int u = 0; u < NKP; ++u) {
-                const uint32_t off = (uint32_t)k_pos[u] * (uint32_t)(D * 4) + k_cs_off[u];
-                const floatx4 v = *reinterpret_cast<const floatx4 *>(rope_b + off + (q >> 1) * (D * 2) + (q & 1) * 16);
-                if (q < 2) k_c[u][q & 1] = v;
-                else k_s[u][q & 1] = v;
+                for (int h = 0; h < 2; ++h) {
+                    c[h] *= p.scale_log2;
+                    sn[h] *= p.scale_log2;
+                }
+                rope8_bf16(lo, hi, c, sn, qf[s], qf[s + NS / 2]);
             }
         }
-    };
-    auto load_tile = [&]() __attribute__((always_inline)) {
-#pragma unroll
-        for (int j = 0; j < NLOAD; ++j) load_piece(j);
-    };
 
-    // staging of one tile, in pieces that fit between MFMAs: the rotation of word wd (two
-    // (x_i, x_{i+d/2}) pairs) of every K piece, then the LDS writes. K', V and key positions of a
-    // tile share ring slot sl (of 3); the mask bit of the slot records whether any key of the tile
-    // lies after the wave's first row.
-    // step k rotates pair k & 1 of word k >> 1 (the even pair is held until the odd one is ready
-    // to be packed with it)
-    float rx[NKP], ry[NKP];
-    auto rope_step = [&](int k) __attribute__((always_inline)) {
-        const int wd = k >> 1, h = k & 1;
-        if constexpr (SEG) {
-            // a negative rotation: sines negated here, where the rotation first needs them (done
-            // right after their load it would wait for the load there); k_sgn is wave-uniform
-            if (k == 0) {
-#pragma unroll
-                for (int u = 0; u < NKP; ++u)
-                    if (k_sgn[u])
-#pragma unroll
-                        for (int i = 0; i < 2; ++i)
-                            k_s[u][i] = __builtin_bit_cast(floatx4, __builtin_bit_cast(u32x4, k_s[u][i]) ^ k_sgn[u]);
-            }
+        // position of the wave's first row: its rows are consecutive selected rows of one request, in
+        // increasing position, so a key tile needs no mask for this wave when no key lies after it (a
+        // wave without rows never needs the mask: its outputs are not written)
+        const int rpos0 = __builtin_amdgcn_readfirstlane(rpos);
+        const int wave_rpos0 = rpos0 < 0 ? INT_MAX : rpos0;
+        // ... and of its last row (-1: no rows)
+        int rlast = rpos;
+        // the wave's largest row position: XOR swizzles within each half (no lane-address
+        // registers), then the two halves
+        rlast = max(rlast, __builtin_amdgcn_ds_swizzle(rlast, 0x1f | (16 << 10)));
+        rlast = max(rlast, __builtin_amdgcn_ds_swizzle(rlast, 0x1f | (8 << 10)));
+        rlast = max(rlast, __builtin_amdgcn_ds_swizzle(rlast, 0x1f | (4 << 10)));
+        rlast = max(rlast, __builtin_amdgcn_ds_swizzle(rlast, 0x1f | (2 << 10)));
+        rlast = max(rlast, __builtin_amdgcn_ds_swizzle(rlast, 0x1f | (1 << 10)));
+        {
+            const auto sw = __builtin_amdgcn_permlane32_swap(rlast, rlast, false, false);
+            rlast = max((int)sw[0], (int)sw[1]);
         }
-#pragma unroll
-        for (int u = 0; u < NKP; ++u) {
-            const float x = h ? bf_hi(k_lo[u][wd]) : bf_lo(k_lo[u][wd]);
-            const float y = h ? bf_hi(k_hi[u][wd]) : bf_lo(k_hi[u][wd]);
-            const float c = k_c[u][wd >> 1][2 * (wd & 1) + h], sn = k_s[u][wd >> 1][2 * (wd & 1) + h];
-            const float xr = fmaf(x, c, -y * sn), yr = fmaf(y, c, x * sn);
-            if (h == 0) {
-                rx[u] = xr;
-                ry[u] = yr;
-            } else {
-                k_olo[u][wd] = pack_bf16(rx[u], xr);
-                k_ohi[u][wd] = pack_bf16(ry[u], yr);
-            }
-        }
-    };
-    auto write_k = [&](int sl) __attribute__((always_inline)) {
-        uint16_t *kb = ks + sl * KBUF;
+        const int wave_rpos1 = __builtin_amdgcn_readfirstlane(rlast);
+
+        // ---- staging registers of one key tile (global -> registers -> LDS)
+        u32x4 k_lo[NKP], k_hi[NKP];
+        int k_pos[NKP];
+        uint32_t k_sgn[NKP];               // SEG: sign bit of the rotation (a negative angle flips the sines)
+        floatx4 k_c[NKP][2], k_s[NKP][2];
+        u32x4 v_r[NVC];
+        u32x4 k_olo[NKP], k_ohi[NKP];      // rotated K halves on their way to LDS
+        int kp_stage = kNeverAttended;
+        unsigned mask_ring = 7u;           // bit (t % 3): tile t needs the causal/padding mask
+
+        // Loop-invariant byte offsets of this thread's pieces inside a page (and inside a cos/sin
+        // row), so that each load is a scalar page base plus a 32-bit lane offset.
+        const char *kpool_b = static_cast<const char *>(KR ? p.k_rot : p.k_pool);
+        const char *vpool_b = static_cast<const char *>(p.v_pool);
+        const char *rope_b = reinterpret_cast<const char *>(p.rope);
+        const uint32_t page_bytes = (uint32_t)p.page_elems * 2u;
+        const int lpage0 = w.page_base + w.page_begin;   // logical page of the item's first page
+        uint32_t k_loff[NKP], k_cs_off[NKP], v_loff[NVC];
+        int k_slot[NKP];
 #pragma unroll
         for (int u = 0; u < NKP; ++u) {
             const int pi = tid + NT * u;
-            if (KPAIRS % NT != 0 && pi >= KPAIRS) break;
             const int key = pi / (D / 16), c = pi % (D / 16);
-            *reinterpret_cast<u32x4 *>(&kb[key * KS + 8 * c]) = k_olo[u];
-            *reinterpret_cast<u32x4 *>(&kb[key * KS + D / 2 + 8 * c]) = k_ohi[u];
+            k_slot[u] = key & (page_size - 1);
+            k_loff[u] = (uint32_t)(head_off + k_slot[u] * D + 8 * c) * 2u;
+            k_cs_off[u] = (uint32_t)(8 * c) * 4u;
         }
-    };
-    auto write_v = [&](int vsl, int sl) __attribute__((always_inline)) {
-        uint16_t *vb = vs + vsl * VBUF;
 #pragma unroll
         for (int u = 0; u < NVC; ++u) {
             const int pi = tid + NT * u;
-            if (VCHUNKS % NT != 0 && pi >= VCHUNKS) break;
             const int key = pi / (D / 8), c16 = pi % (D / 8);
-            *reinterpret_cast<u32x4 *>(&vb[key * VS + 8 * c16]) = v_r[u];
+            v_loff[u] = (uint32_t)(head_off + (key & (page_size - 1)) * D + 8 * c16) * 2u;
         }
-        kpos_s[sl * KT + lane] = kp_stage;   // every wave writes the same 64 values
-        const unsigned bit = 1u << sl;
-        mask_ring = __any(kp_stage > wave_rpos0) ? (mask_ring | bit) : (mask_ring & ~bit);
-    };
-    auto write_piece = [&](int j, int sl, int vsl) __attribute__((always_inline)) {
-        if (j == 0) {
-            kpos_s[sl * KT + lane] = kp_stage;
-            const unsigned bit = 1u << sl;
-            mask_ring = __any(kp_stage > wave_rpos0) ? (mask_ring | bit) : (mask_ring & ~bit);
-            uint16_t *kb = ks + sl * KBUF;
+
+        // The work item's page table is staged in LDS once: the physical page, and the page's first
+        // position and valid token count packed as pos0 << 7 | valid (pos0 < 2^22, valid <= 64).
+        // The descriptors of a tile's KT / page pages are read from LDS early in the MFMA phase and
+        // moved to SGPRs where the loads of the same phase use them. Keys of one wave's K pieces (and
+        // of each of its V pieces) lie in one page (page >= 16 tokens). Keys past the work item's
+        // range or in page padding read real, finite pool data (the last page, or the zeroed padding
+        // slots) and are removed by the mask (position kNeverAttended).
+        const int n_pages = w.page_end - w.page_begin;
+        for (int i = tid; i < n_pages; i += NT) {
+            const PageDesc d = pg[w.page_begin + i];
+            pg_phys[i] = d.phys;
+            pg_pv[i] = (d.pos0 << 7) | d.valid;
+            if constexpr (SEG) pg_seg[i] = d.seg0;
+        }
+        lds_barrier();
+        // descriptor values read ahead from LDS: the wave's K page and V pages (uniform) and the
+        // page of key `lane` (for the mask positions). The reads are unconditional (clamped to the
+        // last page) and the range test is applied where the values are used: a conditional read
+        // becomes a branch whose join waits for the LDS result at once.
+        int rk_phys[NKP], rk_pv[NKP], rk_seg[NKP], rv_phys[NVC], rl_pv;
+        bool rk_in[NKP], rl_in;
+        auto load_desc = [&](int t) __attribute__((always_inline)) {
+            const int r0 = t * ppt;
+            const int wv = __builtin_amdgcn_readfirstlane(wave);
 #pragma unroll
             for (int u = 0; u < NKP; ++u) {
-                const int pi = tid + NT * u;
-                if (KPAIRS % NT != 0 && pi >= KPAIRS) break;
-                const int key = pi / (D / 16), c = pi % (D / 16);
-                *reinterpret_cast<u32x4 *>(&kb[key * KS + 8 * c]) = k_lo[u];
-            }
-        } else if (j == 1) {
-            uint16_t *kb = ks + sl * KBUF;
-#pragma unroll
-            for (int u = 0; u < NKP; ++u) {
-                const int pi = tid + NT * u;
-                if (KPAIRS % NT != 0 && pi >= KPAIRS) break;
-                const int key = pi / (D / 16), c = pi % (D / 16);
-                *reinterpret_cast<u32x4 *>(&kb[key * KS + D / 2 + 8 * c]) = k_hi[u];
-            }
-        } else {
-            const int u = j - 2;
-            const int pi = tid + NT * u;
-            if (VCHUNKS % NT == 0 || pi < VCHUNKS) {
-                const int key = pi / (D / 8), c16 = pi % (D / 8);
-                *reinterpret_cast<u32x4 *>(&(vs + vsl * VBUF)[key * VS + 8 * c16]) = v_r[u];
-            }
-        }
-    };
-    auto store_tile = [&](int sl, int vsl) __attribute__((always_inline)) {
-        if constexpr (KR) {
-#pragma unroll
-            for (int u = 0; u < NKP; ++u) {
-                k_olo[u] = k_lo[u];
-                k_ohi[u] = k_hi[u];
-            }
-        } else {
-#pragma unroll
-            for (int r = 0; r < 8; ++r) rope_step(r);
-        }
-        write_k(sl);
-        write_v(vsl, sl);
-    };
-
-    // S^T of one tile: two 32-key blocks, NS k-steps each
-    auto qk = [&](int sl, floatx16 (&sacc)[2]) {
-        const uint16_t *kb = ks + sl * KBUF;
-#pragma unroll
-        for (int b = 0; b < 2; ++b)
-#pragma unroll
-            for (int r = 0; r < 16; ++r) sacc[b][r] = 0.0f;
-#pragma unroll
-        for (int s = 0; s < NS; ++s)
-#pragma unroll
-            for (int b = 0; b < 2; ++b) {
-                const bf16x8 a = *reinterpret_cast<const bf16x8 *>(&kb[(b * 32 + ln) * KS + 16 * s + 8 * lg]);
-                sacc[b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, __builtin_bit_cast(bf16x8, qf[s]), sacc[b],
-                                                                   0, 0, 0);
-            }
-    };
-
-    floatx16 oacc[NDB];
-#pragma unroll
-    for (int db = 0; db < NDB; ++db)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) oacc[db][r] = 0.0f;
-    // Online softmax with a lazily moved maximum carried as an MFMA bias. mrow is the running
-    // maximum in log2 units of the scaled scores, kept on bf16 values, and one extra MFMA per
-    // 32-key block adds -mrow to every S^T entry before the K'Q'^T k-steps (A = a unit vector
-    // along one k, B = -mrow of each row along the same k), so the accumulators hold s - mrow and
-    // the weights are plain exp2 of them. mrow moves only when a lane's partial sum of one tile's
-    // weights leaves (0, 2^kRescaleLog2] (a weight may exceed 2^kRescaleLog2, or overflowed),
-    // while the row has no maximum yet, or on tiles that need the causal/padding mask.
-    float mrow = 0.0f, lrow = 0.0f;
-    bool have_max = false;
-    const bf16x8 bias_a = __builtin_bit_cast(bf16x8, u32x4{lg == 0 ? 0x3f80u : 0u, 0u, 0u, 0u});   // e_0
-    u32x4 bias_b = {0u, 0u, 0u, 0u};   // -mrow at k = 0 (lanes 0-31 hold k 0..7 of their row)
-    floatx16 sacc[2];   // S^T - mrow of the tile in flight
-    u32x4 pf[2][2];     // its bf16 softmax weights, the B operands of PV
-
-    auto tile_sum = [&](const float (&e)[2][16]) -> float {
-        float part[4];
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            part[i] = e[i >> 1][8 * (i & 1)];
-#pragma unroll
-            for (int r = 1; r < 8; ++r) part[i] += e[i >> 1][8 * (i & 1) + r];
-        }
-        return (part[0] + part[1]) + (part[2] + part[3]);
-    };
-    // the row sum adds the fp32 weights with plain adds (a v_dot2 shares the matrix pipe and
-    // would stall behind the other wave's MFMAs)
-    auto apply_mask = [&](int sl) __attribute__((always_inline)) {
-        const int *kp = kpos_s + sl * KT;
-#pragma unroll
-        for (int b = 0; b < 2; ++b)
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const i32x4 kp4 = *reinterpret_cast<const i32x4 *>(&kp[b * 32 + 8 * i + 4 * lg]);
-#pragma unroll
-                for (int j = 0; j < 4; ++j) sacc[b][4 * i + j] = kp4[j] > rpos ? -INFINITY : sacc[b][4 * i + j];
-            }
-    };
-
-    // `loads(j)` issues load piece j of the next tile; the pieces are spread between the
-    // exponentials so that the wave group's loads do not queue up in the vector memory pipeline
-    auto softmax = [&](bool masked, int kc, auto loads) __attribute__((always_inline)) {
-        constexpr int NL = decltype(loads)::count;
-        float e[2][16];
-        float lsum = 0.0f;
-        bool exact = masked;
-        if (!masked) {
-#pragma unroll
-            for (int i = 0; i < 32; ++i) {
-                e[i >> 4][i & 15] = __builtin_amdgcn_exp2f(sacc[i >> 4][i & 15]);
-                if (NL > 0 && (i & 3) == 3 && (i >> 2) < NL) {
-                    loads(i >> 2);
-                    __builtin_amdgcn_sched_barrier(0);
+                const int rq = r0 + (((NT * u + 64 * wv) / (D / 16)) >> p.pshift);
+                const int r = min(rq, n_pages - 1);
+                if constexpr (KR) {
+                    rk_phys[u] = lpage0 + r;
+                } else {
+                    rk_phys[u] = pg_phys[r];
+                    rk_pv[u] = pg_pv[r];
+                    if constexpr (SEG) rk_seg[u] = pg_seg[r];
+                    rk_in[u] = rq < n_pages;
                 }
             }
-            lsum = tile_sum(e);
-            const bool ok = have_max && lsum <= (float)(1 << (int)kRescaleLog2);   // false for inf, NaN
-            exact = __any(!ok);
-        }
-        if (exact) {
-            if (masked) {
 #pragma unroll
-                for (int j = 0; j < NL; ++j) loads(j);
-                apply_mask(kc);
-            }
-            // the tile's maximum relative to mrow, over both lane halves of the row
-            float mx = sacc[0][0];
-#pragma unroll
-            for (int b = 0; b < 2; ++b)
-#pragma unroll
-                for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sacc[b][r]);
-            const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(mx), __float_as_uint(mx), false, false);
-            mx = fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1]));
-            float target = mrow;
-            bool first = false;
-            if (mx != -INFINITY) {            // the row sees a key of this tile
-                if (!have_max) {
-                    target = mrow + mx;       // nothing accumulated yet
-                    first = true;
-                    have_max = true;
-                } else if (mx > 0.0f) {
-                    target = mrow + mx;
-                }
-            }
-            // the new maximum is a bf16 value (it enters the MFMA as a bf16 operand); the shift
-            // between two bf16 values is exact in fp32
-            const uint32_t tb = pack_bf16(-target, 0.0f) & 0xffffu;
-            const float mnew = -bf_lo(tb);
-            const float shift = mnew - mrow;
-            const float alpha = first ? 1.0f : __builtin_amdgcn_exp2f(-shift);
-            mrow = mnew;
-            bias_b[0] = lg == 0 ? tb : 0u;
-#pragma unroll
-            for (int b = 0; b < 2; ++b)
-#pragma unroll
-                for (int r = 0; r < 16; ++r) e[b][r] = __builtin_amdgcn_exp2f(sacc[b][r] - shift);
-            lsum = tile_sum(e);
-            lrow *= alpha;
-            if (__any(alpha != 1.0f)) {
-#pragma unroll
-                for (int db = 0; db < NDB; ++db)
-#pragma unroll
-                    for (int r = 0; r < 16; ++r) oacc[db][r] *= alpha;
-            }
-        }
-#pragma unroll
-        for (int b = 0; b < 2; ++b)
-#pragma unroll
-            for (int s2 = 0; s2 < 2; ++s2)
-#pragma unroll
-                for (int u = 0; u < 4; ++u) pf[b][s2][u] = pack_bf16(e[b][8 * s2 + 2 * u], e[b][8 * s2 + 2 * u + 1]);
-        lrow += lsum;
-    };
-
-    // X phase: O^T += V^T P^T for tile t (V^T operands from pairs of transposing 8-byte LDS
-    // reads), then S^T = K' Q'^T for tile t+1. Only MFMAs and their operand reads: a wave issues
-    // one instruction per four cycles at best, so every other instruction in this phase would
-    // delay the MFMAs. Every MFMA's LDS operand is read three MFMAs ahead; the slots are
-    // separated by scheduling barriers, so the order below is the issue order.
-    typedef short v4s __attribute__((ext_vector_type(4)));
-    constexpr int NPV = 4 * NDB;       // PV MFMAs per tile
-    constexpr int NQK = 2 * NS;        // QK^T k-step MFMAs per tile
-    constexpr int NBIAS = 2;           // bias MFMAs (one per 32-key block) ahead of them
-    constexpr int AHEAD = 3;
-    v4s vlo[NPV], vhi[NPV];
-    bf16x8 ka[NQK];
-    auto xphase = [&](int vsl, int ksl, auto with_qk) __attribute__((always_inline)) {
-        constexpr bool QK = decltype(with_qk)::value;
-        constexpr int NM = NPV + (QK ? NBIAS + NQK : 0);
-        const int gi = lane >> 4, jj = (lane >> 2) & 3, qq = lane & 3;
-        const uint16_t *vb = vs + vsl * VBUF + (4 * lg + jj) * VS + 16 * (gi & 1) + 4 * qq;
-        const uint16_t *kb = ks + ksl * KBUF + ln * KS + 8 * lg;
-        // PV MFMA i takes d block i % NDB and k-step i / NDB (32-key block b, half s2), so that
-        // consecutive MFMAs accumulate into different output blocks; each block still takes its
-        // k-steps in the same order
-        auto read = [&](int i) __attribute__((always_inline)) {
-            if (i < NPV) {
-                const int db = i % NDB, b = (i / NDB) >> 1, s2 = (i / NDB) & 1;
-                const uint16_t *a = vb + (b * 32 + 16 * s2) * VS + db * 32;
-                vlo[i] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) v4s *)a);
-                vhi[i] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                    (__attribute__((address_space(3))) v4s *)(a + 8 * VS));
-            } else if (i >= NPV + NBIAS) {
-                const int j = i - NPV - NBIAS, s = j >> 1, b = j & 1;
-                ka[j] = *reinterpret_cast<const bf16x8 *>(kb + b * 32 * KS + 16 * s);
-            }
+            for (int u = 0; u < NVC; ++u)
+                rv_phys[u] = pg_phys[min(r0 + (((NT * u + 64 * wv) / (D / 8)) >> p.pshift), n_pages - 1)];
+            const int rq = r0 + (lane >> p.pshift);
+            rl_pv = pg_pv[min(rq, n_pages - 1)];
+            rl_in = rq < n_pages;
         };
-        auto mma = [&](int i) __attribute__((always_inline)) {
-            if (i < NPV) {
-                const int db = i % NDB, b = (i / NDB) >> 1, s2 = (i / NDB) & 1;
-                const bf16x8 a = __builtin_bit_cast(bf16x8, __builtin_shufflevector(vlo[i], vhi[i], 0, 1, 2, 3, 4, 5, 6, 7));
-                oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, __builtin_bit_cast(bf16x8, pf[b][s2]), oacc[db],
-                                                                   0, 0, 0);
-            } else if (i < NPV + NBIAS) {
-                const floatx16 zero = {};
-                sacc[i - NPV] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bias_a, __builtin_bit_cast(bf16x8, bias_b), zero,
-                                                                        0, 0, 0);
+        // the loads of one tile, one instruction per piece so that they can be spread between MFMAs:
+        // piece 0 takes the page descriptors into SGPRs, sets the keys' positions and loads the K low
+        // halves, 1 the K high halves, then V, then (keys rotated here) the cos/sin rows at the keys'
+        // positions
+        constexpr int NLOAD = 2 + NVC + (KR ? 0 : 4);
+        __amdgpu_buffer_rsrc_t k_page[NKP];   // the key pages of this thread's pieces, as buffers
+        auto load_piece = [&](int j) __attribute__((always_inline)) {
+            if (j == 0) {
+#pragma unroll
+                for (int u = 0; u < NKP; ++u) {
+                    const uint32_t phys = (uint32_t)__builtin_amdgcn_readfirstlane(rk_phys[u]);
+                    if constexpr (!KR) {
+                        const int pv = __builtin_amdgcn_readfirstlane(rk_pv[u]);
+                        const int pos0 = pv >> 7, valid = pv & 127;
+                        const int pi = tid + NT * u;
+                        const bool ok = (KPAIRS % NT == 0 || pi < KPAIRS) && rk_in[u] && k_slot[u] < valid;
+                        // the cos/sin row of the key's rotation (padding slots hold zeros, which
+                        // rotate to zeros with any row)
+                        if constexpr (SEG) {
+                            // the segment's rotation may be negative (keys compiled after leading tokens
+                            // linked before them): the row of its magnitude, sines negated
+                            const int r = __builtin_amdgcn_readfirstlane(rk_seg[u]);
+                            k_pos[u] = r < 0 ? -r : r;
+                            k_sgn[u] = r < 0 ? 0x80000000u : 0u;
+                        } else {
+                            k_pos[u] = ok ? pos0 + k_slot[u] : pos0;
+                        }
+                    }
+                    k_page[u] = page_rsrc(kpool_b + (uint64_t)phys * page_bytes, page_bytes);
+                    k_lo[u] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(k_page[u], (int)k_loff[u], 0, 0));
+                }
+                const int slot = lane & (page_size - 1);
+                kp_stage = rl_in && slot < (rl_pv & 127) ? (rl_pv >> 7) + slot : kNeverAttended;
+            } else if (j == 1) {
+#pragma unroll
+                for (int u = 0; u < NKP; ++u)
+                    k_hi[u] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(k_page[u], (int)(k_loff[u] + D), 0, 0));
+            } else if (j < 2 + NVC) {
+                const int u = j - 2;
+                const char *page = vpool_b + (uint64_t)(uint32_t)__builtin_amdgcn_readfirstlane(rv_phys[u]) * page_bytes;
+                v_r[u] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(page_rsrc(page, page_bytes), (int)v_loff[u], 0, 0));
             } else {
-                const int j = i - NPV - NBIAS, s = j >> 1, b = j & 1;
-                sacc[b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[j], __builtin_bit_cast(bf16x8, qf[s]), sacc[b], 0, 0, 0);
+                const int q = j - 2 - NVC;   // 0: cos lo, 1: cos hi, 2: sin lo, 3: sin hi
+#pragma unroll
+                for (int u = 0; u < NKP; ++u) {
+                    const uint32_t off = (uint32_t)k_pos[u] * (uint32_t)(D * 4) + k_cs_off[u];
+                    const floatx4 v = *reinterpret_cast<const floatx4 *>(rope_b + off + (q >> 1) * (D * 2) + (q & 1) * 16);
+                    if (q < 2) k_c[u][q & 1] = v;
+                    else k_s[u][q & 1] = v;
+                }
             }
         };
-#pragma unroll
-        for (int i = 0; i < AHEAD; ++i) read(i);
-        __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-        for (int i = 0; i < NM; ++i) {
-            mma(i);
-            if (i + AHEAD < NM) read(i + AHEAD);
-            __builtin_amdgcn_sched_barrier(0);
-        }
-    };
-
-    const int ntiles = (w.page_end - w.page_begin + ppt - 1) / ppt;
-    const bool group_b = wave >= 4;
-    // Key tiles this wave attends: those whose first key is at or before its last row, a prefix
-    // [0, n_act) of the item's tiles (page positions increase). Past it the wave only stages tiles
-    // for the other waves, and its SIMD partner runs alone.
-    int n_act;
-    {
-        int lo = 0, hi = n_pages;   // first page whose first position lies after the last row
-        while (lo < hi) {
-            const int mid = (lo + hi) >> 1;
-            if ((pg_pv[mid] >> 7) <= wave_rpos1) lo = mid + 1;
-            else hi = mid;
-        }
-        n_act = __builtin_amdgcn_readfirstlane((lo + ppt - 1) / ppt);
-    }
-
-    load_desc(0);
-    load_tile();
-    store_tile(0, 0);
-    load_desc(1);
-    load_tile();
-    store_tile(1, 1);
-    lds_barrier();
-    qk(0, sacc);
-    load_desc(2);
-    load_tile();
-    load_desc(3);
-    if (group_b) lds_barrier();
-
-    // ring slots of tiles t, t+1, t+2: K' and key positions in a ring of 3, V in a ring of 4 (the
-    // one-phase skew between the wave groups keeps a V tile in use one phase longer)
-    int kc = 0, kn = 1, ks2 = 2, vc = 0;
-    // one tile. Y(t): LDS staging of tile t+2 from the registers loaded one step earlier and
-    // the loads of tile t+3 into the freed registers (a whole step ahead of their use), with the
-    // softmax of tile t. X(t): PV of tile t, QK^T of tile t+1, and the page descriptors of the
-    // next step's loads.
-    auto step = [&](int t, auto next_qk, auto staging, auto next_staging) __attribute__((always_inline)) {
-        constexpr bool STAGE = decltype(staging)::value;
-        if constexpr (KR) {
-            // each staged piece goes to LDS just before the load that reuses its registers, so the
-            // tile's LDS writes are spread over the exponentials
-            const int wsl = ks2, wvsl = (vc + 2) & 3;
-            const bool masked = (mask_ring >> kc) & 1u;   // read before piece 0 updates the ring
-            auto stage_load = [&](int j) __attribute__((always_inline)) {
-                write_piece(j, wsl, wvsl);
-                load_piece(j);
-            };
-            softmax(masked, kc, Loads<STAGE ? NLOAD : 0, decltype(stage_load) &>{stage_load});
-        } else {
-            if constexpr (STAGE) store_tile(ks2, (vc + 2) & 3);
-            softmax((mask_ring >> kc) & 1u, kc, Loads<STAGE ? NLOAD : 0, decltype(load_piece) &>{load_piece});
-        }
-        __builtin_amdgcn_sched_barrier(0);
-        lds_barrier();
-        xphase(vc, kn, next_qk);
-        if constexpr (decltype(next_staging)::value) load_desc(t + 4);
-        __builtin_amdgcn_sched_barrier(0);
-        lds_barrier();
-        const int old = kc;
-        kc = kn;
-        kn = ks2;
-        ks2 = old;
-        vc = (vc + 1) & 3;
-    };
-    // a step of a wave past its last key tile: the staging of tile t+2 and the loads of tile t+3,
-    // with the same two barriers as `step`
-    auto idle_step = [&](int t, auto staging, auto next_staging) __attribute__((always_inline)) {
-        if constexpr (decltype(staging)::value) {
-            store_tile(ks2, (vc + 2) & 3);
+        auto load_tile = [&]() __attribute__((always_inline)) {
 #pragma unroll
             for (int j = 0; j < NLOAD; ++j) load_piece(j);
-        }
-        __builtin_amdgcn_sched_barrier(0);
-        lds_barrier();
-        if constexpr (decltype(next_staging)::value) load_desc(t + 4);
-        __builtin_amdgcn_sched_barrier(0);
-        lds_barrier();
-        const int old = kc;
-        kc = kn;
-        kn = ks2;
-        ks2 = old;
-        vc = (vc + 1) & 3;
-    };
-    using yes = std::integral_constant<bool, true>;
-    using no = std::integral_constant<bool, false>;
-    // every wave passes 2 barriers per tile for all ntiles tiles, active or not
-    int t = 0;
-    const int t_main = min(n_act, ntiles - 3);
-    for (; t < t_main; ++t) step(t, yes{}, yes{}, yes{});
-    for (; t + 3 < ntiles; ++t) idle_step(t, yes{}, yes{});
-    if (t + 2 < ntiles) {
-        if (t < n_act) step(t, yes{}, yes{}, no{});
-        else idle_step(t, yes{}, no{});
-        ++t;
-    }
-    if (t + 1 < ntiles) {
-        if (t < n_act) step(t, yes{}, no{}, no{});
-        else idle_step(t, no{}, no{});
-        ++t;
-    }
-    if (t < ntiles) {
-        if (t < n_act) step(t, no{}, no{}, no{});
-        else idle_step(t, no{}, no{});
-    }
-    if (!group_b) lds_barrier();
+        };
 
-    // ---- epilogue: normalise, write the output (or this split's partial result)
-    {
-        const int m = wave * 32 + ln;
-        const int ti = m >> p.gshift;
-        const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(lrow), __float_as_uint(lrow), false, false);
-        const float lt = __uint_as_float(sw[0]) + __uint_as_float(sw[1]);
-        const float inv = lt > 0.0f ? 1.0f / lt : 0.0f;
-        const float lse_v = lt > 0.0f ? (mrow + __builtin_amdgcn_logf(lt)) * 0.6931471805599453f : -INFINITY;
-        if (ti < w.n_rows) {
-            const int row = w.row0 + ti;
-            const int qh = w.kv_head * G + (m & (G - 1));
-            if (w.partial < 0) {
-                uint16_t *orow = static_cast<uint16_t *>(p.out) + ((int64_t)row * p.hq + qh) * D;
+        // staging of one tile, in pieces that fit between MFMAs: the rotation of word wd (two
+        // (x_i, x_{i+d/2}) pairs) of every K piece, then the LDS writes. K', V and key positions of a
+        // tile share ring slot sl (of 3); the mask bit of the slot records whether any key of the tile
+        // lies after the wave's first row.
+        // step k rotates pair k & 1 of word k >> 1 (the even pair is held until the odd one is ready
+        // to be packed with it)
+        float rx[NKP], ry[NKP];
+        auto rope_step = [&](int k) __attribute__((always_inline)) {
+            const int wd = k >> 1, h = k & 1;
+            if constexpr (SEG) {
+                // a negative rotation: sines negated here, where the rotation first needs them (done
+                // right after their load it would wait for the load there); k_sgn is wave-uniform
+                if (k == 0) {
 #pragma unroll
-                for (int db = 0; db < NDB; ++db)
+                    for (int u = 0; u < NKP; ++u)
+                        if (k_sgn[u])
 #pragma unroll
-                    for (int i = 0; i < 4; ++i) {
-                        const int d0 = db * 32 + 8 * i + 4 * lg;
-                        u32x2 v;
-                        v[0] = pack_bf16(oacc[db][4 * i] * inv, oacc[db][4 * i + 1] * inv);
-                        v[1] = pack_bf16(oacc[db][4 * i + 2] * inv, oacc[db][4 * i + 3] * inv);
-                        *reinterpret_cast<u32x2 *>(orow + d0) = v;
-                    }
-                if (p.lse && lg == 0) p.lse[(int64_t)row * p.hq + qh] = lse_v;
+                            for (int i = 0; i < 2; ++i)
+                                k_s[u][i] = __builtin_bit_cast(floatx4, __builtin_bit_cast(u32x4, k_s[u][i]) ^ k_sgn[u]);
+                }
+            }
+#pragma unroll
+            for (int u = 0; u < NKP; ++u) {
+                const float x = h ? bf_hi(k_lo[u][wd]) : bf_lo(k_lo[u][wd]);
+                const float y = h ? bf_hi(k_hi[u][wd]) : bf_lo(k_hi[u][wd]);
+                const float c = k_c[u][wd >> 1][2 * (wd & 1) + h], sn = k_s[u][wd >> 1][2 * (wd & 1) + h];
+                const float xr = fmaf(x, c, -y * sn), yr = fmaf(y, c, x * sn);
+                if (h == 0) {
+                    rx[u] = xr;
+                    ry[u] = yr;
+                } else {
+                    k_olo[u][wd] = pack_bf16(rx[u], xr);
+                    k_ohi[u][wd] = pack_bf16(ry[u], yr);
+                }
+            }
+        };
+        auto write_k = [&](int sl) __attribute__((always_inline)) {
+            uint16_t *kb = ks + sl * KBUF;
+#pragma unroll
+            for (int u = 0; u < NKP; ++u) {
+                const int pi = tid + NT * u;
+                if (KPAIRS % NT != 0 && pi >= KPAIRS) break;
+                const int key = pi / (D / 16), c = pi % (D / 16);
+                *reinterpret_cast<u32x4 *>(&kb[key * KS + 8 * c]) = k_olo[u];
+                *reinterpret_cast<u32x4 *>(&kb[key * KS + D / 2 + 8 * c]) = k_ohi[u];
+            }
+        };
+        auto write_v = [&](int vsl, int sl) __attribute__((always_inline)) {
+            uint16_t *vb = vs + vsl * VBUF;
+#pragma unroll
+            for (int u = 0; u < NVC; ++u) {
+                const int pi = tid + NT * u;
+                if (VCHUNKS % NT != 0 && pi >= VCHUNKS) break;
+                const int key = pi / (D / 8), c16 = pi % (D / 8);
+                *reinterpret_cast<u32x4 *>(&vb[key * VS + 8 * c16]) = v_r[u];
+            }
+            kpos_s[sl * KT + lane] = kp_stage;   // every wave writes the same 64 values
+            const unsigned bit = 1u << sl;
+            mask_ring = __any(kp_stage > wave_rpos0) ? (mask_ring | bit) : (mask_ring & ~bit);
+        };
+        auto write_piece = [&](int j, int sl, int vsl) __attribute__((always_inline)) {
+            if (j == 0) {
+                kpos_s[sl * KT + lane] = kp_stage;
+                const unsigned bit = 1u << sl;
+                mask_ring = __any(kp_stage > wave_rpos0) ? (mask_ring | bit) : (mask_ring & ~bit);
+                uint16_t *kb = ks + sl * KBUF;
+#pragma unroll
+                for (int u = 0; u < NKP; ++u) {
+                    const int pi = tid + NT * u;
+                    if (KPAIRS % NT != 0 && pi >= KPAIRS) break;
+                    const int key = pi / (D / 16), c = pi % (D / 16);
+                    *reinterpret_cast<u32x4 *>(&kb[key * KS + 8 * c]) = k_lo[u];
+                }
+            } else if (j == 1) {
+                uint16_t *kb = ks + sl * KBUF;
+#pragma unroll
+                for (int u = 0; u < NKP; ++u) {
+                    const int pi = tid + NT * u;
+                    if (KPAIRS % NT != 0 && pi >= KPAIRS) break;
+                    const int key = pi / (D / 16), c = pi % (D / 16);
+                    *reinterpret_cast<u32x4 *>(&kb[key * KS + D / 2 + 8 * c]) = k_hi[u];
+                }
             } else {
-                float *po = p.part_o + ((int64_t)w.partial * TQ + m) * D;
+                const int u = j - 2;
+                const int pi = tid + NT * u;
+                if (VCHUNKS % NT == 0 || pi < VCHUNKS) {
+                    const int key = pi / (D / 8), c16 = pi % (D / 8);
+                    *reinterpret_cast<u32x4 *>(&(vs + vsl * VBUF)[key * VS + 8 * c16]) = v_r[u];
+                }
+            }
+        };
+        auto store_tile = [&](int sl, int vsl) __attribute__((always_inline)) {
+            if constexpr (KR) {
 #pragma unroll
-                for (int db = 0; db < NDB; ++db)
+                for (int u = 0; u < NKP; ++u) {
+                    k_olo[u] = k_lo[u];
+                    k_ohi[u] = k_hi[u];
+                }
+            } else {
 #pragma unroll
-                    for (int i = 0; i < 4; ++i) {
-                        const int d0 = db * 32 + 8 * i + 4 * lg;
-                        floatx4 v = {oacc[db][4 * i] * inv, oacc[db][4 * i + 1] * inv, oacc[db][4 * i + 2] * inv,
-                                     oacc[db][4 * i + 3] * inv};
-                        *reinterpret_cast<floatx4 *>(po + d0) = v;
+                for (int r = 0; r < 8; ++r) rope_step(r);
+            }
+            write_k(sl);
+            write_v(vsl, sl);
+        };
+
+        // S^T of one tile: two 32-key blocks, NS k-steps each
+        auto qk = [&](int sl, floatx16 (&sacc)[2]) {
+            const uint16_t *kb = ks + sl * KBUF;
+#pragma unroll
+            for (int b = 0; b < 2; ++b)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) sacc[b][r] = 0.0f;
+#pragma unroll
+            for (int s = 0; s < NS; ++s)
+#pragma unroll
+                for (int b = 0; b < 2; ++b) {
+                    const bf16x8 a = *reinterpret_cast<const bf16x8 *>(&kb[(b * 32 + ln) * KS + 16 * s + 8 * lg]);
+                    sacc[b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, __builtin_bit_cast(bf16x8, qf[s]), sacc[b],
+                                                                       0, 0, 0);
+                }
+        };
+
+        floatx16 oacc[NDB];
+#pragma unroll
+        for (int db = 0; db < NDB; ++db)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) oacc[db][r] = 0.0f;
+        // Online softmax with a lazily moved maximum carried as an MFMA bias. mrow is the running
+        // maximum in log2 units of the scaled scores, kept on bf16 values, and one extra MFMA per
+        // 32-key block adds -mrow to every S^T entry before the K'Q'^T k-steps (A = a unit vector
+        // along one k, B = -mrow of each row along the same k), so the accumulators hold s - mrow and
+        // the weights are plain exp2 of them. mrow moves only when a lane's partial sum of one tile's
+        // weights leaves (0, 2^kRescaleLog2] (a weight may exceed 2^kRescaleLog2, or overflowed),
+        // while the row has no maximum yet, or on tiles that need the causal/padding mask.
+        float mrow = 0.0f, lrow = 0.0f;
+        bool have_max = false;
+        const bf16x8 bias_a = __builtin_bit_cast(bf16x8, u32x4{lg == 0 ? 0x3f80u : 0u, 0u, 0u, 0u});   // e_0
+        u32x4 bias_b = {0u, 0u, 0u, 0u};   // -mrow at k = 0 (lanes 0-31 hold k 0..7 of their row)
+        floatx16 sacc[2];   // S^T - mrow of the tile in flight
+        u32x4 pf[2][2];     // its bf16 softmax weights, the B operands of PV
+
+        auto tile_sum = [&](const float (&e)[2][16]) -> float {
+            float part[4];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                part[i] = e[i >> 1][8 * (i & 1)];
+#pragma unroll
+                for (int r = 1; r < 8; ++r) part[i] += e[i >> 1][8 * (i & 1) + r];
+            }
+            return (part[0] + part[1]) + (part[2] + part[3]);
+        };
+        // the row sum adds the fp32 weights with plain adds (a v_dot2 shares the matrix pipe and
+        // would stall behind the other wave's MFMAs)
+        auto apply_mask = [&](int sl) __attribute__((always_inline)) {
+            const int *kp = kpos_s + sl * KT;
+#pragma unroll
+            for (int b = 0; b < 2; ++b)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const i32x4 kp4 = *reinterpret_cast<const i32x4 *>(&kp[b * 32 + 8 * i + 4 * lg]);
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) sacc[b][4 * i + j] = kp4[j] > rpos ? -INFINITY : sacc[b][4 * i + j];
+                }
+        };
+
+        // `loads(j)` issues load piece j of the next tile; the pieces are spread between the
+        // exponentials so that the wave group's loads do not queue up in the vector memory pipeline
+        auto softmax = [&](bool masked, int kc, auto loads) __attribute__((always_inline)) {
+            constexpr int NL = decltype(loads)::count;
+            float e[2][16];
+            float lsum = 0.0f;
+            bool exact = masked;
+            if (!masked) {
+#pragma unroll
+                for (int i = 0; i < 32; ++i) {
+                    e[i >> 4][i & 15] = __builtin_amdgcn_exp2f(sacc[i >> 4][i & 15]);
+                    if (NL > 0 && (i & 3) == 3 && (i >> 2) < NL) {
+                        loads(i >> 2);
+                        __builtin_amdgcn_sched_barrier(0);
                     }
-                if (lg == 0) p.part_lse[(int64_t)w.partial * TQ + m] = lse_v;
+                }
+                lsum = tile_sum(e);
+                const bool ok = have_max && lsum <= (float)(1 << (int)kRescaleLog2);   // false for inf, NaN
+                exact = __any(!ok);
+            }
+            if (exact) {
+                if (masked) {
+#pragma unroll
+                    for (int j = 0; j < NL; ++j) loads(j);
+                    apply_mask(kc);
+                }
+                // the tile's maximum relative to mrow, over both lane halves of the row
+                float mx = sacc[0][0];
+#pragma unroll
+                for (int b = 0; b < 2; ++b)
+#pragma unroll
+                    for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sacc[b][r]);
+                const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(mx), __float_as_uint(mx), false, false);
+                mx = fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1]));
+                float target = mrow;
+                bool first = false;
+                if (mx != -INFINITY) {            // the row sees a key of this tile
+                    if (!have_max) {
+                        target = mrow + mx;       // nothing accumulated yet
+                        first = true;
+                        have_max = true;
+                    } else if (mx > 0.0f) {
+                        target = mrow + mx;
+                    }
+                }
+                // the new maximum is a bf16 value (it enters the MFMA as a bf16 operand); the shift
+                // between two bf16 values is exact in fp32
+                const uint32_t tb = pack_bf16(-target, 0.0f) & 0xffffu;
+                const float mnew = -bf_lo(tb);
+                const float shift = mnew - mrow;
+                const float alpha = first ? 1.0f : __builtin_amdgcn_exp2f(-shift);
+                mrow = mnew;
+                bias_b[0] = lg == 0 ? tb : 0u;
+#pragma unroll
+                for (int b = 0; b < 2; ++b)
+#pragma unroll
+                    for (int r = 0; r < 16; ++r) e[b][r] = __builtin_amdgcn_exp2f(sacc[b][r] - shift);
+                lsum = tile_sum(e);
+                lrow *= alpha;
+                if (__any(alpha != 1.0f)) {
+#pragma unroll
+                    for (int db = 0; db < NDB; ++db)
+#pragma unroll
+                        for (int r = 0; r < 16; ++r) oacc[db][r] *= alpha;
+                }
+            }
+#pragma unroll
+            for (int b = 0; b < 2; ++b)
+#pragma unroll
+                for (int s2 = 0; s2 < 2; ++s2)
+#pragma unroll
+                    for (int u = 0; u < 4; ++u) pf[b][s2][u] = pack_bf16(e[b][8 * s2 + 2 * u], e[b][8 * s2 + 2 * u + 1]);
+            lrow += lsum;
+        };
+
+        // X phase: O^T += V^T P^T for tile t (V^T operands from pairs of transposing 8-byte LDS
+        // reads), then S^T = K' Q'^T for tile t+1. Only MFMAs and their operand reads: a wave issues
+        // one instruction per four cycles at best, so every other instruction in this phase would
+        // delay the MFMAs. Every MFMA's LDS operand is read three MFMAs ahead; the slots are
+        // separated by scheduling barriers, so the order below is the issue order.
+        typedef short v4s __attribute__((ext_vector_type(4)));
+        constexpr int NPV = 4 * NDB;       // PV MFMAs per tile
+        constexpr int NQK = 2 * NS;        // QK^T k-step MFMAs per tile
+        constexpr int NBIAS = 2;           // bias MFMAs (one per 32-key block) ahead of them
+        constexpr int AHEAD = 3;
+        v4s vlo[NPV], vhi[NPV];
+        bf16x8 ka[NQK];
+        auto xphase = [&](int vsl, int ksl, auto with_qk) __attribute__((always_inline)) {
+            constexpr bool QK = decltype(with_qk)::value;
+            constexpr int NM = NPV + (QK ? NBIAS + NQK : 0);
+            const int gi = lane >> 4, jj = (lane >> 2) & 3, qq = lane & 3;
+            const uint16_t *vb = vs + vsl * VBUF + (4 * lg + jj) * VS + 16 * (gi & 1) + 4 * qq;
+            const uint16_t *kb = ks + ksl * KBUF + ln * KS + 8 * lg;
+            // PV MFMA i takes d block i % NDB and k-step i / NDB (32-key block b, half s2), so that
+            // consecutive MFMAs accumulate into different output blocks; each block still takes its
+            // k-steps in the same order
+            auto read = [&](int i) __attribute__((always_inline)) {
+                if (i < NPV) {
+                    const int db = i % NDB, b = (i / NDB) >> 1, s2 = (i / NDB) & 1;
+                    const uint16_t *a = vb + (b * 32 + 16 * s2) * VS + db * 32;
+                    vlo[i] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) v4s *)a);
+                    vhi[i] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                        (__attribute__((address_space(3))) v4s *)(a + 8 * VS));
+                } else if (i >= NPV + NBIAS) {
+                    const int j = i - NPV - NBIAS, s = j >> 1, b = j & 1;
+                    ka[j] = *reinterpret_cast<const bf16x8 *>(kb + b * 32 * KS + 16 * s);
+                }
+            };
+            auto mma = [&](int i) __attribute__((always_inline)) {
+                if (i < NPV) {
+                    const int db = i % NDB, b = (i / NDB) >> 1, s2 = (i / NDB) & 1;
+                    const bf16x8 a = __builtin_bit_cast(bf16x8, __builtin_shufflevector(vlo[i], vhi[i], 0, 1, 2, 3, 4, 5, 6, 7));
+                    oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, __builtin_bit_cast(bf16x8, pf[b][s2]), oacc[db],
+                                                                       0, 0, 0);
+                } else if (i < NPV + NBIAS) {
+                    const floatx16 zero = {};
+                    sacc[i - NPV] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bias_a, __builtin_bit_cast(bf16x8, bias_b), zero,
+                                                                            0, 0, 0);
+                } else {
+                    const int j = i - NPV - NBIAS, s = j >> 1, b = j & 1;
+                    sacc[b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[j], __builtin_bit_cast(bf16x8, qf[s]), sacc[b], 0, 0, 0);
+                }
+            };
+#pragma unroll
+            for (int i = 0; i < AHEAD; ++i) read(i);
+            __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+            for (int i = 0; i < NM; ++i) {
+                mma(i);
+                if (i + AHEAD < NM) read(i + AHEAD);
+                __builtin_amdgcn_sched_barrier(0);
+            }
+        };
+
+        const int ntiles = (w.page_end - w.page_begin + ppt - 1) / ppt;
+        const bool group_b = wave >= 4;
+        // Key tiles this wave attends: those whose first key is at or before its last row, a prefix
+        // [0, n_act) of the item's tiles (page positions increase). Past it the wave only stages tiles
+        // for the other waves, and its SIMD partner runs alone.
+        int n_act;
+        {
+            int lo = 0, hi = n_pages;   // first page whose first position lies after the last row
+            while (lo < hi) {
+                const int mid = (lo + hi) >> 1;
+                if ((pg_pv[mid] >> 7) <= wave_rpos1) lo = mid + 1;
+                else hi = mid;
+            }
+            n_act = __builtin_amdgcn_readfirstlane((lo + ppt - 1) / ppt);
+        }
+
+        load_desc(0);
+        load_tile();
+        store_tile(0, 0);
+        load_desc(1);
+        load_tile();
+        store_tile(1, 1);
+        lds_barrier();
+        qk(0, sacc);
+        load_desc(2);
+        load_tile();
+        load_desc(3);
+        if (group_b) lds_barrier();
+
+        // ring slots of tiles t, t+1, t+2: K' and key positions in a ring of 3, V in a ring of 4 (the
+        // one-phase skew between the wave groups keeps a V tile in use one phase longer)
+        int kc = 0, kn = 1, ks2 = 2, vc = 0;
+        // one tile. Y(t): LDS staging of tile t+2 from the registers loaded one step earlier and
+        // the loads of tile t+3 into the freed registers (a whole step ahead of their use), with the
+        // softmax of tile t. X(t): PV of tile t, QK^T of tile t+1, and the page descriptors of the
+        // next step's loads.
+        auto step = [&](int t, auto next_qk, auto staging, auto next_staging) __attribute__((always_inline)) {
+            constexpr bool STAGE = decltype(staging)::value;
+            if constexpr (KR) {
+                // each staged piece goes to LDS just before the load that reuses its registers, so the
+                // tile's LDS writes are spread over the exponentials
+                const int wsl = ks2, wvsl = (vc + 2) & 3;
+                const bool masked = (mask_ring >> kc) & 1u;   // read before piece 0 updates the ring
+                auto stage_load = [&](int j) __attribute__((always_inline)) {
+                    write_piece(j, wsl, wvsl);
+                    load_piece(j);
+                };
+                softmax(masked, kc, Loads<STAGE ? NLOAD : 0, decltype(stage_load) &>{stage_load});
+            } else {
+                if constexpr (STAGE) store_tile(ks2, (vc + 2) & 3);
+                softmax((mask_ring >> kc) & 1u, kc, Loads<STAGE ? NLOAD : 0, decltype(load_piece) &>{load_piece});
+            }
+            __builtin_amdgcn_sched_barrier(0);
+            lds_barrier();
+            xphase(vc, kn, next_qk);
+            if constexpr (decltype(next_staging)::value) load_desc(t + 4);
+            __builtin_amdgcn_sched_barrier(0);
+            lds_barrier();
+            const int old = kc;
+            kc = kn;
+            kn = ks2;
+            ks2 = old;
+            vc = (vc + 1) & 3;
+        };
+        // a step of a wave past its last key tile: the staging of tile t+2 and the loads of tile t+3,
+        // with the same two barriers as `step`
+        auto idle_step = [&](int t, auto staging, auto next_staging) __attribute__((always_inline)) {
+            if constexpr (decltype(staging)::value) {
+                store_tile(ks2, (vc + 2) & 3);
+#pragma unroll
+                for (int j = 0; j < NLOAD; ++j) load_piece(j);
+            }
+            __builtin_amdgcn_sched_barrier(0);
+            lds_barrier();
+            if constexpr (decltype(next_staging)::value) load_desc(t + 4);
+            __builtin_amdgcn_sched_barrier(0);
+            lds_barrier();
+            const int old = kc;
+            kc = kn;
+            kn = ks2;
+            ks2 = old;
+            vc = (vc + 1) & 3;
+        };
+        using yes = std::integral_constant<bool, true>;
+        using no = std::integral_constant<bool, false>;
+        // every wave passes 2 barriers per tile for all ntiles tiles, active or not
+        int t = 0;
+        const int t_main = min(n_act, ntiles - 3);
+        for (; t < t_main; ++t) step(t, yes{}, yes{}, yes{});
+        for (; t + 3 < ntiles; ++t) idle_step(t, yes{}, yes{});
+        if (t + 2 < ntiles) {
+            if (t < n_act) step(t, yes{}, yes{}, no{});
+            else idle_step(t, yes{}, no{});
+            ++t;
+        }
+        if (t + 1 < ntiles) {
+            if (t < n_act) step(t, yes{}, no{}, no{});
+            else idle_step(t, no{}, no{});
+            ++t;
+        }
+        if (t < ntiles) {
+            if (t < n_act) step(t, no{}, no{}, no{});
+            else idle_step(t, no{}, no{});
+        }
+        if (!group_b) lds_barrier();
+
+        // ---- epilogue: normalise, write the output (or this split's partial result)
+        {
+            const int m = wave * 32 + ln;
+            const int ti = m >> p.gshift;
+            const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(lrow), __float_as_uint(lrow), false, false);
+            const float lt = __uint_as_float(sw[0]) + __uint_as_float(sw[1]);
+            const float inv = lt > 0.0f ? 1.0f / lt : 0.0f;
+            const float lse_v = lt > 0.0f ? (mrow + __builtin_amdgcn_logf(lt)) * 0.6931471805599453f : -INFINITY;
+            if (ti < w.n_rows) {
+                const int row = w.row0 + ti;
+                const int qh = w.kv_head * G + (m & (G - 1));
+                if (w.partial < 0) {
+                    uint16_t *orow = static_cast<uint16_t *>(p.out) + ((int64_t)row * p.hq + qh) * D;
+#pragma unroll
+                    for (int db = 0; db < NDB; ++db)
+#pragma unroll
+                        for (int i = 0; i < 4; ++i) {
+                            const int d0 = db * 32 + 8 * i + 4 * lg;
+                            u32x2 v;
+                            v[0] = pack_bf16(oacc[db][4 * i] * inv, oacc[db][4 * i + 1] * inv);
+                            v[1] = pack_bf16(oacc[db][4 * i + 2] * inv, oacc[db][4 * i + 3] * inv);
+                            *reinterpret_cast<u32x2 *>(orow + d0) = v;
+                        }
+                    if (p.lse && lg == 0) p.lse[(int64_t)row * p.hq + qh] = lse_v;
+                } else {
+                    float *po = p.part_o + ((int64_t)w.partial * TQ + m) * D;
+#pragma unroll
+                    for (int db = 0; db < NDB; ++db)
+#pragma unroll
+                        for (int i = 0; i < 4; ++i) {
+                            const int d0 = db * 32 + 8 * i + 4 * lg;
+                            floatx4 v = {oacc[db][4 * i] * inv, oacc[db][4 * i + 1] * inv, oacc[db][4 * i + 2] * inv,
+                                         oacc[db][4 * i + 3] * inv};
+                            *reinterpret_cast<floatx4 *>(po + d0) = v;
+                        }
+                    if (lg == 0) p.part_lse[(int64_t)w.partial * TQ + m] = lse_v;
+                }
             }
         }
     }
+    if (threadIdx.x == 0) release_work_queues(p);
 }
 
 // ---------------------------------------------------------------------------------------------
@@ -845,512 +923,535 @@ __global__ __launch_bounds__(512, 1) void link_attention_bf16_dl(AttnParams p) {
     __shared__ __attribute__((aligned(16))) int kpos_s[4 * KT];
     __shared__ int pg_phys[kMaxItemPages], pg_pv[kMaxItemPages];
 
-    const WorkDesc w = p.work[blockIdx.x];
-    if (w.n_rows <= 0) return;
+    // the work group's items, one after the other (next_work_item)
+    __shared__ int item_s;
+    int wstate = 0;   // thread 0's
+    for (;;) {
+        barrier_dl();   // every wave is done with the previous item's LDS, item_s included
+        if (threadIdx.x == 0) item_s = next_work_item(p, wstate);
+        barrier_dl();
+        const int item = __builtin_amdgcn_readfirstlane(item_s);
+        if (item < 0) break;
+        const WorkDesc w = p.work[item];
+        if (w.n_rows <= 0) continue;
 
-    const int tid = threadIdx.x;
-    const int wave = tid >> 6, lane = tid & 63, ln = lane & 31, lg = lane >> 5;
-    const int wv = __builtin_amdgcn_readfirstlane(wave);
-    const int G = 1 << p.gshift;
-    const int page_size = 1 << p.pshift;
-    const int ppt = KT >> p.pshift;
-    const PageDesc *pg = p.pages + w.page_base;
-    const int64_t head_off = (int64_t)w.kv_head * page_size * D;
+        // the lane's index as an opaque value per item: values derived from it are computed inside
+        // the loop instead of being held in registers across it
+        int tid = threadIdx.x;
+        asm volatile("" : "+v"(tid));
+        const int wave = tid >> 6, lane = tid & 63, ln = lane & 31, lg = lane >> 5;
+        const int wv = __builtin_amdgcn_readfirstlane(wave);
+        const int G = 1 << p.gshift;
+        const int page_size = 1 << p.pshift;
+        const int ppt = KT >> p.pshift;
+        const PageDesc *pg = p.pages + w.page_base;
+        const int64_t head_off = (int64_t)w.kv_head * page_size * D;
 
-    // slots: compile-time (std::integral_constant) in the unrolled main loop, else run-time
-    auto kslot = [&](auto s) -> uint16_t * {
-        if constexpr (IsSlot<decltype(s)>::value) {
-            constexpr int S = decltype(s)::value;
-            if constexpr (S == 0) return k0;
-            else if constexpr (S == 1) return k1;
-            else if constexpr (S == 2) return k2;
-            else return k3;
-        } else {
-            const int S = s & 3;
-            return S == 0 ? k0 : S == 1 ? k1 : S == 2 ? k2 : k3;
-        }
-    };
-    auto vslot = [&](auto s) -> uint16_t * {
-        if constexpr (IsSlot<decltype(s)>::value) {
-            constexpr int S = decltype(s)::value;
-            if constexpr (S == 0) return v0;
-            else if constexpr (S == 1) return v1;
-            else if constexpr (S == 2) return v2;
-            else return v3;
-        } else {
-            const int S = s & 3;
-            return S == 0 ? v0 : S == 1 ? v1 : S == 2 ? v2 : v3;
-        }
-    };
-    auto slot_plus = [](auto s, auto k) {
-        if constexpr (IsSlot<decltype(s)>::value)
-            return std::integral_constant<int, (decltype(s)::value + decltype(k)::value) & 3>{};
-        else
-            return (int)((s + decltype(k)::value) & 3);
-    };
-    using one = std::integral_constant<int, 1>;
-    using three = std::integral_constant<int, 3>;
-
-    // ---- rotated Q fragments, held for the whole key range
-    u32x4 qf[NS];
-    int rpos;
-    {
-        const int m = wave * 32 + ln;
-        const int ti = m >> p.gshift;
-        const bool valid = ti < w.n_rows;
-        const int row = w.row0 + (valid ? ti : 0);
-        const int qh = w.kv_head * G + (m & (G - 1));
-        const int rp = valid ? p.row_pos[row] : -1;
-        rpos = rp;
-        const uint16_t *qrow = static_cast<const uint16_t *>(p.q) + ((int64_t)row * p.hq + qh) * D;
-        const float *cs = p.rope + (int64_t)(valid ? rp : 0) * D;
-#pragma unroll
-        for (int s = 0; s < NS / 2; ++s) {
-            const int e0 = 16 * s + 8 * lg;
-            u32x4 lo = {0, 0, 0, 0}, hi = {0, 0, 0, 0};
-            if (valid) {
-                lo = *reinterpret_cast<const u32x4 *>(qrow + e0);
-                hi = *reinterpret_cast<const u32x4 *>(qrow + D / 2 + e0);
+        // slots: compile-time (std::integral_constant) in the unrolled main loop, else run-time
+        auto kslot = [&](auto s) -> uint16_t * {
+            if constexpr (IsSlot<decltype(s)>::value) {
+                constexpr int S = decltype(s)::value;
+                if constexpr (S == 0) return k0;
+                else if constexpr (S == 1) return k1;
+                else if constexpr (S == 2) return k2;
+                else return k3;
+            } else {
+                const int S = s & 3;
+                return S == 0 ? k0 : S == 1 ? k1 : S == 2 ? k2 : k3;
             }
-            floatx4 c[2], sn[2];
-            c[0] = *reinterpret_cast<const floatx4 *>(cs + e0);
-            c[1] = *reinterpret_cast<const floatx4 *>(cs + e0 + 4);
-            sn[0] = *reinterpret_cast<const floatx4 *>(cs + D / 2 + e0);
-            sn[1] = *reinterpret_cast<const floatx4 *>(cs + D / 2 + e0 + 4);
-#pragma unroll
-            for (int h = 0; h < 2; ++h) {
-                c[h] *= p.scale_log2;
-                sn[h] *= p.scale_log2;
+        };
+        auto vslot = [&](auto s) -> uint16_t * {
+            if constexpr (IsSlot<decltype(s)>::value) {
+                constexpr int S = decltype(s)::value;
+                if constexpr (S == 0) return v0;
+                else if constexpr (S == 1) return v1;
+                else if constexpr (S == 2) return v2;
+                else return v3;
+            } else {
+                const int S = s & 3;
+                return S == 0 ? v0 : S == 1 ? v1 : S == 2 ? v2 : v3;
             }
-            rope8_bf16(lo, hi, c, sn, qf[s], qf[s + NS / 2]);
-        }
-    }
-    const int rpos0 = __builtin_amdgcn_readfirstlane(rpos);
-    const int wave_rpos0 = rpos0 < 0 ? INT_MAX : rpos0;
-    int rlast = rpos;
-#pragma unroll
-    for (int o = 32; o > 0; o >>= 1) rlast = max(rlast, __shfl_xor(rlast, o));
-    const int wave_rpos1 = __builtin_amdgcn_readfirstlane(rlast);
+        };
+        auto slot_plus = [](auto s, auto k) {
+            if constexpr (IsSlot<decltype(s)>::value)
+                return std::integral_constant<int, (decltype(s)::value + decltype(k)::value) & 3>{};
+            else
+                return (int)((s + decltype(k)::value) & 3);
+        };
+        using one = std::integral_constant<int, 1>;
+        using three = std::integral_constant<int, 3>;
 
-    // ---- the item's page table in LDS: physical page, and pos0 << 7 | valid
-    const int n_pages = w.page_end - w.page_begin;
-    for (int i = tid; i < n_pages; i += NT) {
-        const PageDesc d = pg[w.page_begin + i];
-        pg_phys[i] = d.phys;
-        pg_pv[i] = (d.pos0 << 7) | d.valid;
-    }
-    barrier_dl();
-
-    // ---- direct loads. Instruction m (0, 1) of wave wv covers key rows 8 wv + 4 m .. + 3 of a tile
-    // (one page: pages hold at least 16 keys); lane i fetches the global chunk that lands at LDS
-    // chunk position i % 16 of row 8 wv + 4 m + i / 16. The page is the load's buffer and the
-    // lane's offset in it (k_doff, v_doff) is the same for every tile: the buffer form took 1.3%
-    // off attention at the 50k-token request against 64-bit addresses per lane.
-    const char *kpool_b = static_cast<const char *>(p.k_rot);
-    const char *vpool_b = static_cast<const char *>(p.v_pool);
-    const uint32_t page_bytes = (uint32_t)p.page_elems * 2u;
-    const int lpage0 = w.page_base + w.page_begin;   // logical page of the item's first page
-    const int pg_in_tile = (8 * wv) >> p.pshift;
-    uint32_t k_doff[2], v_doff[2];
+        // ---- rotated Q fragments, held for the whole key range
+        u32x4 qf[NS];
+        int rpos;
+        {
+            const int m = wave * 32 + ln;
+            const int ti = m >> p.gshift;
+            const bool valid = ti < w.n_rows;
+            const int row = w.row0 + (valid ? ti : 0);
+            const int qh = w.kv_head * G + (m & (G - 1));
+            const int rp = valid ? p.row_pos[row] : -1;
+            rpos = rp;
+            const uint16_t *qrow = static_cast<const uint16_t *>(p.q) + ((int64_t)row * p.hq + qh) * D;
+            const float *cs = p.rope + (int64_t)(valid ? rp : 0) * D;
 #pragma unroll
-    for (int m = 0; m < 2; ++m) {
-        const int r = 8 * wave + 4 * m + (lane >> 4);
-        const int pc = lane & 15;
-        const uint32_t row_off = (uint32_t)(head_off + (int64_t)(r & (page_size - 1)) * D) * 2u;
-        k_doff[m] = row_off + (uint32_t)((pc ^ (r & 15)) * 16);
-        v_doff[m] = row_off + (uint32_t)((pc ^ (4 * (r & 3))) * 16);
-    }
-    // page of this wave's rows of tile t (keys past the item's range read its last page; the mask
-    // removes them)
-    auto tile_page = [&](int t) { return min(t * ppt + pg_in_tile, n_pages - 1); };
-    auto dma_k = [&](int t, uint16_t *dst, int m) __attribute__((always_inline)) {
-        const uint32_t phys = (uint32_t)(lpage0 + tile_page(t));
-        dma16_page(kpool_b + (uint64_t)phys * page_bytes, page_bytes, k_doff[m], lds_addr(dst + (8 * wv + 4 * m) * D));
-    };
-    int v_phys_next = 0;   // V page of the next V tile this wave loads (read from LDS one phase ahead)
-    auto dma_v = [&](uint16_t *dst, int m) __attribute__((always_inline)) {
-        const uint32_t phys = (uint32_t)__builtin_amdgcn_readfirstlane(v_phys_next);
-        dma16_page(vpool_b + (uint64_t)phys * page_bytes, page_bytes, v_doff[m], lds_addr(dst + (8 * wv + 4 * m) * D));
-    };
-    // key positions of tile t into ring slot sl, and the wave's mask bit of the slot
-    unsigned mask_ring = 15u;          // bit sl: the tile in slot sl needs the causal/padding mask
-    auto stage_kpos = [&](int t, int sl) __attribute__((always_inline)) {
-        const int rq = t * ppt + (lane >> p.pshift);
-        const int pv = pg_pv[min(rq, n_pages - 1)];
-        const int slot = lane & (page_size - 1);
-        const int kp = rq < n_pages && slot < (pv & 127) ? (pv >> 7) + slot : kNeverAttended;
-        kpos_s[sl * KT + lane] = kp;   // every wave writes the same 64 values
-        const unsigned bit = 1u << sl;
-        mask_ring = __any(kp > wave_rpos0) ? (mask_ring | bit) : (mask_ring & ~bit);
-    };
-    auto wait_loads = [&](auto n) __attribute__((always_inline)) {
-        // s_waitcnt vmcnt(n): lgkmcnt and expcnt left at their maxima
-        __builtin_amdgcn_s_waitcnt((decltype(n)::value & 15) | ((decltype(n)::value >> 4) << 14) | (7 << 4) |
-                                   (15 << 8));
-    };
-
-    // per-lane LDS fragment offsets (elements) of the swizzled rows. K' k-step s of key row ln reads
-    // chunk (2s + lg) ^ (ln & 15): offset kfo0 ^ 16 s, since the XOR only touches bits 4-6. V^T
-    // d block db of key row 4 lg + jj reads chunk (4 db + 2 (gi & 1) + qq / 2) ^ 4 jj: offset
-    // vfo0 ^ 32 db (bits 5-6). Written as XORs of a per-lane base, they cost one VALU each where the
-    // compiler does not keep them in registers.
-    const uint32_t kfo0 = (uint32_t)(ln * D + 8 * (lg ^ (ln & 1)) + 16 * ((ln & 15) >> 1));
-    auto kfo = [&](int s) { return kfo0 ^ (uint32_t)(16 * s); };
-    const int gi = lane >> 4, jj = (lane >> 2) & 3, qq = lane & 3;
-    const uint32_t vfo0 = (uint32_t)((4 * lg + jj) * D + 32 * jj + 16 * (gi & 1) + 4 * qq);
-    auto vfo = [&](int db) { return vfo0 ^ (uint32_t)(32 * db); };
-
-    auto qk = [&](auto ksl, floatx16 (&sacc)[2]) {
-        const uint16_t *kb = kslot(ksl);
+            for (int s = 0; s < NS / 2; ++s) {
+                const int e0 = 16 * s + 8 * lg;
+                u32x4 lo = {0, 0, 0, 0}, hi = {0, 0, 0, 0};
+                if (valid) {
+                    lo = *reinterpret_cast<const u32x4 *>(qrow + e0);
+                    hi = *reinterpret_cast<const u32x4 *>(qrow + D / 2 + e0);
+                }
+                floatx4 c[2], sn[2];
+                c[0] = *reinterpret_cast<const floatx4 *>(cs + e0);
+                c[1] = *reinterpret_cast<const floatx4 *>(cs + e0 + 4);
+                sn[0] = *reinterpret_cast<const floatx4 *>(cs + D / 2 + e0);
+                sn[1] = *reinterpret_cast<const floatx4 *>(cs + D / 2 + e0 + 4);
 #pragma unroll
-        for (int b = 0; b < 2; ++b)
-#pragma unroll
-            for (int r = 0; r < 16; ++r) sacc[b][r] = 0.0f;
-#pragma unroll
-        for (int s = 0; s < NS; ++s)
-#pragma unroll
-            for (int b = 0; b < 2; ++b) {
-                const bf16x8 a = *reinterpret_cast<const bf16x8 *>(kb + kfo(s) + b * 32 * D);
-                sacc[b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, __builtin_bit_cast(bf16x8, qf[s]), sacc[b],
-                                                                   0, 0, 0);
+                for (int h = 0; h < 2; ++h) {
+                    c[h] *= p.scale_log2;
+                    sn[h] *= p.scale_log2;
+                }
+                rope8_bf16(lo, hi, c, sn, qf[s], qf[s + NS / 2]);
             }
-    };
-
-    floatx16 oacc[NDB];
-#pragma unroll
-    for (int db = 0; db < NDB; ++db)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) oacc[db][r] = 0.0f;
-    float mrow = 0.0f, lrow = 0.0f;
-    bool have_max = false;
-    const bf16x8 bias_a = __builtin_bit_cast(bf16x8, u32x4{lg == 0 ? 0x3f80u : 0u, 0u, 0u, 0u});   // e_0
-    u32x4 bias_b = {0u, 0u, 0u, 0u};
-    floatx16 sacc[2];
-    u32x4 pf[2][2];
-
-    auto tile_sum = [&](const float (&e)[2][16]) -> float {
-        float part[4];
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            part[i] = e[i >> 1][8 * (i & 1)];
-#pragma unroll
-            for (int r = 1; r < 8; ++r) part[i] += e[i >> 1][8 * (i & 1) + r];
         }
-        return (part[0] + part[1]) + (part[2] + part[3]);
-    };
-    auto apply_mask = [&](int sl) __attribute__((always_inline)) {
-        const int *kp = kpos_s + sl * KT;
+        const int rpos0 = __builtin_amdgcn_readfirstlane(rpos);
+        const int wave_rpos0 = rpos0 < 0 ? INT_MAX : rpos0;
+        int rlast = rpos;
+        // the wave's largest row position: XOR swizzles within each half (no lane-address
+        // registers), then the two halves
+        rlast = max(rlast, __builtin_amdgcn_ds_swizzle(rlast, 0x1f | (16 << 10)));
+        rlast = max(rlast, __builtin_amdgcn_ds_swizzle(rlast, 0x1f | (8 << 10)));
+        rlast = max(rlast, __builtin_amdgcn_ds_swizzle(rlast, 0x1f | (4 << 10)));
+        rlast = max(rlast, __builtin_amdgcn_ds_swizzle(rlast, 0x1f | (2 << 10)));
+        rlast = max(rlast, __builtin_amdgcn_ds_swizzle(rlast, 0x1f | (1 << 10)));
+        {
+            const auto sw = __builtin_amdgcn_permlane32_swap(rlast, rlast, false, false);
+            rlast = max((int)sw[0], (int)sw[1]);
+        }
+        const int wave_rpos1 = __builtin_amdgcn_readfirstlane(rlast);
+
+        // ---- the item's page table in LDS: physical page, and pos0 << 7 | valid
+        const int n_pages = w.page_end - w.page_begin;
+        for (int i = tid; i < n_pages; i += NT) {
+            const PageDesc d = pg[w.page_begin + i];
+            pg_phys[i] = d.phys;
+            pg_pv[i] = (d.pos0 << 7) | d.valid;
+        }
+        barrier_dl();
+
+        // ---- direct loads. Instruction m (0, 1) of wave wv covers key rows 8 wv + 4 m .. + 3 of a tile
+        // (one page: pages hold at least 16 keys); lane i fetches the global chunk that lands at LDS
+        // chunk position i % 16 of row 8 wv + 4 m + i / 16. The page is the load's buffer and the
+        // lane's offset in it (k_doff, v_doff) is the same for every tile: the buffer form took 1.3%
+        // off attention at the 50k-token request against 64-bit addresses per lane.
+        const char *kpool_b = static_cast<const char *>(p.k_rot);
+        const char *vpool_b = static_cast<const char *>(p.v_pool);
+        const uint32_t page_bytes = (uint32_t)p.page_elems * 2u;
+        const int lpage0 = w.page_base + w.page_begin;   // logical page of the item's first page
+        const int pg_in_tile = (8 * wv) >> p.pshift;
+        uint32_t k_doff[2], v_doff[2];
 #pragma unroll
-        for (int b = 0; b < 2; ++b)
+        for (int m = 0; m < 2; ++m) {
+            const int r = 8 * wave + 4 * m + (lane >> 4);
+            const int pc = lane & 15;
+            const uint32_t row_off = (uint32_t)(head_off + (int64_t)(r & (page_size - 1)) * D) * 2u;
+            k_doff[m] = row_off + (uint32_t)((pc ^ (r & 15)) * 16);
+            v_doff[m] = row_off + (uint32_t)((pc ^ (4 * (r & 3))) * 16);
+        }
+        // page of this wave's rows of tile t (keys past the item's range read its last page; the mask
+        // removes them)
+        auto tile_page = [&](int t) { return min(t * ppt + pg_in_tile, n_pages - 1); };
+        auto dma_k = [&](int t, uint16_t *dst, int m) __attribute__((always_inline)) {
+            const uint32_t phys = (uint32_t)(lpage0 + tile_page(t));
+            dma16_page(kpool_b + (uint64_t)phys * page_bytes, page_bytes, k_doff[m], lds_addr(dst + (8 * wv + 4 * m) * D));
+        };
+        int v_phys_next = 0;   // V page of the next V tile this wave loads (read from LDS one phase ahead)
+        auto dma_v = [&](uint16_t *dst, int m) __attribute__((always_inline)) {
+            const uint32_t phys = (uint32_t)__builtin_amdgcn_readfirstlane(v_phys_next);
+            dma16_page(vpool_b + (uint64_t)phys * page_bytes, page_bytes, v_doff[m], lds_addr(dst + (8 * wv + 4 * m) * D));
+        };
+        // key positions of tile t into ring slot sl, and the wave's mask bit of the slot
+        unsigned mask_ring = 15u;          // bit sl: the tile in slot sl needs the causal/padding mask
+        auto stage_kpos = [&](int t, int sl) __attribute__((always_inline)) {
+            const int rq = t * ppt + (lane >> p.pshift);
+            const int pv = pg_pv[min(rq, n_pages - 1)];
+            const int slot = lane & (page_size - 1);
+            const int kp = rq < n_pages && slot < (pv & 127) ? (pv >> 7) + slot : kNeverAttended;
+            kpos_s[sl * KT + lane] = kp;   // every wave writes the same 64 values
+            const unsigned bit = 1u << sl;
+            mask_ring = __any(kp > wave_rpos0) ? (mask_ring | bit) : (mask_ring & ~bit);
+        };
+        auto wait_loads = [&](auto n) __attribute__((always_inline)) {
+            // s_waitcnt vmcnt(n): lgkmcnt and expcnt left at their maxima
+            __builtin_amdgcn_s_waitcnt((decltype(n)::value & 15) | ((decltype(n)::value >> 4) << 14) | (7 << 4) |
+                                       (15 << 8));
+        };
+
+        // per-lane LDS fragment offsets (elements) of the swizzled rows. K' k-step s of key row ln reads
+        // chunk (2s + lg) ^ (ln & 15): offset kfo0 ^ 16 s, since the XOR only touches bits 4-6. V^T
+        // d block db of key row 4 lg + jj reads chunk (4 db + 2 (gi & 1) + qq / 2) ^ 4 jj: offset
+        // vfo0 ^ 32 db (bits 5-6). Written as XORs of a per-lane base, they cost one VALU each where the
+        // compiler does not keep them in registers.
+        const uint32_t kfo0 = (uint32_t)(ln * D + 8 * (lg ^ (ln & 1)) + 16 * ((ln & 15) >> 1));
+        auto kfo = [&](int s) { return kfo0 ^ (uint32_t)(16 * s); };
+        const int gi = lane >> 4, jj = (lane >> 2) & 3, qq = lane & 3;
+        const uint32_t vfo0 = (uint32_t)((4 * lg + jj) * D + 32 * jj + 16 * (gi & 1) + 4 * qq);
+        auto vfo = [&](int db) { return vfo0 ^ (uint32_t)(32 * db); };
+
+        auto qk = [&](auto ksl, floatx16 (&sacc)[2]) {
+            const uint16_t *kb = kslot(ksl);
+#pragma unroll
+            for (int b = 0; b < 2; ++b)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) sacc[b][r] = 0.0f;
+#pragma unroll
+            for (int s = 0; s < NS; ++s)
+#pragma unroll
+                for (int b = 0; b < 2; ++b) {
+                    const bf16x8 a = *reinterpret_cast<const bf16x8 *>(kb + kfo(s) + b * 32 * D);
+                    sacc[b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, __builtin_bit_cast(bf16x8, qf[s]), sacc[b],
+                                                                       0, 0, 0);
+                }
+        };
+
+        floatx16 oacc[NDB];
+#pragma unroll
+        for (int db = 0; db < NDB; ++db)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) oacc[db][r] = 0.0f;
+        float mrow = 0.0f, lrow = 0.0f;
+        bool have_max = false;
+        const bf16x8 bias_a = __builtin_bit_cast(bf16x8, u32x4{lg == 0 ? 0x3f80u : 0u, 0u, 0u, 0u});   // e_0
+        u32x4 bias_b = {0u, 0u, 0u, 0u};
+        floatx16 sacc[2];
+        u32x4 pf[2][2];
+
+        auto tile_sum = [&](const float (&e)[2][16]) -> float {
+            float part[4];
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
-                const i32x4 kp4 = *reinterpret_cast<const i32x4 *>(&kp[b * 32 + 8 * i + 4 * lg]);
+                part[i] = e[i >> 1][8 * (i & 1)];
 #pragma unroll
-                for (int j = 0; j < 4; ++j) sacc[b][4 * i + j] = kp4[j] > rpos ? -INFINITY : sacc[b][4 * i + j];
+                for (int r = 1; r < 8; ++r) part[i] += e[i >> 1][8 * (i & 1) + r];
             }
-    };
-    // the softmax of one tile (as link_attention_bf16); `loads(j)` issues load j of a later tile,
-    // spread between the exponentials
-    auto softmax = [&](bool masked, int kc, auto loads) __attribute__((always_inline)) {
-        constexpr int NL = decltype(loads)::count;
-        float e[2][16];
-        float lsum = 0.0f;
-        bool exact = masked;
-        if (!masked) {
-#pragma unroll
-            for (int i = 0; i < 32; ++i) {
-                e[i >> 4][i & 15] = __builtin_amdgcn_exp2f(sacc[i >> 4][i & 15]);
-                if (NL > 0 && (i & 7) == 7 && (i >> 3) < NL) {
-                    loads(i >> 3);
-                    __builtin_amdgcn_sched_barrier(0);
-                }
-            }
-            lsum = tile_sum(e);
-            const bool ok = have_max && lsum <= (float)(1 << (int)kRescaleLog2);   // false for inf, NaN
-            exact = __any(!ok);
-        }
-        if (exact) {
-            if (masked) {
-#pragma unroll
-                for (int j = 0; j < NL; ++j) loads(j);
-                apply_mask(kc);
-            }
-            float mx = sacc[0][0];
+            return (part[0] + part[1]) + (part[2] + part[3]);
+        };
+        auto apply_mask = [&](int sl) __attribute__((always_inline)) {
+            const int *kp = kpos_s + sl * KT;
 #pragma unroll
             for (int b = 0; b < 2; ++b)
 #pragma unroll
-                for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sacc[b][r]);
-            const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(mx), __float_as_uint(mx), false, false);
-            mx = fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1]));
-            float target = mrow;
-            bool first = false;
-            if (mx != -INFINITY) {
-                if (!have_max) {
-                    target = mrow + mx;
-                    first = true;
-                    have_max = true;
-                } else if (mx > 0.0f) {
-                    target = mrow + mx;
+                for (int i = 0; i < 4; ++i) {
+                    const i32x4 kp4 = *reinterpret_cast<const i32x4 *>(&kp[b * 32 + 8 * i + 4 * lg]);
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) sacc[b][4 * i + j] = kp4[j] > rpos ? -INFINITY : sacc[b][4 * i + j];
+                }
+        };
+        // the softmax of one tile (as link_attention_bf16); `loads(j)` issues load j of a later tile,
+        // spread between the exponentials
+        auto softmax = [&](bool masked, int kc, auto loads) __attribute__((always_inline)) {
+            constexpr int NL = decltype(loads)::count;
+            float e[2][16];
+            float lsum = 0.0f;
+            bool exact = masked;
+            if (!masked) {
+#pragma unroll
+                for (int i = 0; i < 32; ++i) {
+                    e[i >> 4][i & 15] = __builtin_amdgcn_exp2f(sacc[i >> 4][i & 15]);
+                    if (NL > 0 && (i & 7) == 7 && (i >> 3) < NL) {
+                        loads(i >> 3);
+                        __builtin_amdgcn_sched_barrier(0);
+                    }
+                }
+                lsum = tile_sum(e);
+                const bool ok = have_max && lsum <= (float)(1 << (int)kRescaleLog2);   // false for inf, NaN
+                exact = __any(!ok);
+            }
+            if (exact) {
+                if (masked) {
+#pragma unroll
+                    for (int j = 0; j < NL; ++j) loads(j);
+                    apply_mask(kc);
+                }
+                float mx = sacc[0][0];
+#pragma unroll
+                for (int b = 0; b < 2; ++b)
+#pragma unroll
+                    for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sacc[b][r]);
+                const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(mx), __float_as_uint(mx), false, false);
+                mx = fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1]));
+                float target = mrow;
+                bool first = false;
+                if (mx != -INFINITY) {
+                    if (!have_max) {
+                        target = mrow + mx;
+                        first = true;
+                        have_max = true;
+                    } else if (mx > 0.0f) {
+                        target = mrow + mx;
+                    }
+                }
+                const uint32_t tb = pack_bf16(-target, 0.0f) & 0xffffu;
+                const float mnew = -bf_lo(tb);
+                const float shift = mnew - mrow;
+                const float alpha = first ? 1.0f : __builtin_amdgcn_exp2f(-shift);
+                mrow = mnew;
+                bias_b[0] = lg == 0 ? tb : 0u;
+#pragma unroll
+                for (int b = 0; b < 2; ++b)
+#pragma unroll
+                    for (int r = 0; r < 16; ++r) e[b][r] = __builtin_amdgcn_exp2f(sacc[b][r] - shift);
+                lsum = tile_sum(e);
+                lrow *= alpha;
+                if (__any(alpha != 1.0f)) {
+#pragma unroll
+                    for (int db = 0; db < NDB; ++db)
+#pragma unroll
+                        for (int r = 0; r < 16; ++r) oacc[db][r] *= alpha;
                 }
             }
-            const uint32_t tb = pack_bf16(-target, 0.0f) & 0xffffu;
-            const float mnew = -bf_lo(tb);
-            const float shift = mnew - mrow;
-            const float alpha = first ? 1.0f : __builtin_amdgcn_exp2f(-shift);
-            mrow = mnew;
-            bias_b[0] = lg == 0 ? tb : 0u;
 #pragma unroll
             for (int b = 0; b < 2; ++b)
 #pragma unroll
-                for (int r = 0; r < 16; ++r) e[b][r] = __builtin_amdgcn_exp2f(sacc[b][r] - shift);
-            lsum = tile_sum(e);
-            lrow *= alpha;
-            if (__any(alpha != 1.0f)) {
+                for (int s2 = 0; s2 < 2; ++s2)
 #pragma unroll
-                for (int db = 0; db < NDB; ++db)
-#pragma unroll
-                    for (int r = 0; r < 16; ++r) oacc[db][r] *= alpha;
-            }
-        }
-#pragma unroll
-        for (int b = 0; b < 2; ++b)
-#pragma unroll
-            for (int s2 = 0; s2 < 2; ++s2)
-#pragma unroll
-                for (int u = 0; u < 4; ++u) pf[b][s2][u] = pack_bf16(e[b][8 * s2 + 2 * u], e[b][8 * s2 + 2 * u + 1]);
-        lrow += lsum;
-    };
-
-    // X phase: PV of the tile in V slot vsl, QK^T of the tile in K' slot ksl, MFMAs and their
-    // operand reads only (operands read three MFMAs ahead), then `vloads` (V of a later tile). The
-    // V loads go last: issued at the start they slowed the operand reads of the same phase.
-    typedef short v4s __attribute__((ext_vector_type(4)));
-    constexpr int NPV = 4 * NDB;
-    constexpr int NQK = 2 * NS;
-    constexpr int NBIAS = 2;
-    constexpr int AHEAD = 3;
-    v4s vlo[NPV], vhi[NPV];
-    bf16x8 ka[NQK];
-    auto xphase = [&](auto vsl, auto ksl, auto with_qk, auto vloads) __attribute__((always_inline)) {
-        constexpr bool QK = decltype(with_qk)::value;
-        constexpr int NM = NPV + (QK ? NBIAS + NQK : 0);
-        const uint16_t *vb = vslot(vsl);
-        const uint16_t *kb = kslot(ksl);
-        auto read = [&](int i) __attribute__((always_inline)) {
-            if (i < NPV) {
-                const int db = i % NDB, b = (i / NDB) >> 1, s2 = (i / NDB) & 1;
-                const uint16_t *a = vb + vfo(db) + (b * 32 + 16 * s2) * D;
-                vlo[i] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) v4s *)a);
-                vhi[i] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) v4s *)(a + 8 * D));
-            } else if (i >= NPV + NBIAS) {
-                const int j = i - NPV - NBIAS, s = j >> 1, b = j & 1;
-                ka[j] = *reinterpret_cast<const bf16x8 *>(kb + kfo(s) + b * 32 * D);
-            }
+                    for (int u = 0; u < 4; ++u) pf[b][s2][u] = pack_bf16(e[b][8 * s2 + 2 * u], e[b][8 * s2 + 2 * u + 1]);
+            lrow += lsum;
         };
-        auto mma = [&](int i) __attribute__((always_inline)) {
-            if (i < NPV) {
-                const int db = i % NDB, b = (i / NDB) >> 1, s2 = (i / NDB) & 1;
-                const bf16x8 a = __builtin_bit_cast(bf16x8, __builtin_shufflevector(vlo[i], vhi[i], 0, 1, 2, 3, 4, 5, 6, 7));
-                oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, __builtin_bit_cast(bf16x8, pf[b][s2]), oacc[db],
-                                                                   0, 0, 0);
-            } else if (i < NPV + NBIAS) {
-                const floatx16 zero = {};
-                sacc[i - NPV] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bias_a, __builtin_bit_cast(bf16x8, bias_b), zero,
-                                                                        0, 0, 0);
-            } else {
-                const int j = i - NPV - NBIAS, s = j >> 1, b = j & 1;
-                sacc[b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[j], __builtin_bit_cast(bf16x8, qf[s]), sacc[b], 0, 0, 0);
-            }
-        };
-        // issue order: the bias MFMAs first, then PV and QK^T alternating, so that each QK^T MFMA
-        // follows the previous one on its accumulator four MFMAs later (two when they ran back to
-        // back): 1.25% shorter at the 50k-token request. Each accumulator keeps its order, so the
-        // results are those of the plain order bit for bit.
-        auto op = [&](int k) -> int {
-            if constexpr (!QK) return k;
-            if (k < NBIAS) return NPV + k;
-            const int r = k - NBIAS;
-            return (r & 1) ? NPV + NBIAS + (r >> 1) : (r >> 1);
-        };
-#pragma unroll
-        for (int k = 0; k < AHEAD; ++k) read(op(k));
-        __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-        for (int k = 0; k < NM; ++k) {
-            mma(op(k));
-            if (k + AHEAD < NM) read(op(k + AHEAD));
-            __builtin_amdgcn_sched_barrier(0);
-        }
-        vloads();
-        __builtin_amdgcn_sched_barrier(0);
-    };
 
-    const int ntiles = (n_pages + ppt - 1) / ppt;
-    const bool group_b = wave >= 4;
-    int n_act;
-    {
-        int lo = 0, hi = n_pages;
-        while (lo < hi) {
-            const int mid = (lo + hi) >> 1;
-            if ((pg_pv[mid] >> 7) <= wave_rpos1) lo = mid + 1;
-            else hi = mid;
-        }
-        n_act = __builtin_amdgcn_readfirstlane((lo + ppt - 1) / ppt);
-    }
-
-    using yes = std::integral_constant<bool, true>;
-    using no = std::integral_constant<bool, false>;
-    using S0 = std::integral_constant<int, 0>;
-    using S1 = std::integral_constant<int, 1>;
-    using S2 = std::integral_constant<int, 2>;
-    using S3 = std::integral_constant<int, 3>;
-    using W6 = std::integral_constant<int, 6>;
-    using W8 = std::integral_constant<int, 8>;
-    using W10 = std::integral_constant<int, 10>;
-    using W0 = std::integral_constant<int, 0>;
-
-    // ---- prologue: tiles 0, 1, 2 (K', V, positions) in slots 0, 1, 2; QK^T of tile 0
-    auto v_page = [&](int t) { return pg_phys[tile_page(t)]; };
-    auto prologue_tile = [&](int t, auto sl) __attribute__((always_inline)) {
-        dma_k(t, kslot(sl), 0);
-        dma_k(t, kslot(sl), 1);
-        v_phys_next = v_page(t);
-        dma_v(vslot(sl), 0);
-        dma_v(vslot(sl), 1);
-        stage_kpos(t, decltype(sl)::value);
-    };
-    prologue_tile(0, S0{});
-    if (ntiles > 1) prologue_tile(1, S1{});
-    if (ntiles > 2) prologue_tile(2, S2{});
-    if (ntiles > 3) v_phys_next = v_page(3);
-    if (ntiles > 2) wait_loads(W10{});
-    else wait_loads(W0{});
-    barrier_dl();
-    qk(S0{}, sacc);
-    if (group_b) {
-        // A's X(0) needs K'(1) and V(0) of every wave
-        if (ntiles > 2) wait_loads(W6{});
-        else wait_loads(W0{});
-        barrier_dl();
-    }
-
-    // one tile. Y(t): softmax of tile t with K'(t+3) loaded between its exponentials, positions of
-    // tile t+3; X(t): PV of tile t, QK^T of tile t+1, V(t+3) loaded. `stage`: tile t+3 exists.
-    auto step = [&](int t, auto sl, auto next_qk, auto stage, auto active) __attribute__((always_inline)) {
-        constexpr bool STAGE = decltype(stage)::value;
-        constexpr bool ACT = decltype(active)::value;
-        const auto sl1 = slot_plus(sl, one{});
-        const auto sl3 = slot_plus(sl, three{});
-        uint16_t *kdst = kslot(sl3);
-        if constexpr (ACT) {
-            const bool masked = (mask_ring >> (int)sl) & 1u;
-            auto kload = [&](int j) __attribute__((always_inline)) {
-                if constexpr (STAGE) dma_k(t + 3, kdst, j);
+        // X phase: PV of the tile in V slot vsl, QK^T of the tile in K' slot ksl, MFMAs and their
+        // operand reads only (operands read three MFMAs ahead), then `vloads` (V of a later tile). The
+        // V loads go last: issued at the start they slowed the operand reads of the same phase.
+        typedef short v4s __attribute__((ext_vector_type(4)));
+        constexpr int NPV = 4 * NDB;
+        constexpr int NQK = 2 * NS;
+        constexpr int NBIAS = 2;
+        constexpr int AHEAD = 3;
+        v4s vlo[NPV], vhi[NPV];
+        bf16x8 ka[NQK];
+        auto xphase = [&](auto vsl, auto ksl, auto with_qk, auto vloads) __attribute__((always_inline)) {
+            constexpr bool QK = decltype(with_qk)::value;
+            constexpr int NM = NPV + (QK ? NBIAS + NQK : 0);
+            const uint16_t *vb = vslot(vsl);
+            const uint16_t *kb = kslot(ksl);
+            auto read = [&](int i) __attribute__((always_inline)) {
+                if (i < NPV) {
+                    const int db = i % NDB, b = (i / NDB) >> 1, s2 = (i / NDB) & 1;
+                    const uint16_t *a = vb + vfo(db) + (b * 32 + 16 * s2) * D;
+                    vlo[i] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) v4s *)a);
+                    vhi[i] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) v4s *)(a + 8 * D));
+                } else if (i >= NPV + NBIAS) {
+                    const int j = i - NPV - NBIAS, s = j >> 1, b = j & 1;
+                    ka[j] = *reinterpret_cast<const bf16x8 *>(kb + kfo(s) + b * 32 * D);
+                }
             };
-            softmax(masked, (int)sl, Loads<STAGE ? 2 : 0, decltype(kload) &>{kload});
-        } else if constexpr (STAGE) {
-            dma_k(t + 3, kdst, 0);
-            dma_k(t + 3, kdst, 1);
-        }
-        if constexpr (STAGE) stage_kpos(t + 3, (int)sl3);
-        __builtin_amdgcn_sched_barrier(0);
-        // group A's X(t) needs K'(t+1) (8 later loads may be in flight); B's X(t) follows this
-        // barrier too and needs the same
-        if constexpr (STAGE) wait_loads(W8{});
-        else wait_loads(W0{});
-        barrier_dl();
-        uint16_t *vdst = vslot(sl3);
-        auto vload = [&]() __attribute__((always_inline)) {
-            if constexpr (STAGE) {
-                dma_v(vdst, 0);
-                dma_v(vdst, 1);
+            auto mma = [&](int i) __attribute__((always_inline)) {
+                if (i < NPV) {
+                    const int db = i % NDB, b = (i / NDB) >> 1, s2 = (i / NDB) & 1;
+                    const bf16x8 a = __builtin_bit_cast(bf16x8, __builtin_shufflevector(vlo[i], vhi[i], 0, 1, 2, 3, 4, 5, 6, 7));
+                    oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, __builtin_bit_cast(bf16x8, pf[b][s2]), oacc[db],
+                                                                       0, 0, 0);
+                } else if (i < NPV + NBIAS) {
+                    const floatx16 zero = {};
+                    sacc[i - NPV] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bias_a, __builtin_bit_cast(bf16x8, bias_b), zero,
+                                                                            0, 0, 0);
+                } else {
+                    const int j = i - NPV - NBIAS, s = j >> 1, b = j & 1;
+                    sacc[b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[j], __builtin_bit_cast(bf16x8, qf[s]), sacc[b], 0, 0, 0);
+                }
+            };
+            // issue order: the bias MFMAs first, then PV and QK^T alternating, so that each QK^T MFMA
+            // follows the previous one on its accumulator four MFMAs later (two when they ran back to
+            // back): 1.25% shorter at the 50k-token request. Each accumulator keeps its order, so the
+            // results are those of the plain order bit for bit.
+            auto op = [&](int k) -> int {
+                if constexpr (!QK) return k;
+                if (k < NBIAS) return NPV + k;
+                const int r = k - NBIAS;
+                return (r & 1) ? NPV + NBIAS + (r >> 1) : (r >> 1);
+            };
+#pragma unroll
+            for (int k = 0; k < AHEAD; ++k) read(op(k));
+            __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+            for (int k = 0; k < NM; ++k) {
+                mma(op(k));
+                if (k + AHEAD < NM) read(op(k + AHEAD));
+                __builtin_amdgcn_sched_barrier(0);
             }
+            vloads();
+            __builtin_amdgcn_sched_barrier(0);
         };
-        if constexpr (ACT) {
-            xphase(sl, sl1, next_qk, vload);
-        } else {
-            vload();
+
+        const int ntiles = (n_pages + ppt - 1) / ppt;
+        const bool group_b = wave >= 4;
+        int n_act;
+        {
+            int lo = 0, hi = n_pages;
+            while (lo < hi) {
+                const int mid = (lo + hi) >> 1;
+                if ((pg_pv[mid] >> 7) <= wave_rpos1) lo = mid + 1;
+                else hi = mid;
+            }
+            n_act = __builtin_amdgcn_readfirstlane((lo + ppt - 1) / ppt);
         }
-        // the V page of the next tile this wave loads, read from LDS ahead of its use
-        if constexpr (STAGE) {
-            if (t + 4 < ntiles) v_phys_next = v_page(t + 4);
-        }
-        __builtin_amdgcn_sched_barrier(0);
-        // the barrier that ends B's X(t) opens A's X(t+1), which needs K'(t+2) (6 later loads may be
-        // in flight); for A this is one phase early
-        if constexpr (STAGE) wait_loads(W6{});
+
+        using yes = std::integral_constant<bool, true>;
+        using no = std::integral_constant<bool, false>;
+        using S0 = std::integral_constant<int, 0>;
+        using S1 = std::integral_constant<int, 1>;
+        using S2 = std::integral_constant<int, 2>;
+        using S3 = std::integral_constant<int, 3>;
+        using W6 = std::integral_constant<int, 6>;
+        using W8 = std::integral_constant<int, 8>;
+        using W10 = std::integral_constant<int, 10>;
+        using W0 = std::integral_constant<int, 0>;
+
+        // ---- prologue: tiles 0, 1, 2 (K', V, positions) in slots 0, 1, 2; QK^T of tile 0
+        auto v_page = [&](int t) { return pg_phys[tile_page(t)]; };
+        auto prologue_tile = [&](int t, auto sl) __attribute__((always_inline)) {
+            dma_k(t, kslot(sl), 0);
+            dma_k(t, kslot(sl), 1);
+            v_phys_next = v_page(t);
+            dma_v(vslot(sl), 0);
+            dma_v(vslot(sl), 1);
+            stage_kpos(t, decltype(sl)::value);
+        };
+        prologue_tile(0, S0{});
+        if (ntiles > 1) prologue_tile(1, S1{});
+        if (ntiles > 2) prologue_tile(2, S2{});
+        if (ntiles > 3) v_phys_next = v_page(3);
+        if (ntiles > 2) wait_loads(W10{});
         else wait_loads(W0{});
         barrier_dl();
-    };
+        qk(S0{}, sacc);
+        if (group_b) {
+            // A's X(0) needs K'(1) and V(0) of every wave
+            if (ntiles > 2) wait_loads(W6{});
+            else wait_loads(W0{});
+            barrier_dl();
+        }
 
-    int t = 0;
-    const int t_main = min(n_act, ntiles - 3);
-    for (; t + 4 <= t_main; t += 4) {
-        step(t, S0{}, yes{}, yes{}, yes{});
-        step(t + 1, S1{}, yes{}, yes{}, yes{});
-        step(t + 2, S2{}, yes{}, yes{}, yes{});
-        step(t + 3, S3{}, yes{}, yes{}, yes{});
-    }
-    if (t < t_main) step(t++, S0{}, yes{}, yes{}, yes{});
-    if (t < t_main) step(t++, S1{}, yes{}, yes{}, yes{});
-    if (t < t_main) step(t++, S2{}, yes{}, yes{}, yes{});
-    // waves past their last key tile keep loading tiles for the others
-    for (; t + 3 < ntiles; ++t) step(t, t & 3, no{}, yes{}, no{});
-    if (t + 2 < ntiles) {
-        if (t < n_act) step(t, t & 3, yes{}, no{}, yes{});
-        else step(t, t & 3, no{}, no{}, no{});
-        ++t;
-    }
-    if (t + 1 < ntiles) {
-        if (t < n_act) step(t, t & 3, yes{}, no{}, yes{});
-        else step(t, t & 3, no{}, no{}, no{});
-        ++t;
-    }
-    if (t < ntiles) {
-        if (t < n_act) step(t, t & 3, no{}, no{}, yes{});
-        else step(t, t & 3, no{}, no{}, no{});
-    }
-    if (!group_b) barrier_dl();
-
-    // ---- epilogue: normalise, write the output (or this split's partial result)
-    {
-        const int m = wave * 32 + ln;
-        const int ti = m >> p.gshift;
-        const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(lrow), __float_as_uint(lrow), false, false);
-        const float lt = __uint_as_float(sw[0]) + __uint_as_float(sw[1]);
-        const float inv = lt > 0.0f ? 1.0f / lt : 0.0f;
-        const float lse_v = lt > 0.0f ? (mrow + __builtin_amdgcn_logf(lt)) * 0.6931471805599453f : -INFINITY;
-        if (ti < w.n_rows) {
-            const int row = w.row0 + ti;
-            const int qh = w.kv_head * G + (m & (G - 1));
-            if (w.partial < 0) {
-                uint16_t *orow = static_cast<uint16_t *>(p.out) + ((int64_t)row * p.hq + qh) * D;
-#pragma unroll
-                for (int db = 0; db < NDB; ++db)
-#pragma unroll
-                    for (int i = 0; i < 4; ++i) {
-                        const int d0 = db * 32 + 8 * i + 4 * lg;
-                        u32x2 v;
-                        v[0] = pack_bf16(oacc[db][4 * i] * inv, oacc[db][4 * i + 1] * inv);
-                        v[1] = pack_bf16(oacc[db][4 * i + 2] * inv, oacc[db][4 * i + 3] * inv);
-                        *reinterpret_cast<u32x2 *>(orow + d0) = v;
-                    }
-                if (p.lse && lg == 0) p.lse[(int64_t)row * p.hq + qh] = lse_v;
+        // one tile. Y(t): softmax of tile t with K'(t+3) loaded between its exponentials, positions of
+        // tile t+3; X(t): PV of tile t, QK^T of tile t+1, V(t+3) loaded. `stage`: tile t+3 exists.
+        auto step = [&](int t, auto sl, auto next_qk, auto stage, auto active) __attribute__((always_inline)) {
+            constexpr bool STAGE = decltype(stage)::value;
+            constexpr bool ACT = decltype(active)::value;
+            const auto sl1 = slot_plus(sl, one{});
+            const auto sl3 = slot_plus(sl, three{});
+            uint16_t *kdst = kslot(sl3);
+            if constexpr (ACT) {
+                const bool masked = (mask_ring >> (int)sl) & 1u;
+                auto kload = [&](int j) __attribute__((always_inline)) {
+                    if constexpr (STAGE) dma_k(t + 3, kdst, j);
+                };
+                softmax(masked, (int)sl, Loads<STAGE ? 2 : 0, decltype(kload) &>{kload});
+            } else if constexpr (STAGE) {
+                dma_k(t + 3, kdst, 0);
+                dma_k(t + 3, kdst, 1);
+            }
+            if constexpr (STAGE) stage_kpos(t + 3, (int)sl3);
+            __builtin_amdgcn_sched_barrier(0);
+            // group A's X(t) needs K'(t+1) (8 later loads may be in flight); B's X(t) follows this
+            // barrier too and needs the same
+            if constexpr (STAGE) wait_loads(W8{});
+            else wait_loads(W0{});
+            barrier_dl();
+            uint16_t *vdst = vslot(sl3);
+            auto vload = [&]() __attribute__((always_inline)) {
+                if constexpr (STAGE) {
+                    dma_v(vdst, 0);
+                    dma_v(vdst, 1);
+                }
+            };
+            if constexpr (ACT) {
+                xphase(sl, sl1, next_qk, vload);
             } else {
-                float *po = p.part_o + ((int64_t)w.partial * TQ + m) * D;
+                vload();
+            }
+            // the V page of the next tile this wave loads, read from LDS ahead of its use
+            if constexpr (STAGE) {
+                if (t + 4 < ntiles) v_phys_next = v_page(t + 4);
+            }
+            __builtin_amdgcn_sched_barrier(0);
+            // the barrier that ends B's X(t) opens A's X(t+1), which needs K'(t+2) (6 later loads may be
+            // in flight); for A this is one phase early
+            if constexpr (STAGE) wait_loads(W6{});
+            else wait_loads(W0{});
+            barrier_dl();
+        };
+
+        int t = 0;
+        const int t_main = min(n_act, ntiles - 3);
+        for (; t + 4 <= t_main; t += 4) {
+            step(t, S0{}, yes{}, yes{}, yes{});
+            step(t + 1, S1{}, yes{}, yes{}, yes{});
+            step(t + 2, S2{}, yes{}, yes{}, yes{});
+            step(t + 3, S3{}, yes{}, yes{}, yes{});
+        }
+        if (t < t_main) step(t++, S0{}, yes{}, yes{}, yes{});
+        if (t < t_main) step(t++, S1{}, yes{}, yes{}, yes{});
+        if (t < t_main) step(t++, S2{}, yes{}, yes{}, yes{});
+        // waves past their last key tile keep loading tiles for the others
+        for (; t + 3 < ntiles; ++t) step(t, t & 3, no{}, yes{}, no{});
+        if (t + 2 < ntiles) {
+            if (t < n_act) step(t, t & 3, yes{}, no{}, yes{});
+            else step(t, t & 3, no{}, no{}, no{});
+            ++t;
+        }
+        if (t + 1 < ntiles) {
+            if (t < n_act) step(t, t & 3, yes{}, no{}, yes{});
+            else step(t, t & 3, no{}, no{}, no{});
+            ++t;
+        }
+        if (t < ntiles) {
+            if (t < n_act) step(t, t & 3, no{}, no{}, yes{});
+            else step(t, t & 3, no{}, no{}, no{});
+        }
+        if (!group_b) barrier_dl();
+
+        // ---- epilogue: normalise, write the output (or this split's partial result)
+        {
+            const int m = wave * 32 + ln;
+            const int ti = m >> p.gshift;
+            const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(lrow), __float_as_uint(lrow), false, false);
+            const float lt = __uint_as_float(sw[0]) + __uint_as_float(sw[1]);
+            const float inv = lt > 0.0f ? 1.0f / lt : 0.0f;
+            const float lse_v = lt > 0.0f ? (mrow + __builtin_amdgcn_logf(lt)) * 0.6931471805599453f : -INFINITY;
+            if (ti < w.n_rows) {
+                const int row = w.row0 + ti;
+                const int qh = w.kv_head * G + (m & (G - 1));
+                if (w.partial < 0) {
+                    uint16_t *orow = static_cast<uint16_t *>(p.out) + ((int64_t)row * p.hq + qh) * D;
 #pragma unroll
-                for (int db = 0; db < NDB; ++db)
+                    for (int db = 0; db < NDB; ++db)
 #pragma unroll
-                    for (int i = 0; i < 4; ++i) {
-                        const int d0 = db * 32 + 8 * i + 4 * lg;
-                        floatx4 v = {oacc[db][4 * i] * inv, oacc[db][4 * i + 1] * inv, oacc[db][4 * i + 2] * inv,
-                                     oacc[db][4 * i + 3] * inv};
-                        *reinterpret_cast<floatx4 *>(po + d0) = v;
-                    }
-                if (lg == 0) p.part_lse[(int64_t)w.partial * TQ + m] = lse_v;
+                        for (int i = 0; i < 4; ++i) {
+                            const int d0 = db * 32 + 8 * i + 4 * lg;
+                            u32x2 v;
+                            v[0] = pack_bf16(oacc[db][4 * i] * inv, oacc[db][4 * i + 1] * inv);
+                            v[1] = pack_bf16(oacc[db][4 * i + 2] * inv, oacc[db][4 * i + 3] * inv);
+                            *reinterpret_cast<u32x2 *>(orow + d0) = v;
+                        }
+                    if (p.lse && lg == 0) p.lse[(int64_t)row * p.hq + qh] = lse_v;
+                } else {
+                    float *po = p.part_o + ((int64_t)w.partial * TQ + m) * D;
+#pragma unroll
+                    for (int db = 0; db < NDB; ++db)
+#pragma unroll
+                        for (int i = 0; i < 4; ++i) {
+                            const int d0 = db * 32 + 8 * i + 4 * lg;
+                            floatx4 v = {oacc[db][4 * i] * inv, oacc[db][4 * i + 1] * inv, oacc[db][4 * i + 2] * inv,
+                                         oacc[db][4 * i + 3] * inv};
+                            *reinterpret_cast<floatx4 *>(po + d0) = v;
+                        }
+                    if (lg == 0) p.part_lse[(int64_t)w.partial * TQ + m] = lse_v;
+                }
             }
         }
     }
+    if (threadIdx.x == 0) release_work_queues(p);
 }
 
 // ---------------------------------------------------------------------------------------------
@@ -2367,6 +2468,10 @@ hipError_t launch_attention(const LayerShape &s, const void *q, const void *k_po
     p.pages = t.pages;
     p.row_pos = t.row_pos;
     p.work = t.work;
+    p.ticket = t.ticket;
+    p.n_work = t.n_work;
+    p.n_queues = t.n_queues;
+    p.persistent = t.n_groups < t.n_work;
     p.out = out;
     p.lse = lse;
     p.part_o = t.part_o;
@@ -2380,16 +2485,17 @@ hipError_t launch_attention(const LayerShape &s, const void *q, const void *k_po
     p.scale_log2 = 1.4426950408889634f / sqrtf((float)s.d);
     p.seg_keys = s.key_layout;
     dim3 grid(t.n_work);
+    const dim3 groups(t.n_groups);   // the bf16 kernels: persistent when there are fewer groups than items
     if (s.dtype == 0) {
         if (t.k_rot) {
-            if (s.d == 128) hipLaunchKernelGGL(link_attention_bf16_dl<128>, grid, dim3(512), 0, stream, p);
-            else hipLaunchKernelGGL((link_attention_bf16<64, true, false>), grid, dim3(512), 0, stream, p);
+            if (s.d == 128) hipLaunchKernelGGL(link_attention_bf16_dl<128>, groups, dim3(512), 0, stream, p);
+            else hipLaunchKernelGGL((link_attention_bf16<64, true, false>), groups, dim3(512), 0, stream, p);
         } else if (s.key_layout) {
-            if (s.d == 128) hipLaunchKernelGGL((link_attention_bf16<128, false, true>), grid, dim3(512), 0, stream, p);
-            else hipLaunchKernelGGL((link_attention_bf16<64, false, true>), grid, dim3(512), 0, stream, p);
+            if (s.d == 128) hipLaunchKernelGGL((link_attention_bf16<128, false, true>), groups, dim3(512), 0, stream, p);
+            else hipLaunchKernelGGL((link_attention_bf16<64, false, true>), groups, dim3(512), 0, stream, p);
         } else {
-            if (s.d == 128) hipLaunchKernelGGL((link_attention_bf16<128, false, false>), grid, dim3(512), 0, stream, p);
-            else hipLaunchKernelGGL((link_attention_bf16<64, false, false>), grid, dim3(512), 0, stream, p);
+            if (s.d == 128) hipLaunchKernelGGL((link_attention_bf16<128, false, false>), groups, dim3(512), 0, stream, p);
+            else hipLaunchKernelGGL((link_attention_bf16<64, false, false>), groups, dim3(512), 0, stream, p);
         }
     } else {
         if (s.d == 128) hipLaunchKernelGGL(link_attention_f32<128>, grid, dim3(kThreads), 0, stream, p);

@@ -43,6 +43,9 @@ struct AttnTables {
     const int32_t *row_pos;
     const WorkDesc *work;
     int n_work;
+    uint32_t *ticket;              // kMaxWorkQueues + 1 work counters (zero between launches)
+    int n_queues;                  // queues of the work list (its items interleaved)
+    int n_groups;                  // work groups of a persistent attention launch
     const MergeDesc *merge;
     int n_merge;
     float *part_o;

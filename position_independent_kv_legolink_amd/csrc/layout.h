@@ -92,6 +92,7 @@ struct DecodeMergeDesc {
 };
 
 constexpr int kKeysPerTile = 64;   // keys staged in LDS per attention iteration
+constexpr int kMaxWorkQueues = 8;    // queues of an attention work list (one per XCD)
 constexpr int kMaxItemPages = 2048;  // longest KV range of one attention work item (its page table sits in LDS)
 constexpr int kMaxDecodePages = 1024;  // longest KV range of one decode work item (its page table sits in LDS)
 constexpr int kDecodeMinPages = 96;    // decode ranges shorter than this give way to one range per compute unit

@@ -229,10 +229,12 @@ pic_plan *build_plan(pic_store *s, const pic_request *reqs, int32_t n_reqs, cons
         plan->n_split_items += used;
     }
     std::stable_sort(split.begin(), split.end(), [](const Item &a, const Item &b) { return a.len > b.len; });
-    constexpr int kXcds = 8;
+    constexpr int kXcds = kMaxWorkQueues;
     if (cfg.num_kv_heads % kXcds == 0) {
         // work groups are dispatched round-robin over the XCDs: slot i runs on XCD i % 8, so
-        // bucket the items by KV head and interleave the buckets
+        // bucket the items by KV head and interleave the buckets. The persistent kernel takes the
+        // buckets as queues, work group i from queue i % 8 first.
+        plan->work_queues = kXcds;
         std::vector<std::vector<WorkDesc>> bucket(kXcds);
         for (const Item &it : split) bucket[it.w.kv_head % kXcds].push_back(it.w);
         size_t depth = 0;
@@ -318,6 +320,9 @@ pic_plan *build_plan(pic_store *s, const pic_request *reqs, int32_t n_reqs, cons
     plan->off_scatter = place((int64_t)plan->scatter.size() * sizeof(ScatterDesc));
     plan->off_work = place((int64_t)plan->work.size() * sizeof(WorkDesc));
     plan->off_merge = place((int64_t)plan->merge.size() * sizeof(MergeDesc));
+    // the attention launch's work counters: zero in the uploaded tables, and back to zero at the
+    // end of every launch
+    plan->off_ticket = place((kMaxWorkQueues + 1) * sizeof(uint32_t));
     plan->off_dec_work = place((int64_t)plan->dec_work.size() * sizeof(DecodeDesc));
     plan->off_dec_merge = place((int64_t)plan->dec_merge.size() * sizeof(DecodeMergeDesc));
     plan->table_bytes = off;

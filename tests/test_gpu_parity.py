@@ -82,7 +82,7 @@ def run_workload(cfg, *, n_requests=None, sample_rows=None, pos_offset=0, split_
     want = (oracle_outputs(segs, cached, rows, cfg.rope_theta, sample=sample, key_layout=key_layout,
                            compile_offset=compile_offset) if with_oracle else None)
     extras = dict(store=store, plan=plan, export=ex, segs=segs, cached=cached, rows=rows, sample=sample,
-                  lse=got_lse, outs=outs)
+                  lse=got_lse, outs=outs, link_requests=wl.link_requests())
     return outs[0], want, extras
 
 
