@@ -3,8 +3,9 @@
 pic_link_attend_static runs the same kernels on the library's static device scratch (64 MiB per
 GPU) instead of a caller workspace, so its outputs and log-sum-exps must equal pic_link_attend's
 bit for bit. Two calls run back to back on one stream, the second with a smaller request, then
-the first again; each is also checked against the fp64 oracle. A plan whose workspace exceeds the
-scratch is refused before any copy or launch.
+the first again; each is also checked against the fp64 oracle. A plan with more work items than
+compute units (persistent attention, its work counters in the scratch) repeats exactly over three
+calls. A plan whose workspace exceeds the scratch is refused before any copy or launch.
 """
 from __future__ import annotations
 
@@ -36,7 +37,7 @@ def _need_gpu():
     pic.lib()
 
 
-def _job(cfg, rope_keys):
+def _job(cfg, rope_keys, split_pages=0):
     wl = Workload(cfg)
     segs = wl.segments()
     cached = wl.cached()
@@ -45,7 +46,8 @@ def _job(cfg, rope_keys):
     stored = sum(-(-v[0].shape[0] // B) for v in cached.values())
     n_tokens = max(oplan.total_tokens(s) for s in segs)
     store = gpu_store(cfg, cached, num_pages=stored + private + 8, max_position=n_tokens + 1)
-    plan = store.link_plan(wl.link_requests(), k=cfg.k, block_level=cfg.block_level, rope_keys=rope_keys)
+    plan = store.link_plan(wl.link_requests(), k=cfg.k, block_level=cfg.block_level, rope_keys=rope_keys,
+                           split_pages=split_pages)
     rows = wl.new_rows(segs)
     tdt = torch.bfloat16 if cfg.dtype == "bf16" else torch.float32
     q, kn, vn = (torch.from_numpy(np.concatenate([r[i] for r in rows])).to("cuda", tdt).contiguous() for i in range(3))
@@ -84,6 +86,42 @@ def test_static_scratch_reproduces_link_attend_on_consecutive_calls():
         outs[i][1].fill_(float("nan"))
     for j in jobs:
         j["plan"].free()
+
+
+@pytest.mark.parametrize("rope_keys", [1, 2])
+def test_static_scratch_runs_persistent_launches(rope_keys):
+    """A plan with more work items than compute units (4-page pieces: 360 of them) runs its
+    attention on persistent work groups whose work counters sit in the static scratch. Three
+    static calls, with a call on the plan's own workspace between the second and the third,
+    all equal pic_link_attend bit for bit."""
+    cfg = small_cfg(num_q_heads=4, num_kv_heads=2, chunk_len=300, chunks_per_request=6, k=20, n_requests=3)
+    j = _job(cfg, rope_keys, split_pages=4)
+    sz = j["plan"].sizes
+    assert sz["work_items"] > torch.cuda.get_device_properties(0).multi_processor_count
+    assert sz["workspace_bytes"] <= pic.STATIC_SCRATCH_BYTES
+    R = j["plan"].rows
+    lse = torch.empty((R, cfg.num_q_heads), dtype=torch.float32, device="cuda")
+    ref = pic.link_attend(j["store"], j["plan"], j["q"], j["k"], j["v"], lse=lse)
+    torch.cuda.synchronize()
+    ref, ref_lse = ref.float().cpu().numpy(), lse.cpu().numpy()
+    out = torch.empty((R, cfg.num_q_heads, cfg.head_dim), dtype=j["q"].dtype, device="cuda")
+    out_lse = torch.empty((R, cfg.num_q_heads), dtype=torch.float32, device="cuda")
+    for call in range(3):
+        _say(f"static scratch, persistent launch {call} (rope_keys {rope_keys}, {sz['work_items']} items)")
+        if call == 2:
+            pic.link_attend(j["store"], j["plan"], j["q"], j["k"], j["v"])
+        out.fill_(float("nan"))
+        out_lse.fill_(float("nan"))
+        pic.link_attend_static(j["store"], j["plan"], j["q"], j["k"], j["v"], out=out, lse=out_lse)
+        torch.cuda.synchronize()
+        assert np.array_equal(out.float().cpu().numpy(), ref), f"call {call}: outputs differ"
+        assert np.array_equal(out_lse.cpu().numpy(), ref_lse), f"call {call}: lse differs"
+    want = oracle_outputs(j["segs"], j["cached"], j["rows"], cfg.rope_theta)
+    got = out.float().cpu().numpy()
+    for i, (wo, _) in enumerate(want):
+        r0 = j["plan"].export()["cu_rows"][i]
+        check_rows(got[r0:r0 + wo.shape[0]], wo, cfg.dtype, f"static scratch, persistent, request {i}")
+    j["plan"].free()
 
 
 def test_static_scratch_refuses_a_plan_larger_than_the_scratch():
