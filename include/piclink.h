@@ -319,7 +319,9 @@ pic_status pic_plan_upload(pic_store *store, pic_plan *plan, void *workspace, in
  * small, misaligned), PIC_ERR_INVALID (null row tensor with rows > 0),
  * PIC_ERR_STATE (metadata-only store), PIC_ERR_DEVICE (launch failure).
  * Asynchronous; no kernel is launched when an error is returned before the
- * first launch. */
+ * first launch. The workspace also holds the split partials and the attention
+ * launch's work counters (zero between calls): link calls on one workspace
+ * whose device work overlaps (other streams) race. */
 pic_status pic_link_attend(pic_store *store, const pic_plan *plan, const void *q_new, const void *k_new,
                            const void *v_new, void *out, float *lse, void *workspace, int64_t workspace_bytes,
                            hipStream_t stream);
