@@ -66,7 +66,11 @@ def run_workload(cfg, *, n_requests=None, sample_rows=None, pos_offset=0, split_
     outs = []
     lse_t = torch.empty((plan.rows, cfg.num_q_heads), dtype=torch.float32, device="cuda") if lse else None
     for _ in range(repeat):
-        out = pic.link_attend(store, plan, q, kn, vn, lse=lse_t)
+        # every launch writes into NaN: an item a launch skipped would show
+        out = torch.full((plan.rows, cfg.num_q_heads, cfg.head_dim), float("nan"), dtype=tdt, device="cuda")
+        if lse_t is not None:
+            lse_t.fill_(float("nan"))
+        out = pic.link_attend(store, plan, q, kn, vn, out=out, lse=lse_t)
         torch.cuda.synchronize()
         outs.append(out.float().cpu().numpy())
     got_lse = lse_t.cpu().numpy() if lse else None
