@@ -7,8 +7,10 @@ ahead of attention), attention, and split merge. The default workload is the
 suffix, LegoLink-32, Llama-3-8B layer shape, bf16). Its chunk KV and new rows
 are seeded synthetic data, resident in HBM before timing starts.
 
-Output: one JSON line with the step throughput (algorithmic TFLOP/s), the
-attention kernel's roofline position (timed live with HIP events on the
+Output: one JSON line with the step throughput (algorithmic TFLOP/s; steps
+back to back as a serving loop runs them, each step's table upload on a copy
+stream into the other of two workspaces, overlapping the previous step's
+kernels), the attention kernel's roofline position (timed live with HIP events on the
 stream it runs on), the link latency (each step alone between
 synchronisations: 10th, 50th and 90th percentile), the same step with the
 256 MiB MALL evicted before each step ("cold"), decode after link, the dense
@@ -145,6 +147,34 @@ class LinkJob:
         self.pic.link_attend(self.store, plan, self.q, self.k, self.v, out=self.out)
         plan.free()
 
+    def step_pipelined(self):
+        """One step as a serving loop runs them back to back: the same planning, upload and link
+        call, with the upload on a copy stream into the other of two workspaces, so that the
+        table copy overlaps the previous step's kernels instead of standing between them (the
+        upload still waits for the step that last used that workspace, and the link call for
+        the upload)."""
+        torch = self.torch
+        if not hasattr(self, "_pipe"):
+            self._pipe = dict(ws=[self.workspace, torch.empty_like(self.workspace)], copy=torch.cuda.Stream(),
+                              done=[None, None], k=0)
+        pp = self._pipe
+        k = pp["k"]
+        pp["k"] ^= 1
+        plan = self.store.link_plan(self.requests, **self.plan_kw)
+        compute = torch.cuda.current_stream()
+        with torch.cuda.stream(pp["copy"]):
+            if pp["done"][k] is not None:
+                pp["copy"].wait_event(pp["done"][k])
+            plan.upload(pp["ws"][k])
+            uploaded = torch.cuda.Event()
+            uploaded.record(pp["copy"])
+        compute.wait_event(uploaded)
+        self.pic.link_attend(self.store, plan, self.q, self.k, self.v, out=self.out)
+        done = torch.cuda.Event()
+        done.record(compute)
+        pp["done"][k] = done
+        plan.free()
+
 
 class NoGC:
     """Python's cyclic collector is off inside timed regions: one full collection over the
@@ -161,16 +191,18 @@ class NoGC:
 
 
 def time_steps(job, steps, warmup):
+    """Throughput: steps back to back, each table upload overlapping the previous step's kernels
+    (LinkJob.step_pipelined). Returns ms per step and the per-kernel profile."""
     torch = job.torch
     for _ in range(warmup):
-        job.step()
+        job.step_pipelined()
     torch.cuda.synchronize()
     job.store.profile_enable(True)
     torch.cuda.synchronize()
     with NoGC():
         t0 = time.perf_counter()
         for _ in range(steps):
-            job.step()
+            job.step_pipelined()
         torch.cuda.synchronize()
         t1 = time.perf_counter()
     prof = job.store.profile_read()
@@ -186,7 +218,7 @@ def time_steps_no_events(job, steps):
     with NoGC():
         t0 = time.perf_counter()
         for _ in range(steps):
-            job.step()
+            job.step_pipelined()
         torch.cuda.synchronize()
         return (time.perf_counter() - t0) * 1e3 / steps
 
@@ -651,8 +683,10 @@ def main():
         copy_src = torch.ones(args.copy_probe_mib << 18, dtype=torch.float32, device="cuda")
         copy_dst = torch.empty_like(copy_src)
 
-    ms_step, prof = time_steps(job, args.steps, args.warmup)
-    ms_step_bare = time_steps_no_events(job, args.steps)
+    # the kernel durations come from a run with the library's per-kernel events; the step time from
+    # the same steps without them (each event pair costs the GPU a few microseconds)
+    ms_step_events, prof = time_steps(job, args.steps, args.warmup)
+    ms_step = time_steps_no_events(job, args.steps)
     lat = time_steps_latency(job, args.steps)
     latency = dict(steps=len(lat), **percentiles(lat))
     if copy_src is not None:
@@ -725,7 +759,9 @@ def main():
         "steps": args.steps,
         "warmup": args.warmup,
         "ms_per_step": round(ms_step, 4),
-        "ms_per_step_without_kernel_events": round(ms_step_bare, 4),
+        "ms_per_step_with_kernel_events": round(ms_step_events, 4),
+        "step_pipeline": "table upload on a copy stream into the other of two workspaces, overlapping the "
+                         "previous step's kernels; link_latency_wall_ms times steps alone",
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
