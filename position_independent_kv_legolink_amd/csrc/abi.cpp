@@ -79,6 +79,7 @@ void pack_tables(const pic_plan &plan, uint8_t *blob) {
         if (bytes) memcpy(blob + off, src, bytes);
     };
     put(plan.off_pages, plan.pages.data(), plan.pages.size() * sizeof(PageDesc));
+    put(plan.off_page_scatter, plan.page_scatter.data(), plan.page_scatter.size() * sizeof(int32_t));
     put(plan.off_row_pos, plan.row_pos.data(), plan.row_pos.size() * sizeof(int32_t));
     put(plan.off_scatter, plan.scatter.data(), plan.scatter.size() * sizeof(ScatterDesc));
     put(plan.off_work, plan.work.data(), plan.work.size() * sizeof(WorkDesc));
@@ -162,15 +163,22 @@ void launch_link(pic_store *s, const pic_plan *plan, int layer, const void *q_ne
         }
         check_hip(hipEventRecord(marks.ev[0], stream), "hipEventRecord");
     }
-    check_hip(launch_scatter(s->shape, k_pool, v_pool, k_new, v_new, s->rope,
-                             reinterpret_cast<const ScatterDesc *>(ws + plan->off_scatter), (int)plan->scatter.size(),
-                             stream),
-              "scatter launch");
-    if (prof) check_hip(hipEventRecord(marks.ev[1], stream), "hipEventRecord");
-    if (plan->rotate_keys)
-        check_hip(launch_rotate_keys(s->shape, k_pool, s->rope, t.pages, (int)plan->pages.size(),
-                                     const_cast<void *>(t.k_rot), stream),
-                  "key rotation launch");
+    const auto *table = reinterpret_cast<const ScatterDesc *>(ws + plan->off_scatter);
+    if (plan->rotate_keys) {
+        // the scatter runs inside the key rotation's launch: the profile's scatter interval is
+        // empty and its rotation interval holds both
+        if (prof) check_hip(hipEventRecord(marks.ev[1], stream), "hipEventRecord");
+        check_hip(launch_prepare(s->shape, k_pool, v_pool, k_new, v_new, s->rope, t.pages,
+                                 reinterpret_cast<const int32_t *>(ws + plan->off_page_scatter),
+                                 (int)plan->pages.size(), table, (int)plan->scatter.size(),
+                                 const_cast<void *>(t.k_rot), stream),
+                  "scatter and key rotation launch");
+    } else {
+        check_hip(launch_scatter(s->shape, k_pool, v_pool, k_new, v_new, s->rope, table, (int)plan->scatter.size(),
+                                 stream),
+                  "scatter launch");
+        if (prof) check_hip(hipEventRecord(marks.ev[1], stream), "hipEventRecord");
+    }
     if (prof) check_hip(hipEventRecord(marks.ev[2], stream), "hipEventRecord");
     check_hip(launch_attention(s->shape, q_new, k_pool, v_pool, s->rope, t, out, lse, stream),
               "attention launch");
@@ -505,6 +513,7 @@ pic_status pic_link_attend_static(pic_store *s, const pic_plan *plan, const void
                 check_hip(hipMemcpyAsync(ws + off, src, bytes, hipMemcpyHostToDevice, stream), "plan table copy");
         };
         put(plan->off_pages, plan->pages.data(), plan->pages.size() * sizeof(PageDesc));
+        put(plan->off_page_scatter, plan->page_scatter.data(), plan->page_scatter.size() * sizeof(int32_t));
         put(plan->off_row_pos, plan->row_pos.data(), plan->row_pos.size() * sizeof(int32_t));
         put(plan->off_scatter, plan->scatter.data(), plan->scatter.size() * sizeof(ScatterDesc));
         put(plan->off_work, plan->work.data(), plan->work.size() * sizeof(WorkDesc));

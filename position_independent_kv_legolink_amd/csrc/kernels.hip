@@ -1816,12 +1816,10 @@ __global__ __launch_bounds__(kThreads) void store_fill(FillPages pages, uint8_t 
 // In a store of keys rotated at their position inside their segment (rotate_new), a new row's
 // key is written in that form: rotated at slot position local0 + slot, with the table values and
 // the fp32 arithmetic of the attention kernels' key rotation. Cached rows are copied as stored.
-__global__ __launch_bounds__(kThreads) void link_scatter(const ScatterDesc *table, uint8_t *k_pool, uint8_t *v_pool,
-                                                         const uint8_t *k_new, const uint8_t *v_new, const float *rope,
-                                                         int rotate_new, int elem, int hkv, int page_size,
-                                                         int row_bytes, int64_t page_bytes) {
-    const ScatterDesc sd = table[blockIdx.x];
-    const int h = blockIdx.y;
+__device__ __forceinline__ void scatter_page_head(const ScatterDesc &sd, int h, uint8_t *k_pool, uint8_t *v_pool,
+                                                  const uint8_t *k_new, const uint8_t *v_new, const float *rope,
+                                                  int rotate_new, int elem, int hkv, int page_size, int row_bytes,
+                                                  int64_t page_bytes) {
     const int pieces_per_row = row_bytes / 16;
     const int64_t head_bytes = (int64_t)h * page_size * row_bytes;
     const int64_t dst0 = (int64_t)sd.dst * page_bytes + head_bytes;
@@ -1881,36 +1879,77 @@ __global__ __launch_bounds__(kThreads) void link_scatter(const ScatterDesc *tabl
     }
 }
 
-// Keys of every logical page of a plan rotated once to the page's absolute positions, with the
+__global__ __launch_bounds__(kThreads) void link_scatter(const ScatterDesc *table, uint8_t *k_pool, uint8_t *v_pool,
+                                                         const uint8_t *k_new, const uint8_t *v_new, const float *rope,
+                                                         int rotate_new, int elem, int hkv, int page_size,
+                                                         int row_bytes, int64_t page_bytes) {
+    scatter_page_head(table[blockIdx.x], blockIdx.y, k_pool, v_pool, k_new, v_new, rope, rotate_new, elem, hkv,
+                      page_size, row_bytes, page_bytes);
+}
+
+// The copy-on-write scatter and the key rotation of a plan in one launch (bfloat16 stores whose
+// plan rotates its keys ahead of attention). Work groups [0, n_pages) rotate the keys of one
+// logical page each; the rest run the scatter, one (private page, KV head) each. The two roles
+// touch different memory: a private page's rotation reads the keys the scatter writes into that
+// page from where the scatter takes them (the new rows, the copy-on-write source page, zeros),
+// so the scatter's small, latency-bound work runs beside the rotation's streaming.
+//   Rotation: the keys of a logical page turned once to the page's absolute positions, with the
 // attention kernel's table values and arithmetic, into the pool's page layout indexed by logical
 // page ([page][Hkv][page_size][d]); padding slots are written as zeros (the pools hold zeros
 // there, which rotate to zeros). A position-free key is rotated by its position; a key stored
-// rotated at its position inside its segment (seg_keys) by the segment's start. One work group
-// per logical page. A thread takes 8 (x_i, x_{i+d/2}) pairs of one slot, loads their cos/sin
-// once, and rotates them in every head of its head group (heads hg, hg + n_hg, ...), loading
-// up to HB heads' keys before the first store; consecutive threads take consecutive pairs of a
-// row, so every key row is read and written in whole 128-byte runs.
-template <int D>
-__global__ __launch_bounds__(kThreads) void rotate_keys_bf16(const PageDesc *pages, const uint8_t *__restrict__ k_pool,
-                                                             const float *__restrict__ rope, uint8_t *__restrict__ k_rot,
-                                                             int hkv, int pshift, int64_t page_bytes, int seg_keys) {
+// rotated at its position inside its segment (SEG) by the segment's start (a new row's key
+// first takes the form the scatter stores: rotated at its position inside its segment). A
+// thread takes 8 (x_i, x_{i+d/2}) pairs of one slot, loads their cos/sin once, and rotates them
+// in every head of its head group (heads hg, hg + n_hg, ...), loading up to HB heads' keys
+// before the first store; consecutive threads take consecutive pairs of a row, so every key row
+// is read and written in whole 128-byte runs.
+struct PrepareParams {
+    const PageDesc *pages;
+    const int32_t *page_scatter;   // per logical page: its scatter entry, or -1 for a shared page
+    const ScatterDesc *scatter;
+    uint8_t *k_pool;
+    uint8_t *v_pool;
+    const uint8_t *k_new;
+    const uint8_t *v_new;
+    const float *rope;
+    uint8_t *k_rot;
+    int n_pages, hkv, pshift;
+    int64_t page_bytes;
+};
+
+// Five waves per SIMD for position-free keys (84 VGPRs), as the rotation pass had on its own;
+// keys rotated inside their segment need the second cos/sin row of a new key and keep four.
+template <int D, bool SEG>
+__global__ __launch_bounds__(kThreads, SEG ? 4 : 5) void link_prepare_bf16(PrepareParams p) {
     constexpr int PPR = D / 16;   // pieces of 8 pairs per row
     constexpr int HB = 4;         // heads loaded ahead of their stores
-    const PageDesc pd = pages[blockIdx.x];
-    const int page_size = 1 << pshift;
+    const int page_size = 1 << p.pshift;
+    if ((int)blockIdx.x >= p.n_pages) {
+        const int b = blockIdx.x - p.n_pages;
+        scatter_page_head(p.scatter[b / p.hkv], b % p.hkv, p.k_pool, p.v_pool, p.k_new, p.v_new, p.rope,
+                          SEG, 2, p.hkv, page_size, D * 2, p.page_bytes);
+        return;
+    }
+    const PageDesc pd = p.pages[blockIdx.x];
+    const int si = p.page_scatter[blockIdx.x];
+    const ScatterDesc sd = si >= 0 ? p.scatter[si] : ScatterDesc{pd.phys, -1, 0, 0, pd.valid, 0, 0, 0};
     const int items = page_size * PPR;                           // (slot, piece) of one head
-    const int n_hg = max(1, min(hkv, kThreads / items));         // head groups side by side
-    const uint8_t *src = k_pool + (int64_t)pd.phys * page_bytes;
-    uint8_t *dst = k_rot + (int64_t)blockIdx.x * page_bytes;
+    const int n_hg = max(1, min(p.hkv, kThreads / items));       // head groups side by side
+    // the page's keys as the pool holds them once the scatter has run: a shared page's own, or a
+    // private page's new rows, copy-on-write source rows and zeros
+    const uint8_t *page_src = p.k_pool + (int64_t)(si >= 0 ? max(sd.src, 0) : pd.phys) * p.page_bytes;
+    uint8_t *dst = p.k_rot + (int64_t)blockIdx.x * p.page_bytes;
     for (int i = threadIdx.x; i < items * n_hg; i += kThreads) {
         const int c = i % PPR, slot = (i / PPR) & (page_size - 1), hg = i / items;
         const bool valid = slot < pd.valid;
-        floatx4 co[2] = {}, sn[2] = {};
+        const bool is_new = slot < sd.n_new;                      // a new row (private pages only)
+        const bool from_page = !is_new && slot < sd.n_valid;      // the page's or the source page's row
+        floatx4 co[2] = {}, sn[2] = {}, cl[2] = {}, sl[2] = {};
         if (valid) {
             // a negative rotation (keys compiled after leading tokens, linked before them) takes the
             // row of its magnitude with the sines negated, as the attention kernels do
-            const int rot = seg_keys ? pd.seg0 : pd.pos0 + slot;
-            const float *cs = rope + (int64_t)(rot < 0 ? -rot : rot) * D + 8 * c;
+            const int rot = SEG ? pd.seg0 : pd.pos0 + slot;
+            const float *cs = p.rope + (int64_t)(rot < 0 ? -rot : rot) * D + 8 * c;
             co[0] = *reinterpret_cast<const floatx4 *>(cs);
             co[1] = *reinterpret_cast<const floatx4 *>(cs + 4);
             sn[0] = *reinterpret_cast<const floatx4 *>(cs + D / 2);
@@ -1919,26 +1958,47 @@ __global__ __launch_bounds__(kThreads) void rotate_keys_bf16(const PageDesc *pag
                 sn[0] = -sn[0];
                 sn[1] = -sn[1];
             }
+            if (SEG && is_new) {
+                const float *cw = p.rope + (int64_t)(sd.local0 + slot) * D + 8 * c;
+                cl[0] = *reinterpret_cast<const floatx4 *>(cw);
+                cl[1] = *reinterpret_cast<const floatx4 *>(cw + 4);
+                sl[0] = *reinterpret_cast<const floatx4 *>(cw + D / 2);
+                sl[1] = *reinterpret_cast<const floatx4 *>(cw + D / 2 + 4);
+            }
         }
-        for (int h0 = hg; h0 < hkv; h0 += HB * n_hg) {
+        for (int h0 = hg; h0 < p.hkv; h0 += HB * n_hg) {
             u32x4 lo[HB], hi[HB];
 #pragma unroll
             for (int j = 0; j < HB; ++j) {
                 const int h = h0 + j * n_hg;
                 lo[j] = u32x4{0, 0, 0, 0};
                 hi[j] = u32x4{0, 0, 0, 0};
-                if (valid && h < hkv) {
-                    const int64_t off = ((int64_t)h * page_size + slot) * D * 2 + c * 16;
-                    lo[j] = *reinterpret_cast<const u32x4 *>(src + off);
-                    hi[j] = *reinterpret_cast<const u32x4 *>(src + off + D);
+                if (valid && h < p.hkv) {
+                    if (is_new) {
+                        const int64_t off = ((int64_t)(sd.row0 + slot) * p.hkv + h) * D * 2 + c * 16;
+                        lo[j] = *reinterpret_cast<const u32x4 *>(p.k_new + off);
+                        hi[j] = *reinterpret_cast<const u32x4 *>(p.k_new + off + D);
+                    } else if (from_page) {
+                        const int64_t off = ((int64_t)h * page_size + slot) * D * 2 + c * 16;
+                        lo[j] = *reinterpret_cast<const u32x4 *>(page_src + off);
+                        hi[j] = *reinterpret_cast<const u32x4 *>(page_src + off + D);
+                    }
                 }
             }
 #pragma unroll
             for (int j = 0; j < HB; ++j) {
                 const int h = h0 + j * n_hg;
-                if (h >= hkv) break;
+                if (h >= p.hkv) break;
                 u32x4 olo = {0, 0, 0, 0}, ohi = {0, 0, 0, 0};
-                if (valid) rope8_bf16(lo[j], hi[j], co, sn, olo, ohi);
+                if (valid) {
+                    if (SEG && is_new) {
+                        u32x4 plo, phi;
+                        rope8_bf16(lo[j], hi[j], cl, sl, plo, phi);
+                        lo[j] = plo;
+                        hi[j] = phi;
+                    }
+                    rope8_bf16(lo[j], hi[j], co, sn, olo, ohi);
+                }
                 const int64_t off = ((int64_t)h * page_size + slot) * D * 2 + c * 16;
                 *reinterpret_cast<u32x4 *>(dst + off) = olo;
                 *reinterpret_cast<u32x4 *>(dst + off + D) = ohi;
@@ -2438,20 +2498,34 @@ hipError_t launch_scatter(const LayerShape &s, void *k_pool, void *v_pool, const
     return hipGetLastError();
 }
 
-hipError_t launch_rotate_keys(const LayerShape &s, const void *k_pool, const float *rope, const PageDesc *pages,
-                              int n_pages, void *k_rot, hipStream_t stream) {
-    if (n_pages <= 0) return hipSuccess;
+hipError_t launch_prepare(const LayerShape &s, void *k_pool, void *v_pool, const void *k_new, const void *v_new,
+                          const float *rope, const PageDesc *pages, const int32_t *page_scatter, int n_pages,
+                          const ScatterDesc *table, int n_scatter, void *k_rot, hipStream_t stream) {
     if (s.dtype != 0) return hipErrorInvalidValue;
-    const int pshift = log2_exact(s.page_size);
-    const int64_t page_bytes = s.page_elems * 2;
-    if (s.d == 128)
-        hipLaunchKernelGGL(rotate_keys_bf16<128>, dim3(n_pages), dim3(kThreads), 0, stream, pages,
-                           static_cast<const uint8_t *>(k_pool), rope, static_cast<uint8_t *>(k_rot), s.hkv, pshift,
-                           page_bytes, s.key_layout);
-    else
-        hipLaunchKernelGGL(rotate_keys_bf16<64>, dim3(n_pages), dim3(kThreads), 0, stream, pages,
-                           static_cast<const uint8_t *>(k_pool), rope, static_cast<uint8_t *>(k_rot), s.hkv, pshift,
-                           page_bytes, s.key_layout);
+    const int n_groups = n_pages + n_scatter * s.hkv;
+    if (n_groups <= 0) return hipSuccess;
+    PrepareParams p;
+    p.pages = pages;
+    p.page_scatter = page_scatter;
+    p.scatter = table;
+    p.k_pool = static_cast<uint8_t *>(k_pool);
+    p.v_pool = static_cast<uint8_t *>(v_pool);
+    p.k_new = static_cast<const uint8_t *>(k_new);
+    p.v_new = static_cast<const uint8_t *>(v_new);
+    p.rope = rope;
+    p.k_rot = static_cast<uint8_t *>(k_rot);
+    p.n_pages = n_pages;
+    p.hkv = s.hkv;
+    p.pshift = log2_exact(s.page_size);
+    p.page_bytes = s.page_elems * 2;
+    const dim3 grid(n_groups);
+    if (s.key_layout) {
+        if (s.d == 128) hipLaunchKernelGGL((link_prepare_bf16<128, true>), grid, dim3(kThreads), 0, stream, p);
+        else hipLaunchKernelGGL((link_prepare_bf16<64, true>), grid, dim3(kThreads), 0, stream, p);
+    } else {
+        if (s.d == 128) hipLaunchKernelGGL((link_prepare_bf16<128, false>), grid, dim3(kThreads), 0, stream, p);
+        else hipLaunchKernelGGL((link_prepare_bf16<64, false>), grid, dim3(kThreads), 0, stream, p);
+    }
     return hipGetLastError();
 }
 

@@ -32,11 +32,14 @@ hipError_t launch_store_fill(const LayerShape &s, void *k_pool, void *v_pool, co
 hipError_t launch_scatter(const LayerShape &s, void *k_pool, void *v_pool, const void *k_new, const void *v_new,
                           const float *rope, const ScatterDesc *table, int n, hipStream_t stream);
 
-// K of `n_pages` logical pages (device PageDesc table) rotated to their absolute positions into
-// k_rot ([logical page][Hkv][page][d]): by each key's position, or by its segment's start when
-// the store's keys are rotated inside their segment; bfloat16 layers only.
-hipError_t launch_rotate_keys(const LayerShape &s, const void *k_pool, const float *rope, const PageDesc *pages,
-                              int n_pages, void *k_rot, hipStream_t stream);
+// The scatter of `n_scatter` private pages and the keys of `n_pages` logical pages (device
+// PageDesc table) rotated to their absolute positions into k_rot ([logical page][Hkv][page][d]),
+// in one launch: by each key's position, or by its segment's start when the store's keys are
+// rotated inside their segment. page_scatter[i] is logical page i's entry in `table`, or -1 for a
+// shared page. bfloat16 layers only.
+hipError_t launch_prepare(const LayerShape &s, void *k_pool, void *v_pool, const void *k_new, const void *v_new,
+                          const float *rope, const PageDesc *pages, const int32_t *page_scatter, int n_pages,
+                          const ScatterDesc *table, int n_scatter, void *k_rot, hipStream_t stream);
 
 struct AttnTables {
     const PageDesc *pages;

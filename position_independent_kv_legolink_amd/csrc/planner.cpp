@@ -131,10 +131,12 @@ pic_plan *build_plan(pic_store *s, const pic_request *reqs, int32_t n_reqs, cons
                         plan->page_refs.push_back(src);
                     }
                     // slots past the new rows are copied from the stored page, or zeroed
+                    plan->page_scatter.push_back((int32_t)plan->scatter.size());
                     plan->scatter.push_back(
                         {dst, src, n_new, seg_row0 + q * B, src >= 0 ? valid : n_new, q * B + c_off, 0, 0});
                     phys[q] = dst;
                 } else {
+                    plan->page_scatter.push_back(-1);
                     phys[q] = g.chunk->pages[q];
                     store_ref(s, phys[q]);
                 }
@@ -316,6 +318,7 @@ pic_plan *build_plan(pic_store *s, const pic_request *reqs, int32_t n_reqs, cons
         return at;
     };
     plan->off_pages = place((int64_t)plan->pages.size() * sizeof(PageDesc));
+    plan->off_page_scatter = place((int64_t)plan->page_scatter.size() * sizeof(int32_t));
     plan->off_row_pos = place((int64_t)plan->row_pos.size() * sizeof(int32_t));
     plan->off_scatter = place((int64_t)plan->scatter.size() * sizeof(ScatterDesc));
     plan->off_work = place((int64_t)plan->work.size() * sizeof(WorkDesc));

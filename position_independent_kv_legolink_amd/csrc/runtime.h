@@ -94,6 +94,7 @@ struct pic_plan {
     std::vector<int32_t> row_pos, row_dst, cu_rows, cu_pages;
     std::vector<piclink::PageDesc> pages;
     std::vector<piclink::ScatterDesc> scatter;
+    std::vector<int32_t> page_scatter;  // per logical page: its scatter entry, or -1 (shared page)
     std::vector<int32_t> cow_src, cow_dst;
     std::vector<piclink::WorkDesc> work;
     int32_t work_queues = 1;            // queues interleaved in `work` (its size is a multiple)
@@ -102,7 +103,7 @@ struct pic_plan {
     int32_t n_slots = 0;
     int64_t n_split_items = 0;
     // workspace layout (byte offsets)
-    int64_t off_pages = 0, off_row_pos = 0, off_scatter = 0, off_work = 0, off_merge = 0, off_ticket = 0;
+    int64_t off_pages = 0, off_page_scatter = 0, off_row_pos = 0, off_scatter = 0, off_work = 0, off_merge = 0, off_ticket = 0;
     int64_t off_part_o = 0, off_part_lse = 0, table_bytes = 0, workspace_bytes = 0;
     bool rotate_keys = false;           // keys rotated into the workspace before attention
     int64_t off_k_rot = 0;
