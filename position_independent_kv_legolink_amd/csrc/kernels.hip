@@ -2018,7 +2018,7 @@ __global__ __launch_bounds__(kThreads, SEG ? 4 : 5) void link_prepare_bf16(Prepa
 // Keys come from the link call's rotated copy when it made one (read as they are), else from the
 // pools, read as stored and rotated here, so that decode needs no per-request copy of shared
 // pages. A key of a store of keys rotated inside their segment turns by its segment's rotation (one
-// cos/sin row per page, as rotate_keys_bf16 turns it). A position-free key at position t = b + o
+// cos/sin row per page, as the rotation pass turns it). A position-free key at position t = b + o
 // (b = its page's first position plus its slot rounded down to 16, o = slot mod 16) turns by
 // R(b) R(o): the cos/sin of t come from rows b and o by the angle-addition formulas, so a 32-key
 // block reads two rows of the table (one per 16-key group, staged through LDS) and the 16 rows of

@@ -14,8 +14,8 @@ hipError_t launch_scatter(const LayerShape &, void *, void *, const void *, cons
                           const ScatterDesc *, int, hipStream_t) {
     return hipErrorNotSupported;
 }
-hipError_t launch_rotate_keys(const LayerShape &, const void *, const float *, const PageDesc *, int, void *,
-                              hipStream_t) {
+hipError_t launch_prepare(const LayerShape &, void *, void *, const void *, const void *, const float *,
+                          const PageDesc *, const int32_t *, int, const ScatterDesc *, int, void *, hipStream_t) {
     return hipErrorNotSupported;
 }
 hipError_t launch_attention(const LayerShape &, const void *, const void *, const void *, const float *,
